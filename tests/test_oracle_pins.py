@@ -1,0 +1,417 @@
+"""Pins of the fp64 oracle against things other than itself: pure-Python brute
+force on tiny inputs, closed forms, second formulations and invariants.
+All CPU, no GPU."""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from oracle import brute
+from synthetic import bf16_round, get_config, make_inputs, token_grid
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _tolist(a):
+    return np.asarray(a, np.float64).tolist()
+
+
+# ----------------------------------------------------------- inputs / grid ---
+def test_token_grid_matches_page_example():
+    g = json.load(open(os.path.join(GOLDEN, "token_grid.json")))
+    t, y, x = token_grid(g["frames"], g["patch_rows"], g["patch_cols"])
+    assert len(t) == g["tokens"]
+    assert int(np.sum(t == 0)) == g["tokens_per_frame"]
+    n = (t * g["patch_rows"] + y) * g["patch_cols"] + x
+    assert np.array_equal(n, np.arange(g["tokens"]))
+
+
+def test_generator_is_deterministic_and_bf16():
+    cfg = get_config("C1")
+    q1, k1, v1 = make_inputs(cfg)
+    q2, k2, v2 = make_inputs(cfg)
+    assert np.array_equal(q1, q2) and np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    assert np.array_equal(bf16_round(q1), q1)
+    logits = q1[0] @ k1[0].T / math.sqrt(cfg.d)
+    assert 2.0 < logits.std() < 4.0
+
+
+# ------------------------------------------------------------------- Weyl ---
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 2048, 32760, 75600, 118800])
+def test_weyl_sequence_is_a_permutation(n):
+    a = orc.weyl_multiplier(n)
+    assert math.gcd(a, n) == 1
+    idx = orc.weyl_indices(n, n)
+    assert np.array_equal(np.sort(idx), np.arange(n))
+
+
+@pytest.mark.parametrize("n", [2048, 32760, 75600, 118800])
+def test_weyl_multiplier_is_golden_fraction(n):
+    # independent arithmetic: floor(n / phi) in 50-digit decimals, then the
+    # smallest value >= it that is coprime to n
+    getcontext().prec = 50
+    phi = (1 + Decimal(5).sqrt()) / 2
+    a = int((Decimal(n) / phi).to_integral_value(rounding="ROUND_FLOOR"))
+    while math.gcd(a, n) != 1:
+        a += 1
+    assert orc.weyl_multiplier(n) == a
+
+
+# ------------------------------------------------------------- key metric ---
+def test_key_metric_is_sample_second_moment():
+    q = _rand((50, 6), 1)
+    m = orc.key_metric(q, 10)
+    idx = orc.weyl_indices(50, 10)
+    for i in range(6):
+        for j in range(6):
+            ref = sum(q[s, i] * q[s, j] for s in idx) / 10
+            assert abs(m[i, j] - ref) < 1e-13
+    assert np.allclose(m, m.T)
+    assert np.min(np.linalg.eigvalsh(m)) > -1e-12
+    assert abs(np.trace(m) - np.mean(np.sum(q[idx] ** 2, axis=1))) < 1e-12
+
+
+def test_key_projection_full_rank_equals_response_profiles():
+    """With r_K = d, k-means on Z = K W must give the labels of k-means on the
+    raw response profiles Q_s k / sqrt(M_s) (a second formulation of the metric)."""
+    rng = np.random.default_rng(3)
+    d, n, ms = 8, 300, 40
+    centres = rng.standard_normal((6, d)) * 3
+    k = centres[rng.integers(6, size=n)] + rng.standard_normal((n, d))
+    q = rng.standard_normal((n, d))
+    w, lam = orc.key_projection(orc.key_metric(q, ms), d)
+    lab_z, _ = orc.lloyd(k @ w, 6, 5)
+    qs = q[orc.weyl_indices(n, ms)]
+    prof = k @ qs.T / math.sqrt(ms)
+    lab_p, _ = orc.lloyd(prof, 6, 5)
+    assert np.array_equal(lab_z, lab_p)
+    assert np.all(np.diff(lam) <= 0)
+
+
+def test_key_projection_distances_are_truncated_metric():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((100, 10))
+    m = orc.key_metric(q, 30)
+    w, _ = orc.key_projection(m, 4)
+    lam, u = np.linalg.eigh(m)
+    mr = u[:, -4:] @ np.diag(lam[-4:]) @ u[:, -4:].T
+    a, b = rng.standard_normal(10), rng.standard_normal(10)
+    assert abs(np.sum(((a - b) @ w) ** 2) - (a - b) @ mr @ (a - b)) < 1e-10
+
+
+def test_partition_labels_invariant_to_power_of_two_scaling():
+    cfg = get_config("C1")
+    q, k, _ = make_inputs(cfg)
+    st = cfg.settings
+    args = (st.n_sample, st.key_rank, st.kv_groups, st.q_groups, st.kmeans_iters)
+    p1 = orc.partition(q[0], k[0], *args)
+    p2 = orc.partition(2 * q[0], 2 * k[0], *args)
+    assert np.array_equal(p1.key_labels, p2.key_labels)
+    assert np.array_equal(p1.q_labels, p2.q_labels)
+
+
+# ----------------------------------------------------------------- k-means ---
+@pytest.mark.parametrize("seed", range(6))
+def test_lloyd_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    n, dim, g = int(rng.integers(8, 64)), int(rng.integers(1, 5)), int(rng.integers(1, 8))
+    x = rng.standard_normal((n, dim)).round(1)          # coarse values: many exact ties
+    if seed % 2:
+        x[n // 2:] = x[: n - n // 2]                    # duplicated points
+    lab, _ = orc.lloyd(x, g, 4)
+    ref = brute.lloyd(_tolist(x), orc.weyl_indices(n, g).tolist(), 4)
+    assert lab.tolist() == ref
+
+
+def test_lloyd_degenerate_group_counts():
+    x = _rand((40, 3), 7)
+    lab, _ = orc.lloyd(x, 1, 5)
+    assert np.all(lab == 0)
+    lab, _ = orc.lloyd(x, 40, 5)                        # every point seeds itself
+    seeds = orc.weyl_indices(40, 40)
+    expect = np.empty(40, np.int64)
+    expect[seeds] = np.arange(40)
+    assert np.array_equal(lab, expect)
+
+
+def test_lloyd_all_equal_points_go_to_group_zero():
+    lab, _ = orc.lloyd(np.ones((30, 4)), 5, 5)
+    assert np.all(lab == 0)
+
+
+def test_query_profile_kmeans_equals_cholesky_coordinates():
+    """Profile-space distances equal |(q - c) L|^2 with L L^T = C_K^T C_K / d, so
+    k-means in either space must give identical labels."""
+    rng = np.random.default_rng(5)
+    d, n, gk = 6, 400, 12
+    ck = rng.standard_normal((gk, d))
+    q = rng.standard_normal((n, d)) * 2
+    lab_p, _ = orc.lloyd(orc.query_profiles(q, ck), 9, 5)
+    low = np.linalg.cholesky(ck.T @ ck / d)
+    lab_c, _ = orc.lloyd(q @ low, 9, 5)
+    assert np.array_equal(lab_p, lab_c)
+
+
+def test_query_centroid_profile_is_profile_mean():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((50, 5))
+    ck = rng.standard_normal((7, 5))
+    lab = rng.integers(4, size=50)
+    cq = orc.group_means(q, lab, 4)
+    prof = orc.query_profiles(q, ck)
+    for g in range(4):
+        assert np.allclose(orc.query_profiles(cq[g:g + 1], ck)[0], prof[lab == g].mean(0))
+
+
+# ------------------------------------------------------------------ layout ---
+def test_group_major_is_stable_permutation_and_round_trips():
+    rng = np.random.default_rng(8)
+    lab = rng.integers(0, 9, size=500).astype(np.int32)
+    lab[lab == 4] = 5                                   # an empty group
+    perm, off = orc.group_major(lab, 9)
+    assert np.array_equal(np.sort(perm), np.arange(500))
+    assert off[0] == 0 and off[-1] == 500 and np.all(np.diff(off) >= 0)
+    assert off[5] == off[4]
+    for g in range(9):
+        seg = perm[off[g]:off[g + 1]]
+        assert np.all(lab[seg] == g) and np.all(np.diff(seg) > 0)
+    x = rng.standard_normal((500, 3))
+    back = np.empty_like(x)
+    back[perm] = x[perm]
+    assert np.array_equal(back, x)
+
+
+# ----------------------------------------------------------------- routing ---
+def test_routed_count_rule():
+    assert orc.routed_count(0.25, 16) == 4
+    assert orc.routed_count(0.26, 256) == 67
+    assert orc.routed_count(0.22, 256) == 57
+    assert orc.routed_count(0.15, 256) == 39
+    assert orc.routed_count(0.35, 256) == 90
+    assert orc.routed_count(0.24, 384) == 93
+    assert orc.routed_count(1.0, 256) == 256
+    assert orc.routed_count(1e-6, 256) == 1
+
+
+def test_route_matches_sorted_tuples():
+    rng = np.random.default_rng(9)
+    cq = rng.standard_normal((11, 4)).round(0)           # integer centroids: many ties
+    ck = rng.standard_normal((13, 4)).round(0)
+    counts = rng.integers(0, 3, size=13)
+    k = 5
+    blocks = orc.route(cq, ck, counts, k)
+    for i in range(11):
+        cand = [(-float(np.dot(cq[i], ck[j])), j) for j in range(13) if counts[j] > 0]
+        pick = sorted(j for _, j in sorted(cand)[:k])
+        assert blocks[i].tolist() == pick + [-1] * (k - len(pick))
+
+
+def test_route_density_one_and_argmax():
+    rng = np.random.default_rng(10)
+    cq, ck = rng.standard_normal((6, 3)), rng.standard_normal((8, 3))
+    counts = np.array([3, 0, 1, 2, 5, 0, 1, 1])
+    full = orc.route(cq, ck, counts, 8)
+    for row in full:
+        assert row.tolist() == [0, 2, 3, 4, 6, 7, -1, -1]
+    one = orc.route(cq, ck, counts, 1)
+    s = cq @ ck.T
+    s[:, counts == 0] = -np.inf
+    assert np.array_equal(one[:, 0], np.argmax(s, axis=1))
+
+
+# ------------------------------------------------------------------ probes ---
+def _hamilton(counts, probes):
+    n = sum(counts)
+    quota = [Fraction(probes * c, n) for c in counts]
+    m = [int(math.floor(x)) for x in quota]
+    left = probes - sum(m)
+    order = sorted(range(len(counts)), key=lambda i: (-(quota[i] - m[i]), i))
+    for i in order[:left]:
+        m[i] += 1
+    return m
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_probe_allocation_is_largest_remainder(seed):
+    rng = np.random.default_rng(200 + seed)
+    counts = rng.integers(0, 40, size=int(rng.integers(1, 20)))
+    counts[0] += 1
+    n = int(counts.sum())
+    for p in {0, 1, n // 3, n - 1, n}:
+        pos = orc.probe_positions(counts, p)
+        assert len(pos) == p and len(set(pos.tolist())) == p
+        off = np.concatenate([[0], np.cumsum(counts)])
+        got = [int(np.sum((pos >= off[i]) & (pos < off[i + 1]))) for i in range(len(counts))]
+        assert got == _hamilton(counts.tolist(), p)
+        if p == n:
+            assert np.array_equal(pos, np.arange(n))
+
+
+def test_probe_ranks_are_centred():
+    pos = orc.probe_positions(np.array([10, 20]), 3)    # m = (1, 2)
+    assert pos.tolist() == [5, 10 + 5, 10 + 15]
+
+
+# --------------------------------------------------------------- attention ---
+def test_dense_matches_brute_force():
+    q, k, v = _rand((9, 5), 11), _rand((13, 5), 12), _rand((13, 3), 13)
+    ref = brute.attention(_tolist(q), _tolist(k), _tolist(v))
+    assert np.allclose(orc.dense_attention(q, k, v), ref, atol=1e-13)
+
+
+def test_dense_closed_forms():
+    q, v = _rand((7, 4), 14), _rand((10, 3), 15)
+    k = np.tile(_rand((1, 4), 16), (10, 1))             # identical keys: uniform weights
+    assert np.allclose(orc.dense_attention(q, k, v), np.tile(v.mean(0), (7, 1)), atol=1e-13)
+    vc = np.tile(_rand((1, 3), 17), (10, 1))            # constant values
+    assert np.allclose(orc.dense_attention(q, _rand((10, 4), 18), vc), vc[:7], atol=1e-13)
+
+
+def test_sparse_matches_brute_force_masked_softmax():
+    rng = np.random.default_rng(19)
+    n, d = 40, 4
+    qlab = rng.integers(0, 4, size=n)
+    klab = rng.integers(0, 5, size=n)
+    qlab[:4] = np.arange(4)
+    klab[:5] = np.arange(5)
+    q, k, v = _rand((n, d), 20), _rand((n, d), 21), _rand((n, 3), 22)
+    qperm, qoff = orc.group_major(qlab, 4)
+    kperm, koff = orc.group_major(klab, 5)
+    blocks = np.array([[0, 2], [1, -1], [3, 4], [0, 4]])
+    o = orc.sparse_attention(q[qperm], k[kperm], v[kperm], qoff, koff, blocks)
+    allowed = [[int(klab[kperm[j]]) in blocks[int(qlab[qperm[i]])].tolist() for j in range(n)]
+               for i in range(n)]
+    ref = brute.attention(_tolist(q[qperm]), _tolist(k[kperm]), _tolist(v[kperm]), allowed)
+    assert np.allclose(o, ref, atol=1e-13)
+    sub = orc.sparse_attention(q[qperm], k[kperm], v[kperm], qoff, koff, blocks,
+                               rows=np.array([7, 3, 30]))
+    assert np.allclose(sub, o[[7, 3, 30]], atol=1e-14)
+
+
+def test_sparse_with_all_groups_is_dense_and_key_order_free():
+    rng = np.random.default_rng(23)
+    n = 50
+    lab = rng.integers(0, 6, size=n)
+    lab[:6] = np.arange(6)
+    q, k, v = _rand((n, 4), 24), _rand((n, 4), 25), _rand((n, 2), 26)
+    perm, off = orc.group_major(lab, 6)
+    blocks = np.tile(np.arange(6), (6, 1))
+    o = orc.sparse_attention(q[perm], k[perm], v[perm], off, off, blocks)
+    assert np.allclose(o, orc.dense_attention(q[perm], k, v), atol=1e-13)
+    o_rev = orc.sparse_attention(q[perm], k[perm], v[perm], off, off, blocks[:, ::-1].copy())
+    assert np.allclose(o, o_rev, atol=1e-14)
+
+
+# -------------------------------------------------------------------- fit ---
+def test_ridge_matches_brute_normal_equations():
+    x, y = _rand((12, 3), 27), _rand((12, 2), 28)
+    b_mat, b_vec = orc.ridge_affine(x, y, 0.3)
+    rb_mat, rb_vec = brute.ridge_affine(_tolist(x), _tolist(y), 0.3)
+    assert np.allclose(b_mat, rb_mat, atol=1e-12) and np.allclose(b_vec, rb_vec, atol=1e-12)
+
+
+def test_ridge_recovers_exact_affine_map():
+    x = _rand((40, 5), 29)
+    b_true, c_true = _rand((5, 5), 30), _rand((5,), 31)
+    y = c_true + x @ b_true
+    for lam in (0.0, 1e-12):
+        b_mat, b_vec = orc.ridge_affine(x, y, lam)
+        assert np.allclose(b_mat, b_true, atol=1e-8) and np.allclose(b_vec, c_true, atol=1e-8)
+
+
+def test_ridge_limits():
+    x, y = _rand((20, 4), 32), _rand((20, 4), 33)
+    b_mat, b_vec = orc.ridge_affine(x, y, 1e14)
+    assert np.abs(b_mat).max() < 1e-10 and np.allclose(b_vec, y.mean(0), atol=1e-9)
+    b_mat, b_vec = orc.ridge_affine(x[:1], y[:1], 1e-3)
+    assert np.all(b_mat == 0) and np.allclose(b_vec, y[0])
+
+
+def test_projector_closed_forms():
+    rng = np.random.default_rng(34)
+    y = rng.standard_normal((30, 3)) @ rng.standard_normal((3, 8))        # rank 3
+    pi, _ = orc.residual_projector(y, 5)
+    assert np.allclose(pi @ y.T, y.T, atol=1e-10)
+    assert abs(np.trace(pi) - 3) < 1e-9
+    assert np.allclose(pi, pi.T) and np.allclose(pi @ pi, pi, atol=1e-12)
+    full = rng.standard_normal((30, 8))
+    assert np.allclose(orc.residual_projector(full, 8)[0], np.eye(8), atol=1e-12)
+    assert np.all(orc.residual_projector(np.zeros((30, 8)), 4)[0] == 0)
+    pi2, s = orc.residual_projector(full, 2)
+    _, _, vt = np.linalg.svd(full)
+    top = vt[:2].T
+    assert np.allclose(pi2, top @ top.T, atol=1e-12)
+    assert np.allclose(pi2 @ (full.T @ full) @ top, full.T @ full @ top, atol=1e-9)
+
+
+def test_projector_on_right_singular_space():
+    """Pi acts on the output (column) side: it fixes the rows of Y, not its columns."""
+    rng = np.random.default_rng(35)
+    y = rng.standard_normal((6, 2)) @ rng.standard_normal((2, 9))        # P < d
+    pi, _ = orc.residual_projector(y, 2)
+    assert pi.shape == (9, 9)
+    assert np.allclose(y @ pi, y, atol=1e-12)
+
+
+def test_probe_fit_single_probe():
+    x, y = _rand((1, 4), 36), _rand((1, 4), 37)
+    b_mat, b_vec = orc.probe_fit(x, y, 1e-3, 2)
+    assert np.all(b_mat == 0) and np.allclose(b_vec, y[0], atol=1e-14)
+
+
+# -------------------------------------------------------------- full call ---
+def _c1(**kw):
+    cfg = get_config("C1")
+    q, k, v = make_inputs(cfg)
+    st = cfg.settings
+    args = dict(n_sample=st.n_sample, key_rank=st.key_rank, kv_groups=st.kv_groups,
+                q_groups=st.q_groups, kmeans_iters=st.kmeans_iters, density=st.density,
+                probes=st.probes, ridge_lambda=st.ridge_lambda, corr_rank=st.corr_rank)
+    args.update(kw)
+    return q[0], k[0], v[0], args
+
+
+def test_call_with_no_probes_is_plain_sparse_output():
+    q, k, v, a = _c1(probes=0)
+    r = orc.oracle_head(q, k, v, **a)
+    back = np.empty_like(r.o_sparse)
+    back[r.q_perm] = r.o_sparse
+    assert np.array_equal(r.o, back)
+
+
+def test_call_with_every_row_probed_is_dense():
+    q, k, v, a = _c1(probes=2048)
+    r = orc.oracle_head(q, k, v, **a)
+    assert np.allclose(r.o, orc.dense_attention(q, k, v), atol=1e-12)
+
+
+def test_call_at_full_density_is_dense():
+    q, k, v, a = _c1(density=1.0)
+    r = orc.oracle_head(q, k, v, **a)
+    assert np.all(r.blocks >= 0) or np.all((r.blocks >= 0).sum(1) == (np.diff(r.key_off) > 0).sum())
+    assert np.abs(r.y).max() < 1e-12
+    assert np.allclose(r.o, orc.dense_attention(q, k, v), atol=1e-11)
+
+
+def test_call_c1_structure():
+    q, k, v, a = _c1()
+    r = orc.oracle_head(q, k, v, **a)
+    assert np.array_equal(np.sort(r.q_perm), np.arange(2048))
+    assert r.blocks.shape == (16, 4) and len(r.probe_pos) == 64
+    assert np.all(np.isfinite(r.o))
+    # the unprobed rows get exactly O_s + b' + O_s B', in original order
+    o_perm = r.o_sparse + r.b_vec + r.o_sparse @ r.b_mat
+    unprobed = np.setdiff1d(np.arange(2048), r.probe_pos)
+    assert np.allclose(r.o[r.q_perm[unprobed]], o_perm[unprobed], atol=1e-13)
+    # probe rows output their exact dense value
+    dense = orc.dense_attention(q, k, v)
+    assert np.allclose(r.o[r.probe_orig], dense[r.probe_orig], atol=1e-12)
