@@ -1,0 +1,763 @@
+// C ABI of the SparsePR attention-call hot path: validation, workspace, stage
+// sequencing, host fp64 solves and launches. See include/sparsepr.h for the contract.
+#include "../../include/sparsepr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <numeric>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "host_linalg.h"
+#include "kernels.h"
+
+using namespace spr;
+
+struct sparsepr_ctx {
+    sparsepr_params p{};
+    int device = 0;
+    int H = 0, N = 0, d = 0, Gk = 0, Gq = 0, rK = 0, Dq = 0, k = 0, P = 0, T = 0;
+    int nblk = 0, maxu = 0, splits = 0, dense_units = 0, gmax = 0;
+    int64_t weyl_a = 0;
+
+    void* arena = nullptr;
+    size_t arena_bytes = 0;
+    // bf16 copies of fp32 inputs, and the group-major Q/K/V
+    bf16_t *qb = nullptr, *kb = nullptr, *vb = nullptr;
+    bf16_t *qp = nullptr, *kp = nullptr, *vp = nullptr;
+    // partition
+    float *z = nullptr, *zerr = nullptr, *yq = nullptr, *yerr = nullptr;
+    int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
+    int32_t *koff = nullptr, *qoff = nullptr, *kgrp = nullptr;
+    int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
+    double *mk = nullptr, *w64 = nullptr, *l64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
+    double *kraw = nullptr, *qraw = nullptr;
+    float *w32 = nullptr, *l32 = nullptr, *wfro = nullptr, *lfro = nullptr;
+    float *kc32 = nullptr, *qc32 = nullptr, *kcn = nullptr, *qcn = nullptr;
+    // route
+    int32_t *blocks = nullptr, *ucount = nullptr, *probe_pos = nullptr, *probe_orig = nullptr;
+    int32_t *probe_grp = nullptr, *probe_of = nullptr, *nunits = nullptr;
+    int2* units = nullptr;
+    int64_t* pairs = nullptr;
+    // attention, probes, fit
+    float *o_s = nullptr, *part_ml = nullptr, *part_od = nullptr, *part_os = nullptr;
+    float *px = nullptr, *py = nullptr, *pod = nullptr, *bm32 = nullptr, *bv32 = nullptr;
+    // dense baseline: one query group and one key group holding every token
+    int32_t *dense_meta = nullptr;     // qoff {0,N}, koff {0,N}, blocks {0}, nunits {..}
+    int2* dense_unit_list = nullptr;
+
+    // host mirrors
+    std::vector<double> h_mk, h_w64, h_kraw, h_l64, h_bm, h_bv;
+    std::vector<float> h_w32, h_wfro, h_l32, h_lfro, h_x, h_y, h_bm32, h_bv32;
+
+    int stage = 0;
+    bool poisoned = false;
+    std::string err;
+    hipStream_t last_stream = nullptr;
+    bool timing = false;
+    hipEvent_t ev[8] = {};
+    bool ev_used[8] = {};
+};
+
+namespace {
+
+constexpr int kStagePartition = 1, kStageRoute = 2, kStageAttn = 3, kStageFit = 4, kStageCorrect = 5;
+
+int64_t weyl_multiplier(int64_t n) {
+    int64_t a = static_cast<int64_t>((static_cast<uint64_t>(n) * 0x9E3779B9ull) >> 32);
+    while (std::gcd(a, n) != 1) ++a;
+    return a;
+}
+
+int routed_count(double density, int gk) {
+    int k = static_cast<int>(std::ceil(density * gk - 1e-9));
+    return std::min(std::max(k, 1), gk);
+}
+
+int32_t validate(const sparsepr_params* p) {
+    if (!p) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->heads < 1 || p->n < 1 || p->n > (1 << 24)) return SPARSEPR_ERR_SHAPE;
+    if ((int64_t)p->heads * p->n > 0x7fffffffLL) return SPARSEPR_ERR_SHAPE;
+    if (p->d != 64 && p->d != 128) return SPARSEPR_ERR_SHAPE;
+    if (p->dtype != SPARSEPR_BF16 && p->dtype != SPARSEPR_F32) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->n_sample < 1 || p->n_sample > p->n) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->key_rank < 1 || p->key_rank > p->d) return SPARSEPR_ERR_INVALID_ARG;
+    const int gmax = std::min(p->n, kMaxGroups);
+    if (p->kv_groups < 1 || p->kv_groups > gmax) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->q_groups < 1 || p->q_groups > gmax) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->kmeans_iters < 1 || p->kmeans_iters > 100) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->probes < 0 || p->probes > std::min(p->n, 4096)) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->corr_rank < 0 || p->corr_rank > p->d) return SPARSEPR_ERR_INVALID_ARG;
+    if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
+    if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->flags & ~SPARSEPR_F_STAGE_TIMING) return SPARSEPR_ERR_INVALID_ARG;
+    return SPARSEPR_OK;
+}
+
+// Arena layout: every buffer 256-byte aligned; pass 1 sizes, pass 2 assigns.
+struct Arena {
+    char* base = nullptr;
+    size_t used = 0;
+    template <typename T>
+    void take(T*& ptr, size_t count) {
+        used = (used + 255) & ~size_t(255);
+        ptr = base ? reinterpret_cast<T*>(base + used) : nullptr;
+        used += sizeof(T) * std::max<size_t>(count, 1);
+    }
+};
+
+void derive(sparsepr_ctx& c) {
+    const sparsepr_params& p = c.p;
+    c.H = p.heads;
+    c.N = p.n;
+    c.d = p.d;
+    c.Gk = p.kv_groups;
+    c.Gq = p.q_groups;
+    c.rK = p.key_rank;
+    c.Dq = (c.Gk <= c.d) ? c.Gk : c.d;
+    c.k = routed_count(p.density, c.Gk);
+    c.P = p.probes;
+    c.T = p.kmeans_iters;
+    c.nblk = (c.N + kSortChunk - 1) / kSortChunk;
+    c.maxu = (c.N + kAttnRows - 1) / kAttnRows + c.Gq;
+    c.dense_units = (c.N + kAttnRows - 1) / kAttnRows;
+    c.splits = probe_splits(c.N);
+    c.gmax = std::max(c.Gk, c.Gq);
+    c.weyl_a = weyl_multiplier(c.N);
+}
+
+void layout(sparsepr_ctx& c, Arena& a) {
+    const size_t H = c.H, N = c.N, d = c.d, HN = H * N, HND = HN * d;
+    const size_t P = std::max(c.P, 1);
+    if (c.p.dtype == SPARSEPR_F32) {
+        a.take(c.qb, HND);
+        a.take(c.kb, HND);
+        a.take(c.vb, HND);
+    }
+    a.take(c.qp, HND);
+    a.take(c.kp, HND);
+    a.take(c.vp, HND);
+    a.take(c.z, HN * c.rK);
+    a.take(c.zerr, HN);
+    a.take(c.yq, HN * c.Dq);
+    a.take(c.yerr, HN);
+    a.take(c.klab, HN);
+    a.take(c.qlab, HN);
+    a.take(c.kperm, HN);
+    a.take(c.qperm, HN);
+    a.take(c.koff, H * (c.Gk + 1));
+    a.take(c.qoff, H * (c.Gq + 1));
+    a.take(c.kgrp, HN);
+    a.take(c.flag_cnt, 2 * (size_t)c.T * H);
+    a.take(c.flag_list, HN);
+    a.take(c.blkhist, H * c.nblk * c.gmax);
+    a.take(c.blkoff, H * c.nblk * c.gmax);
+    a.take(c.mk, H * d * d);
+    a.take(c.w64, H * d * c.rK);
+    a.take(c.l64, H * d * c.Dq);
+    a.take(c.kc64, H * c.Gk * c.rK);
+    a.take(c.qc64, H * c.Gq * c.Dq);
+    a.take(c.kraw, H * c.Gk * d);
+    a.take(c.qraw, H * c.Gq * d);
+    a.take(c.w32, H * d * c.rK);
+    a.take(c.l32, H * d * c.Dq);
+    a.take(c.wfro, H);
+    a.take(c.lfro, H);
+    a.take(c.kc32, H * c.Gk * c.rK);
+    a.take(c.qc32, H * c.Gq * c.Dq);
+    a.take(c.kcn, H * c.Gk);
+    a.take(c.qcn, H * c.Gq);
+    a.take(c.blocks, H * c.Gq * c.k);
+    a.take(c.ucount, H * c.Gq);
+    a.take(c.probe_pos, H * P);
+    a.take(c.probe_orig, H * P);
+    a.take(c.probe_grp, H * P);
+    a.take(c.probe_of, HN);
+    a.take(c.nunits, H);
+    a.take(c.units, H * c.maxu);
+    a.take(c.pairs, H);
+    a.take(c.o_s, HND);
+    a.take(c.part_ml, H * c.splits * P * 4);
+    a.take(c.part_od, H * c.splits * P * d);
+    a.take(c.part_os, H * c.splits * P * d);
+    a.take(c.px, H * P * d);
+    a.take(c.py, H * P * d);
+    a.take(c.pod, H * P * d);
+    a.take(c.bm32, H * d * d);
+    a.take(c.bv32, H * d);
+    a.take(c.dense_meta, 8);
+    a.take(c.dense_unit_list, c.dense_units);
+}
+
+void parallel_heads(int heads, const std::function<void(int)>& fn) {
+    const int hw = std::max(1u, std::thread::hardware_concurrency());
+    const int nt = std::min(heads, std::min(hw, 32));
+    if (nt <= 1) {
+        for (int h = 0; h < heads; ++h) fn(h);
+        return;
+    }
+    std::vector<std::thread> pool;
+    for (int t = 0; t < nt; ++t)
+        pool.emplace_back([&, t]() {
+            for (int h = t; h < heads; h += nt) fn(h);
+        });
+    for (auto& th : pool) th.join();
+}
+
+int32_t fail(sparsepr_ctx* c, int32_t code, const std::string& msg) {
+    if (c) {
+        c->err = msg;
+        if (code == SPARSEPR_ERR_HIP) c->poisoned = true;
+    }
+    return code;
+}
+
+#define SPR_HIP(ctx, expr)                                                                  \
+    do {                                                                                    \
+        hipError_t e_ = (expr);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail((ctx), SPARSEPR_ERR_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+    } while (0)
+
+#define SPR_LAUNCHED(ctx, what)                                                             \
+    do {                                                                                    \
+        hipError_t e_ = hipGetLastError();                                                  \
+        if (e_ != hipSuccess)                                                               \
+            return fail((ctx), SPARSEPR_ERR_HIP, std::string(what ": ") + hipGetErrorString(e_)); \
+    } while (0)
+
+int32_t enter(sparsepr_ctx* c, int need_stage) {
+    if (!c) return SPARSEPR_ERR_INVALID_ARG;
+    if (c->poisoned) return fail(c, SPARSEPR_ERR_HIP, "context poisoned by an earlier HIP error");
+    if (c->stage < need_stage) return fail(c, SPARSEPR_ERR_ORDER, "stage called before its prerequisite");
+    if (hipSetDevice(c->device) != hipSuccess) return fail(c, SPARSEPR_ERR_HIP, "hipSetDevice");
+    return SPARSEPR_OK;
+}
+
+void mark(sparsepr_ctx* c, int slot, hipStream_t st) {
+    if (c->timing) {
+        hipEventRecord(c->ev[slot], st);
+        c->ev_used[slot] = true;
+    }
+}
+
+// bf16 view of an input tensor (converted into the workspace when the dtype is fp32)
+const bf16_t* as_bf16(sparsepr_ctx* c, const void* x, bf16_t* scratch, hipStream_t st) {
+    if (c->p.dtype == SPARSEPR_BF16) return static_cast<const bf16_t*>(x);
+    launch_to_bf16(static_cast<const float*>(x), scratch, (size_t)c->H * c->N * c->d, st);
+    return scratch;
+}
+
+bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
+
+// Lloyd rounds on the device: assign (fp32, certified) -> fp64 recheck -> counting sort
+// -> fp64 means and projected centroids. After the last round `sorted`/`off` are the
+// stable group-major permutation and `mean_raw` the raw group means (zero if empty).
+int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, const float* y, const float* yerr, int dim,
+              const double* l64, int groups, int32_t* labels, int32_t* flags, int32_t* sorted,
+              int32_t* off, double* mean_raw, double* c64, float* c32, float* cnorm,
+              hipStream_t st) {
+    launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, c64, c32, cnorm, st);
+    SPR_LAUNCHED(c, "seed centroids");
+    for (int t = 0; t < c->T; ++t) {
+        int32_t* fc = flags + (size_t)t * c->H;
+        launch_assign(y, yerr, c->H, c->N, dim, c32, cnorm, groups, labels, fc, c->flag_list, st);
+        SPR_LAUNCHED(c, "assign");
+        launch_recheck(x, c->H, c->N, c->d, l64, dim, c64, groups, fc, c->flag_list, labels, st);
+        SPR_LAUNCHED(c, "recheck");
+        launch_counting_sort(labels, c->H, c->N, groups, c->blkhist, c->blkoff, sorted, off, st);
+        SPR_LAUNCHED(c, "counting sort");
+        launch_group_means(x, c->H, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, c32,
+                           cnorm, st);
+        SPR_LAUNCHED(c, "group means");
+    }
+    return SPARSEPR_OK;
+}
+
+double frob32(const float* a, size_t count) {
+    double s = 0.0;
+    for (size_t i = 0; i < count; ++i) s += (double)a[i] * a[i];
+    return std::sqrt(s);
+}
+
+// Host: query metric factor per head from the raw key centroids, then upload.
+int32_t query_factor_all(sparsepr_ctx* c, hipStream_t st) {
+    const size_t H = c->H, d = c->d, Gk = c->Gk, Dq = c->Dq;
+    c->h_kraw.resize(H * Gk * d);
+    SPR_HIP(c, hipMemcpyAsync(c->h_kraw.data(), c->kraw, sizeof(double) * H * Gk * d,
+                              hipMemcpyDeviceToHost, st));
+    SPR_HIP(c, hipStreamSynchronize(st));
+    c->h_l64.assign(H * d * Dq, 0.0);
+    c->h_l32.resize(H * d * Dq);
+    c->h_lfro.resize(H);
+    std::vector<int> rc(H, 0), dims(H, 0);
+    parallel_heads((int)H, [&](int h) {
+        rc[h] = query_factor((int)d, (int)Gk, &c->h_kraw[h * Gk * d], &c->h_l64[h * d * Dq], &dims[h]);
+    });
+    for (size_t h = 0; h < H; ++h) {
+        if (rc[h] != 0 || dims[h] != (int)Dq)
+            return fail(c, SPARSEPR_ERR_NUMERIC, "query metric factor failed (non-finite centroids)");
+        for (size_t i = 0; i < d * Dq; ++i) c->h_l32[h * d * Dq + i] = (float)c->h_l64[h * d * Dq + i];
+        c->h_lfro[h] = (float)(frob32(&c->h_l32[h * d * Dq], d * Dq) * (1.0 + 1e-6));
+    }
+    SPR_HIP(c, hipMemcpyAsync(c->l64, c->h_l64.data(), sizeof(double) * H * d * Dq,
+                              hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->l32, c->h_l32.data(), sizeof(float) * H * d * Dq,
+                              hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->lfro, c->h_lfro.data(), sizeof(float) * H, hipMemcpyHostToDevice, st));
+    return SPARSEPR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparsepr_validate(const sparsepr_params* p) { return validate(p); }
+
+size_t sparsepr_workspace_bytes(const sparsepr_params* p) {
+    if (validate(p) != SPARSEPR_OK) return 0;
+    sparsepr_ctx c;
+    c.p = *p;
+    derive(c);
+    Arena a;
+    layout(c, a);
+    return a.used;
+}
+
+const char* sparsepr_status_str(int32_t s) {
+    switch (s) {
+        case SPARSEPR_OK: return "ok";
+        case SPARSEPR_ERR_INVALID_ARG: return "invalid argument";
+        case SPARSEPR_ERR_SHAPE: return "unsupported shape";
+        case SPARSEPR_ERR_OOM: return "out of memory";
+        case SPARSEPR_ERR_HIP: return "HIP error";
+        case SPARSEPR_ERR_ORDER: return "stage order";
+        case SPARSEPR_ERR_NUMERIC: return "numerical failure";
+        default: return "unknown status";
+    }
+}
+
+const char* sparsepr_last_error(const sparsepr_ctx* c) { return c ? c->err.c_str() : ""; }
+
+int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
+    if (!out) return SPARSEPR_ERR_INVALID_ARG;
+    const int32_t v = validate(p);
+    if (v != SPARSEPR_OK) return v;
+    sparsepr_ctx* c = new (std::nothrow) sparsepr_ctx();
+    if (!c) return SPARSEPR_ERR_OOM;
+    c->p = *p;
+    derive(*c);
+    c->timing = (p->flags & SPARSEPR_F_STAGE_TIMING) != 0;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return SPARSEPR_ERR_HIP;
+    }
+    Arena a;
+    layout(*c, a);
+    c->arena_bytes = a.used;
+    if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+        delete c;
+        return SPARSEPR_ERR_OOM;
+    }
+    Arena b;
+    b.base = static_cast<char*>(c->arena);
+    layout(*c, b);
+    if (c->timing)
+        for (auto& e : c->ev) hipEventCreate(&e);
+    // dense baseline metadata
+    const int meta[8] = {0, c->N, 0, c->N, 0, c->dense_units, 0, 0};
+    if (hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice) != hipSuccess) {
+        sparsepr_destroy(c);
+        return SPARSEPR_ERR_HIP;
+    }
+    launch_units(c->dense_meta, 1, 1, kAttnRows, c->dense_units, c->dense_unit_list,
+                 c->dense_meta + 6, nullptr);
+    if (hipDeviceSynchronize() != hipSuccess) {
+        sparsepr_destroy(c);
+        return SPARSEPR_ERR_HIP;
+    }
+    *out = c;
+    return SPARSEPR_OK;
+}
+
+void sparsepr_destroy(sparsepr_ctx* c) {
+    if (!c) return;
+    hipSetDevice(c->device);
+    hipDeviceSynchronize();
+    if (c->timing)
+        for (auto& e : c->ev)
+            if (e) hipEventDestroy(e);
+    if (c->arena) hipFree(c->arena);
+    delete c;
+}
+
+int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* stream) {
+    int32_t rc = enter(c, 0);
+    if (rc) return rc;
+    if (!q || !k || !aligned16(q) || !aligned16(k)) return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned q/k");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    c->stage = 0;
+    mark(c, 0, st);
+    const size_t H = c->H, d = c->d, rK = c->rK;
+    const bf16_t* q16 = as_bf16(c, q, c->qb, st);
+    const bf16_t* k16 = as_bf16(c, k, c->kb, st);
+    launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * H, st);
+    // M_K and its leading eigenvectors (host fp64)
+    launch_metric(q16, c->H, c->N, c->d, c->p.n_sample, c->weyl_a, c->mk, st);
+    SPR_LAUNCHED(c, "metric");
+    c->h_mk.resize(H * d * d);
+    SPR_HIP(c, hipMemcpyAsync(c->h_mk.data(), c->mk, sizeof(double) * H * d * d,
+                              hipMemcpyDeviceToHost, st));
+    SPR_HIP(c, hipStreamSynchronize(st));
+    c->h_w64.assign(H * d * rK, 0.0);
+    c->h_w32.resize(H * d * rK);
+    c->h_wfro.resize(H);
+    std::vector<int> prc(H, 0);
+    parallel_heads((int)H, [&](int h) {
+        prc[h] = key_projection((int)d, &c->h_mk[h * d * d], (int)rK, &c->h_w64[h * d * rK]);
+    });
+    for (size_t h = 0; h < H; ++h) {
+        if (prc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "metric eigensolve failed (non-finite input)");
+        for (size_t i = 0; i < d * rK; ++i) c->h_w32[h * d * rK + i] = (float)c->h_w64[h * d * rK + i];
+        c->h_wfro[h] = (float)(frob32(&c->h_w32[h * d * rK], d * rK) * (1.0 + 1e-6));
+    }
+    SPR_HIP(c, hipMemcpyAsync(c->w64, c->h_w64.data(), sizeof(double) * H * d * rK, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->w32, c->h_w32.data(), sizeof(float) * H * d * rK, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->wfro, c->h_wfro.data(), sizeof(float) * H, hipMemcpyHostToDevice, st));
+    // keys: Z = K W, Lloyd
+    launch_project(k16, c->H, c->N, c->d, c->w32, c->rK, c->wfro, c->z, c->zerr, st);
+    SPR_LAUNCHED(c, "project keys");
+    rc = lloyd(c, k16, c->z, c->zerr, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff,
+               c->kraw, c->kc64, c->kc32, c->kcn, st);
+    if (rc) return rc;
+    // queries: logit-profile metric factor (host fp64), Y = Q L, Lloyd
+    rc = query_factor_all(c, st);
+    if (rc) return rc;
+    launch_project(q16, c->H, c->N, c->d, c->l32, c->Dq, c->lfro, c->yq, c->yerr, st);
+    SPR_LAUNCHED(c, "project queries");
+    rc = lloyd(c, q16, c->yq, c->yerr, c->Dq, c->l64, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H,
+               c->qperm, c->qoff, c->qraw, c->qc64, c->qc32, c->qcn, st);
+    if (rc) return rc;
+    mark(c, 1, st);
+    c->stage = kStagePartition;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_set_partition(sparsepr_ctx* c, const void* q, const void* k,
+                               const int32_t* key_labels, const int32_t* q_labels, int32_t host,
+                               void* stream) {
+    int32_t rc = enter(c, 0);
+    if (rc) return rc;
+    if (!q || !k || !key_labels || !q_labels || !aligned16(q) || !aligned16(k))
+        return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned argument");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    const size_t HN = (size_t)c->H * c->N;
+    if (host) {
+        for (size_t i = 0; i < HN; ++i)
+            if (key_labels[i] < 0 || key_labels[i] >= c->Gk || q_labels[i] < 0 || q_labels[i] >= c->Gq)
+                return fail(c, SPARSEPR_ERR_INVALID_ARG, "label out of range");
+    }
+    const hipMemcpyKind kind = host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+    SPR_HIP(c, hipMemcpyAsync(c->klab, key_labels, sizeof(int32_t) * HN, kind, st));
+    SPR_HIP(c, hipMemcpyAsync(c->qlab, q_labels, sizeof(int32_t) * HN, kind, st));
+    const bf16_t* q16 = as_bf16(c, q, c->qb, st);
+    const bf16_t* k16 = as_bf16(c, k, c->kb, st);
+    launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * c->H, st);
+    launch_counting_sort(c->klab, c->H, c->N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
+    launch_group_means(k16, c->H, c->N, c->d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr,
+                       nullptr, nullptr, st);
+    launch_counting_sort(c->qlab, c->H, c->N, c->Gq, c->blkhist, c->blkoff, c->qperm, c->qoff, st);
+    launch_group_means(q16, c->H, c->N, c->d, c->qperm, c->qoff, c->Gq, c->qraw, nullptr, 0, nullptr,
+                       nullptr, nullptr, st);
+    SPR_LAUNCHED(c, "set partition");
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));   // host labels must stay valid until copied
+    c->stage = kStagePartition;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void* v, void* stream) {
+    int32_t rc = enter(c, kStagePartition);
+    if (rc) return rc;
+    if (!q || !k || !v || !aligned16(q) || !aligned16(k) || !aligned16(v))
+        return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned q/k/v");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    mark(c, 2, st);
+    const bf16_t* q16 = as_bf16(c, q, c->qb, st);
+    const bf16_t* k16 = as_bf16(c, k, c->kb, st);
+    const bf16_t* v16 = as_bf16(c, v, c->vb, st);
+    launch_permute(q16, c->qperm, c->H, c->N, c->d, c->qp, st);
+    launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, st);
+    launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
+    SPR_LAUNCHED(c, "permute");
+    launch_fill_groups(c->koff, c->H, c->N, c->Gk, c->kgrp, st);
+    launch_fill_i64(c->pairs, 0, c->H, st);
+    launch_route(c->qraw, c->kraw, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k, c->blocks,
+                 c->ucount, c->pairs, st);
+    SPR_LAUNCHED(c, "route");
+    launch_fill_i32(c->probe_of, -1, (size_t)c->H * c->N, st);
+    launch_probes(c->qoff, c->qperm, c->H, c->N, c->Gq, c->P, c->probe_pos, c->probe_orig,
+                  c->probe_grp, c->probe_of, st);
+    launch_units(c->qoff, c->H, c->Gq, kAttnRows, c->maxu, c->units, c->nunits, st);
+    SPR_LAUNCHED(c, "probes/units");
+    mark(c, 3, st);
+    c->stage = kStageRoute;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
+    int32_t rc = enter(c, kStageRoute);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    launch_vbsa(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
+                c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, c->o_s, 0,
+                st);
+    SPR_LAUNCHED(c, "sparse attention");
+    mark(c, 4, st);
+    launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P, c->kgrp,
+                 c->Gk, c->blocks, c->Gq, c->k, c->part_ml, c->part_od, c->part_os, st);
+    launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
+                       c->py, c->pod, st);
+    SPR_LAUNCHED(c, "probe rows");
+    mark(c, 5, st);
+    c->stage = kStageAttn;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
+    int32_t rc = enter(c, kStageAttn);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    const size_t H = c->H, d = c->d, P = c->P;
+    c->h_bm.assign(H * d * d, 0.0);
+    c->h_bv.assign(H * d, 0.0);
+    if (P > 0) {
+        c->h_x.resize(H * P * d);
+        c->h_y.resize(H * P * d);
+        SPR_HIP(c, hipMemcpyAsync(c->h_x.data(), c->px, sizeof(float) * H * P * d, hipMemcpyDeviceToHost, st));
+        SPR_HIP(c, hipMemcpyAsync(c->h_y.data(), c->py, sizeof(float) * H * P * d, hipMemcpyDeviceToHost, st));
+        SPR_HIP(c, hipStreamSynchronize(st));
+        std::vector<int> frc(H, 0);
+        parallel_heads((int)H, [&](int h) {
+            std::vector<double> x(P * d), y(P * d);
+            for (size_t i = 0; i < P * d; ++i) {
+                x[i] = c->h_x[h * P * d + i];
+                y[i] = c->h_y[h * P * d + i];
+            }
+            frc[h] = probe_fit((int)P, (int)d, x.data(), y.data(), c->p.ridge_lambda, c->p.corr_rank,
+                               &c->h_bm[h * d * d], &c->h_bv[h * d]);
+        });
+        for (size_t h = 0; h < H; ++h)
+            if (frc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "probe fit failed (non-finite probe outputs)");
+    }
+    c->h_bm32.resize(H * d * d);
+    c->h_bv32.resize(H * d);
+    for (size_t i = 0; i < H * d * d; ++i) c->h_bm32[i] = (float)c->h_bm[i];
+    for (size_t i = 0; i < H * d; ++i) c->h_bv32[i] = (float)c->h_bv[i];
+    SPR_HIP(c, hipMemcpyAsync(c->bm32, c->h_bm32.data(), sizeof(float) * H * d * d, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->bv32, c->h_bv32.data(), sizeof(float) * H * d, hipMemcpyHostToDevice, st));
+    mark(c, 6, st);
+    c->stage = kStageFit;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_correct(sparsepr_ctx* c, void* o, void* stream) {
+    int32_t rc = enter(c, kStageFit);
+    if (rc) return rc;
+    if (!o || !aligned16(o)) return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned o");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    launch_correct(c->o_s, c->bm32, c->bv32, c->pod, c->probe_of, c->qperm, c->H, c->N, c->d, c->P, o,
+                   c->p.dtype == SPARSEPR_F32 ? 1 : 0, st);
+    SPR_LAUNCHED(c, "correct");
+    mark(c, 7, st);
+    c->stage = kStageCorrect;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_attention(sparsepr_ctx* c, const void* q, const void* k, const void* v, void* o,
+                           void* stream) {
+    int32_t rc = sparsepr_partition(c, q, k, stream);
+    if (!rc) rc = sparsepr_route(c, q, k, v, stream);
+    if (!rc) rc = sparsepr_sparse_attn(c, stream);
+    if (!rc) rc = sparsepr_probe_fit(c, stream);
+    if (!rc) rc = sparsepr_correct(c, o, stream);
+    return rc;
+}
+
+int32_t sparsepr_dense_attn(sparsepr_ctx* c, const void* q, const void* k, const void* v, void* o,
+                            void* stream) {
+    int32_t rc = enter(c, 0);
+    if (rc) return rc;
+    if (!q || !k || !v || !o || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned argument");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    const bf16_t* q16 = as_bf16(c, q, c->qb, st);
+    const bf16_t* k16 = as_bf16(c, k, c->kb, st);
+    const bf16_t* v16 = as_bf16(c, v, c->vb, st);
+    launch_vbsa(q16, k16, v16, c->H, c->N, c->d, c->dense_meta, 0, c->dense_meta + 2, 0,
+                c->dense_meta + 4, 0, 1, c->dense_unit_list, 0, c->dense_meta + 6, 0, c->dense_units, o,
+                c->p.dtype == SPARSEPR_F32 ? 0 : 1, st);
+    SPR_LAUNCHED(c, "dense attention");
+    return SPARSEPR_OK;
+}
+
+// ---------------------------------------------------------------- inspection ---
+static int32_t copy_out(sparsepr_ctx* c, void* dst, const void* src, size_t bytes, int32_t host,
+                        hipStream_t st) {
+    if (!dst) return SPARSEPR_OK;
+    SPR_HIP(c, hipMemcpyAsync(dst, src, bytes, host ? hipMemcpyDeviceToHost : hipMemcpyDeviceToDevice, st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_partition(sparsepr_ctx* c, int32_t* key_labels, int32_t* q_labels,
+                               int32_t* key_perm, int32_t* q_perm, int32_t* key_off, int32_t* q_off,
+                               int32_t host, void* stream) {
+    int32_t rc = enter(c, kStagePartition);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t HN = (size_t)c->H * c->N;
+    if ((rc = copy_out(c, key_labels, c->klab, 4 * HN, host, st))) return rc;
+    if ((rc = copy_out(c, q_labels, c->qlab, 4 * HN, host, st))) return rc;
+    if ((rc = copy_out(c, key_perm, c->kperm, 4 * HN, host, st))) return rc;
+    if ((rc = copy_out(c, q_perm, c->qperm, 4 * HN, host, st))) return rc;
+    if ((rc = copy_out(c, key_off, c->koff, 4 * (size_t)c->H * (c->Gk + 1), host, st))) return rc;
+    if ((rc = copy_out(c, q_off, c->qoff, 4 * (size_t)c->H * (c->Gq + 1), host, st))) return rc;
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_routing(sparsepr_ctx* c, int32_t* blocks, int32_t* probe_orig, int32_t* probe_pos,
+                             int32_t host, void* stream) {
+    int32_t rc = enter(c, kStageRoute);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = copy_out(c, blocks, c->blocks, 4 * (size_t)c->H * c->Gq * c->k, host, st))) return rc;
+    if (c->P > 0) {
+        if ((rc = copy_out(c, probe_orig, c->probe_orig, 4 * (size_t)c->H * c->P, host, st))) return rc;
+        if ((rc = copy_out(c, probe_pos, c->probe_pos, 4 * (size_t)c->H * c->P, host, st))) return rc;
+    }
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_centroids(sparsepr_ctx* c, double* key_centroids, double* q_centroids, int32_t host,
+                               void* stream) {
+    int32_t rc = enter(c, kStagePartition);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = copy_out(c, key_centroids, c->kraw, 8 * (size_t)c->H * c->Gk * c->d, host, st))) return rc;
+    if ((rc = copy_out(c, q_centroids, c->qraw, 8 * (size_t)c->H * c->Gq * c->d, host, st))) return rc;
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_sparse_out(sparsepr_ctx* c, float* o_sparse, int32_t host, void* stream) {
+    int32_t rc = enter(c, kStageAttn);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = copy_out(c, o_sparse, c->o_s, 4 * (size_t)c->H * c->N * c->d, host, st))) return rc;
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_probes(sparsepr_ctx* c, float* x, float* y, int32_t host, void* stream) {
+    int32_t rc = enter(c, kStageAttn);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c->P > 0) {
+        if ((rc = copy_out(c, x, c->px, 4 * (size_t)c->H * c->P * c->d, host, st))) return rc;
+        if ((rc = copy_out(c, y, c->py, 4 * (size_t)c->H * c->P * c->d, host, st))) return rc;
+    }
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_fit(sparsepr_ctx* c, double* b_mat, double* b_vec, int32_t host, void* stream) {
+    int32_t rc = enter(c, kStageFit);
+    if (rc) return rc;
+    const size_t H = c->H, d = c->d;
+    if (host) {
+        if (b_mat) std::memcpy(b_mat, c->h_bm.data(), 8 * H * d * d);
+        if (b_vec) std::memcpy(b_vec, c->h_bv.data(), 8 * H * d);
+        return SPARSEPR_OK;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (b_mat) SPR_HIP(c, hipMemcpyAsync(b_mat, c->h_bm.data(), 8 * H * d * d, hipMemcpyHostToDevice, st));
+    if (b_vec) SPR_HIP(c, hipMemcpyAsync(b_vec, c->h_bv.data(), 8 * H * d, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_get_stats(sparsepr_ctx* c, sparsepr_stats* out) {
+    if (!c || !out) return SPARSEPR_ERR_INVALID_ARG;
+    int32_t rc = enter(c, 0);
+    if (rc) return rc;
+    std::memset(out, 0, sizeof(*out));
+    out->routed_k = c->k;
+    out->query_dims = c->Dq;
+    if (c->last_stream || c->stage > 0) SPR_HIP(c, hipStreamSynchronize(c->last_stream));
+    if (c->stage >= kStageRoute) {
+        std::vector<int64_t> pairs(c->H);
+        SPR_HIP(c, hipMemcpy(pairs.data(), c->pairs, 8 * (size_t)c->H, hipMemcpyDeviceToHost));
+        for (int64_t v : pairs) out->routed_pairs += v;
+        out->probe_pairs = (int64_t)c->P * c->N * c->H;
+        out->exec_density = (double)(out->routed_pairs + out->probe_pairs) /
+                            ((double)c->H * (double)c->N * (double)c->N);
+    }
+    if (c->stage >= kStagePartition) {
+        std::vector<int32_t> fl(2 * (size_t)c->T * c->H);
+        SPR_HIP(c, hipMemcpy(fl.data(), c->flag_cnt, 4 * fl.size(), hipMemcpyDeviceToHost));
+        for (int32_t v : fl) out->recheck_points += v;
+    }
+    if (c->timing) {
+        const int pairs_ev[6][2] = {{0, 1}, {2, 3}, {3, 4}, {4, 5}, {5, 6}, {6, 7}};
+        for (int i = 0; i < 6; ++i) {
+            float ms = 0.f;
+            if (c->ev_used[pairs_ev[i][0]] && c->ev_used[pairs_ev[i][1]] &&
+                hipEventElapsedTime(&ms, c->ev[pairs_ev[i][0]], c->ev[pairs_ev[i][1]]) == hipSuccess)
+                out->stage_ms[i] = ms;
+        }
+    }
+    return SPARSEPR_OK;
+}
+
+// ------------------------------------------------------------- host solves ---
+int32_t sparsepr_host_sym_eig_top(int32_t n, const double* a, int32_t r, double* lam, double* vec) {
+    if (n < 1 || n > 1024 || r < 0 || r > n || !a || (r > 0 && (!lam || !vec))) return SPARSEPR_ERR_INVALID_ARG;
+    return sym_eig_top(n, a, r, lam, vec) == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
+}
+
+int32_t sparsepr_host_key_projection(int32_t d, const double* m_k, int32_t r, double* w) {
+    if (d < 1 || d > 1024 || r < 1 || r > d || !m_k || !w) return SPARSEPR_ERR_INVALID_ARG;
+    return key_projection(d, m_k, r, w) == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
+}
+
+int32_t sparsepr_host_query_factor(int32_t d, int32_t g, const double* c, double* l, int32_t* dims) {
+    if (d < 1 || d > 1024 || g < 1 || !c || !l || !dims) return SPARSEPR_ERR_INVALID_ARG;
+    int dd = 0;
+    const int rc = query_factor(d, g, c, l, &dd);
+    *dims = dd;
+    return rc == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
+}
+
+int32_t sparsepr_host_probe_fit(int32_t p, int32_t d, const double* x, const double* y, double lambda,
+                                int32_t rank, double* b_mat, double* b_vec) {
+    if (p < 0 || d < 1 || d > 1024 || rank < 0 || rank > d || !(lambda >= 0.0) || !b_mat || !b_vec ||
+        (p > 0 && (!x || !y)))
+        return SPARSEPR_ERR_INVALID_ARG;
+    return probe_fit(p, d, x, y, lambda, rank, b_mat, b_vec) == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
+}
+
+}  // extern "C"

@@ -1,0 +1,23 @@
+// Host-side fp64 small dense solves (no GPU). Return 0 on success, < 0 on failure.
+#pragma once
+#include <cstdint>
+
+namespace spr {
+
+// Top-r eigenpairs of symmetric a [n][n]: lam[r] descending, vec [n][r] (columns).
+int sym_eig_top(int n, const double* a, int r, double* lam, double* vec);
+
+// Lower Cholesky factor l [n][n] of a; -1 if a is not numerically positive definite.
+int cholesky_lower(int n, const double* a, double* l);
+
+// W [d][r] = U_r diag(sqrt(max(lambda_r, 0))) for the metric m_k [d][d].
+int key_projection(int d, const double* m_k, int r, double* w);
+
+// L [d][dims] with L L^T = C^T C / d (see sparsepr_host_query_factor).
+int query_factor(int d, int g, const double* c, double* l, int* dims);
+
+// B' [d][d], b' [d] from X, Y [p][d].
+int probe_fit(int p, int d, const double* x, const double* y, double lambda, int rank,
+              double* b_mat, double* b_vec);
+
+}  // namespace spr

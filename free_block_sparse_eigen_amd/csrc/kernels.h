@@ -1,0 +1,76 @@
+// Launchers of the SparsePR HIP kernels (host-callable; all asynchronous on `st`).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "common.h"
+
+namespace spr {
+
+constexpr int kSortChunk = 1024;      // points per counting-sort block
+constexpr int kMaxGroups = 1024;      // G_k, G_q upper bound (LDS tables)
+constexpr int kAttnRows = 128;        // query rows per attention work unit
+constexpr int kKeyTile = 64;          // keys per attention tile
+constexpr int kProbeRows = 128;       // probe rows per probe work unit
+
+// ---- generic ----
+void launch_to_bf16(const float* in, bf16_t* out, size_t count, hipStream_t st);
+void launch_fill_i32(int32_t* p, int32_t value, size_t count, hipStream_t st);
+void launch_fill_i64(int64_t* p, int64_t value, size_t count, hipStream_t st);
+
+// ---- partition ----
+void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64_t a, double* mk,
+                   hipStream_t st);
+void launch_project(const bf16_t* x, int heads, int n, int d, const float* l32, int dout,
+                    const float* lfro, float* y, float* yerr, hipStream_t st);
+void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
+                           int groups, int64_t a, double* c64, float* c32, float* cnorm,
+                           hipStream_t st);
+void launch_assign(const float* y, const float* yerr, int heads, int n, int dim, const float* c32,
+                   const float* cnorm, int groups, int32_t* labels, int32_t* flag_count,
+                   int32_t* flag_list, hipStream_t st);
+void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
+                    const double* c64, int groups, const int32_t* flag_count,
+                    const int32_t* flag_list, int32_t* labels, hipStream_t st);
+void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, int32_t* blkhist,
+                          int32_t* blkoff, int32_t* sorted, int32_t* off, hipStream_t st);
+void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
+                        const int32_t* off, int groups, double* mean_raw, const double* l64,
+                        int dout, double* c64, float* c32, float* cnorm, hipStream_t st);
+
+// ---- route ----
+void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,
+                    hipStream_t st);
+void launch_fill_groups(const int32_t* off, int heads, int n, int groups, int32_t* grp,
+                        hipStream_t st);
+void launch_route(const double* cq, const double* ck, const int32_t* qoff, const int32_t* koff,
+                  int heads, int gq, int gk, int d, int k, int32_t* blocks, int32_t* ucount,
+                  int64_t* pairs, hipStream_t st);
+void launch_probes(const int32_t* qoff, const int32_t* qperm, int heads, int n, int gq, int probes,
+                   int32_t* probe_pos, int32_t* probe_orig, int32_t* probe_grp, int32_t* probe_of,
+                   hipStream_t st);
+void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int max_units,
+                  int2* units, int32_t* nunits, hipStream_t st);
+
+// ---- attention ----
+// out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index)
+void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+                 const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
+                 const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
+                 int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
+                 void* out, int out_mode, hipStream_t st);
+int probe_splits(int n);
+void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+                  const int32_t* probe_pos, const int32_t* probe_grp, int probes,
+                  const int32_t* kgrp, int gk, const int32_t* blocks, int gq, int kblk,
+                  float* part_ml, float* part_od, float* part_os, hipStream_t st);
+void launch_probe_merge(int heads, int probes, int d, int splits, const float* part_ml,
+                        const float* part_od, const float* part_os, float* x, float* y, float* od,
+                        hipStream_t st);
+
+// ---- correction ----
+void launch_correct(const float* o_s, const float* bmat, const float* bvec, const float* od,
+                    const int32_t* probe_of, const int32_t* qperm, int heads, int n, int d,
+                    int probes, void* o, int out_f32, hipStream_t st);
+
+}  // namespace spr

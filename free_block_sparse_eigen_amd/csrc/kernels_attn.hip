@@ -1,0 +1,560 @@
+// Variable-block-sparse attention and exact probe rows.
+//
+// "Partition the Support, Reconstruct the Residual" (gist.science summary), section 2C:
+// tokens are in contiguous group-major order and each query group attends only to the
+// union U_i of its routed key groups; the softmax is normalised over U_i alone (the
+// block-selection item of "Attention Sparsity is Input-Stable ... Online QK
+// Co-Clustering", papernotes.org). Unrouted key groups are never loaded or multiplied:
+// a work unit walks the routed segments only (the cloud.baidu.com explainer's point that
+// skipping, not computing-then-masking, is what saves work). Section 2B: probe rows get
+// the exact dense output and the routed-subset output from the same logits.
+//
+// Work unit = (head, query group, up to 128 query rows); 4 waves x 32 rows.
+//   S^T = K Q^T  : A = K tile from LDS (row-major), B = Q^T fragments held in VGPRs
+//   O^T += V^T P^T: A = V^T tile from LDS (transposed while staging), B = P^T straight
+//                   from the S^T accumulators (bf16, no cross-lane traffic)
+// Keys stream in 64-key tiles packed across the routed segments (only the last tile
+// of the union is partial), staged global -> VGPR -> LDS, double-buffered, one barrier
+// per tile. Softmax in fp32 base-2 with a lazily raised running max.
+#include "kernels.h"
+
+#include <cmath>
+
+namespace spr {
+
+namespace {
+
+constexpr int KT = kKeyTile;
+constexpr float kLazy = 8.0f;  // raise the running max only when a tile exceeds it by 2^8
+
+__device__ inline uint32_t word_of(const uint4& v, int w) {
+    return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+// 8 keys x 8 dims (one 16-byte chunk per key) -> 8 dims x 8 keys
+__device__ inline void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int we = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            o[p] = __builtin_amdgcn_perm(word_of(in[2 * p + 1], we), word_of(in[2 * p], we), sel);
+        out[e] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+__device__ inline uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Tile staging shared by both kernels: the K tile row-major (16-byte chunk c of row r at
+// c ^ (r & 7)), the V tile transposed: row = dim, 64 keys, where 16-key slice s holds its
+// keys in the order [0-3, 8-11, 4-7, 12-15] so that the 8 keys an MFMA lane half needs
+// are one 16-byte chunk; chunk index (2 s + half) ^ (dim & 7).
+template <int D>
+struct Tile {
+    static constexpr int CH = D / 8;
+    static constexpr int NV = 8 * CH;      // V items: (slice, half, chunk), 8 key rows each
+    static constexpr int NK = 256 - NV;    // threads staging K
+    static constexpr int KCH = KT * CH;
+
+    __device__ static void load(const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
+                                size_t head_row0, const int* __restrict__ phys, int tid,
+                                uint4 (&stg)[8]) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        if (tid < NV) {
+            const int s4 = tid / (2 * CH), hh = (tid / CH) & 1, c = tid % CH;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int kk = 16 * s4 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                const int r = phys[kk];
+                stg[i] = (r >= 0) ? ldg16(vp + (head_row0 + r) * D + c * 8) : z;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int ci = (tid - NV) + m * NK;
+                if (ci < KCH) {
+                    const int r = phys[ci / CH];
+                    stg[m] = (r >= 0) ? ldg16(kp + (head_row0 + r) * D + (ci % CH) * 8) : z;
+                }
+            }
+        }
+    }
+
+    __device__ static void store(uint4* __restrict__ sk, uint4* __restrict__ svt, int tid,
+                                 const uint4 (&stg)[8]) {
+        if (tid < NV) {
+            const int s4 = tid / (2 * CH), hh = (tid / CH) & 1, c = tid % CH;
+            uint4 t[8];
+            transpose8(stg, t);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int dim = c * 8 + e;
+                svt[dim * 8 + ((2 * s4 + hh) ^ (dim & 7))] = t[e];
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int ci = (tid - NV) + m * NK;
+                if (ci < KCH) {
+                    const int r = ci / CH, c = ci % CH;
+                    sk[r * CH + (c ^ (r & 7))] = stg[m];
+                }
+            }
+        }
+    }
+};
+
+// S^T block kb (32 keys x 32 queries) of the tile for this lane's query column.
+template <int D>
+__device__ inline f32x16 qk_block(const uint4* __restrict__ sk, const uint4 (&qf)[D / 16], int kb,
+                                  int lane) {
+    constexpr int CH = D / 8;
+    f32x16 s = {};
+    const int row = kb * 32 + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        const uint4 a = sk[row * CH + ((2 * kk + (lane >> 5)) ^ (lane & 7))];
+        s = mfma32x32x16(a, qf[kk], s);
+    }
+    return s;
+}
+
+// O^T[db] += V^T(dims of block db, 16 keys of slice s4) . P^T(slice s4)
+__device__ inline uint4 vt_frag(const uint4* __restrict__ svt, int db, int s4, int lane) {
+    const int dim = db * 32 + (lane & 31);
+    return svt[dim * 8 + ((2 * s4 + (lane >> 5)) ^ (dim & 7))];
+}
+
+__device__ inline float swap_halves_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+
+// Key tile -> physical rows: the smallest segment s with prefix[s+1] > u holds virtual key u.
+__device__ inline int segment_row(const int* __restrict__ pre, const int* __restrict__ start,
+                                  int nseg, int u) {
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid + 1] > u) hi = mid; else lo = mid + 1;
+    }
+    return start[lo] + (u - pre[lo]);
+}
+
+}  // namespace
+
+template <int D, int OUTM>
+__global__ __launch_bounds__(256, 2) void k_vbsa(
+    const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
+    int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
+    int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
+    const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
+    int nunits_stride, float scale_log2, void* __restrict__ out) {
+    using TL = Tile<D>;
+    constexpr int DB = D / 32;
+    __shared__ int s_pre[kMaxGroups + 1];
+    __shared__ int s_start[kMaxGroups];
+    __shared__ int s_phys[2][KT];
+    __shared__ uint4 s_k[2][TL::KCH];
+    __shared__ uint4 s_vt[2][D * 8];
+
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if ((int)blockIdx.x >= nunits[(size_t)h * nunits_stride]) return;
+    const int2 un = units[(size_t)h * units_head_stride + blockIdx.x];
+    const int gi = un.x, row0 = un.y;
+    const int32_t* qo = qoff + (size_t)h * qoff_stride;
+    const int rows = min(kAttnRows, qo[gi + 1] - row0);
+    const int32_t* ko = koff + (size_t)h * koff_stride;
+    const int32_t* bl = blocks + (size_t)h * blocks_head_stride + (size_t)gi * kblk;
+    const size_t head_row0 = (size_t)h * n;
+
+    for (int s = tid; s < kblk; s += 256) {
+        const int j = bl[s];
+        s_start[s] = (j >= 0) ? ko[j] : 0;
+        s_pre[s + 1] = (j >= 0) ? (ko[j + 1] - ko[j]) : 0;
+    }
+    if (tid == 0) s_pre[0] = 0;
+    __syncthreads();
+    if (tid == 0)
+        for (int s = 1; s <= kblk; ++s) s_pre[s] += s_pre[s - 1];
+    __syncthreads();
+    const int U = s_pre[kblk];
+    const int ntiles = (U + KT - 1) / KT;
+
+    auto fill_phys = [&](int t, int buf) {
+        if (tid < KT) {
+            const int u = t * KT + tid;
+            s_phys[buf][tid] = (u < U) ? segment_row(s_pre, s_start, kblk, u) : -1;
+        }
+    };
+
+    // Q^T fragments of this wave's 32 rows
+    const bool active = w * 32 < rows;
+    const int qrow = w * 32 + (lane & 31);
+    const bool qvalid = qrow < rows;
+    uint4 qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        qf[kk] = qvalid ? ldg16(qp + (head_row0 + row0 + qrow) * D + 16 * kk + 8 * (lane >> 5))
+                        : make_uint4(0, 0, 0, 0);
+
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    uint4 stg[8];
+    fill_phys(0, 0);
+    __syncthreads();
+    TL::load(kp, vp, head_row0, s_phys[0], tid, stg);
+    TL::store(s_k[0], s_vt[0], tid, stg);
+    if (ntiles > 1) fill_phys(1, 1);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) TL::load(kp, vp, head_row0, s_phys[buf ^ 1], tid, stg);
+        if (active) {
+            f32x16 s0 = qk_block<D>(s_k[buf], qf, 0, lane);
+            f32x16 s1 = qk_block<D>(s_k[buf], qf, 1, lane);
+            const int nvk = U - t * KT;
+            if (nvk < KT) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (key >= nvk) s0[r] = -INFINITY;
+                    if (key + 32 >= nvk) s1[r] = -INFINITY;
+                }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+            mx = swap_halves_max(mx);
+            const float mt = mx * scale_log2;
+            if (__ballot(mt > m_run + kLazy)) {
+                const float mnew = fmaxf(m_run, mt);
+                const float alpha = exp2f(m_run - mnew);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[db] *= alpha;
+                m_run = mnew;
+            }
+            const float mneg = -m_run;
+            uint4 pb[4];
+            const bf16x2_ones_t ones = ones_bf16x2();
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 8 * (sl & 1) + 2 * i;
+                    const float x0 = (sl < 2) ? s0[r] : s1[r];
+                    const float x1 = (sl < 2) ? s0[r + 1] : s1[r + 1];
+                    const float p0 = exp2f(fmaf(x0, scale_log2, mneg));
+                    const float p1 = exp2f(fmaf(x1, scale_log2, mneg));
+                    wv[i] = pack_bf16x2(p0, p1);
+                    l_run = dot2_bf16(wv[i], ones, l_run);
+                }
+                pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    o[db] = mfma32x32x16(vt_frag(s_vt[buf], db, sl, lane), pb[sl], o[db]);
+        }
+        if (more) {
+            TL::store(s_k[buf ^ 1], s_vt[buf ^ 1], tid, stg);
+            if (t + 2 < ntiles) fill_phys(t + 2, buf);
+        }
+        __syncthreads();
+    }
+
+    if (!active) return;
+    l_run += __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_run;
+    if (!qvalid) return;
+    const size_t orow = head_row0 + row0 + qrow;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int dim = db * 32 + 8 * g + 4 * (lane >> 5);
+            const float v0 = o[db][4 * g] * inv, v1 = o[db][4 * g + 1] * inv;
+            const float v2 = o[db][4 * g + 2] * inv, v3 = o[db][4 * g + 3] * inv;
+            if (OUTM == 0) {
+                *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * D + dim) =
+                    make_float4(v0, v1, v2, v3);
+            } else {
+                *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + orow * D + dim) =
+                    make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            }
+        }
+}
+
+void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+                 const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
+                 const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
+                 int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
+                 void* out, int out_mode, hipStream_t st) {
+    const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    dim3 grid(max_units, heads);
+#define SPR_VBSA(DD, MM)                                                                     \
+    hipLaunchKernelGGL((k_vbsa<DD, MM>), grid, dim3(256), 0, st, qp, kp, vp, n, qoff,        \
+                       qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units, \
+                       units_head_stride, nunits, nunits_stride, scale_log2, out)
+    if (d == 128) {
+        if (out_mode == 0) SPR_VBSA(128, 0); else SPR_VBSA(128, 1);
+    } else {
+        if (out_mode == 0) SPR_VBSA(64, 0); else SPR_VBSA(64, 1);
+    }
+#undef SPR_VBSA
+}
+
+// ------------------------------------------------------------------- probes ---
+// Work unit = (head, 128 probe rows, one key split). Both accumulators share the logits:
+// the dense one over every key, the routed one over keys whose group is routed for the
+// probe's query group. P.V uses a bf16 hi/lo split of P (about 2^-17 relative) so that
+// the probe outputs are near fp32 accuracy. Partial (max, sum, unnormalised O) per split.
+int probe_splits(int n) {
+    int s = (n + 4095) / 4096;
+    if (s < 1) s = 1;
+    if (s > 64) s = 64;
+    return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_probe(
+    const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
+    int n, const int32_t* __restrict__ probe_pos, const int32_t* __restrict__ probe_grp,
+    int probes, const int32_t* __restrict__ kgrp, int gk, const int32_t* __restrict__ blocks,
+    int gq, int kblk, int chunk, float scale_log2, float* __restrict__ part_ml,
+    float* __restrict__ part_od, float* __restrict__ part_os) {
+    using TL = Tile<D>;
+    constexpr int DB = D / 32;
+    __shared__ int s_phys[2][KT];
+    __shared__ int s_kg[2][KT];
+    __shared__ uint32_t s_bits[kProbeRows][kMaxGroups / 32];
+    __shared__ uint4 s_k[2][TL::KCH];
+    __shared__ uint4 s_vt[2][D * 8];
+
+    const int h = blockIdx.z, split = blockIdx.y, splits = gridDim.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int p0 = blockIdx.x * kProbeRows;
+    const int gw = (gk + 31) / 32;
+    const size_t head_row0 = (size_t)h * n;
+    for (int i = tid; i < kProbeRows * (kMaxGroups / 32); i += 256) (&s_bits[0][0])[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < kProbeRows * kblk; i += 256) {
+        const int lp = i / kblk, s = i % kblk;
+        const int p = p0 + lp;
+        if (p < probes) {
+            const int grp = probe_grp[(size_t)h * probes + p];
+            const int j = blocks[((size_t)h * gq + grp) * kblk + s];
+            if (j >= 0) atomicOr(&s_bits[lp][j >> 5], 1u << (j & 31));
+        }
+    }
+    const int k0 = split * chunk;
+    const int k1 = min(n, k0 + chunk);
+    const int nkeys = max(0, k1 - k0);
+    const int ntiles = (nkeys + KT - 1) / KT;
+    auto fill_phys = [&](int t, int buf) {
+        if (tid < KT) {
+            const int u = t * KT + tid;
+            const int r = (u < nkeys) ? k0 + u : -1;
+            s_phys[buf][tid] = r;
+            s_kg[buf][tid] = (r >= 0) ? kgrp[head_row0 + r] : 0;
+        }
+    };
+
+    const int lp = w * 32 + (lane & 31);
+    const int p = p0 + lp;
+    const bool pvalid = p < probes;
+    const bool active = p0 + w * 32 < probes;
+    uint4 qf[D / 16];
+    {
+        const int qrow = pvalid ? probe_pos[(size_t)h * probes + p] : 0;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = pvalid ? ldg16(qp + (head_row0 + qrow) * D + 16 * kk + 8 * (lane >> 5))
+                            : make_uint4(0, 0, 0, 0);
+    }
+    (void)gw;
+    f32x16 od[DB], os[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { od[db] = f32x16{}; os[db] = f32x16{}; }
+    float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
+
+    uint4 stg[8];
+    if (ntiles > 0) {
+        fill_phys(0, 0);
+        __syncthreads();
+        TL::load(kp, vp, head_row0, s_phys[0], tid, stg);
+        TL::store(s_k[0], s_vt[0], tid, stg);
+        if (ntiles > 1) fill_phys(1, 1);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) TL::load(kp, vp, head_row0, s_phys[buf ^ 1], tid, stg);
+        if (active) {
+            f32x16 sv[2];
+            sv[0] = qk_block<D>(s_k[buf], qf, 0, lane);
+            sv[1] = qk_block<D>(s_k[buf], qf, 1, lane);
+            const int nvk = nkeys - t * KT;
+            float xd[32], xs[32];
+            float mxd = -INFINITY, mxs = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    float x = sv[kb][r] * scale_log2;
+                    if (key >= nvk) x = -INFINITY;
+                    const int j = s_kg[buf][key];
+                    const bool routed = (s_bits[lp][j >> 5] >> (j & 31)) & 1u;
+                    xd[kb * 16 + r] = x;
+                    xs[kb * 16 + r] = routed ? x : -INFINITY;
+                    mxd = fmaxf(mxd, x);
+                    mxs = fmaxf(mxs, xs[kb * 16 + r]);
+                }
+            mxd = swap_halves_max(mxd);
+            mxs = swap_halves_max(mxs);
+            const float mdn = fmaxf(md, mxd), msn = fmaxf(ms, mxs);
+            const float ad = (mdn == -INFINITY) ? 1.f : exp2f(md - mdn);
+            const float as = (msn == -INFINITY) ? 1.f : exp2f(ms - msn);
+            ld *= ad;
+            ls *= as;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) { od[db] *= ad; os[db] *= as; }
+            md = mdn;
+            ms = msn;
+            uint4 dh[4], dl[4], sh[4], sl4[4];
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                uint32_t a[4], b[4], c[4], e[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = 16 * (sl >> 1) + 8 * (sl & 1) + 2 * i;   // index into xd/xs
+                    float pd[2], ps[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        pd[u] = (md == -INFINITY) ? 0.f : exp2f(xd[k + u] - md);
+                        ps[u] = (ms == -INFINITY) ? 0.f : exp2f(xs[k + u] - ms);
+                        ld += pd[u];
+                        ls += ps[u];
+                    }
+                    a[i] = pack_bf16x2(pd[0], pd[1]);
+                    b[i] = pack_bf16x2(pd[0] - bf16_to_f32((bf16_t)(a[i] & 0xFFFF)),
+                                       pd[1] - bf16_to_f32((bf16_t)(a[i] >> 16)));
+                    c[i] = pack_bf16x2(ps[0], ps[1]);
+                    e[i] = pack_bf16x2(ps[0] - bf16_to_f32((bf16_t)(c[i] & 0xFFFF)),
+                                       ps[1] - bf16_to_f32((bf16_t)(c[i] >> 16)));
+                }
+                dh[sl] = make_uint4(a[0], a[1], a[2], a[3]);
+                dl[sl] = make_uint4(b[0], b[1], b[2], b[3]);
+                sh[sl] = make_uint4(c[0], c[1], c[2], c[3]);
+                sl4[sl] = make_uint4(e[0], e[1], e[2], e[3]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const uint4 a = vt_frag(s_vt[buf], db, sl, lane);
+                    od[db] = mfma32x32x16(a, dh[sl], od[db]);
+                    od[db] = mfma32x32x16(a, dl[sl], od[db]);
+                    os[db] = mfma32x32x16(a, sh[sl], os[db]);
+                    os[db] = mfma32x32x16(a, sl4[sl], os[db]);
+                }
+        }
+        if (more) {
+            TL::store(s_k[buf ^ 1], s_vt[buf ^ 1], tid, stg);
+            if (t + 2 < ntiles) fill_phys(t + 2, buf);
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+    ld += __shfl_xor(ld, 32, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (!pvalid) return;
+    const size_t base = ((size_t)h * splits + split) * probes + p;
+    if (lane < 32) {
+        float4* ml = reinterpret_cast<float4*>(part_ml) + base;
+        *ml = make_float4(md, ld, ms, ls);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int dim = db * 32 + 8 * g + 4 * (lane >> 5);
+            *reinterpret_cast<float4*>(part_od + base * D + dim) =
+                make_float4(od[db][4 * g], od[db][4 * g + 1], od[db][4 * g + 2], od[db][4 * g + 3]);
+            *reinterpret_cast<float4*>(part_os + base * D + dim) =
+                make_float4(os[db][4 * g], os[db][4 * g + 1], os[db][4 * g + 2], os[db][4 * g + 3]);
+        }
+}
+
+void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+                  const int32_t* probe_pos, const int32_t* probe_grp, int probes,
+                  const int32_t* kgrp, int gk, const int32_t* blocks, int gq, int kblk,
+                  float* part_ml, float* part_od, float* part_os, hipStream_t st) {
+    if (probes == 0) return;
+    const int splits = probe_splits(n);
+    int chunk = (n + splits - 1) / splits;
+    chunk = (chunk + KT - 1) / KT * KT;
+    const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    dim3 grid((probes + kProbeRows - 1) / kProbeRows, splits, heads);
+    if (d == 128)
+        hipLaunchKernelGGL(k_probe<128>, grid, dim3(256), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
+                           probes, kgrp, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
+                           part_os);
+    else
+        hipLaunchKernelGGL(k_probe<64>, grid, dim3(256), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
+                           probes, kgrp, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
+                           part_os);
+}
+
+// Merge the key splits of every probe row in split order; X = routed output,
+// Y = dense - routed, and the dense output itself.
+__global__ void k_probe_merge(int probes, int d, int splits, const float* __restrict__ part_ml,
+                              const float* __restrict__ part_od, const float* __restrict__ part_os,
+                              float* __restrict__ x, float* __restrict__ y,
+                              float* __restrict__ od) {
+    const int h = blockIdx.y, p = blockIdx.x, j = threadIdx.x;
+    if (j >= d) return;
+    const float4* ml = reinterpret_cast<const float4*>(part_ml);
+    float mdx = -INFINITY, msx = -INFINITY;
+    for (int s = 0; s < splits; ++s) {
+        const float4 v = ml[((size_t)h * splits + s) * probes + p];
+        mdx = fmaxf(mdx, v.x);
+        msx = fmaxf(msx, v.z);
+    }
+    float sd = 0.f, ss = 0.f, nd = 0.f, ns = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const size_t base = ((size_t)h * splits + s) * probes + p;
+        const float4 v = ml[base];
+        const float wd = (v.x == -INFINITY) ? 0.f : exp2f(v.x - mdx);
+        const float ws = (v.z == -INFINITY) ? 0.f : exp2f(v.z - msx);
+        sd += wd * v.y;
+        ss += ws * v.w;
+        nd += wd * part_od[base * d + j];
+        ns += ws * part_os[base * d + j];
+    }
+    const float vd = nd / sd, vs = ns / ss;
+    const size_t o = ((size_t)h * probes + p) * d + j;
+    x[o] = vs;
+    y[o] = vd - vs;
+    od[o] = vd;
+}
+
+void launch_probe_merge(int heads, int probes, int d, int splits, const float* part_ml,
+                        const float* part_od, const float* part_os, float* x, float* y, float* od,
+                        hipStream_t st) {
+    if (probes == 0) return;
+    hipLaunchKernelGGL(k_probe_merge, dim3(probes, heads), dim3(128), 0, st, probes, d, splits,
+                       part_ml, part_od, part_os, x, y, od);
+}
+
+}  // namespace spr

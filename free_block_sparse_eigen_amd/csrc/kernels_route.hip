@@ -1,0 +1,201 @@
+// Route-stage kernels.
+//  * permute: contiguous group-major layout of Q/K/V ("Partition the Support,
+//    Reconstruct the Residual", gist.science summary, section 2C), 16-byte row chunks
+//  * route: centroid-logit top-k key groups per query group (block selection of
+//    "Attention Sparsity is Input-Stable ... Online QK Co-Clustering", papernotes.org)
+//  * probes: stratified probe rows across query groups (section 2B)
+//  * units: query tiles of the attention kernel, one list per head
+#include "kernels.h"
+
+#include <cmath>
+
+namespace spr {
+
+__global__ __launch_bounds__(256) void k_permute(const bf16_t* __restrict__ src,
+                                                 const int32_t* __restrict__ perm, int n, int d,
+                                                 bf16_t* __restrict__ dst) {
+    const int h = blockIdx.y;
+    const int chunks = d / 8;
+    const size_t i = blockIdx.x * (size_t)256 + threadIdx.x;
+    if (i >= (size_t)n * chunks) return;
+    const int row = (int)(i / chunks), c = (int)(i % chunks);
+    const int from = perm[(size_t)h * n + row];
+    const uint4 v = *reinterpret_cast<const uint4*>(src + ((size_t)h * n + from) * d + c * 8);
+    *reinterpret_cast<uint4*>(dst + ((size_t)h * n + row) * d + c * 8) = v;
+}
+
+void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,
+                    hipStream_t st) {
+    const size_t total = (size_t)n * (d / 8);
+    hipLaunchKernelGGL(k_permute, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, st,
+                       src, perm, n, d, dst);
+}
+
+__global__ void k_fill_groups(const int32_t* __restrict__ off, int n, int groups,
+                              int32_t* __restrict__ grp) {
+    const int h = blockIdx.y, g = blockIdx.x;
+    const int32_t* oh = off + (size_t)h * (groups + 1);
+    for (int m = oh[g] + threadIdx.x; m < oh[g + 1]; m += blockDim.x) grp[(size_t)h * n + m] = g;
+}
+
+void launch_fill_groups(const int32_t* off, int heads, int n, int groups, int32_t* grp,
+                        hipStream_t st) {
+    hipLaunchKernelGGL(k_fill_groups, dim3(groups, heads), dim3(256), 0, st, off, n, groups, grp);
+}
+
+// Block per (query group, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64; key group j is
+// kept when it is non-empty and fewer than k non-empty groups rank above it by
+// (score descending, index ascending). Kept groups are written in ascending order.
+__global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
+                                               const double* __restrict__ ck,
+                                               const int32_t* __restrict__ qoff,
+                                               const int32_t* __restrict__ koff, int gq, int gk,
+                                               int d, int k, int32_t* __restrict__ blocks,
+                                               int32_t* __restrict__ ucount,
+                                               int64_t* __restrict__ pairs) {
+    __shared__ double cs[128];
+    __shared__ double sc[kMaxGroups];
+    __shared__ int ne[kMaxGroups];
+    __shared__ int sel[kMaxGroups];
+    const int h = blockIdx.y, i = blockIdx.x, tid = threadIdx.x;
+    const double* ci = cq + ((size_t)h * gq + i) * d;
+    for (int t = tid; t < d; t += 256) cs[t] = ci[t];
+    __syncthreads();
+    const int32_t* ko = koff + (size_t)h * (gk + 1);
+    const double rs = sqrt((double)d);
+    for (int j = tid; j < gk; j += 256) {
+        const double* cj = ck + ((size_t)h * gk + j) * d;
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) s += cs[t] * cj[t];
+        sc[j] = s / rs;
+        ne[j] = (ko[j + 1] > ko[j]) ? 1 : 0;
+    }
+    __syncthreads();
+    for (int j = tid; j < gk; j += 256) {
+        int rank = 0;
+        const double sj = sc[j];
+        for (int t = 0; t < gk; ++t)
+            rank += (ne[t] && (sc[t] > sj || (sc[t] == sj && t < j))) ? 1 : 0;
+        sel[j] = (ne[j] && rank < k) ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int32_t* out = blocks + ((size_t)h * gq + i) * k;
+        int pos = 0;
+        int64_t u = 0;
+        for (int j = 0; j < gk; ++j)
+            if (sel[j]) {
+                out[pos++] = j;
+                u += ko[j + 1] - ko[j];
+            }
+        for (; pos < k; ++pos) out[pos] = -1;
+        ucount[(size_t)h * gq + i] = (int32_t)u;
+        const int32_t* qo = qoff + (size_t)h * (gq + 1);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&pairs[h]),
+                  (unsigned long long)(u * (int64_t)(qo[i + 1] - qo[i])));
+    }
+}
+
+void launch_route(const double* cq, const double* ck, const int32_t* qoff, const int32_t* koff,
+                  int heads, int gq, int gk, int d, int k, int32_t* blocks, int32_t* ucount,
+                  int64_t* pairs, hipStream_t st) {
+    hipLaunchKernelGGL(k_route, dim3(gq, heads), dim3(256), 0, st, cq, ck, qoff, koff, gq, gk, d, k,
+                       blocks, ucount, pairs);
+}
+
+// Block per head. m_i = floor(P n_i / N); the leftover P - sum m_i go one each to the
+// groups of largest remainder (P n_i mod N), lower index first; the probes of group i
+// sit at ranks floor((2t + 1) n_i / (2 m_i)), t < m_i.
+__global__ __launch_bounds__(1024) void k_probes(const int32_t* __restrict__ qoff,
+                                                 const int32_t* __restrict__ qperm, int n, int gq,
+                                                 int probes, int32_t* __restrict__ probe_pos,
+                                                 int32_t* __restrict__ probe_orig,
+                                                 int32_t* __restrict__ probe_grp,
+                                                 int32_t* __restrict__ probe_of) {
+    __shared__ int64_t rem[kMaxGroups];
+    __shared__ int m[kMaxGroups];
+    __shared__ int base[kMaxGroups];
+    __shared__ int left;
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int32_t* qo = qoff + (size_t)h * (gq + 1);
+    if (probes == 0) return;
+    for (int i = tid; i < gq; i += 1024) {
+        const int64_t ni = qo[i + 1] - qo[i];
+        m[i] = (int)((probes * ni) / n);
+        rem[i] = (probes * ni) % n;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int s = 0;
+        for (int i = 0; i < gq; ++i) s += m[i];
+        left = probes - s;
+    }
+    __syncthreads();
+    for (int i = tid; i < gq; i += 1024) {
+        int rank = 0;
+        const int64_t ri = rem[i];
+        for (int t = 0; t < gq; ++t) rank += (rem[t] > ri || (rem[t] == ri && t < i)) ? 1 : 0;
+        if (rank < left) m[i] += 1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < gq; ++i) {
+            base[i] = run;
+            run += m[i];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < gq; i += 1024) {
+        const int64_t ni = qo[i + 1] - qo[i];
+        const int mi = m[i];
+        for (int t = 0; t < mi; ++t) {
+            const int pos = qo[i] + (int)(((2 * (int64_t)t + 1) * ni) / (2 * (int64_t)mi));
+            const int idx = base[i] + t;
+            probe_pos[(size_t)h * probes + idx] = pos;
+            probe_orig[(size_t)h * probes + idx] = qperm[(size_t)h * n + pos];
+            probe_grp[(size_t)h * probes + idx] = i;
+            probe_of[(size_t)h * n + pos] = idx;
+        }
+    }
+}
+
+void launch_probes(const int32_t* qoff, const int32_t* qperm, int heads, int n, int gq, int probes,
+                   int32_t* probe_pos, int32_t* probe_orig, int32_t* probe_grp, int32_t* probe_of,
+                   hipStream_t st) {
+    hipLaunchKernelGGL(k_probes, dim3(heads), dim3(1024), 0, st, qoff, qperm, n, gq, probes,
+                       probe_pos, probe_orig, probe_grp, probe_of);
+}
+
+// Block per head: query tiles of `rows_per_unit` rows inside each query group.
+__global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff, int gq,
+                                                int rows_per_unit, int max_units,
+                                                int2* __restrict__ units,
+                                                int32_t* __restrict__ nunits) {
+    __shared__ int base[kMaxGroups + 1];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int32_t* qo = qoff + (size_t)h * (gq + 1);
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < gq; ++i) {
+            base[i] = run;
+            run += (qo[i + 1] - qo[i] + rows_per_unit - 1) / rows_per_unit;
+        }
+        base[gq] = run;
+        nunits[h] = run;
+    }
+    __syncthreads();
+    for (int i = tid; i < gq; i += 1024) {
+        const int t_i = base[i + 1] - base[i];
+        for (int t = 0; t < t_i; ++t)
+            units[(size_t)h * max_units + base[i] + t] = make_int2(i, qo[i] + t * rows_per_unit);
+    }
+}
+
+void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int max_units,
+                  int2* units, int32_t* nunits, hipStream_t st) {
+    hipLaunchKernelGGL(k_units, dim3(heads), dim3(1024), 0, st, qoff, gq, rows_per_unit, max_units,
+                       units, nunits);
+}
+
+}  // namespace spr

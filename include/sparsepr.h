@@ -1,0 +1,212 @@
+/*
+ * sparsepr.h -- C ABI of the SparsePR attention-call hot path on MI355X (gfx950).
+ *
+ * One call computes, per head, an approximation of softmax(Q K^T / sqrt(d)) V
+ * (the attention formula of the framerc.cn post "SparsePR稀疏注意力：无训练加速
+ * 视频生成与世界模型推理", section 1.2) in five stages, following the method
+ * summary "Partition the Support, Reconstruct the Residual: Training-Free Sparse
+ * Attention for Video Generation and World Models" (gist.science), section 2:
+ *
+ *   sparsepr_partition   2A  response-coupled partition (keys by k-means in the
+ *                            eigen-coordinates of M_K = Q_s^T Q_s / M_s, then queries
+ *                            by k-means of their logit profile on the key-group centroids)
+ *   sparsepr_route       2C  group-major layout of Q/K/V; centroid-logit top-k key groups
+ *                            per query group (the block selection of "Attention Sparsity
+ *                            is Input-Stable ... Online QK Co-Clustering", papernotes.org);
+ *                        2B  stratified probe rows
+ *   sparsepr_sparse_attn 2C  variable-block-sparse attention over the routed pairs, and
+ *                        2B  exact dense attention of the probe rows
+ *   sparsepr_probe_fit   2B  ridge affine fit R ~ b + x B of the probe residuals, restricted
+ *                            to the leading right singular subspace of the residuals
+ *   sparsepr_correct     2B  fitted residual added to the unprobed rows; original order
+ *
+ * Conventions for every entry point
+ *   - Q, K, V and O are [heads][n][d] row-major, contiguous, 16-byte aligned device
+ *     buffers of the context's dtype (bf16, or fp32 holding any values: fp32 inputs
+ *     are rounded to bf16, nearest-even, on entry; O is written in the same dtype).
+ *   - Device work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream). Entry points return once the work is enqueued, except where
+ *     noted: the partition and probe-fit stages solve small fp64 eigen/linear
+ *     systems on the host and synchronise `stream` to do so.
+ *   - The caller owns Q/K/V/O and keeps them alive until the stream work is done.
+ *     The context owns every intermediate; nothing is kept between calls except
+ *     what the inspection getters read back.
+ *   - Every function returns a sparsepr_status; nothing throws or aborts across the
+ *     ABI. Arguments are validated before anything is enqueued. A HIP error returns
+ *     SPARSEPR_ERR_HIP and poisons the context (destroy it). Stages must run in order
+ *     partition -> route -> sparse_attn -> probe_fit -> correct (else
+ *     SPARSEPR_ERR_ORDER). A context is bound to one device, is not thread-safe, and
+ *     overlapping calls on one context race.
+ *   - Results are bitwise deterministic for identical inputs and parameters.
+ */
+#ifndef SPARSEPR_H
+#define SPARSEPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sparsepr_ctx sparsepr_ctx;
+
+enum {
+    SPARSEPR_OK = 0,
+    SPARSEPR_ERR_INVALID_ARG = 1,   /* bad pointer or parameter value */
+    SPARSEPR_ERR_SHAPE = 2,         /* shape outside the supported range */
+    SPARSEPR_ERR_OOM = 3,           /* device or host allocation failed */
+    SPARSEPR_ERR_HIP = 4,           /* HIP runtime / launch error (context poisoned) */
+    SPARSEPR_ERR_ORDER = 5,         /* stage called before its prerequisite */
+    SPARSEPR_ERR_NUMERIC = 6        /* a small solve failed (non-finite input) */
+};
+
+enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
+
+/* flags */
+#define SPARSEPR_F_STAGE_TIMING 1u  /* record per-stage HIP events (sparsepr_get_stats) */
+
+typedef struct {
+    int32_t heads;          /* H >= 1 */
+    int32_t n;              /* tokens N, 1 .. 2^24 */
+    int32_t d;              /* head dim, 64 or 128 */
+    int32_t dtype;          /* SPARSEPR_BF16 or SPARSEPR_F32 (Q, K, V and O) */
+    int32_t n_sample;       /* M_s sampled queries for M_K, 1 .. n */
+    int32_t key_rank;       /* r_K leading eigenvectors of M_K, 1 .. d */
+    int32_t kv_groups;      /* G_k, 1 .. min(n, 1024) */
+    int32_t q_groups;       /* G_q, 1 .. min(n, 1024) */
+    int32_t kmeans_iters;   /* T >= 1 Lloyd rounds per k-means */
+    int32_t probes;         /* P probe rows per head, 0 .. min(n, 4096) */
+    int32_t corr_rank;      /* r, 0 .. d */
+    uint32_t flags;         /* SPARSEPR_F_* */
+    double density;         /* rho in (0, 1]: k = ceil(rho G_k - 1e-9) key groups per query group */
+    double ridge_lambda;    /* lambda >= 0 (absolute; 0 = minimum-norm least squares) */
+} sparsepr_params;
+
+typedef struct {
+    int64_t routed_pairs;      /* sum over heads and query rows of |U_i| */
+    int64_t probe_pairs;       /* P * N * H */
+    double  exec_density;      /* (routed_pairs + probe_pairs) / (H N^2) */
+    int64_t recheck_points;    /* k-means points resolved in fp64 after an uncertified fp32 margin */
+    int32_t routed_k;          /* key groups kept per query group */
+    int32_t query_dims;        /* dimension of the query k-means space */
+    float   stage_ms[6];       /* partition, route, sparse_attn(main), sparse_attn(probes), probe_fit, correct */
+} sparsepr_stats;
+
+/* ---- parameters and lifetime (host only; sparsepr_create allocates on the current device) ---- */
+
+/* Check a parameter set; no GPU work. Returns SPARSEPR_OK or the first violation. */
+int32_t sparsepr_validate(const sparsepr_params* p);
+
+/* Device bytes a context needs for these parameters (0 if invalid). */
+size_t sparsepr_workspace_bytes(const sparsepr_params* p);
+
+/* Validate and allocate a context on the current HIP device. *out is set only on success. */
+int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out);
+
+/* Free the context (synchronises its device first). NULL is ignored. */
+void sparsepr_destroy(sparsepr_ctx* ctx);
+
+/* Static text for a status code. */
+const char* sparsepr_status_str(int32_t status);
+
+/* Detail of the context's last error ("" if none). */
+const char* sparsepr_last_error(const sparsepr_ctx* ctx);
+
+/* ---- the five stages (section 2 of the method summary) ---- */
+
+/* 2A. Reads q, k. Host-synchronising (fp64 eigensolve of M_K; fp64 factor of the
+ * query metric C_K^T C_K / d). Leaves key/query labels and centroids in the context. */
+int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void* stream);
+
+/* 2C/2B. Reads q, k, v. Stable group-major permutation of Q/K/V, top-k key groups per
+ * query group (ties to the lower group index, empty key groups never kept), probe rows. */
+int32_t sparsepr_route(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
+                       void* stream);
+
+/* 2C/2B. Block-sparse attention over the routed pairs (unrouted blocks are never
+ * touched) and exact dense + routed attention of the probe rows. */
+int32_t sparsepr_sparse_attn(sparsepr_ctx* ctx, void* stream);
+
+/* 2B. Host-synchronising fp64 fit: B' = B Pi and b' = b Pi per head. */
+int32_t sparsepr_probe_fit(sparsepr_ctx* ctx, void* stream);
+
+/* 2B. Writes o [H][n][d] (context dtype) in the original token order: unprobed rows
+ * get O_s + b' + O_s B', probe rows their exact dense output. */
+int32_t sparsepr_correct(sparsepr_ctx* ctx, void* o, void* stream);
+
+/* ---- convenience and baseline ---- */
+
+/* All five stages in order. */
+int32_t sparsepr_attention(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
+                           void* o, void* stream);
+
+/* Dense softmax(Q K^T / sqrt(d)) V with this library's attention kernel (one group
+ * holding every key); uses the context's shapes and workspace, no other stage state. */
+int32_t sparsepr_dense_attn(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
+                            void* o, void* stream);
+
+/* ---- inspection (copy context-owned results out; NULL destinations are skipped).
+ * host != 0: destinations are host memory and `stream` is synchronised before return;
+ * host == 0: destinations are device memory, copies are enqueued on `stream`. ---- */
+
+/* int32 [H][n] labels and permutations (perm[new] = old), int32 [H][G+1] offsets. */
+int32_t sparsepr_get_partition(sparsepr_ctx* ctx, int32_t* key_labels, int32_t* q_labels,
+                               int32_t* key_perm, int32_t* q_perm, int32_t* key_off,
+                               int32_t* q_off, int32_t host, void* stream);
+
+/* blocks int32 [H][G_q][k] ascending, -1 padded; probe rows int32 [H][P] as original
+ * token indices and as group-major positions. */
+int32_t sparsepr_get_routing(sparsepr_ctx* ctx, int32_t* blocks, int32_t* probe_orig,
+                             int32_t* probe_pos, int32_t host, void* stream);
+
+/* Raw fp64 centroids: keys [H][G_k][d], queries [H][G_q][d] (zero for an empty group). */
+int32_t sparsepr_get_centroids(sparsepr_ctx* ctx, double* key_centroids, double* q_centroids,
+                               int32_t host, void* stream);
+
+/* fp32 [H][n][d] sparse output in group-major order (before correction). */
+int32_t sparsepr_get_sparse_out(sparsepr_ctx* ctx, float* o_sparse, int32_t host, void* stream);
+
+/* fp32 [H][P][d] probe sparse outputs X and residuals Y = O_dense - X. */
+int32_t sparsepr_get_probes(sparsepr_ctx* ctx, float* x, float* y, int32_t host, void* stream);
+
+/* fp64 B' [H][d][d] and b' [H][d]. */
+int32_t sparsepr_get_fit(sparsepr_ctx* ctx, double* b_mat, double* b_vec, int32_t host,
+                         void* stream);
+
+/* Counters of the last call (synchronises the context's last stream). */
+int32_t sparsepr_get_stats(sparsepr_ctx* ctx, sparsepr_stats* out);
+
+/* Test hook: replace the partition with given labels (int32 [H][n] each, values in
+ * [0, G); host != 0: host memory, else device memory) for the device inputs q, k;
+ * the raw group centroids and the group-major permutations are recomputed, and the
+ * context is then ready for sparsepr_route. Out-of-range labels: SPARSEPR_ERR_INVALID_ARG
+ * (checked only for host labels). */
+int32_t sparsepr_set_partition(sparsepr_ctx* ctx, const void* q, const void* k,
+                               const int32_t* key_labels, const int32_t* q_labels, int32_t host,
+                               void* stream);
+
+/* ---- host-side fp64 solves used by the partition and probe-fit stages (no GPU) ---- */
+
+/* Top-r eigenpairs of a symmetric n x n matrix a (row-major, n <= 1024): eigenvalues
+ * descending into lam[r], eigenvectors as columns of vec [n][r]. */
+int32_t sparsepr_host_sym_eig_top(int32_t n, const double* a, int32_t r, double* lam,
+                                  double* vec);
+
+/* Key projection W = U_r diag(sqrt(max(lambda_r, 0))) [d][r] of the metric m_k [d][d]. */
+int32_t sparsepr_host_key_projection(int32_t d, const double* m_k, int32_t r, double* w);
+
+/* Factor L [d][dims] with L L^T = C^T C / d for key centroids c [g][d]: Cholesky if
+ * g > d and the metric is positive definite, else the profile map C^T / sqrt(d)
+ * (dims = g, needs g <= d) or an eigen factor (dims = d). Returns dims in *dims. */
+int32_t sparsepr_host_query_factor(int32_t d, int32_t g, const double* c, double* l,
+                                   int32_t* dims);
+
+/* Probe fit from X, Y [p][d] (fp64): B' [d][d], b' [d]. */
+int32_t sparsepr_host_probe_fit(int32_t p, int32_t d, const double* x, const double* y,
+                                double lambda, int32_t rank, double* b_mat, double* b_vec);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEPR_H */

@@ -1,0 +1,160 @@
+"""CPU tests of the C ABI: exported symbols, parameter validation, and the host-side
+fp64 solves (checked against numpy and the oracle). No GPU calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import free_block_sparse_eigen_amd as spr
+import oracle as orc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sparsepr.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsepr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(spr.lib, n), n
+    assert sorted(spr.EXPORTS) == names
+
+
+def _params(**kw):
+    base = dict(heads=2, n=2048, d=64, dtype=spr.F32, kv_groups=16, q_groups=16, density=0.25,
+                probes=64, corr_rank=8)
+    base.update(kw)
+    return spr.make_params(**base)
+
+
+def test_validation_accepts_configs_and_rejects_bad_values():
+    assert spr.sparsepr_validate(_params()) == 0
+    assert spr.sparsepr_workspace_bytes(_params()) > 0
+    bad = [dict(d=96), dict(n=0), dict(heads=0), dict(kv_groups=0), dict(kv_groups=2049),
+           dict(q_groups=1025, n=4096), dict(density=0.0), dict(density=1.5), dict(probes=-1),
+           dict(probes=4097, n=8192), dict(corr_rank=65), dict(ridge_lambda=-1.0),
+           dict(ridge_lambda=float("nan")), dict(kmeans_iters=0), dict(key_rank=0),
+           dict(key_rank=65), dict(n_sample=0), dict(dtype=7), dict(flags=8)]
+    for kw in bad:
+        p = _params(**kw)
+        if "n_sample" in kw:
+            p.n_sample = kw["n_sample"]
+        assert spr.sparsepr_validate(p) != 0, kw
+        assert spr.sparsepr_workspace_bytes(p) == 0, kw
+
+
+def test_status_strings():
+    for s in range(7):
+        assert spr.lib.sparsepr_status_str(s).decode()
+    assert spr.lib.sparsepr_last_error(None).decode() == ""
+
+
+def test_null_context_is_rejected_without_gpu():
+    assert spr.lib.sparsepr_sparse_attn(None, None) == 1
+    assert spr.lib.sparsepr_probe_fit(None, None) == 1
+    s = spr.Stats()
+    assert spr.lib.sparsepr_get_stats(None, ctypes.byref(s)) == 1
+
+
+# --------------------------------------------------------------- host solves ---
+@pytest.mark.parametrize("n,r,seed", [(1, 1, 0), (2, 2, 1), (7, 3, 2), (64, 16, 3),
+                                      (128, 32, 4), (128, 128, 5)])
+def test_sym_eig_top_matches_numpy(n, r, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((n, n))
+    a = a @ a.T / n
+    lam, vec = spr.sparsepr_host_sym_eig_top(a, r)
+    ref = np.linalg.eigvalsh(a)[::-1][:r]
+    assert np.allclose(lam, ref, rtol=1e-12, atol=1e-13 * abs(ref[0]))
+    assert np.allclose(a @ vec, vec * lam, atol=1e-10 * abs(ref[0]))
+    assert np.allclose(vec.T @ vec, np.eye(r), atol=1e-10)
+
+
+def test_sym_eig_top_clustered_and_deficient():
+    rng = np.random.default_rng(7)
+    u, _ = np.linalg.qr(rng.standard_normal((40, 40)))
+    lam = np.concatenate([[5.0, 5.0, 5.0, 3.0, 3.0 + 1e-12], np.zeros(35)])
+    a = u @ np.diag(lam) @ u.T
+    got, vec = spr.sparsepr_host_sym_eig_top(a, 5)
+    assert np.allclose(got, lam[:5], atol=1e-12)
+    assert np.allclose(vec.T @ vec, np.eye(5), atol=1e-9)
+    proj = vec[:, :3] @ vec[:, :3].T
+    assert np.allclose(proj, u[:, :3] @ u[:, :3].T, atol=1e-9)
+
+
+def test_sym_eig_top_zero_matrix():
+    lam, vec = spr.sparsepr_host_sym_eig_top(np.zeros((5, 5)), 2)
+    assert np.all(lam == 0) and np.allclose(vec.T @ vec, np.eye(2))
+
+
+def test_key_projection_matches_oracle_metric_distances():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((300, 64))
+    mk = orc.key_metric(q, 128)
+    w = spr.sparsepr_host_key_projection(mk, 16)
+    w_ref, _ = orc.key_projection(mk, 16)
+    # columns may differ by sign; W W^T is unique
+    assert np.allclose(w @ w.T, w_ref @ w_ref.T, atol=1e-11)
+
+
+@pytest.mark.parametrize("g,d", [(16, 64), (256, 128), (40, 16)])
+def test_query_factor_gives_the_profile_metric(g, d):
+    rng = np.random.default_rng(9)
+    c = rng.standard_normal((g, d))
+    l = spr.sparsepr_host_query_factor(c)
+    assert l.shape == (d, min(g, d) if g <= d else d)
+    assert np.allclose(l @ l.T, c.T @ c / d, atol=1e-11)
+
+
+def test_query_factor_semidefinite_falls_back_to_eigen_factor():
+    rng = np.random.default_rng(10)
+    c = np.zeros((40, 16))
+    c[:5] = rng.standard_normal((5, 16))             # rank 5 < d: Cholesky fails
+    l = spr.sparsepr_host_query_factor(c)
+    assert l.shape == (16, 16)
+    assert np.allclose(l @ l.T, c.T @ c / 16, atol=1e-11)
+
+
+@pytest.mark.parametrize("p,d,lam,r", [(64, 64, 1e-3, 8), (256, 128, 1e-3, 16), (300, 32, 0.5, 4),
+                                       (1, 16, 1e-3, 4), (10, 16, 1e-3, 16)])
+def test_probe_fit_matches_oracle(p, d, lam, r):
+    rng = np.random.default_rng(11 + p)
+    x = rng.standard_normal((p, d))
+    y = 0.1 * rng.standard_normal((p, d)) + 0.05 * x @ rng.standard_normal((d, d))
+    bm, bv = spr.sparsepr_host_probe_fit(x, y, lam, r)
+    rbm, rbv = orc.probe_fit(x, y, lam, r)
+    scale = max(1.0, np.abs(rbm).max())
+    assert np.allclose(bm, rbm, atol=1e-9 * scale) and np.allclose(bv, rbv, atol=1e-9 * scale)
+
+
+def test_probe_fit_zero_residual_and_no_probes():
+    x = np.random.default_rng(12).standard_normal((50, 8))
+    bm, bv = spr.sparsepr_host_probe_fit(x, np.zeros((50, 8)), 1e-3, 4)
+    assert np.all(bm == 0) and np.all(bv == 0)
+    bm, bv = spr.sparsepr_host_probe_fit(np.zeros((0, 8)), np.zeros((0, 8)), 1e-3, 4)
+    assert np.all(bm == 0) and np.all(bv == 0)
+
+
+def test_probe_fit_exact_low_rank_residual():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((80, 12))
+    y = rng.standard_normal((80, 3)) @ rng.standard_normal((3, 12))
+    bm, bv = spr.sparsepr_host_probe_fit(x, y, 1e-6, 8)
+    rbm, rbv = orc.probe_fit(x, y, 1e-6, 8)
+    assert np.allclose(bm, rbm, atol=1e-8) and np.allclose(bv, rbv, atol=1e-8)
+
+
+def test_probe_fit_min_norm_least_squares():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((40, 6))
+    y = rng.standard_normal((40, 6))
+    bm, bv = spr.sparsepr_host_probe_fit(x, y, 0.0, 6)
+    rbm, rbv = orc.probe_fit(x, y, 0.0, 6)
+    assert np.allclose(bm, rbm, atol=1e-9) and np.allclose(bv, rbv, atol=1e-9)
