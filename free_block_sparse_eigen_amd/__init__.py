@@ -58,7 +58,7 @@ class Stats(ctypes.Structure):
     _fields_ = [("routed_pairs", ctypes.c_int64), ("probe_pairs", ctypes.c_int64),
                 ("exec_density", ctypes.c_double), ("recheck_points", ctypes.c_int64),
                 ("routed_k", ctypes.c_int32), ("query_dims", ctypes.c_int32),
-                ("stage_ms", ctypes.c_float * 6)]
+                ("stage_ms", ctypes.c_float * 6), ("timed_calls", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -304,4 +304,4 @@ class SparsePR:
         return {"routed_pairs": s.routed_pairs, "probe_pairs": s.probe_pairs,
                 "exec_density": s.exec_density, "recheck_points": s.recheck_points,
                 "routed_k": s.routed_k, "query_dims": s.query_dims,
-                "stage_ms": list(s.stage_ms)}
+                "stage_ms": list(s.stage_ms), "timed_calls": s.timed_calls}

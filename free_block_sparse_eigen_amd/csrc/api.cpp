@@ -61,8 +61,12 @@ struct sparsepr_ctx {
     std::string err;
     hipStream_t last_stream = nullptr;
     bool timing = false;
-    hipEvent_t ev[8] = {};
-    bool ev_used[8] = {};
+    static constexpr int kRing = 64;   // per-call stage events kept for averaging
+    hipEvent_t ev[kRing][8] = {};
+    bool ev_used[kRing][8] = {};
+    int64_t calls = 0;
+    int64_t stats_from = 0;            // first call averaged by the next sparsepr_get_stats
+    int slot = 0;
 };
 
 namespace {
@@ -240,11 +244,16 @@ int32_t enter(sparsepr_ctx* c, int need_stage) {
     return SPARSEPR_OK;
 }
 
-void mark(sparsepr_ctx* c, int slot, hipStream_t st) {
-    if (c->timing) {
-        hipEventRecord(c->ev[slot], st);
-        c->ev_used[slot] = true;
-    }
+void mark(sparsepr_ctx* c, int point, hipStream_t st) {
+    if (c->timing && hipEventRecord(c->ev[c->slot][point], st) == hipSuccess)
+        c->ev_used[c->slot][point] = true;
+}
+
+// A new call starts at the partition stage: take the next ring slot.
+void begin_call(sparsepr_ctx* c) {
+    c->slot = static_cast<int>(c->calls % sparsepr_ctx::kRing);
+    ++c->calls;
+    for (bool& u : c->ev_used[c->slot]) u = false;
 }
 
 // bf16 view of an input tensor (converted into the workspace when the dtype is fp32)
@@ -369,7 +378,9 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     b.base = static_cast<char*>(c->arena);
     layout(*c, b);
     if (c->timing)
-        for (auto& e : c->ev) hipEventCreate(&e);
+        for (auto& row : c->ev)
+            for (auto& e : row)
+                if (hipEventCreate(&e) != hipSuccess) e = nullptr;
     // dense baseline metadata
     const int meta[8] = {0, c->N, 0, c->N, 0, c->dense_units, 0, 0};
     if (hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice) != hipSuccess) {
@@ -388,12 +399,13 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
 
 void sparsepr_destroy(sparsepr_ctx* c) {
     if (!c) return;
-    hipSetDevice(c->device);
-    hipDeviceSynchronize();
+    (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
     if (c->timing)
-        for (auto& e : c->ev)
-            if (e) hipEventDestroy(e);
-    if (c->arena) hipFree(c->arena);
+        for (auto& row : c->ev)
+            for (auto& e : row)
+                if (e) (void)hipEventDestroy(e);
+    if (c->arena) (void)hipFree(c->arena);
     delete c;
 }
 
@@ -404,6 +416,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
     c->stage = 0;
+    begin_call(c);
     mark(c, 0, st);
     const size_t H = c->H, d = c->d, rK = c->rK;
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
@@ -722,13 +735,25 @@ int32_t sparsepr_get_stats(sparsepr_ctx* c, sparsepr_stats* out) {
         for (int32_t v : fl) out->recheck_points += v;
     }
     if (c->timing) {
+        // average over the calls since the previous sparsepr_get_stats that the ring still holds
         const int pairs_ev[6][2] = {{0, 1}, {2, 3}, {3, 4}, {4, 5}, {5, 6}, {6, 7}};
+        const int64_t first = std::max(c->stats_from, c->calls - sparsepr_ctx::kRing);
         for (int i = 0; i < 6; ++i) {
-            float ms = 0.f;
-            if (c->ev_used[pairs_ev[i][0]] && c->ev_used[pairs_ev[i][1]] &&
-                hipEventElapsedTime(&ms, c->ev[pairs_ev[i][0]], c->ev[pairs_ev[i][1]]) == hipSuccess)
-                out->stage_ms[i] = ms;
+            double sum = 0.0;
+            int cnt = 0;
+            for (int64_t call = first; call < c->calls; ++call) {
+                const int s = (int)(call % sparsepr_ctx::kRing);
+                float ms = 0.f;
+                if (c->ev_used[s][pairs_ev[i][0]] && c->ev_used[s][pairs_ev[i][1]] &&
+                    hipEventElapsedTime(&ms, c->ev[s][pairs_ev[i][0]], c->ev[s][pairs_ev[i][1]]) == hipSuccess) {
+                    sum += ms;
+                    ++cnt;
+                }
+            }
+            out->stage_ms[i] = cnt ? (float)(sum / cnt) : 0.f;
+            if (i == 2) out->timed_calls = cnt;
         }
+        c->stats_from = c->calls;
     }
     return SPARSEPR_OK;
 }

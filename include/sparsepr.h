@@ -90,7 +90,11 @@ typedef struct {
     int64_t recheck_points;    /* k-means points resolved in fp64 after an uncertified fp32 margin */
     int32_t routed_k;          /* key groups kept per query group */
     int32_t query_dims;        /* dimension of the query k-means space */
-    float   stage_ms[6];       /* partition, route, sparse_attn(main), sparse_attn(probes), probe_fit, correct */
+    float   stage_ms[6];       /* mean ms per call of: partition, route, sparse attention kernel,
+                                  probe rows, probe fit, correction (SPARSEPR_F_STAGE_TIMING;
+                                  averaged over the calls since the previous
+                                  sparsepr_get_stats, at most the last 64) */
+    int32_t timed_calls;       /* calls averaged into stage_ms */
 } sparsepr_stats;
 
 /* ---- parameters and lifetime (host only; sparsepr_create allocates on the current device) ---- */
@@ -174,7 +178,8 @@ int32_t sparsepr_get_probes(sparsepr_ctx* ctx, float* x, float* y, int32_t host,
 int32_t sparsepr_get_fit(sparsepr_ctx* ctx, double* b_mat, double* b_vec, int32_t host,
                          void* stream);
 
-/* Counters of the last call (synchronises the context's last stream). */
+/* Counters of the last call and mean stage times since the previous call of this
+ * function (synchronises the context's last stream). */
 int32_t sparsepr_get_stats(sparsepr_ctx* ctx, sparsepr_stats* out);
 
 /* Test hook: replace the partition with given labels (int32 [H][n] each, values in
