@@ -32,14 +32,13 @@ struct sparsepr_ctx {
     bf16_t *qb = nullptr, *kb = nullptr, *vb = nullptr;
     bf16_t *qp = nullptr, *kp = nullptr, *vp = nullptr;
     // partition
-    float *z = nullptr, *zerr = nullptr, *yq = nullptr, *yerr = nullptr;
     int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
     int32_t *koff = nullptr, *qoff = nullptr, *kgrp = nullptr;
     int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
     double *mk = nullptr, *w64 = nullptr, *l64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
     double *kraw = nullptr, *qraw = nullptr;
-    float *w32 = nullptr, *l32 = nullptr, *wfro = nullptr, *lfro = nullptr;
-    float *kc32 = nullptr, *qc32 = nullptr, *kcn = nullptr, *qcn = nullptr;
+    bf16_t *kcp = nullptr, *qcp = nullptr;               // screening vectors, bf16 hi/lo
+    float *kcn2 = nullptr, *qcn2 = nullptr, *kcpn = nullptr, *qcpn = nullptr;
     // route
     int32_t *blocks = nullptr, *ucount = nullptr, *probe_pos = nullptr, *probe_orig = nullptr;
     int32_t *probe_grp = nullptr, *probe_of = nullptr, *nunits = nullptr;
@@ -48,13 +47,15 @@ struct sparsepr_ctx {
     // attention, probes, fit
     float *o_s = nullptr, *part_ml = nullptr, *part_od = nullptr, *part_os = nullptr;
     float *px = nullptr, *py = nullptr, *pod = nullptr, *bm32 = nullptr, *bv32 = nullptr;
+    double *fit_m = nullptr, *fit_g = nullptr;   // [H][2][d] means, [H][3][d][d] Grams
+    double* mq = nullptr;                        // [H][d][d] query metric C_K^T C_K / d
     // dense baseline: one query group and one key group holding every token
     int32_t *dense_meta = nullptr;     // qoff {0,N}, koff {0,N}, blocks {0}, nunits {..}
     int2* dense_unit_list = nullptr;
 
     // host mirrors
-    std::vector<double> h_mk, h_w64, h_kraw, h_l64, h_bm, h_bv;
-    std::vector<float> h_w32, h_wfro, h_l32, h_lfro, h_x, h_y, h_bm32, h_bv32;
+    std::vector<double> h_mk, h_w64, h_kraw, h_l64, h_bm, h_bv, h_fit_m, h_fit_g, h_mq;
+    std::vector<float> h_x, h_y, h_bm32, h_bv32;
 
     int stage = 0;
     bool poisoned = false;
@@ -147,10 +148,6 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.qp, HND);
     a.take(c.kp, HND);
     a.take(c.vp, HND);
-    a.take(c.z, HN * c.rK);
-    a.take(c.zerr, HN);
-    a.take(c.yq, HN * c.Dq);
-    a.take(c.yerr, HN);
     a.take(c.klab, HN);
     a.take(c.qlab, HN);
     a.take(c.kperm, HN);
@@ -169,14 +166,12 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.qc64, H * c.Gq * c.Dq);
     a.take(c.kraw, H * c.Gk * d);
     a.take(c.qraw, H * c.Gq * d);
-    a.take(c.w32, H * d * c.rK);
-    a.take(c.l32, H * d * c.Dq);
-    a.take(c.wfro, H);
-    a.take(c.lfro, H);
-    a.take(c.kc32, H * c.Gk * c.rK);
-    a.take(c.qc32, H * c.Gq * c.Dq);
-    a.take(c.kcn, H * c.Gk);
-    a.take(c.qcn, H * c.Gq);
+    a.take(c.kcp, H * 2 * c.Gk * d);
+    a.take(c.qcp, H * 2 * c.Gq * d);
+    a.take(c.kcn2, H * c.Gk);
+    a.take(c.qcn2, H * c.Gq);
+    a.take(c.kcpn, H * c.Gk);
+    a.take(c.qcpn, H * c.Gq);
     a.take(c.blocks, H * c.Gq * c.k);
     a.take(c.ucount, H * c.Gq);
     a.take(c.probe_pos, H * P);
@@ -193,6 +188,9 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.px, H * P * d);
     a.take(c.py, H * P * d);
     a.take(c.pod, H * P * d);
+    a.take(c.fit_m, H * 2 * d);
+    a.take(c.fit_g, H * 3 * d * d);
+    a.take(c.mq, H * d * d);
     a.take(c.bm32, H * d * d);
     a.take(c.bv32, H * d);
     a.take(c.dense_meta, 8);
@@ -265,61 +263,61 @@ const bf16_t* as_bf16(sparsepr_ctx* c, const void* x, bf16_t* scratch, hipStream
 
 bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
 
-// Lloyd rounds on the device: assign (fp32, certified) -> fp64 recheck -> counting sort
-// -> fp64 means and projected centroids. After the last round `sorted`/`off` are the
+// Lloyd rounds on the device: assign (MFMA screening, certified) -> fp64 recheck ->
+// counting sort -> fp64 means and centroids. After the last round `sorted`/`off` are the
 // stable group-major permutation and `mean_raw` the raw group means (zero if empty).
-int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, const float* y, const float* yerr, int dim,
-              const double* l64, int groups, int32_t* labels, int32_t* flags, int32_t* sorted,
-              int32_t* off, double* mean_raw, double* c64, float* c32, float* cnorm,
-              hipStream_t st) {
-    launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, c64, c32, cnorm, st);
+int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, int dim, const double* l64, int groups,
+              int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
+              double* c64, bf16_t* cpart, float* cn2, float* cpn, hipStream_t st) {
+    launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, c64, cpart, cn2, cpn, st);
     SPR_LAUNCHED(c, "seed centroids");
     for (int t = 0; t < c->T; ++t) {
         int32_t* fc = flags + (size_t)t * c->H;
-        launch_assign(y, yerr, c->H, c->N, dim, c32, cnorm, groups, labels, fc, c->flag_list, st);
+        launch_assign(x, c->H, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, c->flag_list, st);
         SPR_LAUNCHED(c, "assign");
         launch_recheck(x, c->H, c->N, c->d, l64, dim, c64, groups, fc, c->flag_list, labels, st);
         SPR_LAUNCHED(c, "recheck");
         launch_counting_sort(labels, c->H, c->N, groups, c->blkhist, c->blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");
-        launch_group_means(x, c->H, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, c32,
-                           cnorm, st);
+        launch_group_means(x, c->H, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
+                           cn2, cpn, st);
         SPR_LAUNCHED(c, "group means");
     }
     return SPARSEPR_OK;
 }
 
-double frob32(const float* a, size_t count) {
-    double s = 0.0;
-    for (size_t i = 0; i < count; ++i) s += (double)a[i] * a[i];
-    return std::sqrt(s);
-}
-
-// Host: query metric factor per head from the raw key centroids, then upload.
+// Host: query metric factor per head, then upload. For G_k <= d the factor is the
+// profile map C_K^T / sqrt(d) (needs the centroids); otherwise it comes from the
+// metric C_K^T C_K / d, whose Gram is formed on the device.
 int32_t query_factor_all(sparsepr_ctx* c, hipStream_t st) {
     const size_t H = c->H, d = c->d, Gk = c->Gk, Dq = c->Dq;
-    c->h_kraw.resize(H * Gk * d);
-    SPR_HIP(c, hipMemcpyAsync(c->h_kraw.data(), c->kraw, sizeof(double) * H * Gk * d,
-                              hipMemcpyDeviceToHost, st));
+    const bool profile = c->Gk <= c->d;
+    if (profile) {
+        c->h_kraw.resize(H * Gk * d);
+        SPR_HIP(c, hipMemcpyAsync(c->h_kraw.data(), c->kraw, sizeof(double) * H * Gk * d,
+                                  hipMemcpyDeviceToHost, st));
+    } else {
+        launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
+        SPR_LAUNCHED(c, "query metric gram");
+        c->h_mq.resize(H * d * d);
+        SPR_HIP(c, hipMemcpyAsync(c->h_mq.data(), c->mq, sizeof(double) * H * d * d,
+                                  hipMemcpyDeviceToHost, st));
+    }
     SPR_HIP(c, hipStreamSynchronize(st));
     c->h_l64.assign(H * d * Dq, 0.0);
-    c->h_l32.resize(H * d * Dq);
-    c->h_lfro.resize(H);
-    std::vector<int> rc(H, 0), dims(H, 0);
+    std::vector<int> rc(H, 0), dims(H, (int)Dq);
     parallel_heads((int)H, [&](int h) {
-        rc[h] = query_factor((int)d, (int)Gk, &c->h_kraw[h * Gk * d], &c->h_l64[h * d * Dq], &dims[h]);
+        if (profile)
+            rc[h] = query_factor((int)d, (int)Gk, &c->h_kraw[h * Gk * d], &c->h_l64[h * d * Dq], &dims[h]);
+        else
+            rc[h] = query_factor_from_metric((int)d, &c->h_mq[h * d * d], &c->h_l64[h * d * Dq]);
     });
     for (size_t h = 0; h < H; ++h) {
         if (rc[h] != 0 || dims[h] != (int)Dq)
             return fail(c, SPARSEPR_ERR_NUMERIC, "query metric factor failed (non-finite centroids)");
-        for (size_t i = 0; i < d * Dq; ++i) c->h_l32[h * d * Dq + i] = (float)c->h_l64[h * d * Dq + i];
-        c->h_lfro[h] = (float)(frob32(&c->h_l32[h * d * Dq], d * Dq) * (1.0 + 1e-6));
     }
     SPR_HIP(c, hipMemcpyAsync(c->l64, c->h_l64.data(), sizeof(double) * H * d * Dq,
                               hipMemcpyHostToDevice, st));
-    SPR_HIP(c, hipMemcpyAsync(c->l32, c->h_l32.data(), sizeof(float) * H * d * Dq,
-                              hipMemcpyHostToDevice, st));
-    SPR_HIP(c, hipMemcpyAsync(c->lfro, c->h_lfro.data(), sizeof(float) * H, hipMemcpyHostToDevice, st));
     return SPARSEPR_OK;
 }
 
@@ -430,33 +428,23 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
                               hipMemcpyDeviceToHost, st));
     SPR_HIP(c, hipStreamSynchronize(st));
     c->h_w64.assign(H * d * rK, 0.0);
-    c->h_w32.resize(H * d * rK);
-    c->h_wfro.resize(H);
     std::vector<int> prc(H, 0);
     parallel_heads((int)H, [&](int h) {
         prc[h] = key_projection((int)d, &c->h_mk[h * d * d], (int)rK, &c->h_w64[h * d * rK]);
     });
     for (size_t h = 0; h < H; ++h) {
         if (prc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "metric eigensolve failed (non-finite input)");
-        for (size_t i = 0; i < d * rK; ++i) c->h_w32[h * d * rK + i] = (float)c->h_w64[h * d * rK + i];
-        c->h_wfro[h] = (float)(frob32(&c->h_w32[h * d * rK], d * rK) * (1.0 + 1e-6));
     }
     SPR_HIP(c, hipMemcpyAsync(c->w64, c->h_w64.data(), sizeof(double) * H * d * rK, hipMemcpyHostToDevice, st));
-    SPR_HIP(c, hipMemcpyAsync(c->w32, c->h_w32.data(), sizeof(float) * H * d * rK, hipMemcpyHostToDevice, st));
-    SPR_HIP(c, hipMemcpyAsync(c->wfro, c->h_wfro.data(), sizeof(float) * H, hipMemcpyHostToDevice, st));
-    // keys: Z = K W, Lloyd
-    launch_project(k16, c->H, c->N, c->d, c->w32, c->rK, c->wfro, c->z, c->zerr, st);
-    SPR_LAUNCHED(c, "project keys");
-    rc = lloyd(c, k16, c->z, c->zerr, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff,
-               c->kraw, c->kc64, c->kc32, c->kcn, st);
+    // keys: Lloyd in the M_K eigen-coordinates
+    rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw, c->kc64,
+               c->kcp, c->kcn2, c->kcpn, st);
     if (rc) return rc;
-    // queries: logit-profile metric factor (host fp64), Y = Q L, Lloyd
+    // queries: logit-profile metric factor (host fp64), Lloyd
     rc = query_factor_all(c, st);
     if (rc) return rc;
-    launch_project(q16, c->H, c->N, c->d, c->l32, c->Dq, c->lfro, c->yq, c->yerr, st);
-    SPR_LAUNCHED(c, "project queries");
-    rc = lloyd(c, q16, c->yq, c->yerr, c->Dq, c->l64, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H,
-               c->qperm, c->qoff, c->qraw, c->qc64, c->qc32, c->qcn, st);
+    rc = lloyd(c, q16, c->Dq, c->l64, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm,
+               c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, st);
     if (rc) return rc;
     mark(c, 1, st);
     c->stage = kStagePartition;
@@ -486,10 +474,10 @@ int32_t sparsepr_set_partition(sparsepr_ctx* c, const void* q, const void* k,
     launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * c->H, st);
     launch_counting_sort(c->klab, c->H, c->N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
     launch_group_means(k16, c->H, c->N, c->d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr,
-                       nullptr, nullptr, st);
+                       nullptr, nullptr, nullptr, st);
     launch_counting_sort(c->qlab, c->H, c->N, c->Gq, c->blkhist, c->blkoff, c->qperm, c->qoff, st);
     launch_group_means(q16, c->H, c->N, c->d, c->qperm, c->qoff, c->Gq, c->qraw, nullptr, 0, nullptr,
-                       nullptr, nullptr, st);
+                       nullptr, nullptr, nullptr, st);
     SPR_LAUNCHED(c, "set partition");
     if (host) SPR_HIP(c, hipStreamSynchronize(st));   // host labels must stay valid until copied
     c->stage = kStagePartition;
@@ -555,20 +543,29 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
     c->h_bm.assign(H * d * d, 0.0);
     c->h_bv.assign(H * d, 0.0);
     if (P > 0) {
-        c->h_x.resize(H * P * d);
-        c->h_y.resize(H * P * d);
-        SPR_HIP(c, hipMemcpyAsync(c->h_x.data(), c->px, sizeof(float) * H * P * d, hipMemcpyDeviceToHost, st));
-        SPR_HIP(c, hipMemcpyAsync(c->h_y.data(), c->py, sizeof(float) * H * P * d, hipMemcpyDeviceToHost, st));
+        // means and Grams on the device (fp64), the d x d solves on the host
+        double* xm = c->fit_m;
+        double* ym = c->fit_m + H * d;
+        double* gxx = c->fit_g;
+        double* gxy = c->fit_g + H * d * d;
+        double* gyy = c->fit_g + 2 * H * d * d;
+        launch_col_means_f32(c->px, c->H, c->P, c->d, xm, st);
+        launch_col_means_f32(c->py, c->H, c->P, c->d, ym, st);
+        launch_gram_f32(c->px, c->px, xm, xm, c->H, c->P, c->d, gxx, st);
+        launch_gram_f32(c->px, c->py, xm, ym, c->H, c->P, c->d, gxy, st);
+        launch_gram_f32(c->py, c->py, nullptr, nullptr, c->H, c->P, c->d, gyy, st);
+        SPR_LAUNCHED(c, "fit grams");
+        c->h_fit_m.resize(H * 2 * d);
+        c->h_fit_g.resize(H * 3 * d * d);
+        SPR_HIP(c, hipMemcpyAsync(c->h_fit_m.data(), c->fit_m, sizeof(double) * H * 2 * d, hipMemcpyDeviceToHost, st));
+        SPR_HIP(c, hipMemcpyAsync(c->h_fit_g.data(), c->fit_g, sizeof(double) * H * 3 * d * d, hipMemcpyDeviceToHost, st));
         SPR_HIP(c, hipStreamSynchronize(st));
         std::vector<int> frc(H, 0);
         parallel_heads((int)H, [&](int h) {
-            std::vector<double> x(P * d), y(P * d);
-            for (size_t i = 0; i < P * d; ++i) {
-                x[i] = c->h_x[h * P * d + i];
-                y[i] = c->h_y[h * P * d + i];
-            }
-            frc[h] = probe_fit((int)P, (int)d, x.data(), y.data(), c->p.ridge_lambda, c->p.corr_rank,
-                               &c->h_bm[h * d * d], &c->h_bv[h * d]);
+            frc[h] = probe_fit_from_grams((int)P, (int)d, &c->h_fit_m[h * d], &c->h_fit_m[(H + h) * d],
+                                          &c->h_fit_g[h * d * d], &c->h_fit_g[(H + h) * d * d],
+                                          &c->h_fit_g[(2 * H + h) * d * d], c->p.ridge_lambda,
+                                          c->p.corr_rank, &c->h_bm[h * d * d], &c->h_bv[h * d]);
         });
         for (size_t h = 0; h < H; ++h)
             if (frc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "probe fit failed (non-finite probe outputs)");

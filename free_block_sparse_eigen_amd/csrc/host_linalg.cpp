@@ -80,29 +80,39 @@ void tridiagonalize(int n, const double* a_in, Tridiag& t) {
     if (n >= 2) t.off[n - 2] = a[static_cast<size_t>(n - 1) * n + (n - 2)];
 }
 
-// Number of eigenvalues of T strictly below x (Sturm sequence of the LDL^T pivots).
-int sturm_count(const Tridiag& t, double x, double pivmin) {
-    int count = 0;
-    double q = t.diag[0] - x;
-    if (std::fabs(q) < pivmin) q = -pivmin;
-    if (q < 0) ++count;
-    for (int i = 1; i < t.n; ++i) {
-        q = (t.diag[i] - x) - t.off[i - 1] * t.off[i - 1] / q;
-        if (std::fabs(q) < pivmin) q = -pivmin;
-        if (q < 0) ++count;
+// Eigenvalues of ascending ranks first .. first+count-1 by bisection on Sturm counts, all
+// intervals advanced together so that the per-eigenvalue recurrences interleave.
+void bisect_eigenvalues(const Tridiag& t, int first, int count, double lo0, double hi0,
+                        double pivmin, double* out) {
+    std::vector<double> lo(count, lo0), hi(count, hi0), q(count), mid(count);
+    std::vector<int> cnt(count);
+    for (int it = 0; it < 80; ++it) {
+        for (int j = 0; j < count; ++j) mid[j] = 0.5 * (lo[j] + hi[j]);
+        for (int j = 0; j < count; ++j) {
+            double v = t.diag[0] - mid[j];
+            if (std::fabs(v) < pivmin) v = -pivmin;
+            q[j] = v;
+            cnt[j] = v < 0 ? 1 : 0;
+        }
+        for (int i = 1; i < t.n; ++i) {
+            const double e2 = t.off[i - 1] * t.off[i - 1];
+            const double di = t.diag[i];
+            for (int j = 0; j < count; ++j) {
+                double v = (di - mid[j]) - e2 / q[j];
+                if (std::fabs(v) < pivmin) v = -pivmin;
+                q[j] = v;
+                cnt[j] += v < 0 ? 1 : 0;
+            }
+        }
+        bool done = true;
+        for (int j = 0; j < count; ++j) {
+            if (cnt[j] > first + j) hi[j] = mid[j]; else lo[j] = mid[j];
+            if (hi[j] - lo[j] > 2.0 * kEps * std::max(std::fabs(lo[j]), std::fabs(hi[j])) + pivmin)
+                done = false;
+        }
+        if (done) break;
     }
-    return count;
-}
-
-// Eigenvalue of rank `idx` in ascending order (0 = smallest) by bisection.
-double bisect_eigenvalue(const Tridiag& t, int idx, double lo, double hi, double pivmin) {
-    for (int it = 0; it < 200; ++it) {
-        const double mid = 0.5 * (lo + hi);
-        if (mid <= lo || mid >= hi) break;
-        if (sturm_count(t, mid, pivmin) > idx) hi = mid; else lo = mid;
-        if (hi - lo <= 2.0 * kEps * std::max(std::fabs(lo), std::fabs(hi)) + pivmin) break;
-    }
-    return 0.5 * (lo + hi);
+    for (int j = 0; j < count; ++j) out[j] = 0.5 * (lo[j] + hi[j]);
 }
 
 // Solve (T - lambda I) y = b in place with Gaussian elimination and partial pivoting;
@@ -204,7 +214,11 @@ int sym_eig_top(int n, const double* a, int r, double* lam, double* vec) {
     glo -= pad;
     ghi += pad;
     // eigenvalues, descending: the j-th largest is ascending rank n-1-j
-    for (int j = 0; j < r; ++j) lam[j] = bisect_eigenvalue(t, n - 1 - j, glo, ghi, pivmin);
+    {
+        std::vector<double> asc(r);
+        bisect_eigenvalues(t, n - r, r, glo, ghi, pivmin, asc.data());
+        for (int j = 0; j < r; ++j) lam[j] = asc[r - 1 - j];
+    }
 
     // eigenvectors of T by inverse iteration
     const double tiny = kEps * tnorm;
@@ -286,6 +300,8 @@ int key_projection(int d, const double* m_k, int r, double* w) {
     return 0;
 }
 
+int query_factor_from_metric(int d, const double* m, double* l);
+
 int query_factor(int d, int g, const double* c, double* l, int* dims) {
     for (size_t i = 0; i < static_cast<size_t>(g) * d; ++i)
         if (!std::isfinite(c[i])) return -2;
@@ -304,131 +320,161 @@ int query_factor(int d, int g, const double* c, double* l, int* dims) {
             m[static_cast<size_t>(i) * d + j] = m[static_cast<size_t>(j) * d + i] = s / d;
         }
     *dims = d;
-    if (cholesky_lower(d, m.data(), l) == 0) return 0;
-    // semi-definite metric: L = U diag(sqrt(max(lambda, 0)))
-    return key_projection(d, m.data(), d, l);
+    return query_factor_from_metric(d, m.data(), l);
 }
 
-int probe_fit(int p, int d, const double* x, const double* y, double lambda, int rank,
-              double* b_mat, double* b_vec) {
-    std::memset(b_mat, 0, sizeof(double) * d * d);
-    std::memset(b_vec, 0, sizeof(double) * d);
-    if (p == 0) return 0;
-    for (size_t i = 0; i < static_cast<size_t>(p) * d; ++i)
-        if (!std::isfinite(x[i]) || !std::isfinite(y[i])) return -2;
-    // centred ridge: B = (Xc^T Xc + lambda I)^-1 Xc^T Yc, b = ybar - xbar B
-    std::vector<double> xm(d, 0.0), ym(d, 0.0);
+// Centred Grams of X, Y [p][d] (and the uncentred Y^T Y): the same quantities the
+// device computes before the host solve.
+void probe_grams(int p, int d, const double* x, const double* y, double* xm, double* ym, double* gxx,
+                 double* gxy, double* gyy) {
+    std::fill(xm, xm + d, 0.0);
+    std::fill(ym, ym + d, 0.0);
     for (int r = 0; r < p; ++r)
         for (int c = 0; c < d; ++c) {
             xm[c] += x[static_cast<size_t>(r) * d + c];
             ym[c] += y[static_cast<size_t>(r) * d + c];
         }
     for (int c = 0; c < d; ++c) { xm[c] /= p; ym[c] /= p; }
-    std::vector<double> xc(static_cast<size_t>(p) * d), yc(static_cast<size_t>(p) * d);
-    for (int r = 0; r < p; ++r)
-        for (int c = 0; c < d; ++c) {
-            xc[static_cast<size_t>(r) * d + c] = x[static_cast<size_t>(r) * d + c] - xm[c];
-            yc[static_cast<size_t>(r) * d + c] = y[static_cast<size_t>(r) * d + c] - ym[c];
-        }
-    std::vector<double> gram(static_cast<size_t>(d) * d, 0.0), rhs(static_cast<size_t>(d) * d, 0.0);
+    std::fill(gxx, gxx + static_cast<size_t>(d) * d, 0.0);
+    std::fill(gxy, gxy + static_cast<size_t>(d) * d, 0.0);
+    std::fill(gyy, gyy + static_cast<size_t>(d) * d, 0.0);
+    std::vector<double> xc(d), yc(d);
     for (int r = 0; r < p; ++r) {
-        const double* xr = &xc[static_cast<size_t>(r) * d];
-        const double* yr = &yc[static_cast<size_t>(r) * d];
+        const double* xr = &x[static_cast<size_t>(r) * d];
+        const double* yr = &y[static_cast<size_t>(r) * d];
+        for (int c = 0; c < d; ++c) { xc[c] = xr[c] - xm[c]; yc[c] = yr[c] - ym[c]; }
         for (int i = 0; i < d; ++i) {
-            const double xi = xr[i];
-            double* gi = &gram[static_cast<size_t>(i) * d];
-            double* ri = &rhs[static_cast<size_t>(i) * d];
-            for (int j = 0; j < d; ++j) { gi[j] += xi * xr[j]; ri[j] += xi * yr[j]; }
-        }
-    }
-    std::vector<double> bfull(static_cast<size_t>(d) * d, 0.0);
-    if (lambda > 0.0) {
-        for (int i = 0; i < d; ++i) gram[static_cast<size_t>(i) * d + i] += lambda;
-        std::vector<double> l(static_cast<size_t>(d) * d);
-        if (cholesky_lower(d, gram.data(), l.data()) != 0) return -3;
-        // solve L L^T B = rhs column by column
-        std::vector<double> z(d);
-        for (int col = 0; col < d; ++col) {
-            for (int i = 0; i < d; ++i) {
-                double s = rhs[static_cast<size_t>(i) * d + col];
-                for (int k = 0; k < i; ++k) s -= l[static_cast<size_t>(i) * d + k] * z[k];
-                z[i] = s / l[static_cast<size_t>(i) * d + i];
-            }
-            for (int i = d - 1; i >= 0; --i) {
-                double s = z[i];
-                for (int k = i + 1; k < d; ++k) s -= l[static_cast<size_t>(k) * d + i] * bfull[static_cast<size_t>(k) * d + col];
-                bfull[static_cast<size_t>(i) * d + col] = s / l[static_cast<size_t>(i) * d + i];
+            double* gi = &gxx[static_cast<size_t>(i) * d];
+            double* hi = &gxy[static_cast<size_t>(i) * d];
+            double* ki = &gyy[static_cast<size_t>(i) * d];
+            const double xi = xc[i], yi = yr[i];
+            for (int j = 0; j < d; ++j) {
+                gi[j] += xi * xc[j];
+                hi[j] += xi * yc[j];
+                ki[j] += yi * yr[j];
             }
         }
-    } else {
-        // minimum-norm least squares through the eigenpairs of Xc^T Xc
-        std::vector<double> lam(d), vec(static_cast<size_t>(d) * d);
-        if (sym_eig_top(d, gram.data(), d, lam.data(), vec.data()) != 0) return -3;
-        const double thr = std::max(lam[0], 0.0) * std::max(p, d) * kEps;
-        std::vector<double> tmp(static_cast<size_t>(d) * d, 0.0);   // diag(1/lam) V^T rhs
-        for (int e = 0; e < d; ++e) {
-            if (!(lam[e] > thr)) continue;
-            for (int col = 0; col < d; ++col) {
-                double s = 0.0;
-                for (int i = 0; i < d; ++i) s += vec[static_cast<size_t>(i) * d + e] * rhs[static_cast<size_t>(i) * d + col];
-                tmp[static_cast<size_t>(e) * d + col] = s / lam[e];
-            }
-        }
-        for (int i = 0; i < d; ++i)
-            for (int col = 0; col < d; ++col) {
-                double s = 0.0;
-                for (int e = 0; e < d; ++e) s += vec[static_cast<size_t>(i) * d + e] * tmp[static_cast<size_t>(e) * d + col];
-                bfull[static_cast<size_t>(i) * d + col] = s;
-            }
     }
-    std::vector<double> bv(d);
-    for (int j = 0; j < d; ++j) {
-        double s = ym[j];
-        for (int i = 0; i < d; ++i) s -= xm[i] * bfull[static_cast<size_t>(i) * d + j];
-        bv[j] = s;
-    }
-    // projector onto the leading right singular vectors of the uncentred Y
+}
+
+// Fit from the Grams: with V_r the leading eigenvectors of Y^T Y (the right singular
+// vectors of Y), B' = B V_r V_r^T where B V_r = (Xc^T Xc + lambda I)^-1 (Xc^T Yc V_r), and
+// b' = ybar Pi - xbar B'.
+int probe_fit_from_grams(int p, int d, const double* xm, const double* ym, const double* gxx_in,
+                         const double* gxy, const double* gyy, double lambda, int rank,
+                         double* b_mat, double* b_vec) {
+    std::memset(b_mat, 0, sizeof(double) * d * d);
+    std::memset(b_vec, 0, sizeof(double) * d);
+    if (p == 0) return 0;
+    for (size_t i = 0; i < static_cast<size_t>(d) * d; ++i)
+        if (!std::isfinite(gxx_in[i]) || !std::isfinite(gxy[i]) || !std::isfinite(gyy[i])) return -2;
     const int rmax = std::min(rank, std::min(p, d));
     if (rmax <= 0) return 0;
-    std::vector<double> yty(static_cast<size_t>(d) * d, 0.0);
-    for (int r = 0; r < p; ++r) {
-        const double* yr = &y[static_cast<size_t>(r) * d];
-        for (int i = 0; i < d; ++i) {
-            double* gi = &yty[static_cast<size_t>(i) * d];
-            for (int j = 0; j < d; ++j) gi[j] += yr[i] * yr[j];
-        }
-    }
     std::vector<double> lam(rmax), vec(static_cast<size_t>(d) * rmax);
-    if (sym_eig_top(d, yty.data(), rmax, lam.data(), vec.data()) != 0) return -3;
+    if (sym_eig_top(d, gyy, rmax, lam.data(), vec.data()) != 0) return -3;
     // singular values from the Gram eigenvalues; values below 2^-20 sigma_1 are not
     // resolved by the Gram route and count as zero
     const double s1 = std::sqrt(std::max(lam[0], 0.0));
-    int r_eff = 0;
+    int r = 0;
     if (s1 > 0.0) {
         const double thr = s1 * std::max(std::ldexp(1.0, -20), std::max(p, d) * kEps);
-        while (r_eff < rmax && std::sqrt(std::max(lam[r_eff], 0.0)) > thr) ++r_eff;
+        while (r < rmax && std::sqrt(std::max(lam[r], 0.0)) > thr) ++r;
     }
-    if (r_eff == 0) return 0;
-    std::vector<double> pi(static_cast<size_t>(d) * d, 0.0);
+    if (r == 0) return 0;
+    // R = Xc^T Yc V_r  [d][r]
+    std::vector<double> rhs(static_cast<size_t>(d) * r, 0.0), bv(static_cast<size_t>(d) * r, 0.0);
     for (int i = 0; i < d; ++i)
+        for (int t = 0; t < d; ++t) {
+            const double g = gxy[static_cast<size_t>(i) * d + t];
+            for (int e = 0; e < r; ++e) rhs[static_cast<size_t>(i) * r + e] += g * vec[static_cast<size_t>(t) * rmax + e];
+        }
+    if (lambda > 0.0) {
+        std::vector<double> gxx(gxx_in, gxx_in + static_cast<size_t>(d) * d);
+        for (int i = 0; i < d; ++i) gxx[static_cast<size_t>(i) * d + i] += lambda;
+        std::vector<double> l(static_cast<size_t>(d) * d);
+        if (cholesky_lower(d, gxx.data(), l.data()) != 0) return -3;
+        // forward then backward substitution, all r columns per row
+        std::vector<double> z(static_cast<size_t>(d) * r);
+        for (int i = 0; i < d; ++i) {
+            double* zi = &z[static_cast<size_t>(i) * r];
+            for (int e = 0; e < r; ++e) zi[e] = rhs[static_cast<size_t>(i) * r + e];
+            for (int k = 0; k < i; ++k) {
+                const double lik = l[static_cast<size_t>(i) * d + k];
+                const double* zk = &z[static_cast<size_t>(k) * r];
+                for (int e = 0; e < r; ++e) zi[e] -= lik * zk[e];
+            }
+            const double inv = 1.0 / l[static_cast<size_t>(i) * d + i];
+            for (int e = 0; e < r; ++e) zi[e] *= inv;
+        }
+        for (int i = d - 1; i >= 0; --i) {
+            double* bi = &bv[static_cast<size_t>(i) * r];
+            for (int e = 0; e < r; ++e) bi[e] = z[static_cast<size_t>(i) * r + e];
+            for (int k = i + 1; k < d; ++k) {
+                const double lki = l[static_cast<size_t>(k) * d + i];
+                const double* bk = &bv[static_cast<size_t>(k) * r];
+                for (int e = 0; e < r; ++e) bi[e] -= lki * bk[e];
+            }
+            const double inv = 1.0 / l[static_cast<size_t>(i) * d + i];
+            for (int e = 0; e < r; ++e) bi[e] *= inv;
+        }
+    } else {
+        // minimum-norm least squares through the eigenpairs of Xc^T Xc
+        std::vector<double> el(d), ev(static_cast<size_t>(d) * d);
+        if (sym_eig_top(d, gxx_in, d, el.data(), ev.data()) != 0) return -3;
+        const double thr = std::max(el[0], 0.0) * std::max(p, d) * kEps;
+        for (int k = 0; k < d; ++k) {
+            if (!(el[k] > thr)) continue;
+            for (int e = 0; e < r; ++e) {
+                double sdot = 0.0;
+                for (int i = 0; i < d; ++i) sdot += ev[static_cast<size_t>(i) * d + k] * rhs[static_cast<size_t>(i) * r + e];
+                sdot /= el[k];
+                for (int i = 0; i < d; ++i) bv[static_cast<size_t>(i) * r + e] += ev[static_cast<size_t>(i) * d + k] * sdot;
+            }
+        }
+    }
+    // B' = (B V_r) V_r^T; b' = ybar Pi - xbar B'
+    for (int i = 0; i < d; ++i) {
+        const double* bi = &bv[static_cast<size_t>(i) * r];
+        double* out = &b_mat[static_cast<size_t>(i) * d];
         for (int j = 0; j < d; ++j) {
             double s = 0.0;
-            for (int e = 0; e < r_eff; ++e) s += vec[static_cast<size_t>(i) * rmax + e] * vec[static_cast<size_t>(j) * rmax + e];
-            pi[static_cast<size_t>(i) * d + j] = s;
+            for (int e = 0; e < r; ++e) s += bi[e] * vec[static_cast<size_t>(j) * rmax + e];
+            out[j] = s;
         }
-    for (int i = 0; i < d; ++i)
-        for (int j = 0; j < d; ++j) {
-            double s = 0.0;
-            const double* bi = &bfull[static_cast<size_t>(i) * d];
-            for (int t = 0; t < d; ++t) s += bi[t] * pi[static_cast<size_t>(t) * d + j];
-            b_mat[static_cast<size_t>(i) * d + j] = s;
-        }
+    }
+    std::vector<double> yv(r, 0.0);
+    for (int e = 0; e < r; ++e)
+        for (int t = 0; t < d; ++t) yv[e] += ym[t] * vec[static_cast<size_t>(t) * rmax + e];
     for (int j = 0; j < d; ++j) {
         double s = 0.0;
-        for (int t = 0; t < d; ++t) s += bv[t] * pi[static_cast<size_t>(t) * d + j];
+        for (int e = 0; e < r; ++e) s += yv[e] * vec[static_cast<size_t>(j) * rmax + e];
+        for (int i = 0; i < d; ++i) s -= xm[i] * b_mat[static_cast<size_t>(i) * d + j];
         b_vec[j] = s;
     }
     return 0;
+}
+
+int probe_fit(int p, int d, const double* x, const double* y, double lambda, int rank,
+              double* b_mat, double* b_vec) {
+    if (p == 0) {
+        std::memset(b_mat, 0, sizeof(double) * d * d);
+        std::memset(b_vec, 0, sizeof(double) * d);
+        return 0;
+    }
+    for (size_t i = 0; i < static_cast<size_t>(p) * d; ++i)
+        if (!std::isfinite(x[i]) || !std::isfinite(y[i])) return -2;
+    std::vector<double> xm(d), ym(d), gxx(static_cast<size_t>(d) * d), gxy(static_cast<size_t>(d) * d),
+        gyy(static_cast<size_t>(d) * d);
+    probe_grams(p, d, x, y, xm.data(), ym.data(), gxx.data(), gxy.data(), gyy.data());
+    return probe_fit_from_grams(p, d, xm.data(), ym.data(), gxx.data(), gxy.data(), gyy.data(), lambda,
+                                rank, b_mat, b_vec);
+}
+
+// L [d][dims] from the metric m = C^T C / d (d x d): Cholesky if positive definite,
+// else the eigen factor U diag(sqrt(max(lambda, 0))).
+int query_factor_from_metric(int d, const double* m, double* l) {
+    if (cholesky_lower(d, m, l) == 0) return 0;
+    return key_projection(d, m, d, l);
 }
 
 }  // namespace spr

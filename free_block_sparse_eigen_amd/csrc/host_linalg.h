@@ -16,6 +16,18 @@ int key_projection(int d, const double* m_k, int r, double* w);
 // L [d][dims] with L L^T = C^T C / d (see sparsepr_host_query_factor).
 int query_factor(int d, int g, const double* c, double* l, int* dims);
 
+// L [d][d] from the metric m = C^T C / d (Cholesky, else eigen factor).
+int query_factor_from_metric(int d, const double* m, double* l);
+
+// Column means and centred Grams Xc^T Xc, Xc^T Yc, and Y^T Y (uncentred) of X, Y [p][d].
+void probe_grams(int p, int d, const double* x, const double* y, double* xm, double* ym, double* gxx,
+                 double* gxy, double* gyy);
+
+// B' [d][d], b' [d] from the probe Grams.
+int probe_fit_from_grams(int p, int d, const double* xm, const double* ym, const double* gxx,
+                         const double* gxy, const double* gyy, double lambda, int rank,
+                         double* b_mat, double* b_vec);
+
 // B' [d][d], b' [d] from X, Y [p][d].
 int probe_fit(int p, int d, const double* x, const double* y, double lambda, int rank,
               double* b_mat, double* b_vec);

@@ -21,13 +21,11 @@ void launch_fill_i64(int64_t* p, int64_t value, size_t count, hipStream_t st);
 // ---- partition ----
 void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64_t a, double* mk,
                    hipStream_t st);
-void launch_project(const bf16_t* x, int heads, int n, int d, const float* l32, int dout,
-                    const float* lfro, float* y, float* yerr, hipStream_t st);
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
-                           int groups, int64_t a, double* c64, float* c32, float* cnorm,
-                           hipStream_t st);
-void launch_assign(const float* y, const float* yerr, int heads, int n, int dim, const float* c32,
-                   const float* cnorm, int groups, int32_t* labels, int32_t* flag_count,
+                           int groups, int64_t a, double* c64, bf16_t* cpart, float* cn2,
+                           float* cpn, hipStream_t st);
+void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
+                   const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st);
 void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
                     const double* c64, int groups, const int32_t* flag_count,
@@ -36,7 +34,8 @@ void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, i
                           int32_t* blkoff, int32_t* sorted, int32_t* off, hipStream_t st);
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
-                        int dout, double* c64, float* c32, float* cnorm, hipStream_t st);
+                        int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
+                        hipStream_t st);
 
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,
@@ -72,5 +71,12 @@ void launch_probe_merge(int heads, int probes, int d, int splits, const float* p
 void launch_correct(const float* o_s, const float* bmat, const float* bvec, const float* od,
                     const int32_t* probe_of, const int32_t* qperm, int heads, int n, int d,
                     int probes, void* o, int out_f32, hipStream_t st);
+
+// ---- fit Grams (fp64) ----
+void launch_col_means_f32(const float* a, int heads, int p, int d, double* mean, hipStream_t st);
+void launch_gram_f32(const float* a, const float* b, const double* ma, const double* mb, int heads,
+                     int p, int d, double* out, hipStream_t st);
+void launch_gram_f64(const double* a, int heads, int p, int d, double scale, double* out,
+                     hipStream_t st);
 
 }  // namespace spr

@@ -3,10 +3,10 @@
 //
 //  * metric      M_K = Q_s^T Q_s / M_s over Weyl-sampled queries (fp64 sums of exact
 //                bf16 products)
-//  * project     Y = X L in fp32 (keys: L = W, the scaled leading eigenvectors of M_K;
-//                queries: L L^T = C_K^T C_K / d), plus a per-row forward error bound
-//  * assign      nearest centroid in fp32 with a certified margin; uncertified points
-//                are queued and resolved in fp64 by `recheck` (lowest index on ties)
+//  * metric spaces: keys use L = W (the scaled leading eigenvectors of M_K), queries
+//                L with L L^T = C_K^T C_K / d (their logit-profile metric)
+//  * assign      nearest centroid screened on MFMA with a certified margin; uncertified
+//                points are queued and resolved in fp64 by `recheck` (lowest index on ties)
 //  * counting sort (histogram, scan, stable scatter) and fp64 group means: the
 //                centroid update and, after the last round, the group-major permutation
 #include "kernels.h"
@@ -66,212 +66,224 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
     hipLaunchKernelGGL(k_metric, dim3(d, heads), dim3(d), 0, st, q, n, d, n_sample, a, mk);
 }
 
-// ------------------------------------------------------------------ project ---
-// y[h][r][0..dout) = x[h][r][:] . L[h] (fp32, i ascending), for 64 rows per block.
-// yerr[h][r] bounds |y_fp32 - y_exact|_2 by (d + 4) u |x_r| |L|_F (u = 2^-24), which
-// covers the fp32 rounding of L and the length-d fp32 dot products.
-constexpr int kProjRows = 64;
-
-__global__ __launch_bounds__(256) void k_project(const bf16_t* __restrict__ x, int n, int d,
-                                                 const float* __restrict__ l32, int dout,
-                                                 const float* __restrict__ lfro,
-                                                 float* __restrict__ y, float* __restrict__ yerr) {
-    __shared__ float smem[128 * 128 + kProjRows * 128];
-    float* ls = smem;                                  // [d][dout]
-    float* xs = smem + d * dout;                       // [64][d]
-    const int h = blockIdx.y;
-    const int r0 = blockIdx.x * kProjRows;
+// --------------------------------------------------------- centroid finish ---
+// For a raw-space centroid mean m (fp64, in LDS), with the metric factor L [d][D]:
+//   projected centroid   c = m L          (fp64, used by the fp64 recheck)
+//   screening vector     C' = L c^T       (d-dim; x . C' = (x L) . c for any point x)
+//   split of C' into bf16 hi + lo parts   (the MFMA operand; |C' - hi - lo| <= 2^-17 |C'|)
+//   |c|^2 (fp32, nearest) and |C'| (fp32, rounded up) for the screening score and bound
+// The block needs blockDim >= max(d, D).
+__device__ void finish_centroid(const double* __restrict__ mean, double* __restrict__ cp_lds,
+                                const double* __restrict__ lh, int d, int dout, int groups,
+                                int h, int g, double* __restrict__ c64, bf16_t* __restrict__ cpart,
+                                float* __restrict__ cn2, float* __restrict__ cpn,
+                                double* __restrict__ red) {
     const int tid = threadIdx.x;
-    const float* lh = l32 + (size_t)h * d * dout;
-    for (int i = tid; i < d * dout; i += 256) ls[i] = lh[i];
-    const bf16_t* xh = x + (size_t)h * n * d;
-    for (int i = tid; i < kProjRows * d; i += 256) {
-        const int r = r0 + i / d;
-        xs[i] = (r < n) ? bf16_to_f32(xh[(size_t)r * d + (i % d)]) : 0.f;
+    double cv = 0.0;
+    if (tid < dout) {
+        for (int i = 0; i < d; ++i) cv += mean[i] * lh[(size_t)i * dout + tid];
+        cp_lds[tid] = cv;
+        c64[((size_t)h * groups + g) * dout + tid] = cv;
     }
     __syncthreads();
-    const int r = tid >> 2, part = tid & 3;
-    float acc[32];
-#pragma unroll
-    for (int m = 0; m < 32; ++m) acc[m] = 0.f;
-    const float* xr = xs + r * d;
-    for (int i = 0; i < d; ++i) {
-        const float xv = xr[i];
-        const float* li = ls + i * dout;
-#pragma unroll
-        for (int m = 0; m < 32; ++m) {
-            const int j = part + 4 * m;
-            if (j < dout) acc[m] = fmaf(xv, li[j], acc[m]);
-        }
+    double sv = 0.0;
+    if (tid < d) {
+        for (int j = 0; j < dout; ++j) sv += lh[(size_t)tid * dout + j] * cp_lds[j];
+        const float hi = bf16_to_f32(f32_to_bf16((float)sv));
+        const bf16_t lo = f32_to_bf16((float)(sv - (double)hi));
+        cpart[((size_t)(h * 2 + 0) * groups + g) * d + tid] = f32_to_bf16((float)sv);
+        cpart[((size_t)(h * 2 + 1) * groups + g) * d + tid] = lo;
     }
-    const int row = r0 + r;
-    if (row < n) {
-        float* yr = y + ((size_t)h * n + row) * dout;
-#pragma unroll
-        for (int m = 0; m < 32; ++m) {
-            const int j = part + 4 * m;
-            if (j < dout) yr[j] = acc[m];
+    // norms: thread-strided partial sums, fixed-order reduction by thread 0
+    red[tid] = (tid < dout) ? cv * cv : 0.0;
+    red[blockDim.x + tid] = (tid < d) ? sv * sv : 0.0;
+    __syncthreads();
+    if (tid == 0) {
+        double a = 0.0, b = 0.0;
+        for (int i = 0; i < (int)blockDim.x; ++i) {
+            a += red[i];
+            b += red[blockDim.x + i];
         }
-        if (part == 0) {
-            double s = 0.0;
-            for (int i = 0; i < d; ++i) s += (double)xr[i] * xr[i];
-            const double e = (d + 4) * 5.9604644775390625e-08 * sqrt(s) * (double)lfro[h];
-            yerr[(size_t)h * n + row] = (float)(e * 1.0625);
-        }
+        cn2[(size_t)h * groups + g] = (float)a;                      // nearest: enters the score
+        cpn[(size_t)h * groups + g] = (float)(sqrt(b) * (1.0 + 1e-6));  // rounded up: bound only
     }
-}
-
-void launch_project(const bf16_t* x, int heads, int n, int d, const float* l32, int dout,
-                    const float* lfro, float* y, float* yerr, hipStream_t st) {
-    hipLaunchKernelGGL(k_project, dim3((n + kProjRows - 1) / kProjRows, heads), dim3(256), 0, st,
-                       x, n, d, l32, dout, lfro, y, yerr);
 }
 
 // ------------------------------------------------------------------- seeds ---
-// c[h][g] = x[h][(g a) mod n] . L64[h] in fp64 (the seed point's exact coordinates).
-__global__ void k_seed(const bf16_t* __restrict__ x, int n, int d, const double* __restrict__ l64,
-                       int dout, int64_t a, double* __restrict__ c64, float* __restrict__ c32,
-                       float* __restrict__ cnorm) {
-    __shared__ double xs[128];
-    __shared__ double red[128];
+// Seed centroid g is the point at Weyl index (g a) mod n.
+__global__ __launch_bounds__(128) void k_seed(const bf16_t* __restrict__ x, int n, int d,
+                                              const double* __restrict__ l64, int dout, int groups,
+                                              int64_t a, double* __restrict__ c64,
+                                              bf16_t* __restrict__ cpart, float* __restrict__ cn2,
+                                              float* __restrict__ cpn) {
+    __shared__ double mean[128];
+    __shared__ double cp[128];
+    __shared__ double red[256];
     const int h = blockIdx.y, g = blockIdx.x, j = threadIdx.x;
     const int64_t idx = ((int64_t)g * a) % n;
     const bf16_t* row = x + ((size_t)h * n + idx) * d;
-    if (j < d) xs[j] = (double)bf16_to_f32(row[j]);
+    if (j < d) mean[j] = (double)bf16_to_f32(row[j]);
     __syncthreads();
-    double s = 0.0;
-    if (j < dout) {
-        const double* lh = l64 + (size_t)h * d * dout;
-        for (int i = 0; i < d; ++i) s += xs[i] * lh[(size_t)i * dout + j];
-        c64[((size_t)h * gridDim.x + g) * dout + j] = s;
-        c32[((size_t)h * gridDim.x + g) * dout + j] = (float)s;
-    }
-    const float f = (j < dout) ? (float)s : 0.f;
-    red[j] = (double)f * f;
-    __syncthreads();
-    if (j == 0) {
-        double t = 0.0;
-        for (int i = 0; i < 128; ++i) t += red[i];
-        cnorm[(size_t)h * gridDim.x + g] = (float)(sqrt(t) * 1.0000002);
-    }
+    finish_centroid(mean, cp, l64 + (size_t)h * d * dout, d, dout, groups, h, g, c64, cpart, cn2,
+                    cpn, red);
 }
 
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
-                           int groups, int64_t a, double* c64, float* c32, float* cnorm,
-                           hipStream_t st) {
-    hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, l64, dout, a, c64,
-                       c32, cnorm);
+                           int groups, int64_t a, double* c64, bf16_t* cpart, float* cn2,
+                           float* cpn, hipStream_t st) {
+    hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, l64, dout, groups, a,
+                       c64, cpart, cn2, cpn);
 }
 
 // ------------------------------------------------------------------ assign ---
-// One point per thread; centroids staged through LDS in tiles. Distances are
-// sum_j (y_j - c_j)^2 in fp32 (DP = padded dimension, zero-filled). The point is
-// certified when the two smallest distances are separated by more than their
-// error bounds (see eps below); otherwise it is queued for the fp64 recheck.
-constexpr float kU32 = 5.9604644775390625e-08f;  // 2^-24
-
-template <int DP>
-__global__ __launch_bounds__(256) void k_assign(const float* __restrict__ y,
-                                                const float* __restrict__ yerr, int n, int dim,
-                                                const float* __restrict__ c32,
-                                                const float* __restrict__ cnorm, int groups,
+// Nearest centroid in the metric space, screened on MFMA. With y = x L the point's
+// coordinates, |y - c_g|^2 = |y|^2 + s_g with s_g = |c_g|^2 - 2 x . C'_g; |y|^2 is the
+// same for every g, so the argmin of s_g is the label. x . C'_g runs as a bf16 GEMM of
+// the raw rows (exact bf16) against the hi/lo split of C' with fp32 accumulation:
+//   |computed - exact| <= kappa |x| |C'_g|,  kappa = 2 d u (1 + 2^-8) + 2^-17  (u = 2^-24)
+// and the score s~_g = fl(|c_g|^2 - 2 S~_g) is within
+//   eps_g = 1.1 [2 kappa |x| |C'_g| + u |c_g|^2 + u |s~_g|]
+// of the exact s_g. The label is certified when every other centroid's lower end
+// s~_g - eps_g exceeds the best's upper end s~_best + eps_best; otherwise the point is
+// queued for the fp64 recheck (which also settles exact ties by the lowest index).
+//
+// Block = 4 waves x 64 points; centroids stream through LDS in tiles of 64 (hi and lo
+// parts), 16-byte chunk c of centroid row r stored at c ^ (r & 7).
+template <int D>
+__global__ __launch_bounds__(256) void k_assign(const bf16_t* __restrict__ x, int n,
+                                                const bf16_t* __restrict__ cpart,
+                                                const float* __restrict__ cn2,
+                                                const float* __restrict__ cpn, int groups,
                                                 int32_t* __restrict__ labels,
                                                 int32_t* __restrict__ flag_count,
                                                 int32_t* __restrict__ flag_list) {
-    constexpr int kTileBytes = 32768;
-    constexpr int GT = kTileBytes / (DP * 4);       // centroids per LDS tile
-    __shared__ float4 cs[GT * DP / 4];
-    __shared__ float red[256];
-    const int h = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int p = blockIdx.x * 256 + tid;
-    const bool valid = p < n;
-    // largest centroid norm of this head (bound term)
-    float cm = 0.f;
-    for (int g = tid; g < groups; g += 256) cm = fmaxf(cm, cnorm[(size_t)h * groups + g]);
-    red[tid] = cm;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-        __syncthreads();
+    constexpr int CH = D / 8;
+    constexpr int TG = 64;
+    constexpr float kU = 5.9604644775390625e-08f;
+    constexpr float kappa = 2.f * D * kU * 1.00390625f + 7.62939453125e-06f;
+    __shared__ uint4 s_c[2][TG * CH];
+    __shared__ float s_cn2[kMaxGroups];
+    __shared__ float s_cpn[kMaxGroups];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int half = lane >> 5;
+    for (int g = tid; g < groups; g += 256) {
+        s_cn2[g] = cn2[(size_t)h * groups + g];
+        s_cpn[g] = cpn[(size_t)h * groups + g];
     }
-    const float cmax = red[0];
-    float yv[DP];
-    const float* yp = y + ((size_t)h * n + (valid ? p : 0)) * dim;
+    const int p_base = blockIdx.x * 256 + w * 64;
+    uint4 xf[2][D / 16];
+    float kx[2];
 #pragma unroll
-    for (int j = 0; j < DP; ++j) yv[j] = (valid && j < dim) ? yp[j] : 0.f;
-    float best = INFINITY, second = INFINITY;
-    int bg = 0;
-    const float* ch = c32 + (size_t)h * groups * dim;
-    for (int g0 = 0; g0 < groups; g0 += GT) {
-        const int gt = min(GT, groups - g0);
-        __syncthreads();
-        float* csf = reinterpret_cast<float*>(cs);
-        for (int i = tid; i < GT * DP; i += 256) {
-            const int g = i / DP, j = i % DP;
-            csf[i] = (g < gt && j < dim) ? ch[(size_t)(g0 + g) * dim + j] : 0.f;
-        }
-        __syncthreads();
-        for (int g = 0; g < gt; ++g) {
-            float dist = 0.f;
+    for (int pb = 0; pb < 2; ++pb) {
+        const int pt = p_base + 32 * pb + (lane & 31);
+        const bool valid = pt < n;
+        float ss = 0.f;
 #pragma unroll
-            for (int j4 = 0; j4 < DP / 4; ++j4) {
-                const float4 c = cs[g * (DP / 4) + j4];
-                const float d0 = yv[4 * j4 + 0] - c.x, d1 = yv[4 * j4 + 1] - c.y;
-                const float d2 = yv[4 * j4 + 2] - c.z, d3 = yv[4 * j4 + 3] - c.w;
-                dist = fmaf(d0, d0, dist);
-                dist = fmaf(d1, d1, dist);
-                dist = fmaf(d2, d2, dist);
-                dist = fmaf(d3, d3, dist);
-            }
-            if (dist < best) {
-                second = best;
-                best = dist;
-                bg = g0 + g;
-            } else if (dist < second) {
-                second = dist;
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const uint4 v = valid ? *reinterpret_cast<const uint4*>(x + ((size_t)h * n + pt) * D +
+                                                                  16 * kk + 8 * half)
+                                  : make_uint4(0, 0, 0, 0);
+            xf[pb][kk] = v;
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = bf16_to_f32((bf16_t)(wd[e] & 0xFFFF));
+                const float hi = bf16_to_f32((bf16_t)(wd[e] >> 16));
+                ss = fmaf(lo, lo, fmaf(hi, hi, ss));
             }
         }
+        ss += __shfl_xor(ss, 32, 64);
+        kx[pb] = 1.1f * 2.f * kappa * sqrtf(ss) * 1.000001f;
     }
-    if (!valid) return;
-    labels[(size_t)h * n + p] = bg;
-    // |computed - exact| <= eps(x) for a computed distance x:
-    //   F = E + u |c|max + 2u sqrt(x) bounds |a_computed - a_exact|_2 (a = y - c),
-    //   eps = 1.1 [ (dim + 2) u x + F (2 sqrt(x) + F) ].
-    // x - eps(x) is increasing once x >= 4 F^2, so checking the runner-up suffices.
-    bool certified = false;
-    if (groups == 1) {
-        certified = true;
-    } else if (isfinite(second)) {
-        const float e = yerr[(size_t)h * n + p];
-        auto eps = [&](float x, float& fx) {
-            const float sx = sqrtf(x);
-            fx = e + kU32 * cmax + 2.f * kU32 * sx;
-            return 1.1f * ((dim + 2) * kU32 * x + fx * (2.f * sx + fx)) + 1e-30f;
-        };
-        float f1, f2;
-        const float e1 = eps(best, f1), e2 = eps(second, f2);
-        certified = (second - e2 > best + e1) && (second >= 4.f * f2 * f2);
+    constexpr float ku = 1.1f * kU;
+    float best[2] = {INFINITY, INFINITY}, eb[2] = {0.f, 0.f}, low2[2] = {INFINITY, INFINITY};
+    int bg[2] = {0x7fffffff, 0x7fffffff};
+    for (int g0 = 0; g0 < groups; g0 += TG) {
+        __syncthreads();
+        for (int i = tid; i < 2 * TG * CH; i += 256) {
+            const int part = i / (TG * CH), rem = i % (TG * CH);
+            const int row = rem / CH, c = rem % CH;
+            const int g = g0 + row;
+            s_c[part][row * CH + (c ^ (row & 7))] =
+                (g < groups) ? *reinterpret_cast<const uint4*>(
+                                   cpart + ((size_t)(h * 2 + part) * groups + g) * D + c * 8)
+                             : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int sub = 0; sub < TG / 32; ++sub) {
+            const int gb = g0 + 32 * sub;
+            if (gb >= groups) break;
+            f32x16 acc[2] = {};
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const uint4 a =
+                        s_c[part][(32 * sub + (lane & 31)) * CH + ((2 * kk + half) ^ (lane & 7))];
+                    acc[0] = mfma32x32x16(a, xf[0][kk], acc[0]);
+                    acc[1] = mfma32x32x16(a, xf[1][kk], acc[1]);
+                }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int g = gb + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (g < groups) {
+                    const float c2 = s_cn2[g], cp = s_cpn[g];
+#pragma unroll
+                    for (int pb = 0; pb < 2; ++pb) {
+                        const float v = fmaf(-2.f, acc[pb][r], c2);
+                        const float e = fmaf(kx[pb], cp, ku * (c2 + fabsf(v))) + 1e-30f;
+                        if (v < best[pb]) {
+                            low2[pb] = fminf(low2[pb], best[pb] - eb[pb]);
+                            best[pb] = v;
+                            eb[pb] = e;
+                            bg[pb] = g;
+                        } else {
+                            low2[pb] = fminf(low2[pb], v - e);
+                        }
+                    }
+                }
+            }
+        }
     }
-    if (!certified) {
-        const int slot = atomicAdd(&flag_count[h], 1);
-        flag_list[(size_t)h * n + slot] = p;
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+        // merge the two lane halves: best by (value, index); the other best joins low2
+        const float ob = __shfl_xor(best[pb], 32, 64);
+        const float oe = __shfl_xor(eb[pb], 32, 64);
+        const float ol = __shfl_xor(low2[pb], 32, 64);
+        const int og = __shfl_xor(bg[pb], 32, 64);
+        float b = best[pb], e = eb[pb], l2 = fminf(low2[pb], ol);
+        int gsel = bg[pb];
+        if (ob < b || (ob == b && og < gsel)) {
+            l2 = fminf(l2, b - e);
+            b = ob;
+            e = oe;
+            gsel = og;
+        } else {
+            l2 = fminf(l2, ob - oe);
+        }
+        const int pt = p_base + 32 * pb + lane;
+        if (lane < 32 && pt < n) {
+            labels[(size_t)h * n + pt] = gsel;
+            if (groups > 1 && !(l2 > b + e)) {
+                const int slot = atomicAdd(&flag_count[h], 1);
+                flag_list[(size_t)h * n + slot] = pt;
+            }
+        }
     }
 }
 
-void launch_assign(const float* y, const float* yerr, int heads, int n, int dim, const float* c32,
-                   const float* cnorm, int groups, int32_t* labels, int32_t* flag_count,
+void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
+                   const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st) {
     dim3 grid((n + 255) / 256, heads);
-    if (dim <= 32)
-        hipLaunchKernelGGL(k_assign<32>, grid, dim3(256), 0, st, y, yerr, n, dim, c32, cnorm, groups,
-                           labels, flag_count, flag_list);
-    else if (dim <= 64)
-        hipLaunchKernelGGL(k_assign<64>, grid, dim3(256), 0, st, y, yerr, n, dim, c32, cnorm, groups,
+    if (d == 128)
+        hipLaunchKernelGGL(k_assign<128>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
                            labels, flag_count, flag_list);
     else
-        hipLaunchKernelGGL(k_assign<128>, grid, dim3(256), 0, st, y, yerr, n, dim, c32, cnorm,
-                           groups, labels, flag_count, flag_list);
+        hipLaunchKernelGGL(k_assign<64>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
+                           labels, flag_count, flag_list);
 }
 
 // ----------------------------------------------------------------- recheck ---
@@ -434,15 +446,16 @@ void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, i
 // -------------------------------------------------------------- group means ---
 // Block per (group, head): fp64 sum of the members' raw rows in sorted order (fixed
 // split over row lanes, fixed-order reduction), mean = sum / count (zero if empty).
-// With l64 given, a non-empty group also gets its projected centroid c = mean . L64.
+// With l64 given, a non-empty group also gets its projected centroid, screening vector
+// and norms (an empty group keeps its previous centroid).
 __global__ __launch_bounds__(256) void k_group_means(
     const bf16_t* __restrict__ x, int n, int d, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ off, int groups, double* __restrict__ mean_raw,
-    const double* __restrict__ l64, int dout, double* __restrict__ c64, float* __restrict__ c32,
-    float* __restrict__ cnorm) {
+    const double* __restrict__ l64, int dout, double* __restrict__ c64,
+    bf16_t* __restrict__ cpart, float* __restrict__ cn2, float* __restrict__ cpn) {
     __shared__ double red[256 * 8];
     __shared__ double mean[128];
-    __shared__ double nrm[128];
+    __shared__ double cp[128];
     const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     const int chunks = d / 8;
     const int lanes = 256 / chunks;
@@ -476,30 +489,16 @@ __global__ __launch_bounds__(256) void k_group_means(
     }
     __syncthreads();
     if (l64 == nullptr || cnt == 0) return;           // empty: keep the previous centroid
-    double cv = 0.0;
-    if (tid < dout) {
-        const double* lh = l64 + (size_t)h * d * dout;
-        for (int i = 0; i < d; ++i) cv += mean[i] * lh[(size_t)i * dout + tid];
-        c64[((size_t)h * groups + g) * dout + tid] = cv;
-        c32[((size_t)h * groups + g) * dout + tid] = (float)cv;
-    }
-    if (tid < 128) {
-        const float f = (tid < dout) ? (float)cv : 0.f;
-        nrm[tid] = (double)f * f;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        double t = 0.0;
-        for (int i = 0; i < 128; ++i) t += nrm[i];
-        cnorm[(size_t)h * groups + g] = (float)(sqrt(t) * 1.0000002);
-    }
+    finish_centroid(mean, cp, l64 + (size_t)h * d * dout, d, dout, groups, h, g, c64, cpart, cn2,
+                    cpn, red);
 }
 
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
-                        int dout, double* c64, float* c32, float* cnorm, hipStream_t st) {
+                        int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
+                        hipStream_t st) {
     hipLaunchKernelGGL(k_group_means, dim3(groups, heads), dim3(256), 0, st, x, n, d, sorted, off,
-                       groups, mean_raw, l64, dout, c64, c32, cnorm);
+                       groups, mean_raw, l64, dout, c64, cpart, cn2, cpn);
 }
 
 }  // namespace spr
