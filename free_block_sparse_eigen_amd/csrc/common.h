@@ -20,19 +20,30 @@ __host__ __device__ inline float bf16_to_f32(bf16_t b) {
     return v.f;
 }
 
-// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs): the hardware
+// conversion on the device, the same rounding written out on the host.
 __host__ __device__ inline bf16_t f32_to_bf16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+#else
     union { uint32_t u; float f; } v;
     v.f = f;
     uint32_t u = v.u;
     u += 0x7FFFu + ((u >> 16) & 1u);
     return static_cast<bf16_t>(u >> 16);
+#endif
 }
 
-// Two fp32 -> packed bf16 pair (low half = a), round to nearest even.
+// Two fp32 -> packed bf16 pair (low half = a), round to nearest even (one instruction).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+// 2^x with the hardware instruction (results below 2^-126 flush to zero).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -49,6 +60,16 @@ __device__ inline bf16x2 ones_bf16x2() { return __builtin_bit_cast(bf16x2, 0x3F8
 // acc + lo(packed) + hi(packed), the bf16 pair summed in fp32
 __device__ inline float dot2_bf16(uint32_t packed, bf16x2 ones, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
+}
+
+// LDS row swizzle for tiles of 16-byte chunks: chunk c of row r is stored at c ^ swz(r).
+// swz is a bit permutation of r's low bits (bits 0,1 -> 1,2; bit 2 -> 0; bit 3 -> 3), so
+// 16 consecutive rows read at one logical chunk land on 16 distinct chunk slots, and 4
+// consecutive rows read at two adjacent chunks land on 8 distinct slots.
+template <int CH>
+__host__ __device__ inline int swz(int r) {
+    const int f = ((r & 3) << 1) | ((r >> 2) & 1);
+    return (CH >= 16) ? (f | (r & 8)) : f;
 }
 
 template <typename T>

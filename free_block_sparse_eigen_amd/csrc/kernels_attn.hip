@@ -11,11 +11,13 @@
 //
 // Work unit = (head, query group, up to 128 query rows); 4 waves x 32 rows.
 //   S^T = K Q^T  : A = K tile from LDS (row-major), B = Q^T fragments held in VGPRs
-//   O^T += V^T P^T: A = V^T tile from LDS (transposed while staging), B = P^T straight
-//                   from the S^T accumulators (bf16, no cross-lane traffic)
+//   O^T += V^T P^T: A = V^T read from the row-major V tile with the transposing LDS
+//                   read, B = P^T straight from the S^T accumulators (bf16, no
+//                   cross-lane traffic)
 // Keys stream in 64-key tiles packed across the routed segments (only the last tile
-// of the union is partial), staged global -> VGPR -> LDS, double-buffered, one barrier
-// per tile. Softmax in fp32 base-2 with a lazily raised running max.
+// of the union is partial), loaded global -> LDS directly (no VGPR staging),
+// double-buffered, one barrier per tile. Softmax in fp32 base-2 with a lazily raised
+// running max.
 #include "kernels.h"
 
 #include <cmath>
@@ -27,84 +29,44 @@ namespace {
 constexpr int KT = kKeyTile;
 constexpr float kLazy = 8.0f;  // raise the running max only when a tile exceeds it by 2^8
 
-__device__ inline uint32_t word_of(const uint4& v, int w) {
-    return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-}
-
-// 8 keys x 8 dims (one 16-byte chunk per key) -> 8 dims x 8 keys
-__device__ inline void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int we = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            o[p] = __builtin_amdgcn_perm(word_of(in[2 * p + 1], we), word_of(in[2 * p], we), sel);
-        out[e] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
 __device__ inline uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Tile staging shared by both kernels: the K tile row-major (16-byte chunk c of row r at
-// c ^ (r & 7)), the V tile transposed: row = dim, 64 keys, where 16-key slice s holds its
-// keys in the order [0-3, 8-11, 4-7, 12-15] so that the 8 keys an MFMA lane half needs
-// are one 16-byte chunk; chunk index (2 s + half) ^ (dim & 7).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Key tiles live in LDS row-major for both K and V: row r (a key), 16-byte chunk c
+// (dims 8c..8c+7) at slot r * CH + (c ^ swz(r)). They are filled by direct
+// global-to-LDS loads (no VGPR staging): one 16-byte load per lane lands at
+// LDS base + 16 * lane, so the swizzle is applied to the global addresses instead.
 template <int D>
 struct Tile {
     static constexpr int CH = D / 8;
-    static constexpr int NV = 8 * CH;      // V items: (slice, half, chunk), 8 key rows each
-    static constexpr int NK = 256 - NV;    // threads staging K
-    static constexpr int KCH = KT * CH;
+    static constexpr int SLOTS = KT * CH;           // 16-byte slots per tensor per tile
+    static constexpr int PER_WAVE = SLOTS / 256;    // load instructions per wave per tensor
 
-    __device__ static void load(const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
-                                size_t head_row0, const int* __restrict__ phys, int tid,
-                                uint4 (&stg)[8]) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        if (tid < NV) {
-            const int s4 = tid / (2 * CH), hh = (tid / CH) & 1, c = tid % CH;
+    // phys[] holds a valid row for every key of the tile (keys past the end of the
+    // union repeat a real row and are masked out of the softmax).
+    __device__ static void issue(const bf16_t* __restrict__ kbase, const bf16_t* __restrict__ vbase,
+                                 const int* __restrict__ phys, uint4* sk, uint4* sv, int w,
+                                 int lane) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int kk = 16 * s4 + 8 * (i >> 2) + 4 * hh + (i & 3);
-                const int r = phys[kk];
-                stg[i] = (r >= 0) ? ldg16(vp + (head_row0 + r) * D + c * 8) : z;
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int ci = (tid - NV) + m * NK;
-                if (ci < KCH) {
-                    const int r = phys[ci / CH];
-                    stg[m] = (r >= 0) ? ldg16(kp + (head_row0 + r) * D + (ci % CH) * 8) : z;
-                }
-            }
-        }
-    }
-
-    __device__ static void store(uint4* __restrict__ sk, uint4* __restrict__ svt, int tid,
-                                 const uint4 (&stg)[8]) {
-        if (tid < NV) {
-            const int s4 = tid / (2 * CH), hh = (tid / CH) & 1, c = tid % CH;
-            uint4 t[8];
-            transpose8(stg, t);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int dim = c * 8 + e;
-                svt[dim * 8 + ((2 * s4 + hh) ^ (dim & 7))] = t[e];
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int ci = (tid - NV) + m * NK;
-                if (ci < KCH) {
-                    const int r = ci / CH, c = ci % CH;
-                    sk[r * CH + (c ^ (r & 7))] = stg[m];
-                }
-            }
+        for (int m = 0; m < PER_WAVE; ++m) {
+            const int first = (w * PER_WAVE + m) * 64;
+            const int slot = first + lane;
+            const int r = slot / CH, pc = slot % CH;
+            const int off = phys[r] * D + ((pc ^ swz<CH>(r)) * 8);
+            __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sk + first), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sv + first), 16, 0, 0);
         }
     }
 };
+
+// Wait for this thread's outstanding direct loads, then for every wave of the block.
+__device__ inline void tile_ready() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
 
 // S^T block kb (32 keys x 32 queries) of the tile for this lane's query column.
 template <int D>
@@ -115,19 +77,53 @@ __device__ inline f32x16 qk_block(const uint4* __restrict__ sk, const uint4 (&qf
     const int row = kb * 32 + (lane & 31);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = sk[row * CH + ((2 * kk + (lane >> 5)) ^ (lane & 7))];
+        const uint4 a = sk[row * CH + ((2 * kk + (lane >> 5)) ^ swz<CH>(row))];
         s = mfma32x32x16(a, qf[kk], s);
     }
     return s;
 }
 
-// O^T[db] += V^T(dims of block db, 16 keys of slice s4) . P^T(slice s4)
-__device__ inline uint4 vt_frag(const uint4* __restrict__ svt, int db, int s4, int lane) {
-    const int dim = db * 32 + (lane & 31);
-    return svt[dim * 8 + ((2 * s4 + (lane >> 5)) ^ (dim & 7))];
+// A operand of O^T[db] += V^T P^T for 16-key slice s4: lane l needs V^T[dim][8 keys] with
+// dim = db*32 + (l & 31) and keys 16*s4 + 4*(l/32) + {0..3} (slots 0..3) and the same + 8
+// (slots 4..7) -- the key order of the P^T operand taken from the S^T accumulators.
+// ds_read_tr16_b64 gives lane L of a 16-lane group element (L % 4) of the 8-byte chunks
+// read by lanes L/4 + 4k (k = 0..3); so lane j supplies row key(j >> 2), columns
+// base + 4 (j & 3), and lane L receives dim base + L at the four keys.
+template <int D>
+__device__ inline uint4 vt_frag(const uint4* __restrict__ sv, int db, int s4, int lane) {
+    constexpr int CH = D / 8;
+    const int g = lane >> 4, j = lane & 15;
+    const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+    const int key0 = 16 * s4 + 4 * (g >> 1) + (j >> 2);
+    const int key1 = key0 + 8;
+    const bf16_t* base = reinterpret_cast<const bf16_t*>(sv);
+    const bf16_t* p0 = base + key0 * D + (((col >> 3) ^ swz<CH>(key0)) << 3) + (col & 7);
+    const bf16_t* p1 = base + key1 * D + (((col >> 3) ^ swz<CH>(key1)) << 3) + (col & 7);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return make_uint4(ua.x, ua.y, ub.x, ub.y);
 }
 
-__device__ inline float swap_halves_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+// Lanes l and l ^ 32 hold the two halves of one query column.
+__device__ inline float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Blocks of one XCD get a contiguous range of work units (the hardware hands workgroups
+// to the 8 XCDs round-robin), so units that stream the same key tiles share an L2.
+__device__ inline int xcd_linear_id() {
+    const int total = gridDim.x * gridDim.y * gridDim.z;
+    const int lid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int xcd = lid & 7, k = lid >> 3;
+    const int q = total >> 3, r = total & 7;
+    return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
 
 // Key tile -> physical rows: the smallest segment s with prefix[s+1] > u holds virtual key u.
 __device__ inline int segment_row(const int* __restrict__ pre, const int* __restrict__ start,
@@ -154,13 +150,15 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     __shared__ int s_pre[kMaxGroups + 1];
     __shared__ int s_start[kMaxGroups];
     __shared__ int s_phys[2][KT];
-    __shared__ uint4 s_k[2][TL::KCH];
-    __shared__ uint4 s_vt[2][D * 8];
+    __shared__ uint4 s_k[2][TL::SLOTS];
+    __shared__ uint4 s_v[2][TL::SLOTS];
 
-    const int h = blockIdx.y;
+    const int nid = xcd_linear_id();
+    const int max_units = gridDim.x;
+    const int h = nid / max_units, ui = nid % max_units;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if ((int)blockIdx.x >= nunits[(size_t)h * nunits_stride]) return;
-    const int2 un = units[(size_t)h * units_head_stride + blockIdx.x];
+    if (ui >= nunits[(size_t)h * nunits_stride]) return;
+    const int2 un = units[(size_t)h * units_head_stride + ui];
     const int gi = un.x, row0 = un.y;
     const int32_t* qo = qoff + (size_t)h * qoff_stride;
     const int rows = min(kAttnRows, qo[gi + 1] - row0);
@@ -181,10 +179,11 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     const int U = s_pre[kblk];
     const int ntiles = (U + KT - 1) / KT;
 
+    // rows of tile t; keys past the union repeat the tile's first row (masked later)
     auto fill_phys = [&](int t, int buf) {
         if (tid < KT) {
             const int u = t * KT + tid;
-            s_phys[buf][tid] = (u < U) ? segment_row(s_pre, s_start, kblk, u) : -1;
+            s_phys[buf][tid] = segment_row(s_pre, s_start, kblk, (u < U) ? u : t * KT);
         }
     };
 
@@ -202,77 +201,104 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
+    const bf16x2 ones = ones_bf16x2();
+    const int half = lane >> 5;
 
-    uint4 stg[8];
+    const bf16_t* kbase = kp + head_row0 * D;
+    const bf16_t* vbase = vp + head_row0 * D;
     fill_phys(0, 0);
     __syncthreads();
-    TL::load(kp, vp, head_row0, s_phys[0], tid, stg);
-    TL::store(s_k[0], s_vt[0], tid, stg);
+    TL::issue(kbase, vbase, s_phys[0], s_k[0], s_v[0], w, lane);
     if (ntiles > 1) fill_phys(1, 1);
-    __syncthreads();
+    tile_ready();
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) TL::load(kp, vp, head_row0, s_phys[buf ^ 1], tid, stg);
+        if (t + 1 < ntiles) TL::issue(kbase, vbase, s_phys[buf ^ 1], s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
         if (active) {
-            f32x16 s0 = qk_block<D>(s_k[buf], qf, 0, lane);
-            f32x16 s1 = qk_block<D>(s_k[buf], qf, 1, lane);
+            // S^T for both 32-key blocks: two independent accumulation chains
+            const uint4* sk = s_k[buf];
+            f32x16 s0 = {}, s1 = {};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const int c = (2 * kk + half) ^ swz<TL::CH>(lane & 31);   // swz(r) = swz(r + 32)
+                s0 = mfma32x32x16(sk[(lane & 31) * TL::CH + c], qf[kk], s0);
+                s1 = mfma32x32x16(sk[(32 + (lane & 31)) * TL::CH + c], qf[kk], s1);
+            }
             const int nvk = U - t * KT;
             if (nvk < KT) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (key >= nvk) s0[r] = -INFINITY;
-                    if (key + 32 >= nvk) s1[r] = -INFINITY;
+                    const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+                    s0[r] = (key < nvk) ? s0[r] : -INFINITY;
+                    s1[r] = (key + 32 < nvk) ? s1[r] : -INFINITY;
                 }
             }
-            float mx = -INFINITY;
+            float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = swap_halves_max(mx);
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+            mx = pair_max(mx);
             const float mt = mx * scale_log2;
             if (__ballot(mt > m_run + kLazy)) {
                 const float mnew = fmaxf(m_run, mt);
-                const float alpha = exp2f(m_run - mnew);
+                const float alpha = fast_exp2(m_run - mnew);
                 l_run *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[db] *= alpha;
                 m_run = mnew;
             }
             const float mneg = -m_run;
+            // P^T slices 0,1 (keys 0..31), then PV of those slices overlapped with the
+            // exponentials of slices 2,3 (keys 32..63)
             uint4 pb[4];
-            const bf16x2_ones_t ones = ones_bf16x2();
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl) {
+            for (int sl = 0; sl < 2; ++sl) {
                 uint32_t wv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 8 * (sl & 1) + 2 * i;
-                    const float x0 = (sl < 2) ? s0[r] : s1[r];
-                    const float x1 = (sl < 2) ? s0[r + 1] : s1[r + 1];
-                    const float p0 = exp2f(fmaf(x0, scale_log2, mneg));
-                    const float p1 = exp2f(fmaf(x1, scale_log2, mneg));
-                    wv[i] = pack_bf16x2(p0, p1);
+                    const int r = 8 * sl + 2 * i;
+                    wv[i] = pack_bf16x2(fast_exp2(fmaf(s0[r], scale_log2, mneg)),
+                                        fast_exp2(fmaf(s0[r + 1], scale_log2, mneg)));
+                    l_run = dot2_bf16(wv[i], ones, l_run);
+                }
+                pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+            const uint4* sv = s_v[buf];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    o[db] = mfma32x32x16(vt_frag<D>(sv, db, sl, lane), pb[sl], o[db]);
+#pragma unroll
+            for (int sl = 2; sl < 4; ++sl) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 8 * (sl - 2) + 2 * i;
+                    wv[i] = pack_bf16x2(fast_exp2(fmaf(s1[r], scale_log2, mneg)),
+                                        fast_exp2(fmaf(s1[r + 1], scale_log2, mneg)));
                     l_run = dot2_bf16(wv[i], ones, l_run);
                 }
                 pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
+            for (int sl = 2; sl < 4; ++sl)
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    o[db] = mfma32x32x16(vt_frag(s_vt[buf], db, sl, lane), pb[sl], o[db]);
+                    o[db] = mfma32x32x16(vt_frag<D>(sv, db, sl, lane), pb[sl], o[db]);
+            // interleave: the first 2*DB MFMAs of PV with the exponentials of keys 32..63
+#pragma unroll
+            for (int i = 0; i < 2 * DB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+            }
         }
-        if (more) {
-            TL::store(s_k[buf ^ 1], s_vt[buf ^ 1], tid, stg);
-            if (t + 2 < ntiles) fill_phys(t + 2, buf);
-        }
-        __syncthreads();
+        if (t + 2 < ntiles) fill_phys(t + 2, buf);
+        tile_ready();
     }
 
     if (!active) return;
-    l_run += __shfl_xor(l_run, 32, 64);
+    l_run = pair_sum(l_run);
     const float inv = 1.0f / l_run;
     if (!qvalid) return;
     const size_t orow = head_row0 + row0 + qrow;
@@ -280,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int dim = db * 32 + 8 * g + 4 * (lane >> 5);
+            const int dim = db * 32 + 8 * g + 4 * half;
             const float v0 = o[db][4 * g] * inv, v1 = o[db][4 * g + 1] * inv;
             const float v2 = o[db][4 * g + 2] * inv, v3 = o[db][4 * g + 3] * inv;
             if (OUTM == 0) {
@@ -336,8 +362,8 @@ __global__ __launch_bounds__(256) void k_probe(
     __shared__ int s_phys[2][KT];
     __shared__ int s_kg[2][KT];
     __shared__ uint32_t s_bits[kProbeRows][kMaxGroups / 32];
-    __shared__ uint4 s_k[2][TL::KCH];
-    __shared__ uint4 s_vt[2][D * 8];
+    __shared__ uint4 s_k[2][TL::SLOTS];
+    __shared__ uint4 s_v[2][TL::SLOTS];
 
     const int h = blockIdx.z, split = blockIdx.y, splits = gridDim.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -362,9 +388,9 @@ __global__ __launch_bounds__(256) void k_probe(
     auto fill_phys = [&](int t, int buf) {
         if (tid < KT) {
             const int u = t * KT + tid;
-            const int r = (u < nkeys) ? k0 + u : -1;
+            const int r = (u < nkeys) ? k0 + u : k0;        // padding keys repeat row k0 (masked)
             s_phys[buf][tid] = r;
-            s_kg[buf][tid] = (r >= 0) ? kgrp[head_row0 + r] : 0;
+            s_kg[buf][tid] = kgrp[head_row0 + r];
         }
     };
 
@@ -386,19 +412,18 @@ __global__ __launch_bounds__(256) void k_probe(
     for (int db = 0; db < DB; ++db) { od[db] = f32x16{}; os[db] = f32x16{}; }
     float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
 
-    uint4 stg[8];
+    const bf16_t* kbase = kp + head_row0 * D;
+    const bf16_t* vbase = vp + head_row0 * D;
     if (ntiles > 0) {
         fill_phys(0, 0);
         __syncthreads();
-        TL::load(kp, vp, head_row0, s_phys[0], tid, stg);
-        TL::store(s_k[0], s_vt[0], tid, stg);
+        TL::issue(kbase, vbase, s_phys[0], s_k[0], s_v[0], w, lane);
         if (ntiles > 1) fill_phys(1, 1);
     }
-    __syncthreads();
+    tile_ready();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) TL::load(kp, vp, head_row0, s_phys[buf ^ 1], tid, stg);
+        if (t + 1 < ntiles) TL::issue(kbase, vbase, s_phys[buf ^ 1], s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
         if (active) {
             f32x16 sv[2];
             sv[0] = qk_block<D>(s_k[buf], qf, 0, lane);
@@ -420,11 +445,11 @@ __global__ __launch_bounds__(256) void k_probe(
                     mxd = fmaxf(mxd, x);
                     mxs = fmaxf(mxs, xs[kb * 16 + r]);
                 }
-            mxd = swap_halves_max(mxd);
-            mxs = swap_halves_max(mxs);
+            mxd = pair_max(mxd);
+            mxs = pair_max(mxs);
             const float mdn = fmaxf(md, mxd), msn = fmaxf(ms, mxs);
-            const float ad = (mdn == -INFINITY) ? 1.f : exp2f(md - mdn);
-            const float as = (msn == -INFINITY) ? 1.f : exp2f(ms - msn);
+            const float ad = (mdn == -INFINITY) ? 1.f : fast_exp2(md - mdn);
+            const float as = (msn == -INFINITY) ? 1.f : fast_exp2(ms - msn);
             ld *= ad;
             ls *= as;
 #pragma unroll
@@ -441,8 +466,8 @@ __global__ __launch_bounds__(256) void k_probe(
                     float pd[2], ps[2];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
-                        pd[u] = (md == -INFINITY) ? 0.f : exp2f(xd[k + u] - md);
-                        ps[u] = (ms == -INFINITY) ? 0.f : exp2f(xs[k + u] - ms);
+                        pd[u] = (md == -INFINITY) ? 0.f : fast_exp2(xd[k + u] - md);
+                        ps[u] = (ms == -INFINITY) ? 0.f : fast_exp2(xs[k + u] - ms);
                         ld += pd[u];
                         ls += ps[u];
                     }
@@ -462,22 +487,19 @@ __global__ __launch_bounds__(256) void k_probe(
             for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const uint4 a = vt_frag(s_vt[buf], db, sl, lane);
+                    const uint4 a = vt_frag<D>(s_v[buf], db, sl, lane);
                     od[db] = mfma32x32x16(a, dh[sl], od[db]);
                     od[db] = mfma32x32x16(a, dl[sl], od[db]);
                     os[db] = mfma32x32x16(a, sh[sl], os[db]);
                     os[db] = mfma32x32x16(a, sl4[sl], os[db]);
                 }
         }
-        if (more) {
-            TL::store(s_k[buf ^ 1], s_vt[buf ^ 1], tid, stg);
-            if (t + 2 < ntiles) fill_phys(t + 2, buf);
-        }
-        __syncthreads();
+        if (t + 2 < ntiles) fill_phys(t + 2, buf);
+        tile_ready();
     }
     if (!active) return;
-    ld += __shfl_xor(ld, 32, 64);
-    ls += __shfl_xor(ls, 32, 64);
+    ld = pair_sum(ld);
+    ls = pair_sum(ls);
     if (!pvalid) return;
     const size_t base = ((size_t)h * splits + split) * probes + p;
     if (lane < 32) {

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void k_correct(const float* __restrict__ o_s,
                                                  int probes, void* __restrict__ out, int out_f32) {
     constexpr int CH = D / 8;          // 16-byte chunks per bf16 row of B'^T
     constexpr int JB = D / 32;         // 32-column output blocks
-    __shared__ uint4 s_b[2][D * CH];   // B'^T hi / lo: row j, chunk c at c ^ (j & 7)
+    __shared__ uint4 s_b[2][D * CH];   // B'^T hi / lo: row j, chunk c at c ^ swz(j)
     __shared__ float s_bv[D];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5;
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_correct(const float* __restrict__ o_s,
             hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
             lw[e] = pack_bf16x2(v0 - bf16_to_f32(h0), v1 - bf16_to_f32(h1));
         }
-        const int pc = c ^ (j & 7);
+        const int pc = c ^ swz<CH>(j);
         s_b[0][j * CH + pc] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         s_b[1][j * CH + pc] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_correct(const float* __restrict__ o_s,
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
             const int j = jb * 32 + (lane & 31);
-            const int pc = (2 * kk + half) ^ (j & 7);
+            const int pc = (2 * kk + half) ^ swz<CH>(j);
             const uint4 ahi = s_b[0][j * CH + pc];
             const uint4 alo = s_b[1][j * CH + pc];
             acc[jb] = mfma32x32x16(ahi, bhi, acc[jb]);

@@ -148,7 +148,7 @@ void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const doubl
 // queued for the fp64 recheck (which also settles exact ties by the lowest index).
 //
 // Block = 4 waves x 64 points; centroids stream through LDS in tiles of 64 (hi and lo
-// parts), 16-byte chunk c of centroid row r stored at c ^ (r & 7).
+// parts), 16-byte chunk c of centroid row r stored at c ^ swz(r).
 template <int D>
 __global__ __launch_bounds__(256) void k_assign(const bf16_t* __restrict__ x, int n,
                                                 const bf16_t* __restrict__ cpart,
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void k_assign(const bf16_t* __restrict__ x, in
             const int part = i / (TG * CH), rem = i % (TG * CH);
             const int row = rem / CH, c = rem % CH;
             const int g = g0 + row;
-            s_c[part][row * CH + (c ^ (row & 7))] =
+            s_c[part][row * CH + (c ^ swz<CH>(row))] =
                 (g < groups) ? *reinterpret_cast<const uint4*>(
                                    cpart + ((size_t)(h * 2 + part) * groups + g) * D + c * 8)
                              : make_uint4(0, 0, 0, 0);
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void k_assign(const bf16_t* __restrict__ x, in
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
                     const uint4 a =
-                        s_c[part][(32 * sub + (lane & 31)) * CH + ((2 * kk + half) ^ (lane & 7))];
+                        s_c[part][(32 * sub + (lane & 31)) * CH + ((2 * kk + half) ^ swz<CH>(lane & 31))];
                     acc[0] = mfma32x32x16(a, xf[0][kk], acc[0]);
                     acc[1] = mfma32x32x16(a, xf[1][kk], acc[1]);
                 }
