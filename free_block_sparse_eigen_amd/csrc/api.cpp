@@ -54,8 +54,12 @@ struct sparsepr_ctx {
     int2* dense_unit_list = nullptr;
 
     // host mirrors
-    std::vector<double> h_mk, h_w64, h_kraw, h_l64, h_bm, h_bv, h_fit_m, h_fit_g, h_mq;
-    std::vector<float> h_x, h_y, h_bm32, h_bv32;
+    std::vector<double> h_mk, h_w64, h_kraw, h_l64, h_bm, h_bv, h_mq;
+    std::vector<float> h_x, h_y;
+    // pinned host buffers of the fit: Grams in (device -> host), B' and b' out
+    double* h_fit = nullptr;          // [H][2][d] means, then [H][3][d][d] Grams
+    float* h_b32 = nullptr;           // [H][d][d] B', then [H][d] b'
+    hipEvent_t ev_probe = nullptr;    // probe rows and fit Grams are on the host
 
     int stage = 0;
     bool poisoned = false;
@@ -269,7 +273,8 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, int dim, const double* l64, int groups,
               int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
               double* c64, bf16_t* cpart, float* cn2, float* cpn, hipStream_t st) {
-    launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, c64, cpart, cn2, cpn, st);
+    launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
+                          cpn, st);
     SPR_LAUNCHED(c, "seed centroids");
     for (int t = 0; t < c->T; ++t) {
         int32_t* fc = flags + (size_t)t * c->H;
@@ -379,6 +384,15 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
         for (auto& row : c->ev)
             for (auto& e : row)
                 if (hipEventCreate(&e) != hipSuccess) e = nullptr;
+    {
+        const size_t H = c->H, d = c->d;
+        if (hipHostMalloc(reinterpret_cast<void**>(&c->h_fit), sizeof(double) * H * (2 * d + 3 * d * d)) != hipSuccess ||
+            hipHostMalloc(reinterpret_cast<void**>(&c->h_b32), sizeof(float) * H * (d * d + d)) != hipSuccess ||
+            hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming) != hipSuccess) {
+            sparsepr_destroy(c);
+            return SPARSEPR_ERR_OOM;
+        }
+    }
     // dense baseline metadata
     const int meta[8] = {0, c->N, 0, c->N, 0, c->dense_units, 0, 0};
     if (hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice) != hipSuccess) {
@@ -403,6 +417,9 @@ void sparsepr_destroy(sparsepr_ctx* c) {
         for (auto& row : c->ev)
             for (auto& e : row)
                 if (e) (void)hipEventDestroy(e);
+    if (c->ev_probe) (void)hipEventDestroy(c->ev_probe);
+    if (c->h_fit) (void)hipHostFree(c->h_fit);
+    if (c->h_b32) (void)hipHostFree(c->h_b32);
     if (c->arena) (void)hipFree(c->arena);
     delete c;
 }
@@ -519,16 +536,36 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
+    const size_t H = c->H, d = c->d;
+    // Probe rows first, with the fit's fp64 means and Grams, copied to pinned host
+    // memory; the host solve (sparsepr_probe_fit) then overlaps the main kernel.
+    if (c->P > 0) {
+        launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P, c->kgrp,
+                     c->Gk, c->blocks, c->Gq, c->k, c->part_ml, c->part_od, c->part_os, st);
+        launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
+                           c->py, c->pod, st);
+        SPR_LAUNCHED(c, "probe rows");
+        double* xm = c->fit_m;
+        double* ym = c->fit_m + H * d;
+        double* gxx = c->fit_g;
+        double* gxy = c->fit_g + H * d * d;
+        double* gyy = c->fit_g + 2 * H * d * d;
+        launch_col_means_f32(c->px, c->H, c->P, c->d, xm, st);
+        launch_col_means_f32(c->py, c->H, c->P, c->d, ym, st);
+        launch_gram_f32(c->px, c->px, xm, xm, c->H, c->P, c->d, gxx, st);
+        launch_gram_f32(c->px, c->py, xm, ym, c->H, c->P, c->d, gxy, st);
+        launch_gram_f32(c->py, c->py, nullptr, nullptr, c->H, c->P, c->d, gyy, st);
+        SPR_LAUNCHED(c, "fit grams");
+        SPR_HIP(c, hipMemcpyAsync(c->h_fit, c->fit_m, sizeof(double) * H * 2 * d, hipMemcpyDeviceToHost, st));
+        SPR_HIP(c, hipMemcpyAsync(c->h_fit + H * 2 * d, c->fit_g, sizeof(double) * H * 3 * d * d,
+                                  hipMemcpyDeviceToHost, st));
+    }
+    SPR_HIP(c, hipEventRecord(c->ev_probe, st));
+    mark(c, 4, st);
     launch_vbsa(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
                 c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, c->o_s, 0,
                 st);
     SPR_LAUNCHED(c, "sparse attention");
-    mark(c, 4, st);
-    launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P, c->kgrp,
-                 c->Gk, c->blocks, c->Gq, c->k, c->part_ml, c->part_od, c->part_os, st);
-    launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
-                       c->py, c->pod, st);
-    SPR_LAUNCHED(c, "probe rows");
     mark(c, 5, st);
     c->stage = kStageAttn;
     return SPARSEPR_OK;
@@ -542,40 +579,26 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
     const size_t H = c->H, d = c->d, P = c->P;
     c->h_bm.assign(H * d * d, 0.0);
     c->h_bv.assign(H * d, 0.0);
+    // waits for the probe rows and Grams only: the main kernel keeps running
+    SPR_HIP(c, hipEventSynchronize(c->ev_probe));
     if (P > 0) {
-        // means and Grams on the device (fp64), the d x d solves on the host
-        double* xm = c->fit_m;
-        double* ym = c->fit_m + H * d;
-        double* gxx = c->fit_g;
-        double* gxy = c->fit_g + H * d * d;
-        double* gyy = c->fit_g + 2 * H * d * d;
-        launch_col_means_f32(c->px, c->H, c->P, c->d, xm, st);
-        launch_col_means_f32(c->py, c->H, c->P, c->d, ym, st);
-        launch_gram_f32(c->px, c->px, xm, xm, c->H, c->P, c->d, gxx, st);
-        launch_gram_f32(c->px, c->py, xm, ym, c->H, c->P, c->d, gxy, st);
-        launch_gram_f32(c->py, c->py, nullptr, nullptr, c->H, c->P, c->d, gyy, st);
-        SPR_LAUNCHED(c, "fit grams");
-        c->h_fit_m.resize(H * 2 * d);
-        c->h_fit_g.resize(H * 3 * d * d);
-        SPR_HIP(c, hipMemcpyAsync(c->h_fit_m.data(), c->fit_m, sizeof(double) * H * 2 * d, hipMemcpyDeviceToHost, st));
-        SPR_HIP(c, hipMemcpyAsync(c->h_fit_g.data(), c->fit_g, sizeof(double) * H * 3 * d * d, hipMemcpyDeviceToHost, st));
-        SPR_HIP(c, hipStreamSynchronize(st));
+        const double* hm = c->h_fit;
+        const double* hg = c->h_fit + H * 2 * d;
         std::vector<int> frc(H, 0);
         parallel_heads((int)H, [&](int h) {
-            frc[h] = probe_fit_from_grams((int)P, (int)d, &c->h_fit_m[h * d], &c->h_fit_m[(H + h) * d],
-                                          &c->h_fit_g[h * d * d], &c->h_fit_g[(H + h) * d * d],
-                                          &c->h_fit_g[(2 * H + h) * d * d], c->p.ridge_lambda,
-                                          c->p.corr_rank, &c->h_bm[h * d * d], &c->h_bv[h * d]);
+            frc[h] = probe_fit_from_grams((int)P, (int)d, &hm[h * d], &hm[(H + h) * d], &hg[h * d * d],
+                                          &hg[(H + h) * d * d], &hg[(2 * H + h) * d * d],
+                                          c->p.ridge_lambda, c->p.corr_rank, &c->h_bm[h * d * d],
+                                          &c->h_bv[h * d]);
         });
         for (size_t h = 0; h < H; ++h)
             if (frc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "probe fit failed (non-finite probe outputs)");
     }
-    c->h_bm32.resize(H * d * d);
-    c->h_bv32.resize(H * d);
-    for (size_t i = 0; i < H * d * d; ++i) c->h_bm32[i] = (float)c->h_bm[i];
-    for (size_t i = 0; i < H * d; ++i) c->h_bv32[i] = (float)c->h_bv[i];
-    SPR_HIP(c, hipMemcpyAsync(c->bm32, c->h_bm32.data(), sizeof(float) * H * d * d, hipMemcpyHostToDevice, st));
-    SPR_HIP(c, hipMemcpyAsync(c->bv32, c->h_bv32.data(), sizeof(float) * H * d, hipMemcpyHostToDevice, st));
+    // (the previous call's upload from this buffer finished before ev_probe fired)
+    for (size_t i = 0; i < H * d * d; ++i) c->h_b32[i] = (float)c->h_bm[i];
+    for (size_t i = 0; i < H * d; ++i) c->h_b32[H * d * d + i] = (float)c->h_bv[i];
+    SPR_HIP(c, hipMemcpyAsync(c->bm32, c->h_b32, sizeof(float) * H * d * d, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->bv32, c->h_b32 + H * d * d, sizeof(float) * H * d, hipMemcpyHostToDevice, st));
     mark(c, 6, st);
     c->stage = kStageFit;
     return SPARSEPR_OK;
@@ -733,7 +756,7 @@ int32_t sparsepr_get_stats(sparsepr_ctx* c, sparsepr_stats* out) {
     }
     if (c->timing) {
         // average over the calls since the previous sparsepr_get_stats that the ring still holds
-        const int pairs_ev[6][2] = {{0, 1}, {2, 3}, {3, 4}, {4, 5}, {5, 6}, {6, 7}};
+        const int pairs_ev[6][2] = {{0, 1}, {2, 3}, {4, 5}, {3, 4}, {5, 6}, {6, 7}};
         const int64_t first = std::max(c->stats_from, c->calls - sparsepr_ctx::kRing);
         for (int i = 0; i < 6; ++i) {
             double sum = 0.0;

@@ -91,7 +91,9 @@ typedef struct {
     int32_t routed_k;          /* key groups kept per query group */
     int32_t query_dims;        /* dimension of the query k-means space */
     float   stage_ms[6];       /* mean ms per call of: partition, route, sparse attention kernel,
-                                  probe rows, probe fit, correction (SPARSEPR_F_STAGE_TIMING;
+                                  probe rows (with the fit Grams), probe fit (the part of the
+                                  host solve and upload not hidden behind the sparse kernel),
+                                  correction (SPARSEPR_F_STAGE_TIMING;
                                   averaged over the calls since the previous
                                   sparsepr_get_stats, at most the last 64) */
     int32_t timed_calls;       /* calls averaged into stage_ms */
@@ -128,11 +130,14 @@ int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void
 int32_t sparsepr_route(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
                        void* stream);
 
-/* 2C/2B. Block-sparse attention over the routed pairs (unrouted blocks are never
- * touched) and exact dense + routed attention of the probe rows. */
+/* 2C/2B. Exact dense + routed attention of the probe rows and the fit's fp64 Grams
+ * (copied to pinned host memory), then block-sparse attention over the routed pairs
+ * (unrouted blocks are never touched). Asynchronous: returns once both are enqueued. */
 int32_t sparsepr_sparse_attn(sparsepr_ctx* ctx, void* stream);
 
-/* 2B. Host-synchronising fp64 fit: B' = B Pi and b' = b Pi per head. */
+/* 2B. fp64 fit on the host: B' = B Pi and b' = b Pi per head. Waits only for the probe
+ * rows and Grams enqueued by sparsepr_sparse_attn, so the solve overlaps the sparse
+ * kernel; B' and b' are uploaded on `stream`. */
 int32_t sparsepr_probe_fit(sparsepr_ctx* ctx, void* stream);
 
 /* 2B. Writes o [H][n][d] (context dtype) in the original token order: unprobed rows
