@@ -22,8 +22,8 @@ void launch_fill_i64(int64_t* p, int64_t value, size_t count, hipStream_t st);
 void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64_t a, double* mk,
                    hipStream_t st);
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
-                           int groups, int64_t a, double* c64, bf16_t* cpart, float* cn2,
-                           float* cpn, hipStream_t st);
+                           int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
+                           float* cn2, float* cpn, hipStream_t st);
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st);

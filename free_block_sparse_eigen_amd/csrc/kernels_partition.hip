@@ -67,72 +67,103 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
 }
 
 // --------------------------------------------------------- centroid finish ---
-// For a raw-space centroid mean m (fp64, in LDS), with the metric factor L [d][D]:
+// For raw-space centroid means m (fp64), with the metric factor L [d][D]:
 //   projected centroid   c = m L          (fp64, used by the fp64 recheck)
 //   screening vector     C' = L c^T       (d-dim; x . C' = (x L) . c for any point x)
 //   split of C' into bf16 hi + lo parts   (the MFMA operand; |C' - hi - lo| <= 2^-17 |C'|)
 //   |c|^2 (fp32, nearest) and |C'| (fp32, rounded up) for the screening score and bound
-// The block needs blockDim >= max(d, D).
-__device__ void finish_centroid(const double* __restrict__ mean, double* __restrict__ cp_lds,
-                                const double* __restrict__ lh, int d, int dout, int groups,
-                                int h, int g, double* __restrict__ c64, bf16_t* __restrict__ cpart,
-                                float* __restrict__ cn2, float* __restrict__ cpn,
-                                double* __restrict__ red) {
-    const int tid = threadIdx.x;
-    double cv = 0.0;
-    if (tid < dout) {
-        for (int i = 0; i < d; ++i) cv += mean[i] * lh[(size_t)i * dout + tid];
-        cp_lds[tid] = cv;
-        c64[((size_t)h * groups + g) * dout + tid] = cv;
+// Block = 16 centroids of one head, so each element of L read from L2 serves 16 of
+// them. With `off` given, empty groups are skipped (they keep their previous centroid).
+constexpr int kFinG = 16;
+
+// fixed-order sum of v over the 64 lanes (butterfly; identical on every lane)
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_raw, int d,
+                                                const double* __restrict__ l64, int dout, int groups,
+                                                const int32_t* __restrict__ off,
+                                                double* __restrict__ c64, bf16_t* __restrict__ cpart,
+                                                float* __restrict__ cn2, float* __restrict__ cpn) {
+    __shared__ double s_m[kFinG][129];     // means (padded rows)
+    __shared__ double s_c[kFinG][129];     // projected centroids
+    __shared__ double s_s[kFinG][129];     // screening vectors
+    const int h = blockIdx.y, g0 = blockIdx.x * kFinG, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const double* lh = l64 + (size_t)h * d * dout;
+    for (int o = tid; o < kFinG * d; o += 256) {
+        const int gs = o / d, i = o % d, g = g0 + gs;
+        s_m[gs][i] = (g < groups) ? mean_raw[((size_t)h * groups + g) * d + i] : 0.0;
     }
     __syncthreads();
-    double sv = 0.0;
-    if (tid < d) {
-        for (int j = 0; j < dout; ++j) sv += lh[(size_t)tid * dout + j] * cp_lds[j];
-        const float hi = bf16_to_f32(f32_to_bf16((float)sv));
-        const bf16_t lo = f32_to_bf16((float)(sv - (double)hi));
-        cpart[((size_t)(h * 2 + 0) * groups + g) * d + tid] = f32_to_bf16((float)sv);
-        cpart[((size_t)(h * 2 + 1) * groups + g) * d + tid] = lo;
+    // c[gs][j] = sum_i m[gs][i] L[i][j]   (lanes along j: coalesced rows of L)
+    for (int o = tid; o < kFinG * dout; o += 256) {
+        const int gs = o / dout, j = o % dout;
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += s_m[gs][i] * lh[(size_t)i * dout + j];
+        s_c[gs][j] = acc;
     }
-    // norms: thread-strided partial sums, fixed-order reduction by thread 0
-    red[tid] = (tid < dout) ? cv * cv : 0.0;
-    red[blockDim.x + tid] = (tid < d) ? sv * sv : 0.0;
     __syncthreads();
-    if (tid == 0) {
+    // C'[gs][i] = sum_j L[i][j] c[gs][j]   (16 lanes share one element of L)
+    for (int o = tid; o < kFinG * d; o += 256) {
+        const int i = o / kFinG, gs = o % kFinG;
+        double acc = 0.0;
+        for (int j = 0; j < dout; ++j) acc += lh[(size_t)i * dout + j] * s_c[gs][j];
+        s_s[gs][i] = acc;
+    }
+    __syncthreads();
+    // one wave per centroid: stores and norms
+    for (int gs = w; gs < kFinG; gs += 4) {
+        const int g = g0 + gs;
+        if (g >= groups) break;
+        if (off != nullptr && off[(size_t)h * (groups + 1) + g + 1] == off[(size_t)h * (groups + 1) + g])
+            continue;                                   // empty: keep the previous centroid
         double a = 0.0, b = 0.0;
-        for (int i = 0; i < (int)blockDim.x; ++i) {
-            a += red[i];
-            b += red[blockDim.x + i];
+        for (int j = lane; j < dout; j += 64) {
+            const double cv = s_c[gs][j];
+            c64[((size_t)h * groups + g) * dout + j] = cv;
+            a += cv * cv;
         }
-        cn2[(size_t)h * groups + g] = (float)a;                      // nearest: enters the score
-        cpn[(size_t)h * groups + g] = (float)(sqrt(b) * (1.0 + 1e-6));  // rounded up: bound only
+        for (int i = lane; i < d; i += 64) {
+            const double sv = s_s[gs][i];
+            const bf16_t hi = f32_to_bf16((float)sv);
+            cpart[((size_t)(h * 2 + 0) * groups + g) * d + i] = hi;
+            cpart[((size_t)(h * 2 + 1) * groups + g) * d + i] = f32_to_bf16((float)(sv - (double)bf16_to_f32(hi)));
+            b += sv * sv;
+        }
+        a = wave_sum_f64(a);
+        b = wave_sum_f64(b);
+        if (lane == 0) {
+            cn2[(size_t)h * groups + g] = (float)a;                          // nearest: enters the score
+            cpn[(size_t)h * groups + g] = (float)(sqrt(b) * (1.0 + 1e-6));   // rounded up: bound only
+        }
     }
+}
+
+static void launch_finish(const double* mean_raw, int heads, int d, const double* l64, int dout,
+                          int groups, const int32_t* off, double* c64, bf16_t* cpart, float* cn2,
+                          float* cpn, hipStream_t st) {
+    hipLaunchKernelGGL(k_finish, dim3((groups + kFinG - 1) / kFinG, heads), dim3(256), 0, st, mean_raw,
+                       d, l64, dout, groups, off, c64, cpart, cn2, cpn);
 }
 
 // ------------------------------------------------------------------- seeds ---
-// Seed centroid g is the point at Weyl index (g a) mod n.
-__global__ __launch_bounds__(128) void k_seed(const bf16_t* __restrict__ x, int n, int d,
-                                              const double* __restrict__ l64, int dout, int groups,
-                                              int64_t a, double* __restrict__ c64,
-                                              bf16_t* __restrict__ cpart, float* __restrict__ cn2,
-                                              float* __restrict__ cpn) {
-    __shared__ double mean[128];
-    __shared__ double cp[128];
-    __shared__ double red[256];
+// Seed centroid g is the point at Weyl index (g a) mod n (written as the raw mean).
+__global__ __launch_bounds__(128) void k_seed(const bf16_t* __restrict__ x, int n, int d, int groups,
+                                              int64_t a, double* __restrict__ mean_raw) {
     const int h = blockIdx.y, g = blockIdx.x, j = threadIdx.x;
     const int64_t idx = ((int64_t)g * a) % n;
-    const bf16_t* row = x + ((size_t)h * n + idx) * d;
-    if (j < d) mean[j] = (double)bf16_to_f32(row[j]);
-    __syncthreads();
-    finish_centroid(mean, cp, l64 + (size_t)h * d * dout, d, dout, groups, h, g, c64, cpart, cn2,
-                    cpn, red);
+    if (j < d) mean_raw[((size_t)h * groups + g) * d + j] = (double)bf16_to_f32(x[((size_t)h * n + idx) * d + j]);
 }
 
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
-                           int groups, int64_t a, double* c64, bf16_t* cpart, float* cn2,
-                           float* cpn, hipStream_t st) {
-    hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, l64, dout, groups, a,
-                       c64, cpart, cn2, cpn);
+                           int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
+                           float* cn2, float* cpn, hipStream_t st) {
+    hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, groups, a, mean_raw);
+    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, st);
 }
 
 // ------------------------------------------------------------------ assign ---
@@ -142,37 +173,73 @@ void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const doubl
 // the raw rows (exact bf16) against the hi/lo split of C' with fp32 accumulation:
 //   |computed - exact| <= kappa |x| |C'_g|,  kappa = 2 d u (1 + 2^-8) + 2^-17  (u = 2^-24)
 // and the score s~_g = fl(|c_g|^2 - 2 S~_g) is within
-//   eps_g = 1.1 [2 kappa |x| |C'_g| + u |c_g|^2 + u |s~_g|]
-// of the exact s_g. The label is certified when every other centroid's lower end
-// s~_g - eps_g exceeds the best's upper end s~_best + eps_best; otherwise the point is
-// queued for the fp64 recheck (which also settles exact ties by the lowest index).
+//   e_g = 1.1 [2 kappa |x| |C'_g| + u |c_g|^2 + u |s~_g|] <= 1.1 [A + u |s~_g|],
+//   A = 2 kappa |x| max_g |C'_g| + u max_g |c_g|^2
+// of the exact s_g. Since s - 1.1 u |s| grows with s, every other centroid's lower end
+// is at least that of the runner-up, so the label is certified when
+//   s~_2nd - s~_best > 2.2 A + 1.1 u (|s~_2nd| + |s~_best|)
+// (checked with a further margin for the fp32 evaluation of the test itself);
+// otherwise the point is queued for the fp64 recheck, which also settles exact ties by
+// the lowest index. Each lane tracks only the best and runner-up scores.
 //
 // Block = 4 waves x 64 points; centroids stream through LDS in tiles of 64 (hi and lo
-// parts), 16-byte chunk c of centroid row r stored at c ^ swz(r).
+// parts, 16-byte chunk c of centroid row r at c ^ swz(r)), double-buffered and filled
+// by direct global-to-LDS loads. Padding centroids score +inf.
 template <int D>
-__global__ __launch_bounds__(256) void k_assign(const bf16_t* __restrict__ x, int n,
-                                                const bf16_t* __restrict__ cpart,
-                                                const float* __restrict__ cn2,
-                                                const float* __restrict__ cpn, int groups,
-                                                int32_t* __restrict__ labels,
-                                                int32_t* __restrict__ flag_count,
-                                                int32_t* __restrict__ flag_list) {
+__global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x, int n,
+                                                   const bf16_t* __restrict__ cpart,
+                                                   const float* __restrict__ cn2,
+                                                   const float* __restrict__ cpn, int groups,
+                                                   int32_t* __restrict__ labels,
+                                                   int32_t* __restrict__ flag_count,
+                                                   int32_t* __restrict__ flag_list) {
     constexpr int CH = D / 8;
     constexpr int TG = 64;
+    constexpr int SLOTS = 2 * TG * CH;         // 16-byte slots per tile (hi and lo)
+    constexpr int PER = SLOTS / 256;           // direct loads per thread per tile
     constexpr float kU = 5.9604644775390625e-08f;
     constexpr float kappa = 2.f * D * kU * 1.00390625f + 7.62939453125e-06f;
-    __shared__ uint4 s_c[2][TG * CH];
-    __shared__ float s_cn2[kMaxGroups];
-    __shared__ float s_cpn[kMaxGroups];
+    __shared__ uint4 s_c0[SLOTS];
+    __shared__ uint4 s_c1[SLOTS];
+    __shared__ float s_cn2[kMaxGroups + TG];
+    __shared__ float s_red[8];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5;
-    for (int g = tid; g < groups; g += 256) {
-        s_cn2[g] = cn2[(size_t)h * groups + g];
-        s_cpn[g] = cpn[(size_t)h * groups + g];
+    const int ntiles = (groups + TG - 1) / TG;
+    float c2m = 0.f, cpm = 0.f;
+    for (int g = tid; g < ntiles * TG; g += 256) {
+        float c2 = INFINITY;
+        if (g < groups) {
+            c2 = cn2[(size_t)h * groups + g];
+            c2m = fmaxf(c2m, c2);
+            cpm = fmaxf(cpm, cpn[(size_t)h * groups + g]);
+        }
+        s_cn2[g] = c2;
     }
+    c2m = wave_max(c2m);
+    cpm = wave_max(cpm);
+    if (lane == 0) {
+        s_red[w] = c2m;
+        s_red[4 + w] = cpm;
+    }
+    const bf16_t* ch = cpart + (size_t)h * 2 * groups * D;
+    auto issue = [&](int t, uint4* buf) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int first = (w * PER + m) * 64;
+            const int slot = first + lane;
+            const int part = slot / (TG * CH), rem = slot % (TG * CH);
+            const int row = rem / CH, pc = rem % CH;
+            const int g = min(t * TG + row, groups - 1);
+            const bf16_t* src = ch + ((size_t)part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8);
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + first), 16, 0, 0);
+        }
+    };
+    issue(0, s_c0);
+    // this wave's 64 points as MFMA B fragments, and their norms
     const int p_base = blockIdx.x * 256 + w * 64;
     uint4 xf[2][D / 16];
-    float kx[2];
+    float xn[2];
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
         const int pt = p_base + 32 * pb + (lane & 31);
@@ -193,80 +260,73 @@ __global__ __launch_bounds__(256) void k_assign(const bf16_t* __restrict__ x, in
             }
         }
         ss += __shfl_xor(ss, 32, 64);
-        kx[pb] = 1.1f * 2.f * kappa * sqrtf(ss) * 1.000001f;
+        xn[pb] = sqrtf(ss) * 1.000001f;
     }
-    constexpr float ku = 1.1f * kU;
-    float best[2] = {INFINITY, INFINITY}, eb[2] = {0.f, 0.f}, low2[2] = {INFINITY, INFINITY};
+    float best[2] = {INFINITY, INFINITY}, second[2] = {INFINITY, INFINITY};
     int bg[2] = {0x7fffffff, 0x7fffffff};
-    for (int g0 = 0; g0 < groups; g0 += TG) {
-        __syncthreads();
-        for (int i = tid; i < 2 * TG * CH; i += 256) {
-            const int part = i / (TG * CH), rem = i % (TG * CH);
-            const int row = rem / CH, c = rem % CH;
-            const int g = g0 + row;
-            s_c[part][row * CH + (c ^ swz<CH>(row))] =
-                (g < groups) ? *reinterpret_cast<const uint4*>(
-                                   cpart + ((size_t)(h * 2 + part) * groups + g) * D + c * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
-        __syncthreads();
+    auto compute = [&](int t, const uint4* buf) {
 #pragma unroll
         for (int sub = 0; sub < TG / 32; ++sub) {
-            const int gb = g0 + 32 * sub;
+            const int gb = t * TG + 32 * sub;
             if (gb >= groups) break;
             f32x16 acc[2] = {};
+            const int row = 32 * sub + (lane & 31);
 #pragma unroll
             for (int part = 0; part < 2; ++part)
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
-                    const uint4 a =
-                        s_c[part][(32 * sub + (lane & 31)) * CH + ((2 * kk + half) ^ swz<CH>(lane & 31))];
+                    const uint4 a = buf[part * TG * CH + row * CH + ((2 * kk + half) ^ swz<CH>(row))];
                     acc[0] = mfma32x32x16(a, xf[0][kk], acc[0]);
                     acc[1] = mfma32x32x16(a, xf[1][kk], acc[1]);
                 }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int g = gb + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (g < groups) {
-                    const float c2 = s_cn2[g], cp = s_cpn[g];
+                const float c2 = s_cn2[g];
 #pragma unroll
-                    for (int pb = 0; pb < 2; ++pb) {
-                        const float v = fmaf(-2.f, acc[pb][r], c2);
-                        const float e = fmaf(kx[pb], cp, ku * (c2 + fabsf(v))) + 1e-30f;
-                        if (v < best[pb]) {
-                            low2[pb] = fminf(low2[pb], best[pb] - eb[pb]);
-                            best[pb] = v;
-                            eb[pb] = e;
-                            bg[pb] = g;
-                        } else {
-                            low2[pb] = fminf(low2[pb], v - e);
-                        }
-                    }
+                for (int pb = 0; pb < 2; ++pb) {
+                    const float v = fmaf(-2.f, acc[pb][r], c2);
+                    second[pb] = fminf(second[pb], fmaxf(best[pb], v));
+                    bg[pb] = (v < best[pb]) ? g : bg[pb];
+                    best[pb] = fminf(best[pb], v);
                 }
             }
         }
+    };
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles) issue(t + 1, s_c1);
+        compute(t, s_c0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 >= ntiles) break;
+        if (t + 2 < ntiles) issue(t + 2, s_c0);
+        compute(t + 1, s_c1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
+    const float c2max = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float cpmax = fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7]));
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
-        // merge the two lane halves: best by (value, index); the other best joins low2
+        // merge the two lane halves: best by (value, index); the other best joins second
         const float ob = __shfl_xor(best[pb], 32, 64);
-        const float oe = __shfl_xor(eb[pb], 32, 64);
-        const float ol = __shfl_xor(low2[pb], 32, 64);
+        const float os = __shfl_xor(second[pb], 32, 64);
         const int og = __shfl_xor(bg[pb], 32, 64);
-        float b = best[pb], e = eb[pb], l2 = fminf(low2[pb], ol);
+        float b = best[pb];
         int gsel = bg[pb];
+        const float s2 = fminf(fminf(second[pb], os), fmaxf(b, ob));
         if (ob < b || (ob == b && og < gsel)) {
-            l2 = fminf(l2, b - e);
             b = ob;
-            e = oe;
             gsel = og;
-        } else {
-            l2 = fminf(l2, ob - oe);
         }
+        const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
+        const float bound = 2.4f * A + 2.4f * kU * (fabsf(s2) + fabsf(b)) + 1e-30f;
         const int pt = p_base + 32 * pb + lane;
         if (lane < 32 && pt < n) {
             labels[(size_t)h * n + pt] = gsel;
-            if (groups > 1 && !(l2 > b + e)) {
+            if (!(s2 - b > bound)) {
                 const int slot = atomicAdd(&flag_count[h], 1);
                 flag_list[(size_t)h * n + slot] = pt;
             }
@@ -444,22 +504,20 @@ void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, i
 }
 
 // -------------------------------------------------------------- group means ---
-// Block per (group, head): fp64 sum of the members' raw rows in sorted order (fixed
-// split over row lanes, fixed-order reduction), mean = sum / count (zero if empty).
-// With l64 given, a non-empty group also gets its projected centroid, screening vector
-// and norms (an empty group keeps its previous centroid).
-__global__ __launch_bounds__(256) void k_group_means(
-    const bf16_t* __restrict__ x, int n, int d, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ off, int groups, double* __restrict__ mean_raw,
-    const double* __restrict__ l64, int dout, double* __restrict__ c64,
-    bf16_t* __restrict__ cpart, float* __restrict__ cn2, float* __restrict__ cpn) {
-    __shared__ double red[256 * 8];
-    __shared__ double mean[128];
-    __shared__ double cp[128];
+// Block per (group, head): fp64 sum of the members' raw rows in sorted order, over a
+// fixed split of rows to row lanes (four rows in flight per lane) and a fixed-order
+// reduction; mean = sum / count (zero if empty). With l64 given, the non-empty groups
+// then get their projected centroid, screening vector and norms (k_finish).
+template <int D>
+__global__ __launch_bounds__(256) void k_group_sum(const bf16_t* __restrict__ x, int n,
+                                                   const int32_t* __restrict__ sorted,
+                                                   const int32_t* __restrict__ off, int groups,
+                                                   double* __restrict__ mean_raw) {
+    constexpr int CH = D / 8;          // 16-byte chunks per row
+    constexpr int RL = 256 / CH;       // row lanes
+    __shared__ double red[RL][D + 1];
     const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
-    const int chunks = d / 8;
-    const int lanes = 256 / chunks;
-    const int c = tid % chunks, rl = tid / chunks;
+    const int c = tid % CH, rl = tid / CH;
     const int32_t* oh = off + (size_t)h * (groups + 1);
     const int beg = oh[g], end = oh[g + 1];
     const int cnt = end - beg;
@@ -467,38 +525,51 @@ __global__ __launch_bounds__(256) void k_group_means(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     const int32_t* sh = sorted + (size_t)h * n;
-    const bf16_t* xh = x + (size_t)h * n * d;
-    for (int m = beg + rl; m < end; m += lanes) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xh + (size_t)sh[m] * d + c * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const bf16_t* xh = x + (size_t)h * n * D + c * 8;
+    auto add = [&](const uint4 v) {
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += (double)bf16_to_f32((bf16_t)(w[e] & 0xFFFF));
-            acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(w[e] >> 16));
+            acc[2 * e] += (double)bf16_to_f32((bf16_t)(wd[e] & 0xFFFF));
+            acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(wd[e] >> 16));
         }
+    };
+    int m = beg + rl;
+    for (; m + 3 * RL < end; m += 4 * RL) {
+        const int i0 = sh[m], i1 = sh[m + RL], i2 = sh[m + 2 * RL], i3 = sh[m + 3 * RL];
+        const uint4 v0 = *reinterpret_cast<const uint4*>(xh + (size_t)i0 * D);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(xh + (size_t)i1 * D);
+        const uint4 v2 = *reinterpret_cast<const uint4*>(xh + (size_t)i2 * D);
+        const uint4 v3 = *reinterpret_cast<const uint4*>(xh + (size_t)i3 * D);
+        add(v0);
+        add(v1);
+        add(v2);
+        add(v3);
     }
+    for (; m < end; m += RL) add(*reinterpret_cast<const uint4*>(xh + (size_t)sh[m] * D));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[(size_t)rl * d + c * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) red[rl][c * 8 + e] = acc[e];
     __syncthreads();
-    if (tid < d) {
+    if (tid < D) {
         double s = 0.0;
-        for (int r = 0; r < lanes; ++r) s += red[(size_t)r * d + tid];
-        const double mv = (cnt > 0) ? s / cnt : 0.0;
-        mean[tid] = mv;
-        mean_raw[((size_t)h * groups + g) * d + tid] = mv;
+#pragma unroll
+        for (int r = 0; r < RL; ++r) s += red[r][tid];
+        mean_raw[((size_t)h * groups + g) * D + tid] = (cnt > 0) ? s / cnt : 0.0;
     }
-    __syncthreads();
-    if (l64 == nullptr || cnt == 0) return;           // empty: keep the previous centroid
-    finish_centroid(mean, cp, l64 + (size_t)h * d * dout, d, dout, groups, h, g, c64, cpart, cn2,
-                    cpn, red);
 }
 
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
                         hipStream_t st) {
-    hipLaunchKernelGGL(k_group_means, dim3(groups, heads), dim3(256), 0, st, x, n, d, sorted, off,
-                       groups, mean_raw, l64, dout, c64, cpart, cn2, cpn);
+    if (d == 128)
+        hipLaunchKernelGGL(k_group_sum<128>, dim3(groups, heads), dim3(256), 0, st, x, n, sorted, off,
+                           groups, mean_raw);
+    else
+        hipLaunchKernelGGL(k_group_sum<64>, dim3(groups, heads), dim3(256), 0, st, x, n, sorted, off,
+                           groups, mean_raw);
+    if (l64 != nullptr)
+        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, st);
 }
 
 }  // namespace spr
