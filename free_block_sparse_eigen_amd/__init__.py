@@ -62,7 +62,7 @@ class Stats(ctypes.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m free_block_sparse_eigen_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python free_block_sparse_eigen_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

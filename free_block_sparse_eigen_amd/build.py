@@ -1,6 +1,6 @@
 """Build libsparsepr.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m free_block_sparse_eigen_amd.build   (or build() from Python)
+Usage: python free_block_sparse_eigen_amd/build.py   (or __graft_entry__.build())
 """
 from __future__ import annotations
 
@@ -16,11 +16,19 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparsepr.so")
 SOURCES = ["api.cpp", "host_linalg.cpp", "kernels_partition.hip", "kernels_route.hip",
            "kernels_attn.hip", "kernels_correct.hip"]
+HOST_ONLY = {"host_linalg.cpp"}       # plain C++ (no HIP): built by the host compiler alone
 ARCH = os.environ.get("SPARSEPR_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # no packed-fp32 instructions in any device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
+
+
+def _host_cxx() -> str:
+    for cand in (shutil.which("g++"), "/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
 
 
 def _hipcc() -> str:
@@ -40,7 +48,10 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src in HOST_ONLY:
+            cmd = [_host_cxx(), "-O3", "-std=c++17", "-fPIC", "-c", os.path.join(CSRC, src), "-o", obj]
+        else:
+            cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         msg = _quiet(r.stdout + r.stderr)
         if r.returncode != 0:

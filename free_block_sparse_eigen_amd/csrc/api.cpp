@@ -203,7 +203,7 @@ void layout(sparsepr_ctx& c, Arena& a) {
 
 void parallel_heads(int heads, const std::function<void(int)>& fn) {
     const int hw = std::max(1u, std::thread::hardware_concurrency());
-    const int nt = std::min(heads, std::min(hw, 32));
+    const int nt = std::min(heads, std::min(hw, 16));
     if (nt <= 1) {
         for (int h = 0; h < heads; ++h) fn(h);
         return;

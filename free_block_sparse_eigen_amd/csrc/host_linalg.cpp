@@ -23,6 +23,14 @@ namespace {
 
 constexpr double kEps = std::numeric_limits<double>::epsilon();
 
+// The O(n^3) loops are written once (always inlined) and built twice: for AVX2 + FMA and
+// for baseline x86-64; the AVX2 build runs when the CPU reports both features.
+#define SPR_BODY static inline __attribute__((always_inline))
+bool cpu_avx2_fma() {
+    static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
+    return ok;
+}
+
 struct Tridiag {
     int n = 0;
     std::vector<double> diag, off;     // off[i] couples rows i and i+1
@@ -31,74 +39,105 @@ struct Tridiag {
 };
 
 // A = Q T Q^T with Q = H_0 H_1 ... H_{n-3}, H_k = I - beta_k v_k v_k^T acting on rows k+1..n-1.
-void tridiagonalize(int n, const double* a_in, Tridiag& t) {
-    t.n = n;
-    t.diag.assign(n, 0.0);
-    t.off.assign(std::max(n - 1, 0), 0.0);
-    t.hv.assign(static_cast<size_t>(n) * n, 0.0);
-    t.hbeta.assign(n, 0.0);
-    std::vector<double> a(a_in, a_in + static_cast<size_t>(n) * n);
-    std::vector<double> p(n), w(n);
+// Works on the lower triangle only (row i holds columns 0..i).
+// Raw-pointer core (a is overwritten; p, w are scratch of length n).
+SPR_BODY void tridiag_body(int n, double* a, double* diag, double* off, double* hv,
+                           double* hbeta, double* p, double* w) {
+    auto A = [&](int i, int j) -> double& { return a[static_cast<size_t>(i) * n + j]; };   // i >= j
     for (int k = 0; k + 2 < n; ++k) {
-        const int m = n - k - 1;
-        double* v = &t.hv[static_cast<size_t>(k) * n];
+        const int m = n - k - 1, o = k + 1;
+        double* v = &hv[static_cast<size_t>(k) * n];
         double sigma2 = 0.0;
         for (int i = 0; i < m; ++i) {
-            v[i] = a[static_cast<size_t>(k + 1 + i) * n + k];
+            v[i] = A(o + i, k);
             sigma2 += v[i] * v[i];
         }
-        double tail2 = sigma2 - v[0] * v[0];
+        const double tail2 = sigma2 - v[0] * v[0];
         if (tail2 <= 0.0) {            // already tridiagonal in this column
-            t.off[k] = v[0];
-            t.hbeta[k] = 0.0;
+            off[k] = v[0];
+            hbeta[k] = 0.0;
             continue;
         }
         const double sigma = std::sqrt(sigma2);
         const double alpha = (v[0] >= 0.0) ? -sigma : sigma;
         v[0] -= alpha;
-        const double vtv = tail2 + v[0] * v[0];
-        const double beta = 2.0 / vtv;
-        t.hbeta[k] = beta;
-        t.off[k] = alpha;
-        // p = beta * A22 v
+        const double beta = 2.0 / (tail2 + v[0] * v[0]);
+        hbeta[k] = beta;
+        off[k] = alpha;
+        // p = beta * A22 v from the lower triangle: row i contributes a_ij v_j (j < i)
+        // to p_i and a_ij v_i to p_j
+        for (int i = 0; i < m; ++i) p[i] = 0.0;
         for (int i = 0; i < m; ++i) {
-            const double* row = &a[static_cast<size_t>(k + 1 + i) * n + (k + 1)];
-            double s = 0.0;
-            for (int j = 0; j < m; ++j) s += row[j] * v[j];
-            p[i] = beta * s;
+            const double* row = &A(o + i, o);
+            const double vi = v[i];
+            double s4[4] = {0.0, 0.0, 0.0, 0.0};   // fixed-order partial sums (vectorisable)
+            int j = 0;
+            for (; j + 4 <= i; j += 4)
+                for (int e = 0; e < 4; ++e) {
+                    s4[e] += row[j + e] * v[j + e];
+                    p[j + e] += row[j + e] * vi;
+                }
+            for (; j < i; ++j) {
+                s4[0] += row[j] * v[j];
+                p[j] += row[j] * vi;
+            }
+            p[i] += ((s4[0] + s4[1]) + (s4[2] + s4[3])) + row[i] * vi;
         }
         double kk = 0.0;
-        for (int i = 0; i < m; ++i) kk += v[i] * p[i];
+        for (int i = 0; i < m; ++i) {
+            p[i] *= beta;
+            kk += v[i] * p[i];
+        }
         kk *= 0.5 * beta;
         for (int i = 0; i < m; ++i) w[i] = p[i] - kk * v[i];
         for (int i = 0; i < m; ++i) {
-            double* row = &a[static_cast<size_t>(k + 1 + i) * n + (k + 1)];
-            for (int j = 0; j < m; ++j) row[j] -= v[i] * w[j] + w[i] * v[j];
+            double* row = &A(o + i, o);
+            const double vi = v[i], wi = w[i];
+            for (int j = 0; j <= i; ++j) row[j] -= vi * w[j] + wi * v[j];
         }
     }
-    for (int i = 0; i < n; ++i) t.diag[i] = a[static_cast<size_t>(i) * n + i];
-    if (n >= 2) t.off[n - 2] = a[static_cast<size_t>(n - 1) * n + (n - 2)];
+    for (int i = 0; i < n; ++i) diag[i] = A(i, i);
+    if (n >= 2) off[n - 2] = A(n - 1, n - 2);
+}
+
+#define SPR_TWO_BUILDS(name, body, params, args)                                         \
+    __attribute__((target("avx2,fma"))) void name##_avx2 params { body args; }           \
+    void name##_base params { body args; }                                               \
+    void name params {                                                                   \
+        if (cpu_avx2_fma()) name##_avx2 args; else name##_base args;                     \
+    }
+SPR_TWO_BUILDS(tridiag_core, tridiag_body,
+               (int n, double* a, double* diag, double* off, double* hv, double* hbeta, double* p, double* w),
+               (n, a, diag, off, hv, hbeta, p, w))
+
+void tridiagonalize(int n, const double* a_in, Tridiag& t) {
+    t.n = n;
+    t.diag.assign(n, 0.0);
+    t.off.assign(std::max(n - 1, 1), 0.0);
+    t.hv.assign(static_cast<size_t>(n) * n, 0.0);
+    t.hbeta.assign(n, 0.0);
+    std::vector<double> a(a_in, a_in + static_cast<size_t>(n) * n), p(n), w(n);
+    tridiag_core(n, a.data(), t.diag.data(), t.off.data(), t.hv.data(), t.hbeta.data(), p.data(), w.data());
 }
 
 // Eigenvalues of ascending ranks first .. first+count-1 by bisection on Sturm counts, all
-// intervals advanced together so that the per-eigenvalue recurrences interleave.
-void bisect_eigenvalues(const Tridiag& t, int first, int count, double lo0, double hi0,
-                        double pivmin, double* out) {
-    std::vector<double> lo(count, lo0), hi(count, hi0), q(count), mid(count);
-    std::vector<int> cnt(count);
+// intervals advanced together so that the per-eigenvalue recurrences interleave. Stops
+// at a relative width of `rtol` (the caller polishes with Rayleigh quotients).
+SPR_BODY void bisect_body(int n, const double* diag, const double* e2, int first, int count,
+                          double* lo, double* hi, double* q, double* mid, int* cnt, double pivmin,
+                          double rtol) {
     for (int it = 0; it < 80; ++it) {
         for (int j = 0; j < count; ++j) mid[j] = 0.5 * (lo[j] + hi[j]);
         for (int j = 0; j < count; ++j) {
-            double v = t.diag[0] - mid[j];
+            double v = diag[0] - mid[j];
             if (std::fabs(v) < pivmin) v = -pivmin;
             q[j] = v;
             cnt[j] = v < 0 ? 1 : 0;
         }
-        for (int i = 1; i < t.n; ++i) {
-            const double e2 = t.off[i - 1] * t.off[i - 1];
-            const double di = t.diag[i];
+        for (int i = 1; i < n; ++i) {
+            const double ei = e2[i], di = diag[i];
             for (int j = 0; j < count; ++j) {
-                double v = (di - mid[j]) - e2 / q[j];
+                double v = (di - mid[j]) - ei / q[j];
                 if (std::fabs(v) < pivmin) v = -pivmin;
                 q[j] = v;
                 cnt[j] += v < 0 ? 1 : 0;
@@ -107,77 +146,115 @@ void bisect_eigenvalues(const Tridiag& t, int first, int count, double lo0, doub
         bool done = true;
         for (int j = 0; j < count; ++j) {
             if (cnt[j] > first + j) hi[j] = mid[j]; else lo[j] = mid[j];
-            if (hi[j] - lo[j] > 2.0 * kEps * std::max(std::fabs(lo[j]), std::fabs(hi[j])) + pivmin)
+            if (hi[j] - lo[j] > rtol * std::max(std::fabs(lo[j]), std::fabs(hi[j])) + pivmin)
                 done = false;
         }
         if (done) break;
     }
+}
+
+SPR_TWO_BUILDS(bisect_core, bisect_body,
+               (int n, const double* diag, const double* e2, int first, int count, double* lo, double* hi,
+                double* q, double* mid, int* cnt, double pivmin, double rtol),
+               (n, diag, e2, first, count, lo, hi, q, mid, cnt, pivmin, rtol))
+
+void bisect_eigenvalues(const Tridiag& t, int first, int count, double lo0, double hi0,
+                        double pivmin, double rtol, double* out) {
+    std::vector<double> lo(count, lo0), hi(count, hi0), q(count), mid(count), e2(t.n, 0.0);
+    std::vector<int> cnt(count);
+    for (int i = 1; i < t.n; ++i) e2[i] = t.off[i - 1] * t.off[i - 1];
+    bisect_core(t.n, t.diag.data(), e2.data(), first, count, lo.data(), hi.data(), q.data(),
+                mid.data(), cnt.data(), pivmin, rtol);
     for (int j = 0; j < count; ++j) out[j] = 0.5 * (lo[j] + hi[j]);
 }
 
-// Solve (T - lambda I) y = b in place with Gaussian elimination and partial pivoting;
-// zero pivots are replaced by `tiny` (inverse iteration wants the near-singular solve).
-void tridiag_shifted_solve(const Tridiag& t, double lambda, double tiny, std::vector<double>& y) {
-    const int n = t.n;
-    // U has a diagonal, first and second super-diagonal; L multipliers with row swaps.
-    std::vector<double> u0(n), u1(n, 0.0), u2(n, 0.0), mult(n, 0.0);
-    std::vector<char> swapped(n, 0);
-    // current row i content: cur0 at col i, cur1 at col i+1
-    double cur0 = t.diag[0] - lambda;
-    double cur1 = (n > 1) ? t.off[0] : 0.0;
-    for (int i = 0; i < n - 1; ++i) {
-        const double nl = t.off[i];                                   // row i+1, col i
-        const double nd = t.diag[i + 1] - lambda;                      // row i+1, col i+1
-        const double nc = (i + 2 < n) ? t.off[i + 1] : 0.0;           // row i+1, col i+2
-        if (std::fabs(nl) > std::fabs(cur0)) {
-            // swap: pivot row is row i+1
-            swapped[i] = 1;
-            u0[i] = nl;
-            u1[i] = nd;
-            u2[i] = nc;
-            const double m = cur0 / nl;
-            mult[i] = m;
-            cur0 = cur1 - m * nd;
-            cur1 = -m * nc;
-        } else {
-            if (cur0 == 0.0) cur0 = tiny;
-            u0[i] = cur0;
-            u1[i] = cur1;
-            u2[i] = 0.0;
-            const double m = nl / cur0;
-            mult[i] = m;
-            cur0 = nd - m * cur1;
-            cur1 = nc;
+// Back-transform X = H_0 (H_1 (... H_{n-3} Y)) for r vectors at once (x [n][r]; sv scratch [r]).
+SPR_BODY void back_transform_body(int n, int r, const double* hv, const double* hbeta, double* x,
+                                  double* sv) {
+    for (int k = n - 3; k >= 0; --k) {
+        const double beta = hbeta[k];
+        if (beta == 0.0) continue;
+        const double* v = &hv[static_cast<size_t>(k) * n];
+        const int m = n - k - 1;
+        for (int j = 0; j < r; ++j) sv[j] = 0.0;
+        for (int i = 0; i < m; ++i) {
+            const double vi = v[i];
+            const double* xr = &x[static_cast<size_t>(k + 1 + i) * r];
+            for (int j = 0; j < r; ++j) sv[j] += vi * xr[j];
         }
-    }
-    if (cur0 == 0.0) cur0 = tiny;
-    u0[n - 1] = cur0;
-    // forward: apply the same swaps and multipliers to y
-    for (int i = 0; i < n - 1; ++i) {
-        if (swapped[i]) {
-            const double a = y[i], b = y[i + 1];
-            y[i] = b;
-            y[i + 1] = a - mult[i] * b;
-        } else {
-            y[i + 1] -= mult[i] * y[i];
+        for (int j = 0; j < r; ++j) sv[j] *= beta;
+        for (int i = 0; i < m; ++i) {
+            const double vi = v[i];
+            double* xr = &x[static_cast<size_t>(k + 1 + i) * r];
+            for (int j = 0; j < r; ++j) xr[j] -= sv[j] * vi;
         }
-    }
-    // back substitution
-    for (int i = n - 1; i >= 0; --i) {
-        double s = y[i];
-        if (i + 1 < n) s -= u1[i] * y[i + 1];
-        if (i + 2 < n) s -= u2[i] * y[i + 2];
-        double piv = u0[i];
-        if (piv == 0.0) piv = tiny;
-        y[i] = s / piv;
     }
 }
 
-double norm2(const std::vector<double>& x) {
-    double s = 0.0;
-    for (double v : x) s += v * v;
-    return std::sqrt(s);
-}
+SPR_TWO_BUILDS(back_transform_core, back_transform_body,
+               (int n, int r, const double* hv, const double* hbeta, double* x, double* sv),
+               (n, r, hv, hbeta, x, sv))
+
+// LU factorisation (partial pivoting) of T - lambda I, reused for several solves; zero
+// pivots are replaced by `tiny` (inverse iteration wants the near-singular solve).
+struct ShiftedLU {
+    std::vector<double> u0, u1, u2, mult, rinv;
+    std::vector<char> swapped;
+    void factor(const Tridiag& t, double lambda, double tiny) {
+        const int n = t.n;
+        u0.assign(n, 0.0);
+        u1.assign(n, 0.0);
+        u2.assign(n, 0.0);
+        mult.assign(n, 0.0);
+        swapped.assign(n, 0);
+        double cur0 = t.diag[0] - lambda;                  // current row: col i, col i+1
+        double cur1 = (n > 1) ? t.off[0] : 0.0;
+        for (int i = 0; i < n - 1; ++i) {
+            const double nl = t.off[i];                                   // row i+1, col i
+            const double nd = t.diag[i + 1] - lambda;                      // row i+1, col i+1
+            const double nc = (i + 2 < n) ? t.off[i + 1] : 0.0;           // row i+1, col i+2
+            if (std::fabs(nl) > std::fabs(cur0)) {
+                swapped[i] = 1;                                           // pivot row is i+1
+                u0[i] = nl;
+                u1[i] = nd;
+                u2[i] = nc;
+                const double m = cur0 / nl;
+                mult[i] = m;
+                cur0 = cur1 - m * nd;
+                cur1 = -m * nc;
+            } else {
+                if (cur0 == 0.0) cur0 = tiny;
+                u0[i] = cur0;
+                u1[i] = cur1;
+                const double m = nl / cur0;
+                mult[i] = m;
+                cur0 = nd - m * cur1;
+                cur1 = nc;
+            }
+        }
+        if (cur0 == 0.0) cur0 = tiny;
+        u0[n - 1] = cur0;
+        rinv.resize(n);
+        for (int i = 0; i < n; ++i) rinv[i] = 1.0 / u0[i];
+    }
+    void solve(double* y, int n) const {
+        for (int i = 0; i < n - 1; ++i) {
+            if (swapped[i]) {
+                const double a = y[i], b = y[i + 1];
+                y[i] = b;
+                y[i + 1] = a - mult[i] * b;
+            } else {
+                y[i + 1] -= mult[i] * y[i];
+            }
+        }
+        for (int i = n - 1; i >= 0; --i) {
+            double s = y[i];
+            if (i + 1 < n) s -= u1[i] * y[i + 1];
+            if (i + 2 < n) s -= u2[i] * y[i + 2];
+            y[i] = s * rinv[i];
+        }
+    }
+};
 
 }  // namespace
 
@@ -213,25 +290,28 @@ int sym_eig_top(int n, const double* a, int r, double* lam, double* vec) {
     const double pad = 2.0 * kEps * tnorm * n + pivmin;
     glo -= pad;
     ghi += pad;
-    // eigenvalues, descending: the j-th largest is ascending rank n-1-j
+    // eigenvalues, descending: the j-th largest is ascending rank n-1-j. Bisection to a
+    // relative width of 2^-30 (the shift of inverse iteration), then each eigenvalue is
+    // replaced by the Rayleigh quotient of its converged eigenvector.
     {
         std::vector<double> asc(r);
-        bisect_eigenvalues(t, n - r, r, glo, ghi, pivmin, asc.data());
+        bisect_eigenvalues(t, n - r, r, glo, ghi, pivmin, std::ldexp(1.0, -30), asc.data());
         for (int j = 0; j < r; ++j) lam[j] = asc[r - 1 - j];
     }
 
-    // eigenvectors of T by inverse iteration
+    // eigenvectors of T by inverse iteration (one factorisation, three solves each)
     const double tiny = kEps * tnorm;
+    const double sep = std::ldexp(1.0, -28) * tnorm;  // shifts closer than this are split
     const double cluster_tol = 1e-3 * tnorm;
-    std::vector<std::vector<double>> ys(r, std::vector<double>(n));
-    std::vector<double> y(n);
+    std::vector<double> ys(static_cast<size_t>(r) * n);
+    ShiftedLU lu;
     double prev_shift = 0.0;
     for (int j = 0; j < r; ++j) {
         double shift = lam[j];
-        if (j > 0 && std::fabs(shift - lam[j - 1]) < 10.0 * tiny) {
-            shift = prev_shift - 10.0 * tiny;   // separate equal eigenvalues (descending)
-        }
+        if (j > 0 && prev_shift - shift < sep) shift = prev_shift - sep;   // keep shifts apart
         prev_shift = shift;
+        lu.factor(t, shift, tiny);
+        double* y = &ys[static_cast<size_t>(j) * n];
         // deterministic start vector with all components non-zero
         for (int i = 0; i < n; ++i) {
             const uint32_t h = (static_cast<uint32_t>(i) + 1u) * 2654435761u ^ (static_cast<uint32_t>(j) + 7u) * 40503u;
@@ -240,35 +320,40 @@ int sym_eig_top(int n, const double* a, int r, double* lam, double* vec) {
         int first_in_cluster = j;
         while (first_in_cluster > 0 && std::fabs(lam[first_in_cluster - 1] - lam[j]) < cluster_tol)
             --first_in_cluster;
-        for (int it = 0; it < 5; ++it) {
-            const double nb = norm2(y);
-            for (double& v : y) v /= nb;
-            tridiag_shifted_solve(t, shift, tiny, y);
+        for (int it = 0; it < 3; ++it) {
+            double nb = 0.0;
+            for (int i = 0; i < n; ++i) nb += y[i] * y[i];
+            nb = 1.0 / std::sqrt(nb);
+            for (int i = 0; i < n; ++i) y[i] *= nb;
+            lu.solve(y, n);
             for (int c = first_in_cluster; c < j; ++c) {     // re-orthogonalise in the cluster
+                const double* yc = &ys[static_cast<size_t>(c) * n];
                 double dot = 0.0;
-                for (int i = 0; i < n; ++i) dot += y[i] * ys[c][i];
-                for (int i = 0; i < n; ++i) y[i] -= dot * ys[c][i];
+                for (int i = 0; i < n; ++i) dot += y[i] * yc[i];
+                for (int i = 0; i < n; ++i) y[i] -= dot * yc[i];
             }
         }
-        const double ny = norm2(y);
+        double ny = 0.0;
+        for (int i = 0; i < n; ++i) ny += y[i] * y[i];
+        ny = std::sqrt(ny);
         if (!(ny > 0.0) || !std::isfinite(ny)) return -3;
-        for (int i = 0; i < n; ++i) ys[j][i] = y[i] / ny;
-    }
-    // back-transform: x = H_0 (H_1 (... H_{n-3} y))
-    for (int j = 0; j < r; ++j) {
-        std::vector<double>& x = ys[j];
-        for (int k = n - 3; k >= 0; --k) {
-            const double beta = t.hbeta[k];
-            if (beta == 0.0) continue;
-            const double* v = &t.hv[static_cast<size_t>(k) * n];
-            const int m = n - k - 1;
-            double s = 0.0;
-            for (int i = 0; i < m; ++i) s += v[i] * x[k + 1 + i];
-            s *= beta;
-            for (int i = 0; i < m; ++i) x[k + 1 + i] -= s * v[i];
+        for (int i = 0; i < n; ++i) y[i] /= ny;
+        // Rayleigh quotient y^T T y
+        double rq = 0.0;
+        for (int i = 0; i < n; ++i) {
+            double ty = t.diag[i] * y[i];
+            if (i > 0) ty += t.off[i - 1] * y[i - 1];
+            if (i + 1 < n) ty += t.off[i] * y[i + 1];
+            rq += y[i] * ty;
         }
-        for (int i = 0; i < n; ++i) vec[static_cast<size_t>(i) * r + j] = x[i];
+        lam[j] = rq;
     }
+    // back-transform X = H_0 (H_1 (... H_{n-3} Y)) for all r vectors at once (X [n][r])
+    std::vector<double> xs(static_cast<size_t>(n) * r), sv(r);
+    for (int j = 0; j < r; ++j)
+        for (int i = 0; i < n; ++i) xs[static_cast<size_t>(i) * r + j] = ys[static_cast<size_t>(j) * n + i];
+    back_transform_core(n, r, t.hv.data(), t.hbeta.data(), xs.data(), sv.data());
+    std::copy(xs.begin(), xs.end(), vec);
     return 0;
 }
 

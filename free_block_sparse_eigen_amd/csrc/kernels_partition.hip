@@ -72,9 +72,10 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
 //   screening vector     C' = L c^T       (d-dim; x . C' = (x L) . c for any point x)
 //   split of C' into bf16 hi + lo parts   (the MFMA operand; |C' - hi - lo| <= 2^-17 |C'|)
 //   |c|^2 (fp32, nearest) and |C'| (fp32, rounded up) for the screening score and bound
-// Block = 16 centroids of one head, so each element of L read from L2 serves 16 of
-// them. With `off` given, empty groups are skipped (they keep their previous centroid).
-constexpr int kFinG = 16;
+// Block = 4 centroids of one head (each element of L read from L2 serves 4 of them;
+// small blocks keep every CU busy). With `off` given, empty groups are skipped (they
+// keep their previous centroid).
+constexpr int kFinG = 4;
 
 // fixed-order sum of v over the 64 lanes (butterfly; identical on every lane)
 __device__ inline double wave_sum_f64(double v) {
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
     for (int o = tid; o < kFinG * dout; o += 256) {
         const int gs = o / dout, j = o % dout;
         double acc = 0.0;
+#pragma unroll 8
         for (int i = 0; i < d; ++i) acc += s_m[gs][i] * lh[(size_t)i * dout + j];
         s_c[gs][j] = acc;
     }
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
     for (int o = tid; o < kFinG * d; o += 256) {
         const int i = o / kFinG, gs = o % kFinG;
         double acc = 0.0;
+#pragma unroll 8
         for (int j = 0; j < dout; ++j) acc += lh[(size_t)i * dout + j] * s_c[gs][j];
         s_s[gs][i] = acc;
     }
@@ -347,37 +350,48 @@ void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart
 }
 
 // ----------------------------------------------------------------- recheck ---
-// One wave per queued point: exact-input fp64 coordinates y = x L64, fp64 distances
-// to every fp64 centroid, argmin with the lowest index on ties.
-__global__ __launch_bounds__(64) void k_recheck(const bf16_t* __restrict__ x, int n, int d,
-                                                const double* __restrict__ l64, int dim,
-                                                const double* __restrict__ c64, int groups,
-                                                const int32_t* __restrict__ flag_count,
-                                                const int32_t* __restrict__ flag_list,
-                                                int32_t* __restrict__ labels) {
+// One block per queued point: exact-input fp64 coordinates y = x L64 (two halves of the
+// depth summed in a fixed order), fp64 distances to every fp64 centroid (a thread per
+// centroid), argmin with the lowest index on ties.
+__global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, int n, int d,
+                                                 const double* __restrict__ l64, int dim,
+                                                 const double* __restrict__ c64, int groups,
+                                                 const int32_t* __restrict__ flag_count,
+                                                 const int32_t* __restrict__ flag_list,
+                                                 int32_t* __restrict__ labels) {
     __shared__ double xs[128];
+    __shared__ double part[2][128];
     __shared__ double ys[128];
-    const int h = blockIdx.y;
-    const int lane = threadIdx.x;
+    __shared__ double wbest[4];
+    __shared__ int wbg[4];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int count = flag_count[h];
     const double* lh = l64 + (size_t)h * d * dim;
     const double* ch = c64 + (size_t)h * groups * dim;
+    const int dh = d / 2;
     for (int idx = blockIdx.x; idx < count; idx += gridDim.x) {
         const int p = flag_list[(size_t)h * n + idx];
-        const bf16_t* row = x + ((size_t)h * n + p) * d;
-        for (int i = lane; i < d; i += 64) xs[i] = (double)bf16_to_f32(row[i]);
+        if (tid < d) xs[tid] = (double)bf16_to_f32(x[((size_t)h * n + p) * d + tid]);
         __syncthreads();
-        for (int j = lane; j < dim; j += 64) {
-            double s = 0.0;
-            for (int i = 0; i < d; ++i) s += xs[i] * lh[(size_t)i * dim + j];
-            ys[j] = s;
+        {
+            const int j = tid & 127, hf = tid >> 7;
+            if (j < dim) {
+                const int i0 = hf * dh, i1 = hf ? d : dh;
+                double s = 0.0;
+#pragma unroll 8
+                for (int i = i0; i < i1; ++i) s += xs[i] * lh[(size_t)i * dim + j];
+                part[hf][j] = s;
+            }
         }
+        __syncthreads();
+        if (tid < dim) ys[tid] = part[0][tid] + part[1][tid];
         __syncthreads();
         double best = INFINITY;
         int bg = 0x7fffffff;
-        for (int g = lane; g < groups; g += 64) {
+        for (int g = tid; g < groups; g += 256) {
             const double* c = ch + (size_t)g * dim;
             double dist = 0.0;
+#pragma unroll 8
             for (int j = 0; j < dim; ++j) {
                 const double t = ys[j] - c[j];
                 dist += t * t;
@@ -389,7 +403,18 @@ __global__ __launch_bounds__(64) void k_recheck(const bf16_t* __restrict__ x, in
             const int og = __shfl_xor(bg, o, 64);
             if (ob < best || (ob == best && og < bg)) { best = ob; bg = og; }
         }
-        if (lane == 0) labels[(size_t)h * n + p] = bg;
+        if (lane == 0) {
+            wbest[w] = best;
+            wbg[w] = bg;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double b = wbest[0];
+            int g = wbg[0];
+            for (int k = 1; k < 4; ++k)
+                if (wbest[k] < b || (wbest[k] == b && wbg[k] < g)) { b = wbest[k]; g = wbg[k]; }
+            labels[(size_t)h * n + p] = g;
+        }
         __syncthreads();
     }
 }
@@ -398,8 +423,8 @@ void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64,
                     const double* c64, int groups, const int32_t* flag_count,
                     const int32_t* flag_list, int32_t* labels, hipStream_t st) {
     int blocks = (n + 63) / 64;
-    if (blocks > 2048) blocks = 2048;
-    hipLaunchKernelGGL(k_recheck, dim3(blocks, heads), dim3(64), 0, st, x, n, d, l64, dim, c64,
+    if (blocks > 512) blocks = 512;
+    hipLaunchKernelGGL(k_recheck, dim3(blocks, heads), dim3(256), 0, st, x, n, d, l64, dim, c64,
                        groups, flag_count, flag_list, labels);
 }
 
@@ -420,30 +445,32 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ labels
     for (int g = tid; g < groups; g += 256) out[g] = hist[g];
 }
 
-// per head: group totals, exclusive scan over groups, then per-block bases in block order
+// per head: group totals, exclusive scan over groups (wave scans + a scan of the wave
+// totals), then per-block bases in block order
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ blkhist, int nblk,
                                                int groups, int n, int32_t* __restrict__ blkoff,
                                                int32_t* __restrict__ off) {
-    __shared__ int tot[kMaxGroups];
-    const int h = blockIdx.x, g = threadIdx.x;
+    __shared__ int wtot[16];
+    const int h = blockIdx.x, g = threadIdx.x, lane = g & 63, w = g >> 6;
     const int32_t* hh = blkhist + (size_t)h * nblk * groups;
+    int tot = 0;
     if (g < groups) {
-        int s = 0;
-        for (int b = 0; b < nblk; ++b) s += hh[(size_t)b * groups + g];
-        tot[g] = s;
+#pragma unroll 8
+        for (int b = 0; b < nblk; ++b) tot += hh[(size_t)b * groups + g];
     }
-    __syncthreads();
-    if (g == 0) {
-        int run = 0;
-        for (int i = 0; i < groups; ++i) {
-            const int c = tot[i];
-            tot[i] = run;
-            run += c;
-        }
+    // inclusive scan inside the wave
+    int inc = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
     }
+    if (lane == 63) wtot[w] = inc;
     __syncthreads();
+    int base = 0;
+    for (int k = 0; k < w; ++k) base += wtot[k];
     if (g < groups) {
-        int run = tot[g];
+        int run = base + inc - tot;      // exclusive prefix
         off[(size_t)h * (groups + 1) + g] = run;
         int32_t* bo = blkoff + (size_t)h * nblk * groups;
         for (int b = 0; b < nblk; ++b) {
