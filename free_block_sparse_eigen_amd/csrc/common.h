@@ -63,13 +63,15 @@ __device__ inline float dot2_bf16(uint32_t packed, bf16x2 ones, float acc) {
 }
 
 // LDS row swizzle for tiles of 16-byte chunks: chunk c of row r is stored at c ^ swz(r).
-// swz is a bit permutation of r's low bits (bits 0,1 -> 1,2; bit 2 -> 0; bit 3 -> 3), so
-// 16 consecutive rows read at one logical chunk land on 16 distinct chunk slots, and 4
-// consecutive rows read at two adjacent chunks land on 8 distinct slots.
+// With 16 chunks per row, swz rotates r's low 4 bits by two ((r & 3) << 2 | (r >> 2) & 3):
+// 16-byte reads of one logical chunk by 32 consecutive rows, and the transposed 8-byte
+// reads of 4 consecutive rows x 4 adjacent chunks, then run without bank conflicts on
+// gfx950 (checked with the LDS bank-conflict counter). With 8 chunks per row it is a
+// bit permutation of r's low 3 bits (bits 0,1 -> 1,2; bit 2 -> 0).
 template <int CH>
 __host__ __device__ inline int swz(int r) {
-    const int f = ((r & 3) << 1) | ((r >> 2) & 1);
-    return (CH >= 16) ? (f | (r & 8)) : f;
+    if (CH >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
 template <typename T>

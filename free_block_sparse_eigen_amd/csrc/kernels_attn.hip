@@ -150,8 +150,10 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     __shared__ int s_pre[kMaxGroups + 1];
     __shared__ int s_start[kMaxGroups];
     __shared__ int s_phys[2][KT];
-    __shared__ uint4 s_k[2][TL::SLOTS];
-    __shared__ uint4 s_v[2][TL::SLOTS];
+    // distinct arrays per buffer: the compiler then knows that the loads in flight into
+    // one buffer cannot alias the reads of the other (no wait before the tile math)
+    __shared__ uint4 s_k0[TL::SLOTS], s_k1[TL::SLOTS];
+    __shared__ uint4 s_v0[TL::SLOTS], s_v1[TL::SLOTS];
 
     const int nid = xcd_linear_id();
     const int max_units = gridDim.x;
@@ -208,23 +210,40 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     const bf16_t* vbase = vp + head_row0 * D;
     fill_phys(0, 0);
     __syncthreads();
-    TL::issue(kbase, vbase, s_phys[0], s_k[0], s_v[0], w, lane);
+    TL::issue(kbase, vbase, s_phys[0], s_k0, s_v0, w, lane);
     if (ntiles > 1) fill_phys(1, 1);
     tile_ready();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) TL::issue(kbase, vbase, s_phys[buf ^ 1], s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
+    // one tile: loads of tile t+1 into (nk, nv) overlap the math on (sk, sv)
+    auto step = [&](int t, int buf, const uint4* sk, const uint4* sv, uint4* nk, uint4* nv) {
+        if (t + 1 < ntiles) TL::issue(kbase, vbase, s_phys[buf ^ 1], nk, nv, w, lane);
         if (active) {
-            // S^T for both 32-key blocks: two independent accumulation chains
-            const uint4* sk = s_k[buf];
+            // S^T for both 32-key blocks: two independent accumulation chains, the K
+            // fragments read one depth step ahead of their MFMAs
+            const int rl = lane & 31, sw = swz<TL::CH>(rl);     // same swizzle for row + 32
+            const uint4* k0p = sk + rl * TL::CH;
+            const uint4* k1p = sk + (32 + rl) * TL::CH;
             f32x16 s0 = {}, s1 = {};
+            uint4 a0 = k0p[half ^ sw], a1 = k1p[half ^ sw];
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                const int c = (2 * kk + half) ^ swz<TL::CH>(lane & 31);   // swz(r) = swz(r + 32)
-                s0 = mfma32x32x16(sk[(lane & 31) * TL::CH + c], qf[kk], s0);
-                s1 = mfma32x32x16(sk[(32 + (lane & 31)) * TL::CH + c], qf[kk], s1);
+                uint4 n0 = a0, n1 = a1;
+                if (kk + 1 < D / 16) {
+                    const int c = (2 * (kk + 1) + half) ^ sw;
+                    n0 = k0p[c];
+                    n1 = k1p[c];
+                }
+                s0 = mfma32x32x16(a0, qf[kk], s0);
+                s1 = mfma32x32x16(a1, qf[kk], s1);
+                a0 = n0;
+                a1 = n1;
             }
+            // V^T fragments of keys 0..31, read now so that the softmax hides their latency
+            uint4 vf[2][DB];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) vf[sl][db] = vt_frag<D>(sv, db, sl, lane);
             const int nvk = U - t * KT;
             if (nvk < KT) {
 #pragma unroll
@@ -248,8 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
                 m_run = mnew;
             }
             const float mneg = -m_run;
-            // P^T slices 0,1 (keys 0..31), then PV of those slices overlapped with the
-            // exponentials of slices 2,3 (keys 32..63)
+            // P^T slices 0,1 (keys 0..31)
             uint4 pb[4];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
@@ -263,12 +281,15 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
                 }
                 pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
-            const uint4* sv = s_v[buf];
+            // PV of keys 0..31; each consumed fragment's registers take the fragment of
+            // the slice two further on, and the exponentials of keys 32..63 run alongside
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    o[db] = mfma32x32x16(vt_frag<D>(sv, db, sl, lane), pb[sl], o[db]);
+                for (int db = 0; db < DB; ++db) {
+                    o[db] = mfma32x32x16(vf[sl][db], pb[sl], o[db]);
+                    vf[sl][db] = vt_frag<D>(sv, db, sl + 2, lane);
+                }
 #pragma unroll
             for (int sl = 2; sl < 4; ++sl) {
                 uint32_t wv[4];
@@ -284,17 +305,21 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
 #pragma unroll
             for (int sl = 2; sl < 4; ++sl)
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    o[db] = mfma32x32x16(vt_frag<D>(sv, db, sl, lane), pb[sl], o[db]);
+                for (int db = 0; db < DB; ++db) o[db] = mfma32x32x16(vf[sl - 2][db], pb[sl], o[db]);
             // interleave: the first 2*DB MFMAs of PV with the exponentials of keys 32..63
 #pragma unroll
             for (int i = 0; i < 2 * DB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // its two LDS reads
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
             }
         }
         if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, 0, s_k0, s_v0, s_k1, s_v1);
+        if (t + 1 < ntiles) step(t + 1, 1, s_k1, s_v1, s_k0, s_v0);
     }
 
     if (!active) return;
