@@ -115,14 +115,40 @@ __device__ inline float pair_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Blocks of one XCD get a contiguous range of work units (the hardware hands workgroups
-// to the 8 XCDs round-robin), so units that stream the same key tiles share an L2.
-__device__ inline int xcd_linear_id() {
-    const int total = gridDim.x * gridDim.y * gridDim.z;
+// Work units are dealt so that the 8 XCDs work through the heads together (the head's
+// keys and values stay hot in the shared last-level cache) while each XCD takes a
+// contiguous eighth of every head's unit list (units of one query group stream the same
+// key tiles and so share that XCD's L2). The hardware hands workgroups to the XCDs
+// round-robin, so block b runs on XCD b % 8 as that XCD's (b / 8)-th workgroup.
+// Returns false for blocks past the last unit. `s_cnt` is LDS scratch of 256 ints;
+// every thread of the block must call this.
+__device__ inline bool unit_of_block(const int32_t* __restrict__ nunits, int stride, int heads,
+                                     int* s_cnt, int& h, int& ui) {
     const int lid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int xcd = lid & 7, k = lid >> 3;
-    const int q = total >> 3, r = total & 7;
-    return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+    const int x = lid & 7;
+    int k = lid >> 3;
+    bool found = false;
+    h = 0;
+    ui = 0;
+    for (int h0 = 0; h0 < heads; h0 += 256) {
+        const int nh = min(256, heads - h0);
+        __syncthreads();
+        if ((int)threadIdx.x < nh) s_cnt[threadIdx.x] = nunits[(size_t)(h0 + threadIdx.x) * stride];
+        __syncthreads();
+        for (int i = 0; i < nh && !found; ++i) {
+            const int n = s_cnt[i], c = (n + 7) >> 3;
+            const int lo = min(x * c, n), cnt = min(lo + c, n) - lo;
+            if (k < cnt) {
+                h = h0 + i;
+                ui = lo + k;
+                found = true;
+            } else {
+                k -= cnt;
+            }
+        }
+    }
+    __syncthreads();
+    return found;
 }
 
 // Key tile -> physical rows: the smallest segment s with prefix[s+1] > u holds virtual key u.
@@ -144,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
     int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
     const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
-    int nunits_stride, float scale_log2, void* __restrict__ out) {
+    int nunits_stride, int heads, float scale_log2, void* __restrict__ out) {
     using TL = Tile<D>;
     constexpr int DB = D / 32;
     __shared__ int s_pre[kMaxGroups + 1];
@@ -155,11 +181,9 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     __shared__ uint4 s_k0[TL::SLOTS], s_k1[TL::SLOTS];
     __shared__ uint4 s_v0[TL::SLOTS], s_v1[TL::SLOTS];
 
-    const int nid = xcd_linear_id();
-    const int max_units = gridDim.x;
-    const int h = nid / max_units, ui = nid % max_units;
+    int h, ui;
+    if (!unit_of_block(nunits, nunits_stride, heads, s_start, h, ui)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (ui >= nunits[(size_t)h * nunits_stride]) return;
     const int2 un = units[(size_t)h * units_head_stride + ui];
     const int gi = un.x, row0 = un.y;
     const int32_t* qo = qoff + (size_t)h * qoff_stride;
@@ -350,11 +374,12 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
                  void* out, int out_mode, hipStream_t st) {
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-    dim3 grid(max_units, heads);
+    // 8 XCD slots per round of units: enough blocks for every head's units at any split
+    dim3 grid(8 * ((max_units + 7) / 8), heads);
 #define SPR_VBSA(DD, MM)                                                                     \
     hipLaunchKernelGGL((k_vbsa<DD, MM>), grid, dim3(256), 0, st, qp, kp, vp, n, qoff,        \
                        qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units, \
-                       units_head_stride, nunits, nunits_stride, scale_log2, out)
+                       units_head_stride, nunits, nunits_stride, heads, scale_log2, out)
     if (d == 128) {
         if (out_mode == 0) SPR_VBSA(128, 0); else SPR_VBSA(128, 1);
     } else {
