@@ -46,7 +46,8 @@ struct sparsepr_ctx {
     int64_t* pairs = nullptr;
     // attention, probes, fit
     float *o_s = nullptr, *part_ml = nullptr, *part_od = nullptr, *part_os = nullptr;
-    float *px = nullptr, *py = nullptr, *pod = nullptr, *bm32 = nullptr, *bv32 = nullptr;
+    float *px = nullptr, *py = nullptr, *pod = nullptr, *bv32 = nullptr;
+    bf16_t* bt16 = nullptr;                      // [H][2][d][d] B'^T as bf16 hi, lo
     double *fit_m = nullptr, *fit_g = nullptr;   // [H][2][d] means, [H][3][d][d] Grams
     double* mq = nullptr;                        // [H][d][d] query metric C_K^T C_K / d
     // dense baseline: one query group and one key group holding every token
@@ -58,7 +59,7 @@ struct sparsepr_ctx {
     std::vector<float> h_x, h_y;
     // pinned host buffers of the fit: Grams in (device -> host), B' and b' out
     double* h_fit = nullptr;          // [H][2][d] means, then [H][3][d][d] Grams
-    float* h_b32 = nullptr;           // [H][d][d] B', then [H][d] b'
+    void* h_b32 = nullptr;            // [H][2][d][d] bf16 B'^T hi/lo, then [H][d] fp32 b'
     hipEvent_t ev_probe = nullptr;    // probe rows and fit Grams are on the host
 
     int stage = 0;
@@ -195,7 +196,7 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.fit_m, H * 2 * d);
     a.take(c.fit_g, H * 3 * d * d);
     a.take(c.mq, H * d * d);
-    a.take(c.bm32, H * d * d);
+    a.take(c.bt16, H * 2 * d * d);
     a.take(c.bv32, H * d);
     a.take(c.dense_meta, 8);
     a.take(c.dense_unit_list, c.dense_units);
@@ -387,7 +388,7 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     {
         const size_t H = c->H, d = c->d;
         if (hipHostMalloc(reinterpret_cast<void**>(&c->h_fit), sizeof(double) * H * (2 * d + 3 * d * d)) != hipSuccess ||
-            hipHostMalloc(reinterpret_cast<void**>(&c->h_b32), sizeof(float) * H * (d * d + d)) != hipSuccess ||
+            hipHostMalloc(&c->h_b32, sizeof(float) * H * (d * d + d)) != hipSuccess ||
             hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming) != hipSuccess) {
             sparsepr_destroy(c);
             return SPARSEPR_ERR_OOM;
@@ -595,10 +596,20 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
             if (frc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "probe fit failed (non-finite probe outputs)");
     }
     // (the previous call's upload from this buffer finished before ev_probe fired)
-    for (size_t i = 0; i < H * d * d; ++i) c->h_b32[i] = (float)c->h_bm[i];
-    for (size_t i = 0; i < H * d; ++i) c->h_b32[H * d * d + i] = (float)c->h_bv[i];
-    SPR_HIP(c, hipMemcpyAsync(c->bm32, c->h_b32, sizeof(float) * H * d * d, hipMemcpyHostToDevice, st));
-    SPR_HIP(c, hipMemcpyAsync(c->bv32, c->h_b32 + H * d * d, sizeof(float) * H * d, hipMemcpyHostToDevice, st));
+    // B'^T split into bf16 hi + lo (nearest even), the correction kernel's MFMA operand
+    bf16_t* hb = static_cast<bf16_t*>(c->h_b32);
+    float* hv = reinterpret_cast<float*>(hb + H * 2 * d * d);
+    for (size_t h = 0; h < H; ++h)
+        for (size_t j = 0; j < d; ++j)
+            for (size_t i = 0; i < d; ++i) {
+                const double b = c->h_bm[(h * d + i) * d + j];
+                const bf16_t bh = f32_to_bf16(static_cast<float>(b));
+                hb[((h * 2 + 0) * d + j) * d + i] = bh;
+                hb[((h * 2 + 1) * d + j) * d + i] = f32_to_bf16(static_cast<float>(b - (double)bf16_to_f32(bh)));
+            }
+    for (size_t i = 0; i < H * d; ++i) hv[i] = (float)c->h_bv[i];
+    SPR_HIP(c, hipMemcpyAsync(c->bt16, hb, sizeof(bf16_t) * H * 2 * d * d, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->bv32, hv, sizeof(float) * H * d, hipMemcpyHostToDevice, st));
     mark(c, 6, st);
     c->stage = kStageFit;
     return SPARSEPR_OK;
@@ -610,7 +621,7 @@ int32_t sparsepr_correct(sparsepr_ctx* c, void* o, void* stream) {
     if (!o || !aligned16(o)) return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned o");
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
-    launch_correct(c->o_s, c->bm32, c->bv32, c->pod, c->probe_of, c->qperm, c->H, c->N, c->d, c->P, o,
+    launch_correct(c->o_s, c->bt16, c->bv32, c->pod, c->probe_of, c->qperm, c->H, c->N, c->d, c->P, o,
                    c->p.dtype == SPARSEPR_F32 ? 1 : 0, st);
     SPR_LAUNCHED(c, "correct");
     mark(c, 7, st);

@@ -7,15 +7,17 @@
 namespace spr {
 
 // Correction GEMM on MFMA: for 32 rows x per wave, C^T = B'^T X^T with
-//   A = B'^T (rows = output column j, depth = i), held in LDS as bf16 hi/lo parts,
+//   A = B'^T (rows = output column j, depth = i), bf16 hi and lo parts prepared by the
+//       host, staged in LDS with coalesced loads,
 //   B = X^T  (depth = i, columns = rows), X's fp32 rows split into bf16 hi/lo in VGPRs,
 // three products hi.hi + hi.lo + lo.hi (relative error about 2^-16 of |X||B'|, so the
 // correction stays accurate when |B'| is large). Each lane then owns one row: it adds
-// X and b', or takes the exact dense output for a probe row, and stores the row at its
+// X and b', or takes the exact dense output for a probe row. The finished rows go
+// through LDS (reusing the B' tile) so that each output row is stored whole, at its
 // original token index.
 template <int D>
 __global__ __launch_bounds__(256) void k_correct(const float* __restrict__ o_s,
-                                                 const float* __restrict__ bmat,
+                                                 const bf16_t* __restrict__ bt16,
                                                  const float* __restrict__ bvec,
                                                  const float* __restrict__ od,
                                                  const int32_t* __restrict__ probe_of,
@@ -23,26 +25,18 @@ __global__ __launch_bounds__(256) void k_correct(const float* __restrict__ o_s,
                                                  int probes, void* __restrict__ out, int out_f32) {
     constexpr int CH = D / 8;          // 16-byte chunks per bf16 row of B'^T
     constexpr int JB = D / 32;         // 32-column output blocks
-    __shared__ uint4 s_b[2][D * CH];   // B'^T hi / lo: row j, chunk c at c ^ swz(j)
+    constexpr int SB = 2 * D * CH;                 // B'^T hi / lo tiles (16-byte slots)
+    constexpr int SO = 4 * 32 * D * 4 / 16;        // output staging, 4 waves x 32 rows (fp32)
+    __shared__ uint4 s_raw[SB > SO ? SB : SO];
+    uint4(*s_b)[D * CH] = reinterpret_cast<uint4(*)[D * CH]>(s_raw);   // row j, chunk c at c ^ swz(j)
     __shared__ float s_bv[D];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5;
-    const float* bh = bmat + (size_t)h * D * D;
-    // stage B'^T as bf16 hi/lo: thread item = (j, chunk c) -> 8 consecutive i
-    for (int it = tid; it < D * CH; it += 256) {
-        const int j = it / CH, c = it % CH;
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v0 = bh[(size_t)(c * 8 + 2 * e) * D + j];
-            const float v1 = bh[(size_t)(c * 8 + 2 * e + 1) * D + j];
-            const bf16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-            hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lw[e] = pack_bf16x2(v0 - bf16_to_f32(h0), v1 - bf16_to_f32(h1));
-        }
-        const int pc = c ^ swz<CH>(j);
-        s_b[0][j * CH + pc] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        s_b[1][j * CH + pc] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    const uint4* bsrc = reinterpret_cast<const uint4*>(bt16 + (size_t)h * 2 * D * D);
+    for (int it = tid; it < 2 * D * CH; it += 256) {
+        const int part = it / (D * CH), rem = it % (D * CH);
+        const int j = rem / CH, c = rem % CH;
+        s_b[part][j * CH + (c ^ swz<CH>(j))] = bsrc[it];
     }
     for (int j = tid; j < D; j += 256) s_bv[j] = bvec[(size_t)h * D + j];
     __syncthreads();
@@ -81,41 +75,61 @@ __global__ __launch_bounds__(256) void k_correct(const float* __restrict__ o_s,
             acc[jb] = mfma32x32x16(alo, bhi, acc[jb]);
         }
     }
-    if (!valid) return;
-    // this lane: row `row`, columns j = jb*32 + 8g + 4*half + 0..3
-    const int pi = probe_of[(size_t)h * n + row];
-    const size_t dst = ((size_t)h * n + qperm[(size_t)h * n + row]) * D;
+    // this lane: row `row`, columns j = jb*32 + 8g + 4*half + 0..3, finished in registers
+    const int pi = valid ? probe_of[(size_t)h * n + row] : -1;
     const float* src = (pi >= 0) ? od + ((size_t)h * probes + pi) * D : xr;
+    float res[JB][16];
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int j = jb * 32 + 8 * g + 4 * half;
-            const float4 xv = *reinterpret_cast<const float4*>(src + j);
-            float v[4] = {xv.x, xv.y, xv.z, xv.w};
-            if (pi < 0) {
+            const float4 xv = valid ? *reinterpret_cast<const float4*>(src + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float v[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (v[e] + s_bv[j + e]) + acc[jb][4 * g + e];
-            }
-            if (out_f32) {
-                *reinterpret_cast<float4*>(static_cast<float*>(out) + dst + j) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-                *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + dst + j) =
-                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
+            for (int e = 0; e < 4; ++e)
+                res[jb][4 * g + e] = (pi < 0) ? (v[e] + s_bv[j + e]) + acc[jb][4 * g + e] : v[e];
         }
+    // stage the wave's 32 finished rows in LDS (over the B' tile), then store whole rows
+    __syncthreads();
+    const int esz = out_f32 ? 4 : 2;
+    char* stage = reinterpret_cast<char*>(s_raw) + (size_t)w * 32 * D * 4;   // 32 rows x D x 4 B
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int j = jb * 32 + 8 * g + 4 * half;
+            char* dst = stage + ((size_t)(lane & 31) * D + j) * esz;
+            if (out_f32)
+                *reinterpret_cast<float4*>(dst) = make_float4(res[jb][4 * g], res[jb][4 * g + 1],
+                                                              res[jb][4 * g + 2], res[jb][4 * g + 3]);
+            else
+                *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(res[jb][4 * g], res[jb][4 * g + 1]),
+                                                            pack_bf16x2(res[jb][4 * g + 2], res[jb][4 * g + 3]));
+        }
+    __syncthreads();
+    // row-contiguous stores: 16-byte pieces, consecutive lanes along a row
+    const int pieces = D * esz / 16;                   // per row
+    const int row_base = blockIdx.x * 128 + w * 32;
+    for (int it = lane; it < 32 * pieces; it += 64) {
+        const int r = it / pieces, pc = it % pieces;
+        const int gr = row_base + r;
+        if (gr >= n) continue;
+        const size_t drow = (size_t)h * n + qperm[(size_t)h * n + gr];
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + (size_t)r * D * esz + pc * 16);
+        *reinterpret_cast<uint4*>(static_cast<char*>(out) + drow * D * esz + pc * 16) = v;
+    }
 }
 
-void launch_correct(const float* o_s, const float* bmat, const float* bvec, const float* od,
+void launch_correct(const float* o_s, const bf16_t* bt16, const float* bvec, const float* od,
                     const int32_t* probe_of, const int32_t* qperm, int heads, int n, int d,
                     int probes, void* o, int out_f32, hipStream_t st) {
     dim3 grid((n + 127) / 128, heads);
     if (d == 128)
-        hipLaunchKernelGGL(k_correct<128>, grid, dim3(256), 0, st, o_s, bmat, bvec, od, probe_of, qperm,
+        hipLaunchKernelGGL(k_correct<128>, grid, dim3(256), 0, st, o_s, bt16, bvec, od, probe_of, qperm,
                            n, probes, o, out_f32);
     else
-        hipLaunchKernelGGL(k_correct<64>, grid, dim3(256), 0, st, o_s, bmat, bvec, od, probe_of, qperm,
+        hipLaunchKernelGGL(k_correct<64>, grid, dim3(256), 0, st, o_s, bt16, bvec, od, probe_of, qperm,
                            n, probes, o, out_f32);
 }
 
