@@ -248,6 +248,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
             const uint4* k0p = sk + rl * TL::CH;
             const uint4* k1p = sk + (32 + rl) * TL::CH;
             f32x16 s0 = {}, s1 = {};
+            __builtin_amdgcn_s_setprio(1);      // MFMA phases at raised wave priority
             uint4 a0 = k0p[half ^ sw], a1 = k1p[half ^ sw];
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
@@ -262,6 +263,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
                 a0 = n0;
                 a1 = n1;
             }
+            __builtin_amdgcn_s_setprio(0);
             // V^T fragments of keys 0..31, read now so that the softmax hides their latency
             uint4 vf[2][DB];
 #pragma unroll
@@ -305,6 +307,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
                 }
                 pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
+            __builtin_amdgcn_s_setprio(1);
             // PV of keys 0..31; each consumed fragment's registers take the fragment of
             // the slice two further on, and the exponentials of keys 32..63 run alongside
 #pragma unroll
@@ -337,6 +340,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // its two LDS reads
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
@@ -394,9 +398,9 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
 // probe's query group. P.V uses a bf16 hi/lo split of P (about 2^-17 relative) so that
 // the probe outputs are near fp32 accuracy. Partial (max, sum, unnormalised O) per split.
 int probe_splits(int n) {
-    int s = (n + 4095) / 4096;
+    int s = (n + 2047) / 2048;
     if (s < 1) s = 1;
-    if (s > 64) s = 64;
+    if (s > 128) s = 128;
     return s;
 }
 
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void k_probe(
     constexpr int DB = D / 32;
     __shared__ int s_phys[2][KT];
     __shared__ int s_kg[2][KT];
-    __shared__ uint32_t s_bits[kProbeRows][kMaxGroups / 32];
+    __shared__ uint32_t s_bits[kProbeRows][kMaxGroups / 32 + 1];   // padded rows: no bank conflicts
     __shared__ uint4 s_k[2][TL::SLOTS];
     __shared__ uint4 s_v[2][TL::SLOTS];
 
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(256) void k_probe(
     const int p0 = blockIdx.x * kProbeRows;
     const int gw = (gk + 31) / 32;
     const size_t head_row0 = (size_t)h * n;
-    for (int i = tid; i < kProbeRows * (kMaxGroups / 32); i += 256) (&s_bits[0][0])[i] = 0u;
+    for (int i = tid; i < kProbeRows * (kMaxGroups / 32 + 1); i += 256) (&s_bits[0][0])[i] = 0u;
     __syncthreads();
     for (int i = tid; i < kProbeRows * kblk; i += 256) {
         const int lp = i / kblk, s = i % kblk;

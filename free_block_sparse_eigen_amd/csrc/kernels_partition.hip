@@ -243,17 +243,24 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
     const int p_base = blockIdx.x * 256 + w * 64;
     uint4 xf[2][D / 16];
     float xn[2];
+    // both point blocks' fragments loaded up front (an invalid point reads point 0 and
+    // is zeroed), then their norms
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
-        const int pt = p_base + 32 * pb + (lane & 31);
-        const bool valid = pt < n;
+        const int pt = min(p_base + 32 * pb + (lane & 31), n - 1);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            xf[pb][kk] = *reinterpret_cast<const uint4*>(x + ((size_t)h * n + pt) * D + 16 * kk + 8 * half);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+        const bool valid = p_base + 32 * pb + (lane & 31) < n;
         float ss = 0.f;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            const uint4 v = valid ? *reinterpret_cast<const uint4*>(x + ((size_t)h * n + pt) * D +
-                                                                  16 * kk + 8 * half)
-                                  : make_uint4(0, 0, 0, 0);
-            xf[pb][kk] = v;
+            if (!valid) xf[pb][kk] = make_uint4(0, 0, 0, 0);
+            const uint4 v = xf[pb][kk];
             const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
