@@ -35,7 +35,8 @@ struct sparsepr_ctx {
     int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
     int32_t *koff = nullptr, *qoff = nullptr, *kgrp = nullptr;
     int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
-    double *mk = nullptr, *w64 = nullptr, *l64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
+    double *mk = nullptr, *w64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
+    double *kc2 = nullptr, *qc2 = nullptr;               // fp64 |c|^2 per centroid
     double *kraw = nullptr, *qraw = nullptr;
     bf16_t *kcp = nullptr, *qcp = nullptr;               // screening vectors, bf16 hi/lo
     float *kcn2 = nullptr, *qcn2 = nullptr, *kcpn = nullptr, *qcpn = nullptr;
@@ -55,7 +56,7 @@ struct sparsepr_ctx {
     int2* dense_unit_list = nullptr;
 
     // host mirrors
-    std::vector<double> h_mk, h_w64, h_kraw, h_l64, h_bm, h_bv, h_mq;
+    std::vector<double> h_mk, h_w64, h_bm, h_bv;
     std::vector<float> h_x, h_y;
     // pinned host buffers of the fit: Grams in (device -> host), B' and b' out
     double* h_fit = nullptr;          // [H][2][d] means, then [H][3][d][d] Grams
@@ -130,7 +131,7 @@ void derive(sparsepr_ctx& c) {
     c.Gk = p.kv_groups;
     c.Gq = p.q_groups;
     c.rK = p.key_rank;
-    c.Dq = (c.Gk <= c.d) ? c.Gk : c.d;
+    c.Dq = c.d;                         // the query metric is used in full (d x d)
     c.k = routed_count(p.density, c.Gk);
     c.P = p.probes;
     c.T = p.kmeans_iters;
@@ -166,9 +167,10 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.blkoff, H * c.nblk * c.gmax);
     a.take(c.mk, H * d * d);
     a.take(c.w64, H * d * c.rK);
-    a.take(c.l64, H * d * c.Dq);
     a.take(c.kc64, H * c.Gk * c.rK);
-    a.take(c.qc64, H * c.Gq * c.Dq);
+    a.take(c.qc64, H * c.Gq * d);
+    a.take(c.kc2, H * c.Gk);
+    a.take(c.qc2, H * c.Gq);
     a.take(c.kraw, H * c.Gk * d);
     a.take(c.qraw, H * c.Gq * d);
     a.take(c.kcp, H * 2 * c.Gk * d);
@@ -269,61 +271,27 @@ const bf16_t* as_bf16(sparsepr_ctx* c, const void* x, bf16_t* scratch, hipStream
 bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
 
 // Lloyd rounds on the device: assign (MFMA screening, certified) -> fp64 recheck ->
-// counting sort -> fp64 means and centroids. After the last round `sorted`/`off` are the
+// counting sort -> fp64 means and centroids. The metric is the factor l64 [d][dim], or
+// with dim == 0 the full metric l64 [d][d]. After the last round `sorted`/`off` are the
 // stable group-major permutation and `mean_raw` the raw group means (zero if empty).
 int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, int dim, const double* l64, int groups,
               int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
-              double* c64, bf16_t* cpart, float* cn2, float* cpn, hipStream_t st) {
+              double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st) {
     launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
-                          cpn, st);
+                          cpn, c2_64, st);
     SPR_LAUNCHED(c, "seed centroids");
     for (int t = 0; t < c->T; ++t) {
         int32_t* fc = flags + (size_t)t * c->H;
         launch_assign(x, c->H, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, c->flag_list, st);
         SPR_LAUNCHED(c, "assign");
-        launch_recheck(x, c->H, c->N, c->d, l64, dim, c64, groups, fc, c->flag_list, labels, st);
+        launch_recheck(x, c->H, c->N, c->d, l64, dim, c64, c2_64, groups, fc, c->flag_list, labels, st);
         SPR_LAUNCHED(c, "recheck");
         launch_counting_sort(labels, c->H, c->N, groups, c->blkhist, c->blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");
         launch_group_means(x, c->H, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
-                           cn2, cpn, st);
+                           cn2, cpn, c2_64, st);
         SPR_LAUNCHED(c, "group means");
     }
-    return SPARSEPR_OK;
-}
-
-// Host: query metric factor per head, then upload. For G_k <= d the factor is the
-// profile map C_K^T / sqrt(d) (needs the centroids); otherwise it comes from the
-// metric C_K^T C_K / d, whose Gram is formed on the device.
-int32_t query_factor_all(sparsepr_ctx* c, hipStream_t st) {
-    const size_t H = c->H, d = c->d, Gk = c->Gk, Dq = c->Dq;
-    const bool profile = c->Gk <= c->d;
-    if (profile) {
-        c->h_kraw.resize(H * Gk * d);
-        SPR_HIP(c, hipMemcpyAsync(c->h_kraw.data(), c->kraw, sizeof(double) * H * Gk * d,
-                                  hipMemcpyDeviceToHost, st));
-    } else {
-        launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
-        SPR_LAUNCHED(c, "query metric gram");
-        c->h_mq.resize(H * d * d);
-        SPR_HIP(c, hipMemcpyAsync(c->h_mq.data(), c->mq, sizeof(double) * H * d * d,
-                                  hipMemcpyDeviceToHost, st));
-    }
-    SPR_HIP(c, hipStreamSynchronize(st));
-    c->h_l64.assign(H * d * Dq, 0.0);
-    std::vector<int> rc(H, 0), dims(H, (int)Dq);
-    parallel_heads((int)H, [&](int h) {
-        if (profile)
-            rc[h] = query_factor((int)d, (int)Gk, &c->h_kraw[h * Gk * d], &c->h_l64[h * d * Dq], &dims[h]);
-        else
-            rc[h] = query_factor_from_metric((int)d, &c->h_mq[h * d * d], &c->h_l64[h * d * Dq]);
-    });
-    for (size_t h = 0; h < H; ++h) {
-        if (rc[h] != 0 || dims[h] != (int)Dq)
-            return fail(c, SPARSEPR_ERR_NUMERIC, "query metric factor failed (non-finite centroids)");
-    }
-    SPR_HIP(c, hipMemcpyAsync(c->l64, c->h_l64.data(), sizeof(double) * H * d * Dq,
-                              hipMemcpyHostToDevice, st));
     return SPARSEPR_OK;
 }
 
@@ -456,13 +424,14 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     SPR_HIP(c, hipMemcpyAsync(c->w64, c->h_w64.data(), sizeof(double) * H * d * rK, hipMemcpyHostToDevice, st));
     // keys: Lloyd in the M_K eigen-coordinates
     rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw, c->kc64,
-               c->kcp, c->kcn2, c->kcpn, st);
+               c->kcp, c->kcn2, c->kcpn, c->kc2, st);
     if (rc) return rc;
-    // queries: logit-profile metric factor (host fp64), Lloyd
-    rc = query_factor_all(c, st);
-    if (rc) return rc;
-    rc = lloyd(c, q16, c->Dq, c->l64, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm,
-               c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, st);
+    // queries: the logit-profile metric M = C_K^T C_K / d (fp64 Gram of the raw key
+    // centroids) used in full on the device, then Lloyd
+    launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
+    SPR_LAUNCHED(c, "query metric");
+    rc = lloyd(c, q16, 0, c->mq, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm, c->qoff,
+               c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
     if (rc) return rc;
     mark(c, 1, st);
     c->stage = kStagePartition;
@@ -492,10 +461,10 @@ int32_t sparsepr_set_partition(sparsepr_ctx* c, const void* q, const void* k,
     launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * c->H, st);
     launch_counting_sort(c->klab, c->H, c->N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
     launch_group_means(k16, c->H, c->N, c->d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr,
-                       nullptr, nullptr, nullptr, st);
+                       nullptr, nullptr, nullptr, nullptr, st);
     launch_counting_sort(c->qlab, c->H, c->N, c->Gq, c->blkhist, c->blkoff, c->qperm, c->qoff, st);
     launch_group_means(q16, c->H, c->N, c->d, c->qperm, c->qoff, c->Gq, c->qraw, nullptr, 0, nullptr,
-                       nullptr, nullptr, nullptr, st);
+                       nullptr, nullptr, nullptr, nullptr, st);
     SPR_LAUNCHED(c, "set partition");
     if (host) SPR_HIP(c, hipStreamSynchronize(st));   // host labels must stay valid until copied
     c->stage = kStagePartition;

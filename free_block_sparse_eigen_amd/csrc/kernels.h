@@ -21,21 +21,23 @@ void launch_fill_i64(int64_t* p, int64_t value, size_t count, hipStream_t st);
 // ---- partition ----
 void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64_t a, double* mk,
                    hipStream_t st);
+// The metric is a factor l64 [d][dout] (metric = L L^T), or with dout == 0 the full
+// metric l64 [d][d]; c64 then holds the fp64 screening vectors M m ([groups][d]).
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
-                           float* cn2, float* cpn, hipStream_t st);
+                           float* cn2, float* cpn, double* c2_64, hipStream_t st);
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st);
 void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
-                    const double* c64, int groups, const int32_t* flag_count,
+                    const double* c64, const double* c2_64, int groups, const int32_t* flag_count,
                     const int32_t* flag_list, int32_t* labels, hipStream_t st);
 void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, int32_t* blkhist,
                           int32_t* blkoff, int32_t* sorted, int32_t* off, hipStream_t st);
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
-                        hipStream_t st);
+                        double* c2_64, hipStream_t st);
 
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,

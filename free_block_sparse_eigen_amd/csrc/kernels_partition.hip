@@ -67,9 +67,12 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
 }
 
 // --------------------------------------------------------- centroid finish ---
-// For raw-space centroid means m (fp64), with the metric factor L [d][D]:
-//   projected centroid   c = m L          (fp64, used by the fp64 recheck)
-//   screening vector     C' = L c^T       (d-dim; x . C' = (x L) . c for any point x)
+// For raw-space centroid means m (fp64), with the metric given either as a factor
+// L [d][D] (metric L L^T) or, with dout == 0, as the full metric M [d][d]:
+//   factor:  projected centroid c = m L (fp64, used by the fp64 recheck),
+//            screening vector C' = L c^T (d-dim; x . C' = (x L) . c for any point x)
+//   metric:  screening vector C' = M m (its fp64 copy is what the recheck uses) and
+//            |c|^2 = m . C' (also kept in fp64)
 //   split of C' into bf16 hi + lo parts   (the MFMA operand; |C' - hi - lo| <= 2^-17 |C'|)
 //   |c|^2 (fp32, nearest) and |C'| (fp32, rounded up) for the screening score and bound
 // Block = 4 centroids of one head (each element of L read from L2 serves 4 of them;
@@ -88,19 +91,23 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
                                                 const double* __restrict__ l64, int dout, int groups,
                                                 const int32_t* __restrict__ off,
                                                 double* __restrict__ c64, bf16_t* __restrict__ cpart,
-                                                float* __restrict__ cn2, float* __restrict__ cpn) {
+                                                float* __restrict__ cn2, float* __restrict__ cpn,
+                                                double* __restrict__ c2_64) {
+    const bool full = dout == 0;                 // full metric M [d][d]
     __shared__ double s_m[kFinG][129];     // means (padded rows)
     __shared__ double s_c[kFinG][129];     // projected centroids
     __shared__ double s_s[kFinG][129];     // screening vectors
     const int h = blockIdx.y, g0 = blockIdx.x * kFinG, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
+    if (full) dout = d;
     const double* lh = l64 + (size_t)h * d * dout;
     for (int o = tid; o < kFinG * d; o += 256) {
         const int gs = o / d, i = o % d, g = g0 + gs;
         s_m[gs][i] = (g < groups) ? mean_raw[((size_t)h * groups + g) * d + i] : 0.0;
     }
     __syncthreads();
-    // c[gs][j] = sum_i m[gs][i] L[i][j]   (lanes along j: coalesced rows of L)
+    // c[gs][j] = sum_i m[gs][i] L[i][j]   (lanes along j: coalesced rows of L); with the
+    // full metric this is C' = M m itself (M is symmetric)
     for (int o = tid; o < kFinG * dout; o += 256) {
         const int gs = o / dout, j = o % dout;
         double acc = 0.0;
@@ -109,8 +116,9 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         s_c[gs][j] = acc;
     }
     __syncthreads();
-    // C'[gs][i] = sum_j L[i][j] c[gs][j]   (16 lanes share one element of L)
+    // C'[gs][i] = sum_j L[i][j] c[gs][j]   (lanes of one i share one element of L)
     for (int o = tid; o < kFinG * d; o += 256) {
+        if (full) break;
         const int i = o / kFinG, gs = o % kFinG;
         double acc = 0.0;
 #pragma unroll 8
@@ -128,10 +136,10 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         for (int j = lane; j < dout; j += 64) {
             const double cv = s_c[gs][j];
             c64[((size_t)h * groups + g) * dout + j] = cv;
-            a += cv * cv;
+            a += full ? s_m[gs][j] * cv : cv * cv;
         }
         for (int i = lane; i < d; i += 64) {
-            const double sv = s_s[gs][i];
+            const double sv = full ? s_c[gs][i] : s_s[gs][i];
             const bf16_t hi = f32_to_bf16((float)sv);
             cpart[((size_t)(h * 2 + 0) * groups + g) * d + i] = hi;
             cpart[((size_t)(h * 2 + 1) * groups + g) * d + i] = f32_to_bf16((float)(sv - (double)bf16_to_f32(hi)));
@@ -142,15 +150,16 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         if (lane == 0) {
             cn2[(size_t)h * groups + g] = (float)a;                          // nearest: enters the score
             cpn[(size_t)h * groups + g] = (float)(sqrt(b) * (1.0 + 1e-6));   // rounded up: bound only
+            c2_64[(size_t)h * groups + g] = a;
         }
     }
 }
 
 static void launch_finish(const double* mean_raw, int heads, int d, const double* l64, int dout,
                           int groups, const int32_t* off, double* c64, bf16_t* cpart, float* cn2,
-                          float* cpn, hipStream_t st) {
+                          float* cpn, double* c2_64, hipStream_t st) {
     hipLaunchKernelGGL(k_finish, dim3((groups + kFinG - 1) / kFinG, heads), dim3(256), 0, st, mean_raw,
-                       d, l64, dout, groups, off, c64, cpart, cn2, cpn);
+                       d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64);
 }
 
 // ------------------------------------------------------------------- seeds ---
@@ -164,9 +173,9 @@ __global__ __launch_bounds__(128) void k_seed(const bf16_t* __restrict__ x, int 
 
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
-                           float* cn2, float* cpn, hipStream_t st) {
+                           float* cn2, float* cpn, double* c2_64, hipStream_t st) {
     hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, groups, a, mean_raw);
-    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, st);
+    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st);
 }
 
 // ------------------------------------------------------------------ assign ---
@@ -357,12 +366,15 @@ void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart
 }
 
 // ----------------------------------------------------------------- recheck ---
-// One block per queued point: exact-input fp64 coordinates y = x L64 (two halves of the
-// depth summed in a fixed order), fp64 distances to every fp64 centroid (a thread per
-// centroid), argmin with the lowest index on ties.
+// One block per queued point, the exact-input point in fp64 against every fp64 centroid,
+// argmin with the lowest index on ties. With a factor L [d][dim]: coordinates y = x L (two
+// halves of the depth summed in a fixed order) and |y - c|^2. With the full metric
+// (dim == 0): |c|^2 - 2 x . C', which differs from the metric distance by x^T M x, the
+// same for every centroid. A thread per centroid.
 __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, int n, int d,
                                                  const double* __restrict__ l64, int dim,
-                                                 const double* __restrict__ c64, int groups,
+                                                 const double* __restrict__ c64,
+                                                 const double* __restrict__ c2_64, int groups,
                                                  const int32_t* __restrict__ flag_count,
                                                  const int32_t* __restrict__ flag_list,
                                                  int32_t* __restrict__ labels) {
@@ -372,15 +384,17 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
     __shared__ double wbest[4];
     __shared__ int wbg[4];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool full = dim == 0;
+    const int cdim = full ? d : dim;
     const int count = flag_count[h];
     const double* lh = l64 + (size_t)h * d * dim;
-    const double* ch = c64 + (size_t)h * groups * dim;
+    const double* ch = c64 + (size_t)h * groups * cdim;
     const int dh = d / 2;
     for (int idx = blockIdx.x; idx < count; idx += gridDim.x) {
         const int p = flag_list[(size_t)h * n + idx];
         if (tid < d) xs[tid] = (double)bf16_to_f32(x[((size_t)h * n + p) * d + tid]);
         __syncthreads();
-        {
+        if (!full) {
             const int j = tid & 127, hf = tid >> 7;
             if (j < dim) {
                 const int i0 = hf * dh, i1 = hf ? d : dh;
@@ -389,19 +403,26 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                 for (int i = i0; i < i1; ++i) s += xs[i] * lh[(size_t)i * dim + j];
                 part[hf][j] = s;
             }
+            __syncthreads();
+            if (tid < dim) ys[tid] = part[0][tid] + part[1][tid];
+            __syncthreads();
         }
-        __syncthreads();
-        if (tid < dim) ys[tid] = part[0][tid] + part[1][tid];
-        __syncthreads();
         double best = INFINITY;
         int bg = 0x7fffffff;
         for (int g = tid; g < groups; g += 256) {
-            const double* c = ch + (size_t)g * dim;
+            const double* c = ch + (size_t)g * cdim;
             double dist = 0.0;
+            if (full) {
+                double dot = 0.0;
 #pragma unroll 8
-            for (int j = 0; j < dim; ++j) {
-                const double t = ys[j] - c[j];
-                dist += t * t;
+                for (int j = 0; j < d; ++j) dot += xs[j] * c[j];
+                dist = c2_64[(size_t)h * groups + g] - 2.0 * dot;
+            } else {
+#pragma unroll 8
+                for (int j = 0; j < dim; ++j) {
+                    const double t = ys[j] - c[j];
+                    dist += t * t;
+                }
             }
             if (dist < best) { best = dist; bg = g; }
         }
@@ -427,11 +448,11 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 }
 
 void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
-                    const double* c64, int groups, const int32_t* flag_count,
+                    const double* c64, const double* c2_64, int groups, const int32_t* flag_count,
                     const int32_t* flag_list, int32_t* labels, hipStream_t st) {
     int blocks = (n + 63) / 64;
     if (blocks > 512) blocks = 512;
-    hipLaunchKernelGGL(k_recheck, dim3(blocks, heads), dim3(256), 0, st, x, n, d, l64, dim, c64,
+    hipLaunchKernelGGL(k_recheck, dim3(blocks, heads), dim3(256), 0, st, x, n, d, l64, dim, c64, c2_64,
                        groups, flag_count, flag_list, labels);
 }
 
@@ -595,7 +616,7 @@ __global__ __launch_bounds__(256) void k_group_sum(const bf16_t* __restrict__ x,
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
-                        hipStream_t st) {
+                        double* c2_64, hipStream_t st) {
     if (d == 128)
         hipLaunchKernelGGL(k_group_sum<128>, dim3(groups, heads), dim3(256), 0, st, x, n, sorted, off,
                            groups, mean_raw);
@@ -603,7 +624,7 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
         hipLaunchKernelGGL(k_group_sum<64>, dim3(groups, heads), dim3(256), 0, st, x, n, sorted, off,
                            groups, mean_raw);
     if (l64 != nullptr)
-        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, st);
+        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, st);
 }
 
 }  // namespace spr

@@ -89,7 +89,8 @@ typedef struct {
     double  exec_density;      /* (routed_pairs + probe_pairs) / (H N^2) */
     int64_t recheck_points;    /* k-means points resolved in fp64 after an uncertified fp32 margin */
     int32_t routed_k;          /* key groups kept per query group */
-    int32_t query_dims;        /* dimension of the query k-means space */
+    int32_t query_dims;        /* dimension the query k-means runs in: d (the logit-profile
+                                  metric C_K^T C_K / d is applied in full) */
     float   stage_ms[6];       /* mean ms per call of: partition, route, sparse attention kernel,
                                   probe rows (with the fit Grams), probe fit (the part of the
                                   host solve and upload not hidden behind the sparse kernel),
@@ -121,8 +122,9 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 
 /* ---- the five stages (section 2 of the method summary) ---- */
 
-/* 2A. Reads q, k. Host-synchronising (fp64 eigensolve of M_K; fp64 factor of the
- * query metric C_K^T C_K / d). Leaves key/query labels and centroids in the context. */
+/* 2A. Reads q, k. Host-synchronising once (fp64 eigensolve of M_K on the host); the
+ * query side runs on the device with the logit-profile metric C_K^T C_K / d in full.
+ * Leaves key/query labels and centroids in the context. */
 int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void* stream);
 
 /* 2C/2B. Reads q, k, v. Stable group-major permutation of Q/K/V, top-k key groups per
