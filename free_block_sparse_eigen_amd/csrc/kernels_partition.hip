@@ -570,7 +570,9 @@ __global__ __launch_bounds__(256) void k_group_sum(const bf16_t* __restrict__ x,
                                                    double* __restrict__ mean_raw) {
     constexpr int CH = D / 8;          // 16-byte chunks per row
     constexpr int RL = 256 / CH;       // row lanes
+    constexpr int IDX = 2048;          // member indices staged per pass
     __shared__ double red[RL][D + 1];
+    __shared__ int s_idx[IDX];
     const int h = blockIdx.y, g = blockIdx.x, tid = threadIdx.x;
     const int c = tid % CH, rl = tid / CH;
     const int32_t* oh = off + (size_t)h * (groups + 1);
@@ -589,19 +591,23 @@ __global__ __launch_bounds__(256) void k_group_sum(const bf16_t* __restrict__ x,
             acc[2 * e + 1] += (double)bf16_to_f32((bf16_t)(wd[e] >> 16));
         }
     };
-    int m = beg + rl;
-    for (; m + 3 * RL < end; m += 4 * RL) {
-        const int i0 = sh[m], i1 = sh[m + RL], i2 = sh[m + 2 * RL], i3 = sh[m + 3 * RL];
-        const uint4 v0 = *reinterpret_cast<const uint4*>(xh + (size_t)i0 * D);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(xh + (size_t)i1 * D);
-        const uint4 v2 = *reinterpret_cast<const uint4*>(xh + (size_t)i2 * D);
-        const uint4 v3 = *reinterpret_cast<const uint4*>(xh + (size_t)i3 * D);
-        add(v0);
-        add(v1);
-        add(v2);
-        add(v3);
+    // members in passes of IDX: indices staged in LDS with coalesced loads, then eight
+    // rows in flight per row lane; member m always goes to row lane m % RL (fixed order)
+    for (int p0 = 0; p0 < cnt; p0 += IDX) {
+        const int np = min(IDX, cnt - p0);
+        __syncthreads();
+        for (int i = tid; i < np; i += 256) s_idx[i] = sh[beg + p0 + i];
+        __syncthreads();
+        int m = rl;
+        for (; m + 7 * RL < np; m += 8 * RL) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(xh + (size_t)s_idx[m + u * RL] * D);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) add(v[u]);
+        }
+        for (; m < np; m += RL) add(*reinterpret_cast<const uint4*>(xh + (size_t)s_idx[m] * D));
     }
-    for (; m < end; m += RL) add(*reinterpret_cast<const uint4*>(xh + (size_t)sh[m] * D));
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rl][c * 8 + e] = acc[e];
     __syncthreads();
