@@ -9,7 +9,7 @@ namespace spr {
 
 constexpr int kSortChunk = 1024;      // points per counting-sort block
 constexpr int kMaxGroups = 1024;      // G_k, G_q upper bound (LDS tables)
-constexpr int kAttnRows = 128;        // query rows per attention work unit
+constexpr int kAttnRows = 256;        // query rows per attention work unit
 constexpr int kKeyTile = 64;          // keys per attention tile
 constexpr int kProbeRows = 128;       // probe rows per probe work unit
 

@@ -9,7 +9,7 @@
 // skipping, not computing-then-masking, is what saves work). Section 2B: probe rows get
 // the exact dense output and the routed-subset output from the same logits.
 //
-// Work unit = (head, query group, up to 128 query rows); 4 waves x 32 rows.
+// Work unit = (head, query group, up to 256 query rows); 8 waves x 32 rows.
 //   S^T = K Q^T  : A = K tile from LDS (row-major), B = Q^T fragments held in VGPRs
 //   O^T += V^T P^T: A = V^T read from the row-major V tile with the transposing LDS
 //                   read, B = P^T straight from the S^T accumulators (bf16, no
@@ -39,11 +39,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // (dims 8c..8c+7) at slot r * CH + (c ^ swz(r)). They are filled by direct
 // global-to-LDS loads (no VGPR staging): one 16-byte load per lane lands at
 // LDS base + 16 * lane, so the swizzle is applied to the global addresses instead.
-template <int D>
+template <int D, int NT = 256>
 struct Tile {
     static constexpr int CH = D / 8;
     static constexpr int SLOTS = KT * CH;           // 16-byte slots per tensor per tile
-    static constexpr int PER_WAVE = SLOTS / 256;    // load instructions per wave per tensor
+    static constexpr int PER_WAVE = SLOTS / NT;     // load instructions per wave per tensor
 
     // phys[] holds a valid row for every key of the tile (keys past the end of the
     // union repeat a real row and are masked out of the softmax).
@@ -164,14 +164,16 @@ __device__ inline int segment_row(const int* __restrict__ pre, const int* __rest
 
 }  // namespace
 
+// Block = 8 waves x 32 query rows: a unit of up to 256 rows shares every key tile.
+constexpr int kVbsaThreads = 512;
 template <int D, int OUTM>
-__global__ __launch_bounds__(256, 2) void k_vbsa(
+__global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
     const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
     int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
     const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
     int nunits_stride, int heads, float scale_log2, void* __restrict__ out) {
-    using TL = Tile<D>;
+    using TL = Tile<D, kVbsaThreads>;
     constexpr int DB = D / 32;
     __shared__ int s_pre[kMaxGroups + 1];
     __shared__ int s_start[kMaxGroups];
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void k_vbsa(
     const int32_t* bl = blocks + (size_t)h * blocks_head_stride + (size_t)gi * kblk;
     const size_t head_row0 = (size_t)h * n;
 
-    for (int s = tid; s < kblk; s += 256) {
+    for (int s = tid; s < kblk; s += kVbsaThreads) {
         const int j = bl[s];
         s_start[s] = (j >= 0) ? ko[j] : 0;
         s_pre[s + 1] = (j >= 0) ? (ko[j + 1] - ko[j]) : 0;
@@ -381,7 +383,7 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
     // 8 XCD slots per round of units: enough blocks for every head's units at any split
     dim3 grid(8 * ((max_units + 7) / 8), heads);
 #define SPR_VBSA(DD, MM)                                                                     \
-    hipLaunchKernelGGL((k_vbsa<DD, MM>), grid, dim3(256), 0, st, qp, kp, vp, n, qoff,        \
+    hipLaunchKernelGGL((k_vbsa<DD, MM>), grid, dim3(kVbsaThreads), 0, st, qp, kp, vp, n, qoff,        \
                        qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units, \
                        units_head_stride, nunits, nunits_stride, heads, scale_log2, out)
     if (d == 128) {
