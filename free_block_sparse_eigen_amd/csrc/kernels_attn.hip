@@ -39,25 +39,51 @@ typedef __attribute__((address_space(3))) void lds_void;
 // (dims 8c..8c+7) at slot r * CH + (c ^ swz(r)). They are filled by direct
 // global-to-LDS loads (no VGPR staging): one 16-byte load per lane lands at
 // LDS base + 16 * lane, so the swizzle is applied to the global addresses instead.
+// Buffer resource over one head's [n][D] bf16 rows (loads past the end return zero).
+// Word 3 (0x00020000) selects the 32-bit data format that untyped buffer loads need on
+// this architecture. The loads below go through buffer resources rather than global
+// addresses because the compiler then tracks them on the vector-memory counter alone;
+// global-address loads into LDS also mark the LDS counter as out of order, which turns
+// every wait on an LDS read into a wait for all of them.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t head_rsrc(const bf16_t* base, int n, int d) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0, n * d * 2,
+                                             0x00020000);
+}
+
 template <int D, int NT = 256>
 struct Tile {
     static constexpr int CH = D / 8;
     static constexpr int SLOTS = KT * CH;           // 16-byte slots per tensor per tile
     static constexpr int PER_WAVE = SLOTS / NT;     // load instructions per wave per tensor
 
+    // byte offset of this lane's 16-byte piece of load m (row phys[r], swizzled chunk)
+    __device__ static int offset(const int* __restrict__ phys, int w, int lane, int m, int& first) {
+        first = (w * PER_WAVE + m) * 64;
+        const int slot = first + lane;
+        const int r = slot / CH, pc = slot % CH;
+        return (phys[r] * D + ((pc ^ swz<CH>(r)) * 8)) * 2;
+    }
     // phys[] holds a valid row for every key of the tile (keys past the end of the
     // union repeat a real row and are masked out of the softmax).
-    __device__ static void issue(const bf16_t* __restrict__ kbase, const bf16_t* __restrict__ vbase,
-                                 const int* __restrict__ phys, uint4* sk, uint4* sv, int w,
-                                 int lane) {
+    __device__ static void issue(rsrc_t rk, rsrc_t rv, const int* __restrict__ phys, uint4* sk,
+                                 uint4* sv, int w, int lane) {
 #pragma unroll
         for (int m = 0; m < PER_WAVE; ++m) {
-            const int first = (w * PER_WAVE + m) * 64;
-            const int slot = first + lane;
-            const int r = slot / CH, pc = slot % CH;
-            const int off = phys[r] * D + ((pc ^ swz<CH>(r)) * 8);
-            __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sk + first), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sv + first), 16, 0, 0);
+            int first;
+            const int off = offset(phys, w, lane, m, first);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + first), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + first), 16, off, 0, 0, 0);
+        }
+    }
+    // one tensor's tile (rows phys[]) into s
+    __device__ static void issue_one(rsrc_t r, const int* __restrict__ phys, uint4* s, int w,
+                                     int lane) {
+#pragma unroll
+        for (int m = 0; m < PER_WAVE; ++m) {
+            int first;
+            const int off = offset(phys, w, lane, m, first);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(s + first), 16, off, 0, 0, 0);
         }
     }
 };
@@ -185,6 +211,8 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
 
     int h, ui;
     if (!unit_of_block(nunits, nunits_stride, heads, s_start, h, ui)) return;
+    h = __builtin_amdgcn_readfirstlane(h);
+    ui = __builtin_amdgcn_readfirstlane(ui);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int2 un = units[(size_t)h * units_head_stride + ui];
     const int gi = un.x, row0 = un.y;
@@ -232,17 +260,17 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
     const bf16x2 ones = ones_bf16x2();
     const int half = lane >> 5;
 
-    const bf16_t* kbase = kp + head_row0 * D;
-    const bf16_t* vbase = vp + head_row0 * D;
+    const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
+    const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
     fill_phys(0, 0);
     __syncthreads();
-    TL::issue(kbase, vbase, s_phys[0], s_k0, s_v0, w, lane);
+    TL::issue(rk, rv, s_phys[0], s_k0, s_v0, w, lane);
     if (ntiles > 1) fill_phys(1, 1);
     tile_ready();
 
     // one tile: loads of tile t+1 into (nk, nv) overlap the math on (sk, sv)
     auto step = [&](int t, int buf, const uint4* sk, const uint4* sv, uint4* nk, uint4* nv) {
-        if (t + 1 < ntiles) TL::issue(kbase, vbase, s_phys[buf ^ 1], nk, nv, w, lane);
+        if (t + 1 < ntiles) TL::issue(rk, rv, s_phys[buf ^ 1], nk, nv, w, lane);
         if (active) {
             // S^T for both 32-key blocks: two independent accumulation chains, the K
             // fragments read one depth step ahead of their MFMAs
@@ -468,18 +496,18 @@ __global__ __launch_bounds__(256) void k_probe(
     for (int db = 0; db < DB; ++db) { od[db] = f32x16{}; os[db] = f32x16{}; }
     float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
 
-    const bf16_t* kbase = kp + head_row0 * D;
-    const bf16_t* vbase = vp + head_row0 * D;
+    const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
+    const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
     if (ntiles > 0) {
         fill_phys(0, 0);
         __syncthreads();
-        TL::issue(kbase, vbase, s_phys[0], s_k[0], s_v[0], w, lane);
+        TL::issue(rk, rv, s_phys[0], s_k[0], s_v[0], w, lane);
         if (ntiles > 1) fill_phys(1, 1);
     }
     tile_ready();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles) TL::issue(kbase, vbase, s_phys[buf ^ 1], s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
+        if (t + 1 < ntiles) TL::issue(rk, rv, s_phys[buf ^ 1], s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
         if (active) {
             f32x16 sv[2];
             sv[0] = qk_block<D>(s_k[buf], qf, 0, lane);
