@@ -511,7 +511,8 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     // memory; the host solve (sparsepr_probe_fit) then overlaps the main kernel.
     if (c->P > 0) {
         launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P, c->kgrp,
-                     c->Gk, c->blocks, c->Gq, c->k, c->part_ml, c->part_od, c->part_os, st);
+                     c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->part_ml, c->part_od,
+                     c->part_os, st);
         launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
                            c->py, c->pod, st);
         SPR_LAUNCHED(c, "probe rows");

@@ -63,8 +63,9 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
 int probe_splits(int n);
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
                   const int32_t* probe_pos, const int32_t* probe_grp, int probes,
-                  const int32_t* kgrp, int gk, const int32_t* blocks, int gq, int kblk,
-                  float* part_ml, float* part_od, float* part_os, hipStream_t st);
+                  const int32_t* kgrp, const int32_t* koff, int koff_stride, int gk,
+                  const int32_t* blocks, int gq, int kblk, float* part_ml, float* part_od,
+                  float* part_os, hipStream_t st);
 void launch_probe_merge(int heads, int probes, int d, int splits, const float* part_ml,
                         const float* part_od, const float* part_os, float* x, float* y, float* od,
                         hipStream_t st);

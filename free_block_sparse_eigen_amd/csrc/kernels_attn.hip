@@ -438,9 +438,9 @@ template <int D>
 __global__ __launch_bounds__(256) void k_probe(
     const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     int n, const int32_t* __restrict__ probe_pos, const int32_t* __restrict__ probe_grp,
-    int probes, const int32_t* __restrict__ kgrp, int gk, const int32_t* __restrict__ blocks,
-    int gq, int kblk, int chunk, float scale_log2, float* __restrict__ part_ml,
-    float* __restrict__ part_od, float* __restrict__ part_os) {
+    int probes, const int32_t* __restrict__ kgrp, const int32_t* __restrict__ koff, int koff_stride,
+    int gk, const int32_t* __restrict__ blocks, int gq, int kblk, int chunk, float scale_log2,
+    float* __restrict__ part_ml, float* __restrict__ part_od, float* __restrict__ part_os) {
     using TL = Tile<D>;
     constexpr int DB = D / 32;
     __shared__ int s_phys[2][KT];
@@ -450,10 +450,10 @@ __global__ __launch_bounds__(256) void k_probe(
     __shared__ uint4 s_v[2][TL::SLOTS];
 
     const int h = blockIdx.z, split = blockIdx.y, splits = gridDim.y;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
     const int p0 = blockIdx.x * kProbeRows;
-    const int gw = (gk + 31) / 32;
     const size_t head_row0 = (size_t)h * n;
+    const int32_t* ko = koff + (size_t)h * koff_stride;
     for (int i = tid; i < kProbeRows * (kMaxGroups / 32 + 1); i += 256) (&s_bits[0][0])[i] = 0u;
     __syncthreads();
     for (int i = tid; i < kProbeRows * kblk; i += 256) {
@@ -465,6 +465,7 @@ __global__ __launch_bounds__(256) void k_probe(
             if (j >= 0) atomicOr(&s_bits[lp][j >> 5], 1u << (j & 31));
         }
     }
+    (void)gk;
     const int k0 = split * chunk;
     const int k1 = min(n, k0 + chunk);
     const int nkeys = max(0, k1 - k0);
@@ -490,11 +491,16 @@ __global__ __launch_bounds__(256) void k_probe(
             qf[kk] = pvalid ? ldg16(qp + (head_row0 + qrow) * D + 16 * kk + 8 * (lane >> 5))
                             : make_uint4(0, 0, 0, 0);
     }
-    (void)gw;
-    f32x16 od[DB], os[DB];
+    // oa: routed keys, ob: the other keys; the dense output is oa + ob. One running max
+    // (of all keys, raised lazily) scales both, so each logit needs one exponential.
+    f32x16 oa[DB], ob[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { od[db] = f32x16{}; os[db] = f32x16{}; }
-    float md = -INFINITY, ld = 0.f, ms = -INFINITY, ls = 0.f;
+    for (int db = 0; db < DB; ++db) { oa[db] = f32x16{}; ob[db] = f32x16{}; }
+    // row sums of the routed (ls) and other (lb) parts, both from the same bf16 hi + lo
+    // operands as the products: with every key routed lb stays 0 and the dense and
+    // routed outputs come out bit-identical
+    float m_run = -INFINITY, lb = 0.f, ls = 0.f;
+    const bf16x2 ones = ones_bf16x2();
 
     const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
     const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
@@ -512,100 +518,120 @@ __global__ __launch_bounds__(256) void k_probe(
             f32x16 sv[2];
             sv[0] = qk_block<D>(s_k[buf], qf, 0, lane);
             sv[1] = qk_block<D>(s_k[buf], qf, 1, lane);
-            const int nvk = nkeys - t * KT;
-            float xd[32], xs[32];
-            float mxd = -INFINITY, mxs = -INFINITY;
+            const int nvk = min(KT, nkeys - t * KT);
+            // routed keys of the tile as a bit mask: keys are in group-major order, so the
+            // tile's keys form runs of whole groups (usually one or two)
+            uint64_t mask = 0;
+            {
+                const int base = k0 + t * KT;
+                const int ga = s_kg[buf][0], gb = s_kg[buf][nvk - 1];
+                for (int g = ga; g <= gb; ++g) {
+                    if ((s_bits[lp][g >> 5] >> (g & 31)) & 1u) {
+                        const int lo = max(0, ko[g] - base), hi = min(nvk, ko[g + 1] - base);
+                        if (hi > lo) {
+                            const uint64_t upto_hi = (hi >= 64) ? ~0ull : ((1ull << hi) - 1);
+                            mask |= upto_hi & ~((1ull << lo) - 1);
+                        }
+                    }
+                }
+            }
+            const uint64_t mh = mask >> (4 * half);    // this lane's keys sit 4*half further on
+            const uint32_t mw[2] = {(uint32_t)mh, (uint32_t)(mh >> 32)};
+            float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    float x = sv[kb][r] * scale_log2;
-                    if (key >= nvk) x = -INFINITY;
-                    const int j = s_kg[buf][key];
-                    const bool routed = (s_bits[lp][j >> 5] >> (j & 31)) & 1u;
-                    xd[kb * 16 + r] = x;
-                    xs[kb * 16 + r] = routed ? x : -INFINITY;
-                    mxd = fmaxf(mxd, x);
-                    mxs = fmaxf(mxs, xs[kb * 16 + r]);
+                    const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    sv[kb][r] = (key < nvk) ? sv[kb][r] * scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, sv[kb][r]);
                 }
-            mxd = pair_max(mxd);
-            mxs = pair_max(mxs);
-            const float mdn = fmaxf(md, mxd), msn = fmaxf(ms, mxs);
-            const float ad = (mdn == -INFINITY) ? 1.f : fast_exp2(md - mdn);
-            const float as = (msn == -INFINITY) ? 1.f : fast_exp2(ms - msn);
-            ld *= ad;
-            ls *= as;
+            mx = pair_max(mx);
+            if (__ballot(mx > m_run + kLazy)) {
+                const float mnew = fmaxf(m_run, mx);
+                const float alpha = fast_exp2(m_run - mnew);
+                lb *= alpha;
+                ls *= alpha;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) { od[db] *= ad; os[db] *= as; }
-            md = mdn;
-            ms = msn;
-            uint4 dh[4], dl[4], sh[4], sl4[4];
+                for (int db = 0; db < DB; ++db) { oa[db] *= alpha; ob[db] *= alpha; }
+                m_run = mnew;
+            }
+            const float mneg = -m_run;
+            // P as bf16 hi + lo (about 2^-17 relative), each split by the routed mask of
+            // its two keys into the (a) and (b) operands
+            uint4 ah[4], al[4], bh[4], bl[4];
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) {
-                uint32_t a[4], b[4], c[4], e[4];
+                uint32_t a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int k = 16 * (sl >> 1) + 8 * (sl & 1) + 2 * i;   // index into xd/xs
-                    float pd[2], ps[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        pd[u] = (md == -INFINITY) ? 0.f : fast_exp2(xd[k + u] - md);
-                        ps[u] = (ms == -INFINITY) ? 0.f : fast_exp2(xs[k + u] - ms);
-                        ld += pd[u];
-                        ls += ps[u];
-                    }
-                    a[i] = pack_bf16x2(pd[0], pd[1]);
-                    b[i] = pack_bf16x2(pd[0] - bf16_to_f32((bf16_t)(a[i] & 0xFFFF)),
-                                       pd[1] - bf16_to_f32((bf16_t)(a[i] >> 16)));
-                    c[i] = pack_bf16x2(ps[0], ps[1]);
-                    e[i] = pack_bf16x2(ps[0] - bf16_to_f32((bf16_t)(c[i] & 0xFFFF)),
-                                       ps[1] - bf16_to_f32((bf16_t)(c[i] >> 16)));
+                    const int kb = sl >> 1, r = 8 * (sl & 1) + 2 * i;
+                    const float e0 = fast_exp2(sv[kb][r] + mneg), e1 = fast_exp2(sv[kb][r + 1] + mneg);
+                    const uint32_t hi = pack_bf16x2(e0, e1);
+                    const uint32_t lo = pack_bf16x2(e0 - bf16_to_f32((bf16_t)(hi & 0xFFFF)),
+                                                    e1 - bf16_to_f32((bf16_t)(hi >> 16)));
+                    // bits of keys r, r+1 of block kb: 0xFFFF halves where routed
+                    const int b = 8 * (r >> 2) + (r & 3);
+                    const uint32_t word = mw[kb];
+                    const uint32_t sel = (((word >> b) & 1u) ? 0x0000FFFFu : 0u) |
+                                         (((word >> (b + 1)) & 1u) ? 0xFFFF0000u : 0u);
+                    a0[i] = hi & sel;
+                    b0[i] = hi ^ a0[i];
+                    a1[i] = lo & sel;
+                    b1[i] = lo ^ a1[i];
+                    ls = dot2_bf16(a0[i], ones, ls);
+                    ls = dot2_bf16(a1[i], ones, ls);
+                    lb = dot2_bf16(b0[i], ones, lb);
+                    lb = dot2_bf16(b1[i], ones, lb);
                 }
-                dh[sl] = make_uint4(a[0], a[1], a[2], a[3]);
-                dl[sl] = make_uint4(b[0], b[1], b[2], b[3]);
-                sh[sl] = make_uint4(c[0], c[1], c[2], c[3]);
-                sl4[sl] = make_uint4(e[0], e[1], e[2], e[3]);
+                ah[sl] = make_uint4(a0[0], a0[1], a0[2], a0[3]);
+                al[sl] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+                bh[sl] = make_uint4(b0[0], b0[1], b0[2], b0[3]);
+                bl[sl] = make_uint4(b1[0], b1[1], b1[2], b1[3]);
             }
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const uint4 a = vt_frag<D>(s_v[buf], db, sl, lane);
-                    od[db] = mfma32x32x16(a, dh[sl], od[db]);
-                    od[db] = mfma32x32x16(a, dl[sl], od[db]);
-                    os[db] = mfma32x32x16(a, sh[sl], os[db]);
-                    os[db] = mfma32x32x16(a, sl4[sl], os[db]);
+                    oa[db] = mfma32x32x16(a, ah[sl], oa[db]);
+                    ob[db] = mfma32x32x16(a, bh[sl], ob[db]);
+                    oa[db] = mfma32x32x16(a, al[sl], oa[db]);
+                    ob[db] = mfma32x32x16(a, bl[sl], ob[db]);
                 }
         }
         if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
     }
     if (!active) return;
-    ld = pair_sum(ld);
+    lb = pair_sum(lb);
     ls = pair_sum(ls);
     if (!pvalid) return;
     const size_t base = ((size_t)h * splits + split) * probes + p;
     if (lane < 32) {
         float4* ml = reinterpret_cast<float4*>(part_ml) + base;
-        *ml = make_float4(md, ld, ms, ls);
+        *ml = make_float4(m_run, ls + lb, m_run, ls);
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int dim = db * 32 + 8 * g + 4 * (lane >> 5);
+            const f32x16& a = oa[db];
+            const f32x16& b = ob[db];
             *reinterpret_cast<float4*>(part_od + base * D + dim) =
-                make_float4(od[db][4 * g], od[db][4 * g + 1], od[db][4 * g + 2], od[db][4 * g + 3]);
+                make_float4(a[4 * g] + b[4 * g], a[4 * g + 1] + b[4 * g + 1], a[4 * g + 2] + b[4 * g + 2],
+                            a[4 * g + 3] + b[4 * g + 3]);
             *reinterpret_cast<float4*>(part_os + base * D + dim) =
-                make_float4(os[db][4 * g], os[db][4 * g + 1], os[db][4 * g + 2], os[db][4 * g + 3]);
+                make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
         }
 }
 
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
                   const int32_t* probe_pos, const int32_t* probe_grp, int probes,
-                  const int32_t* kgrp, int gk, const int32_t* blocks, int gq, int kblk,
-                  float* part_ml, float* part_od, float* part_os, hipStream_t st) {
+                  const int32_t* kgrp, const int32_t* koff, int koff_stride, int gk,
+                  const int32_t* blocks, int gq, int kblk, float* part_ml, float* part_od,
+                  float* part_os, hipStream_t st) {
     if (probes == 0) return;
     const int splits = probe_splits(n);
     int chunk = (n + splits - 1) / splits;
@@ -614,11 +640,11 @@ void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int head
     dim3 grid((probes + kProbeRows - 1) / kProbeRows, splits, heads);
     if (d == 128)
         hipLaunchKernelGGL(k_probe<128>, grid, dim3(256), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
-                           probes, kgrp, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
+                           probes, kgrp, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
                            part_os);
     else
         hipLaunchKernelGGL(k_probe<64>, grid, dim3(256), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
-                           probes, kgrp, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
+                           probes, kgrp, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
                            part_os);
 }
 
