@@ -168,46 +168,79 @@ void launch_correct(const float* o_s, const bf16_t* bt16, const float* bvec, con
 namespace spr {
 
 // ------------------------------------------------------------- fit Grams ---
-// Column means of a [H][p][d] (fixed summation order).
+// Column means of a [H][p][d]: block per (head, 32 columns), 8 row partitions per column
+// (rows r = part, part + 8, ...), combined in a fixed order.
 template <typename T>
-__global__ void k_col_means(const T* __restrict__ a, int p, int d, double* __restrict__ mean) {
-    const int h = blockIdx.x, j = threadIdx.x;
-    if (j >= d) return;
+__global__ __launch_bounds__(256) void k_col_means(const T* __restrict__ a, int p, int d,
+                                                   double* __restrict__ mean) {
+    __shared__ double red[8][32];
+    const int h = blockIdx.y, j = blockIdx.x * 32 + (threadIdx.x & 31), part = threadIdx.x >> 5;
     double s = 0.0;
-    for (int r = 0; r < p; ++r) s += (double)a[((size_t)h * p + r) * d + j];
-    mean[(size_t)h * d + j] = (p > 0) ? s / p : 0.0;
+    for (int r = part; r < p; r += 8) s += (double)a[((size_t)h * p + r) * d + j];
+    red[part][threadIdx.x & 31] = s;
+    __syncthreads();
+    if (part == 0) {
+        double t = red[0][j & 31];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) t += red[q][j & 31];
+        mean[(size_t)h * d + j] = (p > 0) ? t / p : 0.0;
+    }
 }
 
 // out[h][i][j] = scale * sum_r (a[r][i] - ma[i]) (b[r][j] - mb[j]); ma / mb may be null.
+// Block per (head, 32 x 32 output tile): rows staged through LDS 32 at a time, each thread
+// accumulating 4 outputs over ascending r in fp64 (fixed order).
 template <typename T>
-__global__ void k_gram(const T* __restrict__ a, const T* __restrict__ b,
-                       const double* __restrict__ ma, const double* __restrict__ mb, int p, int d,
-                       double scale, double* __restrict__ out) {
-    const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
-    if (j >= d) return;
-    const double ai0 = ma ? ma[(size_t)h * d + i] : 0.0;
-    const double bj0 = mb ? mb[(size_t)h * d + j] : 0.0;
-    double s = 0.0;
-    for (int r = 0; r < p; ++r) {
-        const size_t row = ((size_t)h * p + r) * d;
-        s += ((double)a[row + i] - ai0) * ((double)b[row + j] - bj0);
+__global__ __launch_bounds__(256) void k_gram(const T* __restrict__ a, const T* __restrict__ b,
+                                              const double* __restrict__ ma,
+                                              const double* __restrict__ mb, int p, int d,
+                                              double scale, double* __restrict__ out) {
+    __shared__ double sa[32][33], sb[32][33];
+    const int h = blockIdx.z, ti = blockIdx.y * 32, tj = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const double ca = ma ? ma[(size_t)h * d + ti + tx] : 0.0;
+    const double cb = mb ? mb[(size_t)h * d + tj + tx] : 0.0;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int r0 = 0; r0 < p; r0 += 32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rr = ty + 8 * q, r = r0 + rr;
+            double va = 0.0, vb = 0.0;
+            if (r < p) {
+                const size_t row = ((size_t)h * p + r) * d;
+                va = (double)a[row + ti + tx] - ca;
+                vb = (double)b[row + tj + tx] - cb;
+            }
+            sa[rr][tx] = va;
+            sb[rr][tx] = vb;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int rr = 0; rr < 32; ++rr) {
+            const double bj = sb[rr][tx];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] += sa[rr][ty + 8 * q] * bj;
+        }
+        __syncthreads();
     }
-    out[((size_t)h * d + i) * d + j] = s * scale;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[((size_t)h * d + ti + ty + 8 * q) * d + tj + tx] = acc[q] * scale;
 }
 
 void launch_col_means_f32(const float* a, int heads, int p, int d, double* mean, hipStream_t st) {
-    hipLaunchKernelGGL(k_col_means<float>, dim3(heads), dim3(128), 0, st, a, p, d, mean);
+    hipLaunchKernelGGL(k_col_means<float>, dim3(d / 32, heads), dim3(256), 0, st, a, p, d, mean);
 }
 
 void launch_gram_f32(const float* a, const float* b, const double* ma, const double* mb, int heads,
                      int p, int d, double* out, hipStream_t st) {
-    hipLaunchKernelGGL(k_gram<float>, dim3(d, heads), dim3(128), 0, st, a, b, ma, mb, p, d, 1.0, out);
+    hipLaunchKernelGGL(k_gram<float>, dim3(d / 32, d / 32, heads), dim3(256), 0, st, a, b, ma, mb,
+                       p, d, 1.0, out);
 }
 
 void launch_gram_f64(const double* a, int heads, int p, int d, double scale, double* out,
                      hipStream_t st) {
-    hipLaunchKernelGGL(k_gram<double>, dim3(d, heads), dim3(128), 0, st, a, a, nullptr, nullptr, p,
-                       d, scale, out);
+    hipLaunchKernelGGL(k_gram<double>, dim3(d / 32, d / 32, heads), dim3(256), 0, st, a, a, nullptr,
+                       nullptr, p, d, scale, out);
 }
 
 }  // namespace spr
