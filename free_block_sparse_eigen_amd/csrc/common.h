@@ -74,6 +74,24 @@ __host__ __device__ inline int swz(int r) {
     return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
+// Buffer resource over `bytes` bytes from base (loads past the end return zero); word 3
+// (0x00020000) selects the 32-bit data format that untyped buffer loads need on gfx950.
+// Global-to-LDS loads go through buffer resources rather than global addresses because
+// the compiler then tracks them on the vector-memory counter alone: the global-address
+// form also marks the LDS counter as out of order, which turns every wait on an LDS read
+// into a wait for all of them.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// 16 bytes per lane from byte offset off (per lane) of r into LDS at s + 16 * lane
+// (s is the same for the whole wave)
+__device__ inline void lds_load16(rsrc_t r, void* s, int off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)s, 16, off,
+                                             0, 0, 0);
+}
+
 template <typename T>
 __device__ inline T wave_max(T v) {
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));

@@ -39,16 +39,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // (dims 8c..8c+7) at slot r * CH + (c ^ swz(r)). They are filled by direct
 // global-to-LDS loads (no VGPR staging): one 16-byte load per lane lands at
 // LDS base + 16 * lane, so the swizzle is applied to the global addresses instead.
-// Buffer resource over one head's [n][D] bf16 rows (loads past the end return zero).
-// Word 3 (0x00020000) selects the 32-bit data format that untyped buffer loads need on
-// this architecture. The loads below go through buffer resources rather than global
-// addresses because the compiler then tracks them on the vector-memory counter alone;
-// global-address loads into LDS also mark the LDS counter as out of order, which turns
-// every wait on an LDS read into a wait for all of them.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Buffer resource over one head's [n][D] bf16 rows.
 __device__ inline rsrc_t head_rsrc(const bf16_t* base, int n, int d) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0, n * d * 2,
-                                             0x00020000);
+    return make_rsrc(base, (uint32_t)n * d * 2);
 }
 
 template <int D, int NT = 256>
@@ -72,8 +65,8 @@ struct Tile {
         for (int m = 0; m < PER_WAVE; ++m) {
             int first;
             const int off = offset(phys, w, lane, m, first);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sk + first), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sv + first), 16, off, 0, 0, 0);
+            lds_load16(rk, sk + first, off);
+            lds_load16(rv, sv + first, off);
         }
     }
     // one tensor's tile (rows phys[]) into s
@@ -83,7 +76,7 @@ struct Tile {
         for (int m = 0; m < PER_WAVE; ++m) {
             int first;
             const int off = offset(phys, w, lane, m, first);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(s + first), 16, off, 0, 0, 0);
+            lds_load16(r, s + first, off);
         }
     }
 };

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
         s_red[w] = c2m;
         s_red[4 + w] = cpm;
     }
-    const bf16_t* ch = cpart + (size_t)h * 2 * groups * D;
+    const rsrc_t rc = make_rsrc(cpart + (size_t)h * 2 * groups * D, (uint32_t)(2 * groups * D * 2));
     auto issue = [&](int t, uint4* buf) {
 #pragma unroll
         for (int m = 0; m < PER; ++m) {
@@ -243,8 +243,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
             const int part = slot / (TG * CH), rem = slot % (TG * CH);
             const int row = rem / CH, pc = rem % CH;
             const int g = min(t * TG + row, groups - 1);
-            const bf16_t* src = ch + ((size_t)part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8);
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + first), 16, 0, 0);
+            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8)) * 2);
         }
     };
     issue(0, s_c0);
@@ -289,15 +288,22 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
             const int gb = t * TG + 32 * sub;
             if (gb >= groups) break;
             f32x16 acc[2] = {};
-            const int row = 32 * sub + (lane & 31);
+            const int row = 32 * sub + (lane & 31), sw = swz<CH>(row);
+            const uint4* cr = buf + row * CH;
+            // hi then lo part, each over the depth; fragments read one step ahead
+            constexpr int KS = D / 16;
+            uint4 a = cr[half ^ sw];
 #pragma unroll
-            for (int part = 0; part < 2; ++part)
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const uint4 a = buf[part * TG * CH + row * CH + ((2 * kk + half) ^ swz<CH>(row))];
-                    acc[0] = mfma32x32x16(a, xf[0][kk], acc[0]);
-                    acc[1] = mfma32x32x16(a, xf[1][kk], acc[1]);
+            for (int i = 0; i < 2 * KS; ++i) {
+                uint4 nx = a;
+                if (i + 1 < 2 * KS) {
+                    const int p2 = (i + 1) / KS, k2 = (i + 1) % KS;
+                    nx = cr[p2 * TG * CH + ((2 * k2 + half) ^ sw)];
                 }
+                acc[0] = mfma32x32x16(a, xf[0][i % KS], acc[0]);
+                acc[1] = mfma32x32x16(a, xf[1][i % KS], acc[1]);
+                a = nx;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int g = gb + 8 * (r >> 2) + 4 * half + (r & 3);
