@@ -271,7 +271,6 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
             const uint4* k0p = sk + rl * TL::CH;
             const uint4* k1p = sk + (32 + rl) * TL::CH;
             f32x16 s0 = {}, s1 = {};
-            __builtin_amdgcn_s_setprio(1);      // MFMA phases at raised wave priority
             uint4 a0 = k0p[half ^ sw], a1 = k1p[half ^ sw];
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
@@ -286,7 +285,6 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
                 a0 = n0;
                 a1 = n1;
             }
-            __builtin_amdgcn_s_setprio(0);
             // V^T fragments of keys 0..31, read now so that the softmax hides their latency
             uint4 vf[2][DB];
 #pragma unroll
@@ -330,7 +328,6 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
                 }
                 pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
-            __builtin_amdgcn_s_setprio(1);
             // PV of keys 0..31; each consumed fragment's registers take the fragment of
             // the slice two further on, and the exponentials of keys 32..63 run alongside
 #pragma unroll
@@ -363,7 +360,6 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // its two LDS reads
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
             }
-            __builtin_amdgcn_s_setprio(0);
         }
         if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
