@@ -353,13 +353,6 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
             for (int sl = 2; sl < 4; ++sl)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[db] = mfma32x32x16(vf[sl - 2][db], pb[sl], o[db]);
-            // interleave: the first 2*DB MFMAs of PV with the exponentials of keys 32..63
-#pragma unroll
-            for (int i = 0; i < 2 * DB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // its two LDS reads
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
-            }
         }
         if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
