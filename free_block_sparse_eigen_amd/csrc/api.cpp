@@ -591,7 +591,7 @@ int32_t sparsepr_correct(sparsepr_ctx* c, void* o, void* stream) {
     if (!o || !aligned16(o)) return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned o");
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
-    launch_correct(c->o_s, c->bt16, c->bv32, c->pod, c->probe_of, c->qperm, c->H, c->N, c->d, c->P, o,
+    launch_correct(c->o_s, c->bt16, c->bv32, c->pod, c->probe_orig, c->qperm, c->H, c->N, c->d, c->P, o,
                    c->p.dtype == SPARSEPR_F32 ? 1 : 0, st);
     SPR_LAUNCHED(c, "correct");
     mark(c, 7, st);

@@ -72,7 +72,7 @@ void launch_probe_merge(int heads, int probes, int d, int splits, const float* p
 
 // ---- correction ----
 void launch_correct(const float* o_s, const bf16_t* bt16, const float* bvec, const float* od,
-                    const int32_t* probe_of, const int32_t* qperm, int heads, int n, int d,
+                    const int32_t* probe_orig, const int32_t* qperm, int heads, int n, int d,
                     int probes, void* o, int out_f32, hipStream_t st);
 
 // ---- fit Grams (fp64) ----

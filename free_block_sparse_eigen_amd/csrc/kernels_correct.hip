@@ -11,11 +11,13 @@ namespace spr {
 //       host, staged in LDS once per block with coalesced loads,
 //   B = X^T  (depth = i, columns = rows), X's fp32 rows split into bf16 hi/lo in VGPRs,
 // three products hi.hi + hi.lo + lo.hi (relative error about 2^-16 of |X||B'|, so the
-// correction stays accurate when |B'| is large). Each lane then owns one row: it adds
-// X and b', or takes the exact dense output for a probe row. The finished rows go
-// through LDS so that each output row is stored whole, at its original token index.
-// Blocks (8 waves) are persistent within a head: each stages B' once and walks tiles of
-// 256 rows.
+// correction stays accurate when |B'| is large). Each lane then owns one row and adds X
+// and b' to its columns; the X values it needs there come from its own and its partner
+// lane's (l ^ 32) fragments through one lane-half swap per value, not a second read. The
+// finished rows go through LDS so that each output row is stored whole, at its original
+// token index. Probe rows are overwritten with their exact dense output afterwards
+// (k_probe_rows). Blocks (8 waves) are persistent within a head: each stages B' once and
+// walks tiles of 256 rows, the next tile's rows loaded while the current one is computed.
 constexpr int kCorrWaves = 8;
 constexpr int kCorrRows = 32 * kCorrWaves;
 
@@ -23,12 +25,11 @@ template <int D>
 __global__ __launch_bounds__(64 * kCorrWaves, 1) void k_correct(const float* __restrict__ o_s,
                                                     const bf16_t* __restrict__ bt16,
                                                     const float* __restrict__ bvec,
-                                                    const float* __restrict__ od,
-                                                    const int32_t* __restrict__ probe_of,
                                                     const int32_t* __restrict__ qperm, int n,
-                                                    int probes, void* __restrict__ out, int out_f32) {
+                                                    void* __restrict__ out, int out_f32) {
     constexpr int CH = D / 8;          // 16-byte chunks per bf16 row of B'^T
     constexpr int JB = D / 32;         // 32-column output blocks
+    constexpr int KS = D / 16;         // depth steps
     __shared__ uint4 s_b[2][D * CH];   // B'^T hi / lo: row j, chunk c at c ^ swz(j)
     constexpr int SROW = D * 2 + 16;                 // staged row pitch in bytes (padded)
     __shared__ uint4 s_out[kCorrWaves][32 * SROW / 16];   // per wave: 32 bf16 rows (16 fp32 rows)
@@ -49,27 +50,35 @@ __global__ __launch_bounds__(64 * kCorrWaves, 1) void k_correct(const float* __r
     const int pitch = out_f32 ? 2 * SROW - 16 : SROW; // bytes per staged row (16 B of padding)
     char* stage = reinterpret_cast<char*>(&s_out[w][0]);
     const int ntile = (n + kCorrRows - 1) / kCorrRows;
-    for (int tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
-        const int row_base = tile * kCorrRows + w * 32;
-        const int row = row_base + (lane & 31);
+
+    // a tile's rows for this lane: X fragments (an invalid row reads row 0) and the
+    // original token index
+    float4 xa[KS][2];
+    int dst_row = 0;
+    auto load_tile = [&](int tile, float4 (&x)[KS][2], int& dr) {
+        const int row = tile * kCorrRows + w * 32 + (lane & 31);
         const bool valid = row < n;
         const float* xr = o_s + ((size_t)h * n + (valid ? row : 0)) * D;
-        const int pi = valid ? probe_of[(size_t)h * n + row] : -1;
-        const int dst_row = valid ? qperm[(size_t)h * n + row] : 0;   // original token index
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            x[kk][0] = *reinterpret_cast<const float4*>(xr + 16 * kk + 8 * half);
+            x[kk][1] = *reinterpret_cast<const float4*>(xr + 16 * kk + 8 * half + 4);
+        }
+        dr = valid ? qperm[(size_t)h * n + row] : 0;
+    };
+    if (blockIdx.x < ntile) load_tile(blockIdx.x, xa, dst_row);
+    for (int tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
+        const int row_base = tile * kCorrRows + w * 32;
+        const bool valid = row_base + (lane & 31) < n;
+        float4 xn[KS][2];
+        int dn = 0;
+        if (tile + (int)gridDim.x < ntile) load_tile(tile + gridDim.x, xn, dn);
+        __builtin_amdgcn_sched_barrier(0);      // the next tile's loads go out first
         f32x16 acc[JB];
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) acc[jb] = f32x16{};
-        // every X load of the tile issued up front, unconditionally (an invalid row reads
-        // row 0 and is zeroed), so their latencies overlap
-        float4 xa[D / 16][2];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            xa[kk][0] = *reinterpret_cast<const float4*>(xr + 16 * kk + 8 * half);
-            xa[kk][1] = *reinterpret_cast<const float4*>(xr + 16 * kk + 8 * half + 4);
-        }
-        __builtin_amdgcn_sched_barrier(0);      // keep the loads ahead of the math
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
+        for (int kk = 0; kk < KS; ++kk) {
             const float zf = valid ? 1.f : 0.f;
             float xv[8] = {xa[kk][0].x * zf, xa[kk][0].y * zf, xa[kk][0].z * zf, xa[kk][0].w * zf,
                            xa[kk][1].x * zf, xa[kk][1].y * zf, xa[kk][1].z * zf, xa[kk][1].w * zf};
@@ -93,22 +102,33 @@ __global__ __launch_bounds__(64 * kCorrWaves, 1) void k_correct(const float* __r
                 acc[jb] = mfma32x32x16(alo, bhi, acc[jb]);
             }
         }
-        // this lane: row `row`, columns j = jb*32 + 8g + 4*half + 0..3
-        const float* src = (pi >= 0) ? od + ((size_t)h * probes + pi) * D : xr;
-        const bool corr = pi < 0;
+        // this lane: row `row`, columns j = jb*32 + 8g + 4*half + 0..3, i.e. depth step
+        // kk = 2jb + g/2 at offset 8(g%2) + 4*half. It holds offsets 8*half + 0..7 of every
+        // step; swapping fragment 0 of the low lane half with fragment 1 of the high half
+        // leaves offsets 4*half + 0..3 (g even) in xa[kk][0] and 8 + 4*half + 0..3 (g odd)
+        // in xa[kk][1] on every lane.
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float* f0 = reinterpret_cast<float*>(&xa[kk][0]);
+            float* f1 = reinterpret_cast<float*>(&xa[kk][1]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(f0[e]),
+                                                                __float_as_uint(f1[e]), false, false);
+                f0[e] = __uint_as_float(r[0]);
+                f1[e] = __uint_as_float(r[1]);
+            }
+        }
         float res[JB][16];
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int j = jb * 32 + 8 * g + 4 * half;
-                const float4 xv = *reinterpret_cast<const float4*>(src + j);
+                const float4 xv = xa[2 * jb + (g >> 1)][g & 1];
                 const float v[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float c = (v[e] + s_bv[j + e]) + acc[jb][4 * g + e];
-                    res[jb][4 * g + e] = corr ? c : v[e];
-                }
+                for (int e = 0; e < 4; ++e) res[jb][4 * g + e] = (v[e] + s_bv[j + e]) + acc[jb][4 * g + e];
             }
         // stage finished rows in the wave's own LDS area (a wave-level barrier suffices),
         // then store whole rows: 16-byte pieces, consecutive lanes along a row
@@ -144,11 +164,29 @@ __global__ __launch_bounds__(64 * kCorrWaves, 1) void k_correct(const float* __r
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            xa[kk][0] = xn[kk][0];
+            xa[kk][1] = xn[kk][1];
+        }
+        dst_row = dn;
     }
 }
 
+// Probe rows take their exact dense output: out[h][probe_orig[p]] = od[h][p] (after
+// k_correct, same stream). Block per (probe, head), one thread per column.
+__global__ void k_probe_rows(const float* __restrict__ od, const int32_t* __restrict__ probe_orig,
+                             int n, int d, int probes, void* __restrict__ out, int out_f32) {
+    const int p = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+    if (j >= d) return;
+    const float v = od[((size_t)h * probes + p) * d + j];
+    const size_t o = ((size_t)h * n + probe_orig[(size_t)h * probes + p]) * d + j;
+    if (out_f32) static_cast<float*>(out)[o] = v;
+    else static_cast<bf16_t*>(out)[o] = f32_to_bf16(v);
+}
+
 void launch_correct(const float* o_s, const bf16_t* bt16, const float* bvec, const float* od,
-                    const int32_t* probe_of, const int32_t* qperm, int heads, int n, int d,
+                    const int32_t* probe_orig, const int32_t* qperm, int heads, int n, int d,
                     int probes, void* o, int out_f32, hipStream_t st) {
     const int ntile = (n + kCorrRows - 1) / kCorrRows;
     int per_head = (256 + heads - 1) / heads;         // about one resident block per CU
@@ -156,11 +194,14 @@ void launch_correct(const float* o_s, const bf16_t* bt16, const float* bvec, con
     if (per_head < 1) per_head = 1;
     dim3 grid(per_head, heads);
     if (d == 128)
-        hipLaunchKernelGGL(k_correct<128>, grid, dim3(64 * kCorrWaves), 0, st, o_s, bt16, bvec, od, probe_of, qperm,
-                           n, probes, o, out_f32);
+        hipLaunchKernelGGL(k_correct<128>, grid, dim3(64 * kCorrWaves), 0, st, o_s, bt16, bvec, qperm,
+                           n, o, out_f32);
     else
-        hipLaunchKernelGGL(k_correct<64>, grid, dim3(64 * kCorrWaves), 0, st, o_s, bt16, bvec, od, probe_of, qperm,
-                           n, probes, o, out_f32);
+        hipLaunchKernelGGL(k_correct<64>, grid, dim3(64 * kCorrWaves), 0, st, o_s, bt16, bvec, qperm,
+                           n, o, out_f32);
+    if (probes > 0)
+        hipLaunchKernelGGL(k_probe_rows, dim3(probes, heads), dim3(d), 0, st, od, probe_orig, n, d,
+                           probes, o, out_f32);
 }
 
 }  // namespace spr
