@@ -5,10 +5,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <condition_variable>
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <memory>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <thread>
@@ -18,6 +22,69 @@
 #include "kernels.h"
 
 using namespace spr;
+
+namespace {
+
+// Host worker threads kept for the life of a context (starting threads per call costs
+// more than the per-head work they run). run() hands tasks 0..n-1 out through an atomic
+// counter to the workers and the calling thread, and returns when all have finished.
+class HostPool {
+public:
+    explicit HostPool(int workers) {
+        for (int i = 0; i < workers; ++i) th_.emplace_back([this] { loop(); });
+    }
+    ~HostPool() {
+        {
+            std::lock_guard<std::mutex> g(m_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto& t : th_) t.join();
+    }
+    void run(int tasks, const std::function<void(int)>& fn) {
+        {
+            std::lock_guard<std::mutex> g(m_);
+            job_ = &fn;
+            ntasks_ = tasks;
+            next_.store(0);
+            ++gen_;
+        }
+        cv_.notify_all();
+        drain();
+        std::unique_lock<std::mutex> lk(m_);
+        done_.wait(lk, [&] { return active_ == 0 && next_.load() >= ntasks_; });
+    }
+
+private:
+    void drain() {
+        for (int t; (t = next_.fetch_add(1)) < ntasks_;) (*job_)(t);
+    }
+    void loop() {
+        unsigned seen = 0;
+        std::unique_lock<std::mutex> lk(m_);
+        for (;;) {
+            cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+            if (stop_) return;
+            seen = gen_;
+            ++active_;
+            lk.unlock();
+            drain();
+            lk.lock();
+            if (--active_ == 0) done_.notify_all();
+        }
+    }
+    std::mutex m_;
+    std::condition_variable cv_, done_;
+    std::vector<std::thread> th_;
+    const std::function<void(int)>* job_ = nullptr;
+    int ntasks_ = 0;
+    std::atomic<int> next_{0};
+    int active_ = 0;
+    unsigned gen_ = 0;
+    bool stop_ = false;
+};
+
+}  // namespace
 
 struct sparsepr_ctx {
     sparsepr_params p{};
@@ -74,6 +141,7 @@ struct sparsepr_ctx {
     int64_t calls = 0;
     int64_t stats_from = 0;            // first call averaged by the next sparsepr_get_stats
     int slot = 0;
+    std::unique_ptr<HostPool> pool;    // host workers for per-head work (made on first use)
 };
 
 namespace {
@@ -204,19 +272,16 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.dense_unit_list, c.dense_units);
 }
 
-void parallel_heads(int heads, const std::function<void(int)>& fn) {
+// fn(h) for every head on the context's host workers (up to 16 threads with the caller)
+void parallel_heads(sparsepr_ctx* c, int heads, const std::function<void(int)>& fn) {
     const int hw = std::max(1u, std::thread::hardware_concurrency());
-    const int nt = std::min(heads, std::min(hw, 16));
-    if (nt <= 1) {
+    const int nt = std::min(hw, 16);
+    if (nt <= 1 || heads <= 1) {
         for (int h = 0; h < heads; ++h) fn(h);
         return;
     }
-    std::vector<std::thread> pool;
-    for (int t = 0; t < nt; ++t)
-        pool.emplace_back([&, t]() {
-            for (int h = t; h < heads; h += nt) fn(h);
-        });
-    for (auto& th : pool) th.join();
+    if (!c->pool) c->pool.reset(new HostPool(nt - 1));
+    c->pool->run(heads, fn);
 }
 
 int32_t fail(sparsepr_ctx* c, int32_t code, const std::string& msg) {
@@ -415,7 +480,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     SPR_HIP(c, hipStreamSynchronize(st));
     c->h_w64.assign(H * d * rK, 0.0);
     std::vector<int> prc(H, 0);
-    parallel_heads((int)H, [&](int h) {
+    parallel_heads(c, (int)H, [&](int h) {
         prc[h] = key_projection((int)d, &c->h_mk[h * d * d], (int)rK, &c->h_w64[h * d * rK]);
     });
     for (size_t h = 0; h < H; ++h) {
@@ -556,7 +621,7 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
         const double* hm = c->h_fit;
         const double* hg = c->h_fit + H * 2 * d;
         std::vector<int> frc(H, 0);
-        parallel_heads((int)H, [&](int h) {
+        parallel_heads(c, (int)H, [&](int h) {
             frc[h] = probe_fit_from_grams((int)P, (int)d, &hm[h * d], &hm[(H + h) * d], &hg[h * d * d],
                                           &hg[(H + h) * d * d], &hg[(2 * H + h) * d * d],
                                           c->p.ridge_lambda, c->p.corr_rank, &c->h_bm[h * d * d],
