@@ -123,10 +123,12 @@ struct sparsepr_ctx {
     int2* dense_unit_list = nullptr;
 
     // host mirrors
-    std::vector<double> h_mk, h_w64, h_bm, h_bv;
+    std::vector<double> h_bm, h_bv;
     std::vector<float> h_x, h_y;
     // pinned host buffers of the fit: Grams in (device -> host), B' and b' out
     double* h_fit = nullptr;          // [H][2][d] means, then [H][3][d][d] Grams
+    double* h_mkp = nullptr;          // [H][d][d] M_K (device -> host)
+    double* h_wp = nullptr;           // [H][d][r_K] key projection W (host -> device)
     void* h_b32 = nullptr;            // [H][2][d][d] bf16 B'^T hi/lo, then [H][d] fp32 b'
     hipEvent_t ev_probe = nullptr;    // probe rows and fit Grams are on the host
 
@@ -421,6 +423,8 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     {
         const size_t H = c->H, d = c->d;
         if (hipHostMalloc(reinterpret_cast<void**>(&c->h_fit), sizeof(double) * H * (2 * d + 3 * d * d)) != hipSuccess ||
+            hipHostMalloc(reinterpret_cast<void**>(&c->h_mkp), sizeof(double) * H * d * d) != hipSuccess ||
+            hipHostMalloc(reinterpret_cast<void**>(&c->h_wp), sizeof(double) * H * d * c->rK) != hipSuccess ||
             hipHostMalloc(&c->h_b32, sizeof(float) * H * (d * d + d)) != hipSuccess ||
             hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming) != hipSuccess) {
             sparsepr_destroy(c);
@@ -453,6 +457,8 @@ void sparsepr_destroy(sparsepr_ctx* c) {
                 if (e) (void)hipEventDestroy(e);
     if (c->ev_probe) (void)hipEventDestroy(c->ev_probe);
     if (c->h_fit) (void)hipHostFree(c->h_fit);
+    if (c->h_mkp) (void)hipHostFree(c->h_mkp);
+    if (c->h_wp) (void)hipHostFree(c->h_wp);
     if (c->h_b32) (void)hipHostFree(c->h_b32);
     if (c->arena) (void)hipFree(c->arena);
     delete c;
@@ -474,19 +480,18 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     // M_K and its leading eigenvectors (host fp64)
     launch_metric(q16, c->H, c->N, c->d, c->p.n_sample, c->weyl_a, c->mk, st);
     SPR_LAUNCHED(c, "metric");
-    c->h_mk.resize(H * d * d);
-    SPR_HIP(c, hipMemcpyAsync(c->h_mk.data(), c->mk, sizeof(double) * H * d * d,
-                              hipMemcpyDeviceToHost, st));
+    // (pinned staging both ways; W is rewritten only after the next call's sync)
+    SPR_HIP(c, hipMemcpyAsync(c->h_mkp, c->mk, sizeof(double) * H * d * d, hipMemcpyDeviceToHost, st));
     SPR_HIP(c, hipStreamSynchronize(st));
-    c->h_w64.assign(H * d * rK, 0.0);
     std::vector<int> prc(H, 0);
     parallel_heads(c, (int)H, [&](int h) {
-        prc[h] = key_projection((int)d, &c->h_mk[h * d * d], (int)rK, &c->h_w64[h * d * rK]);
+        std::fill(c->h_wp + h * d * rK, c->h_wp + (h + 1) * d * rK, 0.0);
+        prc[h] = key_projection((int)d, c->h_mkp + h * d * d, (int)rK, c->h_wp + h * d * rK);
     });
     for (size_t h = 0; h < H; ++h) {
         if (prc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "metric eigensolve failed (non-finite input)");
     }
-    SPR_HIP(c, hipMemcpyAsync(c->w64, c->h_w64.data(), sizeof(double) * H * d * rK, hipMemcpyHostToDevice, st));
+    SPR_HIP(c, hipMemcpyAsync(c->w64, c->h_wp, sizeof(double) * H * d * rK, hipMemcpyHostToDevice, st));
     // keys: Lloyd in the M_K eigen-coordinates
     rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw, c->kc64,
                c->kcp, c->kcn2, c->kcpn, c->kc2, st);
