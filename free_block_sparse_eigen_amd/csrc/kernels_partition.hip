@@ -570,12 +570,12 @@ void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, i
 // reduction; mean = sum / count (zero if empty). With l64 given, the non-empty groups
 // then get their projected centroid, screening vector and norms (k_finish).
 template <int D>
-__global__ __launch_bounds__(256) void k_group_sum(const bf16_t* __restrict__ x, int n,
+__global__ __launch_bounds__(512) void k_group_sum(const bf16_t* __restrict__ x, int n,
                                                    const int32_t* __restrict__ sorted,
                                                    const int32_t* __restrict__ off, int groups,
                                                    double* __restrict__ mean_raw) {
     constexpr int CH = D / 8;          // 16-byte chunks per row
-    constexpr int RL = 256 / CH;       // row lanes
+    constexpr int RL = 512 / CH;       // row lanes
     constexpr int IDX = 2048;          // member indices staged per pass
     __shared__ double red[RL][D + 1];
     __shared__ int s_idx[IDX];
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(256) void k_group_sum(const bf16_t* __restrict__ x,
     for (int p0 = 0; p0 < cnt; p0 += IDX) {
         const int np = min(IDX, cnt - p0);
         __syncthreads();
-        for (int i = tid; i < np; i += 256) s_idx[i] = sh[beg + p0 + i];
+        for (int i = tid; i < np; i += 512) s_idx[i] = sh[beg + p0 + i];
         __syncthreads();
         int m = rl;
         for (; m + 7 * RL < np; m += 8 * RL) {
@@ -630,10 +630,10 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
                         double* c2_64, hipStream_t st) {
     if (d == 128)
-        hipLaunchKernelGGL(k_group_sum<128>, dim3(groups, heads), dim3(256), 0, st, x, n, sorted, off,
+        hipLaunchKernelGGL(k_group_sum<128>, dim3(groups, heads), dim3(512), 0, st, x, n, sorted, off,
                            groups, mean_raw);
     else
-        hipLaunchKernelGGL(k_group_sum<64>, dim3(groups, heads), dim3(256), 0, st, x, n, sorted, off,
+        hipLaunchKernelGGL(k_group_sum<64>, dim3(groups, heads), dim3(512), 0, st, x, n, sorted, off,
                            groups, mean_raw);
     if (l64 != nullptr)
         launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, st);
