@@ -170,17 +170,6 @@ __device__ inline bool unit_of_block(const int32_t* __restrict__ nunits, int str
     return found;
 }
 
-// Key tile -> physical rows: the smallest segment s with prefix[s+1] > u holds virtual key u.
-__device__ inline int segment_row(const int* __restrict__ pre, const int* __restrict__ start,
-                                  int nseg, int u) {
-    int lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid + 1] > u) hi = mid; else lo = mid + 1;
-    }
-    return start[lo] + (u - pre[lo]);
-}
-
 }  // namespace
 
 // Block = 8 waves x 32 query rows: a unit of up to 256 rows shares every key tile.
@@ -228,11 +217,17 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
     const int U = s_pre[kblk];
     const int ntiles = (U + KT - 1) / KT;
 
-    // rows of tile t; keys past the union repeat the tile's first row (masked later)
+    // rows of tile t; keys past the union repeat the tile's first row (masked later).
+    // Tiles are filled in order by the first wave: each lane advances from the segment of
+    // the previous tile's last key (usually zero or one step) instead of a binary search.
+    int seg_carry = 0;
     auto fill_phys = [&](int t, int buf) {
         if (tid < KT) {
-            const int u = t * KT + tid;
-            s_phys[buf][tid] = segment_row(s_pre, s_start, kblk, (u < U) ? u : t * KT);
+            const int u = (t * KT + tid < U) ? t * KT + tid : t * KT;
+            int sg = seg_carry;
+            while (s_pre[sg + 1] <= u) ++sg;
+            s_phys[buf][tid] = s_start[sg] + (u - s_pre[sg]);
+            seg_carry = __shfl(sg, KT - 1, 64);
         }
     };
 
