@@ -100,7 +100,7 @@ struct sparsepr_ctx {
     bf16_t *qp = nullptr, *kp = nullptr, *vp = nullptr;
     // partition
     int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
-    int32_t *koff = nullptr, *qoff = nullptr, *kgrp = nullptr;
+    int32_t *koff = nullptr, *qoff = nullptr;
     int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
     double *mk = nullptr, *w64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
     double *kc2 = nullptr, *qc2 = nullptr;               // fp64 |c|^2 per centroid
@@ -208,7 +208,7 @@ void derive(sparsepr_ctx& c) {
     c.nblk = (c.N + kSortChunk - 1) / kSortChunk;
     c.maxu = (c.N + kAttnRows - 1) / kAttnRows + c.Gq;
     c.dense_units = (c.N + kAttnRows - 1) / kAttnRows;
-    c.splits = probe_splits(c.N);
+    c.splits = probe_splits(c.N, c.H, c.P);
     c.gmax = std::max(c.Gk, c.Gq);
     c.weyl_a = weyl_multiplier(c.N);
 }
@@ -230,7 +230,6 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.qperm, HN);
     a.take(c.koff, H * (c.Gk + 1));
     a.take(c.qoff, H * (c.Gq + 1));
-    a.take(c.kgrp, HN);
     a.take(c.flag_cnt, 2 * (size_t)c.T * H);
     a.take(c.flag_list, HN);
     a.take(c.blkhist, H * c.nblk * c.gmax);
@@ -556,7 +555,6 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, st);
     launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
     SPR_LAUNCHED(c, "permute");
-    launch_fill_groups(c->koff, c->H, c->N, c->Gk, c->kgrp, st);
     launch_fill_i64(c->pairs, 0, c->H, st);
     launch_route(c->qraw, c->kraw, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k, c->blocks,
                  c->ucount, c->pairs, st);
@@ -580,9 +578,9 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     // Probe rows first, with the fit's fp64 means and Grams, copied to pinned host
     // memory; the host solve (sparsepr_probe_fit) then overlaps the main kernel.
     if (c->P > 0) {
-        launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P, c->kgrp,
-                     c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->part_ml, c->part_od,
-                     c->part_os, st);
+        launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P,
+                     c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->splits, c->part_ml,
+                     c->part_od, c->part_os, st);
         launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
                            c->py, c->pod, st);
         SPR_LAUNCHED(c, "probe rows");

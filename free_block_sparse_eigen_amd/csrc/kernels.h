@@ -11,7 +11,7 @@ constexpr int kSortChunk = 1024;      // points per counting-sort block
 constexpr int kMaxGroups = 1024;      // G_k, G_q upper bound (LDS tables)
 constexpr int kAttnRows = 256;        // query rows per attention work unit
 constexpr int kKeyTile = 64;          // keys per attention tile
-constexpr int kProbeRows = 128;       // probe rows per probe work unit
+constexpr int kProbeRows = 256;       // probe rows per probe work unit (8 waves of 32)
 
 // ---- generic ----
 void launch_to_bf16(const float* in, bf16_t* out, size_t count, hipStream_t st);
@@ -42,8 +42,6 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,
                     hipStream_t st);
-void launch_fill_groups(const int32_t* off, int heads, int n, int groups, int32_t* grp,
-                        hipStream_t st);
 void launch_route(const double* cq, const double* ck, const int32_t* qoff, const int32_t* koff,
                   int heads, int gq, int gk, int d, int k, int32_t* blocks, int32_t* ucount,
                   int64_t* pairs, hipStream_t st);
@@ -60,12 +58,12 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
                  void* out, int out_mode, hipStream_t st);
-int probe_splits(int n);
+int probe_splits(int n, int heads, int probes);
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
                   const int32_t* probe_pos, const int32_t* probe_grp, int probes,
-                  const int32_t* kgrp, const int32_t* koff, int koff_stride, int gk,
-                  const int32_t* blocks, int gq, int kblk, float* part_ml, float* part_od,
-                  float* part_os, hipStream_t st);
+                  const int32_t* koff, int koff_stride, int gk, const int32_t* blocks, int gq,
+                  int kblk, int splits, float* part_ml, float* part_od, float* part_os,
+                  hipStream_t st);
 void launch_probe_merge(int heads, int probes, int d, int splits, const float* part_ml,
                         const float* part_od, const float* part_os, float* x, float* y, float* od,
                         hipStream_t st);

@@ -69,6 +69,19 @@ struct Tile {
             lds_load16(rv, sv + first, off);
         }
     }
+    // rows row0 .. row0 + KT - 1 of both tensors (a contiguous tile)
+    __device__ static void issue_rows(rsrc_t rk, rsrc_t rv, int row0, uint4* sk, uint4* sv, int w,
+                                      int lane) {
+#pragma unroll
+        for (int m = 0; m < PER_WAVE; ++m) {
+            const int first = (w * PER_WAVE + m) * 64;
+            const int slot = first + lane;
+            const int r = slot / CH, pc = slot % CH;
+            const int off = ((row0 + r) * D + ((pc ^ swz<CH>(r)) * 8)) * 2;
+            lds_load16(rk, sk + first, off);
+            lds_load16(rv, sv + first, off);
+        }
+    }
     // one tensor's tile (rows phys[]) into s
     __device__ static void issue_one(rsrc_t r, const int* __restrict__ phys, uint4* s, int w,
                                      int lane) {
@@ -400,29 +413,46 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
 }
 
 // ------------------------------------------------------------------- probes ---
-// Work unit = (head, 128 probe rows, one key split). Both accumulators share the logits:
-// the dense one over every key, the routed one over keys whose group is routed for the
-// probe's query group. P.V uses a bf16 hi/lo split of P (about 2^-17 relative) so that
-// the probe outputs are near fp32 accuracy. Partial (max, sum, unnormalised O) per split.
-int probe_splits(int n) {
-    int s = (n + 2047) / 2048;
-    if (s < 1) s = 1;
-    if (s > 128) s = 128;
-    return s;
+// Work unit = (head, 256 probe rows = 8 waves of 32, one contiguous split of the head's
+// keys). Keys are in group-major order, so a split's tiles are plain row ranges and the
+// routed keys of a tile are whole runs of groups found from the group offsets. Both
+// accumulators share the logits: the dense one over every key, the routed one over keys
+// whose group is routed for the probe's query group. P.V uses a bf16 hi/lo split of P
+// (about 2^-17 relative) so that the probe outputs are near fp32 accuracy. Partial (max,
+// sum, unnormalised O) per split. Two waves share each SIMD (one block per CU), so one
+// wave's exponentials overlap the other's matrix products.
+int probe_splits(int n, int heads, int probes) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    const int units = heads * std::max(1, (probes + kProbeRows - 1) / kProbeRows);
+    const int max_s = std::max(1, std::min(128, (n + KT - 1) / KT));
+    // fewest key tiles per CU over the whole grid (one block per CU at a time), plus a
+    // per-block cost of two tiles for the prologue and the partial write
+    int best = 1;
+    long best_cost = -1;
+    for (int s = 1; s <= max_s; ++s) {
+        const int chunk = ((n + s - 1) / s + KT - 1) / KT;        // tiles per block
+        const long rounds = ((long)units * s + cus - 1) / cus;
+        const long cost = rounds * (chunk + 2);
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = s; }
+    }
+    return best;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_probe(
+__global__ __launch_bounds__(512, 1) void k_probe(
     const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     int n, const int32_t* __restrict__ probe_pos, const int32_t* __restrict__ probe_grp,
-    int probes, const int32_t* __restrict__ kgrp, const int32_t* __restrict__ koff, int koff_stride,
-    int gk, const int32_t* __restrict__ blocks, int gq, int kblk, int chunk, float scale_log2,
+    int probes, const int32_t* __restrict__ koff, int koff_stride, int gk,
+    const int32_t* __restrict__ blocks, int gq, int kblk, int chunk, float scale_log2,
     float* __restrict__ part_ml, float* __restrict__ part_od, float* __restrict__ part_os) {
-    using TL = Tile<D>;
+    using TL = Tile<D, 512>;
     constexpr int DB = D / 32;
-    __shared__ int s_phys[2][KT];
-    __shared__ int s_kg[2][KT];
-    __shared__ uint32_t s_bits[kProbeRows][kMaxGroups / 32 + 1];   // padded rows: no bank conflicts
+    constexpr int BW = kMaxGroups / 32 + 1;                      // odd row pitch: no bank conflicts
+    __shared__ uint32_t s_bits[kProbeRows][BW];
+    __shared__ int s_ko[kMaxGroups + 1];
     __shared__ uint4 s_k[2][TL::SLOTS];
     __shared__ uint4 s_v[2][TL::SLOTS];
 
@@ -431,10 +461,19 @@ __global__ __launch_bounds__(256) void k_probe(
     const int p0 = blockIdx.x * kProbeRows;
     const size_t head_row0 = (size_t)h * n;
     const int32_t* ko = koff + (size_t)h * koff_stride;
-    for (int i = tid; i < kProbeRows * (kMaxGroups / 32 + 1); i += 256) (&s_bits[0][0])[i] = 0u;
+    const int k0 = split * chunk;
+    const int k1 = min(n, k0 + chunk);
+    const int ntiles = (max(0, k1 - k0) + KT - 1) / KT;
+    const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
+    const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
+    // the first tile's loads go out before the routing bits are set up; rows past the
+    // split are masked below and rows past the head read as zeros
+    if (ntiles > 0) TL::issue_rows(rk, rv, k0, s_k[0], s_v[0], w, lane);
+    for (int i = tid; i < kProbeRows * BW; i += 512) (&s_bits[0][0])[i] = 0u;
+    for (int g = tid; g <= gk; g += 512) s_ko[g] = ko[g];
     __syncthreads();
-    for (int i = tid; i < kProbeRows * kblk; i += 256) {
-        const int lp = i / kblk, s = i % kblk;
+    for (int i = tid; i < kProbeRows * kblk; i += 512) {
+        const int lp = i / kblk, s = i - lp * kblk;
         const int p = p0 + lp;
         if (p < probes) {
             const int grp = probe_grp[(size_t)h * probes + p];
@@ -442,19 +481,6 @@ __global__ __launch_bounds__(256) void k_probe(
             if (j >= 0) atomicOr(&s_bits[lp][j >> 5], 1u << (j & 31));
         }
     }
-    (void)gk;
-    const int k0 = split * chunk;
-    const int k1 = min(n, k0 + chunk);
-    const int nkeys = max(0, k1 - k0);
-    const int ntiles = (nkeys + KT - 1) / KT;
-    auto fill_phys = [&](int t, int buf) {
-        if (tid < KT) {
-            const int u = t * KT + tid;
-            const int r = (u < nkeys) ? k0 + u : k0;        // padding keys repeat row k0 (masked)
-            s_phys[buf][tid] = r;
-            s_kg[buf][tid] = kgrp[head_row0 + r];
-        }
-    };
 
     const int lp = w * 32 + (lane & 31);
     const int p = p0 + lp;
@@ -478,52 +504,48 @@ __global__ __launch_bounds__(256) void k_probe(
     // routed outputs come out bit-identical
     float m_run = -INFINITY, lb = 0.f, ls = 0.f;
     const bf16x2 ones = ones_bf16x2();
+    int gcur = 0;                                   // group of the current tile's first key
 
-    const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
-    const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
-    if (ntiles > 0) {
-        fill_phys(0, 0);
-        __syncthreads();
-        TL::issue(rk, rv, s_phys[0], s_k[0], s_v[0], w, lane);
-        if (ntiles > 1) fill_phys(1, 1);
-    }
     tile_ready();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles) TL::issue(rk, rv, s_phys[buf ^ 1], s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
+        const int base = k0 + t * KT;
+        if (t + 1 < ntiles) TL::issue_rows(rk, rv, base + KT, s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
         if (active) {
             f32x16 sv[2];
             sv[0] = qk_block<D>(s_k[buf], qf, 0, lane);
             sv[1] = qk_block<D>(s_k[buf], qf, 1, lane);
-            const int nvk = min(KT, nkeys - t * KT);
-            // routed keys of the tile as a bit mask: keys are in group-major order, so the
-            // tile's keys form runs of whole groups (usually one or two)
+            const int nvk = min(KT, k1 - base);
+            // routed keys of the tile as a bit mask, from the runs of groups it holds
+            while (s_ko[gcur + 1] <= base) ++gcur;
             uint64_t mask = 0;
-            {
-                const int base = k0 + t * KT;
-                const int ga = s_kg[buf][0], gb = s_kg[buf][nvk - 1];
-                for (int g = ga; g <= gb; ++g) {
-                    if ((s_bits[lp][g >> 5] >> (g & 31)) & 1u) {
-                        const int lo = max(0, ko[g] - base), hi = min(nvk, ko[g + 1] - base);
-                        if (hi > lo) {
-                            const uint64_t upto_hi = (hi >= 64) ? ~0ull : ((1ull << hi) - 1);
-                            mask |= upto_hi & ~((1ull << lo) - 1);
-                        }
+            for (int g = gcur; g < gk && s_ko[g] < base + nvk; ++g) {
+                if ((s_bits[lp][g >> 5] >> (g & 31)) & 1u) {
+                    const int lo = max(0, s_ko[g] - base), hi = min(nvk, s_ko[g + 1] - base);
+                    if (hi > lo) {
+                        const uint64_t upto_hi = (hi >= 64) ? ~0ull : ((1ull << hi) - 1);
+                        mask |= upto_hi & ~((1ull << lo) - 1);
                     }
                 }
             }
             const uint64_t mh = mask >> (4 * half);    // this lane's keys sit 4*half further on
             const uint32_t mw[2] = {(uint32_t)mh, (uint32_t)(mh >> 32)};
+            // raw logits; the scale (> 0) is applied to the max and inside the exponent
+            if (nvk < KT) {                             // a split's ragged last tile
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        if (key >= nvk) sv[kb][r] = -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    sv[kb][r] = (key < nvk) ? sv[kb][r] * scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, sv[kb][r]);
-                }
-            mx = pair_max(mx);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
+            mx = pair_max(mx) * scale_log2;
             if (__ballot(mx > m_run + kLazy)) {
                 const float mnew = fmaxf(m_run, mx);
                 const float alpha = fast_exp2(m_run - mnew);
@@ -534,16 +556,16 @@ __global__ __launch_bounds__(256) void k_probe(
                 m_run = mnew;
             }
             const float mneg = -m_run;
-            // P as bf16 hi + lo (about 2^-17 relative), each split by the routed mask of
-            // its two keys into the (a) and (b) operands
-            uint4 ah[4], al[4], bh[4], bl[4];
+            // per 16-key slice: P as bf16 hi + lo, each split by the routed mask of its
+            // two keys into the (a) and (b) operands, then the slice's products
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) {
                 uint32_t a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int kb = sl >> 1, r = 8 * (sl & 1) + 2 * i;
-                    const float e0 = fast_exp2(sv[kb][r] + mneg), e1 = fast_exp2(sv[kb][r + 1] + mneg);
+                    const float e0 = fast_exp2(fmaf(sv[kb][r], scale_log2, mneg));
+                    const float e1 = fast_exp2(fmaf(sv[kb][r + 1], scale_log2, mneg));
                     const uint32_t hi = pack_bf16x2(e0, e1);
                     const uint32_t lo = pack_bf16x2(e0 - bf16_to_f32((bf16_t)(hi & 0xFFFF)),
                                                     e1 - bf16_to_f32((bf16_t)(hi >> 16)));
@@ -561,23 +583,20 @@ __global__ __launch_bounds__(256) void k_probe(
                     lb = dot2_bf16(b0[i], ones, lb);
                     lb = dot2_bf16(b1[i], ones, lb);
                 }
-                ah[sl] = make_uint4(a0[0], a0[1], a0[2], a0[3]);
-                al[sl] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
-                bh[sl] = make_uint4(b0[0], b0[1], b0[2], b0[3]);
-                bl[sl] = make_uint4(b1[0], b1[1], b1[2], b1[3]);
-            }
-#pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
+                const uint4 ah = make_uint4(a0[0], a0[1], a0[2], a0[3]);
+                const uint4 al = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+                const uint4 bh = make_uint4(b0[0], b0[1], b0[2], b0[3]);
+                const uint4 bl = make_uint4(b1[0], b1[1], b1[2], b1[3]);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const uint4 a = vt_frag<D>(s_v[buf], db, sl, lane);
-                    oa[db] = mfma32x32x16(a, ah[sl], oa[db]);
-                    ob[db] = mfma32x32x16(a, bh[sl], ob[db]);
-                    oa[db] = mfma32x32x16(a, al[sl], oa[db]);
-                    ob[db] = mfma32x32x16(a, bl[sl], ob[db]);
+                    oa[db] = mfma32x32x16(a, ah, oa[db]);
+                    ob[db] = mfma32x32x16(a, bh, ob[db]);
+                    oa[db] = mfma32x32x16(a, al, oa[db]);
+                    ob[db] = mfma32x32x16(a, bl, ob[db]);
                 }
+            }
         }
-        if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
     }
     if (!active) return;
@@ -606,23 +625,22 @@ __global__ __launch_bounds__(256) void k_probe(
 
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
                   const int32_t* probe_pos, const int32_t* probe_grp, int probes,
-                  const int32_t* kgrp, const int32_t* koff, int koff_stride, int gk,
-                  const int32_t* blocks, int gq, int kblk, float* part_ml, float* part_od,
-                  float* part_os, hipStream_t st) {
+                  const int32_t* koff, int koff_stride, int gk, const int32_t* blocks, int gq,
+                  int kblk, int splits, float* part_ml, float* part_od, float* part_os,
+                  hipStream_t st) {
     if (probes == 0) return;
-    const int splits = probe_splits(n);
     int chunk = (n + splits - 1) / splits;
     chunk = (chunk + KT - 1) / KT * KT;
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     dim3 grid((probes + kProbeRows - 1) / kProbeRows, splits, heads);
     if (d == 128)
-        hipLaunchKernelGGL(k_probe<128>, grid, dim3(256), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
-                           probes, kgrp, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
-                           part_os);
+        hipLaunchKernelGGL(k_probe<128>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
+                           probes, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2,
+                           part_ml, part_od, part_os);
     else
-        hipLaunchKernelGGL(k_probe<64>, grid, dim3(256), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
-                           probes, kgrp, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2, part_ml, part_od,
-                           part_os);
+        hipLaunchKernelGGL(k_probe<64>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
+                           probes, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2,
+                           part_ml, part_od, part_os);
 }
 
 // Merge the key splits of every probe row in split order; X = routed output,

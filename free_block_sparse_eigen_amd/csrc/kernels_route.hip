@@ -31,18 +31,6 @@ void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, in
                        src, perm, n, d, dst);
 }
 
-__global__ void k_fill_groups(const int32_t* __restrict__ off, int n, int groups,
-                              int32_t* __restrict__ grp) {
-    const int h = blockIdx.y, g = blockIdx.x;
-    const int32_t* oh = off + (size_t)h * (groups + 1);
-    for (int m = oh[g] + threadIdx.x; m < oh[g + 1]; m += blockDim.x) grp[(size_t)h * n + m] = g;
-}
-
-void launch_fill_groups(const int32_t* off, int heads, int n, int groups, int32_t* grp,
-                        hipStream_t st) {
-    hipLaunchKernelGGL(k_fill_groups, dim3(groups, heads), dim3(256), 0, st, off, n, groups, grp);
-}
-
 // Block per (query group, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64; key group j is
 // kept when it is non-empty and fewer than k non-empty groups rank above it by
 // (score descending, index ascending). Kept groups are written in ascending order.
