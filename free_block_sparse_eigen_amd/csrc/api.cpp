@@ -131,6 +131,8 @@ struct sparsepr_ctx {
     double* h_wp = nullptr;           // [H][d][r_K] key projection W (host -> device)
     void* h_b32 = nullptr;            // [H][2][d][d] bf16 B'^T hi/lo, then [H][d] fp32 b'
     hipEvent_t ev_probe = nullptr;    // probe rows and fit Grams are on the host
+    hipEvent_t ev_rows = nullptr;     // probe rows merged (the fit's inputs are ready)
+    hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
 
     int stage = 0;
     bool poisoned = false;
@@ -425,7 +427,9 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             hipHostMalloc(reinterpret_cast<void**>(&c->h_mkp), sizeof(double) * H * d * d) != hipSuccess ||
             hipHostMalloc(reinterpret_cast<void**>(&c->h_wp), sizeof(double) * H * d * c->rK) != hipSuccess ||
             hipHostMalloc(&c->h_b32, sizeof(float) * H * (d * d + d)) != hipSuccess ||
-            hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming) != hipSuccess) {
+            hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&c->ev_rows, hipEventDisableTiming) != hipSuccess ||
+            hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) {
             sparsepr_destroy(c);
             return SPARSEPR_ERR_OOM;
         }
@@ -455,6 +459,8 @@ void sparsepr_destroy(sparsepr_ctx* c) {
             for (auto& e : row)
                 if (e) (void)hipEventDestroy(e);
     if (c->ev_probe) (void)hipEventDestroy(c->ev_probe);
+    if (c->ev_rows) (void)hipEventDestroy(c->ev_rows);
+    if (c->side) (void)hipStreamDestroy(c->side);
     if (c->h_fit) (void)hipHostFree(c->h_fit);
     if (c->h_mkp) (void)hipHostFree(c->h_mkp);
     if (c->h_wp) (void)hipHostFree(c->h_wp);
@@ -575,8 +581,11 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
     const size_t H = c->H, d = c->d;
-    // Probe rows first, with the fit's fp64 means and Grams, copied to pinned host
-    // memory; the host solve (sparsepr_probe_fit) then overlaps the main kernel.
+    // Probe rows first. The fit's fp64 means and Grams, and their copy to pinned host
+    // memory, run on the side stream while the main kernel runs on this one; the host
+    // solve (sparsepr_probe_fit) waits for them only. This stream first waits for the
+    // previous call's side work, which reads the probe buffers written here.
+    SPR_HIP(c, hipStreamWaitEvent(st, c->ev_probe, 0));
     if (c->P > 0) {
         launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P,
                      c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->splits, c->part_ml,
@@ -584,22 +593,27 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
         launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
                            c->py, c->pod, st);
         SPR_LAUNCHED(c, "probe rows");
+        SPR_HIP(c, hipEventRecord(c->ev_rows, st));
+        hipStream_t sd = c->side;
+        SPR_HIP(c, hipStreamWaitEvent(sd, c->ev_rows, 0));
         double* xm = c->fit_m;
         double* ym = c->fit_m + H * d;
         double* gxx = c->fit_g;
         double* gxy = c->fit_g + H * d * d;
         double* gyy = c->fit_g + 2 * H * d * d;
-        launch_col_means_f32(c->px, c->H, c->P, c->d, xm, st);
-        launch_col_means_f32(c->py, c->H, c->P, c->d, ym, st);
-        launch_gram_f32(c->px, c->px, xm, xm, c->H, c->P, c->d, gxx, st);
-        launch_gram_f32(c->px, c->py, xm, ym, c->H, c->P, c->d, gxy, st);
-        launch_gram_f32(c->py, c->py, nullptr, nullptr, c->H, c->P, c->d, gyy, st);
+        launch_col_means_f32(c->px, c->H, c->P, c->d, xm, sd);
+        launch_col_means_f32(c->py, c->H, c->P, c->d, ym, sd);
+        launch_gram_f32(c->px, c->px, xm, xm, c->H, c->P, c->d, gxx, sd);
+        launch_gram_f32(c->px, c->py, xm, ym, c->H, c->P, c->d, gxy, sd);
+        launch_gram_f32(c->py, c->py, nullptr, nullptr, c->H, c->P, c->d, gyy, sd);
         SPR_LAUNCHED(c, "fit grams");
-        SPR_HIP(c, hipMemcpyAsync(c->h_fit, c->fit_m, sizeof(double) * H * 2 * d, hipMemcpyDeviceToHost, st));
+        SPR_HIP(c, hipMemcpyAsync(c->h_fit, c->fit_m, sizeof(double) * H * 2 * d, hipMemcpyDeviceToHost, sd));
         SPR_HIP(c, hipMemcpyAsync(c->h_fit + H * 2 * d, c->fit_g, sizeof(double) * H * 3 * d * d,
-                                  hipMemcpyDeviceToHost, st));
+                                  hipMemcpyDeviceToHost, sd));
+        SPR_HIP(c, hipEventRecord(c->ev_probe, sd));
+    } else {
+        SPR_HIP(c, hipEventRecord(c->ev_probe, st));
     }
-    SPR_HIP(c, hipEventRecord(c->ev_probe, st));
     mark(c, 4, st);
     launch_vbsa(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
                 c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, c->o_s, 0,
