@@ -372,11 +372,14 @@ void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart
 }
 
 // ----------------------------------------------------------------- recheck ---
-// One block per queued point, the exact-input point in fp64 against every fp64 centroid,
-// argmin with the lowest index on ties. With a factor L [d][dim]: coordinates y = x L (two
-// halves of the depth summed in a fixed order) and |y - c|^2. With the full metric
-// (dim == 0): |c|^2 - 2 x . C', which differs from the metric distance by x^T M x, the
-// same for every centroid. A thread per centroid.
+// A block per batch of 8 queued points, each exact-input point in fp64 against every fp64
+// centroid, argmin with the lowest index on ties. With a factor L [d][dim]: coordinates
+// y = x L (two halves of the depth summed in a fixed order) and |y - c|^2. With the full
+// metric (dim == 0): |c|^2 - 2 x . C', which differs from the metric distance by x^T M x,
+// the same for every centroid. A thread per centroid; each centroid coordinate read serves
+// the whole batch, and every point's sums run in the same order whatever its batch.
+constexpr int kRecheckBatch = 8;
+
 __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, int n, int d,
                                                  const double* __restrict__ l64, int dim,
                                                  const double* __restrict__ c64,
@@ -384,70 +387,108 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                                                  const int32_t* __restrict__ flag_count,
                                                  const int32_t* __restrict__ flag_list,
                                                  int32_t* __restrict__ labels) {
-    __shared__ double xs[128];
-    __shared__ double part[2][128];
-    __shared__ double ys[128];
-    __shared__ double wbest[4];
-    __shared__ int wbg[4];
+    constexpr int RB = kRecheckBatch;
+    __shared__ double xs[128][RB];                 // [coordinate][point of the batch]
+    __shared__ double part[2][128][RB];
+    __shared__ double ys[128][RB];
+    __shared__ double wbest[4][RB];
+    __shared__ int wbg[4][RB];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const bool full = dim == 0;
     const int cdim = full ? d : dim;
     const int count = flag_count[h];
     const double* lh = l64 + (size_t)h * d * dim;
     const double* ch = c64 + (size_t)h * groups * cdim;
+    const int32_t* fl = flag_list + (size_t)h * n;
     const int dh = d / 2;
-    for (int idx = blockIdx.x; idx < count; idx += gridDim.x) {
-        const int p = flag_list[(size_t)h * n + idx];
-        if (tid < d) xs[tid] = (double)bf16_to_f32(x[((size_t)h * n + p) * d + tid]);
+    for (int b0 = blockIdx.x * RB; b0 < count; b0 += gridDim.x * RB) {
+        const int nb = min(RB, count - b0);
+        // a short batch repeats its first point; those results are dropped
+        for (int i = tid; i < RB * d; i += 256) {
+            const int b = i / d, j = i - b * d;
+            const int p = fl[b0 + (b < nb ? b : 0)];
+            xs[j][b] = (double)bf16_to_f32(x[((size_t)h * n + p) * d + j]);
+        }
         __syncthreads();
         if (!full) {
             const int j = tid & 127, hf = tid >> 7;
             if (j < dim) {
                 const int i0 = hf * dh, i1 = hf ? d : dh;
-                double s = 0.0;
-#pragma unroll 8
-                for (int i = i0; i < i1; ++i) s += xs[i] * lh[(size_t)i * dim + j];
-                part[hf][j] = s;
+                double s[RB];
+#pragma unroll
+                for (int b = 0; b < RB; ++b) s[b] = 0.0;
+#pragma unroll 4
+                for (int i = i0; i < i1; ++i) {
+                    const double l = lh[(size_t)i * dim + j];
+#pragma unroll
+                    for (int b = 0; b < RB; ++b) s[b] += xs[i][b] * l;
+                }
+#pragma unroll
+                for (int b = 0; b < RB; ++b) part[hf][j][b] = s[b];
             }
             __syncthreads();
-            if (tid < dim) ys[tid] = part[0][tid] + part[1][tid];
+            for (int i = tid; i < dim * RB; i += 256) {
+                const int j = i / RB, b = i % RB;
+                ys[j][b] = part[0][j][b] + part[1][j][b];
+            }
             __syncthreads();
         }
-        double best = INFINITY;
-        int bg = 0x7fffffff;
+        double best[RB];
+        int bg[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) { best[b] = INFINITY; bg[b] = 0x7fffffff; }
         for (int g = tid; g < groups; g += 256) {
             const double* c = ch + (size_t)g * cdim;
-            double dist = 0.0;
+            double acc[RB];
+#pragma unroll
+            for (int b = 0; b < RB; ++b) acc[b] = 0.0;
             if (full) {
-                double dot = 0.0;
-#pragma unroll 8
-                for (int j = 0; j < d; ++j) dot += xs[j] * c[j];
-                dist = c2_64[(size_t)h * groups + g] - 2.0 * dot;
+#pragma unroll 4
+                for (int j = 0; j < d; ++j) {
+                    const double cj = c[j];
+#pragma unroll
+                    for (int b = 0; b < RB; ++b) acc[b] += xs[j][b] * cj;
+                }
+                const double c2 = c2_64[(size_t)h * groups + g];
+#pragma unroll
+                for (int b = 0; b < RB; ++b) acc[b] = c2 - 2.0 * acc[b];
             } else {
-#pragma unroll 8
+#pragma unroll 4
                 for (int j = 0; j < dim; ++j) {
-                    const double t = ys[j] - c[j];
-                    dist += t * t;
+                    const double cj = c[j];
+#pragma unroll
+                    for (int b = 0; b < RB; ++b) {
+                        const double t = ys[j][b] - cj;
+                        acc[b] += t * t;
+                    }
                 }
             }
-            if (dist < best) { best = dist; bg = g; }
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+                if (acc[b] < best[b]) { best[b] = acc[b]; bg[b] = g; }
         }
-        for (int o = 32; o > 0; o >>= 1) {
-            const double ob = __shfl_xor(best, o, 64);
-            const int og = __shfl_xor(bg, o, 64);
-            if (ob < best || (ob == best && og < bg)) { best = ob; bg = og; }
-        }
-        if (lane == 0) {
-            wbest[w] = best;
-            wbg[w] = bg;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            for (int o = 32; o > 0; o >>= 1) {
+                const double ob = __shfl_xor(best[b], o, 64);
+                const int og = __shfl_xor(bg[b], o, 64);
+                if (ob < best[b] || (ob == best[b] && og < bg[b])) { best[b] = ob; bg[b] = og; }
+            }
+            if (lane == 0) {
+                wbest[w][b] = best[b];
+                wbg[w][b] = bg[b];
+            }
         }
         __syncthreads();
-        if (tid == 0) {
-            double b = wbest[0];
-            int g = wbg[0];
+        if (tid < nb) {
+            double bb = wbest[0][tid];
+            int g = wbg[0][tid];
             for (int k = 1; k < 4; ++k)
-                if (wbest[k] < b || (wbest[k] == b && wbg[k] < g)) { b = wbest[k]; g = wbg[k]; }
-            labels[(size_t)h * n + p] = g;
+                if (wbest[k][tid] < bb || (wbest[k][tid] == bb && wbg[k][tid] < g)) {
+                    bb = wbest[k][tid];
+                    g = wbg[k][tid];
+                }
+            labels[(size_t)h * n + fl[b0 + tid]] = g;
         }
         __syncthreads();
     }
@@ -456,8 +497,8 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
                     const double* c64, const double* c2_64, int groups, const int32_t* flag_count,
                     const int32_t* flag_list, int32_t* labels, hipStream_t st) {
-    int blocks = (n + 63) / 64;
-    if (blocks > 512) blocks = 512;
+    int blocks = (n + kRecheckBatch - 1) / kRecheckBatch;
+    if (blocks > 64) blocks = 64;
     hipLaunchKernelGGL(k_recheck, dim3(blocks, heads), dim3(256), 0, st, x, n, d, l64, dim, c64, c2_64,
                        groups, flag_count, flag_list, labels);
 }
