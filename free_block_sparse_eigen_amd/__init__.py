@@ -63,6 +63,11 @@ class Stats(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python free_block_sparse_eigen_amd/build.py`")
+# torch first: its bundled HIP runtime has the same soname as the system one, so the
+# library then binds to that runtime. Loaded the other way round, the process would hold
+# two HIP runtimes, and torch's device pointers and streams would be foreign to ours.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p
@@ -103,7 +108,7 @@ for _name, (_res, _args) in _sigs.items():
 
 def _check(status: int, ctx=None) -> None:
     if status != 0:
-        detail = lib.sparsepr_last_error(ctx).decode() if ctx else ""
+        detail = lib.sparsepr_last_error(ctx).decode()   # ctx None: why create failed
         raise SparsePRError(status, detail)
 
 

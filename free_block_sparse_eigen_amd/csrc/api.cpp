@@ -392,7 +392,17 @@ const char* sparsepr_status_str(int32_t s) {
     }
 }
 
-const char* sparsepr_last_error(const sparsepr_ctx* c) { return c ? c->err.c_str() : ""; }
+namespace {
+thread_local std::string create_err;   // why this thread's last sparsepr_create failed
+
+int32_t create_fail(sparsepr_ctx* c, int32_t status, const char* what, hipError_t e) {
+    create_err = std::string(what) + ": " + hipGetErrorString(e);
+    if (c) sparsepr_destroy(c);
+    return status;
+}
+}  // namespace
+
+const char* sparsepr_last_error(const sparsepr_ctx* c) { return c ? c->err.c_str() : create_err.c_str(); }
 
 int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     if (!out) return SPARSEPR_ERR_INVALID_ARG;
@@ -403,49 +413,48 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     c->p = *p;
     derive(*c);
     c->timing = (p->flags & SPARSEPR_F_STAGE_TIMING) != 0;
-    if (hipGetDevice(&c->device) != hipSuccess) {
+    hipError_t e;
+    if ((e = hipGetDevice(&c->device)) != hipSuccess) {
         delete c;
-        return SPARSEPR_ERR_HIP;
+        return create_fail(nullptr, SPARSEPR_ERR_HIP, "hipGetDevice", e);
     }
     Arena a;
     layout(*c, a);
     c->arena_bytes = a.used;
-    if (hipMalloc(&c->arena, c->arena_bytes) != hipSuccess) {
+    if ((e = hipMalloc(&c->arena, c->arena_bytes)) != hipSuccess) {
         delete c;
-        return SPARSEPR_ERR_OOM;
+        return create_fail(nullptr, SPARSEPR_ERR_OOM, "hipMalloc (arena)", e);
     }
     Arena b;
     b.base = static_cast<char*>(c->arena);
     layout(*c, b);
     if (c->timing)
         for (auto& row : c->ev)
-            for (auto& e : row)
-                if (hipEventCreate(&e) != hipSuccess) e = nullptr;
+            for (auto& ev : row)
+                if (hipEventCreate(&ev) != hipSuccess) ev = nullptr;
     {
         const size_t H = c->H, d = c->d;
-        if (hipHostMalloc(reinterpret_cast<void**>(&c->h_fit), sizeof(double) * H * (2 * d + 3 * d * d)) != hipSuccess ||
-            hipHostMalloc(reinterpret_cast<void**>(&c->h_mkp), sizeof(double) * H * d * d) != hipSuccess ||
-            hipHostMalloc(reinterpret_cast<void**>(&c->h_wp), sizeof(double) * H * d * c->rK) != hipSuccess ||
-            hipHostMalloc(&c->h_b32, sizeof(float) * H * (d * d + d)) != hipSuccess ||
-            hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&c->ev_rows, hipEventDisableTiming) != hipSuccess ||
-            hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) {
-            sparsepr_destroy(c);
-            return SPARSEPR_ERR_OOM;
-        }
+        if ((e = hipHostMalloc(reinterpret_cast<void**>(&c->h_fit), sizeof(double) * H * (2 * d + 3 * d * d))) != hipSuccess ||
+            (e = hipHostMalloc(reinterpret_cast<void**>(&c->h_mkp), sizeof(double) * H * d * d)) != hipSuccess ||
+            (e = hipHostMalloc(reinterpret_cast<void**>(&c->h_wp), sizeof(double) * H * d * c->rK)) != hipSuccess ||
+            (e = hipHostMalloc(&c->h_b32, sizeof(float) * H * (d * d + d))) != hipSuccess)
+            return create_fail(c, SPARSEPR_ERR_OOM, "hipHostMalloc", e);
+        if ((e = hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&c->ev_rows, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
+            return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
     }
     // dense baseline metadata
     const int meta[8] = {0, c->N, 0, c->N, 0, c->dense_units, 0, 0};
-    if (hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice) != hipSuccess) {
-        sparsepr_destroy(c);
-        return SPARSEPR_ERR_HIP;
-    }
+    if ((e = hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice)) != hipSuccess)
+        return create_fail(c, SPARSEPR_ERR_HIP, "hipMemcpy (metadata)", e);
     launch_units(c->dense_meta, 1, 1, kAttnRows, c->dense_units, c->dense_unit_list,
                  c->dense_meta + 6, nullptr);
-    if (hipDeviceSynchronize() != hipSuccess) {
-        sparsepr_destroy(c);
-        return SPARSEPR_ERR_HIP;
-    }
+    if ((e = hipGetLastError()) != hipSuccess)
+        return create_fail(c, SPARSEPR_ERR_HIP, "launch (dense work units)", e);
+    if ((e = hipDeviceSynchronize()) != hipSuccess)
+        return create_fail(c, SPARSEPR_ERR_HIP, "hipDeviceSynchronize (create)", e);
+    create_err.clear();
     *out = c;
     return SPARSEPR_OK;
 }

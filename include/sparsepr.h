@@ -117,7 +117,8 @@ void sparsepr_destroy(sparsepr_ctx* ctx);
 /* Static text for a status code. */
 const char* sparsepr_status_str(int32_t status);
 
-/* Detail of the context's last error ("" if none). */
+/* Detail of the context's last error ("" if none). With ctx NULL: why this thread's last
+ * sparsepr_create failed (the HIP call and its error string; "" after a success). */
 const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 
 /* ---- the five stages (section 2 of the method summary) ---- */

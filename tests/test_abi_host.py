@@ -158,3 +158,21 @@ def test_probe_fit_min_norm_least_squares():
     bm, bv = spr.sparsepr_host_probe_fit(x, y, 0.0, 6)
     rbm, rbv = orc.probe_fit(x, y, 0.0, 6)
     assert np.allclose(bm, rbm, atol=1e-9) and np.allclose(bv, rbv, atol=1e-9)
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding alone (before anything else loads torch) leaves exactly one
+    HIP runtime mapped: the library must bind to torch's, never load a second copy."""
+    import subprocess
+    import sys
+    code = ("import free_block_sparse_eigen_amd, re\n"
+            "paths = set()\n"
+            "for line in open('/proc/self/maps'):\n"
+            "    f = line.split()[-1]\n"
+            "    if re.search(r'libamdhip64\\.so', f): paths.add(f)\n"
+            "print(len(paths)); print(sorted(paths))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split("\n")[0] == "1", r.stdout
