@@ -29,7 +29,9 @@ METRIC = "ms per sparse attention call + executed-pair TFLOPS (% bf16 MFMA peak)
 BF16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vbsa_c3_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "free_block_sparse_eigen_amd", "csrc", "kernels_attn.hip")
+# sources that define the sparse attention kernel (the traffic counters are tied to them)
+KERNEL_SRCS = [os.path.join(ROOT, "free_block_sparse_eigen_amd", "csrc", f)
+               for f in ("kernels_attn.hip", "attn_tile.h", "common.h", "kernels.h")]
 
 
 def log(msg: str) -> None:
@@ -37,8 +39,23 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(mib: int) -> int:
+    """A plain device-to-device copy of known size, the reference reading for the HBM
+    traffic counters (run under the same counter pass as the kernel)."""
+    import torch
+    x = torch.ones(mib * 2**20 // 4, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    y = x.clone()
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4}))
+    return 0
 
 
 def measured_traffic(flops_per_launch: float, ms: float):
@@ -102,7 +119,11 @@ def main() -> int:
     ap.add_argument("--density", type=float, default=None)
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU baseline and parity leg")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB on the device (traffic counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Heads shard across GPUs with no exchange; "
