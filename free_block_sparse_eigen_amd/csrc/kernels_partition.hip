@@ -111,8 +111,15 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
     for (int o = tid; o < kFinG * dout; o += 256) {
         const int gs = o / dout, j = o % dout;
         double acc = 0.0;
-#pragma unroll 8
-        for (int i = 0; i < d; ++i) acc += s_m[gs][i] * lh[(size_t)i * dout + j];
+        int i = 0;
+        for (; i + 16 <= d; i += 16) {                   // loads 16 at a time, sums in order
+            double lv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)(i + u) * dout + j];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc += s_m[gs][i + u] * lv[u];
+        }
+        for (; i < d; ++i) acc += s_m[gs][i] * lh[(size_t)i * dout + j];
         s_c[gs][j] = acc;
     }
     __syncthreads();
@@ -121,8 +128,15 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         if (full) break;
         const int i = o / kFinG, gs = o % kFinG;
         double acc = 0.0;
-#pragma unroll 8
-        for (int j = 0; j < dout; ++j) acc += lh[(size_t)i * dout + j] * s_c[gs][j];
+        int j = 0;
+        for (; j + 16 <= dout; j += 16) {
+            double lv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)i * dout + j + u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc += lv[u] * s_c[gs][j + u];
+        }
+        for (; j < dout; ++j) acc += lh[(size_t)i * dout + j] * s_c[gs][j];
         s_s[gs][i] = acc;
     }
     __syncthreads();
@@ -417,8 +431,17 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                 double s[RB];
 #pragma unroll
                 for (int b = 0; b < RB; ++b) s[b] = 0.0;
-#pragma unroll 4
-                for (int i = i0; i < i1; ++i) {
+                int i = i0;
+                for (; i + 16 <= i1; i += 16) {          // loads 16 at a time, sums in order
+                    double lv[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)(i + u) * dim + j];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+#pragma unroll
+                        for (int b = 0; b < RB; ++b) s[b] += xs[i + u][b] * lv[u];
+                }
+                for (; i < i1; ++i) {
                     const double l = lh[(size_t)i * dim + j];
 #pragma unroll
                     for (int b = 0; b < RB; ++b) s[b] += xs[i][b] * l;
@@ -443,8 +466,17 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
             for (int b = 0; b < RB; ++b) acc[b] = 0.0;
             if (full) {
-#pragma unroll 4
-                for (int j = 0; j < d; ++j) {
+                int j = 0;
+                for (; j + 16 <= d; j += 16) {           // loads 16 at a time, sums in order
+                    double cv[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) cv[u] = c[j + u];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+#pragma unroll
+                        for (int b = 0; b < RB; ++b) acc[b] += xs[j + u][b] * cv[u];
+                }
+                for (; j < d; ++j) {
                     const double cj = c[j];
 #pragma unroll
                     for (int b = 0; b < RB; ++b) acc[b] += xs[j][b] * cj;
@@ -453,8 +485,20 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
                 for (int b = 0; b < RB; ++b) acc[b] = c2 - 2.0 * acc[b];
             } else {
-#pragma unroll 4
-                for (int j = 0; j < dim; ++j) {
+                int j = 0;
+                for (; j + 16 <= dim; j += 16) {
+                    double cv[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) cv[u] = c[j + u];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+#pragma unroll
+                        for (int b = 0; b < RB; ++b) {
+                            const double t = ys[j + u][b] - cv[u];
+                            acc[b] += t * t;
+                        }
+                }
+                for (; j < dim; ++j) {
                     const double cj = c[j];
 #pragma unroll
                     for (int b = 0; b < RB; ++b) {

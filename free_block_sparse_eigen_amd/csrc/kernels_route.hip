@@ -31,9 +31,11 @@ void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, in
                        src, perm, n, d, dst);
 }
 
-// Block per (query group, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64; key group j is
-// kept when it is non-empty and fewer than k non-empty groups rank above it by
-// (score descending, index ascending). Kept groups are written in ascending order.
+// Block per (query group, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64 (a thread per key
+// group, its sum over the d coordinates in ascending order, loads issued 16 at a time);
+// key group j is kept when it is non-empty and fewer than k non-empty groups rank above
+// it by (score descending, index ascending). Kept groups are written in ascending order
+// (ballot compaction), and the union size is a block reduction.
 __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
                                                const double* __restrict__ ck,
                                                const int32_t* __restrict__ qoff,
@@ -44,8 +46,9 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
     __shared__ double cs[128];
     __shared__ double sc[kMaxGroups];
     __shared__ int ne[kMaxGroups];
-    __shared__ int sel[kMaxGroups];
-    const int h = blockIdx.y, i = blockIdx.x, tid = threadIdx.x;
+    __shared__ int wcnt[4];
+    __shared__ long long wsz[4];
+    const int h = blockIdx.y, i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const double* ci = cq + ((size_t)h * gq + i) * d;
     for (int t = tid; t < d; t += 256) cs[t] = ci[t];
     __syncthreads();
@@ -54,33 +57,55 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
     for (int j = tid; j < gk; j += 256) {
         const double* cj = ck + ((size_t)h * gk + j) * d;
         double s = 0.0;
-        for (int t = 0; t < d; ++t) s += cs[t] * cj[t];
+        int t = 0;
+        for (; t + 16 <= d; t += 16) {
+            double cv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) cv[u] = cj[t + u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) s += cs[t + u] * cv[u];
+        }
+        for (; t < d; ++t) s += cs[t] * cj[t];
         sc[j] = s / rs;
         ne[j] = (ko[j + 1] > ko[j]) ? 1 : 0;
     }
     __syncthreads();
-    for (int j = tid; j < gk; j += 256) {
-        int rank = 0;
-        const double sj = sc[j];
-        for (int t = 0; t < gk; ++t)
-            rank += (ne[t] && (sc[t] > sj || (sc[t] == sj && t < j))) ? 1 : 0;
-        sel[j] = (ne[j] && rank < k) ? 1 : 0;
+    int32_t* out = blocks + ((size_t)h * gq + i) * k;
+    int base = 0;
+    long long u = 0;
+    for (int j0 = 0; j0 < gk; j0 += 256) {
+        const int j = j0 + tid;
+        bool keep = false;
+        if (j < gk && ne[j]) {
+            int rank = 0;
+            const double sj = sc[j];
+            for (int t = 0; t < gk; ++t)
+                rank += (ne[t] && (sc[t] > sj || (sc[t] == sj && t < j))) ? 1 : 0;
+            keep = rank < k;
+        }
+        if (keep) u += ko[j + 1] - ko[j];
+        const uint64_t m = __ballot(keep);
+        if (lane == 0) wcnt[w] = __popcll(m);
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int q = 0; q < 4; ++q) {
+            before += (q < w) ? wcnt[q] : 0;
+            total += wcnt[q];
+        }
+        if (keep) out[base + before + __popcll(m & ((1ull << lane) - 1))] = j;
+        base += total;
+        __syncthreads();
     }
+    for (int p = base + tid; p < k; p += 256) out[p] = -1;
+    for (int o = 32; o > 0; o >>= 1) u += __shfl_xor(u, o, 64);
+    if (lane == 0) wsz[w] = u;
     __syncthreads();
     if (tid == 0) {
-        int32_t* out = blocks + ((size_t)h * gq + i) * k;
-        int pos = 0;
-        int64_t u = 0;
-        for (int j = 0; j < gk; ++j)
-            if (sel[j]) {
-                out[pos++] = j;
-                u += ko[j + 1] - ko[j];
-            }
-        for (; pos < k; ++pos) out[pos] = -1;
-        ucount[(size_t)h * gq + i] = (int32_t)u;
+        const long long us = wsz[0] + wsz[1] + wsz[2] + wsz[3];
+        ucount[(size_t)h * gq + i] = (int32_t)us;
         const int32_t* qo = qoff + (size_t)h * (gq + 1);
         atomicAdd(reinterpret_cast<unsigned long long*>(&pairs[h]),
-                  (unsigned long long)(u * (int64_t)(qo[i + 1] - qo[i])));
+                  (unsigned long long)(us * (int64_t)(qo[i + 1] - qo[i])));
     }
 }
 
