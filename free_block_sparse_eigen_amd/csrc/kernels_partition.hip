@@ -565,18 +565,33 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ labels
 }
 
 // per head: group totals, exclusive scan over groups (wave scans + a scan of the wave
-// totals), then per-block bases in block order
+// totals), then per-block bases in block order. Each group's blocks are split into
+// contiguous ranges over several threads (1024 / groups of them, a power of two).
 __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ blkhist, int nblk,
                                                int groups, int n, int32_t* __restrict__ blkoff,
                                                int32_t* __restrict__ off) {
     __shared__ int wtot[16];
-    const int h = blockIdx.x, g = threadIdx.x, lane = g & 63, w = g >> 6;
+    __shared__ int part[1024];                 // [range][group] partial counts, then bases
+    __shared__ int gbase[kMaxGroups];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int tpg = 1;
+    while (tpg * 2 * groups <= 1024) tpg *= 2;
+    const int chunk = (nblk + tpg - 1) / tpg;
     const int32_t* hh = blkhist + (size_t)h * nblk * groups;
-    int tot = 0;
-    if (g < groups) {
+    const int gq = tid % groups, q = tid / groups;       // group, block range
+    const bool mine = q < tpg;
+    const int b0 = mine ? min(nblk, q * chunk) : 0, b1 = mine ? min(nblk, b0 + chunk) : 0;
+    if (mine) {
+        int t = 0;
 #pragma unroll 8
-        for (int b = 0; b < nblk; ++b) tot += hh[(size_t)b * groups + g];
+        for (int b = b0; b < b1; ++b) t += hh[(size_t)b * groups + gq];
+        part[q * groups + gq] = t;
     }
+    __syncthreads();
+    const int g = tid;
+    int tot = 0;
+    if (g < groups)
+        for (int r = 0; r < tpg; ++r) tot += part[r * groups + g];
     // inclusive scan inside the wave
     int inc = tot;
 #pragma unroll
@@ -589,53 +604,73 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ blkhi
     int base = 0;
     for (int k = 0; k < w; ++k) base += wtot[k];
     if (g < groups) {
-        int run = base + inc - tot;      // exclusive prefix
+        const int run = base + inc - tot;      // exclusive prefix
         off[(size_t)h * (groups + 1) + g] = run;
-        int32_t* bo = blkoff + (size_t)h * nblk * groups;
-        for (int b = 0; b < nblk; ++b) {
-            bo[(size_t)b * groups + g] = run;
-            run += hh[(size_t)b * groups + g];
-        }
+        gbase[g] = run;
     }
     if (g == 0) off[(size_t)h * (groups + 1) + groups] = n;
+    __syncthreads();
+    if (mine) {
+        int run = gbase[gq];
+        for (int r = 0; r < q; ++r) run += part[r * groups + gq];
+        int32_t* bo = blkoff + (size_t)h * nblk * groups;
+        for (int b = b0; b < b1; ++b) {
+            bo[(size_t)b * groups + gq] = run;
+            run += hh[(size_t)b * groups + gq];
+        }
+    }
 }
 
-// Stable scatter: the rank of a point among equal labels follows the point order.
+// Stable scatter: the rank of a point among equal labels follows the point order. Wave w
+// takes the block's points [256 w, 256 w + 256) in 4 rounds of 64: per-wave label counts
+// give each wave its own base per label (block base + the counts of the waves before it);
+// in a round, the lanes holding the same label are found from one ballot per label bit.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ labels, int n,
                                                  int groups, const int32_t* __restrict__ blkoff,
                                                  int32_t* __restrict__ sorted) {
-    __shared__ int cnt[kMaxGroups];
+    __shared__ int cnt[4][kMaxGroups];
     const int h = blockIdx.y, b = blockIdx.x, tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    for (int g = tid; g < groups; g += 256) cnt[g] = 0;
+    for (int i = tid; i < 4 * groups; i += 256) cnt[i / groups][i % groups] = 0;
+    __syncthreads();
+    constexpr int PW = kSortChunk / 4;           // points per wave
+    const int pw0 = b * kSortChunk + wave * PW;
+    int lab[PW / 64];
+#pragma unroll
+    for (int r = 0; r < PW / 64; ++r) {
+        const int p = pw0 + r * 64 + lane;
+        lab[r] = (p < n) ? labels[(size_t)h * n + p] : -1;
+        if (lab[r] >= 0) atomicAdd(&cnt[wave][lab[r]], 1);
+    }
     __syncthreads();
     const int32_t* bo = blkoff + ((size_t)h * gridDim.x + b) * groups;
-    for (int round = 0; round < kSortChunk / 256; ++round) {
-        const int p = b * kSortChunk + round * 256 + tid;
-        const bool valid = p < n;
-        const int lab = valid ? labels[(size_t)h * n + p] : -1;
-        // peers: lanes of this wave holding the same label
-        uint64_t peers = 0;
-        uint64_t todo = __ballot(valid);
-        while (todo) {
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int l = __shfl(lab, leader, 64);
-            const uint64_t m = __ballot(valid && lab == l);
-            if (valid && lab == l) peers = m;
-            todo &= ~m;
-        }
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const int prefix = __popcll(peers & below);
-        const int total = __popcll(peers);
+    for (int g = tid; g < groups; g += 256) {
+        int run = bo[g];
         for (int w = 0; w < 4; ++w) {
-            int basev = 0;
-            if (wave == w && valid) basev = cnt[lab];
-            __syncthreads();
-            if (wave == w && valid) {
-                if (prefix == 0) cnt[lab] = basev + total;
-                sorted[(size_t)h * n + bo[lab] + basev + prefix] = p;
-            }
-            __syncthreads();
+            const int c = cnt[w][g];
+            cnt[w][g] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < groups) ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int r = 0; r < PW / 64; ++r) {
+        const int l = lab[r];
+        const bool valid = l >= 0;
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = valid && ((l >> bit) & 1);
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        if (valid) {
+            const int prefix = __popcll(peers & below);
+            const int basev = cnt[wave][l];
+            sorted[(size_t)h * n + basev + prefix] = pw0 + r * 64 + lane;
+            if (prefix == 0) cnt[wave][l] = basev + __popcll(peers);
         }
     }
 }
