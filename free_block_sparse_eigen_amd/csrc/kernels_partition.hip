@@ -208,32 +208,173 @@ void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const doubl
 // otherwise the point is queued for the fp64 recheck, which also settles exact ties by
 // the lowest index. Each lane tracks only the best and runner-up scores.
 //
-// Block = 4 waves x 64 points; centroids stream through LDS in tiles of 64 (hi and lo
-// parts, 16-byte chunk c of centroid row r at c ^ swz(r)), double-buffered and filled
-// by direct global-to-LDS loads. Padding centroids score +inf.
+// Centroid tiles of 64 (hi and lo parts, 16-byte chunk c of centroid row r at c ^ swz(r))
+// sit in LDS; a wave scores 64 points (two MFMA column blocks of 32) against them. Two
+// kernels share the per-wave steps: k_assign_res keeps every centroid of a head resident
+// in LDS (2 G D 2 bytes <= 128 KB) and lets each wave walk its points with no barriers;
+// k_assign (larger G) streams the tiles, double-buffered. Padding centroids score +inf.
+constexpr int kAssignTG = 64;
+constexpr int kAssignResBytes = 128 * 1024;
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x, int n,
-                                                   const bf16_t* __restrict__ cpart,
-                                                   const float* __restrict__ cn2,
-                                                   const float* __restrict__ cpn, int groups,
-                                                   int32_t* __restrict__ labels,
-                                                   int32_t* __restrict__ flag_count,
-                                                   int32_t* __restrict__ flag_list) {
-    constexpr int CH = D / 8;
-    constexpr int TG = 64;
-    constexpr int SLOTS = 2 * TG * CH;         // 16-byte slots per tile (hi and lo)
-    constexpr int PER = SLOTS / 256;           // direct loads per thread per tile
-    constexpr float kU = 5.9604644775390625e-08f;
-    constexpr float kappa = 2.f * D * kU * 1.00390625f + 7.62939453125e-06f;
-    __shared__ uint4 s_c0[SLOTS];
-    __shared__ uint4 s_c1[SLOTS];
-    __shared__ float s_cn2[kMaxGroups + TG];
-    __shared__ float s_red[8];
-    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int half = lane >> 5;
-    const int ntiles = (groups + TG - 1) / TG;
+struct AssignWave {
+    static constexpr int CH = D / 8;
+    static constexpr int TG = kAssignTG;
+    static constexpr int SLOTS = 2 * TG * CH;   // 16-byte slots per tile (hi and lo)
+    static constexpr float kU = 5.9604644775390625e-08f;
+    static constexpr float kappa = 2.f * D * kU * 1.00390625f + 7.62939453125e-06f;
+
+    uint4 xf[2][D / 16];
+    float xn[2];
+    float best[2], second[2];
+    int bg[2];
+
+    // this wave's 64 points as MFMA B fragments (an invalid point reads the last point
+    // and is zeroed), then their norms
+    __device__ __attribute__((always_inline)) void load(const bf16_t* __restrict__ x, int n,
+                                                        int h, int p_base, int lane) {
+        const int half = lane >> 5;
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            const int pt = min(p_base + 32 * pb + (lane & 31), n - 1);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                xf[pb][kk] = *reinterpret_cast<const uint4*>(x + ((size_t)h * n + pt) * D + 16 * kk + 8 * half);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            const bool valid = p_base + 32 * pb + (lane & 31) < n;
+            float ss = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                if (!valid) xf[pb][kk] = make_uint4(0, 0, 0, 0);
+                const uint4 v = xf[pb][kk];
+                const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_to_f32((bf16_t)(wd[e] & 0xFFFF));
+                    const float hi = bf16_to_f32((bf16_t)(wd[e] >> 16));
+                    ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+                }
+            }
+            ss += __shfl_xor(ss, 32, 64);
+            xn[pb] = sqrtf(ss) * 1.000001f;
+            best[pb] = INFINITY;
+            second[pb] = INFINITY;
+            bg[pb] = 0x7fffffff;
+        }
+    }
+
+    // scores against centroid tile t held at buf: the products of both 32-centroid
+    // sub-tiles run together (four independent accumulator chains), each sub-tile's
+    // sums in the same order (hi then lo over the depth); then the scores in sub-tile
+    // order
+    __device__ __attribute__((always_inline)) void tile(int t, const uint4* buf, int groups,
+                                                        const float* s_cn2, int lane) {
+        const int half = lane >> 5;
+        constexpr int KS = D / 16, PF = 2;
+        const uint4* cr0 = buf + (lane & 31) * CH;
+        const uint4* cr1 = buf + (32 + (lane & 31)) * CH;
+        const int sw0 = swz<CH>(lane & 31), sw1 = swz<CH>(32 + (lane & 31));
+        auto frag = [&](const uint4* cr, int sw, int i) __attribute__((always_inline)) {
+            return cr[(i / KS) * TG * CH + ((2 * (i % KS) + half) ^ sw)];
+        };
+        f32x16 acc[2][2];
+        uint4 f0[PF], f1[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            f0[i] = frag(cr0, sw0, i);
+            f1[i] = frag(cr1, sw1, i);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {
+            const uint4 a0 = f0[i % PF], a1 = f1[i % PF];
+            if (i + PF < 2 * KS) {
+                f0[i % PF] = frag(cr0, sw0, i + PF);
+                f1[i % PF] = frag(cr1, sw1, i + PF);
+            }
+            if (i == 0) {
+                acc[0][0] = mfma32x32x16(a0, xf[0][0], f32x16{});
+                acc[0][1] = mfma32x32x16(a0, xf[1][0], f32x16{});
+                acc[1][0] = mfma32x32x16(a1, xf[0][0], f32x16{});
+                acc[1][1] = mfma32x32x16(a1, xf[1][0], f32x16{});
+            } else {
+                acc[0][0] = mfma32x32x16(a0, xf[0][i % KS], acc[0][0]);
+                acc[0][1] = mfma32x32x16(a0, xf[1][i % KS], acc[0][1]);
+                acc[1][0] = mfma32x32x16(a1, xf[0][i % KS], acc[1][0]);
+                acc[1][1] = mfma32x32x16(a1, xf[1][i % KS], acc[1][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);     // keep the reads PF steps ahead
+        }
+#pragma unroll
+        for (int sub = 0; sub < TG / 32; ++sub) {
+            const int gb = t * TG + 32 * sub;
+            if (gb >= groups) break;
+            // with best <= second, the new runner-up is the median of (best, v, second);
+            // a new best inside this sub-tile is recorded as its accumulator slot r (an
+            // inline constant) and turned into the centroid index once afterwards
+            int code[2] = {-1, -1};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float c2 = s_cn2[gb + 8 * (r >> 2) + 4 * half + (r & 3)];
+#pragma unroll
+                for (int pb = 0; pb < 2; ++pb) {
+                    const float v = fmaf(-2.f, acc[sub][pb][r], c2);
+                    second[pb] = __builtin_amdgcn_fmed3f(best[pb], v, second[pb]);
+                    code[pb] = (v < best[pb]) ? r : code[pb];
+                    best[pb] = fminf(best[pb], v);
+                }
+            }
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb)
+                if (code[pb] >= 0) bg[pb] = gb + 8 * (code[pb] >> 2) + 4 * half + (code[pb] & 3);
+        }
+    }
+
+    // labels, and the points whose label is not certified appended to the recheck queue
+    __device__ __attribute__((always_inline)) void finish(int n, int h, int p_base, int lane,
+                                                          float c2max, float cpmax,
+                                                          int32_t* __restrict__ labels,
+                                                          int32_t* __restrict__ flag_count,
+                                                          int32_t* __restrict__ flag_list) {
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            // merge the two lane halves: best by (value, index); the other best joins second
+            const float ob = __shfl_xor(best[pb], 32, 64);
+            const float os = __shfl_xor(second[pb], 32, 64);
+            const int og = __shfl_xor(bg[pb], 32, 64);
+            float b = best[pb];
+            int gsel = bg[pb];
+            const float s2 = fminf(fminf(second[pb], os), fmaxf(b, ob));
+            if (ob < b || (ob == b && og < gsel)) {
+                b = ob;
+                gsel = og;
+            }
+            const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
+            const float bound = 2.4f * A + 2.4f * kU * (fabsf(s2) + fabsf(b)) + 1e-30f;
+            const int pt = p_base + 32 * pb + lane;
+            if (lane < 32 && pt < n) {
+                labels[(size_t)h * n + pt] = gsel;
+                if (!(s2 - b > bound)) {
+                    const int slot = atomicAdd(&flag_count[h], 1);
+                    flag_list[(size_t)h * n + slot] = pt;
+                }
+            }
+        }
+    }
+};
+
+// |c|^2 of every centroid tile slot into s_cn2 (+inf past the last group), and the head's
+// max |c|^2 and max |C'| for the bound; every thread of the block must call this.
+template <int NT>
+__device__ inline void assign_norms(const float* __restrict__ cn2, const float* __restrict__ cpn,
+                                    int h, int groups, int ntiles, float* s_cn2, float* s_red,
+                                    float& c2max, float& cpmax) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int NW = NT / 64;
     float c2m = 0.f, cpm = 0.f;
-    for (int g = tid; g < ntiles * TG; g += 256) {
+    for (int g = tid; g < ntiles * kAssignTG; g += NT) {
         float c2 = INFINITY;
         if (g < groups) {
             c2 = cn2[(size_t)h * groups + g];
@@ -246,8 +387,86 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
     cpm = wave_max(cpm);
     if (lane == 0) {
         s_red[w] = c2m;
-        s_red[4 + w] = cpm;
+        s_red[NW + w] = cpm;
     }
+    __syncthreads();
+    c2max = s_red[0];
+    cpmax = s_red[NW];
+    for (int k = 1; k < NW; ++k) {
+        c2max = fmaxf(c2max, s_red[k]);
+        cpmax = fmaxf(cpmax, s_red[NW + k]);
+    }
+}
+
+// Block = 8 waves over a contiguous range of 64-point items in head-major order (equal
+// ranges per block, one block per CU); where the range enters a new head the block loads
+// that head's centroids (all tiles) into LDS once, then its waves take the head's items
+// round-robin.
+template <int D>
+__global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict__ x, int n,
+                                                       int heads, const bf16_t* __restrict__ cpart,
+                                                       const float* __restrict__ cn2,
+                                                       const float* __restrict__ cpn, int groups,
+                                                       int items_per_block,
+                                                       int32_t* __restrict__ labels,
+                                                       int32_t* __restrict__ flag_count,
+                                                       int32_t* __restrict__ flag_list) {
+    using AW = AssignWave<D>;
+    constexpr int CH = AW::CH, TG = kAssignTG, SLOTS = AW::SLOTS;
+    __shared__ uint4 s_c[kAssignResBytes / 16];
+    __shared__ float s_cn2[kAssignResBytes / (4 * D) + TG];
+    __shared__ float s_red[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int ntiles = (groups + TG - 1) / TG;
+    const int ipw = (n + 63) / 64;                 // items per head
+    const int total = heads * ipw;
+    int it = blockIdx.x * items_per_block;
+    const int end = min(total, it + items_per_block);
+    AW aw;
+    while (it < end) {
+        const int h = it / ipw;
+        const int seg_end = min(end, (h + 1) * ipw);
+        __syncthreads();                           // the previous head's tiles are done
+        const rsrc_t rc = make_rsrc(cpart + (size_t)h * 2 * groups * D, (uint32_t)(2 * groups * D * 2));
+        for (int slot = tid; slot < ntiles * SLOTS; slot += 512) {
+            // lanes of a wave take consecutive slots, so each load lands at LDS base + 16 lane
+            const int t = slot / SLOTS, rem0 = slot % SLOTS;
+            const int part = rem0 / (TG * CH), rem = rem0 % (TG * CH);
+            const int row = rem / CH, pc = rem % CH;
+            const int g = min(t * TG + row, groups - 1);
+            lds_load16(rc, s_c + (slot - lane), ((part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8)) * 2);
+        }
+        float c2max, cpmax;
+        assign_norms<512>(cn2, cpn, h, groups, ntiles, s_cn2, s_red, c2max, cpmax);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int k = it + w; k < seg_end; k += 8) {
+            const int p_base = (k - h * ipw) * 64;
+            aw.load(x, n, h, p_base, lane);
+            for (int t = 0; t < ntiles; ++t) aw.tile(t, s_c + t * SLOTS, groups, s_cn2, lane);
+            aw.finish(n, h, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
+        }
+        it = seg_end;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x, int n,
+                                                   const bf16_t* __restrict__ cpart,
+                                                   const float* __restrict__ cn2,
+                                                   const float* __restrict__ cpn, int groups,
+                                                   int32_t* __restrict__ labels,
+                                                   int32_t* __restrict__ flag_count,
+                                                   int32_t* __restrict__ flag_list) {
+    using AW = AssignWave<D>;
+    constexpr int CH = AW::CH, TG = kAssignTG, SLOTS = AW::SLOTS;
+    constexpr int PER = SLOTS / 256;           // direct loads per thread per tile
+    __shared__ uint4 s_c0[SLOTS];
+    __shared__ uint4 s_c1[SLOTS];
+    __shared__ float s_cn2[kMaxGroups + TG];
+    __shared__ float s_red[8];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int ntiles = (groups + TG - 1) / TG;
     const rsrc_t rc = make_rsrc(cpart + (size_t)h * 2 * groups * D, (uint32_t)(2 * groups * D * 2));
     auto issue = [&](int t, uint4* buf) {
 #pragma unroll
@@ -261,121 +480,52 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
         }
     };
     issue(0, s_c0);
-    // this wave's 64 points as MFMA B fragments, and their norms
     const int p_base = blockIdx.x * 256 + w * 64;
-    uint4 xf[2][D / 16];
-    float xn[2];
-    // both point blocks' fragments loaded up front (an invalid point reads point 0 and
-    // is zeroed), then their norms
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-        const int pt = min(p_base + 32 * pb + (lane & 31), n - 1);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            xf[pb][kk] = *reinterpret_cast<const uint4*>(x + ((size_t)h * n + pt) * D + 16 * kk + 8 * half);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-        const bool valid = p_base + 32 * pb + (lane & 31) < n;
-        float ss = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            if (!valid) xf[pb][kk] = make_uint4(0, 0, 0, 0);
-            const uint4 v = xf[pb][kk];
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = bf16_to_f32((bf16_t)(wd[e] & 0xFFFF));
-                const float hi = bf16_to_f32((bf16_t)(wd[e] >> 16));
-                ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-            }
-        }
-        ss += __shfl_xor(ss, 32, 64);
-        xn[pb] = sqrtf(ss) * 1.000001f;
-    }
-    float best[2] = {INFINITY, INFINITY}, second[2] = {INFINITY, INFINITY};
-    int bg[2] = {0x7fffffff, 0x7fffffff};
-    auto compute = [&](int t, const uint4* buf) {
-#pragma unroll
-        for (int sub = 0; sub < TG / 32; ++sub) {
-            const int gb = t * TG + 32 * sub;
-            if (gb >= groups) break;
-            f32x16 acc[2] = {};
-            const int row = 32 * sub + (lane & 31), sw = swz<CH>(row);
-            const uint4* cr = buf + row * CH;
-            // hi then lo part, each over the depth; fragments read one step ahead
-            constexpr int KS = D / 16;
-            uint4 a = cr[half ^ sw];
-#pragma unroll
-            for (int i = 0; i < 2 * KS; ++i) {
-                uint4 nx = a;
-                if (i + 1 < 2 * KS) {
-                    const int p2 = (i + 1) / KS, k2 = (i + 1) % KS;
-                    nx = cr[p2 * TG * CH + ((2 * k2 + half) ^ sw)];
-                }
-                acc[0] = mfma32x32x16(a, xf[0][i % KS], acc[0]);
-                acc[1] = mfma32x32x16(a, xf[1][i % KS], acc[1]);
-                a = nx;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int g = gb + 8 * (r >> 2) + 4 * half + (r & 3);
-                const float c2 = s_cn2[g];
-#pragma unroll
-                for (int pb = 0; pb < 2; ++pb) {
-                    const float v = fmaf(-2.f, acc[pb][r], c2);
-                    second[pb] = fminf(second[pb], fmaxf(best[pb], v));
-                    bg[pb] = (v < best[pb]) ? g : bg[pb];
-                    best[pb] = fminf(best[pb], v);
-                }
-            }
-        }
-    };
+    AW aw;
+    aw.load(x, n, h, p_base, lane);
+    float c2max, cpmax;
+    assign_norms<256>(cn2, cpn, h, groups, ntiles, s_cn2, s_red, c2max, cpmax);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
         if (t + 1 < ntiles) issue(t + 1, s_c1);
-        compute(t, s_c0);
+        aw.tile(t, s_c0, groups, s_cn2, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 1 >= ntiles) break;
         if (t + 2 < ntiles) issue(t + 2, s_c0);
-        compute(t + 1, s_c1);
+        aw.tile(t + 1, s_c1, groups, s_cn2, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
-    const float c2max = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float cpmax = fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7]));
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-        // merge the two lane halves: best by (value, index); the other best joins second
-        const float ob = __shfl_xor(best[pb], 32, 64);
-        const float os = __shfl_xor(second[pb], 32, 64);
-        const int og = __shfl_xor(bg[pb], 32, 64);
-        float b = best[pb];
-        int gsel = bg[pb];
-        const float s2 = fminf(fminf(second[pb], os), fmaxf(b, ob));
-        if (ob < b || (ob == b && og < gsel)) {
-            b = ob;
-            gsel = og;
-        }
-        const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
-        const float bound = 2.4f * A + 2.4f * kU * (fabsf(s2) + fabsf(b)) + 1e-30f;
-        const int pt = p_base + 32 * pb + lane;
-        if (lane < 32 && pt < n) {
-            labels[(size_t)h * n + pt] = gsel;
-            if (!(s2 - b > bound)) {
-                const int slot = atomicAdd(&flag_count[h], 1);
-                flag_list[(size_t)h * n + slot] = pt;
-            }
-        }
-    }
+    aw.finish(n, h, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
 }
 
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st) {
+    const int ntiles = (groups + kAssignTG - 1) / kAssignTG;
+    if ((size_t)ntiles * kAssignTG * 2 * d * 2 <= (size_t)kAssignResBytes) {
+        static int cus = 0;
+        if (cus <= 0) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                cus <= 0)
+                cus = 256;
+        }
+        const int total = heads * ((n + 63) / 64);
+        const int blocks = std::max(1, std::min(total, cus));
+        const int ipb = (total + blocks - 1) / blocks;
+        const int nb = (total + ipb - 1) / ipb;
+        if (d == 128)
+            hipLaunchKernelGGL(k_assign_res<128>, dim3(nb), dim3(512), 0, st, x, n, heads, cpart, cn2,
+                               cpn, groups, ipb, labels, flag_count, flag_list);
+        else
+            hipLaunchKernelGGL(k_assign_res<64>, dim3(nb), dim3(512), 0, st, x, n, heads, cpart, cn2,
+                               cpn, groups, ipb, labels, flag_count, flag_list);
+        return;
+    }
     dim3 grid((n + 255) / 256, heads);
     if (d == 128)
         hipLaunchKernelGGL(k_assign<128>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
