@@ -208,8 +208,8 @@ void derive(sparsepr_ctx& c) {
     c.P = p.probes;
     c.T = p.kmeans_iters;
     c.nblk = (c.N + kSortChunk - 1) / kSortChunk;
-    c.maxu = (c.N + kAttnRows - 1) / kAttnRows + c.Gq;
-    c.dense_units = (c.N + kAttnRows - 1) / kAttnRows;
+    c.maxu = (c.N + kSparseRows - 1) / kSparseRows + c.Gq;
+    c.dense_units = (c.N + kDenseRows - 1) / kDenseRows;
     c.splits = probe_splits(c.N, c.H, c.P);
     c.gmax = std::max(c.Gk, c.Gq);
     c.weyl_a = weyl_multiplier(c.N);
@@ -448,7 +448,7 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     const int meta[8] = {0, c->N, 0, c->N, 0, c->dense_units, 0, 0};
     if ((e = hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice)) != hipSuccess)
         return create_fail(c, SPARSEPR_ERR_HIP, "hipMemcpy (metadata)", e);
-    launch_units(c->dense_meta, 1, 1, kAttnRows, c->dense_units, c->dense_unit_list,
+    launch_units(c->dense_meta, 1, 1, kDenseRows, c->dense_units, c->dense_unit_list,
                  c->dense_meta + 6, nullptr);
     if ((e = hipGetLastError()) != hipSuccess)
         return create_fail(c, SPARSEPR_ERR_HIP, "launch (dense work units)", e);
@@ -577,7 +577,7 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     launch_fill_i32(c->probe_of, -1, (size_t)c->H * c->N, st);
     launch_probes(c->qoff, c->qperm, c->H, c->N, c->Gq, c->P, c->probe_pos, c->probe_orig,
                   c->probe_grp, c->probe_of, st);
-    launch_units(c->qoff, c->H, c->Gq, kAttnRows, c->maxu, c->units, c->nunits, st);
+    launch_units(c->qoff, c->H, c->Gq, kSparseRows, c->maxu, c->units, c->nunits, st);
     SPR_LAUNCHED(c, "probes/units");
     mark(c, 3, st);
     c->stage = kStageRoute;
@@ -625,8 +625,8 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     }
     mark(c, 4, st);
     launch_vbsa(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
-                c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, c->o_s, 0,
-                st);
+                c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, kSparseRows,
+                c->o_s, 0, st);
     SPR_LAUNCHED(c, "sparse attention");
     mark(c, 5, st);
     c->stage = kStageAttn;
@@ -712,8 +712,8 @@ int32_t sparsepr_dense_attn(sparsepr_ctx* c, const void* q, const void* k, const
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
     launch_vbsa(q16, k16, v16, c->H, c->N, c->d, c->dense_meta, 0, c->dense_meta + 2, 0,
-                c->dense_meta + 4, 0, 1, c->dense_unit_list, 0, c->dense_meta + 6, 0, c->dense_units, o,
-                c->p.dtype == SPARSEPR_F32 ? 0 : 1, st);
+                c->dense_meta + 4, 0, 1, c->dense_unit_list, 0, c->dense_meta + 6, 0, c->dense_units,
+                kDenseRows, o, c->p.dtype == SPARSEPR_F32 ? 0 : 1, st);
     SPR_LAUNCHED(c, "dense attention");
     return SPARSEPR_OK;
 }

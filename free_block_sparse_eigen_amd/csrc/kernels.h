@@ -9,7 +9,8 @@ namespace spr {
 
 constexpr int kSortChunk = 1024;      // points per counting-sort block
 constexpr int kMaxGroups = 1024;      // G_k, G_q upper bound (LDS tables)
-constexpr int kAttnRows = 256;        // query rows per attention work unit
+constexpr int kSparseRows = 128;      // query rows per sparse attention unit (4 waves, 2 blocks/CU)
+constexpr int kDenseRows = 256;       // query rows per dense attention unit (8 waves, 1 block/CU)
 constexpr int kKeyTile = 64;          // keys per attention tile
 constexpr int kProbeRows = 256;       // probe rows per probe work unit (8 waves of 32)
 
@@ -52,12 +53,13 @@ void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int
                   int2* units, int32_t* nunits, hipStream_t st);
 
 // ---- attention ----
-// out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index)
+// out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index); unit_rows is
+// kSparseRows or kDenseRows (the units' row count, which fixes the block shape)
 void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
-                 void* out, int out_mode, hipStream_t st);
+                 int unit_rows, void* out, int out_mode, hipStream_t st);
 int probe_splits(int n, int heads, int probes);
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
                   const int32_t* probe_pos, const int32_t* probe_grp, int probes,

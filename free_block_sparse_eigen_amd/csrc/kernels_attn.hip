@@ -8,7 +8,11 @@
 // a work unit walks the routed segments only (the cloud.baidu.com explainer's point that
 // skipping, not computing-then-masking, is what saves work).
 //
-// Work unit = (head, query group, up to 256 query rows); 8 waves x 32 rows.
+// Work unit = (head, query group, up to NW x 32 query rows); NW waves x 32 rows. The sparse
+// call runs 4-wave blocks, two per CU: the blocks wait at their tile barriers independently,
+// so one block's waves keep the SIMDs busy while the other's wait (the many partial units
+// of small query groups gain most). The dense baseline, all full units, runs 8-wave
+// blocks that share each key tile over 256 rows.
 //   S^T = K Q^T  : A = K tile from LDS (row-major), B = Q^T fragments held in VGPRs
 //   O^T += V^T P^T: A = V^T read from the row-major V tile with the transposing LDS
 //                   read, B = P^T straight from the S^T accumulators (bf16, no
@@ -61,15 +65,15 @@ __device__ inline bool unit_of_block(const int32_t* __restrict__ nunits, int str
 
 }  // namespace
 
-// Block = 8 waves x 32 query rows: a unit of up to 256 rows shares every key tile.
-constexpr int kVbsaThreads = 512;
-template <int D, int OUTM>
-__global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
+// Block = NW waves x 32 query rows: a unit of up to NW x 32 rows shares every key tile.
+template <int D, int OUTM, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
     const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
     int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
     const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
     int nunits_stride, int heads, float scale_log2, void* __restrict__ out) {
+    constexpr int kVbsaThreads = NW * 64;
     using TL = Tile<D, kVbsaThreads>;
     constexpr int DB = D / 32;
     __shared__ int s_pre[kMaxGroups + 1];
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(kVbsaThreads, 1) void k_vbsa(
     const int2 un = units[(size_t)h * units_head_stride + ui];
     const int gi = un.x, row0 = un.y;
     const int32_t* qo = qoff + (size_t)h * qoff_stride;
-    const int rows = min(kAttnRows, qo[gi + 1] - row0);
+    const int rows = min(NW * 32, qo[gi + 1] - row0);
     const int32_t* ko = koff + (size_t)h * koff_stride;
     const int32_t* bl = blocks + (size_t)h * blocks_head_stride + (size_t)gi * kblk;
     const size_t head_row0 = (size_t)h * n;
@@ -272,18 +276,26 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
-                 void* out, int out_mode, hipStream_t st) {
+                 int unit_rows, void* out, int out_mode, hipStream_t st) {
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     // 8 XCD slots per round of units: enough blocks for every head's units at any split
     dim3 grid(8 * ((max_units + 7) / 8), heads);
-#define SPR_VBSA(DD, MM)                                                                     \
-    hipLaunchKernelGGL((k_vbsa<DD, MM>), grid, dim3(kVbsaThreads), 0, st, qp, kp, vp, n, qoff,        \
+#define SPR_VBSA(DD, MM, NW)                                                                 \
+    hipLaunchKernelGGL((k_vbsa<DD, MM, NW>), grid, dim3(NW * 64), 0, st, qp, kp, vp, n, qoff,         \
                        qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units, \
                        units_head_stride, nunits, nunits_stride, heads, scale_log2, out)
-    if (d == 128) {
-        if (out_mode == 0) SPR_VBSA(128, 0); else SPR_VBSA(128, 1);
+    if (unit_rows == kSparseRows) {
+        if (d == 128) {
+            if (out_mode == 0) SPR_VBSA(128, 0, 4); else SPR_VBSA(128, 1, 4);
+        } else {
+            if (out_mode == 0) SPR_VBSA(64, 0, 4); else SPR_VBSA(64, 1, 4);
+        }
     } else {
-        if (out_mode == 0) SPR_VBSA(64, 0); else SPR_VBSA(64, 1);
+        if (d == 128) {
+            if (out_mode == 0) SPR_VBSA(128, 0, 8); else SPR_VBSA(128, 1, 8);
+        } else {
+            if (out_mode == 0) SPR_VBSA(64, 0, 8); else SPR_VBSA(64, 1, 8);
+        }
     }
 #undef SPR_VBSA
 }
