@@ -69,9 +69,11 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
 // --------------------------------------------------------- centroid finish ---
 // For raw-space centroid means m (fp64), with the metric given either as a factor
 // L [d][D] (metric L L^T) or, with dout == 0, as the full metric M [d][d]:
-//   factor:  projected centroid c = m L (fp64, used by the fp64 recheck),
+//   factor:  projected centroid c = m L (fp64, used by the fp64 recheck; stored
+//            coordinate-major, [dim][G], so that the recheck's reads coalesce),
 //            screening vector C' = L c^T (d-dim; x . C' = (x L) . c for any point x)
-//   metric:  screening vector C' = M m (its fp64 copy is what the recheck uses) and
+//   metric:  screening vector C' = M m (its fp64 copy, coordinate-major, is what the
+//            recheck uses) and
 //            |c|^2 = m . C' (also kept in fp64)
 //   split of C' into bf16 hi + lo parts   (the MFMA operand; |C' - hi - lo| <= 2^-17 |C'|)
 //   |c|^2 (fp32, nearest) and |C'| (fp32, rounded up) for the screening score and bound
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         double a = 0.0, b = 0.0;
         for (int j = lane; j < dout; j += 64) {
             const double cv = s_c[gs][j];
-            c64[((size_t)h * groups + g) * dout + j] = cv;
+            c64[((size_t)h * dout + j) * groups + g] = cv;          // coordinate-major
             a += full ? s_m[gs][j] * cv : cv * cv;
         }
         for (int i = lane; i < d; i += 64) {
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
         for (int b = 0; b < RB; ++b) { best[b] = INFINITY; bg[b] = 0x7fffffff; }
         for (int g = tid; g < groups; g += 256) {
-            const double* c = ch + (size_t)g * cdim;
+            const double* c = ch + g;                  // coordinate j of centroid g at c[j * groups]
             double acc[RB];
 #pragma unroll
             for (int b = 0; b < RB; ++b) acc[b] = 0.0;
@@ -620,14 +622,14 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                 for (; j + 16 <= d; j += 16) {           // loads 16 at a time, sums in order
                     double cv[16];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) cv[u] = c[j + u];
+                    for (int u = 0; u < 16; ++u) cv[u] = c[(size_t)(j + u) * groups];
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
 #pragma unroll
                         for (int b = 0; b < RB; ++b) acc[b] += xs[j + u][b] * cv[u];
                 }
                 for (; j < d; ++j) {
-                    const double cj = c[j];
+                    const double cj = c[(size_t)j * groups];
 #pragma unroll
                     for (int b = 0; b < RB; ++b) acc[b] += xs[j][b] * cj;
                 }
@@ -639,7 +641,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                 for (; j + 16 <= dim; j += 16) {
                     double cv[16];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) cv[u] = c[j + u];
+                    for (int u = 0; u < 16; ++u) cv[u] = c[(size_t)(j + u) * groups];
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
 #pragma unroll
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                         }
                 }
                 for (; j < dim; ++j) {
-                    const double cj = c[j];
+                    const double cj = c[(size_t)j * groups];
 #pragma unroll
                     for (int b = 0; b < RB; ++b) {
                         const double t = ys[j][b] - cj;
