@@ -188,10 +188,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
                     s1[r] = (key + 32 < nvk) ? s1[r] : -INFINITY;
                 }
             }
-            float mx = fmaxf(s0[0], s1[0]);
+            // two chains of three-input maxima (15 v_max3 + 1 v_max for the 32 logits)
+            float ma = fmaxf(s0[0], s1[0]), mb = fmaxf(s0[1], s1[1]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = pair_max(mx);
+            for (int r = 2; r < 16; r += 2) {
+                ma = fmaxf(fmaxf(ma, s0[r]), s1[r]);
+                mb = fmaxf(fmaxf(mb, s0[r + 1]), s1[r + 1]);
+            }
+            float mx = pair_max(fmaxf(ma, mb));
             const float mt = mx * scale_log2;
             if (__ballot(mt > m_run + kLazy)) {
                 const float mnew = fmaxf(m_run, mt);

@@ -137,12 +137,14 @@ __global__ __launch_bounds__(512, 1) void k_probe(
                         if (key >= nvk) sv[kb][r] = -INFINITY;
                     }
             }
-            float mx = -INFINITY;
+            // two chains of three-input maxima (15 v_max3 + 1 v_max for the 32 logits)
+            float ma = fmaxf(sv[0][0], sv[1][0]), mb = fmaxf(sv[0][1], sv[1][1]);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
-            mx = pair_max(mx) * scale_log2;
+            for (int r = 2; r < 16; r += 2) {
+                ma = fmaxf(fmaxf(ma, sv[0][r]), sv[1][r]);
+                mb = fmaxf(fmaxf(mb, sv[0][r + 1]), sv[1][r + 1]);
+            }
+            const float mx = pair_max(fmaxf(ma, mb)) * scale_log2;
             if (__ballot(mx > m_run + kLazy)) {
                 const float mnew = fmaxf(m_run, mx);
                 const float alpha = fast_exp2(m_run - mnew);
