@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libsparsepr.so")
 
 BF16, F32 = 0, 1
 F_STAGE_TIMING = 1
+F_RAW_KMEANS = 2      # comparison partitioner: independent Euclidean k-means of raw Q and K
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "out of memory",
           4: "HIP error", 5: "stage order", 6: "numerical failure"}

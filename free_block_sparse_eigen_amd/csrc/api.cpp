@@ -91,6 +91,7 @@ struct sparsepr_ctx {
     int device = 0;
     int H = 0, N = 0, d = 0, Gk = 0, Gq = 0, rK = 0, Dq = 0, k = 0, P = 0, T = 0;
     int nblk = 0, maxu = 0, splits = 0, dense_units = 0, gmax = 0;
+    bool raw = false;                  // SPARSEPR_F_RAW_KMEANS: identity metrics on both sides
     int64_t weyl_a = 0;
 
     void* arena = nullptr;
@@ -103,6 +104,7 @@ struct sparsepr_ctx {
     int32_t *koff = nullptr, *qoff = nullptr;
     int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
     double *mk = nullptr, *w64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
+    double* ident = nullptr;           // [H][d][d] identity metric (SPARSEPR_F_RAW_KMEANS)
     double *kc2 = nullptr, *qc2 = nullptr;               // fp64 |c|^2 per centroid
     double *kraw = nullptr, *qraw = nullptr;
     bf16_t *kcp = nullptr, *qcp = nullptr;               // screening vectors, bf16 hi/lo
@@ -179,7 +181,7 @@ int32_t validate(const sparsepr_params* p) {
     if (p->corr_rank < 0 || p->corr_rank > p->d) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
-    if (p->flags & ~SPARSEPR_F_STAGE_TIMING) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS)) return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
 }
 
@@ -203,6 +205,7 @@ void derive(sparsepr_ctx& c) {
     c.Gk = p.kv_groups;
     c.Gq = p.q_groups;
     c.rK = p.key_rank;
+    c.raw = (p.flags & SPARSEPR_F_RAW_KMEANS) != 0;
     c.Dq = c.d;                         // the query metric is used in full (d x d)
     c.k = routed_count(p.density, c.Gk);
     c.P = p.probes;
@@ -238,7 +241,8 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.blkoff, H * c.nblk * c.gmax);
     a.take(c.mk, H * d * d);
     a.take(c.w64, H * d * c.rK);
-    a.take(c.kc64, H * c.Gk * c.rK);
+    a.take(c.kc64, H * c.Gk * (c.raw ? d : (size_t)c.rK));
+    if (c.raw) a.take(c.ident, H * d * d);
     a.take(c.qc64, H * c.Gq * d);
     a.take(c.kc2, H * c.Gk);
     a.take(c.qc2, H * c.Gq);
@@ -444,6 +448,14 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
     }
+    if (c->raw) {
+        const size_t H = c->H, d = c->d;
+        std::vector<double> eye(H * d * d, 0.0);
+        for (size_t h = 0; h < H; ++h)
+            for (size_t i = 0; i < d; ++i) eye[(h * d + i) * d + i] = 1.0;
+        if ((e = hipMemcpy(c->ident, eye.data(), sizeof(double) * H * d * d, hipMemcpyHostToDevice)) != hipSuccess)
+            return create_fail(c, SPARSEPR_ERR_HIP, "hipMemcpy (identity metric)", e);
+    }
     // dense baseline metadata
     const int meta[8] = {0, c->N, 0, c->N, 0, c->dense_units, 0, 0};
     if ((e = hipMemcpy(c->dense_meta, meta, sizeof(meta), hipMemcpyHostToDevice)) != hipSuccess)
@@ -491,6 +503,19 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * H, st);
+    if (c->raw) {
+        // comparison partitioner: plain Euclidean k-means of the raw key rows, then of the
+        // raw query rows (full-metric path with M = I: screening vector = mean)
+        rc = lloyd(c, k16, 0, c->ident, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
+                   c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
+        if (rc) return rc;
+        rc = lloyd(c, q16, 0, c->ident, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm,
+                   c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
+        if (rc) return rc;
+        mark(c, 1, st);
+        c->stage = kStagePartition;
+        return SPARSEPR_OK;
+    }
     // M_K and its leading eigenvectors (host fp64)
     launch_metric(q16, c->H, c->N, c->d, c->p.n_sample, c->weyl_a, c->mk, st);
     SPR_LAUNCHED(c, "metric");

@@ -65,6 +65,11 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
 
 /* flags */
 #define SPARSEPR_F_STAGE_TIMING 1u  /* record per-stage HIP events (sparsepr_get_stats) */
+#define SPARSEPR_F_RAW_KMEANS 2u    /* comparison partitioner, not the method: keys and queries
+                                       each clustered by plain Euclidean k-means of their raw
+                                       rows (the independent Q/K clustering of cluster-based
+                                       sparse attention), with the same seeds, rounds, routing,
+                                       probes and correction; no M_K and no host round trip */
 
 typedef struct {
     int32_t heads;          /* H >= 1 */
@@ -125,7 +130,8 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 
 /* 2A. Reads q, k. Host-synchronising once (fp64 eigensolve of M_K on the host); the
  * query side runs on the device with the logit-profile metric C_K^T C_K / d in full.
- * Leaves key/query labels and centroids in the context. */
+ * Leaves key/query labels and centroids in the context. With SPARSEPR_F_RAW_KMEANS both
+ * sides use the identity metric instead (no host round trip). */
 int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void* stream);
 
 /* 2C/2B. Reads q, k, v. Stable group-major permutation of Q/K/V, top-k key groups per

@@ -162,6 +162,21 @@ def partition(q: np.ndarray, k: np.ndarray, n_sample: int, key_rank: int,
     return Partition(key_labels, q_labels, ck, cq, lam)
 
 
+def raw_partition(q: np.ndarray, k: np.ndarray, kv_groups: int, q_groups: int,
+                  iters: int) -> Partition:
+    """Comparison partitioner, not the method: keys and queries each clustered by
+    plain Euclidean k-means of their raw rows, independently of each other (the
+    clustering that [SVOO]'s design-motivation item attributes to cluster-based
+    sparse attention such as SVG2, and that [PR 2A]'s response coupling replaces).
+    Reading: the same Lloyd (seeds, rounds, ties) as the method's partition, so that
+    the two differ only in the space each side is clustered in."""
+    key_labels, _ = lloyd(k, kv_groups, iters)
+    q_labels, _ = lloyd(q, q_groups, iters)
+    ck = group_means(k, key_labels, kv_groups)
+    cq = group_means(q, q_labels, q_groups)
+    return Partition(key_labels, q_labels, ck, cq, np.zeros(0))
+
+
 # ------------------------------------------------------------------ layout ---
 def group_major(labels: np.ndarray, groups: int):
     """Contiguous group-major layout [PR 2C]: a stable sort of token indices by
@@ -362,15 +377,18 @@ class HeadResult:
 def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, key_rank: int,
                 kv_groups: int, q_groups: int, kmeans_iters: int, density: float, probes: int,
                 ridge_lambda: float, corr_rank: int,
-                part: Optional[Partition] = None) -> HeadResult:
+                part: Optional[Partition] = None, raw_kmeans: bool = False) -> HeadResult:
     """One head of one SparsePR call, stage by stage:
     partition -> group-major layout -> routing + probes -> sparse attention and
     exact probe rows -> probe fit -> correction -> original order.
-    `part` injects a partition (labels) instead of computing it."""
+    `part` injects a partition (labels) instead of computing it; `raw_kmeans` uses the
+    comparison partitioner (raw_partition) instead of the method's."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    if part is None:
+    if part is None and raw_kmeans:
+        part = raw_partition(q, k, kv_groups, q_groups, kmeans_iters)
+    elif part is None:
         part = partition(q, k, n_sample, key_rank, kv_groups, q_groups, kmeans_iters)
     ck = group_means(k, part.key_labels, kv_groups)
     cq = group_means(q, part.q_labels, q_groups)
@@ -394,12 +412,12 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
 
 
 def oracle_call(q: np.ndarray, k: np.ndarray, v: np.ndarray, settings,
-                heads: Optional[Sequence[int]] = None) -> List[HeadResult]:
+                heads: Optional[Sequence[int]] = None, raw_kmeans: bool = False) -> List[HeadResult]:
     """All heads of one call; `settings` carries the SparsePR parameters by name."""
     kw = dict(n_sample=settings.n_sample, key_rank=settings.key_rank,
               kv_groups=settings.kv_groups, q_groups=settings.q_groups,
               kmeans_iters=settings.kmeans_iters, density=settings.density,
               probes=settings.probes, ridge_lambda=settings.ridge_lambda,
-              corr_rank=settings.corr_rank)
+              corr_rank=settings.corr_rank, raw_kmeans=raw_kmeans)
     hs = range(q.shape[0]) if heads is None else heads
     return [oracle_head(q[h], k[h], v[h], **kw) for h in hs]

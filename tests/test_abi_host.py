@@ -176,3 +176,23 @@ def test_single_hip_runtime_in_process():
                        timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.split("\n")[0] == "1", r.stdout
+
+
+def test_diagnostics_support_statistics_on_a_constructed_case():
+    """Each query attends (to machine precision) to one key: row supports are 1, a group's
+    aggregate support is the number of distinct keys its rows attend to, and the routed
+    mass is the share of its rows whose key lies in the routed key groups."""
+    from free_block_sparse_eigen_amd import diagnostics as dg
+    d = 4
+    k = (np.eye(d) * 10.0)[None]                      # key j along axis j
+    attend = np.array([0, 0, 1, 2, 0])                # query row -> attended key
+    q = (np.eye(d)[attend] * 10.0)[None]              # logits 50 on the attended key, 0 elsewhere
+    part = {"q_perm": np.array([[0, 1, 2, 3, 4]]), "q_off": np.array([[0, 3, 5]]),
+            "key_perm": np.array([[0, 1, 2, 3]]), "key_off": np.array([[0, 2, 4]])}
+    rout = {"blocks": np.array([[[0], [1]]])}         # q group 0 -> keys {0,1}, group 1 -> {2,3}
+    res = dg._support_stats(q, k, part, rout, groups=2, tau=0.9, d=d)
+    assert [r["group"] for r in res] == [0, 1]
+    g0, g1 = res
+    assert g0["rows"] == 3 and g0["mean_row_support"] == 1.0 and g0["aggregate_support"] == 2
+    assert g0["expansion"] == 2.0 and g0["routed_keys"] == 2 and abs(g0["routed_mass"] - 1.0) < 1e-12
+    assert g1["rows"] == 2 and g1["aggregate_support"] == 2 and abs(g1["routed_mass"] - 0.5) < 1e-12

@@ -148,6 +148,39 @@ def test_lloyd_all_equal_points_go_to_group_zero():
     assert np.all(lab == 0)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_raw_partition_is_brute_force_lloyd_of_each_side(seed):
+    """The comparison partitioner clusters raw keys and raw queries independently."""
+    rng = np.random.default_rng(300 + seed)
+    n, dim = int(rng.integers(10, 40)), int(rng.integers(2, 5))
+    q = rng.standard_normal((n, dim)).round(1)
+    k = rng.standard_normal((n, dim)).round(1)
+    gk, gq = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    part = orc.raw_partition(q, k, gk, gq, 3)
+    assert part.key_labels.tolist() == brute.lloyd(_tolist(k), orc.weyl_indices(n, gk).tolist(), 3)
+    assert part.q_labels.tolist() == brute.lloyd(_tolist(q), orc.weyl_indices(n, gq).tolist(), 3)
+    assert np.allclose(part.key_centroids, orc.group_means(k, part.key_labels, gk))
+
+
+def test_raw_partition_recovers_planted_blobs():
+    """Well-separated blobs whose seed points (the first Weyl indices) lie in distinct
+    blobs come back exactly as the groups, labelled in seed order."""
+    rng = np.random.default_rng(9)
+    n, g, dim = 300, 6, 8
+    centers = rng.standard_normal((g, dim)) * 50
+    blob = rng.integers(0, g, n)
+    seeds = orc.weyl_indices(n, g)
+    blob[seeds] = np.arange(g)
+    k = centers[blob] + rng.standard_normal((n, dim))
+    q = centers[(blob + 1) % g] + rng.standard_normal((n, dim))
+    part = orc.raw_partition(q, k, g, g, 5)
+    assert np.array_equal(part.key_labels, blob)
+    # the query seed at index seeds[j] sits in blob (j + 1) % g, so label j is that blob
+    expect_q = np.empty(g, np.int64)
+    expect_q[(np.arange(g) + 1) % g] = np.arange(g)
+    assert np.array_equal(part.q_labels, expect_q[(blob + 1) % g])
+
+
 def test_query_profile_kmeans_equals_cholesky_coordinates():
     """Profile-space distances equal |(q - c) L|^2 with L L^T = C_K^T C_K / d, so
     k-means in either space must give identical labels."""
