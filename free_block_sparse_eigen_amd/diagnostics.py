@@ -10,6 +10,8 @@ The comparison partitioner clusters raw Q and K independently (SPARSEPR_F_RAW_KM
 Per partitioner, for the given config:
   * hard-drop error  |O_s - O_dense|_F / |O_dense|_F over all rows and heads (GPU);
   * corrected error  |O - O_dense|_F / |O_dense|_F (GPU; probe rows are exact by design);
+  * the corrected error again with the fit redone on the host (the library's fp64 probe
+    fit, on the GPU's own probe rows) for other ridge lambdas, applied to O_s in fp32;
   * on a sample of query groups of head 0 (host fp64, from the library's own partition
     and routing): the routed mass (softmax mass of each row inside its group's routed key
     union, averaged over rows), the mean row support (smallest key set holding a fraction
@@ -28,6 +30,9 @@ import os
 import sys
 
 import numpy as np
+
+
+LAMBDA_SWEEP = (1e-3, 1e-1, 1.0, 10.0, 100.0)
 
 
 def _gpu_errors(spr, torch, cfg, q, k, v, flags):
@@ -54,8 +59,23 @@ def _gpu_errors(spr, torch, cfg, q, k, v, flags):
     hard = torch.linalg.vector_norm(o_s - ref).item() / den
     corr = torch.linalg.vector_norm(od.float() - ref).item() / den
     stats = ctx.sparsepr_get_stats()
+    # corrected error with the fit redone for other lambdas (rank as configured)
+    x, y = ctx.sparsepr_get_probes()
+    porig = rout["probe_orig"]
+    sweep = {}
+    for lam in LAMBDA_SWEEP:
+        o = torch.empty_like(o_s)
+        for h in range(cfg.heads):
+            bm, bv = spr.sparsepr_host_probe_fit(x[h].astype(np.float64), y[h].astype(np.float64),
+                                                 lam, cfg.settings.corr_rank)
+            bmt = torch.from_numpy(bm.astype(np.float32)).to(dev)
+            bvt = torch.from_numpy(bv.astype(np.float32)).to(dev)
+            o[h] = o_s[h] + bvt + o_s[h] @ bmt
+            pr = torch.from_numpy(porig[h].astype(np.int64)).to(dev)
+            o[h].index_copy_(0, pr, ref[h].index_select(0, pr))   # probe rows: exact dense
+        sweep[f"{lam:g}"] = torch.linalg.vector_norm(o - ref).item() / den
     del ctx
-    return hard, corr, part, rout, stats
+    return hard, corr, part, rout, stats, sweep
 
 
 def _support_stats(q, k, part, rout, groups, tau, d):
@@ -114,12 +134,13 @@ def main() -> int:
     q, k, v = make_inputs(cfg)
     for name, flags in (("response_coupled", 0), ("raw_kmeans", spr.F_RAW_KMEANS)):
         print(f"[diag] {name}: GPU call and dense", file=sys.stderr, flush=True)
-        hard, corr, part, rout, stats = _gpu_errors(spr, torch, cfg, q, k, v, flags)
+        hard, corr, part, rout, stats, sweep = _gpu_errors(spr, torch, cfg, q, k, v, flags)
         print(f"[diag] {name}: supports on {args.groups} groups of head 0", file=sys.stderr, flush=True)
         sup = _support_stats(q, k, part, rout, args.groups, args.tau, cfg.d)
         out = {"partitioner": name, "config": args.config, "density": cfg.settings.density,
                "routed_pair_density": stats["routed_pairs"] / (cfg.heads * cfg.n ** 2),
-               "hard_drop_rel_fro": hard, "corrected_rel_fro": corr, "tau": args.tau,
+               "hard_drop_rel_fro": hard, "corrected_rel_fro": corr,
+               "corrected_rel_fro_by_lambda": sweep, "tau": args.tau,
                "sample_routed_mass": float(np.mean([s["routed_mass"] for s in sup])),
                "sample_mean_row_support": float(np.mean([s["mean_row_support"] for s in sup])),
                "sample_aggregate_support": float(np.mean([s["aggregate_support"] for s in sup])),
