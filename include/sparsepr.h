@@ -97,7 +97,7 @@ typedef struct {
     int32_t query_dims;        /* dimension the query k-means runs in: d (the logit-profile
                                   metric C_K^T C_K / d is applied in full) */
     float   stage_ms[6];       /* mean ms per call of: partition, route, sparse attention kernel,
-                                  probe rows (with the fit Grams), probe fit (the part of the
+                                  probe rows (the fit Grams run on a side stream), probe fit (the part of the
                                   host solve and upload not hidden behind the sparse kernel),
                                   correction (SPARSEPR_F_STAGE_TIMING;
                                   averaged over the calls since the previous
