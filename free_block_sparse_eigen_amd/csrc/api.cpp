@@ -96,9 +96,10 @@ struct sparsepr_ctx {
 
     void* arena = nullptr;
     size_t arena_bytes = 0;
-    // bf16 copies of fp32 inputs, and the group-major Q/K/V
+    // bf16 copies of fp32 inputs, and the group-major K/V
     bf16_t *qb = nullptr, *kb = nullptr, *vb = nullptr;
-    bf16_t *qp = nullptr, *kp = nullptr, *vp = nullptr;
+    bf16_t *kp = nullptr, *vp = nullptr;          // K, V in group-major order
+    const bf16_t* q_src = nullptr;                // Q in token order (the route stage's input)
     // partition
     int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
     int32_t *koff = nullptr, *qoff = nullptr;
@@ -226,7 +227,6 @@ void layout(sparsepr_ctx& c, Arena& a) {
         a.take(c.kb, HND);
         a.take(c.vb, HND);
     }
-    a.take(c.qp, HND);
     a.take(c.kp, HND);
     a.take(c.vp, HND);
     a.take(c.klab, HN);
@@ -591,7 +591,7 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
-    launch_permute(q16, c->qperm, c->H, c->N, c->d, c->qp, st);
+    c->q_src = q16;           // the sparse stage gathers query rows through the permutation
     launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, st);
     launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
     SPR_LAUNCHED(c, "permute");
@@ -621,7 +621,7 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     // previous call's side work, which reads the probe buffers written here.
     SPR_HIP(c, hipStreamWaitEvent(st, c->ev_probe, 0));
     if (c->P > 0) {
-        launch_probe(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->probe_pos, c->probe_grp, c->P,
+        launch_probe(c->q_src, c->kp, c->vp, c->H, c->N, c->d, c->probe_orig, c->probe_grp, c->P,
                      c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->splits, c->part_ml,
                      c->part_od, c->part_os, st);
         launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
@@ -649,7 +649,7 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
         SPR_HIP(c, hipEventRecord(c->ev_probe, st));
     }
     mark(c, 4, st);
-    launch_vbsa(c->qp, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
+    launch_vbsa(c->q_src, c->qperm, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
                 c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, kSparseRows,
                 c->o_s, 0, st);
     SPR_LAUNCHED(c, "sparse attention");
@@ -736,7 +736,7 @@ int32_t sparsepr_dense_attn(sparsepr_ctx* c, const void* q, const void* k, const
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
-    launch_vbsa(q16, k16, v16, c->H, c->N, c->d, c->dense_meta, 0, c->dense_meta + 2, 0,
+    launch_vbsa(q16, nullptr, k16, v16, c->H, c->N, c->d, c->dense_meta, 0, c->dense_meta + 2, 0,
                 c->dense_meta + 4, 0, 1, c->dense_unit_list, 0, c->dense_meta + 6, 0, c->dense_units,
                 kDenseRows, o, c->p.dtype == SPARSEPR_F32 ? 0 : 1, st);
     SPR_LAUNCHED(c, "dense attention");

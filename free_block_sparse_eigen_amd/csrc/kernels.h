@@ -55,14 +55,17 @@ void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int
 // ---- attention ----
 // out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index); unit_rows is
 // kSparseRows or kDenseRows (the units' row count, which fixes the block shape)
-void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+// qp: Q in token order; qperm [heads][n] (group-major position -> token) or nullptr
+void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const bf16_t* vp,
+                 int heads, int n, int d,
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
                  int unit_rows, void* out, int out_mode, hipStream_t st);
 int probe_splits(int n, int heads, int probes);
+// qp: Q in token order, probe_orig: the probe rows' token indices; kp, vp group-major
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
-                  const int32_t* probe_pos, const int32_t* probe_grp, int probes,
+                  const int32_t* probe_orig, const int32_t* probe_grp, int probes,
                   const int32_t* koff, int koff_stride, int gk, const int32_t* blocks, int gq,
                   int kblk, int splits, float* part_ml, float* part_od, float* part_os,
                   hipStream_t st);

@@ -68,8 +68,8 @@ __device__ inline bool unit_of_block(const int32_t* __restrict__ nunits, int str
 // Block = NW waves x 32 query rows: a unit of up to NW x 32 rows shares every key tile.
 template <int D, int OUTM, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
-    const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
-    int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
+    const bf16_t* __restrict__ qp, const int32_t* __restrict__ qperm, const bf16_t* __restrict__ kp,
+    const bf16_t* __restrict__ vp, int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
     int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
     const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
     int nunits_stride, int heads, float scale_log2, void* __restrict__ out) {
@@ -124,15 +124,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
         }
     };
 
-    // Q^T fragments of this wave's 32 rows
+    // Q^T fragments of this wave's 32 rows, gathered from token order through the
+    // query permutation (none for the dense baseline)
     const bool active = w * 32 < rows;
     const int qrow = w * 32 + (lane & 31);
     const bool qvalid = qrow < rows;
     uint4 qf[D / 16];
+    {
+        const int src = !qvalid ? 0 : (qperm ? qperm[head_row0 + row0 + qrow] : row0 + qrow);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-        qf[kk] = qvalid ? ldg16(qp + (head_row0 + row0 + qrow) * D + 16 * kk + 8 * (lane >> 5))
-                        : make_uint4(0, 0, 0, 0);
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = qvalid ? ldg16(qp + (head_row0 + src) * D + 16 * kk + 8 * (lane >> 5))
+                            : make_uint4(0, 0, 0, 0);
+    }
 
     f32x16 o[DB];
 #pragma unroll
@@ -276,7 +280,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
         }
 }
 
-void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const bf16_t* vp,
+                 int heads, int n, int d,
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
@@ -285,7 +290,7 @@ void launch_vbsa(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads
     // 8 XCD slots per round of units: enough blocks for every head's units at any split
     dim3 grid(8 * ((max_units + 7) / 8), heads);
 #define SPR_VBSA(DD, MM, NW)                                                                 \
-    hipLaunchKernelGGL((k_vbsa<DD, MM, NW>), grid, dim3(NW * 64), 0, st, qp, kp, vp, n, qoff,         \
+    hipLaunchKernelGGL((k_vbsa<DD, MM, NW>), grid, dim3(NW * 64), 0, st, qp, qperm, kp, vp, n, qoff,  \
                        qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units, \
                        units_head_stride, nunits, nunits_stride, heads, scale_log2, out)
     if (unit_rows == kSparseRows) {

@@ -41,7 +41,7 @@ int probe_splits(int n, int heads, int probes) {
 template <int D>
 __global__ __launch_bounds__(512, 1) void k_probe(
     const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
-    int n, const int32_t* __restrict__ probe_pos, const int32_t* __restrict__ probe_grp,
+    int n, const int32_t* __restrict__ probe_orig, const int32_t* __restrict__ probe_grp,
     int probes, const int32_t* __restrict__ koff, int koff_stride, int gk,
     const int32_t* __restrict__ blocks, int gq, int kblk, int chunk, float scale_log2,
     float* __restrict__ part_ml, float* __restrict__ part_od, float* __restrict__ part_os) {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(512, 1) void k_probe(
     const bool active = p0 + w * 32 < probes;
     uint4 qf[D / 16];
     {
-        const int qrow = pvalid ? probe_pos[(size_t)h * probes + p] : 0;
+        const int qrow = pvalid ? probe_orig[(size_t)h * probes + p] : 0;   // token order
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = pvalid ? ldg16(qp + (head_row0 + qrow) * D + 16 * kk + 8 * (lane >> 5))
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(512, 1) void k_probe(
 }
 
 void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
-                  const int32_t* probe_pos, const int32_t* probe_grp, int probes,
+                  const int32_t* probe_orig, const int32_t* probe_grp, int probes,
                   const int32_t* koff, int koff_stride, int gk, const int32_t* blocks, int gq,
                   int kblk, int splits, float* part_ml, float* part_od, float* part_os,
                   hipStream_t st) {
@@ -233,11 +233,11 @@ void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int head
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     dim3 grid((probes + kProbeRows - 1) / kProbeRows, splits, heads);
     if (d == 128)
-        hipLaunchKernelGGL(k_probe<128>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
+        hipLaunchKernelGGL(k_probe<128>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_orig, probe_grp,
                            probes, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2,
                            part_ml, part_od, part_os);
     else
-        hipLaunchKernelGGL(k_probe<64>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_pos, probe_grp,
+        hipLaunchKernelGGL(k_probe<64>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_orig, probe_grp,
                            probes, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2,
                            part_ml, part_od, part_os);
 }

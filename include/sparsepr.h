@@ -134,14 +134,19 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
  * sides use the identity metric instead (no host round trip). */
 int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void* stream);
 
-/* 2C/2B. Reads q, k, v. Stable group-major permutation of Q/K/V, top-k key groups per
- * query group (ties to the lower group index, empty key groups never kept), probe rows. */
+/* 2C/2B. Reads q, k, v. Stable group-major permutation of K/V, top-k key groups per
+ * query group (ties to the lower group index, empty key groups never kept), probe rows.
+ * Q is not copied: sparsepr_sparse_attn gathers its rows through the query permutation,
+ * so q must stay unchanged until sparsepr_sparse_attn has run (for an fp32 context the
+ * rows come from the context's bf16 copy of q, which sparsepr_dense_attn also rewrites:
+ * do not call it in between). */
 int32_t sparsepr_route(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
                        void* stream);
 
 /* 2C/2B. Exact dense + routed attention of the probe rows and the fit's fp64 Grams
  * (copied to pinned host memory), then block-sparse attention over the routed pairs
- * (unrouted blocks are never touched). Asynchronous: returns once both are enqueued. */
+ * (unrouted blocks are never touched). Reads the q given to sparsepr_route.
+ * Asynchronous: returns once both are enqueued. */
 int32_t sparsepr_sparse_attn(sparsepr_ctx* ctx, void* stream);
 
 /* 2B. fp64 fit on the host: B' = B Pi and b' = b Pi per head. Waits only for the probe
