@@ -189,7 +189,17 @@ void launch_correct(const float* o_s, const bf16_t* bt16, const float* bvec, con
                     const int32_t* probe_orig, const int32_t* qperm, int heads, int n, int d,
                     int probes, void* o, int out_f32, hipStream_t st) {
     const int ntile = (n + kCorrRows - 1) / kCorrRows;
-    int per_head = (256 + heads - 1) / heads;         // about one resident block per CU
+    // one resident block per CU (a block fills a CU): rounding the share per head down
+    // keeps the grid within one round of blocks
+    static int cus = 0;
+    if (cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    int per_head = cus / heads;
     if (per_head > ntile) per_head = ntile;
     if (per_head < 1) per_head = 1;
     dim3 grid(per_head, heads);
