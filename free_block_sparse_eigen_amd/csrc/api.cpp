@@ -135,6 +135,8 @@ struct sparsepr_ctx {
     void* h_b32 = nullptr;            // [H][2][d][d] bf16 B'^T hi/lo, then [H][d] fp32 b'
     hipEvent_t ev_probe = nullptr;    // probe rows and fit Grams are on the host
     hipEvent_t ev_rows = nullptr;     // probe rows merged (the fit's inputs are ready)
+    hipEvent_t ev_kdone = nullptr;    // key partition done (the side stream may permute K)
+    hipEvent_t ev_kperm = nullptr;    // K permuted on the side stream
     hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
 
     int stage = 0;
@@ -445,6 +447,8 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             return create_fail(c, SPARSEPR_ERR_OOM, "hipHostMalloc", e);
         if ((e = hipEventCreateWithFlags(&c->ev_probe, hipEventDisableTiming)) != hipSuccess ||
             (e = hipEventCreateWithFlags(&c->ev_rows, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&c->ev_kdone, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&c->ev_kperm, hipEventDisableTiming)) != hipSuccess ||
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
     }
@@ -481,6 +485,8 @@ void sparsepr_destroy(sparsepr_ctx* c) {
                 if (e) (void)hipEventDestroy(e);
     if (c->ev_probe) (void)hipEventDestroy(c->ev_probe);
     if (c->ev_rows) (void)hipEventDestroy(c->ev_rows);
+    if (c->ev_kdone) (void)hipEventDestroy(c->ev_kdone);
+    if (c->ev_kperm) (void)hipEventDestroy(c->ev_kperm);
     if (c->side) (void)hipStreamDestroy(c->side);
     if (c->h_fit) (void)hipHostFree(c->h_fit);
     if (c->h_mkp) (void)hipHostFree(c->h_mkp);
@@ -489,6 +495,21 @@ void sparsepr_destroy(sparsepr_ctx* c) {
     if (c->arena) (void)hipFree(c->arena);
     delete c;
 }
+
+namespace {
+// K into group-major order on the side stream, overlapping the query side of the
+// partition; the sparse stage waits for ev_kperm before reading it. The side stream
+// starts after all work enqueued so far on st, which includes the previous call's
+// readers of the permuted K.
+int32_t permute_keys_side(sparsepr_ctx* c, const bf16_t* k16, hipStream_t st) {
+    SPR_HIP(c, hipEventRecord(c->ev_kdone, st));
+    SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
+    launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);
+    SPR_LAUNCHED(c, "permute K");
+    SPR_HIP(c, hipEventRecord(c->ev_kperm, c->side));
+    return SPARSEPR_OK;
+}
+}  // namespace
 
 int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* stream) {
     int32_t rc = enter(c, 0);
@@ -509,6 +530,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         rc = lloyd(c, k16, 0, c->ident, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
                    c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
         if (rc) return rc;
+        if ((rc = permute_keys_side(c, k16, st))) return rc;
         rc = lloyd(c, q16, 0, c->ident, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm,
                    c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
         if (rc) return rc;
@@ -535,6 +557,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw, c->kc64,
                c->kcp, c->kcn2, c->kcpn, c->kc2, st);
     if (rc) return rc;
+    if ((rc = permute_keys_side(c, k16, st))) return rc;
     // queries: the logit-profile metric M = C_K^T C_K / d (fp64 Gram of the raw key
     // centroids) used in full on the device, then Lloyd
     launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
@@ -569,6 +592,7 @@ int32_t sparsepr_set_partition(sparsepr_ctx* c, const void* q, const void* k,
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * c->H, st);
     launch_counting_sort(c->klab, c->H, c->N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
+    if ((rc = permute_keys_side(c, k16, st))) return rc;
     launch_group_means(k16, c->H, c->N, c->d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr,
                        nullptr, nullptr, nullptr, nullptr, st);
     launch_counting_sort(c->qlab, c->H, c->N, c->Gq, c->blkhist, c->blkoff, c->qperm, c->qoff, st);
@@ -588,11 +612,10 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
     mark(c, 2, st);
+    // K was permuted in the partition stage (side stream); q is recorded, not copied
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
-    const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
     c->q_src = q16;           // the sparse stage gathers query rows through the permutation
-    launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, st);
     launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
     SPR_LAUNCHED(c, "permute");
     launch_fill_i64(c->pairs, 0, c->H, st);
@@ -620,6 +643,7 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     // solve (sparsepr_probe_fit) waits for them only. This stream first waits for the
     // previous call's side work, which reads the probe buffers written here.
     SPR_HIP(c, hipStreamWaitEvent(st, c->ev_probe, 0));
+    SPR_HIP(c, hipStreamWaitEvent(st, c->ev_kperm, 0));        // K permuted (side stream)
     if (c->P > 0) {
         launch_probe(c->q_src, c->kp, c->vp, c->H, c->N, c->d, c->probe_orig, c->probe_grp, c->P,
                      c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->splits, c->part_ml,

@@ -131,11 +131,15 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 /* 2A. Reads q, k. Host-synchronising once (fp64 eigensolve of M_K on the host); the
  * query side runs on the device with the logit-profile metric C_K^T C_K / d in full.
  * Leaves key/query labels and centroids in the context. With SPARSEPR_F_RAW_KMEANS both
- * sides use the identity metric instead (no host round trip). */
+ * sides use the identity metric instead (no host round trip). K is then permuted into
+ * group-major order on the context's side stream while the query side runs, so k must
+ * stay unchanged until sparsepr_sparse_attn has run (for an fp32 context: do not call
+ * sparsepr_dense_attn in between, which rewrites the context's bf16 copy). */
 int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void* stream);
 
-/* 2C/2B. Reads q, k, v. Stable group-major permutation of K/V, top-k key groups per
- * query group (ties to the lower group index, empty key groups never kept), probe rows.
+/* 2C/2B. Reads v (k is only checked). Stable group-major permutation of V, top-k key
+ * groups per query group (ties to the lower group index, empty key groups never kept),
+ * probe rows.
  * Q is not copied: sparsepr_sparse_attn gathers its rows through the query permutation,
  * so q must stay unchanged until sparsepr_sparse_attn has run (for an fp32 context the
  * rows come from the context's bf16 copy of q, which sparsepr_dense_attn also rewrites:
