@@ -196,3 +196,19 @@ def test_diagnostics_support_statistics_on_a_constructed_case():
     assert g0["rows"] == 3 and g0["mean_row_support"] == 1.0 and g0["aggregate_support"] == 2
     assert g0["expansion"] == 2.0 and g0["routed_keys"] == 2 and abs(g0["routed_mass"] - 1.0) < 1e-12
     assert g1["rows"] == 2 and g1["aggregate_support"] == 2 and abs(g1["routed_mass"] - 0.5) < 1e-12
+
+
+def test_validate_accepts_the_comparison_partitioner_flag():
+    p = spr.make_params(1, 4096, 64, spr.F32, n_sample=128, key_rank=16, kv_groups=16,
+                        q_groups=16, density=0.25, probes=64, corr_rank=8, flags=spr.F_RAW_KMEANS)
+    assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 0
+    p.flags = spr.F_RAW_KMEANS | spr.F_STAGE_TIMING
+    assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 0
+    p.flags = 4
+    assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 1        # SPARSEPR_ERR_INVALID_ARG
+    # the comparison partitioner needs d-wide fp64 key centroids: the workspace grows
+    p.flags = 0
+    base = spr.lib.sparsepr_workspace_bytes(ctypes.byref(p))
+    p.flags = spr.F_RAW_KMEANS
+    assert spr.lib.sparsepr_workspace_bytes(ctypes.byref(p)) > base
+
