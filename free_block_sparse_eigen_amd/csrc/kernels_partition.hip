@@ -53,10 +53,14 @@ __global__ void k_metric(const bf16_t* __restrict__ q, int n, int d, int ms, int
     const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
     const bf16_t* qh = q + (size_t)h * n * d;
     double s = 0.0;
+    int64_t idx = 0;                           // (t a) mod n, stepped (0 <= a < n)
+    const int64_t am = a % n;
+#pragma unroll 8
     for (int t = 0; t < ms; ++t) {
-        const int64_t idx = ((int64_t)t * a) % n;
         const bf16_t* row = qh + idx * d;
         s += (double)bf16_to_f32(row[i]) * (double)bf16_to_f32(row[j]);
+        idx += am;
+        if (idx >= n) idx -= n;
     }
     mk[((size_t)h * d + i) * d + j] = s / ms;
 }
