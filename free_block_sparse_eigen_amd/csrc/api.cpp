@@ -108,6 +108,7 @@ struct sparsepr_ctx {
     double* ident = nullptr;           // [H][d][d] identity metric (SPARSEPR_F_RAW_KMEANS)
     double *kc2 = nullptr, *qc2 = nullptr;               // fp64 |c|^2 per centroid
     double *kraw = nullptr, *qraw = nullptr;
+    double* kraw_t = nullptr;          // [H][d][G_k] coordinate-major key centroids (routing)
     bf16_t *kcp = nullptr, *qcp = nullptr;               // screening vectors, bf16 hi/lo
     float *kcn2 = nullptr, *qcn2 = nullptr, *kcpn = nullptr, *qcpn = nullptr;
     // route
@@ -249,6 +250,7 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.kc2, H * c.Gk);
     a.take(c.qc2, H * c.Gq);
     a.take(c.kraw, H * c.Gk * d);
+    a.take(c.kraw_t, H * c.Gk * d);
     a.take(c.qraw, H * c.Gq * d);
     a.take(c.kcp, H * 2 * c.Gk * d);
     a.take(c.qcp, H * 2 * c.Gq * d);
@@ -619,8 +621,8 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
     SPR_LAUNCHED(c, "permute");
     launch_fill_i64(c->pairs, 0, c->H, st);
-    launch_route(c->qraw, c->kraw, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k, c->blocks,
-                 c->ucount, c->pairs, st);
+    launch_route(c->qraw, c->kraw, c->kraw_t, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k,
+                 c->blocks, c->ucount, c->pairs, st);
     SPR_LAUNCHED(c, "route");
     launch_fill_i32(c->probe_of, -1, (size_t)c->H * c->N, st);
     launch_probes(c->qoff, c->qperm, c->H, c->N, c->Gq, c->P, c->probe_pos, c->probe_orig,

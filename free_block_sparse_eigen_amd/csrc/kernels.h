@@ -43,9 +43,10 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,
                     hipStream_t st);
-void launch_route(const double* cq, const double* ck, const int32_t* qoff, const int32_t* koff,
-                  int heads, int gq, int gk, int d, int k, int32_t* blocks, int32_t* ucount,
-                  int64_t* pairs, hipStream_t st);
+// ck_t: scratch [heads][d][gk] for the coordinate-major copy of ck
+void launch_route(const double* cq, const double* ck, double* ck_t, const int32_t* qoff,
+                  const int32_t* koff, int heads, int gq, int gk, int d, int k, int32_t* blocks,
+                  int32_t* ucount, int64_t* pairs, hipStream_t st);
 void launch_probes(const int32_t* qoff, const int32_t* qperm, int heads, int n, int gq, int probes,
                    int32_t* probe_pos, int32_t* probe_orig, int32_t* probe_grp, int32_t* probe_of,
                    hipStream_t st);

@@ -31,13 +31,33 @@ void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, in
                        src, perm, n, d, dst);
 }
 
+// Coordinate-major copy [heads][d][g] of row-major fp64 rows [heads][g][d].
+__global__ void k_transpose_f64(const double* __restrict__ src, int g, int d,
+                                double* __restrict__ dst) {
+    __shared__ double tile[32][33];
+    const int h = blockIdx.z, r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;     // 32 x 8 threads
+    const double* sh = src + (size_t)h * g * d;
+    double* dh = dst + (size_t)h * d * g;
+    for (int y = ty; y < 32; y += 8) {
+        const int r = r0 + y, c = c0 + tx;
+        tile[y][tx] = (r < g && c < d) ? sh[(size_t)r * d + c] : 0.0;
+    }
+    __syncthreads();
+    for (int y = ty; y < 32; y += 8) {
+        const int c = c0 + y, r = r0 + tx;                        // dst row c, column r
+        if (c < d && r < g) dh[(size_t)c * g + r] = tile[tx][y];
+    }
+}
+
 // Block per (query group, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64 (a thread per key
-// group, its sum over the d coordinates in ascending order, loads issued 16 at a time);
+// group, its sum over the d coordinates in ascending order, reading the coordinate-major
+// copy of the key centroids so that the lanes' loads coalesce, 16 at a time);
 // key group j is kept when it is non-empty and fewer than k non-empty groups rank above
 // it by (score descending, index ascending). Kept groups are written in ascending order
 // (ballot compaction), and the union size is a block reduction.
 __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
-                                               const double* __restrict__ ck,
+                                               const double* __restrict__ ckt,
                                                const int32_t* __restrict__ qoff,
                                                const int32_t* __restrict__ koff, int gq, int gk,
                                                int d, int k, int32_t* __restrict__ blocks,
@@ -55,17 +75,17 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
     const int32_t* ko = koff + (size_t)h * (gk + 1);
     const double rs = sqrt((double)d);
     for (int j = tid; j < gk; j += 256) {
-        const double* cj = ck + ((size_t)h * gk + j) * d;
+        const double* cj = ckt + (size_t)h * d * gk + j;          // coordinate t at cj[t * gk]
         double s = 0.0;
         int t = 0;
         for (; t + 16 <= d; t += 16) {
             double cv[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) cv[u] = cj[t + u];
+            for (int u = 0; u < 16; ++u) cv[u] = cj[(size_t)(t + u) * gk];
 #pragma unroll
             for (int u = 0; u < 16; ++u) s += cs[t + u] * cv[u];
         }
-        for (; t < d; ++t) s += cs[t] * cj[t];
+        for (; t < d; ++t) s += cs[t] * cj[(size_t)t * gk];
         sc[j] = s / rs;
         ne[j] = (ko[j + 1] > ko[j]) ? 1 : 0;
     }
@@ -109,10 +129,12 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
     }
 }
 
-void launch_route(const double* cq, const double* ck, const int32_t* qoff, const int32_t* koff,
-                  int heads, int gq, int gk, int d, int k, int32_t* blocks, int32_t* ucount,
-                  int64_t* pairs, hipStream_t st) {
-    hipLaunchKernelGGL(k_route, dim3(gq, heads), dim3(256), 0, st, cq, ck, qoff, koff, gq, gk, d, k,
+void launch_route(const double* cq, const double* ck, double* ck_t, const int32_t* qoff,
+                  const int32_t* koff, int heads, int gq, int gk, int d, int k, int32_t* blocks,
+                  int32_t* ucount, int64_t* pairs, hipStream_t st) {
+    hipLaunchKernelGGL(k_transpose_f64, dim3((d + 31) / 32, (gk + 31) / 32, heads), dim3(256), 0, st,
+                       ck, gk, d, ck_t);
+    hipLaunchKernelGGL(k_route, dim3(gq, heads), dim3(256), 0, st, cq, ck_t, qoff, koff, gq, gk, d, k,
                        blocks, ucount, pairs);
 }
 
