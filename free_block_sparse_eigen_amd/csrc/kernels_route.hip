@@ -208,16 +208,29 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff
                                                 int2* __restrict__ units,
                                                 int32_t* __restrict__ nunits) {
     __shared__ int base[kMaxGroups + 1];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    __shared__ int wtot[16];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int32_t* qo = qoff + (size_t)h * (gq + 1);
+    // units per group, then their exclusive prefix over the groups (wave scans and a scan
+    // of the wave totals; gq <= 1024 = blockDim)
+    const int cnt = (tid < gq) ? (qo[tid + 1] - qo[tid] + rows_per_unit - 1) / rows_per_unit : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int wb = 0, total = 0;
+    for (int k = 0; k < 16; ++k) {
+        wb += (k < w) ? wtot[k] : 0;
+        total += wtot[k];
+    }
+    if (tid < gq) base[tid] = wb + inc - cnt;
     if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < gq; ++i) {
-            base[i] = run;
-            run += (qo[i + 1] - qo[i] + rows_per_unit - 1) / rows_per_unit;
-        }
-        base[gq] = run;
-        nunits[h] = run;
+        base[gq] = total;
+        nunits[h] = total;
     }
     __syncthreads();
     for (int i = tid; i < gq; i += 1024) {
