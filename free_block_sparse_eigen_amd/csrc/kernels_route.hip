@@ -150,8 +150,27 @@ __global__ __launch_bounds__(1024) void k_probes(const int32_t* __restrict__ qof
     __shared__ int64_t rem[kMaxGroups];
     __shared__ int m[kMaxGroups];
     __shared__ int base[kMaxGroups];
-    __shared__ int left;
-    const int h = blockIdx.x, tid = threadIdx.x;
+    __shared__ int wtot[16];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // exclusive prefix of v over the block's threads (gq <= 1024 = blockDim); all threads
+    auto block_scan = [&](int v, int& total) {
+        int inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += t;
+        }
+        __syncthreads();
+        if (lane == 63) wtot[w] = inc;
+        __syncthreads();
+        int wb = 0;
+        total = 0;
+        for (int k = 0; k < 16; ++k) {
+            wb += (k < w) ? wtot[k] : 0;
+            total += wtot[k];
+        }
+        return wb + inc - v;
+    };
     const int32_t* qo = qoff + (size_t)h * (gq + 1);
     if (probes == 0) return;
     for (int i = tid; i < gq; i += 1024) {
@@ -160,12 +179,9 @@ __global__ __launch_bounds__(1024) void k_probes(const int32_t* __restrict__ qof
         rem[i] = (probes * ni) % n;
     }
     __syncthreads();
-    if (tid == 0) {
-        int s = 0;
-        for (int i = 0; i < gq; ++i) s += m[i];
-        left = probes - s;
-    }
-    __syncthreads();
+    int msum;
+    (void)block_scan(tid < gq ? m[tid] : 0, msum);
+    const int left = probes - msum;
     for (int i = tid; i < gq; i += 1024) {
         int rank = 0;
         const int64_t ri = rem[i];
@@ -173,13 +189,9 @@ __global__ __launch_bounds__(1024) void k_probes(const int32_t* __restrict__ qof
         if (rank < left) m[i] += 1;
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < gq; ++i) {
-            base[i] = run;
-            run += m[i];
-        }
-    }
+    int mtot;
+    const int b0 = block_scan(tid < gq ? m[tid] : 0, mtot);
+    if (tid < gq) base[tid] = b0;
     __syncthreads();
     for (int i = tid; i < gq; i += 1024) {
         const int64_t ni = qo[i + 1] - qo[i];
