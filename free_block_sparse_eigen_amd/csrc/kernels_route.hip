@@ -50,12 +50,15 @@ __global__ void k_transpose_f64(const double* __restrict__ src, int g, int d,
     }
 }
 
-// Block per (query group, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64 (a thread per key
-// group, its sum over the d coordinates in ascending order, reading the coordinate-major
-// copy of the key centroids so that the lanes' loads coalesce, 16 at a time);
-// key group j is kept when it is non-empty and fewer than k non-empty groups rank above
-// it by (score descending, index ascending). Kept groups are written in ascending order
-// (ballot compaction), and the union size is a block reduction.
+// Block per (kRouteGroups query groups, head). S_ij = c^Q_i . c^K_j / sqrt(d) in fp64 (a
+// thread per key group, each query group's sum over the d coordinates in ascending order,
+// reading the coordinate-major copy of the key centroids so that the lanes' loads coalesce,
+// 16 at a time, each load serving all the block's query groups); key group j is kept when
+// it is non-empty and fewer than k non-empty groups rank above it by (score descending,
+// index ascending). Kept groups are written in ascending order (ballot compaction), and the
+// union size is a block reduction.
+constexpr int kRouteGroups = 4;
+
 __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
                                                const double* __restrict__ ckt,
                                                const int32_t* __restrict__ qoff,
@@ -63,67 +66,115 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
                                                int d, int k, int32_t* __restrict__ blocks,
                                                int32_t* __restrict__ ucount,
                                                int64_t* __restrict__ pairs) {
-    __shared__ double cs[128];
-    __shared__ double sc[kMaxGroups];
+    constexpr int QG = kRouteGroups;
+    __shared__ double cs[QG][128];
+    __shared__ double sc[QG][kMaxGroups];
     __shared__ int ne[kMaxGroups];
-    __shared__ int wcnt[4];
-    __shared__ long long wsz[4];
-    const int h = blockIdx.y, i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const double* ci = cq + ((size_t)h * gq + i) * d;
-    for (int t = tid; t < d; t += 256) cs[t] = ci[t];
+    __shared__ int wcnt[QG][4];
+    __shared__ long long wsz[QG][4];
+    const int h = blockIdx.y, i0 = blockIdx.x * QG, tid = threadIdx.x, lane = tid & 63,
+              w = tid >> 6;
+    const int nq = min(QG, gq - i0);
+    for (int t = tid; t < QG * d; t += 256) {
+        const int q = t / d, c = t - q * d;
+        cs[q][c] = q < nq ? cq[((size_t)h * gq + i0 + q) * d + c] : 0.0;
+    }
     __syncthreads();
     const int32_t* ko = koff + (size_t)h * (gk + 1);
     const double rs = sqrt((double)d);
     for (int j = tid; j < gk; j += 256) {
         const double* cj = ckt + (size_t)h * d * gk + j;          // coordinate t at cj[t * gk]
-        double s = 0.0;
+        double s[QG];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) s[q] = 0.0;
         int t = 0;
         for (; t + 16 <= d; t += 16) {
             double cv[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) cv[u] = cj[(size_t)(t + u) * gk];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) s += cs[t + u] * cv[u];
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+                for (int q = 0; q < QG; ++q) s[q] += cs[q][t + u] * cv[u];
         }
-        for (; t < d; ++t) s += cs[t] * cj[(size_t)t * gk];
-        sc[j] = s / rs;
+        for (; t < d; ++t) {
+            const double cv = cj[(size_t)t * gk];
+#pragma unroll
+            for (int q = 0; q < QG; ++q) s[q] += cs[q][t] * cv;
+        }
+#pragma unroll
+        for (int q = 0; q < QG; ++q) sc[q][j] = s[q] / rs;
         ne[j] = (ko[j + 1] > ko[j]) ? 1 : 0;
     }
     __syncthreads();
-    int32_t* out = blocks + ((size_t)h * gq + i) * k;
-    int base = 0;
-    long long u = 0;
+    // The block's query groups are ranked together: one pass over t serves all of them.
+    int base[QG];
+    long long u[QG];
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+        base[q] = 0;
+        u[q] = 0;
+    }
     for (int j0 = 0; j0 < gk; j0 += 256) {
         const int j = j0 + tid;
-        bool keep = false;
+        bool keep[QG];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) keep[q] = false;
         if (j < gk && ne[j]) {
-            int rank = 0;
-            const double sj = sc[j];
-            for (int t = 0; t < gk; ++t)
-                rank += (ne[t] && (sc[t] > sj || (sc[t] == sj && t < j))) ? 1 : 0;
-            keep = rank < k;
+            double sj[QG];
+            int rank[QG];
+#pragma unroll
+            for (int q = 0; q < QG; ++q) {
+                sj[q] = sc[q][j];
+                rank[q] = 0;
+            }
+            for (int t = 0; t < gk; ++t) {
+                if (!ne[t]) continue;
+#pragma unroll
+                for (int q = 0; q < QG; ++q) {
+                    const double st = sc[q][t];
+                    rank[q] += (st > sj[q] || (st == sj[q] && t < j)) ? 1 : 0;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < QG; ++q) keep[q] = rank[q] < k;
         }
-        if (keep) u += ko[j + 1] - ko[j];
-        const uint64_t m = __ballot(keep);
-        if (lane == 0) wcnt[w] = __popcll(m);
+        const int nk = (j < gk) ? ko[j + 1] - ko[j] : 0;
+        uint64_t m[QG];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+            if (keep[q]) u[q] += nk;
+            m[q] = __ballot(keep[q]);
+            if (lane == 0) wcnt[q][w] = __popcll(m[q]);
+        }
         __syncthreads();
-        int before = 0, total = 0;
-        for (int q = 0; q < 4; ++q) {
-            before += (q < w) ? wcnt[q] : 0;
-            total += wcnt[q];
+#pragma unroll
+        for (int q = 0; q < QG; ++q) {
+            int before = 0, total = 0;
+            for (int r = 0; r < 4; ++r) {
+                before += (r < w) ? wcnt[q][r] : 0;
+                total += wcnt[q][r];
+            }
+            if (keep[q] && q < nq)
+                blocks[((size_t)h * gq + i0 + q) * k + base[q] + before +
+                       __popcll(m[q] & ((1ull << lane) - 1))] = j;
+            base[q] += total;
         }
-        if (keep) out[base + before + __popcll(m & ((1ull << lane) - 1))] = j;
-        base += total;
         __syncthreads();
     }
-    for (int p = base + tid; p < k; p += 256) out[p] = -1;
-    for (int o = 32; o > 0; o >>= 1) u += __shfl_xor(u, o, 64);
-    if (lane == 0) wsz[w] = u;
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+        if (q < nq)
+            for (int p = base[q] + tid; p < k; p += 256) blocks[((size_t)h * gq + i0 + q) * k + p] = -1;
+        for (int o = 32; o > 0; o >>= 1) u[q] += __shfl_xor(u[q], o, 64);
+        if (lane == 0) wsz[q][w] = u[q];
+    }
     __syncthreads();
-    if (tid == 0) {
-        const long long us = wsz[0] + wsz[1] + wsz[2] + wsz[3];
-        ucount[(size_t)h * gq + i] = (int32_t)us;
+    if (tid < nq) {
+        const int i = i0 + tid;
+        const long long us = wsz[tid][0] + wsz[tid][1] + wsz[tid][2] + wsz[tid][3];
         const int32_t* qo = qoff + (size_t)h * (gq + 1);
+        ucount[(size_t)h * gq + i] = (int32_t)us;
         atomicAdd(reinterpret_cast<unsigned long long*>(&pairs[h]),
                   (unsigned long long)(us * (int64_t)(qo[i + 1] - qo[i])));
     }
@@ -134,8 +185,8 @@ void launch_route(const double* cq, const double* ck, double* ck_t, const int32_
                   int32_t* ucount, int64_t* pairs, hipStream_t st) {
     hipLaunchKernelGGL(k_transpose_f64, dim3((d + 31) / 32, (gk + 31) / 32, heads), dim3(256), 0, st,
                        ck, gk, d, ck_t);
-    hipLaunchKernelGGL(k_route, dim3(gq, heads), dim3(256), 0, st, cq, ck_t, qoff, koff, gq, gk, d, k,
-                       blocks, ucount, pairs);
+    hipLaunchKernelGGL(k_route, dim3((gq + kRouteGroups - 1) / kRouteGroups, heads), dim3(256), 0,
+                       st, cq, ck_t, qoff, koff, gq, gk, d, k, blocks, ucount, pairs);
 }
 
 // Block per head. m_i = floor(P n_i / N); the leftover P - sum m_i go one each to the
