@@ -138,10 +138,7 @@ struct sparsepr_ctx {
     hipEvent_t ev_rows = nullptr;     // probe rows merged (the fit's inputs are ready)
     hipEvent_t ev_kdone = nullptr;    // key partition done (the side stream may permute K)
     hipEvent_t ev_kperm = nullptr;    // K permuted on the side stream
-    hipEvent_t ev_vdone = nullptr;    // V ready in bf16 (the side stream may permute it)
-    hipEvent_t ev_vperm = nullptr;    // V permuted on the side stream
     bool kperm_recorded = false;      // ev_kperm has been recorded
-    bool vperm_recorded = false;      // ev_vperm has been recorded
     hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
 
     int stage = 0;
@@ -455,8 +452,6 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             (e = hipEventCreateWithFlags(&c->ev_rows, hipEventDisableTiming)) != hipSuccess ||
             (e = hipEventCreateWithFlags(&c->ev_kdone, hipEventDisableTiming)) != hipSuccess ||
             (e = hipEventCreateWithFlags(&c->ev_kperm, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&c->ev_vdone, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&c->ev_vperm, hipEventDisableTiming)) != hipSuccess ||
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
     }
@@ -495,8 +490,6 @@ void sparsepr_destroy(sparsepr_ctx* c) {
     if (c->ev_rows) (void)hipEventDestroy(c->ev_rows);
     if (c->ev_kdone) (void)hipEventDestroy(c->ev_kdone);
     if (c->ev_kperm) (void)hipEventDestroy(c->ev_kperm);
-    if (c->ev_vdone) (void)hipEventDestroy(c->ev_vdone);
-    if (c->ev_vperm) (void)hipEventDestroy(c->ev_vperm);
     if (c->side) (void)hipStreamDestroy(c->side);
     if (c->h_fit) (void)hipHostFree(c->h_fit);
     if (c->h_mkp) (void)hipHostFree(c->h_mkp);
@@ -627,15 +620,8 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
     c->q_src = q16;           // the sparse stage gathers query rows through the permutation
-    // V into group-major order on the side stream, overlapping the routing below; the
-    // side stream starts after all work enqueued so far on st (the previous call's readers
-    // of the permuted V included), and the sparse stage waits for ev_vperm
-    SPR_HIP(c, hipEventRecord(c->ev_vdone, st));
-    SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_vdone, 0));
-    launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, c->side);
-    SPR_LAUNCHED(c, "permute V");
-    SPR_HIP(c, hipEventRecord(c->ev_vperm, c->side));
-    c->vperm_recorded = true;
+    launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
+    SPR_LAUNCHED(c, "permute");
     launch_fill_i64(c->pairs, 0, c->H, st);
     launch_route(c->qraw, c->kraw, c->kraw_t, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k,
                  c->blocks, c->ucount, c->pairs, st);
@@ -662,7 +648,6 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     // previous call's side work, which reads the probe buffers written here.
     SPR_HIP(c, hipStreamWaitEvent(st, c->ev_probe, 0));
     SPR_HIP(c, hipStreamWaitEvent(st, c->ev_kperm, 0));        // K permuted (side stream)
-    SPR_HIP(c, hipStreamWaitEvent(st, c->ev_vperm, 0));        // V permuted (side stream)
     if (c->P > 0) {
         launch_probe(c->q_src, c->kp, c->vp, c->H, c->N, c->d, c->probe_orig, c->probe_grp, c->P,
                      c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->splits, c->part_ml,
@@ -776,9 +761,8 @@ int32_t sparsepr_dense_attn(sparsepr_ctx* c, const void* q, const void* k, const
         return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned argument");
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
-    // the side stream's permutes may still read the bf16 copies rewritten here
+    // the side stream's K permute may still read the bf16 copy of k rewritten here
     if (c->kperm_recorded) SPR_HIP(c, hipStreamWaitEvent(st, c->ev_kperm, 0));
-    if (c->vperm_recorded) SPR_HIP(c, hipStreamWaitEvent(st, c->ev_vperm, 0));
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);

@@ -137,10 +137,9 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
  * permute before it rewrites the context's bf16 copy of an fp32 k). */
 int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void* stream);
 
-/* 2C/2B. Reads v (k is only checked). Stable group-major permutation of V (on the
- * context's side stream, overlapping the routing, so v must stay unchanged until
- * sparsepr_sparse_attn has run), top-k key groups per query group (ties to the lower
- * group index, empty key groups never kept), probe rows.
+/* 2C/2B. Reads v (k is only checked). Stable group-major permutation of V, top-k key
+ * groups per query group (ties to the lower group index, empty key groups never kept),
+ * probe rows.
  * Q is not copied: sparsepr_sparse_attn gathers its rows through the query permutation,
  * so q must stay unchanged until sparsepr_sparse_attn has run (for an fp32 context the
  * rows come from the context's bf16 copy of q, which sparsepr_dense_attn also rewrites:
