@@ -126,6 +126,31 @@ def test_c1_deterministic(spr, c1_run):
         assert np.array_equal(g[key], g2[key]), key
 
 
+def test_c1_dense_between_partition_and_route(spr, c1_run):
+    """An fp32 context's dense entry point rewrites the bf16 copies of its inputs; called
+    between the partition and the route stage it must wait for the partition's K permute
+    (side stream), so the call's results stay bit-identical to the plain sequence."""
+    import torch
+    cfg, (q, k, v), g, _ = c1_run
+    say("C1 dense call between partition and route (fp32 context)")
+    q2, k2, v2 = _random_qkv(1, cfg.n, cfg.d, seed=7)
+    ctx = spr.SparsePR.from_settings(1, cfg.n, cfg.d, spr.F32, cfg.settings)
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    od = torch.empty_like(qd)
+    ctx.sparsepr_partition(qd, kd)
+    o_dense = from_dev(ctx.sparsepr_dense_attn(to_dev(q2, "f32"), to_dev(k2, "f32"),
+                                               to_dev(v2, "f32")))
+    ctx.sparsepr_route(qd, kd, vd)
+    ctx.sparsepr_sparse_attn()
+    ctx.sparsepr_probe_fit()
+    ctx.sparsepr_correct(od)
+    torch.cuda.synchronize()
+    assert np.array_equal(ctx.sparsepr_get_sparse_out().astype(np.float64), g["o_sparse"])
+    assert np.array_equal(from_dev(od), g["o"])
+    check_close(o_dense[0], orc.dense_attention(q2[0], k2[0], v2[0]), "dense in between",
+                out_rel=2.0 ** -24)
+
+
 # ---------------------------------------------------------------- invariants ---
 def _c1_variant(spr, **over):
     cfg = get_config("C1")
