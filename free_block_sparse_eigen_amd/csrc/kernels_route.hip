@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
                                                int64_t* __restrict__ pairs) {
     constexpr int QG = kRouteGroups;
     __shared__ double cs[QG][128];
-    __shared__ double sc[QG][kMaxGroups];
+    static_assert(QG % 2 == 0, "logits are read in pairs");
+    __shared__ __align__(16) double sc[kMaxGroups][QG];     // a key group's logits side by side
     __shared__ int ne[kMaxGroups];
     __shared__ int wcnt[QG][4];
     __shared__ long long wsz[QG][4];
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
             for (int q = 0; q < QG; ++q) s[q] += cs[q][t] * cv;
         }
 #pragma unroll
-        for (int q = 0; q < QG; ++q) sc[q][j] = s[q] / rs;
+        for (int q = 0; q < QG; ++q) sc[j][q] = s[q] / rs;
         ne[j] = (ko[j + 1] > ko[j]) ? 1 : 0;
     }
     __syncthreads();
@@ -125,15 +126,16 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
             int rank[QG];
 #pragma unroll
             for (int q = 0; q < QG; ++q) {
-                sj[q] = sc[q][j];
+                sj[q] = sc[j][q];
                 rank[q] = 0;
             }
             for (int t = 0; t < gk; ++t) {
                 if (!ne[t]) continue;
 #pragma unroll
-                for (int q = 0; q < QG; ++q) {
-                    const double st = sc[q][t];
-                    rank[q] += (st > sj[q] || (st == sj[q] && t < j)) ? 1 : 0;
+                for (int q = 0; q < QG; q += 2) {
+                    const double2 st = *reinterpret_cast<const double2*>(&sc[t][q]);
+                    rank[q] += (st.x > sj[q] || (st.x == sj[q] && t < j)) ? 1 : 0;
+                    rank[q + 1] += (st.y > sj[q + 1] || (st.y == sj[q + 1] && t < j)) ? 1 : 0;
                 }
             }
 #pragma unroll
