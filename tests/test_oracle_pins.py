@@ -217,10 +217,18 @@ def test_group_major_is_stable_permutation_and_round_trips():
     for g in range(9):
         seg = perm[off[g]:off[g + 1]]
         assert np.all(lab[seg] == g) and np.all(np.diff(seg) > 0)
+    # permute: row i of the group-major copy is token perm[i]; unpermute with an inverse
+    # built by an explicit loop (inv[perm[i]] = i), independent of numpy fancy assignment
     x = rng.standard_normal((500, 3))
-    back = np.empty_like(x)
-    back[perm] = x[perm]
+    xp = x[perm]
+    inv = [0] * 500
+    for i, old in enumerate(perm.tolist()):
+        inv[old] = i
+    assert sorted(inv) == list(range(500))
+    back = np.array([xp[inv[t]] for t in range(500)])
     assert np.array_equal(back, x)
+    for i in (0, 17, 499):                              # the layout definition, row by row
+        assert np.array_equal(xp[i], x[perm[i]]) and lab[perm[i]] == np.searchsorted(off, i, "right") - 1
 
 
 # ----------------------------------------------------------------- routing ---
@@ -400,6 +408,128 @@ def test_probe_fit_single_probe():
     b_mat, b_vec = orc.probe_fit(x, y, 1e-3, 2)
     assert np.all(b_mat == 0) and np.allclose(b_vec, y[0], atol=1e-14)
 
+
+
+# ------------------------------------------------------ fit composition pins ---
+def _planted_residual(seed, p=60, d=10, r=3):
+    """Y = b* + X B* with B* = B0 V V^T and b* in span(V): a residual that is exactly
+    affine in X and lies in the r-dimensional subspace span(V)."""
+    rng = np.random.default_rng(seed)
+    v, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    b_star = rng.standard_normal((d, d)) @ v @ v.T
+    b_vec = rng.standard_normal(r) @ v.T
+    x = rng.standard_normal((p, d))
+    return x, b_vec + x @ b_star, b_star, b_vec, v
+
+
+def test_probe_fit_recovers_planted_residual_map():
+    """[PR 2B] With Y = b* + X B*, B* = B0 V V^T, b* in span(V), lambda -> 0 and rank
+    r = rank(V), the residual subspace is span(V) and the fit must return (B*, b*).
+    A projector applied on the wrong side (Pi B) or a transposed map fails here."""
+    x, y, b_star, b_vec, v = _planted_residual(40)
+    for lam in (0.0, 1e-13):
+        bm, bv = orc.probe_fit(x, y, lam, 3)
+        assert np.allclose(bm, b_star, atol=1e-9) and np.allclose(bv, b_vec, atol=1e-9)
+    pi = v @ v.T                                   # the wrong compositions differ here
+    assert np.abs(pi @ b_star - b_star).max() > 0.1
+    assert np.abs(b_star.T - b_star).max() > 0.1
+
+
+def test_probe_fit_map_lies_in_the_residual_subspace():
+    """[PR 2B, subspace restriction] B' and b' have no component outside the leading
+    right singular subspace of the residuals. That subspace is found here by orthogonal
+    iteration on Y^T Y, not by the SVD the oracle uses; a dropped projector fails."""
+    rng = np.random.default_rng(42)
+    p, d, r = 50, 8, 2
+    x = rng.standard_normal((p, d))
+    y = (rng.standard_normal((p, r)) * [5.0, 3.0]) @ np.linalg.qr(rng.standard_normal((d, r)))[0].T
+    y += 0.1 * rng.standard_normal((p, d))
+    bm, bv = orc.probe_fit(x, y, 1e-3, r)
+    g = y.T @ y
+    basis = np.linalg.qr(rng.standard_normal((d, r)))[0]
+    for _ in range(400):
+        basis = np.linalg.qr(g @ basis)[0]
+    pi = basis @ basis.T
+    assert np.abs(bm - bm @ pi).max() < 1e-9 and np.abs(bv - bv @ pi).max() < 1e-9
+    b_raw, v_raw = orc.ridge_affine(x, y, 1e-3)    # without the projection: outside it
+    assert np.abs(b_raw - b_raw @ pi).max() > 1e-3
+
+
+def test_correct_applies_the_map_on_the_right_row_by_row():
+    """[PR 2B, correction] An unprobed row gets O_s[q] + b' + O_s[q] B' (the row vector
+    times B', as in R ~ b + x B); a probe row gets its exact dense value. Explicit loops."""
+    rng = np.random.default_rng(41)
+    n, d = 9, 4
+    o = rng.standard_normal((n, d))
+    bm, bv = rng.standard_normal((d, d)), rng.standard_normal(d)
+    probes, od = [2, 7], rng.standard_normal((2, d))
+    out = orc.correct(o, np.array(probes), od, bm, bv)
+    for i in range(n):
+        for c in range(d):
+            if i in probes:
+                ref = od[probes.index(i)][c]
+            else:
+                ref = o[i][c] + bv[c] + sum(o[i][j] * bm[j][c] for j in range(d))
+            assert abs(out[i][c] - ref) < 1e-12
+
+
+def test_call_residuals_are_dense_minus_sparse_at_the_probes():
+    """[PR 2B] The fit's inputs: X is the routed (sparse) output at the probe rows and
+    Y = O_dense - X there, with O_dense the plain dense attention of those queries over all
+    keys in token order (independent of the group-major layout)."""
+    cfg = get_config("C1")
+    q, k, v = make_inputs(cfg)
+    st = cfg.settings
+    r = orc.oracle_head(q[0], k[0], v[0], n_sample=st.n_sample, key_rank=st.key_rank,
+                        kv_groups=st.kv_groups, q_groups=st.q_groups,
+                        kmeans_iters=st.kmeans_iters, density=st.density, probes=st.probes,
+                        ridge_lambda=st.ridge_lambda, corr_rank=st.corr_rank)
+    dense = orc.dense_attention(q[0][r.probe_orig], k[0], v[0])
+    assert np.allclose(r.x + r.y, dense, atol=1e-12)
+    assert np.array_equal(r.x, r.o_sparse[r.probe_pos])
+    assert np.array_equal(r.q_perm[r.probe_pos], r.probe_orig)
+
+
+# ------------------------------------------------- partition composition pin ---
+def _brute_partition(q, k, ms, rk, gk, gq, iters):
+    """[PR 2A] recomputed with loops: M_K from the Weyl sample, W from numpy's eigh (a library
+    step), pure-Python Lloyd on K W, raw key-group means, logit profiles against those raw
+    means, pure-Python Lloyd on the profiles."""
+    n, d = len(q), len(q[0])
+    idx = orc.weyl_indices(n, ms).tolist()
+    m = [[sum(q[s][i] * q[s][j] for s in idx) / ms for j in range(d)] for i in range(d)]
+    lam, u = np.linalg.eigh(np.array(m))
+    order = np.argsort(-lam, kind="stable")[:rk]
+    w = [[u[c][e] * math.sqrt(max(lam[e], 0.0)) for e in order] for c in range(d)]
+    z = [[sum(k[t][c] * w[c][j] for c in range(d)) for j in range(rk)] for t in range(n)]
+    klab = brute.lloyd(z, orc.weyl_indices(n, gk).tolist(), iters)
+    ck = []
+    for g in range(gk):
+        mem = [k[t] for t in range(n) if klab[t] == g]
+        ck.append([sum(r[c] for r in mem) / len(mem) for c in range(d)] if mem else [0.0] * d)
+    prof = [[sum(q[t][c] * ck[g][c] for c in range(d)) / math.sqrt(d) for g in range(gk)]
+            for t in range(n)]
+    qlab = brute.lloyd(prof, orc.weyl_indices(n, gq).tolist(), iters)
+    return klab, qlab, z, w
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_partition_is_the_brute_force_composition(seed):
+    rng = np.random.default_rng(500 + seed)
+    n, d, ms, rk, gk, gq = 48, 6, 12, 2, 5, 4
+    q = rng.standard_normal((n, d)).round(2)                       # diffuse queries
+    k = (rng.standard_normal((6, d))[rng.integers(0, 6, size=n)] * 2
+         + 0.5 * rng.standard_normal((n, d))).round(2)               # clustered keys
+    part = orc.partition(q, k, ms, rk, gk, gq, 3)
+    klab, qlab, z, w = _brute_partition(_tolist(q), _tolist(k), ms, rk, gk, gq, 3)
+    assert part.key_labels.tolist() == klab
+    assert part.q_labels.tolist() == qlab
+    # profiles of the projected queries against the projected key centroids, instead of the
+    # raw ones, give other query labels on these inputs (the pin separates the two)
+    zc = np.array([np.mean(np.array(z)[np.array(klab) == g], axis=0) for g in range(gk)])
+    wrong = (q @ np.array(w)) @ zc.T / math.sqrt(d)
+    lab_wrong = brute.lloyd(_tolist(wrong), orc.weyl_indices(n, gq).tolist(), 3)
+    assert lab_wrong != qlab
 
 # -------------------------------------------------------------- full call ---
 def _c1(**kw):
