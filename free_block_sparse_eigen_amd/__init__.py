@@ -11,7 +11,6 @@ this package when it is missing raises immediately (there is no fallback path).
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional
 
@@ -23,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libsparsepr.so")
 BF16, F32 = 0, 1
 F_STAGE_TIMING = 1
 F_RAW_KMEANS = 2      # comparison partitioner: independent Euclidean k-means of raw Q and K
+F_CHECK_FINITE = 4    # count non-finite inputs and outputs on the device (sparsepr_get_stats)
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "out of memory",
           4: "HIP error", 5: "stage order", 6: "numerical failure"}
@@ -33,8 +33,9 @@ EXPORTS = [
     "sparsepr_sparse_attn", "sparsepr_probe_fit", "sparsepr_correct", "sparsepr_attention",
     "sparsepr_dense_attn", "sparsepr_get_partition", "sparsepr_get_routing",
     "sparsepr_get_centroids", "sparsepr_get_sparse_out", "sparsepr_get_probes",
-    "sparsepr_get_fit", "sparsepr_get_stats", "sparsepr_set_partition",
-    "sparsepr_host_sym_eig_top", "sparsepr_host_key_projection", "sparsepr_host_query_factor",
+    "sparsepr_get_fit", "sparsepr_get_stats", "sparsepr_set_partition", "sparsepr_routed_count",
+    "sparsepr_get_gaps",
+    "sparsepr_host_sym_eig_top", "sparsepr_host_key_projection",
     "sparsepr_host_probe_fit",
 ]
 
@@ -59,7 +60,9 @@ class Stats(ctypes.Structure):
     _fields_ = [("routed_pairs", ctypes.c_int64), ("probe_pairs", ctypes.c_int64),
                 ("exec_density", ctypes.c_double), ("recheck_points", ctypes.c_int64),
                 ("routed_k", ctypes.c_int32), ("query_dims", ctypes.c_int32),
-                ("stage_ms", ctypes.c_float * 6), ("timed_calls", ctypes.c_int32)]
+                ("stage_ms", ctypes.c_float * 6), ("timed_calls", ctypes.c_int32),
+                ("nonfinite_inputs", ctypes.c_int64), ("nonfinite_outputs", ctypes.c_int64),
+                ("metric_gap_min", ctypes.c_double), ("resid_gap_min", ctypes.c_double)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -96,9 +99,10 @@ _sigs = {
     "sparsepr_get_fit": (_I, [_ctx, _P, _P, _I, _P]),
     "sparsepr_get_stats": (_I, [_ctx, ctypes.POINTER(Stats)]),
     "sparsepr_set_partition": (_I, [_ctx, _P, _P, _P, _P, _I, _P]),
+    "sparsepr_routed_count": (_I, [ctypes.POINTER(Params)]),
+    "sparsepr_get_gaps": (_I, [_ctx, _P, _P, _I, _P]),
     "sparsepr_host_sym_eig_top": (_I, [_I, _P, _I, _P, _P]),
     "sparsepr_host_key_projection": (_I, [_I, _P, _I, _P]),
-    "sparsepr_host_query_factor": (_I, [_I, _I, _P, _P, ctypes.POINTER(_I)]),
     "sparsepr_host_probe_fit": (_I, [_I, _I, _P, _P, ctypes.c_double, _I, _P, _P]),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -136,6 +140,13 @@ def sparsepr_workspace_bytes(p: Params) -> int:
     return lib.sparsepr_workspace_bytes(ctypes.byref(p))
 
 
+def sparsepr_routed_count(p: Params) -> int:
+    k = lib.sparsepr_routed_count(ctypes.byref(p))
+    if k < 0:
+        raise SparsePRError(-k, "invalid parameters")
+    return k
+
+
 def sparsepr_host_sym_eig_top(a: np.ndarray, r: int):
     a = np.ascontiguousarray(a, np.float64)
     n = a.shape[0]
@@ -150,15 +161,6 @@ def sparsepr_host_key_projection(m_k: np.ndarray, r: int) -> np.ndarray:
     w = np.zeros((m_k.shape[0], r))
     _check(lib.sparsepr_host_key_projection(m_k.shape[0], _np_ptr(m_k), r, _np_ptr(w)))
     return w
-
-
-def sparsepr_host_query_factor(c: np.ndarray) -> np.ndarray:
-    c = np.ascontiguousarray(c, np.float64)
-    g, d = c.shape
-    l = np.zeros((d, max(g, d)))
-    dims = ctypes.c_int32(0)
-    _check(lib.sparsepr_host_query_factor(d, g, _np_ptr(c), _np_ptr(l), ctypes.byref(dims)))
-    return l.reshape(-1)[: d * dims.value].reshape(d, dims.value)
 
 
 def sparsepr_host_probe_fit(x: np.ndarray, y: np.ndarray, lam: float, rank: int):
@@ -192,7 +194,7 @@ class SparsePR:
         self.params = params
         self._ctx = _ctx()
         _check(lib.sparsepr_create(ctypes.byref(params), ctypes.byref(self._ctx)))
-        self.k = min(max(math.ceil(params.density * params.kv_groups - 1e-9), 1), params.kv_groups)
+        self.k = sparsepr_routed_count(params)
 
     @classmethod
     def from_settings(cls, heads: int, n: int, d: int, dtype: int, settings, flags: int = 0,
@@ -304,10 +306,18 @@ class SparsePR:
         self._c(lib.sparsepr_get_fit(self._ctx, _np_ptr(bm), _np_ptr(bv), 1, _stream_ptr(stream)))
         return bm, bv
 
+    def sparsepr_get_gaps(self, stream=None):
+        h = self.params.heads
+        mg, rg = np.empty(h), np.empty(h)
+        self._c(lib.sparsepr_get_gaps(self._ctx, _np_ptr(mg), _np_ptr(rg), 1, _stream_ptr(stream)))
+        return mg, rg
+
     def sparsepr_get_stats(self) -> dict:
         s = Stats()
         self._c(lib.sparsepr_get_stats(self._ctx, ctypes.byref(s)))
         return {"routed_pairs": s.routed_pairs, "probe_pairs": s.probe_pairs,
                 "exec_density": s.exec_density, "recheck_points": s.recheck_points,
                 "routed_k": s.routed_k, "query_dims": s.query_dims,
-                "stage_ms": list(s.stage_ms), "timed_calls": s.timed_calls}
+                "stage_ms": list(s.stage_ms), "timed_calls": s.timed_calls,
+                "nonfinite_inputs": s.nonfinite_inputs, "nonfinite_outputs": s.nonfinite_outputs,
+                "metric_gap_min": s.metric_gap_min, "resid_gap_min": s.resid_gap_min}

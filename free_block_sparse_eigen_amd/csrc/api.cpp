@@ -98,8 +98,12 @@ struct sparsepr_ctx {
     size_t arena_bytes = 0;
     // bf16 copies of fp32 inputs, and the group-major K/V
     bf16_t *qb = nullptr, *kb = nullptr, *vb = nullptr;
-    bf16_t *kp = nullptr, *vp = nullptr;          // K, V in group-major order
+    bf16_t* kp = nullptr;                         // K in group-major order
+    uint16_t* vp = nullptr;                       // V in group-major order, fp16 scaled per head
+    uint32_t* vmax = nullptr;                     // [H] largest |v| per head (bf16 magnitude bits)
+    unsigned long long* nonfinite = nullptr;      // [2] non-finite inputs, outputs (CHECK_FINITE)
     const bf16_t* q_src = nullptr;                // Q in token order (the route stage's input)
+    const bf16_t* v_src = nullptr;                // V in token order (the probe rows gather it)
     // partition
     int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
     int32_t *koff = nullptr, *qoff = nullptr;
@@ -128,6 +132,7 @@ struct sparsepr_ctx {
 
     // host mirrors
     std::vector<double> h_bm, h_bv;
+    std::vector<double> h_mgap, h_rgap;          // per-head spectral gaps of the last call
     std::vector<float> h_x, h_y;
     // pinned host buffers of the fit: Grams in (device -> host), B' and b' out
     double* h_fit = nullptr;          // [H][2][d] means, then [H][3][d][d] Grams
@@ -146,6 +151,7 @@ struct sparsepr_ctx {
     std::string err;
     hipStream_t last_stream = nullptr;
     bool timing = false;
+    bool check_finite = false;
     static constexpr int kRing = 64;   // per-call stage events kept for averaging
     hipEvent_t ev[kRing][8] = {};
     bool ev_used[kRing][8] = {};
@@ -173,6 +179,8 @@ int routed_count(double density, int gk) {
 int32_t validate(const sparsepr_params* p) {
     if (!p) return SPARSEPR_ERR_INVALID_ARG;
     if (p->heads < 1 || p->n < 1 || p->n > (1 << 24)) return SPARSEPR_ERR_SHAPE;
+    if ((p->d == 64 || p->d == 128) && (int64_t)p->n * p->d * 2 >= ((int64_t)1 << 31))
+        return SPARSEPR_ERR_SHAPE;                  // one head's rows past 32-bit buffer offsets
     if ((int64_t)p->heads * p->n > 0x7fffffffLL) return SPARSEPR_ERR_SHAPE;
     if (p->d != 64 && p->d != 128) return SPARSEPR_ERR_SHAPE;
     if (p->dtype != SPARSEPR_BF16 && p->dtype != SPARSEPR_F32) return SPARSEPR_ERR_INVALID_ARG;
@@ -186,7 +194,8 @@ int32_t validate(const sparsepr_params* p) {
     if (p->corr_rank < 0 || p->corr_rank > p->d) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
-    if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS)) return SPARSEPR_ERR_INVALID_ARG;
+    if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE))
+        return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
 }
 
@@ -233,6 +242,8 @@ void layout(sparsepr_ctx& c, Arena& a) {
     }
     a.take(c.kp, HND);
     a.take(c.vp, HND);
+    a.take(c.vmax, H);
+    a.take(c.nonfinite, 2);
     a.take(c.klab, HN);
     a.take(c.qlab, HN);
     a.take(c.kperm, HN);
@@ -378,6 +389,11 @@ extern "C" {
 
 int32_t sparsepr_validate(const sparsepr_params* p) { return validate(p); }
 
+int32_t sparsepr_routed_count(const sparsepr_params* p) {
+    const int32_t v = validate(p);
+    return v != SPARSEPR_OK ? -v : routed_count(p->density, p->kv_groups);
+}
+
 size_t sparsepr_workspace_bytes(const sparsepr_params* p) {
     if (validate(p) != SPARSEPR_OK) return 0;
     sparsepr_ctx c;
@@ -422,6 +438,9 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
     c->p = *p;
     derive(*c);
     c->timing = (p->flags & SPARSEPR_F_STAGE_TIMING) != 0;
+    c->check_finite = (p->flags & SPARSEPR_F_CHECK_FINITE) != 0;
+    c->h_mgap.assign(p->heads, 0.0);
+    c->h_rgap.assign(p->heads, INFINITY);
     hipError_t e;
     if ((e = hipGetDevice(&c->device)) != hipSuccess) {
         delete c;
@@ -528,7 +547,14 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * H, st);
+    if (c->check_finite) {
+        launch_fill_i64(reinterpret_cast<int64_t*>(c->nonfinite), 0, 2, st);
+        launch_count_nonfinite(q16, H * c->N * d, 0, c->nonfinite, st);
+        launch_count_nonfinite(k16, H * c->N * d, 0, c->nonfinite, st);
+        SPR_LAUNCHED(c, "finite check (q, k)");
+    }
     if (c->raw) {
+        std::fill(c->h_mgap.begin(), c->h_mgap.end(), 0.0);      // no M_K
         // comparison partitioner: plain Euclidean k-means of the raw key rows, then of the
         // raw query rows (full-metric path with M = I: screening vector = mean)
         rc = lloyd(c, k16, 0, c->ident, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
@@ -551,7 +577,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     std::vector<int> prc(H, 0);
     parallel_heads(c, (int)H, [&](int h) {
         std::fill(c->h_wp + h * d * rK, c->h_wp + (h + 1) * d * rK, 0.0);
-        prc[h] = key_projection((int)d, c->h_mkp + h * d * d, (int)rK, c->h_wp + h * d * rK);
+        prc[h] = key_projection((int)d, c->h_mkp + h * d * d, (int)rK, c->h_wp + h * d * rK, &c->h_mgap[h]);
     });
     for (size_t h = 0; h < H; ++h) {
         if (prc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "metric eigensolve failed (non-finite input)");
@@ -620,7 +646,12 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
     c->q_src = q16;           // the sparse stage gathers query rows through the permutation
-    launch_permute(v16, c->kperm, c->H, c->N, c->d, c->vp, st);
+    c->v_src = v16;           // and the probe rows gather bf16 V rows through the key permutation
+    if (c->check_finite) {
+        launch_count_nonfinite(v16, (size_t)c->H * c->N * c->d, 0, c->nonfinite, st);
+        SPR_LAUNCHED(c, "finite check (v)");
+    }
+    launch_permute_v16(v16, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, st);
     SPR_LAUNCHED(c, "permute");
     launch_fill_i64(c->pairs, 0, c->H, st);
     launch_route(c->qraw, c->kraw, c->kraw_t, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k,
@@ -649,7 +680,7 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     SPR_HIP(c, hipStreamWaitEvent(st, c->ev_probe, 0));
     SPR_HIP(c, hipStreamWaitEvent(st, c->ev_kperm, 0));        // K permuted (side stream)
     if (c->P > 0) {
-        launch_probe(c->q_src, c->kp, c->vp, c->H, c->N, c->d, c->probe_orig, c->probe_grp, c->P,
+        launch_probe(c->q_src, c->kp, c->v_src, c->kperm, c->H, c->N, c->d, c->probe_orig, c->probe_grp, c->P,
                      c->koff, c->Gk + 1, c->Gk, c->blocks, c->Gq, c->k, c->splits, c->part_ml,
                      c->part_od, c->part_os, st);
         launch_probe_merge(c->H, c->P, c->d, c->splits, c->part_ml, c->part_od, c->part_os, c->px,
@@ -677,7 +708,7 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
         SPR_HIP(c, hipEventRecord(c->ev_probe, st));
     }
     mark(c, 4, st);
-    launch_vbsa(c->q_src, c->qperm, c->kp, c->vp, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
+    launch_vbsa(c->q_src, c->qperm, c->kp, c->vp, c->vmax, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
                 c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, kSparseRows,
                 c->o_s, 0, st);
     SPR_LAUNCHED(c, "sparse attention");
@@ -694,6 +725,7 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
     const size_t H = c->H, d = c->d, P = c->P;
     c->h_bm.assign(H * d * d, 0.0);
     c->h_bv.assign(H * d, 0.0);
+    c->h_rgap.assign(H, INFINITY);
     // waits for the probe rows and Grams only: the main kernel keeps running
     SPR_HIP(c, hipEventSynchronize(c->ev_probe));
     if (P > 0) {
@@ -704,7 +736,7 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* c, void* stream) {
             frc[h] = probe_fit_from_grams((int)P, (int)d, &hm[h * d], &hm[(H + h) * d], &hg[h * d * d],
                                           &hg[(H + h) * d * d], &hg[(2 * H + h) * d * d],
                                           c->p.ridge_lambda, c->p.corr_rank, &c->h_bm[h * d * d],
-                                          &c->h_bv[h * d]);
+                                          &c->h_bv[h * d], &c->h_rgap[h]);
         });
         for (size_t h = 0; h < H; ++h)
             if (frc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "probe fit failed (non-finite probe outputs)");
@@ -738,6 +770,11 @@ int32_t sparsepr_correct(sparsepr_ctx* c, void* o, void* stream) {
     launch_correct(c->o_s, c->bt16, c->bv32, c->pod, c->probe_orig, c->qperm, c->H, c->N, c->d, c->P, o,
                    c->p.dtype == SPARSEPR_F32 ? 1 : 0, st);
     SPR_LAUNCHED(c, "correct");
+    if (c->check_finite) {
+        launch_count_nonfinite(o, (size_t)c->H * c->N * c->d, c->p.dtype == SPARSEPR_F32 ? 1 : 0,
+                               c->nonfinite + 1, st);
+        SPR_LAUNCHED(c, "finite check (o)");
+    }
     mark(c, 7, st);
     c->stage = kStageCorrect;
     return SPARSEPR_OK;
@@ -766,7 +803,7 @@ int32_t sparsepr_dense_attn(sparsepr_ctx* c, const void* q, const void* k, const
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     const bf16_t* v16 = as_bf16(c, v, c->vb, st);
-    launch_vbsa(q16, nullptr, k16, v16, c->H, c->N, c->d, c->dense_meta, 0, c->dense_meta + 2, 0,
+    launch_vbsa(q16, nullptr, k16, v16, nullptr, c->H, c->N, c->d, c->dense_meta, 0, c->dense_meta + 2, 0,
                 c->dense_meta + 4, 0, 1, c->dense_unit_list, 0, c->dense_meta + 6, 0, c->dense_units,
                 kDenseRows, o, c->p.dtype == SPARSEPR_F32 ? 0 : 1, st);
     SPR_LAUNCHED(c, "dense attention");
@@ -860,6 +897,20 @@ int32_t sparsepr_get_fit(sparsepr_ctx* c, double* b_mat, double* b_vec, int32_t 
     return SPARSEPR_OK;
 }
 
+int32_t sparsepr_get_gaps(sparsepr_ctx* c, double* metric_gap, double* resid_gap, int32_t host,
+                          void* stream) {
+    int32_t rc = enter(c, kStagePartition);
+    if (rc) return rc;
+    if (!host) return fail(c, SPARSEPR_ERR_INVALID_ARG, "sparsepr_get_gaps writes host memory only");
+    SPR_HIP(c, hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+    if (metric_gap) std::copy(c->h_mgap.begin(), c->h_mgap.end(), metric_gap);
+    if (resid_gap) {
+        if (c->stage >= kStageFit) std::copy(c->h_rgap.begin(), c->h_rgap.end(), resid_gap);
+        else std::fill(resid_gap, resid_gap + c->H, INFINITY);
+    }
+    return SPARSEPR_OK;
+}
+
 int32_t sparsepr_get_stats(sparsepr_ctx* c, sparsepr_stats* out) {
     if (!c || !out) return SPARSEPR_ERR_INVALID_ARG;
     int32_t rc = enter(c, 0);
@@ -876,6 +927,18 @@ int32_t sparsepr_get_stats(sparsepr_ctx* c, sparsepr_stats* out) {
         out->exec_density = (double)(out->routed_pairs + out->probe_pairs) /
                             ((double)c->H * (double)c->N * (double)c->N);
     }
+    if (c->check_finite && c->stage >= kStagePartition) {
+        unsigned long long nf[2] = {0, 0};
+        SPR_HIP(c, hipMemcpy(nf, c->nonfinite, sizeof(nf), hipMemcpyDeviceToHost));
+        out->nonfinite_inputs = (int64_t)nf[0];
+        out->nonfinite_outputs = (int64_t)nf[1];
+    }
+    out->metric_gap_min = INFINITY;
+    out->resid_gap_min = INFINITY;
+    if (c->stage >= kStagePartition)
+        for (double g : c->h_mgap) out->metric_gap_min = std::min(out->metric_gap_min, g);
+    if (c->stage >= kStageFit)
+        for (double g : c->h_rgap) out->resid_gap_min = std::min(out->resid_gap_min, g);
     if (c->stage >= kStagePartition) {
         std::vector<int32_t> fl(2 * (size_t)c->T * c->H);
         SPR_HIP(c, hipMemcpy(fl.data(), c->flag_cnt, 4 * fl.size(), hipMemcpyDeviceToHost));
@@ -913,15 +976,7 @@ int32_t sparsepr_host_sym_eig_top(int32_t n, const double* a, int32_t r, double*
 
 int32_t sparsepr_host_key_projection(int32_t d, const double* m_k, int32_t r, double* w) {
     if (d < 1 || d > 1024 || r < 1 || r > d || !m_k || !w) return SPARSEPR_ERR_INVALID_ARG;
-    return key_projection(d, m_k, r, w) == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
-}
-
-int32_t sparsepr_host_query_factor(int32_t d, int32_t g, const double* c, double* l, int32_t* dims) {
-    if (d < 1 || d > 1024 || g < 1 || !c || !l || !dims) return SPARSEPR_ERR_INVALID_ARG;
-    int dd = 0;
-    const int rc = query_factor(d, g, c, l, &dd);
-    *dims = dd;
-    return rc == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
+    return key_projection(d, m_k, r, w, nullptr) == 0 ? SPARSEPR_OK : SPARSEPR_ERR_NUMERIC;
 }
 
 int32_t sparsepr_host_probe_fit(int32_t p, int32_t d, const double* x, const double* y, double lambda,

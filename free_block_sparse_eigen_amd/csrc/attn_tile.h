@@ -67,6 +67,16 @@ struct Tile {
             lds_load16(rv, sv + first, off);
         }
     }
+    // rows row0 .. row0 + KT - 1 of one tensor (a contiguous tile)
+    __device__ static void issue_rows_one(rsrc_t r, int row0, uint4* s, int w, int lane) {
+#pragma unroll
+        for (int m = 0; m < PER_WAVE; ++m) {
+            const int first = (w * PER_WAVE + m) * 64;
+            const int slot = first + lane;
+            const int rr = slot / CH, pc = slot % CH;
+            lds_load16(r, s + first, ((row0 + rr) * D + ((pc ^ swz<CH>(rr)) * 8)) * 2);
+        }
+    }
     // one tensor's tile (rows phys[]) into s
     __device__ static void issue_one(rsrc_t r, const int* __restrict__ phys, uint4* s, int w,
                                      int lane) {

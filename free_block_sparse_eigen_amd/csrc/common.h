@@ -92,6 +92,57 @@ __device__ inline void lds_load16(rsrc_t r, void* s, int off) {
                                              0, 0, 0);
 }
 
+// ---- fp16 operands of the P.V products ----
+// V is stored group-major in fp16, scaled per head by an exact power of two 2^e chosen from
+// the head's largest |v| (so the scaled values sit below 2^15 and bf16 values convert
+// without rounding); P is rounded to fp16 (11 significant bits against bf16's 8).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline f32x16 mfma32x32x16_f16(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> packed fp16 pair (low half = a), round to nearest even (one instruction).
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+__device__ inline float f16_to_f32(uint32_t h16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h16)));
+}
+
+__device__ inline f16x2 ones_f16x2() { return __builtin_bit_cast(f16x2, 0x3C003C00u); }
+
+// acc + lo(packed) + hi(packed), the fp16 pair summed in fp32
+__device__ inline float dot2_f16(uint32_t packed, f16x2 ones, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
+}
+
+// Exponent e of the per-head V scale from the head's largest bf16 magnitude bits: the
+// largest scaled value lies in [2^14, 2^15). Zero, non-finite or absurdly small heads keep
+// e within [-64, 64] (0 for a zero or non-finite head).
+__host__ __device__ inline int v_scale_exp(uint32_t max_bf16_bits) {
+    const int ef = (int)((max_bf16_bits >> 7) & 0xFF);
+    if (max_bf16_bits == 0 || ef == 0xFF) return 0;
+    int lg;                                            // floor(log2(max))
+    if (ef == 0) {                                     // bf16 subnormal: 7 fraction bits
+        int top = 6;
+        while (top > 0 && !((max_bf16_bits >> top) & 1u)) --top;
+        lg = -133 + top;
+    } else {
+        lg = ef - 127;
+    }
+    const int e = 14 - lg;
+    return e < -64 ? -64 : (e > 64 ? 64 : e);
+}
+
+// P offset for fp16: the lazily raised running max lets P reach 2^8, so exp2(x + 7) stays
+// below 2^15 (fp16 max 65504) and keeps small weights 2^7 further from fp16 subnormals.
+constexpr float kP16Offset = 7.0f;
+
 template <typename T>
 __device__ inline T wave_max(T v) {
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));

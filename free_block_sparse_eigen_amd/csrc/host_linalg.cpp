@@ -301,13 +301,17 @@ int sym_eig_top(int n, const double* a, int r, double* lam, double* vec) {
 
     // eigenvectors of T by inverse iteration (one factorisation, three solves each)
     const double tiny = kEps * tnorm;
-    const double sep = std::ldexp(1.0, -28) * tnorm;  // shifts closer than this are split
+    // shifts closer than 2^-28 of the eigenvalue's own size are split apart (relative, so
+    // that eigenvalues far below |T| keep shifts of their own accuracy; the floor is the
+    // rounding level n eps |T| below which eigenvalues are not resolved)
+    const double noise = n * kEps * tnorm;
     const double cluster_tol = 1e-3 * tnorm;
     std::vector<double> ys(static_cast<size_t>(r) * n);
     ShiftedLU lu;
     double prev_shift = 0.0;
     for (int j = 0; j < r; ++j) {
         double shift = lam[j];
+        const double sep = std::ldexp(1.0, -28) * std::max(std::fabs(lam[j]), noise);
         if (j > 0 && prev_shift - shift < sep) shift = prev_shift - sep;   // keep shifts apart
         prev_shift = shift;
         lu.factor(t, shift, tiny);
@@ -374,38 +378,17 @@ int cholesky_lower(int n, const double* a, double* l) {
     return 0;
 }
 
-int key_projection(int d, const double* m_k, int r, double* w) {
-    std::vector<double> lam(r), vec(static_cast<size_t>(d) * r);
-    const int rc = sym_eig_top(d, m_k, r, lam.data(), vec.data());
+int key_projection(int d, const double* m_k, int r, double* w, double* gap) {
+    const int r1 = std::min(r + 1, d);                 // one more eigenvalue for the gap
+    std::vector<double> lam(r1), vec(static_cast<size_t>(d) * r1);
+    const int rc = sym_eig_top(d, m_k, r1, lam.data(), vec.data());
     if (rc != 0) return rc;
     for (int j = 0; j < r; ++j) {
         const double s = std::sqrt(std::max(lam[j], 0.0));
-        for (int i = 0; i < d; ++i) w[static_cast<size_t>(i) * r + j] = vec[static_cast<size_t>(i) * r + j] * s;
+        for (int i = 0; i < d; ++i) w[static_cast<size_t>(i) * r + j] = vec[static_cast<size_t>(i) * r1 + j] * s;
     }
+    if (gap) *gap = (r1 > r && lam[r] > 0.0) ? lam[r - 1] / lam[r] : INFINITY;
     return 0;
-}
-
-int query_factor_from_metric(int d, const double* m, double* l);
-
-int query_factor(int d, int g, const double* c, double* l, int* dims) {
-    for (size_t i = 0; i < static_cast<size_t>(g) * d; ++i)
-        if (!std::isfinite(c[i])) return -2;
-    if (g <= d) {                               // logit profiles directly: L = C^T / sqrt(d)
-        const double s = 1.0 / std::sqrt(static_cast<double>(d));
-        for (int i = 0; i < d; ++i)
-            for (int j = 0; j < g; ++j) l[static_cast<size_t>(i) * g + j] = c[static_cast<size_t>(j) * d + i] * s;
-        *dims = g;
-        return 0;
-    }
-    std::vector<double> m(static_cast<size_t>(d) * d, 0.0);
-    for (int i = 0; i < d; ++i)
-        for (int j = 0; j <= i; ++j) {
-            double s = 0.0;
-            for (int t = 0; t < g; ++t) s += c[static_cast<size_t>(t) * d + i] * c[static_cast<size_t>(t) * d + j];
-            m[static_cast<size_t>(i) * d + j] = m[static_cast<size_t>(j) * d + i] = s / d;
-        }
-    *dims = d;
-    return query_factor_from_metric(d, m.data(), l);
 }
 
 // Centred Grams of X, Y [p][d] (and the uncentred Y^T Y): the same quantities the
@@ -447,16 +430,19 @@ void probe_grams(int p, int d, const double* x, const double* y, double* xm, dou
 // b' = ybar Pi - xbar B'.
 int probe_fit_from_grams(int p, int d, const double* xm, const double* ym, const double* gxx_in,
                          const double* gxy, const double* gyy, double lambda, int rank,
-                         double* b_mat, double* b_vec) {
+                         double* b_mat, double* b_vec, double* sgap) {
     std::memset(b_mat, 0, sizeof(double) * d * d);
     std::memset(b_vec, 0, sizeof(double) * d);
+    if (sgap) *sgap = INFINITY;
     if (p == 0) return 0;
     for (size_t i = 0; i < static_cast<size_t>(d) * d; ++i)
         if (!std::isfinite(gxx_in[i]) || !std::isfinite(gxy[i]) || !std::isfinite(gyy[i])) return -2;
     const int rmax = std::min(rank, std::min(p, d));
     if (rmax <= 0) return 0;
-    std::vector<double> lam(rmax), vec(static_cast<size_t>(d) * rmax);
-    if (sym_eig_top(d, gyy, rmax, lam.data(), vec.data()) != 0) return -3;
+    // one eigenvalue past the kept rank for the singular gap (vec keeps rmax1 columns)
+    const int rmax1 = std::min(rmax + 1, d);
+    std::vector<double> lam(rmax1), vec(static_cast<size_t>(d) * rmax1);
+    if (sym_eig_top(d, gyy, rmax1, lam.data(), vec.data()) != 0) return -3;
     // singular values from the Gram eigenvalues; values below 2^-20 sigma_1 are not
     // resolved by the Gram route and count as zero
     const double s1 = std::sqrt(std::max(lam[0], 0.0));
@@ -466,12 +452,17 @@ int probe_fit_from_grams(int p, int d, const double* xm, const double* ym, const
         while (r < rmax && std::sqrt(std::max(lam[r], 0.0)) > thr) ++r;
     }
     if (r == 0) return 0;
+    if (sgap) {
+        const bool beyond = r < rmax1 && r < std::min(p, d);
+        const double next = beyond ? std::max(lam[r], 0.0) : 0.0;
+        *sgap = next > 0.0 ? std::sqrt(std::max(lam[r - 1], 0.0) / next) : INFINITY;
+    }
     // R = Xc^T Yc V_r  [d][r]
     std::vector<double> rhs(static_cast<size_t>(d) * r, 0.0), bv(static_cast<size_t>(d) * r, 0.0);
     for (int i = 0; i < d; ++i)
         for (int t = 0; t < d; ++t) {
             const double g = gxy[static_cast<size_t>(i) * d + t];
-            for (int e = 0; e < r; ++e) rhs[static_cast<size_t>(i) * r + e] += g * vec[static_cast<size_t>(t) * rmax + e];
+            for (int e = 0; e < r; ++e) rhs[static_cast<size_t>(i) * r + e] += g * vec[static_cast<size_t>(t) * rmax1 + e];
         }
     if (lambda > 0.0) {
         std::vector<double> gxx(gxx_in, gxx_in + static_cast<size_t>(d) * d);
@@ -523,16 +514,16 @@ int probe_fit_from_grams(int p, int d, const double* xm, const double* ym, const
         double* out = &b_mat[static_cast<size_t>(i) * d];
         for (int j = 0; j < d; ++j) {
             double s = 0.0;
-            for (int e = 0; e < r; ++e) s += bi[e] * vec[static_cast<size_t>(j) * rmax + e];
+            for (int e = 0; e < r; ++e) s += bi[e] * vec[static_cast<size_t>(j) * rmax1 + e];
             out[j] = s;
         }
     }
     std::vector<double> yv(r, 0.0);
     for (int e = 0; e < r; ++e)
-        for (int t = 0; t < d; ++t) yv[e] += ym[t] * vec[static_cast<size_t>(t) * rmax + e];
+        for (int t = 0; t < d; ++t) yv[e] += ym[t] * vec[static_cast<size_t>(t) * rmax1 + e];
     for (int j = 0; j < d; ++j) {
         double s = 0.0;
-        for (int e = 0; e < r; ++e) s += yv[e] * vec[static_cast<size_t>(j) * rmax + e];
+        for (int e = 0; e < r; ++e) s += yv[e] * vec[static_cast<size_t>(j) * rmax1 + e];
         for (int i = 0; i < d; ++i) s -= xm[i] * b_mat[static_cast<size_t>(i) * d + j];
         b_vec[j] = s;
     }
@@ -552,14 +543,7 @@ int probe_fit(int p, int d, const double* x, const double* y, double lambda, int
         gyy(static_cast<size_t>(d) * d);
     probe_grams(p, d, x, y, xm.data(), ym.data(), gxx.data(), gxy.data(), gyy.data());
     return probe_fit_from_grams(p, d, xm.data(), ym.data(), gxx.data(), gxy.data(), gyy.data(), lambda,
-                                rank, b_mat, b_vec);
-}
-
-// L [d][dims] from the metric m = C^T C / d (d x d): Cholesky if positive definite,
-// else the eigen factor U diag(sqrt(max(lambda, 0))).
-int query_factor_from_metric(int d, const double* m, double* l) {
-    if (cholesky_lower(d, m, l) == 0) return 0;
-    return key_projection(d, m, d, l);
+                                rank, b_mat, b_vec, nullptr);
 }
 
 }  // namespace spr

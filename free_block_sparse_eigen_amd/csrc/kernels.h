@@ -18,6 +18,9 @@ constexpr int kProbeRows = 256;       // probe rows per probe work unit (8 waves
 void launch_to_bf16(const float* in, bf16_t* out, size_t count, hipStream_t st);
 void launch_fill_i32(int32_t* p, int32_t value, size_t count, hipStream_t st);
 void launch_fill_i64(int64_t* p, int64_t value, size_t count, hipStream_t st);
+// adds the number of non-finite values among x[0 .. count) (bf16, or fp32 if is_f32) to *counter
+void launch_count_nonfinite(const void* x, size_t count, int is_f32, unsigned long long* counter,
+                            hipStream_t st);
 
 // ---- partition ----
 void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64_t a, double* mk,
@@ -43,6 +46,10 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,
                     hipStream_t st);
+// V into group-major fp16 scaled per head by 2^v_scale_exp(vmax[h]); vmax [heads] receives
+// each head's largest |v| as bf16 magnitude bits
+void launch_permute_v16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
+                        uint32_t* vmax, uint16_t* dst, hipStream_t st);
 // ck_t: scratch [heads][d][gk] for the coordinate-major copy of ck
 void launch_route(const double* cq, const double* ck, double* ck_t, const int32_t* qoff,
                   const int32_t* koff, int heads, int gq, int gk, int d, int k, int32_t* blocks,
@@ -57,15 +64,19 @@ void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int
 // out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index); unit_rows is
 // kSparseRows or kDenseRows (the units' row count, which fixes the block shape)
 // qp: Q in token order; qperm [heads][n] (group-major position -> token) or nullptr
-void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const bf16_t* vp,
-                 int heads, int n, int d,
+// vp: bf16 [heads][n][d] with vmax == nullptr (dense baseline), or fp16 scaled per head by
+// 2^v_scale_exp(vmax[h]) (the sparse call, 128-row units)
+void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const void* vp,
+                 const uint32_t* vmax, int heads, int n, int d,
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
                  int unit_rows, void* out, int out_mode, hipStream_t st);
 int probe_splits(int n, int heads, int probes);
-// qp: Q in token order, probe_orig: the probe rows' token indices; kp, vp group-major
-void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+// qp: Q in token order, probe_orig: the probe rows' token indices; kp group-major
+// vtok: bf16 V in token order, gathered through kperm [heads][n] (group-major -> token)
+void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vtok, const int32_t* kperm,
+                  int heads, int n, int d,
                   const int32_t* probe_orig, const int32_t* probe_grp, int probes,
                   const int32_t* koff, int koff_stride, int gk, const int32_t* blocks, int gq,
                   int kblk, int splits, float* part_ml, float* part_od, float* part_os,

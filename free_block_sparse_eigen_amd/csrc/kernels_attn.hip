@@ -65,14 +65,35 @@ __device__ inline bool unit_of_block(const int32_t* __restrict__ nunits, int str
 
 }  // namespace
 
+// P^T operand: two probabilities packed as fp16 (VH, V in scaled fp16) or bf16, and the
+// row sum of exactly the packed values
+template <bool VH>
+__device__ inline uint32_t pack_p(float a, float b) {
+    if constexpr (VH) return pack_f16x2(a, b);
+    else return pack_bf16x2(a, b);
+}
+template <bool VH>
+__device__ inline float sum_p(uint32_t w, float acc) {
+    if constexpr (VH) return dot2_f16(w, ones_f16x2(), acc);
+    else return dot2_bf16(w, ones_bf16x2(), acc);
+}
+template <bool VH>
+__device__ inline f32x16 mfma_pv(uint4 v, uint4 p, f32x16 c) {
+    if constexpr (VH) return mfma32x32x16_f16(v, p, c);
+    else return mfma32x32x16(v, p, c);
+}
+
 // Block = NW waves x 32 query rows: a unit of up to NW x 32 rows shares every key tile.
-template <int D, int OUTM, int NW>
+// VH: V is group-major fp16 scaled per head by 2^e (vmax, see v_scale_exp), and P is
+// rounded to fp16 with the 2^7 offset; otherwise V and P are bf16.
+template <int D, int OUTM, int NW, bool VH>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
     const bf16_t* __restrict__ qp, const int32_t* __restrict__ qperm, const bf16_t* __restrict__ kp,
     const bf16_t* __restrict__ vp, int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
     int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
     const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
-    int nunits_stride, int heads, float scale_log2, void* __restrict__ out) {
+    int nunits_stride, int heads, float scale_log2, const uint32_t* __restrict__ vmax,
+    void* __restrict__ out) {
     constexpr int kVbsaThreads = NW * 64;
     using TL = Tile<D, kVbsaThreads>;
     constexpr int DB = D / 32;
@@ -142,7 +163,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
-    const bf16x2 ones = ones_bf16x2();
     const int half = lane >> 5;
 
     const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
@@ -209,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
                 for (int db = 0; db < DB; ++db) o[db] *= alpha;
                 m_run = mnew;
             }
-            const float mneg = -m_run;
+            const float mneg = VH ? kP16Offset - m_run : -m_run;
             // P^T slices 0,1 (keys 0..31)
             uint4 pb[4];
 #pragma unroll
@@ -218,9 +238,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 8 * sl + 2 * i;
-                    wv[i] = pack_bf16x2(fast_exp2(fmaf(s0[r], scale_log2, mneg)),
-                                        fast_exp2(fmaf(s0[r + 1], scale_log2, mneg)));
-                    l_run = dot2_bf16(wv[i], ones, l_run);
+                    wv[i] = pack_p<VH>(fast_exp2(fmaf(s0[r], scale_log2, mneg)),
+                                       fast_exp2(fmaf(s0[r + 1], scale_log2, mneg)));
+                    l_run = sum_p<VH>(wv[i], l_run);
                 }
                 pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
@@ -230,7 +250,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    o[db] = mfma32x32x16(vf[sl][db], pb[sl], o[db]);
+                    o[db] = mfma_pv<VH>(vf[sl][db], pb[sl], o[db]);
                     vf[sl][db] = vt_frag<D>(sv, db, sl + 2, lane);
                 }
 #pragma unroll
@@ -239,16 +259,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 8 * (sl - 2) + 2 * i;
-                    wv[i] = pack_bf16x2(fast_exp2(fmaf(s1[r], scale_log2, mneg)),
-                                        fast_exp2(fmaf(s1[r + 1], scale_log2, mneg)));
-                    l_run = dot2_bf16(wv[i], ones, l_run);
+                    wv[i] = pack_p<VH>(fast_exp2(fmaf(s1[r], scale_log2, mneg)),
+                                       fast_exp2(fmaf(s1[r + 1], scale_log2, mneg)));
+                    l_run = sum_p<VH>(wv[i], l_run);
                 }
                 pb[sl] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
 #pragma unroll
             for (int sl = 2; sl < 4; ++sl)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) o[db] = mfma32x32x16(vf[sl - 2][db], pb[sl], o[db]);
+                for (int db = 0; db < DB; ++db) o[db] = mfma_pv<VH>(vf[sl - 2][db], pb[sl], o[db]);
         }
         if (t + 2 < ntiles) fill_phys(t + 2, buf);
         tile_ready();
@@ -260,7 +280,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
 
     if (!active) return;
     l_run = pair_sum(l_run);
-    const float inv = 1.0f / l_run;
+    float inv = 1.0f / l_run;
+    if constexpr (VH) inv *= ldexpf(1.0f, -v_scale_exp(vmax[h]));      // undo the V scale
     if (!qvalid) return;
     const size_t orow = head_row0 + row0 + qrow;
 #pragma unroll
@@ -280,8 +301,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
         }
 }
 
-void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const bf16_t* vp,
-                 int heads, int n, int d,
+void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const void* vp,
+                 const uint32_t* vmax, int heads, int n, int d,
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
@@ -289,21 +310,24 @@ void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     // 8 XCD slots per round of units: enough blocks for every head's units at any split
     dim3 grid(8 * ((max_units + 7) / 8), heads);
-#define SPR_VBSA(DD, MM, NW)                                                                 \
-    hipLaunchKernelGGL((k_vbsa<DD, MM, NW>), grid, dim3(NW * 64), 0, st, qp, qperm, kp, vp, n, qoff,  \
-                       qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units, \
-                       units_head_stride, nunits, nunits_stride, heads, scale_log2, out)
-    if (unit_rows == kSparseRows) {
+#define SPR_VBSA(DD, MM, NW, VH)                                                               \
+    hipLaunchKernelGGL((k_vbsa<DD, MM, NW, VH>), grid, dim3(NW * 64), 0, st, qp, qperm, kp,     \
+                       static_cast<const bf16_t*>(vp), n, qoff, qoff_stride, koff, koff_stride,  \
+                       blocks, blocks_head_stride, kblk, units, units_head_stride, nunits,       \
+                       nunits_stride, heads, scale_log2, vmax, out)
+    // the sparse call: 4-wave blocks, fp32 output, fp16 V with its per-head scale
+    // (vmax != nullptr); the dense baseline: 8-wave blocks, bf16 V
+    if (unit_rows == kSparseRows && vmax) {
         if (d == 128) {
-            if (out_mode == 0) SPR_VBSA(128, 0, 4); else SPR_VBSA(128, 1, 4);
+            if (out_mode == 0) SPR_VBSA(128, 0, 4, true); else SPR_VBSA(128, 1, 4, true);
         } else {
-            if (out_mode == 0) SPR_VBSA(64, 0, 4); else SPR_VBSA(64, 1, 4);
+            if (out_mode == 0) SPR_VBSA(64, 0, 4, true); else SPR_VBSA(64, 1, 4, true);
         }
     } else {
         if (d == 128) {
-            if (out_mode == 0) SPR_VBSA(128, 0, 8); else SPR_VBSA(128, 1, 8);
+            if (out_mode == 0) SPR_VBSA(128, 0, 8, false); else SPR_VBSA(128, 1, 8, false);
         } else {
-            if (out_mode == 0) SPR_VBSA(64, 0, 8); else SPR_VBSA(64, 1, 8);
+            if (out_mode == 0) SPR_VBSA(64, 0, 8, false); else SPR_VBSA(64, 1, 8, false);
         }
     }
 #undef SPR_VBSA

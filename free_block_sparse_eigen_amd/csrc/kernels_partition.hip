@@ -11,6 +11,7 @@
 //                centroid update and, after the last round, the group-major permutation
 #include "kernels.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace spr {
@@ -44,6 +45,30 @@ void launch_fill_i32(int32_t* p, int32_t value, size_t count, hipStream_t st) {
 }
 void launch_fill_i64(int64_t* p, int64_t value, size_t count, hipStream_t st) {
     hipLaunchKernelGGL(k_fill<int64_t>, dim3(grid_for(count, 256)), dim3(256), 0, st, p, value, count);
+}
+
+// Non-finite values of x (bf16 or fp32, `count` elements) added to *counter.
+template <typename T>
+__global__ __launch_bounds__(256) void k_count_nonfinite(const T* __restrict__ x, size_t count,
+                                                         unsigned long long* __restrict__ counter) {
+    unsigned c = 0;
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < count; i += (size_t)gridDim.x * 256) {
+        if constexpr (sizeof(T) == 2) c += ((x[i] & 0x7F80u) == 0x7F80u) ? 1u : 0u;
+        else c += ((__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u) ? 1u : 0u;
+    }
+    c = wave_sum(c);
+    if ((threadIdx.x & 63) == 0 && c) atomicAdd(counter, (unsigned long long)c);
+}
+
+void launch_count_nonfinite(const void* x, size_t count, int is_f32, unsigned long long* counter,
+                            hipStream_t st) {
+    const int grid = std::min(grid_for(count, 256), 2048);
+    if (is_f32)
+        hipLaunchKernelGGL(k_count_nonfinite<float>, dim3(grid), dim3(256), 0, st,
+                           static_cast<const float*>(x), count, counter);
+    else
+        hipLaunchKernelGGL(k_count_nonfinite<bf16_t>, dim3(grid), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(x), count, counter);
 }
 
 // ------------------------------------------------------------------- metric ---

@@ -14,7 +14,10 @@ namespace spr {
 // routed keys of a tile are whole runs of groups found from the group offsets. Both
 // accumulators share the logits: the dense one over every key, the routed one over keys
 // whose group is routed for the probe's query group. P.V uses a bf16 hi/lo split of P
-// (about 2^-17 relative) so that the probe outputs are near fp32 accuracy. Partial (max,
+// (about 2^-17 relative) so that the probe outputs are near fp32 accuracy; V is the bf16
+// input in token order, its rows gathered through the key permutation (bf16 keeps fp32's
+// exponent range, so the routed weights stay exact even when the row's largest logit lies
+// outside its routed groups and every routed weight is tiny). Partial (max,
 // sum, unnormalised O) per split. Two waves share each SIMD (one block per CU), so one
 // wave's exponentials overlap the other's matrix products.
 int probe_splits(int n, int heads, int probes) {
@@ -40,8 +43,8 @@ int probe_splits(int n, int heads, int probes) {
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void k_probe(
-    const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
-    int n, const int32_t* __restrict__ probe_orig, const int32_t* __restrict__ probe_grp,
+    const bf16_t* __restrict__ qp, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vtok,
+    const int32_t* __restrict__ kperm, int n, const int32_t* __restrict__ probe_orig, const int32_t* __restrict__ probe_grp,
     int probes, const int32_t* __restrict__ koff, int koff_stride, int gk,
     const int32_t* __restrict__ blocks, int gq, int kblk, int chunk, float scale_log2,
     float* __restrict__ part_ml, float* __restrict__ part_od, float* __restrict__ part_os) {
@@ -52,6 +55,7 @@ __global__ __launch_bounds__(512, 1) void k_probe(
     __shared__ int s_ko[kMaxGroups + 1];
     __shared__ uint4 s_k[2][TL::SLOTS];
     __shared__ uint4 s_v[2][TL::SLOTS];
+    __shared__ int s_vrow[2][KT];                 // token rows of a tile's keys (V gather)
 
     const int h = blockIdx.z, split = blockIdx.y, splits = gridDim.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
@@ -62,13 +66,22 @@ __global__ __launch_bounds__(512, 1) void k_probe(
     const int k1 = min(n, k0 + chunk);
     const int ntiles = (max(0, k1 - k0) + KT - 1) / KT;
     const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
-    const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
-    // the first tile's loads go out before the routing bits are set up; rows past the
-    // split are masked below and rows past the head read as zeros
-    if (ntiles > 0) TL::issue_rows(rk, rv, k0, s_k[0], s_v[0], w, lane);
+    const rsrc_t rv = head_rsrc(vtok + head_row0 * D, n, D);
+    // token row of group-major key position pos; positions past the head are clamped to a
+    // real row (their logits are masked below)
+    const int32_t* kpm = kperm + head_row0;
+    auto vrow = [&](int pos) { return kpm[min(pos, n - 1)]; };
+    if (tid < KT && ntiles > 0) s_vrow[0][tid] = vrow(k0 + tid);
+    if (tid >= KT && tid < 2 * KT && ntiles > 1) s_vrow[1][tid - KT] = vrow(k0 + tid);
     for (int i = tid; i < kProbeRows * BW; i += 512) (&s_bits[0][0])[i] = 0u;
     for (int g = tid; g <= gk; g += 512) s_ko[g] = ko[g];
     __syncthreads();
+    // the first tile's loads go out before the routing bits are set up; K rows past the
+    // split are masked below and rows past the head read as zeros
+    if (ntiles > 0) {
+        TL::issue_rows_one(rk, k0, s_k[0], w, lane);
+        TL::issue_one(rv, s_vrow[0], s_v[0], w, lane);
+    }
     for (int i = tid; i < kProbeRows * kblk; i += 512) {
         const int lp = i / kblk, s = i - lp * kblk;
         const int p = p0 + lp;
@@ -107,7 +120,10 @@ __global__ __launch_bounds__(512, 1) void k_probe(
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         const int base = k0 + t * KT;
-        if (t + 1 < ntiles) TL::issue_rows(rk, rv, base + KT, s_k[buf ^ 1], s_v[buf ^ 1], w, lane);
+        if (t + 1 < ntiles) {
+            TL::issue_rows_one(rk, base + KT, s_k[buf ^ 1], w, lane);
+            TL::issue_one(rv, s_vrow[buf ^ 1], s_v[buf ^ 1], w, lane);
+        }
         if (active) {
             f32x16 sv[2];
             sv[0] = qk_block<D>(s_k[buf], qf, 0, lane);
@@ -196,6 +212,8 @@ __global__ __launch_bounds__(512, 1) void k_probe(
                 }
             }
         }
+        // V rows of tile t + 2 into the row buffer that tile t's loads have finished with
+        if (t + 2 < ntiles && tid < KT) s_vrow[buf][tid] = vrow(base + 2 * KT + tid);
         tile_ready();
     }
     if (!active) return;
@@ -222,7 +240,8 @@ __global__ __launch_bounds__(512, 1) void k_probe(
         }
 }
 
-void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int heads, int n, int d,
+void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vtok, const int32_t* kperm,
+                  int heads, int n, int d,
                   const int32_t* probe_orig, const int32_t* probe_grp, int probes,
                   const int32_t* koff, int koff_stride, int gk, const int32_t* blocks, int gq,
                   int kblk, int splits, float* part_ml, float* part_od, float* part_os,
@@ -233,11 +252,11 @@ void launch_probe(const bf16_t* qp, const bf16_t* kp, const bf16_t* vp, int head
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     dim3 grid((probes + kProbeRows - 1) / kProbeRows, splits, heads);
     if (d == 128)
-        hipLaunchKernelGGL(k_probe<128>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_orig, probe_grp,
+        hipLaunchKernelGGL(k_probe<128>, grid, dim3(512), 0, st, qp, kp, vtok, kperm, n, probe_orig, probe_grp,
                            probes, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2,
                            part_ml, part_od, part_os);
     else
-        hipLaunchKernelGGL(k_probe<64>, grid, dim3(512), 0, st, qp, kp, vp, n, probe_orig, probe_grp,
+        hipLaunchKernelGGL(k_probe<64>, grid, dim3(512), 0, st, qp, kp, vtok, kperm, n, probe_orig, probe_grp,
                            probes, koff, koff_stride, gk, blocks, gq, kblk, chunk, scale_log2,
                            part_ml, part_od, part_os);
 }

@@ -7,6 +7,7 @@
 //  * units: query tiles of the attention kernel, one list per head
 #include "kernels.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace spr {
@@ -29,6 +30,60 @@ void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, in
     const size_t total = (size_t)n * (d / 8);
     hipLaunchKernelGGL(k_permute, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, st,
                        src, perm, n, d, dst);
+}
+
+// Largest |v| of each head as bf16 magnitude bits (vmax[h] must start at 0). Magnitude
+// bits order like the magnitudes, so an integer maximum suffices.
+__global__ __launch_bounds__(256) void k_absmax_bits(const bf16_t* __restrict__ src, size_t per_head,
+                                                     uint32_t* __restrict__ vmax) {
+    const int h = blockIdx.y;
+    const uint4* p = reinterpret_cast<const uint4*>(src + (size_t)h * per_head);
+    const size_t chunks = per_head / 8;
+    uint32_t m = 0;
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < chunks; i += (size_t)gridDim.x * 256) {
+        const uint4 v = p[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+    }
+    m = wave_max(m);
+    __shared__ uint32_t s_m[4];
+    if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(vmax + h, max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3])));
+}
+
+// Group-major permute of V into fp16 scaled by 2^e(head) (exact for the scaled bf16 values
+// above 2^-14; see v_scale_exp).
+__global__ __launch_bounds__(256) void k_permute_f16(const bf16_t* __restrict__ src,
+                                                     const int32_t* __restrict__ perm, int n, int d,
+                                                     const uint32_t* __restrict__ vmax,
+                                                     uint16_t* __restrict__ dst) {
+    const int h = blockIdx.y;
+    const int chunks = d / 8;
+    const size_t i = blockIdx.x * (size_t)256 + threadIdx.x;
+    if (i >= (size_t)n * chunks) return;
+    const float scale = ldexpf(1.0f, v_scale_exp(vmax[h]));
+    const int row = (int)(i / chunks), c = (int)(i % chunks);
+    const int from = perm[(size_t)h * n + row];
+    const uint4 v = *reinterpret_cast<const uint4*>(src + ((size_t)h * n + from) * d + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = pack_f16x2(bf16_to_f32((bf16_t)(w[j] & 0xFFFF)) * scale, bf16_to_f32((bf16_t)(w[j] >> 16)) * scale);
+    *reinterpret_cast<uint4*>(dst + ((size_t)h * n + row) * d + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+void launch_permute_v16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
+                        uint32_t* vmax, uint16_t* dst, hipStream_t st) {
+    launch_fill_i32(reinterpret_cast<int32_t*>(vmax), 0, heads, st);
+    const size_t per_head = (size_t)n * d;
+    const unsigned blocks = (unsigned)std::min<size_t>((per_head / 8 + 255) / 256, 256);
+    hipLaunchKernelGGL(k_absmax_bits, dim3(blocks, heads), dim3(256), 0, st, src, per_head, vmax);
+    const size_t total = (size_t)n * (d / 8);
+    hipLaunchKernelGGL(k_permute_f16, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, st,
+                       src, perm, n, d, vmax, dst);
 }
 
 // Coordinate-major copy [heads][d][g] of row-major fp64 rows [heads][g][d].

@@ -70,10 +70,16 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        rows (the independent Q/K clustering of cluster-based
                                        sparse attention), with the same seeds, rounds, routing,
                                        probes and correction; no M_K and no host round trip */
+#define SPARSEPR_F_CHECK_FINITE 4u  /* count non-finite values of q and k (partition), v (route)
+                                       and o (correct) on the device; read the counts with
+                                       sparsepr_get_stats. The stages stay asynchronous and do not
+                                       fail on them (a non-finite M_K or probe fit still returns
+                                       SPARSEPR_ERR_NUMERIC where the stage solves on the host). */
 
 typedef struct {
     int32_t heads;          /* H >= 1 */
-    int32_t n;              /* tokens N, 1 .. 2^24 */
+    int32_t n;              /* tokens N, 1 .. 2^24 with n * d * 2 < 2^31 (one head's bf16 rows
+                               must fit the kernels' 32-bit buffer offsets) */
     int32_t d;              /* head dim, 64 or 128 */
     int32_t dtype;          /* SPARSEPR_BF16 or SPARSEPR_F32 (Q, K, V and O) */
     int32_t n_sample;       /* M_s sampled queries for M_K, 1 .. n */
@@ -103,12 +109,25 @@ typedef struct {
                                   averaged over the calls since the previous
                                   sparsepr_get_stats, at most the last 64) */
     int32_t timed_calls;       /* calls averaged into stage_ms */
+    int64_t nonfinite_inputs;  /* SPARSEPR_F_CHECK_FINITE: non-finite values in q, k, v of the last call */
+    int64_t nonfinite_outputs; /* SPARSEPR_F_CHECK_FINITE: non-finite values in o of the last call */
+    double  metric_gap_min;    /* min over heads of lambda_r / lambda_{r+1}, the gap after the r_K
+                                  leading eigenvalues of M_K (+inf when r_K = d or lambda_{r+1} <= 0;
+                                  0 with SPARSEPR_F_RAW_KMEANS, which has no M_K). Near 1 the key
+                                  coordinates, and so the key labels, are not unique. */
+    double  resid_gap_min;     /* min over heads of sigma_r / sigma_{r+1} of the probe residuals Y
+                                  (+inf when the kept rank reaches min(P, d) or sigma_{r+1} = 0).
+                                  Near 1 the correction subspace is not unique. */
 } sparsepr_stats;
 
 /* ---- parameters and lifetime (host only; sparsepr_create allocates on the current device) ---- */
 
 /* Check a parameter set; no GPU work. Returns SPARSEPR_OK or the first violation. */
 int32_t sparsepr_validate(const sparsepr_params* p);
+
+/* k = ceil(rho G_k - 1e-9) clamped to [1, G_k]: the key groups routed per query group
+ * (the width of the block lists). -status for an invalid parameter set. */
+int32_t sparsepr_routed_count(const sparsepr_params* p);
 
 /* Device bytes a context needs for these parameters (0 if invalid). */
 size_t sparsepr_workspace_bytes(const sparsepr_params* p);
@@ -140,10 +159,13 @@ int32_t sparsepr_partition(sparsepr_ctx* ctx, const void* q, const void* k, void
 /* 2C/2B. Reads v (k is only checked). Stable group-major permutation of V, top-k key
  * groups per query group (ties to the lower group index, empty key groups never kept),
  * probe rows.
+ * V is copied into group-major fp16, scaled per head by an exact power of two (exact for
+ * every bf16 value above 2^-29 of the head's largest |v|), for the sparse kernel's fp16 P.V.
  * Q is not copied: sparsepr_sparse_attn gathers its rows through the query permutation,
- * so q must stay unchanged until sparsepr_sparse_attn has run (for an fp32 context the
- * rows come from the context's bf16 copy of q, which sparsepr_dense_attn also rewrites:
- * do not call it in between). */
+ * and the probe rows gather bf16 V rows through the key permutation, so q and v must stay
+ * unchanged until sparsepr_sparse_attn has run (for an fp32 context the rows come from the
+ * context's bf16 copies, which sparsepr_dense_attn also rewrites: do not call it in
+ * between). */
 int32_t sparsepr_route(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
                        void* stream);
 
@@ -201,6 +223,12 @@ int32_t sparsepr_get_probes(sparsepr_ctx* ctx, float* x, float* y, int32_t host,
 int32_t sparsepr_get_fit(sparsepr_ctx* ctx, double* b_mat, double* b_vec, int32_t host,
                          void* stream);
 
+/* Per-head spectral gaps of the last call (fp64 [H] each; NULL skips): lambda_r/lambda_{r+1}
+ * of M_K and sigma_r/sigma_{r+1} of the probe residuals (see sparsepr_stats). Host memory
+ * only (host must be 1); synchronises `stream`. */
+int32_t sparsepr_get_gaps(sparsepr_ctx* ctx, double* metric_gap, double* resid_gap, int32_t host,
+                          void* stream);
+
 /* Counters of the last call and mean stage times since the previous call of this
  * function (synchronises the context's last stream). */
 int32_t sparsepr_get_stats(sparsepr_ctx* ctx, sparsepr_stats* out);
@@ -223,12 +251,6 @@ int32_t sparsepr_host_sym_eig_top(int32_t n, const double* a, int32_t r, double*
 
 /* Key projection W = U_r diag(sqrt(max(lambda_r, 0))) [d][r] of the metric m_k [d][d]. */
 int32_t sparsepr_host_key_projection(int32_t d, const double* m_k, int32_t r, double* w);
-
-/* Factor L [d][dims] with L L^T = C^T C / d for key centroids c [g][d]: Cholesky if
- * g > d and the metric is positive definite, else the profile map C^T / sqrt(d)
- * (dims = g, needs g <= d) or an eigen factor (dims = d). Returns dims in *dims. */
-int32_t sparsepr_host_query_factor(int32_t d, int32_t g, const double* c, double* l,
-                                   int32_t* dims);
 
 /* Probe fit from X, Y [p][d] (fp64): B' [d][d], b' [d]. */
 int32_t sparsepr_host_probe_fit(int32_t p, int32_t d, const double* x, const double* y,

@@ -41,7 +41,7 @@ def test_validation_accepts_configs_and_rejects_bad_values():
            dict(q_groups=1025, n=4096), dict(density=0.0), dict(density=1.5), dict(probes=-1),
            dict(probes=4097, n=8192), dict(corr_rank=65), dict(ridge_lambda=-1.0),
            dict(ridge_lambda=float("nan")), dict(kmeans_iters=0), dict(key_rank=0),
-           dict(key_rank=65), dict(n_sample=0), dict(dtype=7), dict(flags=8)]
+           dict(key_rank=65), dict(n_sample=0), dict(dtype=7), dict(flags=1 << 20)]
     for kw in bad:
         p = _params(**kw)
         if "n_sample" in kw:
@@ -102,24 +102,6 @@ def test_key_projection_matches_oracle_metric_distances():
     w_ref, _ = orc.key_projection(mk, 16)
     # columns may differ by sign; W W^T is unique
     assert np.allclose(w @ w.T, w_ref @ w_ref.T, atol=1e-11)
-
-
-@pytest.mark.parametrize("g,d", [(16, 64), (256, 128), (40, 16)])
-def test_query_factor_gives_the_profile_metric(g, d):
-    rng = np.random.default_rng(9)
-    c = rng.standard_normal((g, d))
-    l = spr.sparsepr_host_query_factor(c)
-    assert l.shape == (d, min(g, d) if g <= d else d)
-    assert np.allclose(l @ l.T, c.T @ c / d, atol=1e-11)
-
-
-def test_query_factor_semidefinite_falls_back_to_eigen_factor():
-    rng = np.random.default_rng(10)
-    c = np.zeros((40, 16))
-    c[:5] = rng.standard_normal((5, 16))             # rank 5 < d: Cholesky fails
-    l = spr.sparsepr_host_query_factor(c)
-    assert l.shape == (16, 16)
-    assert np.allclose(l @ l.T, c.T @ c / 16, atol=1e-11)
 
 
 @pytest.mark.parametrize("p,d,lam,r", [(64, 64, 1e-3, 8), (256, 128, 1e-3, 16), (300, 32, 0.5, 4),
@@ -204,7 +186,9 @@ def test_validate_accepts_the_comparison_partitioner_flag():
     assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 0
     p.flags = spr.F_RAW_KMEANS | spr.F_STAGE_TIMING
     assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 0
-    p.flags = 4
+    p.flags = spr.F_RAW_KMEANS | spr.F_CHECK_FINITE
+    assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 0
+    p.flags = 1 << 20
     assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 1        # SPARSEPR_ERR_INVALID_ARG
     # the comparison partitioner needs d-wide fp64 key centroids: the workspace grows
     p.flags = 0
@@ -212,3 +196,55 @@ def test_validate_accepts_the_comparison_partitioner_flag():
     p.flags = spr.F_RAW_KMEANS
     assert spr.lib.sparsepr_workspace_bytes(ctypes.byref(p)) > base
 
+
+
+@pytest.mark.parametrize("gk,rho", [(16, 0.25), (128, 0.25), (256, 0.15), (256, 0.22), (256, 0.26),
+                                    (256, 0.35), (256, 1.0), (384, 0.24), (256, 1e-6), (7, 0.5)])
+def test_routed_count_comes_from_the_library(gk, rho):
+    """The block-list width k is the library's (the binding computes nothing of the method);
+    it follows the oracle's rule k = ceil(rho G_k - 1e-9) clamped to [1, G_k]."""
+    p = _params(n=4096, kv_groups=gk, density=rho)
+    assert spr.sparsepr_routed_count(p) == orc.routed_count(rho, gk)
+    p.density = 0.0
+    assert spr.lib.sparsepr_routed_count(ctypes.byref(p)) < 0
+
+
+def test_validate_limits_one_heads_rows_to_32_bit_offsets():
+    """The kernels address one head's bf16 rows with 32-bit buffer offsets: n d 2 < 2^31."""
+    for d, n_max in ((128, (1 << 23) - 1), (64, (1 << 24) - 1)):
+        ok = _params(heads=1, n=n_max, d=d, key_rank=d // 4, corr_rank=8)
+        assert spr.sparsepr_validate(ok) == 0, (d, n_max)
+        big = _params(heads=1, n=n_max + 1, d=d, key_rank=d // 4, corr_rank=8)
+        assert spr.sparsepr_validate(big) == 2, (d, n_max + 1)          # SPARSEPR_ERR_SHAPE
+
+
+def test_sym_eig_top_resolves_eigenvalues_far_below_the_norm():
+    """Eigenvalues spanning 1e-10 of the largest (a Gram of residuals whose singular values
+    span 1e-5): each must come out to high relative accuracy, in order, with orthonormal
+    vectors (shifts kept apart relative to each eigenvalue, not to |A|)."""
+    rng = np.random.default_rng(12)
+    n, r = 64, 20
+    u, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    ev = np.sort(np.concatenate([np.logspace(0, -10, 30), np.zeros(n - 30)]))[::-1]
+    a = (u * ev) @ u.T
+    lam, vec = spr.sparsepr_host_sym_eig_top(a, r)
+    assert np.all(np.abs(lam / ev[:r] - 1) < 1e-5)
+    assert np.all(np.diff(lam) < 0)
+    assert np.abs(vec.T @ vec - np.eye(r)).max() < 1e-12
+    assert np.abs(a @ vec - vec * lam).max() < 1e-13
+
+
+def test_probe_fit_with_a_wide_residual_spectrum_matches_oracle():
+    """Residual singular values spanning 1e-5 (as at the 720p shape with rho = 0.35): the
+    Gram-route fit must still give the oracle's (SVD-route) B' and b'."""
+    rng = np.random.default_rng(13)
+    p, d, r = 256, 128, 16
+    x = rng.standard_normal((p, d))
+    sv = np.logspace(0, -5.5, d)
+    uy, _ = np.linalg.qr(rng.standard_normal((p, d)))
+    vy, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    y = (uy * sv) @ vy.T
+    bm, bv = spr.sparsepr_host_probe_fit(x, y, 1e-3, r)
+    rbm, rbv = orc.probe_fit(x, y, 1e-3, r)
+    scale = max(1.0, np.abs(rbm).max())
+    assert np.abs(bm - rbm).max() < 1e-10 * scale and np.abs(bv - rbv).max() < 1e-10 * scale

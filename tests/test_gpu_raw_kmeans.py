@@ -45,7 +45,7 @@ def test_raw_kmeans_partition_parity(spr, name, heads):
         assert np.array_equal(g["blocks"][i], ref.blocks), f"{name} h{hh} blocks"
         assert np.array_equal(g["probe_orig"][i], ref.probe_orig), f"{name} h{hh} probes"
         check_close(g["o_sparse"][i], ref.o_sparse, f"{name} h{hh} O_s", rel=3e-3, out_rel=2.0 ** -24)
-        amp = max(1.0, float(np.linalg.norm(np.eye(cfg.d) + ref.b_mat, 2)))
+        amp = float(np.linalg.norm(np.eye(cfg.d) + ref.b_mat, 2))
         say(f"{name} h{hh}: O rel_fro={rel_fro(g['o'][i], ref.o):.3e} "
             f"max_abs={max_abs(g['o'][i], ref.o):.3e} |I+B'|={amp:.2f}")
-        check_close(g["o"][i], ref.o, f"{name} h{hh} O", mabs=2e-2 * amp)
+        check_close(g["o"][i], ref.o, f"{name} h{hh} O")
