@@ -6,10 +6,13 @@ rows, probe fit, correction) over all heads of the Wan2.1-1.3B-shaped 720p workl
 (k = 67 of 256 key groups), inputs resident in HBM. Prints one JSON line on stdout;
 progress goes to stderr.
 
-Also reported: the sparse-attention kernel's executed-pair TFLOPS against the bf16 MFMA
-peak (HIP events around that kernel on its stream, averaged over the timed calls),
-this library's dense attention at the same shape, the oracle on the host cores for a
-bounded sample (one head), and bit-exact / tolerance parity of that head.
+The timed calls run in a context without stage timing (no events between stages). A second
+context with stage timing then repeats the same calls: its HIP events, recorded by the
+library on the stream each stage runs on, give the per-stage times and the sparse-attention
+kernel's executed-pair TFLOPS against the bf16 MFMA peak (the roofline figure). Also
+reported: this library's dense attention at the same shape, the oracle on the host cores for
+a bounded sample (one head; optionally every head in parallel processes), and bit-exact /
+tolerance parity of that head.
 """
 from __future__ import annotations
 
@@ -71,19 +74,54 @@ def measured_traffic(flops_per_launch: float, ms: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def oracle_baseline(cfg, q, k, v, gpu_head0):
+def _oracle_head(args):
+    """One head of the oracle call in a worker process with single-threaded BLAS; returns
+    the wall seconds."""
+    cfg_name, density, head = args
+    from threadpoolctl import threadpool_limits
+    import oracle as orc
+    from synthetic import get_config, make_inputs
+    cfg = get_config(cfg_name)
+    if density is not None:
+        cfg = cfg.with_settings(density=density)
+    q, k, v = make_inputs(cfg, heads=[head])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        orc.oracle_call(q, k, v, cfg.settings)
+        return time.perf_counter() - t0
+
+
+def oracle_all_heads(cfg_name, density, heads, workers):
+    """The whole oracle call: every head in its own single-threaded worker process, `workers`
+    at a time. Returns (wall seconds, sum of per-head seconds)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        per_head = pool.map(_oracle_head, [(cfg_name, density, h) for h in range(heads)])
+    return time.perf_counter() - t0, float(sum(per_head))
+
+
+def oracle_baseline(cfg, q, k, v, gpu_head0, threads_limit=None):
     """Time the fp64 oracle on head 0 (a bounded sample of the call) on the host cores,
     and check parity of the GPU's head 0 against it."""
+    import contextlib
     import oracle as orc
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = threadpool_limits(limits=threads_limit) if threads_limit else contextlib.nullcontext()
     except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        threadpool_info = None
+        limit = contextlib.nullcontext()
     cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    ref = orc.oracle_call(q[:1], k[:1], v[:1], cfg.settings)[0]
-    secs = time.perf_counter() - t0
+    with limit:
+        try:
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        t0 = time.perf_counter()
+        ref = orc.oracle_call(q[:1], k[:1], v[:1], cfg.settings)[0]
+        secs = time.perf_counter() - t0
     g = gpu_head0
     parity = {
         "head": 0,
@@ -102,7 +140,7 @@ def oracle_baseline(cfg, q, k, v, gpu_head0):
                           and parity["perms_exact"] and parity["blocks_exact"]
                           and parity["probes_exact"] and parity["o_rel_fro"] <= 5e-3
                           and parity["o_max_abs"] <= 2e-2)
-    cpu = {"value": secs * cfg.heads * 1e3, "unit": "ms", "cores": cores, "threads": threads,
+    cpu = {"value": secs * cfg.heads * 1e3, "unit": "ms", "cores": threads, "host_cores": cores,
            "kind": "oracle",
            "sample": (f"head 0 of {cfg.heads} of one call (whole fp64 oracle: partition, routing, "
                       f"sparse attention of all {cfg.n} rows, probes, fit, correction) timed once "
@@ -119,6 +157,13 @@ def main() -> int:
     ap.add_argument("--density", type=float, default=None)
     ap.add_argument("--no-oracle", action="store_true", help="skip the CPU baseline and parity leg")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--host-solve", action="store_true",
+                    help="eigensolve of the key metric on the host (SPARSEPR_F_HOST_SOLVE)")
+    ap.add_argument("--oracle-threads", type=int, default=None,
+                    help="limit the oracle leg's BLAS threads (1: single-threaded baseline)")
+    ap.add_argument("--oracle-all-heads", type=int, default=0, metavar="WORKERS",
+                    help="also time the whole oracle call, every head in its own "
+                         "single-threaded process, WORKERS at a time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB on the device (traffic counter calibration) and exit")
     args = ap.parse_args()
@@ -145,16 +190,15 @@ def main() -> int:
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v))
     od = torch.empty_like(qd)
-    ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d,
-                                     spr.BF16 if cfg.dtype == "bf16" else spr.F32, st,
-                                     flags=spr.F_STAGE_TIMING)
+    dt = spr.BF16 if cfg.dtype == "bf16" else spr.F32
+    base_flags = spr.F_HOST_SOLVE if args.host_solve else 0
+    ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, st, flags=base_flags)
     stream = torch.cuda.current_stream()
 
     log(f"warmup {args.warmup} calls")
     for _ in range(args.warmup):
         ctx.sparsepr_attention(qd, kd, vd, od)
     torch.cuda.synchronize()
-    ctx.sparsepr_get_stats()                       # start stage averages at the timed calls
     log(f"timing {args.steps} calls")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -166,8 +210,22 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
-    stats = ctx.sparsepr_get_stats()
     ms_call = max(wall_ms, ev_ms)
+    run_stats = ctx.sparsepr_get_stats()
+
+    # stage times and the kernel's own events, in a context of their own
+    log(f"stage timing: {args.steps} calls in a second context")
+    sctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, st,
+                                      flags=base_flags | spr.F_STAGE_TIMING)
+    sctx.sparsepr_attention(qd, kd, vd, od)
+    torch.cuda.synchronize()
+    sctx.sparsepr_get_stats()                      # start stage averages at the timed calls
+    for _ in range(args.steps):
+        sctx.sparsepr_attention(qd, kd, vd, od)
+    torch.cuda.synchronize()
+    stats = sctx.sparsepr_get_stats()
+    sctx.close()
+    assert stats["routed_pairs"] == run_stats["routed_pairs"], "the two contexts routed differently"
     stage = dict(zip(["partition", "route", "sparse_attention_kernel", "probe_rows", "probe_fit",
                       "correct"], [round(x, 4) for x in stats["stage_ms"]]))
     kernel_ms = stats["stage_ms"][2]
@@ -209,8 +267,14 @@ def main() -> int:
               "blocks": rout["blocks"][0], "probe_orig": rout["probe_orig"][0],
               "o_sparse": ctx.sparsepr_get_sparse_out()[0].astype(np.float64),
               "o": od[0].float().cpu().numpy().astype(np.float64)}
-        cpu, parity = oracle_baseline(cfg, q, k, v, g0)
+        cpu, parity = oracle_baseline(cfg, q, k, v, g0, args.oracle_threads)
         log(f"parity {parity}; cpu {cpu['value']:.0f} ms/call ({cpu['cores']} cores)")
+        if args.oracle_all_heads:
+            log(f"whole oracle call: {cfg.heads} heads, {args.oracle_all_heads} single-threaded workers")
+            wall, total = oracle_all_heads(args.config, args.density, cfg.heads, args.oracle_all_heads)
+            cpu["whole_call"] = {"wall_ms": round(wall * 1e3, 1), "sum_of_heads_ms": round(total * 1e3, 1),
+                                 "workers": args.oracle_all_heads, "threads_per_worker": 1}
+            log(f"whole oracle call {cpu['whole_call']}")
 
     traffic = measured_traffic(attn_flops, kernel_ms)
     out = {
@@ -238,6 +302,8 @@ def main() -> int:
         "exec_density": round(stats["exec_density"], 4),
         "routed_pair_density": round(stats["routed_pairs"] / (cfg.heads * cfg.n ** 2), 4),
         "stage_ms": stage,
+        "stage_timing": "second context with stage events; the timed calls above ran without",
+        "metric_eigensolve": "host" if args.host_solve else "device",
         "recheck_points": stats["recheck_points"],
         "dense": dense,
         "roofline": {"kernel": "k_vbsa (variable-block-sparse attention)", "bound": "mfma",

@@ -23,6 +23,7 @@ BF16, F32 = 0, 1
 F_STAGE_TIMING = 1
 F_RAW_KMEANS = 2      # comparison partitioner: independent Euclidean k-means of raw Q and K
 F_CHECK_FINITE = 4    # count non-finite inputs and outputs on the device (sparsepr_get_stats)
+F_HOST_SOLVE = 8      # M_K eigensolve on the host instead of the device
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "out of memory",
           4: "HIP error", 5: "stage order", 6: "numerical failure"}
@@ -34,7 +35,7 @@ EXPORTS = [
     "sparsepr_dense_attn", "sparsepr_get_partition", "sparsepr_get_routing",
     "sparsepr_get_centroids", "sparsepr_get_sparse_out", "sparsepr_get_probes",
     "sparsepr_get_fit", "sparsepr_get_stats", "sparsepr_set_partition", "sparsepr_routed_count",
-    "sparsepr_get_gaps",
+    "sparsepr_get_gaps", "sparsepr_get_metric",
     "sparsepr_host_sym_eig_top", "sparsepr_host_key_projection",
     "sparsepr_host_probe_fit",
 ]
@@ -101,6 +102,7 @@ _sigs = {
     "sparsepr_set_partition": (_I, [_ctx, _P, _P, _P, _P, _I, _P]),
     "sparsepr_routed_count": (_I, [ctypes.POINTER(Params)]),
     "sparsepr_get_gaps": (_I, [_ctx, _P, _P, _I, _P]),
+    "sparsepr_get_metric": (_I, [_ctx, _P, _P, _I, _P]),
     "sparsepr_host_sym_eig_top": (_I, [_I, _P, _I, _P, _P]),
     "sparsepr_host_key_projection": (_I, [_I, _P, _I, _P]),
     "sparsepr_host_probe_fit": (_I, [_I, _I, _P, _P, ctypes.c_double, _I, _P, _P]),
@@ -278,6 +280,13 @@ class SparsePR:
         self._c(lib.sparsepr_get_routing(self._ctx, _np_ptr(blocks), _np_ptr(po), _np_ptr(pp), 1,
                                          _stream_ptr(stream)))
         return {"blocks": blocks, "probe_orig": po[:, :p.probes], "probe_pos": pp[:, :p.probes]}
+
+    def sparsepr_get_metric(self, stream=None):
+        p = self.params
+        mk = np.empty((p.heads, p.d, p.d))
+        w = np.empty((p.heads, p.d, p.key_rank))
+        self._c(lib.sparsepr_get_metric(self._ctx, _np_ptr(mk), _np_ptr(w), 1, _stream_ptr(stream)))
+        return mk, w
 
     def sparsepr_get_centroids(self, stream=None):
         p = self.params

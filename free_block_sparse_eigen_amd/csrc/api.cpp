@@ -109,6 +109,11 @@ struct sparsepr_ctx {
     int32_t *koff = nullptr, *qoff = nullptr;
     int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
     double *mk = nullptr, *w64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
+    // device eigensolve of M_K: tridiagonal form, reflectors, eigenpairs, |T|, gap
+    double *eig_diag = nullptr, *eig_off = nullptr, *eig_hv = nullptr, *eig_beta = nullptr;
+    double *eig_lam = nullptr, *eig_vec = nullptr, *eig_tnorm = nullptr, *mgap = nullptr;
+    bool dev_eig = false;              // M_K eigensolve on the device (else on the host)
+    bool mgap_dev = false;             // the last partition's metric gaps are in mgap
     double* ident = nullptr;           // [H][d][d] identity metric (SPARSEPR_F_RAW_KMEANS)
     double *kc2 = nullptr, *qc2 = nullptr;               // fp64 |c|^2 per centroid
     double *kraw = nullptr, *qraw = nullptr;
@@ -194,7 +199,8 @@ int32_t validate(const sparsepr_params* p) {
     if (p->corr_rank < 0 || p->corr_rank > p->d) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
-    if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE))
+    if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE |
+                     SPARSEPR_F_HOST_SOLVE))
         return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
 }
@@ -230,6 +236,7 @@ void derive(sparsepr_ctx& c) {
     c.splits = probe_splits(c.N, c.H, c.P);
     c.gmax = std::max(c.Gk, c.Gq);
     c.weyl_a = weyl_multiplier(c.N);
+    c.dev_eig = !c.raw && !(p.flags & SPARSEPR_F_HOST_SOLVE) && c.rK <= kEigMaxR && c.d <= kEigMaxN;
 }
 
 void layout(sparsepr_ctx& c, Arena& a) {
@@ -256,6 +263,16 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.blkoff, H * c.nblk * c.gmax);
     a.take(c.mk, H * d * d);
     a.take(c.w64, H * d * c.rK);
+    if (c.dev_eig) {
+        a.take(c.eig_diag, H * d);
+        a.take(c.eig_off, H * d);
+        a.take(c.eig_hv, H * d * d);
+        a.take(c.eig_beta, H * d);
+        a.take(c.eig_lam, H * (c.rK + 1));
+        a.take(c.eig_vec, H * c.rK * d);
+        a.take(c.eig_tnorm, H);
+    }
+    a.take(c.mgap, H);
     a.take(c.kc64, H * c.Gk * (c.raw ? d : (size_t)c.rK));
     if (c.raw) a.take(c.ident, H * d * d);
     a.take(c.qc64, H * c.Gq * d);
@@ -534,6 +551,26 @@ int32_t permute_keys_side(sparsepr_ctx* c, const bf16_t* k16, hipStream_t st) {
 }
 }  // namespace
 
+namespace {
+// Keys: Lloyd in the M_K eigen-coordinates W (already in c->w64); K permuted on the side
+// stream; queries: the logit-profile metric M = C_K^T C_K / d (fp64 Gram of the raw key
+// centroids) used in full on the device, then Lloyd.
+int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
+    int32_t rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
+                       c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
+    if (rc) return rc;
+    if ((rc = permute_keys_side(c, k16, st))) return rc;
+    launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
+    SPR_LAUNCHED(c, "query metric");
+    rc = lloyd(c, q16, 0, c->mq, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * c->H, c->qperm, c->qoff,
+               c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
+    if (rc) return rc;
+    mark(c, 1, st);
+    c->stage = kStagePartition;
+    return SPARSEPR_OK;
+}
+}  // namespace
+
 int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* stream) {
     int32_t rc = enter(c, 0);
     if (rc) return rc;
@@ -555,6 +592,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
     }
     if (c->raw) {
         std::fill(c->h_mgap.begin(), c->h_mgap.end(), 0.0);      // no M_K
+        c->mgap_dev = false;
         // comparison partitioner: plain Euclidean k-means of the raw key rows, then of the
         // raw query rows (full-metric path with M = I: screening vector = mean)
         rc = lloyd(c, k16, 0, c->ident, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
@@ -568,9 +606,16 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         c->stage = kStagePartition;
         return SPARSEPR_OK;
     }
-    // M_K and its leading eigenvectors (host fp64)
+    // M_K and its leading eigenvectors (fp64; on the device unless SPARSEPR_F_HOST_SOLVE)
     launch_metric(q16, c->H, c->N, c->d, c->p.n_sample, c->weyl_a, c->mk, st);
     SPR_LAUNCHED(c, "metric");
+    c->mgap_dev = c->dev_eig;
+    if (c->dev_eig) {
+        launch_sym_eig_top(c->mk, c->H, c->d, c->rK, c->eig_diag, c->eig_off, c->eig_hv, c->eig_beta,
+                           c->eig_lam, c->eig_vec, c->eig_tnorm, c->w64, c->mgap, st);
+        SPR_LAUNCHED(c, "metric eigensolve");
+        return partition_keys_and_queries(c, q16, k16, st);
+    }
     // (pinned staging both ways; W is rewritten only after the next call's sync)
     SPR_HIP(c, hipMemcpyAsync(c->h_mkp, c->mk, sizeof(double) * H * d * d, hipMemcpyDeviceToHost, st));
     SPR_HIP(c, hipStreamSynchronize(st));
@@ -583,21 +628,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         if (prc[h] != 0) return fail(c, SPARSEPR_ERR_NUMERIC, "metric eigensolve failed (non-finite input)");
     }
     SPR_HIP(c, hipMemcpyAsync(c->w64, c->h_wp, sizeof(double) * H * d * rK, hipMemcpyHostToDevice, st));
-    // keys: Lloyd in the M_K eigen-coordinates
-    rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw, c->kc64,
-               c->kcp, c->kcn2, c->kcpn, c->kc2, st);
-    if (rc) return rc;
-    if ((rc = permute_keys_side(c, k16, st))) return rc;
-    // queries: the logit-profile metric M = C_K^T C_K / d (fp64 Gram of the raw key
-    // centroids) used in full on the device, then Lloyd
-    launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
-    SPR_LAUNCHED(c, "query metric");
-    rc = lloyd(c, q16, 0, c->mq, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm, c->qoff,
-               c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
-    if (rc) return rc;
-    mark(c, 1, st);
-    c->stage = kStagePartition;
-    return SPARSEPR_OK;
+    return partition_keys_and_queries(c, q16, k16, st);
 }
 
 int32_t sparsepr_set_partition(sparsepr_ctx* c, const void* q, const void* k,
@@ -849,6 +880,17 @@ int32_t sparsepr_get_routing(sparsepr_ctx* c, int32_t* blocks, int32_t* probe_or
     return SPARSEPR_OK;
 }
 
+int32_t sparsepr_get_metric(sparsepr_ctx* c, double* m_k, double* w, int32_t host, void* stream) {
+    int32_t rc = enter(c, kStagePartition);
+    if (rc) return rc;
+    if (c->raw) return fail(c, SPARSEPR_ERR_ORDER, "no key metric with SPARSEPR_F_RAW_KMEANS");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = copy_out(c, m_k, c->mk, 8 * (size_t)c->H * c->d * c->d, host, st))) return rc;
+    if ((rc = copy_out(c, w, c->w64, 8 * (size_t)c->H * c->d * c->rK, host, st))) return rc;
+    if (host) SPR_HIP(c, hipStreamSynchronize(st));
+    return SPARSEPR_OK;
+}
+
 int32_t sparsepr_get_centroids(sparsepr_ctx* c, double* key_centroids, double* q_centroids, int32_t host,
                                void* stream) {
     int32_t rc = enter(c, kStagePartition);
@@ -903,6 +945,7 @@ int32_t sparsepr_get_gaps(sparsepr_ctx* c, double* metric_gap, double* resid_gap
     if (rc) return rc;
     if (!host) return fail(c, SPARSEPR_ERR_INVALID_ARG, "sparsepr_get_gaps writes host memory only");
     SPR_HIP(c, hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+    if (c->mgap_dev) SPR_HIP(c, hipMemcpy(c->h_mgap.data(), c->mgap, 8 * (size_t)c->H, hipMemcpyDeviceToHost));
     if (metric_gap) std::copy(c->h_mgap.begin(), c->h_mgap.end(), metric_gap);
     if (resid_gap) {
         if (c->stage >= kStageFit) std::copy(c->h_rgap.begin(), c->h_rgap.end(), resid_gap);
@@ -935,8 +978,10 @@ int32_t sparsepr_get_stats(sparsepr_ctx* c, sparsepr_stats* out) {
     }
     out->metric_gap_min = INFINITY;
     out->resid_gap_min = INFINITY;
-    if (c->stage >= kStagePartition)
+    if (c->stage >= kStagePartition) {
+        if (c->mgap_dev) SPR_HIP(c, hipMemcpy(c->h_mgap.data(), c->mgap, 8 * (size_t)c->H, hipMemcpyDeviceToHost));
         for (double g : c->h_mgap) out->metric_gap_min = std::min(out->metric_gap_min, g);
+    }
     if (c->stage >= kStageFit)
         for (double g : c->h_rgap) out->resid_gap_min = std::min(out->resid_gap_min, g);
     if (c->stage >= kStagePartition) {

@@ -23,6 +23,15 @@ void launch_count_nonfinite(const void* x, size_t count, int is_f32, unsigned lo
                             hipStream_t st);
 
 // ---- partition ----
+constexpr int kEigMaxN = 128;         // device eigensolve: matrix order
+constexpr int kEigMaxR = 64;          // device eigensolve: leading eigenvectors kept
+// Leading r eigenpairs of the symmetric m [heads][n][n] (n <= kEigMaxN, r <= kEigMaxR) on the
+// device: w [heads][n][r] = U_r diag(sqrt(max(lambda, 0))), gap [heads] = lambda_r/lambda_{r+1}
+// (+inf if r = n or lambda_{r+1} <= 0). Scratch: diag, off, hbeta, tnorm [heads][n] (tnorm
+// [heads]), hv [heads][n][n], lam [heads][r+1], vec [heads][r][n].
+void launch_sym_eig_top(const double* m, int heads, int n, int r, double* diag, double* off,
+                        double* hv, double* hbeta, double* lam, double* vec, double* tnorm,
+                        double* w, double* gap, hipStream_t st);
 void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64_t a, double* mk,
                    hipStream_t st);
 // The metric is a factor l64 [d][dout] (metric = L L^T), or with dout == 0 the full

@@ -713,7 +713,9 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
                     bb = wbest[k][tid];
                     g = wbg[k][tid];
                 }
-            labels[(size_t)h * n + fl[b0 + tid]] = g;
+            // no finite distance (non-finite coordinates): the lowest index, so a label is
+            // always a group
+            labels[(size_t)h * n + fl[b0 + tid]] = g < groups ? g : 0;
         }
         __syncthreads();
     }
@@ -729,6 +731,12 @@ void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64,
 }
 
 // ---------------------------------------------------------- counting sort ---
+// A label outside [0, groups) counts as group 0 in both passes, so the sort stays a
+// permutation whatever the labels hold.
+__device__ inline int group_of(int32_t label, int groups) {
+    return (uint32_t)label < (uint32_t)groups ? label : 0;
+}
+
 __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ labels, int n, int groups,
                                               int32_t* __restrict__ blkhist) {
     __shared__ int hist[kMaxGroups];
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(256) void k_hist(const int32_t* __restrict__ labels
     const int base = b * kSortChunk;
     for (int i = tid; i < kSortChunk; i += 256) {
         const int p = base + i;
-        if (p < n) atomicAdd(&hist[labels[(size_t)h * n + p]], 1);
+        if (p < n) atomicAdd(&hist[group_of(labels[(size_t)h * n + p], groups)], 1);
     }
     __syncthreads();
     int32_t* out = blkhist + ((size_t)h * gridDim.x + b) * groups;
@@ -820,7 +828,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
 #pragma unroll
     for (int r = 0; r < PW / 64; ++r) {
         const int p = pw0 + r * 64 + lane;
-        lab[r] = (p < n) ? labels[(size_t)h * n + p] : -1;
+        lab[r] = (p < n) ? group_of(labels[(size_t)h * n + p], groups) : -1;
         if (lab[r] >= 0) atomicAdd(&cnt[wave][lab[r]], 1);
     }
     __syncthreads();

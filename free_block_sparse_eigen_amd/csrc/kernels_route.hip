@@ -158,8 +158,10 @@ __global__ __launch_bounds__(256) void k_route(const double* __restrict__ cq,
 #pragma unroll
             for (int q = 0; q < QG; ++q) s[q] += cs[q][t] * cv;
         }
+        // a NaN logit (non-finite centroids) ranks as -inf, so (score, index) stays a total
+        // order and exactly min(k, non-empty) groups are kept
 #pragma unroll
-        for (int q = 0; q < QG; ++q) sc[j][q] = s[q] / rs;
+        for (int q = 0; q < QG; ++q) sc[j][q] = isnan(s[q]) ? -INFINITY : s[q] / rs;
         ne[j] = (ko[j + 1] > ko[j]) ? 1 : 0;
     }
     __syncthreads();

@@ -26,8 +26,9 @@
  *     are rounded to bf16, nearest-even, on entry; O is written in the same dtype).
  *   - Device work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     null stream). Entry points return once the work is enqueued, except where
- *     noted: the partition and probe-fit stages solve small fp64 eigen/linear
- *     systems on the host and synchronise `stream` to do so.
+ *     noted: the probe-fit stage solves a small fp64 system on the host and waits for
+ *     the probe rows (not for the sparse kernel) to do so; the partition stage does the
+ *     same only with SPARSEPR_F_HOST_SOLVE.
  *   - The caller owns Q/K/V/O and keeps them alive until the stream work is done.
  *     The context owns every intermediate; nothing is kept between calls except
  *     what the inspection getters read back.
@@ -70,6 +71,9 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        rows (the independent Q/K clustering of cluster-based
                                        sparse attention), with the same seeds, rounds, routing,
                                        probes and correction; no M_K and no host round trip */
+#define SPARSEPR_F_HOST_SOLVE 8u    /* solve the M_K eigenproblem on the host (fp64, the partition
+                                       stage then synchronises its stream once) instead of on
+                                       the device; also used whenever key_rank > 64 */
 #define SPARSEPR_F_CHECK_FINITE 4u  /* count non-finite values of q and k (partition), v (route)
                                        and o (correct) on the device; read the counts with
                                        sparsepr_get_stats. The stages stay asynchronous and do not
@@ -147,8 +151,11 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 
 /* ---- the five stages (section 2 of the method summary) ---- */
 
-/* 2A. Reads q, k. Host-synchronising once (fp64 eigensolve of M_K on the host); the
- * query side runs on the device with the logit-profile metric C_K^T C_K / d in full.
+/* 2A. Reads q, k. Asynchronous: M_K, its leading eigenpairs (fp64: Householder
+ * tridiagonalisation, bisection, inverse iteration) and both k-means run on the device.
+ * With SPARSEPR_F_HOST_SOLVE, or key_rank > 64, the eigensolve runs on the host instead and
+ * the stage synchronises `stream` once. The query side uses the logit-profile metric
+ * C_K^T C_K / d in full.
  * Leaves key/query labels and centroids in the context. With SPARSEPR_F_RAW_KMEANS both
  * sides use the identity metric instead (no host round trip). K is then permuted into
  * group-major order on the context's side stream while the query side runs, so k must
@@ -208,6 +215,12 @@ int32_t sparsepr_get_partition(sparsepr_ctx* ctx, int32_t* key_labels, int32_t* 
  * token indices and as group-major positions. */
 int32_t sparsepr_get_routing(sparsepr_ctx* ctx, int32_t* blocks, int32_t* probe_orig,
                              int32_t* probe_pos, int32_t host, void* stream);
+
+/* The key metric M_K = Q_s^T Q_s / M_s (fp64 [H][d][d]) and the key coordinates' map
+ * W = U_r diag(sqrt(lambda_r)) (fp64 [H][d][r_K]) of the last partition (section 2A). Only
+ * W W^T is defined (eigenvector signs and rotations inside a repeated eigenvalue are free).
+ * Not available with SPARSEPR_F_RAW_KMEANS (SPARSEPR_ERR_ORDER). */
+int32_t sparsepr_get_metric(sparsepr_ctx* ctx, double* m_k, double* w, int32_t host, void* stream);
 
 /* Raw fp64 centroids: keys [H][G_k][d], queries [H][G_q][d] (zero for an empty group). */
 int32_t sparsepr_get_centroids(sparsepr_ctx* ctx, double* key_centroids, double* q_centroids,

@@ -191,8 +191,11 @@ def test_validate_accepts_the_comparison_partitioner_flag():
     p.flags = 1 << 20
     assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 1        # SPARSEPR_ERR_INVALID_ARG
     # the comparison partitioner needs d-wide fp64 key centroids: the workspace grows
-    p.flags = 0
+    # (against the method with its eigensolve on the host, which has no device eigen scratch)
+    p.flags = spr.F_HOST_SOLVE
     base = spr.lib.sparsepr_workspace_bytes(ctypes.byref(p))
+    p.flags = 0
+    assert spr.lib.sparsepr_workspace_bytes(ctypes.byref(p)) > base      # device eigen scratch
     p.flags = spr.F_RAW_KMEANS
     assert spr.lib.sparsepr_workspace_bytes(ctypes.byref(p)) > base
 
