@@ -35,7 +35,7 @@ EXPORTS = [
     "sparsepr_dense_attn", "sparsepr_get_partition", "sparsepr_get_routing",
     "sparsepr_get_centroids", "sparsepr_get_sparse_out", "sparsepr_get_probes",
     "sparsepr_get_fit", "sparsepr_get_stats", "sparsepr_set_partition", "sparsepr_routed_count",
-    "sparsepr_get_gaps", "sparsepr_get_metric",
+    "sparsepr_get_gaps", "sparsepr_get_metric", "sparsepr_dense_attn_noalloc",
     "sparsepr_host_sym_eig_top", "sparsepr_host_key_projection",
     "sparsepr_host_probe_fit",
 ]
@@ -103,6 +103,7 @@ _sigs = {
     "sparsepr_routed_count": (_I, [ctypes.POINTER(Params)]),
     "sparsepr_get_gaps": (_I, [_ctx, _P, _P, _I, _P]),
     "sparsepr_get_metric": (_I, [_ctx, _P, _P, _I, _P]),
+    "sparsepr_dense_attn_noalloc": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "sparsepr_host_sym_eig_top": (_I, [_I, _P, _I, _P, _P]),
     "sparsepr_host_key_projection": (_I, [_I, _P, _I, _P]),
     "sparsepr_host_probe_fit": (_I, [_I, _I, _P, _P, ctypes.c_double, _I, _P, _P]),
@@ -187,6 +188,19 @@ def _tptr(t) -> int:
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("expected a contiguous GPU tensor")
     return t.data_ptr()
+
+
+def sparsepr_dense_attn_noalloc(q, k, v, o, stream=None):
+    """Dense attention of bf16 q, k, v [H][n][d] into the caller's o with no device
+    allocation (no context; the library's static scratch)."""
+    import torch
+    for t in (q, k, v, o):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or tuple(t.shape) != tuple(q.shape):
+            raise ValueError("q, k, v and o must be bf16 [H][n][d] of one shape")
+    h, n, d = q.shape
+    _check(lib.sparsepr_dense_attn_noalloc(h, n, d, _tptr(q), _tptr(k), _tptr(v), _tptr(o),
+                                           _stream_ptr(stream)))
+    return o
 
 
 class SparsePR:

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparsepr.so")
 SOURCES = ["api.cpp", "host_linalg.cpp", "kernels_partition.hip", "kernels_route.hip",
-           "kernels_attn.hip", "kernels_probe.hip", "kernels_correct.hip", "kernels_eig.hip"]
+           "kernels_attn.hip", "kernels_probe.hip", "kernels_correct.hip", "kernels_eig.hip",
+           "noalloc.hip"]
 HOST_ONLY = {"host_linalg.cpp"}       # plain C++ (no HIP): built by the host compiler alone
 ARCH = os.environ.get("SPARSEPR_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

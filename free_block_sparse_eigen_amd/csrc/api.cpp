@@ -402,6 +402,15 @@ int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, int dim, const double* l64, int 
 
 }  // namespace
 
+namespace {
+// why this thread's last sparsepr_create or context-free call failed
+thread_local std::string create_err;
+}  // namespace
+
+namespace spr {
+void set_call_error(const char* msg) { create_err = msg; }
+}  // namespace spr
+
 extern "C" {
 
 int32_t sparsepr_validate(const sparsepr_params* p) { return validate(p); }
@@ -435,8 +444,6 @@ const char* sparsepr_status_str(int32_t s) {
 }
 
 namespace {
-thread_local std::string create_err;   // why this thread's last sparsepr_create failed
-
 int32_t create_fail(sparsepr_ctx* c, int32_t status, const char* what, hipError_t e) {
     create_err = std::string(what) + ": " + hipGetErrorString(e);
     if (c) sparsepr_destroy(c);

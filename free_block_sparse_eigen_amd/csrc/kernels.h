@@ -68,6 +68,8 @@ void launch_probes(const int32_t* qoff, const int32_t* qperm, int heads, int n, 
                    hipStream_t st);
 void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int max_units,
                   int2* units, int32_t* nunits, hipStream_t st);
+// this thread's error detail for calls without a context (sparsepr_last_error(NULL))
+void set_call_error(const char* msg);
 
 // ---- attention ----
 // out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index); unit_rows is

@@ -146,7 +146,8 @@ void sparsepr_destroy(sparsepr_ctx* ctx);
 const char* sparsepr_status_str(int32_t status);
 
 /* Detail of the context's last error ("" if none). With ctx NULL: why this thread's last
- * sparsepr_create failed (the HIP call and its error string; "" after a success). */
+ * sparsepr_create or sparsepr_dense_attn_noalloc failed (the HIP call and its error
+ * string, or the limit exceeded; "" after a success). */
 const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 
 /* ---- the five stages (section 2 of the method summary) ---- */
@@ -201,6 +202,20 @@ int32_t sparsepr_attention(sparsepr_ctx* ctx, const void* q, const void* k, cons
  * holding every key); uses the context's shapes and workspace, no other stage state. */
 int32_t sparsepr_dense_attn(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
                             void* o, void* stream);
+
+/* The dense baseline with no allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * No context: q, k, v and o are caller-owned bf16 [heads][n][d] device buffers (16-byte
+ * aligned); the same kernel, launch and results as sparsepr_dense_attn on a bf16 context.
+ * The call's only scratch, its work-unit metadata, is a static device array of 65,792
+ * bytes that each device holds until the process ends (its address is looked up on the
+ * first call on a device). Limits: d in {64, 128}, 1 <= n <= 2,097,152 (8192 units of 256
+ * rows), heads * n < 2^31, else SPARSEPR_ERR_SHAPE; null or misaligned pointers give
+ * SPARSEPR_ERR_INVALID_ARG, a failed launch SPARSEPR_ERR_HIP; the detail is in
+ * sparsepr_last_error(NULL). Asynchronous on `stream`. Every call on a device rewrites that
+ * device's array, so calls that overlap on one device (other streams or threads) race. */
+int32_t sparsepr_dense_attn_noalloc(int32_t heads, int32_t n, int32_t d, const void* q,
+                                    const void* k, const void* v, void* o, void* stream);
 
 /* ---- inspection (copy context-owned results out; NULL destinations are skipped).
  * host != 0: destinations are host memory and `stream` is synchronised before return;

@@ -251,3 +251,18 @@ def test_probe_fit_with_a_wide_residual_spectrum_matches_oracle():
     rbm, rbv = orc.probe_fit(x, y, 1e-3, r)
     scale = max(1.0, np.abs(rbm).max())
     assert np.abs(bm - rbm).max() < 1e-10 * scale and np.abs(bv - rbv).max() < 1e-10 * scale
+
+
+def test_noalloc_dense_rejects_shapes_and_pointers_before_any_device_use():
+    """The no-allocation dense entry point checks its limits (d, the static scratch's 8192
+    work units of 256 rows, heads * n) and its pointers on the host, before it touches a
+    device, and reports why through sparsepr_last_error(NULL)."""
+    lib = spr.lib
+    f = lib.sparsepr_dense_attn_noalloc
+    assert f(1, 2097153, 64, None, None, None, None, None) == 2
+    assert b"8192" in lib.sparsepr_last_error(None)
+    assert f(1, 1000, 96, None, None, None, None, None) == 2
+    assert f(0, 1000, 64, None, None, None, None, None) == 2
+    assert f(1100, 2000000, 128, None, None, None, None, None) == 2      # heads * n >= 2^31
+    assert f(1, 2097152, 64, None, None, None, None, None) == 1          # largest n: pointers
+    assert b"null or misaligned" in lib.sparsepr_last_error(None)
