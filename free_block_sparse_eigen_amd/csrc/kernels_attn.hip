@@ -118,15 +118,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
     const int32_t* bl = blocks + (size_t)h * blocks_head_stride + (size_t)gi * kblk;
     const size_t head_row0 = (size_t)h * n;
 
+    // routed segments: start row and length, then the exclusive prefix of the lengths
+    // (one wave: each lane sums a contiguous run, then a wave scan of the run totals)
     for (int s = tid; s < kblk; s += kVbsaThreads) {
         const int j = bl[s];
         s_start[s] = (j >= 0) ? ko[j] : 0;
         s_pre[s + 1] = (j >= 0) ? (ko[j + 1] - ko[j]) : 0;
     }
-    if (tid == 0) s_pre[0] = 0;
     __syncthreads();
-    if (tid == 0)
-        for (int s = 1; s <= kblk; ++s) s_pre[s] += s_pre[s - 1];
+    if (w == 0) {
+        const int per = (kblk + 63) / 64, b0 = min(lane * per, kblk), b1 = min(b0 + per, kblk);
+        int run = 0;
+        for (int s = b0; s < b1; ++s) run += s_pre[s + 1];
+        int inc = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += v;
+        }
+        int acc = inc - run;
+        if (lane == 0) s_pre[0] = 0;
+        for (int s = b0; s < b1; ++s) {
+            acc += s_pre[s + 1];
+            s_pre[s + 1] = acc;
+        }
+    }
     __syncthreads();
     const int U = s_pre[kblk];
     const int ntiles = (U + KT - 1) / KT;
