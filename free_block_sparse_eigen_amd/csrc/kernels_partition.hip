@@ -106,10 +106,12 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
 //            |c|^2 = m . C' (also kept in fp64)
 //   split of C' into bf16 hi + lo parts   (the MFMA operand; |C' - hi - lo| <= 2^-17 |C'|)
 //   |c|^2 (fp32, nearest) and |C'| (fp32, rounded up) for the screening score and bound
-// Block = 4 centroids of one head (each element of L read from L2 serves 4 of them;
-// small blocks keep every CU busy). With `off` given, empty groups are skipped (they
-// keep their previous centroid).
-constexpr int kFinG = 4;
+// Block = 16 centroids of one head. A thread owns one output coordinate for all 16 of
+// them (each element of L it reads from L2 serves 16 accumulators, 16 loads in flight at
+// a time) over a contiguous range of the summed index; the ranges' partial sums are added
+// in range order. The work is latency-bound: a thread's sum has at most 64 terms. With
+// `off` given, empty groups are skipped (they keep their previous centroid).
+constexpr int kFinG = 16;
 
 // fixed-order sum of v over the 64 lanes (butterfly; identical on every lane)
 __device__ inline double wave_sum_f64(double v) {
@@ -124,55 +126,97 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
                                                 double* __restrict__ c64, bf16_t* __restrict__ cpart,
                                                 float* __restrict__ cn2, float* __restrict__ cpn,
                                                 double* __restrict__ c2_64) {
+    constexpr int G = kFinG;
     const bool full = dout == 0;                 // full metric M [d][d]
-    __shared__ double s_m[kFinG][129];     // means (padded rows)
-    __shared__ double s_c[kFinG][129];     // projected centroids
-    __shared__ double s_s[kFinG][129];     // screening vectors
-    const int h = blockIdx.y, g0 = blockIdx.x * kFinG, tid = threadIdx.x;
+    __shared__ double s_m[G][129];               // means (padded rows)
+    __shared__ double s_c[G][129];               // projected centroids
+    __shared__ double s_s[G][129];               // screening vectors
+    __shared__ double s_part[256 * G];           // partial sums [range][g][coordinate]
+    const int h = blockIdx.y, g0 = blockIdx.x * G, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     if (full) dout = d;
     const double* lh = l64 + (size_t)h * d * dout;
-    for (int o = tid; o < kFinG * d; o += 256) {
+    for (int o = tid; o < G * d; o += 256) {
         const int gs = o / d, i = o % d, g = g0 + gs;
         s_m[gs][i] = (g < groups) ? mean_raw[((size_t)h * groups + g) * d + i] : 0.0;
     }
     __syncthreads();
-    // c[gs][j] = sum_i m[gs][i] L[i][j]   (lanes along j: coalesced rows of L); with the
-    // full metric this is C' = M m itself (M is symmetric)
-    for (int o = tid; o < kFinG * dout; o += 256) {
-        const int gs = o / dout, j = o % dout;
-        double acc = 0.0;
-        int i = 0;
-        for (; i + 16 <= d; i += 16) {                   // loads 16 at a time, sums in order
-            double lv[16];
+    // c[gs][j] = sum_i m[gs][i] L[i][j]: thread (range r, coordinate j) sums i over its
+    // range for all G centroids (lanes along j: coalesced rows of L); with the full metric
+    // this is C' = M m itself (M is symmetric)
+    {
+        const int nr = 256 / dout;                       // dout divides 256 (d and r_K are)
+        const int j = tid % dout, r = tid / dout;
+        const int len = (d + nr - 1) / nr, i0 = min(r * len, d), i1 = min(i0 + len, d);
+        double acc[G];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)(i + u) * dout + j];
+        for (int gs = 0; gs < G; ++gs) acc[gs] = 0.0;
+        if (r < nr) {
+            int i = i0;
+            for (; i + 16 <= i1; i += 16) {
+                double lv[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) acc += s_m[gs][i + u] * lv[u];
+                for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)(i + u) * dout + j];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+#pragma unroll
+                    for (int gs = 0; gs < G; ++gs) acc[gs] += s_m[gs][i + u] * lv[u];
+            }
+            for (; i < i1; ++i) {
+                const double l = lh[(size_t)i * dout + j];
+#pragma unroll
+                for (int gs = 0; gs < G; ++gs) acc[gs] += s_m[gs][i] * l;
+            }
+#pragma unroll
+            for (int gs = 0; gs < G; ++gs) s_part[(r * G + gs) * dout + j] = acc[gs];
         }
-        for (; i < d; ++i) acc += s_m[gs][i] * lh[(size_t)i * dout + j];
-        s_c[gs][j] = acc;
-    }
-    __syncthreads();
-    // C'[gs][i] = sum_j L[i][j] c[gs][j]   (lanes of one i share one element of L)
-    for (int o = tid; o < kFinG * d; o += 256) {
-        if (full) break;
-        const int i = o / kFinG, gs = o % kFinG;
-        double acc = 0.0;
-        int j = 0;
-        for (; j + 16 <= dout; j += 16) {
-            double lv[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)i * dout + j + u];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) acc += lv[u] * s_c[gs][j + u];
+        __syncthreads();
+        for (int o = tid; o < G * dout; o += 256) {
+            const int gs = o / dout, jj = o % dout;
+            double c = 0.0;
+            for (int rr = 0; rr < nr; ++rr) c += s_part[(rr * G + gs) * dout + jj];
+            s_c[gs][jj] = c;
         }
-        for (; j < dout; ++j) acc += lh[(size_t)i * dout + j] * s_c[gs][j];
-        s_s[gs][i] = acc;
+        __syncthreads();
     }
-    __syncthreads();
+    // C'[gs][i] = sum_j L[i][j] c[gs][j]: thread (range r, coordinate i) over its j range
+    if (!full) {
+        const int nr = 256 / d;                          // d = 64 or 128
+        const int i = tid % d, r = tid / d;
+        const int len = (dout + nr - 1) / nr, j0 = min(r * len, dout), j1 = min(j0 + len, dout);
+        double acc[G];
+#pragma unroll
+        for (int gs = 0; gs < G; ++gs) acc[gs] = 0.0;
+        if (r < nr) {
+            int j = j0;
+            for (; j + 16 <= j1; j += 16) {
+                double lv[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) lv[u] = lh[(size_t)i * dout + j + u];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+#pragma unroll
+                    for (int gs = 0; gs < G; ++gs) acc[gs] += lv[u] * s_c[gs][j + u];
+            }
+            for (; j < j1; ++j) {
+                const double l = lh[(size_t)i * dout + j];
+#pragma unroll
+                for (int gs = 0; gs < G; ++gs) acc[gs] += l * s_c[gs][j];
+            }
+#pragma unroll
+            for (int gs = 0; gs < G; ++gs) s_part[(r * G + gs) * d + i] = acc[gs];
+        }
+        __syncthreads();
+        for (int o = tid; o < G * d; o += 256) {
+            const int gs = o / d, ii = o % d;
+            double c = 0.0;
+            for (int rr = 0; rr < nr; ++rr) c += s_part[(rr * G + gs) * d + ii];
+            s_s[gs][ii] = c;
+        }
+        __syncthreads();
+    }
     // one wave per centroid: stores and norms
-    for (int gs = w; gs < kFinG; gs += 4) {
+    for (int gs = w; gs < G; gs += 4) {
         const int g = g0 + gs;
         if (g >= groups) break;
         if (off != nullptr && off[(size_t)h * (groups + 1) + g + 1] == off[(size_t)h * (groups + 1) + g])
