@@ -92,6 +92,7 @@ struct sparsepr_ctx {
     int H = 0, N = 0, d = 0, Gk = 0, Gq = 0, rK = 0, Dq = 0, k = 0, P = 0, T = 0;
     int nblk = 0, maxu = 0, splits = 0, dense_units = 0, gmax = 0;
     bool raw = false;                  // SPARSEPR_F_RAW_KMEANS: identity metrics on both sides
+    bool svoo = false;                 // SPARSEPR_F_SVOO: alternating co-clustering
     int64_t weyl_a = 0;
 
     void* arena = nullptr;
@@ -200,8 +201,9 @@ int32_t validate(const sparsepr_params* p) {
     if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
     if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE |
-                     SPARSEPR_F_HOST_SOLVE))
+                     SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO))
         return SPARSEPR_ERR_INVALID_ARG;
+    if ((p->flags & SPARSEPR_F_RAW_KMEANS) && (p->flags & SPARSEPR_F_SVOO)) return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
 }
 
@@ -226,6 +228,7 @@ void derive(sparsepr_ctx& c) {
     c.Gq = p.q_groups;
     c.rK = p.key_rank;
     c.raw = (p.flags & SPARSEPR_F_RAW_KMEANS) != 0;
+    c.svoo = (p.flags & SPARSEPR_F_SVOO) != 0;
     c.Dq = c.d;                         // the query metric is used in full (d x d)
     c.k = routed_count(p.density, c.Gk);
     c.P = p.probes;
@@ -236,7 +239,8 @@ void derive(sparsepr_ctx& c) {
     c.splits = probe_splits(c.N, c.H, c.P);
     c.gmax = std::max(c.Gk, c.Gq);
     c.weyl_a = weyl_multiplier(c.N);
-    c.dev_eig = !c.raw && !(p.flags & SPARSEPR_F_HOST_SOLVE) && c.rK <= kEigMaxR && c.d <= kEigMaxN;
+    c.dev_eig = !c.raw && !c.svoo && !(p.flags & SPARSEPR_F_HOST_SOLVE) && c.rK <= kEigMaxR &&
+                c.d <= kEigMaxN;
 }
 
 void layout(sparsepr_ctx& c, Arena& a) {
@@ -273,7 +277,7 @@ void layout(sparsepr_ctx& c, Arena& a) {
         a.take(c.eig_tnorm, H);
     }
     a.take(c.mgap, H);
-    a.take(c.kc64, H * c.Gk * (c.raw ? d : (size_t)c.rK));
+    a.take(c.kc64, H * c.Gk * (c.raw || c.svoo ? d : (size_t)c.rK));
     if (c.raw) a.take(c.ident, H * d * d);
     a.take(c.qc64, H * c.Gq * d);
     a.take(c.kc2, H * c.Gk);
@@ -559,6 +563,42 @@ int32_t permute_keys_side(sparsepr_ctx* c, const bf16_t* k16, hipStream_t st) {
 }  // namespace
 
 namespace {
+// Comparison partitioner (SPARSEPR_F_SVOO): alternating rounds of one key assignment in the
+// affinity space of the current query centroids (metric C_Q^T C_Q / d, in c->mk) and one
+// query assignment in that of the updated key centroids (C_K^T C_K / d, in c->mq). Each
+// assignment is one round of the method's Lloyd machinery in full-metric mode (certified
+// MFMA screen, fp64 recheck, counting sort, fp64 raw means); the screening tables are rebuilt
+// from the raw means under each new metric, empty groups included (zero centroid).
+int32_t partition_svoo(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
+    const int H = c->H, N = c->N, d = c->d;
+    launch_seed_raw(k16, H, N, d, c->Gk, c->weyl_a, c->kraw, st);
+    launch_seed_raw(q16, H, N, d, c->Gq, c->weyl_a, c->qraw, st);
+    SPR_LAUNCHED(c, "co-clustering seeds");
+    for (int t = 0; t < c->T; ++t) {
+        int32_t* fk = c->flag_cnt + (size_t)t * H;
+        int32_t* fq = c->flag_cnt + (size_t)(c->T + t) * H;
+        // keys against the current query centroids
+        launch_gram_f64(c->qraw, H, c->Gq, d, 1.0 / d, c->mk, st);
+        launch_finish_all(c->kraw, H, d, c->mk, 0, c->Gk, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
+        launch_assign(k16, H, N, d, c->kcp, c->kcn2, c->kcpn, c->Gk, c->klab, fk, c->flag_list, st);
+        launch_recheck(k16, H, N, d, c->mk, 0, c->kc64, c->kc2, c->Gk, fk, c->flag_list, c->klab, st);
+        launch_counting_sort(c->klab, H, N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
+        launch_group_means(k16, H, N, d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, st);
+        SPR_LAUNCHED(c, "co-clustering keys");
+        // queries against the updated key centroids
+        launch_gram_f64(c->kraw, H, c->Gk, d, 1.0 / d, c->mq, st);
+        launch_finish_all(c->qraw, H, d, c->mq, 0, c->Gq, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
+        launch_assign(q16, H, N, d, c->qcp, c->qcn2, c->qcpn, c->Gq, c->qlab, fq, c->flag_list, st);
+        launch_recheck(q16, H, N, d, c->mq, 0, c->qc64, c->qc2, c->Gq, fq, c->flag_list, c->qlab, st);
+        launch_counting_sort(c->qlab, H, N, c->Gq, c->blkhist, c->blkoff, c->qperm, c->qoff, st);
+        launch_group_means(q16, H, N, d, c->qperm, c->qoff, c->Gq, c->qraw, nullptr, 0, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, st);
+        SPR_LAUNCHED(c, "co-clustering queries");
+    }
+    return permute_keys_side(c, k16, st);
+}
+
 // Keys: Lloyd in the M_K eigen-coordinates W (already in c->w64); K permuted on the side
 // stream; queries: the logit-profile metric M = C_K^T C_K / d (fp64 Gram of the raw key
 // centroids) used in full on the device, then Lloyd.
@@ -596,6 +636,14 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         launch_count_nonfinite(q16, H * c->N * d, 0, c->nonfinite, st);
         launch_count_nonfinite(k16, H * c->N * d, 0, c->nonfinite, st);
         SPR_LAUNCHED(c, "finite check (q, k)");
+    }
+    if (c->svoo) {
+        std::fill(c->h_mgap.begin(), c->h_mgap.end(), 0.0);      // no M_K
+        c->mgap_dev = false;
+        if ((rc = partition_svoo(c, q16, k16, st))) return rc;
+        mark(c, 1, st);
+        c->stage = kStagePartition;
+        return SPARSEPR_OK;
     }
     if (c->raw) {
         std::fill(c->h_mgap.begin(), c->h_mgap.end(), 0.0);      // no M_K
@@ -890,7 +938,8 @@ int32_t sparsepr_get_routing(sparsepr_ctx* c, int32_t* blocks, int32_t* probe_or
 int32_t sparsepr_get_metric(sparsepr_ctx* c, double* m_k, double* w, int32_t host, void* stream) {
     int32_t rc = enter(c, kStagePartition);
     if (rc) return rc;
-    if (c->raw) return fail(c, SPARSEPR_ERR_ORDER, "no key metric with SPARSEPR_F_RAW_KMEANS");
+    if (c->raw || c->svoo)
+        return fail(c, SPARSEPR_ERR_ORDER, "no key metric with SPARSEPR_F_RAW_KMEANS or SPARSEPR_F_SVOO");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = copy_out(c, m_k, c->mk, 8 * (size_t)c->H * c->d * c->d, host, st))) return rc;
     if ((rc = copy_out(c, w, c->w64, 8 * (size_t)c->H * c->d * c->rK, host, st))) return rc;

@@ -36,6 +36,12 @@ void launch_metric(const bf16_t* q, int heads, int n, int d, int n_sample, int64
                    hipStream_t st);
 // The metric is a factor l64 [d][dout] (metric = L L^T), or with dout == 0 the full
 // metric l64 [d][d]; c64 then holds the fp64 screening vectors M m ([groups][d]).
+// raw centroids = the rows at the first `groups` Weyl indices (no screening tables)
+void launch_seed_raw(const bf16_t* x, int heads, int n, int d, int groups, int64_t a, double* mean_raw,
+                     hipStream_t st);
+// screening tables of every centroid (empty groups included) from raw means and a metric
+void launch_finish_all(const double* mean_raw, int heads, int d, const double* l64, int dout, int groups,
+                       double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st);
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
                            float* cn2, float* cpn, double* c2_64, hipStream_t st);

@@ -260,6 +260,16 @@ __global__ __launch_bounds__(128) void k_seed(const bf16_t* __restrict__ x, int 
     if (j < d) mean_raw[((size_t)h * groups + g) * d + j] = (double)bf16_to_f32(x[((size_t)h * n + idx) * d + j]);
 }
 
+void launch_seed_raw(const bf16_t* x, int heads, int n, int d, int groups, int64_t a, double* mean_raw,
+                     hipStream_t st) {
+    hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, groups, a, mean_raw);
+}
+
+void launch_finish_all(const double* mean_raw, int heads, int d, const double* l64, int dout, int groups,
+                       double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st) {
+    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st);
+}
+
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
                            float* cn2, float* cpn, double* c2_64, hipStream_t st) {

@@ -5,7 +5,8 @@ the routed blocks keep, and how much support a query group needs compared with i
 that share one routing decision need the union of their keys, which can be much larger than
 any single row's support; the response-coupled partition is meant to lower the hard-drop
 error (the error of keeping only the routed blocks) and so what the probe fit must repair.
-The comparison partitioner clusters raw Q and K independently (SPARSEPR_F_RAW_KMEANS).
+Two comparison partitioners: independent raw Q and K k-means (SPARSEPR_F_RAW_KMEANS) and
+the alternating Q/K co-clustering of "Attention Sparsity is Input-Stable ..." (SPARSEPR_F_SVOO).
 
 Per partitioner, for the given config:
   * hard-drop error  |O_s - O_dense|_F / |O_dense|_F over all rows and heads (GPU);
@@ -19,7 +20,10 @@ Per partitioner, for the given config:
     the ratio of the two, and the routed union's size.
 
 python -m free_block_sparse_eigen_amd.diagnostics --config C3 [--groups 8] [--tau 0.9]
-prints one JSON object per partitioner.
+    [--partitioners response_coupled,raw_kmeans,svoo] [--probes-sweep 0,64,128,256,512]
+prints one JSON object per partitioner, then (with --probes-sweep) one per probe budget for
+the method's partition: the corrected error as the number of probe rows P varies (the
+hard-drop error does not depend on P).
 """
 from __future__ import annotations
 
@@ -123,6 +127,8 @@ def main() -> int:
     ap.add_argument("--config", default="C3")
     ap.add_argument("--groups", type=int, default=8)
     ap.add_argument("--tau", type=float, default=0.9)
+    ap.add_argument("--partitioners", default="response_coupled,raw_kmeans,svoo")
+    ap.add_argument("--probes-sweep", default="", help="comma-separated probe budgets")
     args = ap.parse_args()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     sys.path.insert(0, root)
@@ -132,7 +138,9 @@ def main() -> int:
     cfg = get_config(args.config)
     print(f"[diag] generating {args.config}: {cfg.heads} heads x {cfg.n}", file=sys.stderr, flush=True)
     q, k, v = make_inputs(cfg)
-    for name, flags in (("response_coupled", 0), ("raw_kmeans", spr.F_RAW_KMEANS)):
+    flag_of = {"response_coupled": 0, "raw_kmeans": spr.F_RAW_KMEANS, "svoo": spr.F_SVOO}
+    names = [x for x in args.partitioners.split(",") if x]
+    for name, flags in ((nm, flag_of[nm]) for nm in names):
         print(f"[diag] {name}: GPU call and dense", file=sys.stderr, flush=True)
         hard, corr, part, rout, stats, sweep = _gpu_errors(spr, torch, cfg, q, k, v, flags)
         print(f"[diag] {name}: supports on {args.groups} groups of head 0", file=sys.stderr, flush=True)
@@ -148,6 +156,15 @@ def main() -> int:
                "sample_routed_keys": float(np.mean([s["routed_keys"] for s in sup])),
                "groups": sup}
         print(json.dumps(out), flush=True)
+    for p in (int(x) for x in args.probes_sweep.split(",") if x):
+        pc = cfg.with_settings(probes=p, corr_rank=min(cfg.settings.corr_rank, max(p, 1)))
+        print(f"[diag] probe budget {p}: GPU call and dense", file=sys.stderr, flush=True)
+        hard, corr, _, _, stats, sweep = _gpu_errors(spr, torch, pc, q, k, v, 0)
+        print(json.dumps({"partitioner": "response_coupled", "config": args.config, "probes": p,
+                          "corr_rank": pc.settings.corr_rank,
+                          "probe_row_fraction": p / cfg.n, "hard_drop_rel_fro": hard,
+                          "corrected_rel_fro": corr, "corrected_rel_fro_by_lambda": sweep}),
+              flush=True)
     return 0
 
 

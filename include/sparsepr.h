@@ -71,6 +71,18 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        rows (the independent Q/K clustering of cluster-based
                                        sparse attention), with the same seeds, rounds, routing,
                                        probes and correction; no M_K and no host round trip */
+#define SPARSEPR_F_SVOO 16u         /* comparison partitioner, not the method: the online
+                                       bidirectional co-clustering of "Attention Sparsity is
+                                       Input-Stable ..." (papernotes.org, online co-clustering
+                                       item). kmeans_iters alternating rounds: keys are assigned
+                                       in the affinity space of the current query centroids
+                                       (metric C_Q^T C_Q / d on raw keys), their raw means
+                                       updated, then queries in the affinity space of the new key
+                                       centroids (C_K^T C_K / d); seeds are the rows at the
+                                       first G Weyl indices, an empty block's centroid is the zero
+                                       vector. Same routing, probes and correction; no M_K and no
+                                       host round trip. Not combinable with
+                                       SPARSEPR_F_RAW_KMEANS (SPARSEPR_ERR_INVALID_ARG). */
 #define SPARSEPR_F_HOST_SOLVE 8u    /* solve the M_K eigenproblem on the host (fp64, the partition
                                        stage then synchronises its stream once) instead of on
                                        the device; also used whenever key_rank > 64 */
@@ -234,7 +246,7 @@ int32_t sparsepr_get_routing(sparsepr_ctx* ctx, int32_t* blocks, int32_t* probe_
 /* The key metric M_K = Q_s^T Q_s / M_s (fp64 [H][d][d]) and the key coordinates' map
  * W = U_r diag(sqrt(lambda_r)) (fp64 [H][d][r_K]) of the last partition (section 2A). Only
  * W W^T is defined (eigenvector signs and rotations inside a repeated eigenvalue are free).
- * Not available with SPARSEPR_F_RAW_KMEANS (SPARSEPR_ERR_ORDER). */
+ * Not available with SPARSEPR_F_RAW_KMEANS or SPARSEPR_F_SVOO (SPARSEPR_ERR_ORDER). */
 int32_t sparsepr_get_metric(sparsepr_ctx* ctx, double* m_k, double* w, int32_t host, void* stream);
 
 /* Raw fp64 centroids: keys [H][G_k][d], queries [H][G_q][d] (zero for an empty group). */

@@ -177,6 +177,35 @@ def raw_partition(q: np.ndarray, k: np.ndarray, kv_groups: int, q_groups: int,
     return Partition(key_labels, q_labels, ck, cq, np.zeros(0))
 
 
+def svoo_partition(q: np.ndarray, k: np.ndarray, kv_groups: int, q_groups: int,
+                   iters: int) -> Partition:
+    """Comparison partitioner, not the method: the online bidirectional co-clustering of
+    [SVOO] (its online co-clustering item). Each round has two steps. Step A takes the
+    current query centroids as anchors: every key gets its affinity vector against them
+    (p(k)_i = k . c^Q_i / sqrt(d)) and joins the key block whose centre, the mean affinity
+    vector of the block's current members under the same anchors, is nearest. The raw key
+    centroids are then updated. Step B does the same for the queries against the updated
+    key centroids.
+    Readings (the item gives neither seeds nor round count, nor what an empty block holds):
+    the seeds of both sides are the rows at the first G Weyl indices (as the method's
+    Lloyd), `iters` rounds, ties to the lowest index, and an empty block's raw centroid is
+    the zero vector (as the method's key centroids for the query profiles). By linearity the
+    mean affinity of a block's members is the affinity of their raw mean."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    n = q.shape[0]
+    cq = q[weyl_indices(n, q_groups)].copy()
+    ck = k[weyl_indices(n, kv_groups)].copy()
+    key_labels = np.zeros(n, np.int32)
+    q_labels = np.zeros(n, np.int32)
+    for _ in range(iters):
+        key_labels = assign(query_profiles(k, cq), query_profiles(ck, cq))     # step A
+        ck = group_means(k, key_labels, kv_groups)
+        q_labels = assign(query_profiles(q, ck), query_profiles(cq, ck))       # step B
+        cq = group_means(q, q_labels, q_groups)
+    return Partition(key_labels, q_labels, ck, cq, np.zeros(0))
+
+
 # ------------------------------------------------------------------ layout ---
 def group_major(labels: np.ndarray, groups: int):
     """Contiguous group-major layout [PR 2C]: a stable sort of token indices by
@@ -377,17 +406,20 @@ class HeadResult:
 def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, key_rank: int,
                 kv_groups: int, q_groups: int, kmeans_iters: int, density: float, probes: int,
                 ridge_lambda: float, corr_rank: int,
-                part: Optional[Partition] = None, raw_kmeans: bool = False) -> HeadResult:
+                part: Optional[Partition] = None, raw_kmeans: bool = False,
+                svoo: bool = False) -> HeadResult:
     """One head of one SparsePR call, stage by stage:
     partition -> group-major layout -> routing + probes -> sparse attention and
     exact probe rows -> probe fit -> correction -> original order.
-    `part` injects a partition (labels) instead of computing it; `raw_kmeans` uses the
-    comparison partitioner (raw_partition) instead of the method's."""
+    `part` injects a partition (labels) instead of computing it; `raw_kmeans` and `svoo`
+    use a comparison partitioner (raw_partition, svoo_partition) instead of the method's."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     if part is None and raw_kmeans:
         part = raw_partition(q, k, kv_groups, q_groups, kmeans_iters)
+    elif part is None and svoo:
+        part = svoo_partition(q, k, kv_groups, q_groups, kmeans_iters)
     elif part is None:
         part = partition(q, k, n_sample, key_rank, kv_groups, q_groups, kmeans_iters)
     ck = group_means(k, part.key_labels, kv_groups)
@@ -412,12 +444,13 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
 
 
 def oracle_call(q: np.ndarray, k: np.ndarray, v: np.ndarray, settings,
-                heads: Optional[Sequence[int]] = None, raw_kmeans: bool = False) -> List[HeadResult]:
+                heads: Optional[Sequence[int]] = None, raw_kmeans: bool = False,
+                svoo: bool = False) -> List[HeadResult]:
     """All heads of one call; `settings` carries the SparsePR parameters by name."""
     kw = dict(n_sample=settings.n_sample, key_rank=settings.key_rank,
               kv_groups=settings.kv_groups, q_groups=settings.q_groups,
               kmeans_iters=settings.kmeans_iters, density=settings.density,
               probes=settings.probes, ridge_lambda=settings.ridge_lambda,
-              corr_rank=settings.corr_rank, raw_kmeans=raw_kmeans)
+              corr_rank=settings.corr_rank, raw_kmeans=raw_kmeans, svoo=svoo)
     hs = range(q.shape[0]) if heads is None else heads
     return [oracle_head(q[h], k[h], v[h], **kw) for h in hs]

@@ -266,3 +266,14 @@ def test_noalloc_dense_rejects_shapes_and_pointers_before_any_device_use():
     assert f(1100, 2000000, 128, None, None, None, None, None) == 2      # heads * n >= 2^31
     assert f(1, 2097152, 64, None, None, None, None, None) == 1          # largest n: pointers
     assert b"null or misaligned" in lib.sparsepr_last_error(None)
+
+
+def test_svoo_and_raw_kmeans_flags_are_exclusive():
+    """The two comparison partitioners cannot be combined; each alone is accepted."""
+    kw = dict(kv_groups=16, q_groups=16, density=0.25, probes=8, corr_rank=4)
+    both = spr.make_params(1, 1024, 64, spr.BF16, flags=spr.F_SVOO | spr.F_RAW_KMEANS, **kw)
+    assert spr.sparsepr_validate(both) == 1
+    for f in (spr.F_SVOO, spr.F_RAW_KMEANS):
+        assert spr.sparsepr_validate(spr.make_params(1, 1024, 64, spr.BF16, flags=f, **kw)) == 0
+    # the co-clustering context has no M_K eigensolve but the same workspace otherwise
+    assert spr.sparsepr_workspace_bytes(spr.make_params(1, 1024, 64, spr.BF16, flags=spr.F_SVOO, **kw)) > 0

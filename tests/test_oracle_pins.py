@@ -531,6 +531,85 @@ def test_partition_is_the_brute_force_composition(seed):
     lab_wrong = brute.lloyd(_tolist(wrong), orc.weyl_indices(n, gq).tolist(), 3)
     assert lab_wrong != qlab
 
+def _brute_svoo(q, k, gk, gq, iters):
+    """[SVOO] online co-clustering recomputed with loops, in the pages' terms: affinity
+    vectors against the other side's centroids, each block centre the mean affinity vector of
+    its current members (before the first round, the seed row alone), nearest centre with the
+    lowest index on ties; keys first, then queries against the updated key centroids."""
+    n, d = len(q), len(q[0])
+    rd = math.sqrt(d)
+
+    def aff(x, anchors):
+        return [sum(x[c] * a[c] for c in range(d)) / rd for a in anchors]
+
+    def mean(rows):
+        return [sum(r[c] for r in rows) / len(rows) for c in range(d)] if rows else [0.0] * d
+
+    def nearest(p, centres):
+        best, bi = None, 0
+        for g, ctr in enumerate(centres):
+            dist = sum((p[i] - ctr[i]) ** 2 for i in range(len(p)))
+            if best is None or dist < best:
+                best, bi = dist, g
+        return bi
+
+    kmem = [[k[i]] for i in orc.weyl_indices(n, gk).tolist()]     # members of each key block
+    qmem = [[q[i]] for i in orc.weyl_indices(n, gq).tolist()]
+    cq = [mean(m) for m in qmem]
+    klab = qlab = None
+    for _ in range(iters):
+        centres = [[sum(col) / len(m) for col in zip(*[aff(r, cq) for r in m])] if m else [0.0] * gq
+                   for m in kmem]
+        klab = [nearest(aff(k[t], cq), centres) for t in range(n)]
+        kmem = [[k[t] for t in range(n) if klab[t] == g] for g in range(gk)]
+        ck = [mean(m) for m in kmem]
+        centres = [[sum(col) / len(m) for col in zip(*[aff(r, ck) for r in m])] if m else [0.0] * gk
+                   for m in qmem]
+        qlab = [nearest(aff(q[t], ck), centres) for t in range(n)]
+        qmem = [[q[t] for t in range(n) if qlab[t] == g] for g in range(gq)]
+        cq = [mean(m) for m in qmem]
+    return klab, qlab
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_svoo_partition_is_the_brute_force_co_clustering(seed):
+    """svoo_partition against the loop form of [SVOO]'s alternating steps. The inputs are
+    chosen so that independent raw k-means (raw_partition) and the method's partition both
+    give other labels, and so does running the query step first."""
+    rng = np.random.default_rng(700 + seed)
+    n, d, gk, gq, iters = 48, 6, 5, 4, 3
+    base = rng.standard_normal((6, d))
+    q = (base[rng.integers(0, 6, size=n)] + 0.8 * rng.standard_normal((n, d))).round(2)
+    k = (base[rng.integers(0, 6, size=n)] * 1.5 + 0.6 * rng.standard_normal((n, d))).round(2)
+    part = orc.svoo_partition(q, k, gk, gq, iters)
+    klab, qlab = _brute_svoo(_tolist(q), _tolist(k), gk, gq, iters)
+    assert part.key_labels.tolist() == klab
+    assert part.q_labels.tolist() == qlab
+    assert np.array_equal(part.key_centroids, orc.group_means(k, part.key_labels, gk))
+    raw = orc.raw_partition(q, k, gk, gq, iters)
+    assert (raw.key_labels.tolist(), raw.q_labels.tolist()) != (klab, qlab)
+    meth = orc.partition(q, k, 12, 2, gk, gq, iters)
+    assert (meth.key_labels.tolist(), meth.q_labels.tolist()) != (klab, qlab)
+    # queries first (step B before step A) gives other labels too
+    swapped = orc.svoo_partition(k, q, gq, gk, iters)
+    assert (swapped.q_labels.tolist(), swapped.key_labels.tolist()) != (klab, qlab)
+
+
+def test_svoo_partition_round_is_the_metric_form():
+    """One step A is nearest-centroid assignment of raw keys under the metric
+    C_Q^T C_Q / d (the form the library's kernels use): |(k - c) C_Q^T|^2 / d."""
+    rng = np.random.default_rng(77)
+    n, d, gk, gq = 64, 8, 6, 5
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d)) * 2
+    part = orc.svoo_partition(q, k, gk, gq, 1)
+    cq = q[orc.weyl_indices(n, gq)]
+    ck = k[orc.weyl_indices(n, gk)]
+    m = cq.T @ cq / d
+    dist = np.array([[(k[t] - ck[g]) @ m @ (k[t] - ck[g]) for g in range(gk)] for t in range(n)])
+    assert np.array_equal(part.key_labels, np.argmin(dist, axis=1))
+
+
 # -------------------------------------------------------------- full call ---
 def _c1(**kw):
     cfg = get_config("C1")
