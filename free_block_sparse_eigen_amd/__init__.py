@@ -37,6 +37,7 @@ EXPORTS = [
     "sparsepr_get_centroids", "sparsepr_get_sparse_out", "sparsepr_get_probes",
     "sparsepr_get_fit", "sparsepr_get_stats", "sparsepr_set_partition", "sparsepr_routed_count",
     "sparsepr_get_gaps", "sparsepr_get_metric", "sparsepr_dense_attn_noalloc",
+    "sparsepr_reuse_route", "sparsepr_attention_reuse",
     "sparsepr_host_sym_eig_top", "sparsepr_host_key_projection",
     "sparsepr_host_probe_fit",
 ]
@@ -105,6 +106,8 @@ _sigs = {
     "sparsepr_get_gaps": (_I, [_ctx, _P, _P, _I, _P]),
     "sparsepr_get_metric": (_I, [_ctx, _P, _P, _I, _P]),
     "sparsepr_dense_attn_noalloc": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
+    "sparsepr_reuse_route": (_I, [_ctx, _P, _P, _P, _P]),
+    "sparsepr_attention_reuse": (_I, [_ctx, _P, _P, _P, _P, _P]),
     "sparsepr_host_sym_eig_top": (_I, [_I, _P, _I, _P, _P]),
     "sparsepr_host_key_projection": (_I, [_I, _P, _I, _P]),
     "sparsepr_host_probe_fit": (_I, [_I, _I, _P, _P, ctypes.c_double, _I, _P, _P]),
@@ -259,6 +262,16 @@ class SparsePR:
         o = torch.empty_like(q) if o is None else o
         self._c(lib.sparsepr_attention(self._ctx, _tptr(q), _tptr(k), _tptr(v), _tptr(o),
                                        _stream_ptr(stream)))
+        return o
+
+    def sparsepr_reuse_route(self, q, k, v, stream=None):
+        self._c(lib.sparsepr_reuse_route(self._ctx, _tptr(q), _tptr(k), _tptr(v), _stream_ptr(stream)))
+
+    def sparsepr_attention_reuse(self, q, k, v, o=None, stream=None):
+        import torch
+        o = torch.empty_like(q) if o is None else o
+        self._c(lib.sparsepr_attention_reuse(self._ctx, _tptr(q), _tptr(k), _tptr(v), _tptr(o),
+                                             _stream_ptr(stream)))
         return o
 
     def sparsepr_dense_attn(self, q, k, v, o=None, stream=None):

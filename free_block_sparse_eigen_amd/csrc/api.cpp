@@ -93,6 +93,7 @@ struct sparsepr_ctx {
     int nblk = 0, maxu = 0, splits = 0, dense_units = 0, gmax = 0;
     bool raw = false;                  // SPARSEPR_F_RAW_KMEANS: identity metrics on both sides
     bool svoo = false;                 // SPARSEPR_F_SVOO: alternating co-clustering
+    bool have_route = false;           // a partition and routing exist (sparsepr_reuse_route)
     int64_t weyl_a = 0;
 
     void* arena = nullptr;
@@ -750,6 +751,41 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     SPR_LAUNCHED(c, "probes/units");
     mark(c, 3, st);
     c->stage = kStageRoute;
+    c->have_route = true;
+    return SPARSEPR_OK;
+}
+
+int32_t sparsepr_reuse_route(sparsepr_ctx* c, const void* q, const void* k, const void* v, void* stream) {
+    int32_t rc = enter(c, 0);
+    if (rc) return rc;
+    if (!c->have_route) return fail(c, SPARSEPR_ERR_ORDER, "no earlier partition and routing to reuse");
+    if (!q || !k || !v || !aligned16(q) || !aligned16(k) || !aligned16(v))
+        return fail(c, SPARSEPR_ERR_INVALID_ARG, "null or misaligned q/k/v");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    begin_call(c);
+    mark(c, 0, st);
+    mark(c, 1, st);                                     // no partition in this call
+    mark(c, 2, st);
+    const size_t HND = (size_t)c->H * c->N * c->d;
+    const bf16_t* q16 = as_bf16(c, q, c->qb, st);
+    const bf16_t* k16 = as_bf16(c, k, c->kb, st);
+    const bf16_t* v16 = as_bf16(c, v, c->vb, st);
+    if (c->check_finite) {
+        launch_fill_i64(reinterpret_cast<int64_t*>(c->nonfinite), 0, 2, st);
+        launch_count_nonfinite(q16, HND, 0, c->nonfinite, st);
+        launch_count_nonfinite(k16, HND, 0, c->nonfinite, st);
+        launch_count_nonfinite(v16, HND, 0, c->nonfinite, st);
+        SPR_LAUNCHED(c, "finite check (q, k, v)");
+    }
+    c->q_src = q16;
+    c->v_src = v16;
+    // the new K and V through the kept key permutation; blocks, probes and work units stay
+    if ((rc = permute_keys_side(c, k16, st))) return rc;
+    launch_permute_v16(v16, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, st);
+    SPR_LAUNCHED(c, "permute");
+    mark(c, 3, st);
+    c->stage = kStageRoute;
     return SPARSEPR_OK;
 }
 
@@ -870,6 +906,15 @@ int32_t sparsepr_attention(sparsepr_ctx* c, const void* q, const void* k, const 
                            void* stream) {
     int32_t rc = sparsepr_partition(c, q, k, stream);
     if (!rc) rc = sparsepr_route(c, q, k, v, stream);
+    if (!rc) rc = sparsepr_sparse_attn(c, stream);
+    if (!rc) rc = sparsepr_probe_fit(c, stream);
+    if (!rc) rc = sparsepr_correct(c, o, stream);
+    return rc;
+}
+
+int32_t sparsepr_attention_reuse(sparsepr_ctx* c, const void* q, const void* k, const void* v, void* o,
+                                 void* stream) {
+    int32_t rc = sparsepr_reuse_route(c, q, k, v, stream);
     if (!rc) rc = sparsepr_sparse_attn(c, stream);
     if (!rc) rc = sparsepr_probe_fit(c, stream);
     if (!rc) rc = sparsepr_correct(c, o, stream);

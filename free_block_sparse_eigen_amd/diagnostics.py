@@ -24,6 +24,14 @@ python -m free_block_sparse_eigen_amd.diagnostics --config C3 [--groups 8] [--ta
 prints one JSON object per partitioner, then (with --probes-sweep) one per probe budget for
 the method's partition: the corrected error as the number of probe rows P varies (the
 hard-drop error does not depend on P).
+
+    [--stride-sweep 1,2,4,8 --steps 8 --theta 0.1]
+reuse experiment (not the method): over `steps` successive calls of one layer
+(make_step_inputs: the fine detail of every token turned by theta radians per step), the
+partition and routing are recomputed every S-th call and reused in between
+(sparsepr_attention_reuse). One JSON object per stride: the hard-drop and corrected errors
+against dense at every step, and the amortised call time (t_full + (S - 1) t_reuse) / S
+from separately timed full and reused calls.
 """
 from __future__ import annotations
 
@@ -82,6 +90,66 @@ def _gpu_errors(spr, torch, cfg, q, k, v, flags):
     return hard, corr, part, rout, stats, sweep
 
 
+def _stride_sweep(spr, torch, cfg, strides, steps, theta):
+    from synthetic import make_step_inputs
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dt = spr.BF16 if cfg.dtype == "bf16" else spr.F32
+    inputs = []
+    for s in range(steps):
+        print(f"[diag] step {s} inputs", file=sys.stderr, flush=True)
+        inputs.append(tuple(torch.from_numpy(x).to(tdt).to(dev).contiguous()
+                            for x in make_step_inputs(cfg, s, theta)))
+    ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, cfg.settings)
+    od = torch.empty_like(inputs[0][0])
+    dense = torch.empty_like(od)
+    # timings: full and reused calls on step 0, medians of event-timed calls
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=7):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        return float(np.median(ts))
+
+    q, k, v = inputs[0]
+    t_full = timed(lambda: ctx.sparsepr_attention(q, k, v, od))
+    t_reuse = timed(lambda: ctx.sparsepr_attention_reuse(q, k, v, od))
+    out = []
+    for S in strides:
+        hard, corr = [], []
+        for s in range(steps):
+            q, k, v = inputs[s]
+            if s % S == 0:
+                ctx.sparsepr_attention(q, k, v, od)
+            else:
+                ctx.sparsepr_attention_reuse(q, k, v, od)
+            ctx.sparsepr_dense_attn(q, k, v, dense)
+            torch.cuda.synchronize()
+            part = ctx.sparsepr_get_partition()
+            o_s_perm = torch.from_numpy(ctx.sparsepr_get_sparse_out()).to(dev)
+            qperm = torch.from_numpy(part["q_perm"].astype(np.int64)).to(dev)
+            o_s = torch.empty_like(o_s_perm)
+            for h in range(cfg.heads):
+                o_s[h].index_copy_(0, qperm[h], o_s_perm[h])
+            ref = dense.float()
+            den = torch.linalg.vector_norm(ref).item()
+            hard.append(torch.linalg.vector_norm(o_s - ref).item() / den)
+            corr.append(torch.linalg.vector_norm(od.float() - ref).item() / den)
+        out.append({"stride": S, "steps": steps, "theta": theta, "t_full_ms": t_full,
+                    "t_reuse_ms": t_reuse, "amortised_ms": (t_full + (S - 1) * t_reuse) / S,
+                    "hard_drop_rel_fro": hard, "corrected_rel_fro": corr,
+                    "mean_hard_drop": float(np.mean(hard)), "mean_corrected": float(np.mean(corr))})
+    del ctx
+    return out
+
+
 def _support_stats(q, k, part, rout, groups, tau, d):
     """Host fp64 on head 0: routed mass and supports for `groups` evenly spaced non-empty
     query groups."""
@@ -129,6 +197,9 @@ def main() -> int:
     ap.add_argument("--tau", type=float, default=0.9)
     ap.add_argument("--partitioners", default="response_coupled,raw_kmeans,svoo")
     ap.add_argument("--probes-sweep", default="", help="comma-separated probe budgets")
+    ap.add_argument("--stride-sweep", default="", help="comma-separated reuse strides")
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--theta", type=float, default=0.1)
     args = ap.parse_args()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     sys.path.insert(0, root)
@@ -137,6 +208,12 @@ def main() -> int:
     from synthetic import get_config, make_inputs
     cfg = get_config(args.config)
     print(f"[diag] generating {args.config}: {cfg.heads} heads x {cfg.n}", file=sys.stderr, flush=True)
+    strides = [int(x) for x in args.stride_sweep.split(",") if x]
+    if strides:
+        for rec in _stride_sweep(spr, torch, cfg, strides, args.steps, args.theta):
+            rec.update({"partitioner": "response_coupled", "config": args.config})
+            print(json.dumps(rec), flush=True)
+        return 0
     q, k, v = make_inputs(cfg)
     flag_of = {"response_coupled": 0, "raw_kmeans": spr.F_RAW_KMEANS, "svoo": spr.F_SVOO}
     names = [x for x in args.partitioners.split(",") if x]

@@ -204,11 +204,29 @@ int32_t sparsepr_probe_fit(sparsepr_ctx* ctx, void* stream);
  * get O_s + b' + O_s B', probe rows their exact dense output. */
 int32_t sparsepr_correct(sparsepr_ctx* ctx, void* o, void* stream);
 
+/* Reuse of the last partition and routing, an experiment and not part of the method (the
+ * SparsePR summary, section 2B, says the method itself uses no temporal reuse; the framerc.cn
+ * page's mask_update_stride updates the sparse mask only every few denoising steps). Takes
+ * new q, k, v of the context's shape and treats them as the 2C/2B input of a new call that
+ * keeps the previous call's labels, group-major permutations, block lists, probe rows and
+ * work units: K and V are permuted through the kept key permutation (K on the side stream,
+ * V into scaled fp16 as in sparsepr_route) and Q rows are gathered through the kept query
+ * permutation. Leaves the context ready for sparsepr_sparse_attn; the same lifetime rules
+ * for q, k and v as sparsepr_route apply. SPARSEPR_ERR_ORDER if no sparsepr_route (or
+ * sparsepr_set_partition + sparsepr_route) has completed on this context. Asynchronous. */
+int32_t sparsepr_reuse_route(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
+                             void* stream);
+
 /* ---- convenience and baseline ---- */
 
 /* All five stages in order. */
 int32_t sparsepr_attention(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
                            void* o, void* stream);
+
+/* sparsepr_reuse_route, then the sparse attention, probe fit and correction: one call on
+ * the previous call's partition and routing (the reuse experiment above). */
+int32_t sparsepr_attention_reuse(sparsepr_ctx* ctx, const void* q, const void* k, const void* v,
+                                 void* o, void* stream);
 
 /* Dense softmax(Q K^T / sqrt(d)) V with this library's attention kernel (one group
  * holding every key); uses the context's shapes and workspace, no other stage state. */

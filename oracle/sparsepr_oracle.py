@@ -407,15 +407,21 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
                 kv_groups: int, q_groups: int, kmeans_iters: int, density: float, probes: int,
                 ridge_lambda: float, corr_rank: int,
                 part: Optional[Partition] = None, raw_kmeans: bool = False,
-                svoo: bool = False) -> HeadResult:
+                svoo: bool = False, reuse: Optional["HeadResult"] = None) -> HeadResult:
     """One head of one SparsePR call, stage by stage:
     partition -> group-major layout -> routing + probes -> sparse attention and
     exact probe rows -> probe fit -> correction -> original order.
     `part` injects a partition (labels) instead of computing it; `raw_kmeans` and `svoo`
-    use a comparison partitioner (raw_partition, svoo_partition) instead of the method's."""
+    use a comparison partitioner (raw_partition, svoo_partition) instead of the method's.
+    `reuse` (an experiment, not the method: [PR 2B] uses no temporal reuse, [BLOG]'s
+    mask_update_stride refreshes the mask only every few steps) keeps an earlier call's
+    labels, block lists and probe rows for these new inputs; everything after the routing
+    is computed from the new q, k, v."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    if reuse is not None:
+        part = Partition(reuse.key_labels, reuse.q_labels, None, None, np.zeros(0))
     if part is None and raw_kmeans:
         part = raw_partition(q, k, kv_groups, q_groups, kmeans_iters)
     elif part is None and svoo:
@@ -427,8 +433,11 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
     kperm, koff = group_major(part.key_labels, kv_groups)
     qperm, qoff = group_major(part.q_labels, q_groups)
     kk = routed_count(density, kv_groups)
-    blocks = route(cq, ck, np.diff(koff), kk)
-    ppos = probe_positions(np.diff(qoff), probes)
+    if reuse is not None:
+        blocks, ppos = reuse.blocks, reuse.probe_pos
+    else:
+        blocks = route(cq, ck, np.diff(koff), kk)
+        ppos = probe_positions(np.diff(qoff), probes)
     qp, kp, vp = q[qperm], k[kperm], v[kperm]
     o_s = sparse_attention(qp, kp, vp, qoff, koff, blocks)
     o_d = dense_attention(qp[ppos], kp, vp) if len(ppos) else np.zeros((0, v.shape[1]))

@@ -5,9 +5,9 @@ of the attention method's arithmetic, so both the GPU path's tests and the CPU
 oracle can draw from it without sharing any of the method's code.
 """
 from .configs import CONFIGS, SparsePRSettings, WorkloadConfig, get_config
-from .generator import bf16_round, make_head, make_inputs, token_grid
+from .generator import bf16_round, make_head, make_inputs, make_step_inputs, token_grid
 
 __all__ = [
     "CONFIGS", "SparsePRSettings", "WorkloadConfig", "get_config",
-    "bf16_round", "make_head", "make_inputs", "token_grid",
+    "bf16_round", "make_head", "make_inputs", "make_step_inputs", "token_grid",
 ]

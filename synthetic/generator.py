@@ -25,6 +25,7 @@ import numpy as np
 from .configs import WorkloadConfig
 
 SEED_BASE = 20260820
+STEP_SEED_BASE = 20261203        # the second noise draw of make_step_inputs
 NOISE_STD = 0.3
 DRIFT_STD = 0.05
 N_SCALE_PAIRS = 4096
@@ -74,9 +75,20 @@ def _component_map(rng: np.random.Generator, cfg: WorkloadConfig) -> np.ndarray:
 
 
 def make_head(cfg: WorkloadConfig, rng: np.random.Generator,
-              logit_std: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """One head's (q, k, v), each [N, d] float32 holding bf16-representable values."""
+              logit_std: float, step_mix=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One head's (q, k, v), each [N, d] float32 holding bf16-representable values.
+    step_mix = (alt_rng, c, s): every token's noise becomes c n + s n' with n' drawn from
+    alt_rng (the same structure with the fine detail turned by an angle; c = 1, s = 0 is
+    the plain head)."""
     d, n = cfg.d, cfg.n
+
+    def noise():
+        z = rng.standard_normal((n, d))
+        if step_mix is not None:
+            alt, c, s_ = step_mix
+            z = c * z + s_ * alt.standard_normal((n, d))
+        return NOISE_STD * z
+
     comp = _component_map(rng, cfg)
     mu = rng.standard_normal((cfg.components, d))
     nu = rng.standard_normal((cfg.components, d))
@@ -86,10 +98,10 @@ def make_head(cfg: WorkloadConfig, rng: np.random.Generator,
         mean_qk = mu[comp] + t[:, None] * delta[comp]
     else:
         mean_qk = mu[comp]
-    q = mean_qk + NOISE_STD * rng.standard_normal((n, d))
-    k = mean_qk + NOISE_STD * rng.standard_normal((n, d))
+    q = mean_qk + noise()
+    k = mean_qk + noise()
     del mean_qk
-    v = nu[comp] + NOISE_STD * rng.standard_normal((n, d))
+    v = nu[comp] + noise()
     rot_qk = _haar_rotation(rng, d)
     rot_v = _haar_rotation(rng, d)
     q = q @ rot_qk
@@ -100,6 +112,28 @@ def make_head(cfg: WorkloadConfig, rng: np.random.Generator,
     sigma_hat = np.std(np.sum(q[i] * k[j], axis=1) / np.sqrt(d))
     scale = np.sqrt(logit_std / sigma_hat)
     return bf16_round(q * scale), bf16_round(k * scale), bf16_round(v)
+
+
+def make_step_inputs(cfg: WorkloadConfig, step: int, theta: float = 0.1,
+                     heads: Optional[Iterable[int]] = None
+                     ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Inputs of successive calls of one layer (a stand-in for successive denoising steps):
+    the same components, means, rotations and layout as make_inputs, with each token's noise
+    turned by theta * step radians towards an independent draw. Step 0 is make_inputs."""
+    root = np.random.Generator(np.random.PCG64(SEED_BASE + cfg.index))
+    alt_root = np.random.Generator(np.random.PCG64(STEP_SEED_BASE + cfg.index))
+    children = root.spawn(cfg.heads)
+    alts = alt_root.spawn(cfg.heads)
+    c, s = float(np.cos(theta * step)), float(np.sin(theta * step))
+    sel = list(range(cfg.heads)) if heads is None else list(heads)
+    shape = (len(sel), cfg.n, cfg.d)
+    q = np.empty(shape, np.float32)
+    k = np.empty(shape, np.float32)
+    v = np.empty(shape, np.float32)
+    for out_h, h in enumerate(sel):
+        q[out_h], k[out_h], v[out_h] = make_head(cfg, children[h], cfg.head_logit_std(h),
+                                                 step_mix=(alts[h], c, s))
+    return q, k, v
 
 
 def make_inputs(cfg: WorkloadConfig, heads: Optional[Iterable[int]] = None

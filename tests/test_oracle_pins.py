@@ -657,3 +657,35 @@ def test_call_c1_structure():
     # probe rows output their exact dense value
     dense = orc.dense_attention(q, k, v)
     assert np.allclose(r.o[r.probe_orig], dense[r.probe_orig], atol=1e-12)
+
+
+# ------------------------------------------------------------ reuse experiment ---
+def test_reuse_on_the_same_inputs_is_the_same_call():
+    """oracle_head(reuse=r) on the inputs that produced r reproduces r field by field."""
+    q, k, v, a = _c1()
+    r = orc.oracle_head(q, k, v, **a)
+    again = orc.oracle_head(q, k, v, reuse=r, **a)
+    for f in ("key_labels", "q_labels", "key_perm", "q_perm", "key_off", "q_off", "blocks",
+              "probe_pos", "probe_orig", "o_sparse", "x", "y", "b_mat", "b_vec", "o"):
+        assert np.array_equal(getattr(again, f), getattr(r, f)), f
+
+
+def test_reuse_keeps_the_layout_but_attends_with_the_new_inputs():
+    """With every block pair kept (rho = 1) the sparse output of a reused call is plain dense
+    attention of the NEW inputs, whatever partition was kept; the kept labels, blocks and
+    probe rows are the earlier call's."""
+    q, k, v, a = _c1(density=1.0)
+    r0 = orc.oracle_head(q, k, v, **a)
+    rng = np.random.default_rng(91)
+    q1 = q + 0.5 * rng.standard_normal(q.shape)
+    k1 = k + 0.5 * rng.standard_normal(k.shape)
+    v1 = v[rng.permutation(v.shape[0])]
+    r1 = orc.oracle_head(q1, k1, v1, reuse=r0, **a)
+    assert np.array_equal(r1.key_labels, r0.key_labels) and np.array_equal(r1.blocks, r0.blocks)
+    assert np.array_equal(r1.probe_orig, r0.probe_orig)
+    dense = orc.dense_attention(q1, k1, v1)
+    back = np.empty_like(r1.o_sparse)
+    back[r1.q_perm] = r1.o_sparse
+    assert np.allclose(back, dense, rtol=0, atol=1e-12)
+    # and the new partition of these inputs differs from the kept one (the test separates them)
+    assert not np.array_equal(orc.oracle_head(q1, k1, v1, **a).key_labels, r0.key_labels)
