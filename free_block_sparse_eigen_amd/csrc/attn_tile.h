@@ -132,6 +132,31 @@ __device__ inline uint4 vt_frag(const uint4* __restrict__ sv, int db, int s4, in
     return make_uint4(ua.x, ua.y, ub.x, ub.y);
 }
 
+// The same fragment from byte offsets computed once per kernel: o0, o1 locate this lane's
+// two 8-byte reads for column block db at slice 0 (vt_offsets); slice s4 lies 16 keys further
+// on, which keeps each key's low four bits and so its swizzle, a constant byte offset that
+// the LDS instruction takes as its immediate.
+template <int D>
+__device__ inline void vt_offsets(int lane, int (&o0)[D / 32], int (&o1)[D / 32]) {
+    constexpr int CH = D / 8;
+    const int g = lane >> 4, j = lane & 15;
+    const int key0 = 4 * (g >> 1) + (j >> 2), key1 = key0 + 8;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+        o0[db] = 2 * (key0 * D + (((col >> 3) ^ swz<CH>(key0)) << 3) + (col & 7));
+        o1[db] = 2 * (key1 * D + (((col >> 3) ^ swz<CH>(key1)) << 3) + (col & 7));
+    }
+}
+template <int D>
+__device__ inline uint4 vt_frag_at(const uint4* __restrict__ sv, int o0, int o1, int s4) {
+    const char* base = reinterpret_cast<const char*>(sv) + s4 * 16 * D * 2;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o0));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o1));
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    return make_uint4(ua.x, ua.y, ub.x, ub.y);
+}
+
 // Lanes l and l ^ 32 hold the two halves of one query column.
 __device__ inline float pair_max(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

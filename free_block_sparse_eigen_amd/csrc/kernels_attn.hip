@@ -183,6 +183,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
 
     const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
     const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
+    // this lane's fragment offsets inside a tile, computed once: K row (lane & 31) at each
+    // depth step (row + 32 has the same swizzle, a constant offset), V^T per column block
+    int kfo[D / 16], vo0[DB], vo1[DB];
+    {
+        const int rl = lane & 31, sw = swz<TL::CH>(rl);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) kfo[kk] = rl * TL::CH + ((2 * kk + half) ^ sw);
+        vt_offsets<D>(lane, vo0, vo1);
+    }
     fill_phys(0, 0);
     __syncthreads();
     TL::issue(rk, rv, s_phys[0], s_k0, s_v0, w, lane);
@@ -194,31 +203,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
         if (t + 1 < ntiles) TL::issue(rk, rv, s_phys[buf ^ 1], nk, nv, w, lane);
         if (active) {
             // S^T for both 32-key blocks: two independent accumulation chains, the K
-            // fragments read one depth step ahead of their MFMAs
-            const int rl = lane & 31, sw = swz<TL::CH>(rl);     // same swizzle for row + 32
-            const uint4* k0p = sk + rl * TL::CH;
-            const uint4* k1p = sk + (32 + rl) * TL::CH;
+            // fragments read two depth steps ahead of their MFMAs (a ring of three)
+            constexpr int KA = 2;
+            const uint4* k1s = sk + 32 * TL::CH;                // rows 32..63
             f32x16 s0 = {}, s1 = {};
-            uint4 a0 = k0p[half ^ sw], a1 = k1p[half ^ sw];
+            uint4 a0[KA + 1], a1[KA + 1];
+#pragma unroll
+            for (int kk = 0; kk < KA; ++kk) {
+                a0[kk] = sk[kfo[kk]];
+                a1[kk] = k1s[kfo[kk]];
+            }
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                uint4 n0 = a0, n1 = a1;
-                if (kk + 1 < D / 16) {
-                    const int c = (2 * (kk + 1) + half) ^ sw;
-                    n0 = k0p[c];
-                    n1 = k1p[c];
+                if (kk + KA < D / 16) {
+                    a0[(kk + KA) % (KA + 1)] = sk[kfo[kk + KA]];
+                    a1[(kk + KA) % (KA + 1)] = k1s[kfo[kk + KA]];
                 }
-                s0 = mfma32x32x16(a0, qf[kk], s0);
-                s1 = mfma32x32x16(a1, qf[kk], s1);
-                a0 = n0;
-                a1 = n1;
+                s0 = mfma32x32x16(a0[kk % (KA + 1)], qf[kk], s0);
+                s1 = mfma32x32x16(a1[kk % (KA + 1)], qf[kk], s1);
+                __builtin_amdgcn_sched_barrier(0);          // keep the reads KA steps ahead
             }
             // V^T fragments of keys 0..31, read now so that the softmax hides their latency
             uint4 vf[2][DB];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) vf[sl][db] = vt_frag<D>(sv, db, sl, lane);
+                for (int db = 0; db < DB; ++db) vf[sl][db] = vt_frag_at<D>(sv, vo0[db], vo1[db], sl);
             const int nvk = U - t * KT;
             if (nvk < KT) {
 #pragma unroll
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     o[db] = mfma_pv<VH>(vf[sl][db], pb[sl], o[db]);
-                    vf[sl][db] = vt_frag<D>(sv, db, sl + 2, lane);
+                    vf[sl][db] = vt_frag_at<D>(sv, vo0[db], vo1[db], sl + 2);
                 }
 #pragma unroll
             for (int sl = 2; sl < 4; ++sl) {
