@@ -30,14 +30,15 @@
  *     the probe rows (not for the sparse kernel) to do so; the partition stage does the
  *     same only with SPARSEPR_F_HOST_SOLVE.
  *   - The caller owns Q/K/V/O and keeps them alive until the stream work is done.
- *     The context owns every intermediate; nothing is kept between calls except
- *     what the inspection getters read back.
+ *     The context owns every intermediate. Between calls it keeps only what the
+ *     inspection getters read back and the partition and routing that
+ *     sparsepr_reuse_route reuses.
  *   - Every function returns a sparsepr_status; nothing throws or aborts across the
  *     ABI. Arguments are validated before anything is enqueued. A HIP error returns
  *     SPARSEPR_ERR_HIP and poisons the context (destroy it). Stages must run in order
- *     partition -> route -> sparse_attn -> probe_fit -> correct (else
- *     SPARSEPR_ERR_ORDER). A context is bound to one device, is not thread-safe, and
- *     overlapping calls on one context race.
+ *     partition -> route -> sparse_attn -> probe_fit -> correct, or reuse_route in place
+ *     of the first two (else SPARSEPR_ERR_ORDER). A context is bound to one device, is
+ *     not thread-safe, and overlapping calls on one context race.
  *   - Results are bitwise deterministic for identical inputs and parameters.
  */
 #ifndef SPARSEPR_H
@@ -165,7 +166,8 @@ const char* sparsepr_last_error(const sparsepr_ctx* ctx);
 /* ---- the five stages (section 2 of the method summary) ---- */
 
 /* 2A. Reads q, k. Asynchronous: M_K, its leading eigenpairs (fp64: Householder
- * tridiagonalisation, bisection, inverse iteration) and both k-means run on the device.
+ * tridiagonalisation, bisection, twisted-factorisation eigenvectors, inverse iteration only
+ * inside clusters of near-equal eigenvalues) and both k-means run on the device.
  * With SPARSEPR_F_HOST_SOLVE, or key_rank > 64, the eigensolve runs on the host instead and
  * the stage synchronises `stream` once. The query side uses the logit-profile metric
  * C_K^T C_K / d in full.
