@@ -159,6 +159,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--host-solve", action="store_true",
                     help="eigensolve of the key metric on the host (SPARSEPR_F_HOST_SOLVE)")
+    ap.add_argument("--serial-partition", action="store_true",
+                    help="every head's partition on one stream (SPARSEPR_F_SERIAL_PARTITION)")
     ap.add_argument("--oracle-threads", type=int, default=None,
                     help="limit the oracle leg's BLAS threads (1: single-threaded baseline)")
     ap.add_argument("--oracle-all-heads", type=int, default=0, metavar="WORKERS",
@@ -191,7 +193,8 @@ def main() -> int:
     qd, kd, vd = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v))
     od = torch.empty_like(qd)
     dt = spr.BF16 if cfg.dtype == "bf16" else spr.F32
-    base_flags = spr.F_HOST_SOLVE if args.host_solve else 0
+    base_flags = ((spr.F_HOST_SOLVE if args.host_solve else 0) |
+                  (spr.F_SERIAL_PARTITION if args.serial_partition else 0))
     ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, st, flags=base_flags)
     stream = torch.cuda.current_stream()
 
@@ -304,6 +307,7 @@ def main() -> int:
         "stage_ms": stage,
         "stage_timing": "second context with stage events; the timed calls above ran without",
         "metric_eigensolve": "host" if args.host_solve else "device",
+        "partition_streams": 1 if args.serial_partition or cfg.heads < 2 else 2,
         "recheck_points": stats["recheck_points"],
         "dense": dense,
         "roofline": {"kernel": "k_vbsa (variable-block-sparse attention)", "bound": "mfma",

@@ -152,6 +152,12 @@ struct sparsepr_ctx {
     hipEvent_t ev_kperm = nullptr;    // K permuted on the side stream
     bool kperm_recorded = false;      // ev_kperm has been recorded
     hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
+    // the partition's second half of the heads runs on its own stream (split)
+    bool split = false;
+    hipStream_t part2 = nullptr;
+    hipEvent_t ev_fork = nullptr;     // the second half may start
+    hipEvent_t ev_kdone2 = nullptr;   // the second half's keys are partitioned
+    hipEvent_t ev_join = nullptr;     // the second half is done
 
     int stage = 0;
     bool poisoned = false;
@@ -202,7 +208,7 @@ int32_t validate(const sparsepr_params* p) {
     if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
     if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE |
-                     SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO))
+                     SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO | SPARSEPR_F_SERIAL_PARTITION))
         return SPARSEPR_ERR_INVALID_ARG;
     if ((p->flags & SPARSEPR_F_RAW_KMEANS) && (p->flags & SPARSEPR_F_SVOO)) return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
@@ -242,6 +248,7 @@ void derive(sparsepr_ctx& c) {
     c.weyl_a = weyl_multiplier(c.N);
     c.dev_eig = !c.raw && !c.svoo && !(p.flags & SPARSEPR_F_HOST_SOLVE) && c.rK <= kEigMaxR &&
                 c.d <= kEigMaxN;
+    c.split = c.H >= 2 && !(p.flags & SPARSEPR_F_SERIAL_PARTITION);
 }
 
 void layout(sparsepr_ctx& c, Arena& a) {
@@ -384,21 +391,37 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 // counting sort -> fp64 means and centroids. The metric is the factor l64 [d][dim], or
 // with dim == 0 the full metric l64 [d][d]. After the last round `sorted`/`off` are the
 // stable group-major permutation and `mean_raw` the raw group means (zero if empty).
-int32_t lloyd(sparsepr_ctx* c, const bf16_t* x, int dim, const double* l64, int groups,
+int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const double* l64, int groups,
               int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
               double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st) {
-    launch_seed_centroids(x, c->H, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
+    // heads h0 .. h0 + hh - 1: every buffer is head-major, so the slice starts h0 heads in
+    const size_t h = h0, N = c->N, d = c->d, cdim = dim > 0 ? dim : c->d;
+    x += h * N * d;
+    l64 += h * d * cdim;
+    labels += h * N;
+    sorted += h * N;
+    off += h * (groups + 1);
+    mean_raw += h * groups * d;
+    c64 += h * groups * cdim;
+    cpart += h * 2 * groups * d;
+    cn2 += h * groups;
+    cpn += h * groups;
+    c2_64 += h * groups;
+    int32_t* flag_list = c->flag_list + h * N;
+    int32_t* blkhist = c->blkhist + h * c->nblk * groups;
+    int32_t* blkoff = c->blkoff + h * c->nblk * groups;
+    launch_seed_centroids(x, hh, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
                           cpn, c2_64, st);
     SPR_LAUNCHED(c, "seed centroids");
     for (int t = 0; t < c->T; ++t) {
-        int32_t* fc = flags + (size_t)t * c->H;
-        launch_assign(x, c->H, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, c->flag_list, st);
+        int32_t* fc = flags + (size_t)t * c->H + h;
+        launch_assign(x, hh, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, flag_list, st);
         SPR_LAUNCHED(c, "assign");
-        launch_recheck(x, c->H, c->N, c->d, l64, dim, c64, c2_64, groups, fc, c->flag_list, labels, st);
+        launch_recheck(x, hh, c->N, c->d, l64, dim, c64, c2_64, groups, fc, flag_list, labels, st);
         SPR_LAUNCHED(c, "recheck");
-        launch_counting_sort(labels, c->H, c->N, groups, c->blkhist, c->blkoff, sorted, off, st);
+        launch_counting_sort(labels, hh, c->N, groups, blkhist, blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");
-        launch_group_means(x, c->H, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
+        launch_group_means(x, hh, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
                            cn2, cpn, c2_64, st);
         SPR_LAUNCHED(c, "group means");
     }
@@ -502,6 +525,12 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             (e = hipEventCreateWithFlags(&c->ev_kperm, hipEventDisableTiming)) != hipSuccess ||
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
+        if (c->split &&
+            ((e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming)) != hipSuccess ||
+             (e = hipEventCreateWithFlags(&c->ev_kdone2, hipEventDisableTiming)) != hipSuccess ||
+             (e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming)) != hipSuccess ||
+             (e = hipStreamCreateWithFlags(&c->part2, hipStreamNonBlocking)) != hipSuccess))
+            return create_fail(c, SPARSEPR_ERR_HIP, "event / partition stream", e);
     }
     if (c->raw) {
         const size_t H = c->H, d = c->d;
@@ -539,6 +568,10 @@ void sparsepr_destroy(sparsepr_ctx* c) {
     if (c->ev_kdone) (void)hipEventDestroy(c->ev_kdone);
     if (c->ev_kperm) (void)hipEventDestroy(c->ev_kperm);
     if (c->side) (void)hipStreamDestroy(c->side);
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    if (c->ev_kdone2) (void)hipEventDestroy(c->ev_kdone2);
+    if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+    if (c->part2) (void)hipStreamDestroy(c->part2);
     if (c->h_fit) (void)hipHostFree(c->h_fit);
     if (c->h_mkp) (void)hipHostFree(c->h_mkp);
     if (c->h_wp) (void)hipHostFree(c->h_wp);
@@ -600,19 +633,48 @@ int32_t partition_svoo(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hi
     return permute_keys_side(c, k16, st);
 }
 
-// Keys: Lloyd in the M_K eigen-coordinates W (already in c->w64); K permuted on the side
-// stream; queries: the logit-profile metric M = C_K^T C_K / d (fp64 Gram of the raw key
-// centroids) used in full on the device, then Lloyd.
-int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
-    int32_t rc = lloyd(c, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
-                       c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
+// Keys: Lloyd in the M_K eigen-coordinates W (already in c->w64); queries: the logit-profile
+// metric M = C_K^T C_K / d (fp64 Gram of the raw key centroids) used in full on the device,
+// then Lloyd. Heads h0 .. h0 + hh - 1, all on stream s.
+int32_t partition_heads(sparsepr_ctx* c, int h0, int hh, const bf16_t* q16, const bf16_t* k16,
+                        hipStream_t s, hipEvent_t keys_done) {
+    const size_t h = h0, d = c->d;
+    int32_t rc = lloyd(c, h0, hh, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff,
+                       c->kraw, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, s);
     if (rc) return rc;
-    if ((rc = permute_keys_side(c, k16, st))) return rc;
-    launch_gram_f64(c->kraw, c->H, c->Gk, c->d, 1.0 / c->d, c->mq, st);
+    SPR_HIP(c, hipEventRecord(keys_done, s));
+    launch_gram_f64(c->kraw + h * c->Gk * d, hh, c->Gk, c->d, 1.0 / c->d, c->mq + h * d * d, s);
     SPR_LAUNCHED(c, "query metric");
-    rc = lloyd(c, q16, 0, c->mq, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * c->H, c->qperm, c->qoff,
-               c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
-    if (rc) return rc;
+    return lloyd(c, h0, hh, q16, 0, c->mq, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * c->H, c->qperm,
+                 c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, s);
+}
+
+// The per-head steps run as two halves of the heads on two streams (st and part2), so that
+// the many small, latency-bound launches of one half (recheck, sort, centroid finish)
+// overlap the other half's work; with SPARSEPR_F_SERIAL_PARTITION (or one head) all heads run
+// on st. K is permuted on the side stream once every head's keys are partitioned,
+// overlapping the query side.
+int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
+    int32_t rc;
+    if (!c->split) {
+        if ((rc = partition_heads(c, 0, c->H, q16, k16, st, c->ev_kdone))) return rc;
+        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
+    } else {
+        const int ha = (c->H + 1) / 2, hb = c->H - ha;
+        SPR_HIP(c, hipEventRecord(c->ev_fork, st));
+        SPR_HIP(c, hipStreamWaitEvent(c->part2, c->ev_fork, 0));
+        if ((rc = partition_heads(c, 0, ha, q16, k16, st, c->ev_kdone))) return rc;
+        if ((rc = partition_heads(c, ha, hb, q16, k16, c->part2, c->ev_kdone2))) return rc;
+        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
+        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone2, 0));
+        SPR_HIP(c, hipEventRecord(c->ev_join, c->part2));
+        SPR_HIP(c, hipStreamWaitEvent(st, c->ev_join, 0));
+    }
+    // K into group-major order on the side stream; the sparse stage waits for ev_kperm
+    launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);
+    SPR_LAUNCHED(c, "permute K");
+    SPR_HIP(c, hipEventRecord(c->ev_kperm, c->side));
+    c->kperm_recorded = true;
     mark(c, 1, st);
     c->stage = kStagePartition;
     return SPARSEPR_OK;
@@ -651,11 +713,11 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         c->mgap_dev = false;
         // comparison partitioner: plain Euclidean k-means of the raw key rows, then of the
         // raw query rows (full-metric path with M = I: screening vector = mean)
-        rc = lloyd(c, k16, 0, c->ident, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
+        rc = lloyd(c, 0, c->H, k16, 0, c->ident, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff, c->kraw,
                    c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
         if (rc) return rc;
         if ((rc = permute_keys_side(c, k16, st))) return rc;
-        rc = lloyd(c, q16, 0, c->ident, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm,
+        rc = lloyd(c, 0, c->H, q16, 0, c->ident, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * H, c->qperm,
                    c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
         if (rc) return rc;
         mark(c, 1, st);

@@ -293,13 +293,26 @@ void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const doubl
 // otherwise the point is queued for the fp64 recheck, which also settles exact ties by
 // the lowest index. Each lane tracks only the best and runner-up scores.
 //
+// The scores are compared with the accumulator slot (0..15) of their centroid written
+// into their four low mantissa bits, so one min tracks value and slot together. That
+// moves each score by at most 15 ulp <= 2^-19 |s~|, and the test above gets a further
+// 2^-18 (|s~_2nd| + |s~_best|) for the two compared scores.
+//
 // Centroid tiles of 64 (hi and lo parts, 16-byte chunk c of centroid row r at c ^ swz(r))
 // sit in LDS; a wave scores 64 points (two MFMA column blocks of 32) against them. Two
 // kernels share the per-wave steps: k_assign_res keeps every centroid of a head resident
 // in LDS (2 G D 2 bytes <= 128 KB) and lets each wave walk its points with no barriers;
-// k_assign (larger G) streams the tiles, double-buffered. Padding centroids score +inf.
+// k_assign (larger G) streams the tiles, double-buffered. Padding centroids score
+// kPadScore, a finite value no real score reaches (finite, so the slot bits can be
+// written into it).
 constexpr int kAssignTG = 64;
 constexpr int kAssignResBytes = 128 * 1024;
+constexpr float kPadScore = 3.0e38f;
+
+// a score with accumulator slot r (0..15) in its four low mantissa bits
+__device__ __attribute__((always_inline)) inline float with_slot(float v, int r) {
+    return __uint_as_float((__float_as_uint(v) & ~15u) | (uint32_t)r);
+}
 
 template <int D>
 struct AssignWave {
@@ -396,30 +409,42 @@ struct AssignWave {
         for (int sub = 0; sub < TG / 32; ++sub) {
             const int gb = t * TG + 32 * sub;
             if (gb >= groups) break;
-            // with best <= second, the new runner-up is the median of (best, v, second);
-            // a new best inside this sub-tile is recorded as its accumulator slot r (an
-            // inline constant) and turned into the centroid index once afterwards
-            int code[2] = {-1, -1};
+            scores(acc[sub], gb, s_cn2, half);
+        }
+    }
+
+    // one 32-centroid sub-tile's scores (column blocks pb = 0, 1) into best / runner-up:
+    // with best <= second, the new runner-up is the median of (best, v, second); the
+    // slot-marked best changes only when this sub-tile holds a new best, whose slot then
+    // gives its centroid index
+    __device__ __attribute__((always_inline)) void scores(const f32x16 (&acc)[2], int gb,
+                                                          const float* s_cn2, int half) {
+        const float b0[2] = {best[0], best[1]};
+        // med3 with -inf is the min; an fminf would first quiet its slot-marked operand
+        // (one more instruction per score), so -inf comes from an opaque scalar move
+        uint32_t ninf_bits;
+        asm("s_mov_b32 %0, 0xff800000" : "=s"(ninf_bits));
+        const float ninf = __uint_as_float(ninf_bits);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float c2 = s_cn2[gb + 8 * (r >> 2) + 4 * half + (r & 3)];
+        for (int r = 0; r < 16; ++r) {
+            const float c2 = s_cn2[gb + 8 * (r >> 2) + 4 * half + (r & 3)];
 #pragma unroll
-                for (int pb = 0; pb < 2; ++pb) {
-                    const float v = fmaf(-2.f, acc[sub][pb][r], c2);
-                    second[pb] = __builtin_amdgcn_fmed3f(best[pb], v, second[pb]);
-                    code[pb] = (v < best[pb]) ? r : code[pb];
-                    best[pb] = fminf(best[pb], v);
-                }
+            for (int pb = 0; pb < 2; ++pb) {
+                const float v = with_slot(fmaf(-2.f, acc[pb][r], c2), r);
+                second[pb] = __builtin_amdgcn_fmed3f(best[pb], v, second[pb]);
+                best[pb] = __builtin_amdgcn_fmed3f(best[pb], v, ninf);     // the min
             }
+        }
 #pragma unroll
-            for (int pb = 0; pb < 2; ++pb)
-                if (code[pb] >= 0) bg[pb] = gb + 8 * (code[pb] >> 2) + 4 * half + (code[pb] & 3);
+        for (int pb = 0; pb < 2; ++pb) {
+            const int r = (int)(__float_as_uint(best[pb]) & 15u);
+            if (best[pb] != b0[pb]) bg[pb] = gb + 8 * (r >> 2) + 4 * half + (r & 3);
         }
     }
 
     // labels, and the points whose label is not certified appended to the recheck queue
-    __device__ __attribute__((always_inline)) void finish(int n, int h, int p_base, int lane,
-                                                          float c2max, float cpmax,
+    __device__ __attribute__((always_inline)) void finish(int n, int h, int groups, int p_base,
+                                                          int lane, float c2max, float cpmax,
                                                           int32_t* __restrict__ labels,
                                                           int32_t* __restrict__ flag_count,
                                                           int32_t* __restrict__ flag_list) {
@@ -437,11 +462,13 @@ struct AssignWave {
                 gsel = og;
             }
             const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
-            const float bound = 2.4f * A + 2.4f * kU * (fabsf(s2) + fabsf(b)) + 1e-30f;
+            const float bound = 2.4f * A + (2.4f * kU + 3.814697265625e-06f) * (fabsf(s2) + fabsf(b)) + 1e-30f;
             const int pt = p_base + 32 * pb + lane;
             if (lane < 32 && pt < n) {
-                labels[(size_t)h * n + pt] = gsel;
-                if (!(s2 - b > bound)) {
+                // a padding centroid (only if no real score is finite) is never certified
+                const bool real = gsel < groups;
+                labels[(size_t)h * n + pt] = real ? gsel : 0;
+                if (!(s2 - b > bound) || !real) {
                     const int slot = atomicAdd(&flag_count[h], 1);
                     flag_list[(size_t)h * n + slot] = pt;
                 }
@@ -460,7 +487,7 @@ __device__ inline void assign_norms(const float* __restrict__ cn2, const float* 
     constexpr int NW = NT / 64;
     float c2m = 0.f, cpm = 0.f;
     for (int g = tid; g < ntiles * kAssignTG; g += NT) {
-        float c2 = INFINITY;
+        float c2 = kPadScore;
         if (g < groups) {
             c2 = cn2[(size_t)h * groups + g];
             c2m = fmaxf(c2m, c2);
@@ -529,7 +556,7 @@ __global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict_
             const int p_base = (k - h * ipw) * 64;
             aw.load(x, n, h, p_base, lane);
             for (int t = 0; t < ntiles; ++t) aw.tile(t, s_c + t * SLOTS, groups, s_cn2, lane);
-            aw.finish(n, h, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
+            aw.finish(n, h, groups, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
         }
         it = seg_end;
     }
@@ -583,7 +610,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
-    aw.finish(n, h, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
+    aw.finish(n, h, groups, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
 }
 
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,

@@ -87,6 +87,12 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
 #define SPARSEPR_F_HOST_SOLVE 8u    /* solve the M_K eigenproblem on the host (fp64, the partition
                                        stage then synchronises its stream once) instead of on
                                        the device; also used whenever key_rank > 64 */
+#define SPARSEPR_F_SERIAL_PARTITION 32u  /* run the partition's per-head steps for all heads on the
+                                       caller's stream. By default (H >= 2) the first and the
+                                       second half of the heads run on two streams that the
+                                       partition stage forks from and joins back into the caller's
+                                       stream, so that their small launches overlap; the results
+                                       are the same either way. */
 #define SPARSEPR_F_CHECK_FINITE 4u  /* count non-finite values of q and k (partition), v (route)
                                        and o (correct) on the device; read the counts with
                                        sparsepr_get_stats. The stages stay asynchronous and do not

@@ -277,3 +277,12 @@ def test_svoo_and_raw_kmeans_flags_are_exclusive():
         assert spr.sparsepr_validate(spr.make_params(1, 1024, 64, spr.BF16, flags=f, **kw)) == 0
     # the co-clustering context has no M_K eigensolve but the same workspace otherwise
     assert spr.sparsepr_workspace_bytes(spr.make_params(1, 1024, 64, spr.BF16, flags=spr.F_SVOO, **kw)) > 0
+
+
+def test_serial_partition_flag_is_accepted_alone_and_combined():
+    """SPARSEPR_F_SERIAL_PARTITION only changes which streams the partition runs on."""
+    kw = dict(kv_groups=16, q_groups=16, density=0.25, probes=8, corr_rank=4)
+    for f in (spr.F_SERIAL_PARTITION, spr.F_SERIAL_PARTITION | spr.F_STAGE_TIMING,
+              spr.F_SERIAL_PARTITION | spr.F_HOST_SOLVE | spr.F_CHECK_FINITE):
+        assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=f, **kw)) == 0
+    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=64, **kw)) == 1

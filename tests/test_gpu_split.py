@@ -1,0 +1,62 @@
+"""The partition's two-stream head split against the serial partition.
+
+By default the partition stage runs the first and the second half of the heads on two
+streams (SPARSEPR_F_SERIAL_PARTITION runs them all on the caller's stream). Every step is
+per head, so both must give identical bits everywhere: labels, permutations, offsets,
+centroids, block lists, probes, the sparse and the final outputs. An odd head count makes
+the halves unequal, and one head of the second half is also checked against the oracle so
+that the second half's buffer offsets are pinned to something outside the library. A
+second call on the same context must repeat the first.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+from synthetic import get_config, make_inputs
+from tests.gpu_common import run_gpu_call, say
+
+pytestmark = pytest.mark.gpu
+
+HEADS = [0, 3, 7]          # halves of 2 and 1 heads
+KEYS = ("key_labels", "q_labels", "key_perm", "q_perm", "key_off", "q_off", "blocks",
+        "probe_orig", "o_sparse", "x", "y", "b_mat", "b_vec", "key_centroids", "q_centroids", "o")
+
+
+@pytest.fixture(scope="module")
+def spr():
+    import torch
+    assert torch.cuda.is_available()
+    import free_block_sparse_eigen_amd as mod
+    return mod
+
+
+def _same(a, b, what):
+    for key in KEYS:
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), f"{what}: {key} differs"
+
+
+@pytest.mark.timeout(600)
+def test_split_partition_matches_serial_and_oracle(spr):
+    cfg = get_config("C2")
+    say(f"C2 split partition: generating heads {HEADS}, N={cfg.n}")
+    q, k, v = make_inputs(cfg, heads=HEADS)
+    dt = spr.BF16 if cfg.dtype == "bf16" else spr.F32
+    split = spr.SparsePR.from_settings(len(HEADS), cfg.n, cfg.d, dt, cfg.settings)
+    serial = spr.SparsePR.from_settings(len(HEADS), cfg.n, cfg.d, dt, cfg.settings,
+                                        flags=spr.F_SERIAL_PARTITION)
+    say("C2 split partition: split call 1")
+    g1 = run_gpu_call(split, q, k, v, cfg.dtype)
+    say("C2 split partition: split call 2")
+    g2 = run_gpu_call(split, q, k, v, cfg.dtype)
+    say("C2 split partition: serial call")
+    gs = run_gpu_call(serial, q, k, v, cfg.dtype)
+    split.close()
+    serial.close()
+    _same(g1, gs, "split vs serial")
+    _same(g1, g2, "second split call")
+    i = len(HEADS) - 1                          # the second half's only head
+    say(f"C2 split partition: oracle head {HEADS[i]}")
+    ref = orc.oracle_call(q[i:i + 1], k[i:i + 1], v[i:i + 1], cfg.settings)[0]
+    assert np.array_equal(g1["key_labels"][i], ref.key_labels), "second half: key labels"
+    assert np.array_equal(g1["q_labels"][i], ref.q_labels), "second half: query labels"
+    assert np.array_equal(g1["blocks"][i], ref.blocks), "second half: blocks"
