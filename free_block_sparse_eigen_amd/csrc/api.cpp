@@ -158,6 +158,11 @@ struct sparsepr_ctx {
     hipEvent_t ev_fork = nullptr;     // the second half may start
     hipEvent_t ev_kdone2 = nullptr;   // the second half's keys are partitioned
     hipEvent_t ev_join = nullptr;     // the second half is done
+    // sparsepr_attention hands V to the partition stage (bf16 only), which takes its per-head
+    // magnitudes on the side stream beside the eigensolve and permutes it there right after
+    // K; the route stage skips its own V permute for that V
+    const bf16_t* v_pre = nullptr;
+    bool v_pre_done = false;
 
     int stage = 0;
     bool poisoned = false;
@@ -673,6 +678,11 @@ int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf1
     // K into group-major order on the side stream; the sparse stage waits for ev_kperm
     launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);
     SPR_LAUNCHED(c, "permute K");
+    if (c->v_pre) {              // its magnitudes were taken during the eigensolve
+        launch_permute_f16(c->v_pre, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, c->side);
+        SPR_LAUNCHED(c, "permute V");
+        c->v_pre_done = true;
+    }
     SPR_HIP(c, hipEventRecord(c->ev_kperm, c->side));
     c->kperm_recorded = true;
     mark(c, 1, st);
@@ -723,6 +733,15 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         mark(c, 1, st);
         c->stage = kStagePartition;
         return SPARSEPR_OK;
+    }
+    if (c->v_pre) {
+        // V (handed over by sparsepr_attention) needs the key permutation only for its
+        // permute: its per-head magnitudes run on the side stream beside the metric and its
+        // eigensolve, after the previous call's readers on this stream
+        SPR_HIP(c, hipEventRecord(c->ev_kdone, st));
+        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
+        launch_absmax_v(c->v_pre, c->H, c->N, c->d, c->vmax, c->side);
+        SPR_LAUNCHED(c, "V magnitudes");
     }
     // M_K and its leading eigenvectors (fp64; on the device unless SPARSEPR_F_HOST_SOLVE)
     launch_metric(q16, c->H, c->N, c->d, c->p.n_sample, c->weyl_a, c->mk, st);
@@ -800,8 +819,12 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
         launch_count_nonfinite(v16, (size_t)c->H * c->N * c->d, 0, c->nonfinite, st);
         SPR_LAUNCHED(c, "finite check (v)");
     }
-    launch_permute_v16(v16, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, st);
-    SPR_LAUNCHED(c, "permute");
+    if (!(c->v_pre_done && c->v_pre == v16)) {
+        launch_permute_v16(v16, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, st);
+        SPR_LAUNCHED(c, "permute");
+    }
+    c->v_pre = nullptr;
+    c->v_pre_done = false;
     launch_fill_i64(c->pairs, 0, c->H, st);
     launch_route(c->qraw, c->kraw, c->kraw_t, c->qoff, c->koff, c->H, c->Gq, c->Gk, c->d, c->k,
                  c->blocks, c->ucount, c->pairs, st);
@@ -966,8 +989,14 @@ int32_t sparsepr_correct(sparsepr_ctx* c, void* o, void* stream) {
 
 int32_t sparsepr_attention(sparsepr_ctx* c, const void* q, const void* k, const void* v, void* o,
                            void* stream) {
+    // bf16 V needs no conversion, so the partition stage can permute it beside the query side
+    if (c && c->p.dtype == SPARSEPR_BF16 && v && aligned16(v)) c->v_pre = static_cast<const bf16_t*>(v);
     int32_t rc = sparsepr_partition(c, q, k, stream);
     if (!rc) rc = sparsepr_route(c, q, k, v, stream);
+    if (c) {
+        c->v_pre = nullptr;
+        c->v_pre_done = false;
+    }
     if (!rc) rc = sparsepr_sparse_attn(c, stream);
     if (!rc) rc = sparsepr_probe_fit(c, stream);
     if (!rc) rc = sparsepr_correct(c, o, stream);

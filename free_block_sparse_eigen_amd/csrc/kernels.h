@@ -65,6 +65,10 @@ void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, in
 // each head's largest |v| as bf16 magnitude bits
 void launch_permute_v16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
                         uint32_t* vmax, uint16_t* dst, hipStream_t st);
+// its two halves: the per-head magnitude bits, then the scaled permute that reads them
+void launch_absmax_v(const bf16_t* src, int heads, int n, int d, uint32_t* vmax, hipStream_t st);
+void launch_permute_f16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
+                        const uint32_t* vmax, uint16_t* dst, hipStream_t st);
 // ck_t: scratch [heads][d][gk] for the coordinate-major copy of ck
 void launch_route(const double* cq, const double* ck, double* ck_t, const int32_t* qoff,
                   const int32_t* koff, int heads, int gq, int gk, int d, int k, int32_t* blocks,

@@ -75,15 +75,24 @@ __global__ __launch_bounds__(256) void k_permute_f16(const bf16_t* __restrict__ 
     *reinterpret_cast<uint4*>(dst + ((size_t)h * n + row) * d + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-void launch_permute_v16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
-                        uint32_t* vmax, uint16_t* dst, hipStream_t st) {
+void launch_absmax_v(const bf16_t* src, int heads, int n, int d, uint32_t* vmax, hipStream_t st) {
     launch_fill_i32(reinterpret_cast<int32_t*>(vmax), 0, heads, st);
     const size_t per_head = (size_t)n * d;
     const unsigned blocks = (unsigned)std::min<size_t>((per_head / 8 + 255) / 256, 256);
     hipLaunchKernelGGL(k_absmax_bits, dim3(blocks, heads), dim3(256), 0, st, src, per_head, vmax);
+}
+
+void launch_permute_f16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
+                        const uint32_t* vmax, uint16_t* dst, hipStream_t st) {
     const size_t total = (size_t)n * (d / 8);
     hipLaunchKernelGGL(k_permute_f16, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, st,
                        src, perm, n, d, vmax, dst);
+}
+
+void launch_permute_v16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
+                        uint32_t* vmax, uint16_t* dst, hipStream_t st) {
+    launch_absmax_v(src, heads, n, d, vmax, st);
+    launch_permute_f16(src, perm, heads, n, d, vmax, dst, st);
 }
 
 // Coordinate-major copy [heads][d][g] of row-major fp64 rows [heads][g][d].

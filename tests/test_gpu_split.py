@@ -6,7 +6,9 @@ per head, so both must give identical bits everywhere: labels, permutations, off
 centroids, block lists, probes, the sparse and the final outputs. An odd head count makes
 the halves unequal, and one head of the second half is also checked against the oracle so
 that the second half's buffer offsets are pinned to something outside the library. A
-second call on the same context must repeat the first.
+second call on the same context must repeat the first, and the one-call entry
+(sparsepr_attention, which permutes bf16 V on the side stream during the partition) must
+repeat the stage-by-stage call.
 """
 import numpy as np
 import pytest
@@ -30,6 +32,25 @@ def spr():
     return mod
 
 
+def _one_call(ctx, q, k, v, dtype):
+    """sparsepr_attention, which hands bf16 V to the partition stage, read back like
+    run_gpu_call's stage-by-stage call."""
+    import torch
+    from tests.gpu_common import from_dev, to_dev
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    od = torch.empty_like(qd)
+    ctx.sparsepr_attention(qd, kd, vd, od)
+    torch.cuda.synchronize()
+    out = dict(ctx.sparsepr_get_partition())
+    out.update(ctx.sparsepr_get_routing())
+    out["o_sparse"] = ctx.sparsepr_get_sparse_out().astype(np.float64)
+    out["x"], out["y"] = ctx.sparsepr_get_probes()
+    out["b_mat"], out["b_vec"] = ctx.sparsepr_get_fit()
+    out["key_centroids"], out["q_centroids"] = ctx.sparsepr_get_centroids()
+    out["o"] = from_dev(od)
+    return out
+
+
 def _same(a, b, what):
     for key in KEYS:
         assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), f"{what}: {key} differs"
@@ -50,10 +71,13 @@ def test_split_partition_matches_serial_and_oracle(spr):
     g2 = run_gpu_call(split, q, k, v, cfg.dtype)
     say("C2 split partition: serial call")
     gs = run_gpu_call(serial, q, k, v, cfg.dtype)
+    say("C2 split partition: one-call entry (V permuted beside the partition)")
+    gc = _one_call(split, q, k, v, cfg.dtype)
     split.close()
     serial.close()
     _same(g1, gs, "split vs serial")
     _same(g1, g2, "second split call")
+    _same(g1, gc, "one-call entry vs stage by stage")
     i = len(HEADS) - 1                          # the second half's only head
     say(f"C2 split partition: oracle head {HEADS[i]}")
     ref = orc.oracle_call(q[i:i + 1], k[i:i + 1], v[i:i + 1], cfg.settings)[0]
