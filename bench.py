@@ -215,6 +215,16 @@ def main() -> int:
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms_call = max(wall_ms, ev_ms)
     run_stats = ctx.sparsepr_get_stats()
+    # the partition stage alone, back to back in the same context without stage events
+    # (the stage-event context below records events between the stages)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        ctx.sparsepr_partition(qd, kd)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    partition_only_ms = ev0.elapsed_time(ev1) / args.steps
+    ctx.sparsepr_attention(qd, kd, vd, od)          # leave the context after a whole call
+    torch.cuda.synchronize()
 
     # stage times and the kernel's own events, in a context of their own
     log(f"stage timing: {args.steps} calls in a second context")
@@ -306,6 +316,7 @@ def main() -> int:
         "routed_pair_density": round(stats["routed_pairs"] / (cfg.heads * cfg.n ** 2), 4),
         "stage_ms": stage,
         "stage_timing": "second context with stage events; the timed calls above ran without",
+        "partition_only_ms": round(partition_only_ms, 4),
         "metric_eigensolve": "host" if args.host_solve else "device",
         "partition_streams": 1 if args.serial_partition or cfg.heads < 2 else 2,
         "recheck_points": stats["recheck_points"],

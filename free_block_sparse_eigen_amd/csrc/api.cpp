@@ -86,6 +86,9 @@ private:
 
 }  // namespace
 
+// Streams the partition's heads are spread over (one group of consecutive heads each).
+constexpr int kPartitionStreams = 2;
+
 struct sparsepr_ctx {
     sparsepr_params p{};
     int device = 0;
@@ -152,12 +155,14 @@ struct sparsepr_ctx {
     hipEvent_t ev_kperm = nullptr;    // K permuted on the side stream
     bool kperm_recorded = false;      // ev_kperm has been recorded
     hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
-    // the partition's second half of the heads runs on its own stream (split)
-    bool split = false;
-    hipStream_t part2 = nullptr;
-    hipEvent_t ev_fork = nullptr;     // the second half may start
-    hipEvent_t ev_kdone2 = nullptr;   // the second half's keys are partitioned
-    hipEvent_t ev_join = nullptr;     // the second half is done
+    // the partition's heads in nparts groups, group 0 on the caller's stream, group i > 0 on
+    // pstream[i]
+    static constexpr int kMaxParts = 4;
+    int nparts = 1;
+    hipStream_t pstream[kMaxParts] = {};
+    hipEvent_t ev_fork = nullptr;               // the other groups may start
+    hipEvent_t ev_kd[kMaxParts] = {};           // group i's keys are partitioned ([0]: ev_kdone)
+    hipEvent_t ev_jn[kMaxParts] = {};           // group i is done
     // sparsepr_attention hands V to the partition stage (bf16 only), which takes its per-head
     // magnitudes on the side stream beside the eigensolve and permutes it there right after
     // K; the route stage skips its own V permute for that V
@@ -253,7 +258,7 @@ void derive(sparsepr_ctx& c) {
     c.weyl_a = weyl_multiplier(c.N);
     c.dev_eig = !c.raw && !c.svoo && !(p.flags & SPARSEPR_F_HOST_SOLVE) && c.rK <= kEigMaxR &&
                 c.d <= kEigMaxN;
-    c.split = c.H >= 2 && !(p.flags & SPARSEPR_F_SERIAL_PARTITION);
+    c.nparts = (p.flags & SPARSEPR_F_SERIAL_PARTITION) ? 1 : std::min(c.H, kPartitionStreams);
 }
 
 void layout(sparsepr_ctx& c, Arena& a) {
@@ -530,12 +535,13 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             (e = hipEventCreateWithFlags(&c->ev_kperm, hipEventDisableTiming)) != hipSuccess ||
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
-        if (c->split &&
-            ((e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming)) != hipSuccess ||
-             (e = hipEventCreateWithFlags(&c->ev_kdone2, hipEventDisableTiming)) != hipSuccess ||
-             (e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming)) != hipSuccess ||
-             (e = hipStreamCreateWithFlags(&c->part2, hipStreamNonBlocking)) != hipSuccess))
-            return create_fail(c, SPARSEPR_ERR_HIP, "event / partition stream", e);
+        if (c->nparts > 1 && (e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming)) != hipSuccess)
+            return create_fail(c, SPARSEPR_ERR_HIP, "event (partition fork)", e);
+        for (int i = 1; i < c->nparts; ++i)
+            if ((e = hipEventCreateWithFlags(&c->ev_kd[i], hipEventDisableTiming)) != hipSuccess ||
+                (e = hipEventCreateWithFlags(&c->ev_jn[i], hipEventDisableTiming)) != hipSuccess ||
+                (e = hipStreamCreateWithFlags(&c->pstream[i], hipStreamNonBlocking)) != hipSuccess)
+                return create_fail(c, SPARSEPR_ERR_HIP, "event / partition stream", e);
     }
     if (c->raw) {
         const size_t H = c->H, d = c->d;
@@ -574,9 +580,11 @@ void sparsepr_destroy(sparsepr_ctx* c) {
     if (c->ev_kperm) (void)hipEventDestroy(c->ev_kperm);
     if (c->side) (void)hipStreamDestroy(c->side);
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-    if (c->ev_kdone2) (void)hipEventDestroy(c->ev_kdone2);
-    if (c->ev_join) (void)hipEventDestroy(c->ev_join);
-    if (c->part2) (void)hipStreamDestroy(c->part2);
+    for (int i = 1; i < sparsepr_ctx::kMaxParts; ++i) {
+        if (c->ev_kd[i]) (void)hipEventDestroy(c->ev_kd[i]);
+        if (c->ev_jn[i]) (void)hipEventDestroy(c->ev_jn[i]);
+        if (c->pstream[i]) (void)hipStreamDestroy(c->pstream[i]);
+    }
     if (c->h_fit) (void)hipHostFree(c->h_fit);
     if (c->h_mkp) (void)hipHostFree(c->h_mkp);
     if (c->h_wp) (void)hipHostFree(c->h_wp);
@@ -654,26 +662,29 @@ int32_t partition_heads(sparsepr_ctx* c, int h0, int hh, const bf16_t* q16, cons
                  c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, s);
 }
 
-// The per-head steps run as two halves of the heads on two streams (st and part2), so that
-// the many small, latency-bound launches of one half (recheck, sort, centroid finish)
-// overlap the other half's work; with SPARSEPR_F_SERIAL_PARTITION (or one head) all heads run
-// on st. K is permuted on the side stream once every head's keys are partitioned,
-// overlapping the query side.
+// The per-head steps run as nparts groups of consecutive heads, each on its own stream
+// (group 0 on st), so that the many small, latency-bound launches of one group (recheck,
+// sort, centroid finish) overlap the other groups' work; with SPARSEPR_F_SERIAL_PARTITION
+// (or one head) all heads run on st. The other streams start after an event on st and are
+// joined back into it. K is permuted on the side stream once every group's keys are
+// partitioned, overlapping the query side.
 int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
     int32_t rc;
-    if (!c->split) {
-        if ((rc = partition_heads(c, 0, c->H, q16, k16, st, c->ev_kdone))) return rc;
-        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
-    } else {
-        const int ha = (c->H + 1) / 2, hb = c->H - ha;
+    const int np = c->nparts;
+    if (np > 1) {
         SPR_HIP(c, hipEventRecord(c->ev_fork, st));
-        SPR_HIP(c, hipStreamWaitEvent(c->part2, c->ev_fork, 0));
-        if ((rc = partition_heads(c, 0, ha, q16, k16, st, c->ev_kdone))) return rc;
-        if ((rc = partition_heads(c, ha, hb, q16, k16, c->part2, c->ev_kdone2))) return rc;
-        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
-        SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone2, 0));
-        SPR_HIP(c, hipEventRecord(c->ev_join, c->part2));
-        SPR_HIP(c, hipStreamWaitEvent(st, c->ev_join, 0));
+        for (int i = 1; i < np; ++i) SPR_HIP(c, hipStreamWaitEvent(c->pstream[i], c->ev_fork, 0));
+    }
+    for (int i = 0; i < np; ++i) {
+        const int h0 = (int)((int64_t)c->H * i / np), h1 = (int)((int64_t)c->H * (i + 1) / np);
+        hipStream_t s = i == 0 ? st : c->pstream[i];
+        hipEvent_t kd = i == 0 ? c->ev_kdone : c->ev_kd[i];
+        if ((rc = partition_heads(c, h0, h1 - h0, q16, k16, s, kd))) return rc;
+        SPR_HIP(c, hipStreamWaitEvent(c->side, kd, 0));
+    }
+    for (int i = 1; i < np; ++i) {
+        SPR_HIP(c, hipEventRecord(c->ev_jn[i], c->pstream[i]));
+        SPR_HIP(c, hipStreamWaitEvent(st, c->ev_jn[i], 0));
     }
     // K into group-major order on the side stream; the sparse stage waits for ev_kperm
     launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);

@@ -4,8 +4,8 @@ By default the partition stage runs the first and the second half of the heads o
 streams (SPARSEPR_F_SERIAL_PARTITION runs them all on the caller's stream). Every step is
 per head, so both must give identical bits everywhere: labels, permutations, offsets,
 centroids, block lists, probes, the sparse and the final outputs. An odd head count makes
-the halves unequal, and one head of the second half is also checked against the oracle so
-that the second half's buffer offsets are pinned to something outside the library. A
+the groups unequal, and one head of the second group is also checked against the oracle so
+that its buffer offsets are pinned to something outside the library. A
 second call on the same context must repeat the first, and the one-call entry
 (sparsepr_attention, which permutes bf16 V on the side stream during the partition) must
 repeat the stage-by-stage call.
@@ -19,7 +19,7 @@ from tests.gpu_common import run_gpu_call, say
 
 pytestmark = pytest.mark.gpu
 
-HEADS = [0, 3, 7]          # halves of 2 and 1 heads
+HEADS = [0, 3, 7]          # head groups of 1 and 2 heads
 KEYS = ("key_labels", "q_labels", "key_perm", "q_perm", "key_off", "q_off", "blocks",
         "probe_orig", "o_sparse", "x", "y", "b_mat", "b_vec", "key_centroids", "q_centroids", "o")
 
@@ -78,9 +78,9 @@ def test_split_partition_matches_serial_and_oracle(spr):
     _same(g1, gs, "split vs serial")
     _same(g1, g2, "second split call")
     _same(g1, gc, "one-call entry vs stage by stage")
-    i = len(HEADS) - 1                          # the second half's only head
+    i = len(HEADS) - 1                          # a head of the second group
     say(f"C2 split partition: oracle head {HEADS[i]}")
     ref = orc.oracle_call(q[i:i + 1], k[i:i + 1], v[i:i + 1], cfg.settings)[0]
-    assert np.array_equal(g1["key_labels"][i], ref.key_labels), "second half: key labels"
-    assert np.array_equal(g1["q_labels"][i], ref.q_labels), "second half: query labels"
-    assert np.array_equal(g1["blocks"][i], ref.blocks), "second half: blocks"
+    assert np.array_equal(g1["key_labels"][i], ref.key_labels), "second group: key labels"
+    assert np.array_equal(g1["q_labels"][i], ref.q_labels), "second group: query labels"
+    assert np.array_equal(g1["blocks"][i], ref.blocks), "second group: blocks"
