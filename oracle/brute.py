@@ -88,3 +88,27 @@ def ridge_affine(x: Matrix, y: Matrix, lam: float):
            for i in range(d + 1)]
     sol = solve(a, rhs)
     return [sol[i] for i in range(1, d + 1)], sol[0]
+
+
+def e4m3_values() -> List[float]:
+    """Every finite non-negative FP8 E4M3 value, decoded code by code from the format's
+    definition: code = E M (4 exponent bits, 3 mantissa bits); E = 0 is subnormal,
+    M 2^-9; otherwise (1 + M / 8) 2^(E - 7); the code with E = 15, M = 7 is NaN."""
+    out = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        out.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return out
+
+
+def e4m3_nearest(x: float) -> float:
+    """x rounded to E4M3 by searching the decoded values: the nearest, and on a tie the one
+    whose code has an even mantissa (its lowest bit clear); beyond 448 the largest."""
+    vals = e4m3_values()
+    a = abs(x)
+    best = None
+    for code, v in enumerate(vals):
+        dist = abs(a - v)
+        if best is None or dist < best[0] or (dist == best[0] and (code & 1) == 0):
+            best = (dist, code, v)
+    return math.copysign(best[2], x)

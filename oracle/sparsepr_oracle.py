@@ -319,6 +319,40 @@ def sparse_attention(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray, q_off: np.n
     return out
 
 
+# ------------------------------------------------- fp8 logits (an experiment) ---
+# Not the method: [BLOG] section 8.4 names quantization as an extension to combine with the
+# sparse attention. The experiment computes the sparse logits Q K^T from Q and K rounded to
+# the OCP FP8 E4M3 format after a per-head power-of-two scale; everything else is unchanged.
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest FP8 E4M3 value (OCP 8-bit floating point: 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; below 2^-6 the subnormals share the spacing 2^-9; the largest
+    finite magnitude is 448 and there is no infinity), ties to the even mantissa. Larger
+    magnitudes (which the per-head scale never produces) saturate to 448."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                        # a = f 2^ex, f in [0.5, 1)
+    e = np.maximum(ex.astype(np.float64) - 1.0, -6.0)   # binade [2^e, 2^(e+1)), floored at 2^-6
+    ulp = np.exp2(e - 3.0)                     # three mantissa bits
+    r = np.round(a / ulp) * ulp                # a / ulp is the integer significand; ties to even
+    return np.copysign(np.minimum(r, 448.0), x)
+
+
+def f8_scale_exp(absmax: float) -> int:
+    """The per-head scale exponent: the largest e with absmax 2^e <= 448 (the largest E4M3
+    magnitude), kept within [-120, 120]; 0 for an all-zero tensor."""
+    if not absmax > 0.0:
+        return 0
+    f, ex = math.frexp(float(absmax))           # absmax = (2 f) 2^(ex - 1), 2 f in [1, 2)
+    e = 8 - (ex - 1) if 2.0 * f <= 1.75 else 7 - (ex - 1)   # 448 = 1.75 * 2^8
+    return max(-120, min(120, e))
+
+
+def fp8_dequantized(x: np.ndarray, e: int) -> np.ndarray:
+    """x scaled by 2^e, rounded to E4M3, scaled back: the values the fp8 products see."""
+    return e4m3_round(np.asarray(x, np.float64) * 2.0 ** e) * 2.0 ** (-e)
+
+
 # ------------------------------------------------------ probe-fitted residual ---
 def ridge_affine(x: np.ndarray, y: np.ndarray, lam: float):
     """Ridge-regularised affine fit y ~ b + x B [PR 2B, affine calibration].
@@ -407,7 +441,8 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
                 kv_groups: int, q_groups: int, kmeans_iters: int, density: float, probes: int,
                 ridge_lambda: float, corr_rank: int,
                 part: Optional[Partition] = None, raw_kmeans: bool = False,
-                svoo: bool = False, reuse: Optional["HeadResult"] = None) -> HeadResult:
+                svoo: bool = False, reuse: Optional["HeadResult"] = None,
+                fp8_qk: bool = False) -> HeadResult:
     """One head of one SparsePR call, stage by stage:
     partition -> group-major layout -> routing + probes -> sparse attention and
     exact probe rows -> probe fit -> correction -> original order.
@@ -416,7 +451,11 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
     `reuse` (an experiment, not the method: [PR 2B] uses no temporal reuse, [BLOG]'s
     mask_update_stride refreshes the mask only every few steps) keeps an earlier call's
     labels, block lists and probe rows for these new inputs; everything after the routing
-    is computed from the new q, k, v."""
+    is computed from the new q, k, v.
+    `fp8_qk` (an experiment, see e4m3_round) takes the sparse attention's logits from Q and K
+    rounded to FP8 E4M3 after their per-head power-of-two scales (the largest magnitude of
+    each tensor over the head sets the scale); the probe rows, their fit and the dense rows
+    stay in the inputs' precision, and the correction is applied to that sparse output."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -444,6 +483,10 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
     x = o_s[ppos]
     y = o_d - x
     b_mat, b_vec = probe_fit(x, y, ridge_lambda, corr_rank)
+    if fp8_qk:
+        eq = f8_scale_exp(float(np.max(np.abs(q))) if q.size else 0.0)
+        ek = f8_scale_exp(float(np.max(np.abs(k))) if k.size else 0.0)
+        o_s = sparse_attention(fp8_dequantized(qp, eq), fp8_dequantized(kp, ek), vp, qoff, koff, blocks)
     o_perm = correct(o_s, ppos, o_d, b_mat, b_vec)
     o = np.empty_like(o_perm)
     o[qperm] = o_perm
@@ -454,12 +497,12 @@ def oracle_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_sample: int, k
 
 def oracle_call(q: np.ndarray, k: np.ndarray, v: np.ndarray, settings,
                 heads: Optional[Sequence[int]] = None, raw_kmeans: bool = False,
-                svoo: bool = False) -> List[HeadResult]:
+                svoo: bool = False, fp8_qk: bool = False) -> List[HeadResult]:
     """All heads of one call; `settings` carries the SparsePR parameters by name."""
     kw = dict(n_sample=settings.n_sample, key_rank=settings.key_rank,
               kv_groups=settings.kv_groups, q_groups=settings.q_groups,
               kmeans_iters=settings.kmeans_iters, density=settings.density,
               probes=settings.probes, ridge_lambda=settings.ridge_lambda,
-              corr_rank=settings.corr_rank, raw_kmeans=raw_kmeans, svoo=svoo)
+              corr_rank=settings.corr_rank, raw_kmeans=raw_kmeans, svoo=svoo, fp8_qk=fp8_qk)
     hs = range(q.shape[0]) if heads is None else heads
     return [oracle_head(q[h], k[h], v[h], **kw) for h in hs]

@@ -689,3 +689,86 @@ def test_reuse_keeps_the_layout_but_attends_with_the_new_inputs():
     assert np.allclose(back, dense, rtol=0, atol=1e-12)
     # and the new partition of these inputs differs from the kept one (the test separates them)
     assert not np.array_equal(orc.oracle_head(q1, k1, v1, **a).key_labels, r0.key_labels)
+
+
+# ------------------------------------------------------- fp8 logits (an experiment) ---
+def test_e4m3_round_matches_the_decoded_code_table():
+    """e4m3_round against a search over every decoded E4M3 code: random magnitudes over
+    the whole range, every midpoint between neighbouring values (the ties) and the values
+    themselves."""
+    vals = brute.e4m3_values()
+    rng = np.random.default_rng(8)
+    xs = list(np.exp2(rng.uniform(-12, 9.2, 400)) * rng.choice([-1, 1], 400))
+    xs += [0.5 * (a + b) for a, b in zip(vals[:-1], vals[1:])]
+    xs += vals + [-v for v in vals[1:]] + [0.0, 448.0, 460.0, -1e-6]
+    got = orc.e4m3_round(np.array(xs))
+    want = np.array([brute.e4m3_nearest(float(x)) for x in xs])
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_known_values():
+    """Closed cases of the format: the extremes, the subnormal spacing and ties to even."""
+    r = orc.e4m3_round
+    assert r(np.array([448.0]))[0] == 448.0                    # largest finite
+    assert r(np.array([2.0 ** -6]))[0] == 2.0 ** -6            # smallest normal
+    assert r(np.array([2.0 ** -9]))[0] == 2.0 ** -9            # smallest subnormal
+    assert r(np.array([2.0 ** -10]))[0] == 0.0                 # tie between 0 and 2^-9: even
+    assert r(np.array([1.0625]))[0] == 1.0                     # tie 1.0 / 1.125: even mantissa 0
+    assert r(np.array([1.1875]))[0] == 1.25                    # tie 1.125 / 1.25: even mantissa 2
+    assert r(np.array([-2.5]))[0] == -2.5
+    assert r(np.array([3.3]))[0] == 3.25                       # spacing 0.25 in [2, 4)
+
+
+def test_f8_scale_exp_is_the_largest_exponent_that_fits():
+    rng = np.random.default_rng(9)
+    for a in list(np.exp2(rng.uniform(-30, 30, 300))) + [448.0, 1.75, 1.7500001, 224.0, 1.0]:
+        e = orc.f8_scale_exp(float(a))
+        assert a * 2.0 ** e <= 448.0 < a * 2.0 ** (e + 1)
+    assert orc.f8_scale_exp(0.0) == 0
+
+
+def _tiny_call_inputs(seed, n=48, d=16):
+    rng = np.random.default_rng(seed)
+    return (rng.normal(size=(n, d)), rng.normal(size=(n, d)), rng.normal(size=(n, d)))
+
+
+def test_fp8_logits_are_exact_for_e4m3_representable_inputs():
+    """When every scaled q and k is already an E4M3 value, the fp8 call is the plain call
+    (so the scales are applied and undone exactly)."""
+    vals = np.array(brute.e4m3_values())
+    rng = np.random.default_rng(10)
+    n, d = 48, 16
+    q = rng.choice(vals, size=(n, d)) * rng.choice([-1.0, 1.0], size=(n, d))
+    k = rng.choice(vals, size=(n, d)) * rng.choice([-1.0, 1.0], size=(n, d))
+    q[0, 0], k[0, 0] = 448.0, -448.0                      # scales 2^0 after the 2^-3 below
+    q, k = q * 2.0 ** -3, k * 2.0 ** -5
+    v = rng.normal(size=(n, d))
+    kw = dict(n_sample=8, key_rank=4, kv_groups=4, q_groups=3, kmeans_iters=2, density=0.5,
+              probes=6, ridge_lambda=1e-3, corr_rank=2)
+    plain = orc.oracle_head(q, k, v, **kw)
+    f8 = orc.oracle_head(q, k, v, fp8_qk=True, **kw)
+    assert np.array_equal(plain.o_sparse, f8.o_sparse)
+    assert np.array_equal(plain.o, f8.o)
+
+
+def test_fp8_logits_quantize_q_and_k_per_tensor_and_leave_the_rest():
+    """The fp8 sparse output is the masked softmax of brute-quantized Q and K (each scaled by
+    its own power of two, V untouched), and the probe data and fit are the plain call's."""
+    q, k, v = _tiny_call_inputs(11)
+    kw = dict(n_sample=8, key_rank=4, kv_groups=4, q_groups=3, kmeans_iters=2, density=0.5,
+              probes=6, ridge_lambda=1e-3, corr_rank=2)
+    plain = orc.oracle_head(q, k, v, **kw)
+    f8 = orc.oracle_head(q, k, v, fp8_qk=True, **kw)
+    eq, ek = orc.f8_scale_exp(np.abs(q).max()), orc.f8_scale_exp(np.abs(k).max())
+    qq = [[brute.e4m3_nearest(x * 2.0 ** eq) * 2.0 ** -eq for x in row] for row in q[plain.q_perm]]
+    kq = [[brute.e4m3_nearest(x * 2.0 ** ek) * 2.0 ** -ek for x in row] for row in k[plain.key_perm]]
+    vp = v[plain.key_perm].tolist()
+    for i in range(len(plain.q_off) - 1):
+        allowed_keys = set(orc.routed_keys(plain.key_off, plain.blocks[i]).tolist())
+        rows = range(plain.q_off[i], plain.q_off[i + 1])
+        mask = [[j in allowed_keys for j in range(len(kq))] for _ in rows]
+        want = brute.attention([qq[r] for r in rows], kq, vp, mask)
+        assert np.allclose(f8.o_sparse[list(rows)], np.array(want), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(plain.x, f8.x) and np.array_equal(plain.y, f8.y)
+    assert np.array_equal(plain.b_mat, f8.b_mat)
+    assert not np.array_equal(plain.o_sparse, f8.o_sparse)
