@@ -159,6 +159,9 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--host-solve", action="store_true",
                     help="eigensolve of the key metric on the host (SPARSEPR_F_HOST_SOLVE)")
+    ap.add_argument("--fp8-qk", action="store_true",
+                    help="experiment: the sparse kernel's logits from FP8 E4M3 Q and K "
+                         "(SPARSEPR_F_FP8_QK); not the method's precision, never the headline")
     ap.add_argument("--serial-partition", action="store_true",
                     help="every head's partition on one stream (SPARSEPR_F_SERIAL_PARTITION)")
     ap.add_argument("--oracle-threads", type=int, default=None,
@@ -194,7 +197,8 @@ def main() -> int:
     od = torch.empty_like(qd)
     dt = spr.BF16 if cfg.dtype == "bf16" else spr.F32
     base_flags = ((spr.F_HOST_SOLVE if args.host_solve else 0) |
-                  (spr.F_SERIAL_PARTITION if args.serial_partition else 0))
+                  (spr.F_SERIAL_PARTITION if args.serial_partition else 0) |
+                  (spr.F_FP8_QK if args.fp8_qk else 0))
     ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, st, flags=base_flags)
     stream = torch.cuda.current_stream()
 
@@ -289,7 +293,10 @@ def main() -> int:
                                  "workers": args.oracle_all_heads, "threads_per_worker": 1}
             log(f"whole oracle call {cpu['whole_call']}")
 
-    traffic = measured_traffic(attn_flops, kernel_ms)
+    traffic = None if args.fp8_qk else measured_traffic(attn_flops, kernel_ms)
+    # with fp8 logits half the flops run at the fp8 rate: the time at peak is
+    # (F/2) / 5033.2 + (F/2) / 2516.6, a blended peak of 3355.5 TFLOP/s
+    peak = 2.0 / (1.0 / (2.0 * BF16_PEAK_TFLOPS) + 1.0 / BF16_PEAK_TFLOPS) if args.fp8_qk else BF16_PEAK_TFLOPS
     out = {
         "metric": METRIC,
         "value": round(ms_call, 4),
@@ -301,7 +308,7 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3(QK^T)+fp16(PV)" if args.fp8_qk else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.config} {cfg.name}: {cfg.heads} heads, N={cfg.n} "
                                f"({cfg.frames}x{cfg.patch_rows}x{cfg.patch_cols}), d={cfg.d}, "
@@ -317,13 +324,15 @@ def main() -> int:
         "stage_ms": stage,
         "stage_timing": "second context with stage events; the timed calls above ran without",
         "partition_only_ms": round(partition_only_ms, 4),
+        "experiment": ("fp8 logits (SPARSEPR_F_FP8_QK): Q and K rounded to FP8 E4M3 for the sparse "
+                       "kernel's Q K^T; not the method's precision") if args.fp8_qk else None,
         "metric_eigensolve": "host" if args.host_solve else "device",
         "partition_streams": 1 if args.serial_partition or cfg.heads < 2 else 2,
         "recheck_points": stats["recheck_points"],
         "dense": dense,
         "roofline": {"kernel": "k_vbsa (variable-block-sparse attention)", "bound": "mfma",
-                     "achieved": round(kernel_tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tflops / BF16_PEAK_TFLOPS, 4),
+                     "achieved": round(kernel_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": traffic,
                      "algorithmic_flops_per_launch": attn_flops,
                      "launch_ms": round(kernel_ms, 4)},

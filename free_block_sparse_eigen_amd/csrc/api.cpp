@@ -96,6 +96,7 @@ struct sparsepr_ctx {
     int nblk = 0, maxu = 0, splits = 0, dense_units = 0, gmax = 0;
     bool raw = false;                  // SPARSEPR_F_RAW_KMEANS: identity metrics on both sides
     bool svoo = false;                 // SPARSEPR_F_SVOO: alternating co-clustering
+    bool fp8 = false;                  // SPARSEPR_F_FP8_QK: fp8 logits in the sparse kernel
     bool have_route = false;           // a partition and routing exist (sparsepr_reuse_route)
     int64_t weyl_a = 0;
 
@@ -106,6 +107,9 @@ struct sparsepr_ctx {
     bf16_t* kp = nullptr;                         // K in group-major order
     uint16_t* vp = nullptr;                       // V in group-major order, fp16 scaled per head
     uint32_t* vmax = nullptr;                     // [H] largest |v| per head (bf16 magnitude bits)
+    // SPARSEPR_F_FP8_QK (an experiment): K group-major in FP8 E4M3, per-head largest |q|, |k|
+    uint8_t* kp8 = nullptr;
+    uint32_t *qmax = nullptr, *kmax = nullptr;
     unsigned long long* nonfinite = nullptr;      // [2] non-finite inputs, outputs (CHECK_FINITE)
     const bf16_t* q_src = nullptr;                // Q in token order (the route stage's input)
     const bf16_t* v_src = nullptr;                // V in token order (the probe rows gather it)
@@ -153,6 +157,7 @@ struct sparsepr_ctx {
     hipEvent_t ev_rows = nullptr;     // probe rows merged (the fit's inputs are ready)
     hipEvent_t ev_kdone = nullptr;    // key partition done (the side stream may permute K)
     hipEvent_t ev_kperm = nullptr;    // K permuted on the side stream
+    hipEvent_t ev_qside = nullptr;    // SPARSEPR_F_FP8_QK: the side stream may read q
     bool kperm_recorded = false;      // ev_kperm has been recorded
     hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
     // the partition's heads in nparts groups, group 0 on the caller's stream, group i > 0 on
@@ -218,7 +223,8 @@ int32_t validate(const sparsepr_params* p) {
     if (!(p->density > 0.0) || !(p->density <= 1.0)) return SPARSEPR_ERR_INVALID_ARG;
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
     if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE |
-                     SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO | SPARSEPR_F_SERIAL_PARTITION))
+                     SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO | SPARSEPR_F_SERIAL_PARTITION |
+                     SPARSEPR_F_FP8_QK))
         return SPARSEPR_ERR_INVALID_ARG;
     if ((p->flags & SPARSEPR_F_RAW_KMEANS) && (p->flags & SPARSEPR_F_SVOO)) return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
@@ -246,6 +252,7 @@ void derive(sparsepr_ctx& c) {
     c.rK = p.key_rank;
     c.raw = (p.flags & SPARSEPR_F_RAW_KMEANS) != 0;
     c.svoo = (p.flags & SPARSEPR_F_SVOO) != 0;
+    c.fp8 = (p.flags & SPARSEPR_F_FP8_QK) != 0;
     c.Dq = c.d;                         // the query metric is used in full (d x d)
     c.k = routed_count(p.density, c.Gk);
     c.P = p.probes;
@@ -272,6 +279,11 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.kp, HND);
     a.take(c.vp, HND);
     a.take(c.vmax, H);
+    if (c.fp8) {
+        a.take(c.kp8, HND);
+        a.take(c.qmax, H);
+        a.take(c.kmax, H);
+    }
     a.take(c.nonfinite, 2);
     a.take(c.klab, HN);
     a.take(c.qlab, HN);
@@ -535,6 +547,8 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             (e = hipEventCreateWithFlags(&c->ev_kperm, hipEventDisableTiming)) != hipSuccess ||
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
+        if (c->fp8 && (e = hipEventCreateWithFlags(&c->ev_qside, hipEventDisableTiming)) != hipSuccess)
+            return create_fail(c, SPARSEPR_ERR_HIP, "event (fp8 scales)", e);
         if (c->nparts > 1 && (e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event (partition fork)", e);
         for (int i = 1; i < c->nparts; ++i)
@@ -578,6 +592,7 @@ void sparsepr_destroy(sparsepr_ctx* c) {
     if (c->ev_rows) (void)hipEventDestroy(c->ev_rows);
     if (c->ev_kdone) (void)hipEventDestroy(c->ev_kdone);
     if (c->ev_kperm) (void)hipEventDestroy(c->ev_kperm);
+    if (c->ev_qside) (void)hipEventDestroy(c->ev_qside);
     if (c->side) (void)hipStreamDestroy(c->side);
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     for (int i = 1; i < sparsepr_ctx::kMaxParts; ++i) {
@@ -598,11 +613,28 @@ namespace {
 // partition; the sparse stage waits for ev_kperm before reading it. The side stream
 // starts after all work enqueued so far on st, which includes the previous call's
 // readers of the permuted K.
+// SPARSEPR_F_FP8_QK: the per-head largest |q| and |k| on the side stream, after this
+// stream's work so far (which includes the previous call's readers of them); the side
+// stream's fp8 K permute and ev_kperm, which the sparse stage waits for, come after them.
+int32_t fp8_scales_side(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
+    if (!c->fp8) return SPARSEPR_OK;
+    SPR_HIP(c, hipEventRecord(c->ev_qside, st));
+    SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_qside, 0));
+    launch_absmax_v(q16, c->H, c->N, c->d, c->qmax, c->side);
+    launch_absmax_v(k16, c->H, c->N, c->d, c->kmax, c->side);
+    SPR_LAUNCHED(c, "Q and K magnitudes (fp8)");
+    return SPARSEPR_OK;
+}
+
 int32_t permute_keys_side(sparsepr_ctx* c, const bf16_t* k16, hipStream_t st) {
     SPR_HIP(c, hipEventRecord(c->ev_kdone, st));
     SPR_HIP(c, hipStreamWaitEvent(c->side, c->ev_kdone, 0));
     launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);
     SPR_LAUNCHED(c, "permute K");
+    if (c->fp8) {
+        launch_permute_k8(k16, c->kperm, c->H, c->N, c->d, c->kmax, c->kp8, c->side);
+        SPR_LAUNCHED(c, "permute K (fp8)");
+    }
     SPR_HIP(c, hipEventRecord(c->ev_kperm, c->side));
     c->kperm_recorded = true;
     return SPARSEPR_OK;
@@ -689,6 +721,10 @@ int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf1
     // K into group-major order on the side stream; the sparse stage waits for ev_kperm
     launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);
     SPR_LAUNCHED(c, "permute K");
+    if (c->fp8) {
+        launch_permute_k8(k16, c->kperm, c->H, c->N, c->d, c->kmax, c->kp8, c->side);
+        SPR_LAUNCHED(c, "permute K (fp8)");
+    }
     if (c->v_pre) {              // its magnitudes were taken during the eigensolve
         launch_permute_f16(c->v_pre, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, c->side);
         SPR_LAUNCHED(c, "permute V");
@@ -721,6 +757,7 @@ int32_t sparsepr_partition(sparsepr_ctx* c, const void* q, const void* k, void* 
         launch_count_nonfinite(k16, H * c->N * d, 0, c->nonfinite, st);
         SPR_LAUNCHED(c, "finite check (q, k)");
     }
+    if ((rc = fp8_scales_side(c, q16, k16, st))) return rc;
     if (c->svoo) {
         std::fill(c->h_mgap.begin(), c->h_mgap.end(), 0.0);      // no M_K
         c->mgap_dev = false;
@@ -800,6 +837,7 @@ int32_t sparsepr_set_partition(sparsepr_ctx* c, const void* q, const void* k,
     const bf16_t* q16 = as_bf16(c, q, c->qb, st);
     const bf16_t* k16 = as_bf16(c, k, c->kb, st);
     launch_fill_i32(c->flag_cnt, 0, 2 * (size_t)c->T * c->H, st);
+    if ((rc = fp8_scales_side(c, q16, k16, st))) return rc;
     launch_counting_sort(c->klab, c->H, c->N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
     if ((rc = permute_keys_side(c, k16, st))) return rc;
     launch_group_means(k16, c->H, c->N, c->d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr,
@@ -877,6 +915,7 @@ int32_t sparsepr_reuse_route(sparsepr_ctx* c, const void* q, const void* k, cons
     c->q_src = q16;
     c->v_src = v16;
     // the new K and V through the kept key permutation; blocks, probes and work units stay
+    if ((rc = fp8_scales_side(c, q16, k16, st))) return rc;
     if ((rc = permute_keys_side(c, k16, st))) return rc;
     launch_permute_v16(v16, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, st);
     SPR_LAUNCHED(c, "permute");
@@ -928,7 +967,7 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
     mark(c, 4, st);
     launch_vbsa(c->q_src, c->qperm, c->kp, c->vp, c->vmax, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
                 c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, kSparseRows,
-                c->o_s, 0, st);
+                c->o_s, 0, st, c->fp8 ? c->kp8 : nullptr, c->qmax, c->kmax);
     SPR_LAUNCHED(c, "sparse attention");
     mark(c, 5, st);
     c->stage = kStageAttn;

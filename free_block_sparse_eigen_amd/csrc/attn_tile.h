@@ -89,6 +89,26 @@ struct Tile {
     }
 };
 
+// FP8 K tiles (the fp8-logit experiment): rows of D bytes, 16-byte chunk c of row r at slot
+// r * CH + (c ^ sw(r)), filled like Tile's from a resource over one head's [n][D] bytes.
+template <int D, int NT = 256>
+struct Tile8 {
+    static constexpr int CH = D / 16;
+    static constexpr int SLOTS = KT * CH;
+    static constexpr int PER_WAVE = SLOTS / NT;
+    __host__ __device__ static int sw(int r) { return CH >= 8 ? swz<8>(r) : (r & (CH - 1)); }
+    __device__ static void issue_one(rsrc_t r, const int* __restrict__ phys, uint4* s, int w, int lane) {
+        static_assert(SLOTS % NT == 0, "an fp8 tile must split evenly over the block");
+#pragma unroll
+        for (int m = 0; m < PER_WAVE; ++m) {
+            const int first = (w * PER_WAVE + m) * 64;
+            const int slot = first + lane;
+            const int row = slot / CH, pc = slot % CH;
+            lds_load16(r, s + first, phys[row] * D + (pc ^ sw(row)) * 16);
+        }
+    }
+};
+
 // Wait for this thread's outstanding direct loads, then for every wave of the block.
 __device__ inline void tile_ready() {
     __builtin_amdgcn_s_waitcnt(0);

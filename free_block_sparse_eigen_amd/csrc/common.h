@@ -1,6 +1,7 @@
 // Shared device helpers for the SparsePR HIP kernels (gfx950, wave64).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <cmath>
 #include <cstdint>
 
 namespace spr {
@@ -92,6 +93,24 @@ __device__ inline void lds_load16(rsrc_t r, void* s, int off) {
                                              0, 0, 0);
 }
 
+// ---- FP8 E4M3 operands (the fp8-logit experiment) ----
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// D = A(32x64) * B(64x32) + C with FP8 E4M3 inputs and fp32 accumulation: lane l supplies
+// row l%32 of A and column l%32 of B, 32 bytes each, for the depth half l/32. A and B
+// take their depth bytes in the same order, so the sum over the depth does not depend on
+// which order the instruction pairs them in.
+__device__ inline f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// four fp32 -> four E4M3 bytes (round to nearest even), a in the low byte; the callers'
+// values are at most 448 in magnitude
+__device__ inline uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // ---- fp16 operands of the P.V products ----
 // V is stored group-major in fp16, scaled per head by an exact power of two 2^e chosen from
 // the head's largest |v| (so the scaled values sit below 2^15 and bf16 values convert
@@ -137,6 +156,20 @@ __host__ __device__ inline int v_scale_exp(uint32_t max_bf16_bits) {
     }
     const int e = 14 - lg;
     return e < -64 ? -64 : (e > 64 ? 64 : e);
+}
+
+// Exponent e of a per-head FP8 E4M3 scale from the head's largest bf16 magnitude bits: the
+// largest e with max 2^e <= 448 (the largest E4M3 magnitude), kept within [-120, 120]; 0
+// for a zero or non-finite head. Scaling by 2^e is exact, so only the rounding to E4M3
+// changes the values.
+__host__ __device__ inline int f8_scale_exp(uint32_t max_bf16_bits) {
+    const int ef = (int)((max_bf16_bits >> 7) & 0xFF);
+    if (max_bf16_bits == 0 || ef == 0xFF) return 0;
+    const float a = __builtin_bit_cast(float, max_bf16_bits << 16);
+    int ex;
+    const float f = frexpf(a, &ex);                    // a = f 2^ex, f in [0.5, 1)
+    const int e = (2.f * f <= 1.75f) ? 9 - ex : 8 - ex;   // 448 = 1.75 2^8
+    return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
 
 // P offset for fp16: the lazily raised running max lets P reach 2^8, so exp2(x + 7) stays

@@ -65,6 +65,10 @@ void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, in
 // each head's largest |v| as bf16 magnitude bits
 void launch_permute_v16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
                         uint32_t* vmax, uint16_t* dst, hipStream_t st);
+// K into group-major FP8 E4M3 scaled per head by 2^f8_scale_exp(kmax[h]) (kmax [heads]: each
+// head's largest |k| as bf16 magnitude bits, from launch_absmax_v); the fp8-logit experiment
+void launch_permute_k8(const bf16_t* src, const int32_t* perm, int heads, int n, int d, const uint32_t* kmax,
+                       uint8_t* dst, hipStream_t st);
 // its two halves: the per-head magnitude bits, then the scaled permute that reads them
 void launch_absmax_v(const bf16_t* src, int heads, int n, int d, uint32_t* vmax, hipStream_t st);
 void launch_permute_f16(const bf16_t* src, const int32_t* perm, int heads, int n, int d,
@@ -86,13 +90,16 @@ void set_call_error(const char* msg);
 // kSparseRows or kDenseRows (the units' row count, which fixes the block shape)
 // qp: Q in token order; qperm [heads][n] (group-major position -> token) or nullptr
 // vp: bf16 [heads][n][d] with vmax == nullptr (dense baseline), or fp16 scaled per head by
-// 2^v_scale_exp(vmax[h]) (the sparse call, 128-row units)
+// 2^v_scale_exp(vmax[h]) (the sparse call, 128-row units); kp8 (with qmax, kmax: the
+// per-head largest |q| and |k| as bf16 magnitude bits) selects the fp8-logit experiment:
+// K group-major in FP8 E4M3 scaled by 2^f8_scale_exp(kmax[h]), Q rounded on load
 void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const void* vp,
                  const uint32_t* vmax, int heads, int n, int d,
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
-                 int unit_rows, void* out, int out_mode, hipStream_t st);
+                 int unit_rows, void* out, int out_mode, hipStream_t st, const uint8_t* kp8 = nullptr,
+                 const uint32_t* qmax = nullptr, const uint32_t* kmax = nullptr);
 int probe_splits(int n, int heads, int probes);
 // qp: Q in token order, probe_orig: the probe rows' token indices; kp group-major
 // vtok: bf16 V in token order, gathered through kperm [heads][n] (group-major -> token)

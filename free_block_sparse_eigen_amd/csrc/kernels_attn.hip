@@ -86,16 +86,21 @@ __device__ inline f32x16 mfma_pv(uint4 v, uint4 p, f32x16 c) {
 // Block = NW waves x 32 query rows: a unit of up to NW x 32 rows shares every key tile.
 // VH: V is group-major fp16 scaled per head by 2^e (vmax, see v_scale_exp), and P is
 // rounded to fp16 with the 2^7 offset; otherwise V and P are bf16.
-template <int D, int OUTM, int NW, bool VH>
+// F8 (the fp8-logit experiment, with VH): K is group-major FP8 E4M3 scaled per head by
+// 2^f8_scale_exp(kmax[h]), Q rows are rounded to E4M3 on load after their own per-head
+// scale (qmax), and S^T = K Q^T runs on the 32x32x64 fp8 instruction; the two scales are
+// taken out of the logits with the softmax's own factor.
+template <int D, int OUTM, int NW, bool VH, bool F8>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
-    const bf16_t* __restrict__ qp, const int32_t* __restrict__ qperm, const bf16_t* __restrict__ kp,
+    const bf16_t* __restrict__ qp, const int32_t* __restrict__ qperm, const void* __restrict__ kp,
     const bf16_t* __restrict__ vp, int n, const int32_t* __restrict__ qoff, int qoff_stride, const int32_t* __restrict__ koff,
     int koff_stride, const int32_t* __restrict__ blocks, int blocks_head_stride, int kblk,
     const int2* __restrict__ units, int units_head_stride, const int32_t* __restrict__ nunits,
     int nunits_stride, int heads, float scale_log2, const uint32_t* __restrict__ vmax,
-    void* __restrict__ out) {
+    const uint32_t* __restrict__ qmax, const uint32_t* __restrict__ kmax, void* __restrict__ out) {
     constexpr int kVbsaThreads = NW * 64;
     using TL = Tile<D, kVbsaThreads>;
+    using T8 = Tile8<D, kVbsaThreads>;
     constexpr int DB = D / 32;
     __shared__ int s_pre[kMaxGroups + 1];
     __shared__ int s_start[kMaxGroups];
@@ -166,14 +171,40 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
     const bool active = w * 32 < rows;
     const int qrow = w * 32 + (lane & 31);
     const bool qvalid = qrow < rows;
-    uint4 qf[D / 16];
+    uint4 qf[F8 ? 1 : D / 16];
+    i32x8 qf8[F8 ? D / 64 : 1];
     {
         const int src = !qvalid ? 0 : (qperm ? qperm[head_row0 + row0 + qrow] : row0 + qrow);
+        if constexpr (!F8) {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[kk] = qvalid ? ldg16(qp + (head_row0 + src) * D + 16 * kk + 8 * (lane >> 5))
-                            : make_uint4(0, 0, 0, 0);
+            for (int kk = 0; kk < D / 16; ++kk)
+                qf[kk] = qvalid ? ldg16(qp + (head_row0 + src) * D + 16 * kk + 8 * (lane >> 5))
+                                : make_uint4(0, 0, 0, 0);
+        } else {
+            // depth step ks: this lane's 32 dims 64 ks + 32 (lane / 32) .. +31, scaled and
+            // rounded to E4M3 (the K fragments take the same 32 dims in the same order)
+            const float qs = ldexpf(1.0f, f8_scale_exp(qmax[h]));
+#pragma unroll
+            for (int ks = 0; ks < D / 64; ++ks) {
+                uint32_t wq[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint4 u = qvalid ? ldg16(qp + (head_row0 + src) * D + 64 * ks + 32 * (lane >> 5) + 8 * c)
+                                           : make_uint4(0, 0, 0, 0);
+                    const uint32_t e[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        wq[2 * c + j] = pack_e4m3x4(bf16_to_f32((bf16_t)(e[2 * j] & 0xFFFF)) * qs,
+                                                    bf16_to_f32((bf16_t)(e[2 * j] >> 16)) * qs,
+                                                    bf16_to_f32((bf16_t)(e[2 * j + 1] & 0xFFFF)) * qs,
+                                                    bf16_to_f32((bf16_t)(e[2 * j + 1] >> 16)) * qs);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) qf8[ks][j] = (int)wq[j];
+            }
+        }
     }
+    if constexpr (F8) scale_log2 = ldexpf(scale_log2, -(f8_scale_exp(qmax[h]) + f8_scale_exp(kmax[h])));
 
     f32x16 o[DB];
 #pragma unroll
@@ -181,32 +212,72 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
     float m_run = -INFINITY, l_run = 0.f;
     const int half = lane >> 5;
 
-    const rsrc_t rk = head_rsrc(kp + head_row0 * D, n, D);
+    const rsrc_t rk = F8 ? make_rsrc(static_cast<const uint8_t*>(kp) + head_row0 * D, (uint32_t)n * D)
+                         : head_rsrc(static_cast<const bf16_t*>(kp) + head_row0 * D, n, D);
     const rsrc_t rv = head_rsrc(vp + head_row0 * D, n, D);
     // this lane's fragment offsets inside a tile, computed once: K row (lane & 31) at each
     // depth step (row + 32 has the same swizzle, a constant offset), V^T per column block
-    int kfo[D / 16], vo0[DB], vo1[DB];
+    int kfo[F8 ? D / 32 : D / 16], vo0[DB], vo1[DB];
     {
-        const int rl = lane & 31, sw = swz<TL::CH>(rl);
+        const int rl = lane & 31;
+        if constexpr (!F8) {
+            const int sw = swz<TL::CH>(rl);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) kfo[kk] = rl * TL::CH + ((2 * kk + half) ^ sw);
+            for (int kk = 0; kk < D / 16; ++kk) kfo[kk] = rl * TL::CH + ((2 * kk + half) ^ sw);
+        } else {
+            // fp8 rows of D bytes: the two 16-byte chunks 4 ks + 2 half + {0, 1} of step ks
+            const int sw = T8::sw(rl);
+#pragma unroll
+            for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) kfo[2 * ks + c] = rl * T8::CH + ((4 * ks + 2 * half + c) ^ sw);
+        }
         vt_offsets<D>(lane, vo0, vo1);
     }
+    auto issue_tile = [&](const int* phys, uint4* sk, uint4* sv) {
+        if constexpr (F8) {
+            T8::issue_one(rk, phys, sk, w, lane);
+            TL::issue_one(rv, phys, sv, w, lane);
+        } else {
+            TL::issue(rk, rv, phys, sk, sv, w, lane);
+        }
+    };
     fill_phys(0, 0);
     __syncthreads();
-    TL::issue(rk, rv, s_phys[0], s_k0, s_v0, w, lane);
+    issue_tile(s_phys[0], s_k0, s_v0);
     if (ntiles > 1) fill_phys(1, 1);
     tile_ready();
 
     // one tile: loads of tile t+1 into (nk, nv) overlap the math on (sk, sv)
     auto step = [&](int t, int buf, const uint4* sk, const uint4* sv, uint4* nk, uint4* nv) {
-        if (t + 1 < ntiles) TL::issue(rk, rv, s_phys[buf ^ 1], nk, nv, w, lane);
+        if (t + 1 < ntiles) issue_tile(s_phys[buf ^ 1], nk, nv);
         if (active) {
+            f32x16 s0 = {}, s1 = {};
+            if constexpr (F8) {
+                // S^T for both 32-key blocks from fp8 K and Q: D/64 depth steps each
+                const uint4* k1s = sk + 32 * T8::CH;            // rows 32..63
+                uint4 a0[D / 32], a1[D / 32];
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) {
+                    a0[i] = sk[kfo[i]];
+                    a1[i] = k1s[kfo[i]];
+                }
+#pragma unroll
+                for (int ks = 0; ks < D / 64; ++ks) {
+                    const i32x8 f0 = {(int)a0[2 * ks].x, (int)a0[2 * ks].y, (int)a0[2 * ks].z, (int)a0[2 * ks].w,
+                                      (int)a0[2 * ks + 1].x, (int)a0[2 * ks + 1].y, (int)a0[2 * ks + 1].z,
+                                      (int)a0[2 * ks + 1].w};
+                    const i32x8 f1 = {(int)a1[2 * ks].x, (int)a1[2 * ks].y, (int)a1[2 * ks].z, (int)a1[2 * ks].w,
+                                      (int)a1[2 * ks + 1].x, (int)a1[2 * ks + 1].y, (int)a1[2 * ks + 1].z,
+                                      (int)a1[2 * ks + 1].w};
+                    s0 = mfma32x32x64_f8(f0, qf8[ks], s0);
+                    s1 = mfma32x32x64_f8(f1, qf8[ks], s1);
+                }
+            } else {
             // S^T for both 32-key blocks: two independent accumulation chains, the K
             // fragments read two depth steps ahead of their MFMAs (a ring of three)
             constexpr int KA = 2;
             const uint4* k1s = sk + 32 * TL::CH;                // rows 32..63
-            f32x16 s0 = {}, s1 = {};
             uint4 a0[KA + 1], a1[KA + 1];
 #pragma unroll
             for (int kk = 0; kk < KA; ++kk) {
@@ -222,6 +293,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void k_vbsa(
                 s0 = mfma32x32x16(a0[kk % (KA + 1)], qf[kk], s0);
                 s1 = mfma32x32x16(a1[kk % (KA + 1)], qf[kk], s1);
                 __builtin_amdgcn_sched_barrier(0);          // keep the reads KA steps ahead
+            }
             }
             // V^T fragments of keys 0..31, read now so that the softmax hides their latency
             uint4 vf[2][DB];
@@ -332,28 +404,37 @@ void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const
                  const int32_t* qoff, int qoff_stride, const int32_t* koff, int koff_stride,
                  const int32_t* blocks, int blocks_head_stride, int kblk, const int2* units,
                  int units_head_stride, const int32_t* nunits, int nunits_stride, int max_units,
-                 int unit_rows, void* out, int out_mode, hipStream_t st) {
+                 int unit_rows, void* out, int out_mode, hipStream_t st, const uint8_t* kp8,
+                 const uint32_t* qmax, const uint32_t* kmax) {
     const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     // 8 XCD slots per round of units: enough blocks for every head's units at any split
     dim3 grid(8 * ((max_units + 7) / 8), heads);
-#define SPR_VBSA(DD, MM, NW, VH)                                                               \
-    hipLaunchKernelGGL((k_vbsa<DD, MM, NW, VH>), grid, dim3(NW * 64), 0, st, qp, qperm, kp,     \
-                       static_cast<const bf16_t*>(vp), n, qoff, qoff_stride, koff, koff_stride,  \
-                       blocks, blocks_head_stride, kblk, units, units_head_stride, nunits,       \
-                       nunits_stride, heads, scale_log2, vmax, out)
+#define SPR_VBSA(DD, MM, NW, VH, F8, KP)                                                        \
+    hipLaunchKernelGGL((k_vbsa<DD, MM, NW, VH, F8>), grid, dim3(NW * 64), 0, st, qp, qperm,      \
+                       static_cast<const void*>(KP), static_cast<const bf16_t*>(vp), n, qoff,     \
+                       qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units,   \
+                       units_head_stride, nunits, nunits_stride, heads, scale_log2, vmax, qmax,  \
+                       kmax, out)
     // the sparse call: 4-wave blocks, fp32 output, fp16 V with its per-head scale
-    // (vmax != nullptr); the dense baseline: 8-wave blocks, bf16 V
-    if (unit_rows == kSparseRows && vmax) {
+    // (vmax != nullptr), and with kp8 the fp8 logits; the dense baseline: 8-wave blocks,
+    // bf16 V
+    if (unit_rows == kSparseRows && vmax && kp8) {
         if (d == 128) {
-            if (out_mode == 0) SPR_VBSA(128, 0, 4, true); else SPR_VBSA(128, 1, 4, true);
+            if (out_mode == 0) SPR_VBSA(128, 0, 4, true, true, kp8); else SPR_VBSA(128, 1, 4, true, true, kp8);
         } else {
-            if (out_mode == 0) SPR_VBSA(64, 0, 4, true); else SPR_VBSA(64, 1, 4, true);
+            if (out_mode == 0) SPR_VBSA(64, 0, 4, true, true, kp8); else SPR_VBSA(64, 1, 4, true, true, kp8);
+        }
+    } else if (unit_rows == kSparseRows && vmax) {
+        if (d == 128) {
+            if (out_mode == 0) SPR_VBSA(128, 0, 4, true, false, kp); else SPR_VBSA(128, 1, 4, true, false, kp);
+        } else {
+            if (out_mode == 0) SPR_VBSA(64, 0, 4, true, false, kp); else SPR_VBSA(64, 1, 4, true, false, kp);
         }
     } else {
         if (d == 128) {
-            if (out_mode == 0) SPR_VBSA(128, 0, 8, false); else SPR_VBSA(128, 1, 8, false);
+            if (out_mode == 0) SPR_VBSA(128, 0, 8, false, false, kp); else SPR_VBSA(128, 1, 8, false, false, kp);
         } else {
-            if (out_mode == 0) SPR_VBSA(64, 0, 8, false); else SPR_VBSA(64, 1, 8, false);
+            if (out_mode == 0) SPR_VBSA(64, 0, 8, false, false, kp); else SPR_VBSA(64, 1, 8, false, false, kp);
         }
     }
 #undef SPR_VBSA

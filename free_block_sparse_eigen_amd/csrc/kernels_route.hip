@@ -75,6 +75,39 @@ __global__ __launch_bounds__(256) void k_permute_f16(const bf16_t* __restrict__ 
     *reinterpret_cast<uint4*>(dst + ((size_t)h * n + row) * d + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Group-major permute of K into FP8 E4M3 scaled by 2^e(head) (f8_scale_exp of the head's
+// largest |k|): 16 values per thread, one 16-byte store.
+__global__ __launch_bounds__(256) void k_permute_f8(const bf16_t* __restrict__ src,
+                                                    const int32_t* __restrict__ perm, int n, int d,
+                                                    const uint32_t* __restrict__ kmax,
+                                                    uint8_t* __restrict__ dst) {
+    const int h = blockIdx.y;
+    const int chunks = d / 16;
+    const size_t i = blockIdx.x * (size_t)256 + threadIdx.x;
+    if (i >= (size_t)n * chunks) return;
+    const float scale = ldexpf(1.0f, f8_scale_exp(kmax[h]));
+    const int row = (int)(i / chunks), c = (int)(i % chunks);
+    const int from = perm[(size_t)h * n + row];
+    const bf16_t* s = src + ((size_t)h * n + from) * d + c * 16;
+    const uint4 a = *reinterpret_cast<const uint4*>(s), b = *reinterpret_cast<const uint4*>(s + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = pack_e4m3x4(bf16_to_f32((bf16_t)(w[2 * j] & 0xFFFF)) * scale,
+                           bf16_to_f32((bf16_t)(w[2 * j] >> 16)) * scale,
+                           bf16_to_f32((bf16_t)(w[2 * j + 1] & 0xFFFF)) * scale,
+                           bf16_to_f32((bf16_t)(w[2 * j + 1] >> 16)) * scale);
+    *reinterpret_cast<uint4*>(dst + ((size_t)h * n + row) * d + c * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+void launch_permute_k8(const bf16_t* src, const int32_t* perm, int heads, int n, int d, const uint32_t* kmax,
+                       uint8_t* dst, hipStream_t st) {
+    const size_t total = (size_t)n * (d / 16);
+    hipLaunchKernelGGL(k_permute_f8, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, st,
+                       src, perm, n, d, kmax, dst);
+}
+
 void launch_absmax_v(const bf16_t* src, int heads, int n, int d, uint32_t* vmax, hipStream_t st) {
     launch_fill_i32(reinterpret_cast<int32_t*>(vmax), 0, heads, st);
     const size_t per_head = (size_t)n * d;

@@ -93,6 +93,14 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        partition stage forks from and joins back into the caller's
                                        stream, so that their small launches overlap; the results
                                        are the same either way. */
+#define SPARSEPR_F_FP8_QK 64u       /* an experiment, not the method's precision: the sparse
+                                       kernel's logits Q K^T from Q and K rounded to FP8 E4M3
+                                       (OCP 8-bit float, largest magnitude 448) after per-head
+                                       power-of-two scales (the largest e with max|x| 2^e <= 448),
+                                       on the fp8 matrix instruction; P V, the probe rows, the fit
+                                       and the correction are unchanged. Quantization is the
+                                       extension "SparsePR稀疏注意力..." (framerc.cn) section 8.4
+                                       names. The workspace grows by one byte per K element. */
 #define SPARSEPR_F_CHECK_FINITE 4u  /* count non-finite values of q and k (partition), v (route)
                                        and o (correct) on the device; read the counts with
                                        sparsepr_get_stats. The stages stay asynchronous and do not

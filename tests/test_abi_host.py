@@ -285,4 +285,11 @@ def test_serial_partition_flag_is_accepted_alone_and_combined():
     for f in (spr.F_SERIAL_PARTITION, spr.F_SERIAL_PARTITION | spr.F_STAGE_TIMING,
               spr.F_SERIAL_PARTITION | spr.F_HOST_SOLVE | spr.F_CHECK_FINITE):
         assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=f, **kw)) == 0
-    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=64, **kw)) == 1
+    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=128, **kw)) == 1
+
+
+def test_fp8_logit_flag_grows_the_workspace_by_one_byte_per_key_element():
+    kw = dict(kv_groups=16, q_groups=16, density=0.25, probes=8, corr_rank=4)
+    base = spr.sparsepr_workspace_bytes(spr.make_params(2, 1024, 64, spr.BF16, **kw))
+    f8 = spr.sparsepr_workspace_bytes(spr.make_params(2, 1024, 64, spr.BF16, flags=spr.F_FP8_QK, **kw))
+    assert 2 * 1024 * 64 <= f8 - base <= 2 * 1024 * 64 + 3 * 256
