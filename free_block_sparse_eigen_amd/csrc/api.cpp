@@ -117,6 +117,10 @@ struct sparsepr_ctx {
     int32_t *klab = nullptr, *qlab = nullptr, *kperm = nullptr, *qperm = nullptr;
     int32_t *koff = nullptr, *qoff = nullptr;
     int32_t *flag_cnt = nullptr, *flag_list = nullptr, *blkhist = nullptr, *blkoff = nullptr;
+    // candidate lists of the recheck queue (full metric, streamed centroids: large G)
+    int32_t *cand = nullptr, *ncand = nullptr, *ovf_cnt = nullptr, *ovf_list = nullptr;
+    double* crow = nullptr;            // [H][G][d] row-major screening vectors / coordinates
+    double* ycoord = nullptr;          // [H][N][r_K] every key's coordinates x W (candidate recheck)
     double *mk = nullptr, *w64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
     // device eigensolve of M_K: tridiagonal form, reflectors, eigenpairs, |T|, gap
     double *eig_diag = nullptr, *eig_off = nullptr, *eig_hv = nullptr, *eig_beta = nullptr;
@@ -293,6 +297,15 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.qoff, H * (c.Gq + 1));
     a.take(c.flag_cnt, 2 * (size_t)c.T * H);
     a.take(c.flag_list, HN);
+    if (assign_streams(c.Gq, (int)d) || assign_streams(c.Gk, (int)d)) {
+        a.take(c.cand, HN * kMaxCandidates);
+        a.take(c.ncand, HN);
+        a.take(c.crow, H * c.gmax * d);
+        a.take(c.ovf_cnt, H);
+        a.take(c.ovf_list, HN);
+        if (assign_streams(c.Gk, (int)d) && !c.raw && !c.svoo && c.rK <= kCandidateMaxDim)
+            a.take(c.ycoord, HN * c.rK);
+    }
     a.take(c.blkhist, H * c.nblk * c.gmax);
     a.take(c.blkoff, H * c.nblk * c.gmax);
     a.take(c.mk, H * d * d);
@@ -413,6 +426,32 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 // counting sort -> fp64 means and centroids. The metric is the factor l64 [d][dim], or
 // with dim == 0 the full metric l64 [d][d]. After the last round `sorted`/`off` are the
 // stable group-major permutation and `mean_raw` the raw group means (zero if empty).
+// The fp64 recheck of the queued points of heads h0 .. h0 + hh - 1 (x, l64, c64, c2_64,
+// labels, flags already offset to h0): with streamed centroids (large G) the queue is
+// screened again for candidate lists first, so that only those are checked.
+int32_t recheck(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const double* l64,
+                const double* c64, const double* c2_64, const bf16_t* cpart, const float* cn2,
+                const float* cpn, int groups, const int32_t* fc, int32_t* labels, hipStream_t st) {
+    const size_t h = h0, N = c->N;
+    const int32_t* flag_list = c->flag_list + h * N;
+    if (c->cand && assign_streams(groups, c->d) && dim <= kCandidateMaxDim) {
+        int32_t* cand = c->cand + h * N * kMaxCandidates;
+        int32_t* ncand = c->ncand + h * N;
+        int32_t* ovf_cnt = c->ovf_cnt + h;
+        int32_t* ovf_list = c->ovf_list + h * N;
+        launch_candidates(x, hh, c->N, c->d, cpart, cn2, cpn, groups, fc, flag_list, cand, ncand, ovf_cnt,
+                          ovf_list, st);
+        const double* yc = (dim > 0 && c->ycoord) ? c->ycoord + h * N * dim : nullptr;
+        launch_recheck_cand(x, hh, c->N, c->d, l64, dim, c->crow + h * c->gmax * c->d, c2_64, groups, fc,
+                            flag_list, cand, ncand, yc, labels, st);
+        launch_recheck(x, hh, c->N, c->d, l64, dim, c64, c2_64, groups, ovf_cnt, ovf_list, labels, st);
+    } else {
+        launch_recheck(x, hh, c->N, c->d, l64, dim, c64, c2_64, groups, fc, flag_list, labels, st);
+    }
+    SPR_LAUNCHED(c, "recheck");
+    return SPARSEPR_OK;
+}
+
 int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const double* l64, int groups,
               int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
               double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st) {
@@ -430,21 +469,26 @@ int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const d
     cpn += h * groups;
     c2_64 += h * groups;
     int32_t* flag_list = c->flag_list + h * N;
-    int32_t* blkhist = c->blkhist + h * c->nblk * groups;
-    int32_t* blkoff = c->blkoff + h * c->nblk * groups;
+    // per-head-group bases at gmax strides: a group's key side and another's query side
+    // (different G) run at once and must not share rows
+    int32_t* blkhist = c->blkhist + h * c->nblk * c->gmax;
+    int32_t* blkoff = c->blkoff + h * c->nblk * c->gmax;
+    // each head group's rows start at h0 gmax d: the key side's narrower rows and the query
+    // side's wider ones of two groups running at once never overlap
+    double* crow = c->crow ? c->crow + h * c->gmax * c->d : nullptr;
     launch_seed_centroids(x, hh, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
-                          cpn, c2_64, st);
+                          cpn, c2_64, st, crow);
     SPR_LAUNCHED(c, "seed centroids");
     for (int t = 0; t < c->T; ++t) {
         int32_t* fc = flags + (size_t)t * c->H + h;
         launch_assign(x, hh, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, flag_list, st);
         SPR_LAUNCHED(c, "assign");
-        launch_recheck(x, hh, c->N, c->d, l64, dim, c64, c2_64, groups, fc, flag_list, labels, st);
-        SPR_LAUNCHED(c, "recheck");
+        int32_t rc = recheck(c, h0, hh, x, dim, l64, c64, c2_64, cpart, cn2, cpn, groups, fc, labels, st);
+        if (rc) return rc;
         launch_counting_sort(labels, hh, c->N, groups, blkhist, blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");
         launch_group_means(x, hh, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
-                           cn2, cpn, c2_64, st);
+                           cn2, cpn, c2_64, st, crow);
         SPR_LAUNCHED(c, "group means");
     }
     return SPARSEPR_OK;
@@ -650,6 +694,7 @@ namespace {
 // from the raw means under each new metric, empty groups included (zero centroid).
 int32_t partition_svoo(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
     const int H = c->H, N = c->N, d = c->d;
+    int32_t rc;
     launch_seed_raw(k16, H, N, d, c->Gk, c->weyl_a, c->kraw, st);
     launch_seed_raw(q16, H, N, d, c->Gq, c->weyl_a, c->qraw, st);
     SPR_LAUNCHED(c, "co-clustering seeds");
@@ -658,18 +703,22 @@ int32_t partition_svoo(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hi
         int32_t* fq = c->flag_cnt + (size_t)(c->T + t) * H;
         // keys against the current query centroids
         launch_gram_f64(c->qraw, H, c->Gq, d, 1.0 / d, c->mk, st);
-        launch_finish_all(c->kraw, H, d, c->mk, 0, c->Gk, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st);
+        launch_finish_all(c->kraw, H, d, c->mk, 0, c->Gk, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, st, c->crow);
         launch_assign(k16, H, N, d, c->kcp, c->kcn2, c->kcpn, c->Gk, c->klab, fk, c->flag_list, st);
-        launch_recheck(k16, H, N, d, c->mk, 0, c->kc64, c->kc2, c->Gk, fk, c->flag_list, c->klab, st);
+        if ((rc = recheck(c, 0, H, k16, 0, c->mk, c->kc64, c->kc2, c->kcp, c->kcn2, c->kcpn, c->Gk, fk,
+                          c->klab, st)))
+            return rc;
         launch_counting_sort(c->klab, H, N, c->Gk, c->blkhist, c->blkoff, c->kperm, c->koff, st);
         launch_group_means(k16, H, N, d, c->kperm, c->koff, c->Gk, c->kraw, nullptr, 0, nullptr, nullptr,
                            nullptr, nullptr, nullptr, st);
         SPR_LAUNCHED(c, "co-clustering keys");
         // queries against the updated key centroids
         launch_gram_f64(c->kraw, H, c->Gk, d, 1.0 / d, c->mq, st);
-        launch_finish_all(c->qraw, H, d, c->mq, 0, c->Gq, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st);
+        launch_finish_all(c->qraw, H, d, c->mq, 0, c->Gq, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, st, c->crow);
         launch_assign(q16, H, N, d, c->qcp, c->qcn2, c->qcpn, c->Gq, c->qlab, fq, c->flag_list, st);
-        launch_recheck(q16, H, N, d, c->mq, 0, c->qc64, c->qc2, c->Gq, fq, c->flag_list, c->qlab, st);
+        if ((rc = recheck(c, 0, H, q16, 0, c->mq, c->qc64, c->qc2, c->qcp, c->qcn2, c->qcpn, c->Gq, fq,
+                          c->qlab, st)))
+            return rc;
         launch_counting_sort(c->qlab, H, N, c->Gq, c->blkhist, c->blkoff, c->qperm, c->qoff, st);
         launch_group_means(q16, H, N, d, c->qperm, c->qoff, c->Gq, c->qraw, nullptr, 0, nullptr, nullptr,
                            nullptr, nullptr, nullptr, st);
@@ -684,6 +733,11 @@ int32_t partition_svoo(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hi
 int32_t partition_heads(sparsepr_ctx* c, int h0, int hh, const bf16_t* q16, const bf16_t* k16,
                         hipStream_t s, hipEvent_t keys_done) {
     const size_t h = h0, d = c->d;
+    if (c->ycoord) {                    // every key's W coordinates, for the candidate recheck
+        launch_coords(k16 + h * c->N * d, hh, c->N, c->d, c->w64 + h * d * c->rK, c->rK,
+                      c->ycoord + h * c->N * c->rK, s);
+        SPR_LAUNCHED(c, "key coordinates");
+    }
     int32_t rc = lloyd(c, h0, hh, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff,
                        c->kraw, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, s);
     if (rc) return rc;

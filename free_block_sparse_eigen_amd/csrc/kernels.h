@@ -41,22 +41,42 @@ void launch_seed_raw(const bf16_t* x, int heads, int n, int d, int groups, int64
                      hipStream_t st);
 // screening tables of every centroid (empty groups included) from raw means and a metric
 void launch_finish_all(const double* mean_raw, int heads, int d, const double* l64, int dout, int groups,
-                       double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st);
+                       double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st,
+                       double* crow = nullptr);
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
-                           float* cn2, float* cpn, double* c2_64, hipStream_t st);
+                           float* cn2, float* cpn, double* c2_64, hipStream_t st, double* crow = nullptr);
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st);
 void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
                     const double* c64, const double* c2_64, int groups, const int32_t* flag_count,
                     const int32_t* flag_list, int32_t* labels, hipStream_t st);
+// Candidate lists for a long recheck queue when k_assign streams the centroids
+// (assign_streams): cand [heads][n][kMaxCandidates], ncand [heads][n] by
+// queue position (-1: too many, the point is queued in ovf_count/ovf_list [heads][n] for
+// launch_recheck); then the fp64 recheck over them.
+constexpr int kMaxCandidates = 32;
+constexpr int kCandidateMaxDim = 32;     // factor widths above this take the full recheck
+bool assign_streams(int groups, int d);
+void launch_candidates(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
+                       const float* cpn, int groups, const int32_t* flag_count, const int32_t* flag_list,
+                       int32_t* cand, int32_t* ncand, int32_t* ovf_count, int32_t* ovf_list, hipStream_t st);
+void launch_recheck_cand(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
+                         const double* crow, const double* c2_64, int groups, const int32_t* flag_count,
+                         const int32_t* flag_list, const int32_t* cand, const int32_t* ncand,
+                         const double* ycoord, int32_t* labels, hipStream_t st);
+// every point's factor coordinates y = x L [heads][n][dim], as the recheck forms them
+void launch_coords(const bf16_t* x, int heads, int n, int d, const double* l64, int dim, double* y,
+                   hipStream_t st);
 void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, int32_t* blkhist,
                           int32_t* blkoff, int32_t* sorted, int32_t* off, hipStream_t st);
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
-                        double* c2_64, hipStream_t st);
+                        double* c2_64, hipStream_t st, double* crow = nullptr);
+// crow (optional): a row-major [heads][groups][d or dout] copy of the screening vectors
+// (full metric) or of the centroid coordinates (factor) for the candidate recheck
 
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
                                                 const int32_t* __restrict__ off,
                                                 double* __restrict__ c64, bf16_t* __restrict__ cpart,
                                                 float* __restrict__ cn2, float* __restrict__ cpn,
-                                                double* __restrict__ c2_64) {
+                                                double* __restrict__ c2_64, double* __restrict__ crow) {
     constexpr int G = kFinG;
     const bool full = dout == 0;                 // full metric M [d][d]
     __shared__ double s_m[G][129];               // means (padded rows)
@@ -225,10 +225,12 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         for (int j = lane; j < dout; j += 64) {
             const double cv = s_c[gs][j];
             c64[((size_t)h * dout + j) * groups + g] = cv;          // coordinate-major
+            if (crow && !full) crow[((size_t)h * groups + g) * dout + j] = cv;   // row-major copy
             a += full ? s_m[gs][j] * cv : cv * cv;
         }
         for (int i = lane; i < d; i += 64) {
             const double sv = full ? s_c[gs][i] : s_s[gs][i];
+            if (crow && full) crow[((size_t)h * groups + g) * d + i] = sv;       // row-major copy
             const bf16_t hi = f32_to_bf16((float)sv);
             cpart[((size_t)(h * 2 + 0) * groups + g) * d + i] = hi;
             cpart[((size_t)(h * 2 + 1) * groups + g) * d + i] = f32_to_bf16((float)(sv - (double)bf16_to_f32(hi)));
@@ -246,9 +248,9 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
 
 static void launch_finish(const double* mean_raw, int heads, int d, const double* l64, int dout,
                           int groups, const int32_t* off, double* c64, bf16_t* cpart, float* cn2,
-                          float* cpn, double* c2_64, hipStream_t st) {
+                          float* cpn, double* c2_64, hipStream_t st, double* crow) {
     hipLaunchKernelGGL(k_finish, dim3((groups + kFinG - 1) / kFinG, heads), dim3(256), 0, st, mean_raw,
-                       d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64);
+                       d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, crow);
 }
 
 // ------------------------------------------------------------------- seeds ---
@@ -266,15 +268,17 @@ void launch_seed_raw(const bf16_t* x, int heads, int n, int d, int groups, int64
 }
 
 void launch_finish_all(const double* mean_raw, int heads, int d, const double* l64, int dout, int groups,
-                       double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st) {
-    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st);
+                       double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st,
+                       double* crow) {
+    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st, crow);
 }
 
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
-                           float* cn2, float* cpn, double* c2_64, hipStream_t st) {
+                           float* cn2, float* cpn, double* c2_64, hipStream_t st,
+                           double* crow) {
     hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, groups, a, mean_raw);
-    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st);
+    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st, crow);
 }
 
 // ------------------------------------------------------------------ assign ---
@@ -307,6 +311,8 @@ void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const doubl
 // written into it).
 constexpr int kAssignTG = 64;
 constexpr int kAssignResBytes = 128 * 1024;
+constexpr int kMaxCand = kMaxCandidates;          // candidate centroids listed per queued point
+constexpr int kCandMaxDim = kCandidateMaxDim;     // largest factor width the candidate recheck takes
 constexpr float kPadScore = 3.0e38f;
 
 // a score with accumulator slot r (0..15) in its four low mantissa bits
@@ -364,12 +370,73 @@ struct AssignWave {
         }
     }
 
+    // as load, for the queued points q_base .. q_base + 63 of the head's queue fl (count
+    // entries; a lane past the end reads the last queued point and is zeroed)
+    __device__ __attribute__((always_inline)) void load_queued(const bf16_t* __restrict__ x, int n, int h,
+                                                               const int32_t* __restrict__ fl, int q_base,
+                                                               int count, int lane) {
+        const int half = lane >> 5;
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            const int pt = fl[min(q_base + 32 * pb + (lane & 31), count - 1)];
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                xf[pb][kk] = *reinterpret_cast<const uint4*>(x + ((size_t)h * n + pt) * D + 16 * kk + 8 * half);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            const bool valid = q_base + 32 * pb + (lane & 31) < count;
+            float ss = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                if (!valid) xf[pb][kk] = make_uint4(0, 0, 0, 0);
+                const uint4 v = xf[pb][kk];
+                const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_to_f32((bf16_t)(wd[e] & 0xFFFF));
+                    const float hi = bf16_to_f32((bf16_t)(wd[e] >> 16));
+                    ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+                }
+            }
+            ss += __shfl_xor(ss, 32, 64);
+            xn[pb] = sqrtf(ss) * 1.000001f;
+            best[pb] = INFINITY;
+            second[pb] = INFINITY;
+            bg[pb] = 0x7fffffff;
+        }
+    }
+
+    // After the scores: the window [.., thr] of screened scores that can hold the exact
+    // argmin. A centroid whose screened score s passes the certification test against the
+    // best b (s - b > the test's margin at (s, b)) is certifiably worse than the best, so
+    // only s <= b + W (1 + c) can win, with W the margin at s2 = b and c its coefficient of
+    // |s2|, which covers the larger |s|; thr = b + 1.25 W keeps a wide safety factor
+    // (both halves of the wave get the same value).
+    __device__ __attribute__((always_inline)) float window(int pb, float c2max, float cpmax) const {
+        const float b = fminf(best[pb], __shfl_xor(best[pb], 32, 64));
+        const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
+        const float W = 2.4f * A + (2.4f * kU + 3.814697265625e-06f) * (2.f * fabsf(b)) + 1e-30f;
+        return b + 1.25f * W;
+    }
+
     // scores against centroid tile t held at buf: the products of both 32-centroid
     // sub-tiles run together (four independent accumulator chains), each sub-tile's
     // sums in the same order (hi then lo over the depth); then the scores in sub-tile
     // order
     __device__ __attribute__((always_inline)) void tile(int t, const uint4* buf, int groups,
                                                         const float* s_cn2, int lane) {
+        const int half = lane >> 5;
+        tile_with(t, buf, groups, lane, [&](const f32x16 (&acc)[2], int gb) __attribute__((always_inline)) {
+            scores(acc, gb, s_cn2, half);
+        });
+    }
+
+    // the products of tile t, then epi(acc, gb) for each 32-centroid sub-tile holding groups
+    template <typename EPI>
+    __device__ __attribute__((always_inline)) void tile_with(int t, const uint4* buf, int groups,
+                                                             int lane, EPI&& epi) {
         const int half = lane >> 5;
         constexpr int KS = D / 16, PF = 2;
         const uint4* cr0 = buf + (lane & 31) * CH;
@@ -409,7 +476,7 @@ struct AssignWave {
         for (int sub = 0; sub < TG / 32; ++sub) {
             const int gb = t * TG + 32 * sub;
             if (gb >= groups) break;
-            scores(acc[sub], gb, s_cn2, half);
+            epi(acc[sub], gb);
         }
     }
 
@@ -613,6 +680,314 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
     aw.finish(n, h, groups, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
 }
 
+// ------------------------------------------------------------- candidates ---
+// For a long recheck queue (large G, the full metric): the queued points are screened again
+// (same MFMA products and error bound as k_assign) in two passes over the centroid tiles,
+// the first for each point's best score and window, the second listing the centroids whose
+// screened score lies in the window; the exact argmin is among them, so the fp64 recheck
+// (k_recheck_cand) needs only those. A point with more than kMaxCand goes to a second queue
+// (ovf_list) for the full recheck.
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_candidates(const bf16_t* __restrict__ x, int n,
+                                                       const bf16_t* __restrict__ cpart,
+                                                       const float* __restrict__ cn2,
+                                                       const float* __restrict__ cpn, int groups,
+                                                       const int32_t* __restrict__ flag_count,
+                                                       const int32_t* __restrict__ flag_list,
+                                                       int32_t* __restrict__ cand,
+                                                       int32_t* __restrict__ ncand,
+                                                       int32_t* __restrict__ ovf_count,
+                                                       int32_t* __restrict__ ovf_list) {
+    using AW = AssignWave<D>;
+    constexpr int CH = AW::CH, TG = kAssignTG, SLOTS = AW::SLOTS;
+    constexpr int PER = SLOTS / 256;
+    __shared__ uint4 s_c0[SLOTS];
+    __shared__ uint4 s_c1[SLOTS];
+    __shared__ float s_cn2[kMaxGroups + TG];
+    __shared__ float s_red[8];
+    __shared__ int s_nc[4][64];
+    __shared__ int s_cd[4][64][kMaxCand];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int count = flag_count[h];
+    if (blockIdx.x * 256 >= count) return;            // the whole block: no queued point
+    const int ntiles = (groups + TG - 1) / TG;
+    const rsrc_t rc = make_rsrc(cpart + (size_t)h * 2 * groups * D, (uint32_t)(2 * groups * D * 2));
+    auto issue = [&](int t, uint4* buf) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int first = (w * PER + m) * 64;
+            const int slot = first + lane;
+            const int part = slot / (TG * CH), rem = slot % (TG * CH);
+            const int row = rem / CH, pc = rem % CH;
+            const int g = min(t * TG + row, groups - 1);
+            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8)) * 2);
+        }
+    };
+    const int q_base = blockIdx.x * 256 + w * 64;
+    const int32_t* fl = flag_list + (size_t)h * n;
+    s_nc[w][lane] = 0;
+    issue(0, s_c0);
+    AW aw;
+    aw.load_queued(x, n, h, fl, q_base, count, lane);
+    float c2max, cpmax;
+    assign_norms<256>(cn2, cpn, h, groups, ntiles, s_cn2, s_red, c2max, cpmax);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int half = lane >> 5;
+    float thr[2] = {0.f, 0.f};
+    // pass 0: best scores; pass 1: the window's centroids (tile 0 is reloaded between them)
+    for (int pass = 0; pass < 2; ++pass) {
+        auto run = [&](int t, const uint4* buf) {
+            if (pass == 0) {
+                aw.tile(t, buf, groups, s_cn2, lane);
+            } else {
+                aw.tile_with(t, buf, groups, lane, [&](const f32x16 (&acc)[2], int gb) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int g = gb + 8 * (r >> 2) + 4 * half + (r & 3);
+                        const float c2 = s_cn2[g];
+#pragma unroll
+                        for (int pb = 0; pb < 2; ++pb) {
+                            if (fmaf(-2.f, acc[pb][r], c2) <= thr[pb]) {
+                                const int p = 32 * pb + (lane & 31);
+                                const int slot = atomicAdd(&s_nc[w][p], 1);
+                                if (slot < kMaxCand) s_cd[w][p][slot] = g;
+                            }
+                        }
+                    }
+                });
+            }
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            if (t + 1 < ntiles) issue(t + 1, s_c1);
+            run(t, s_c0);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (t + 1 >= ntiles) break;
+            if (t + 2 < ntiles) issue(t + 2, s_c0);
+            run(t + 1, s_c1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        if (pass == 0) {
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb) thr[pb] = aw.window(pb, c2max, cpmax);
+            issue(0, s_c0);                           // every wave is past its last tile read
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    }
+    // the lists of this wave's points, by queue position
+    const int qi = q_base + lane;
+    if (qi < count) {
+        const int nc = s_nc[w][lane];
+        const bool listed = nc >= 1 && nc <= kMaxCand;
+        ncand[(size_t)h * n + qi] = listed ? nc : -1;
+        for (int c = 0; c < min(nc, kMaxCand); ++c) cand[((size_t)h * n + qi) * kMaxCand + c] = s_cd[w][lane][c];
+        if (!listed) {                                // to the full recheck
+            const int slot = atomicAdd(&ovf_count[h], 1);
+            ovf_list[(size_t)h * n + slot] = fl[qi];
+        }
+    }
+}
+
+// The fp64 recheck of a queued point over its candidate list: the same products, in the
+// same order, as k_recheck, so that both give the same distances. With the full metric
+// (dim 0) |c|^2 - 2 x . C'; with a factor L [D][dim] the point's coordinates y = x L (the
+// two halves of the depth summed separately, then added) and |y - c|^2. crow holds the
+// screening vectors C' (full) or the centroid coordinates (factor) row by row, so each
+// candidate is one contiguous row. The lowest index wins among equal distances.
+template <int D>
+__global__ __launch_bounds__(256) void k_recheck_cand(const bf16_t* __restrict__ x, int n,
+                                                      const double* __restrict__ l64, int dim,
+                                                      const double* __restrict__ crow,
+                                                      const double* __restrict__ c2_64, int groups,
+                                                      const int32_t* __restrict__ flag_count,
+                                                      const int32_t* __restrict__ flag_list,
+                                                      const int32_t* __restrict__ cand,
+                                                      const int32_t* __restrict__ ncand,
+                                                      const double* __restrict__ ycoord,
+                                                      int32_t* __restrict__ labels) {
+    const int h = blockIdx.y;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= flag_count[h]) return;
+    const int nc = ncand[(size_t)h * n + i];
+    if (nc < 0) return;                               // in the full recheck's queue
+    const int p = flag_list[(size_t)h * n + i];
+    const bf16_t* xr = x + ((size_t)h * n + p) * D;
+    const bool full = dim == 0;
+    const int cdim = full ? D : dim;
+    const double* ch = crow + (size_t)h * groups * cdim;
+    uint32_t xw[D / 2];                               // the point, two bf16 per word
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const uint4 u = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        xw[4 * c] = u.x;
+        xw[4 * c + 1] = u.y;
+        xw[4 * c + 2] = u.z;
+        xw[4 * c + 3] = u.w;
+    }
+    auto xv = [&](int ii) __attribute__((always_inline)) {
+        const uint32_t wd = xw[ii >> 1];
+        return (double)bf16_to_f32((bf16_t)((ii & 1) ? (wd >> 16) : (wd & 0xFFFF)));
+    };
+    // the factor's coordinates y = x L: each half of the depth summed in order on its own,
+    // then the two halves added (as k_recheck does)
+    double y[kCandMaxDim];
+    if (!full && ycoord) {                            // computed for every point beforehand
+        const double* yr = ycoord + ((size_t)h * n + p) * dim;
+#pragma unroll
+        for (int jj = 0; jj < kCandMaxDim; ++jj) y[jj] = jj < dim ? yr[jj] : 0.0;
+    } else if (!full) {
+        const double* lh = l64 + (size_t)h * D * dim;
+        double y1[kCandMaxDim];
+#pragma unroll
+        for (int jj = 0; jj < kCandMaxDim; ++jj) y[jj] = y1[jj] = 0.0;
+#pragma unroll 2
+        for (int ii = 0; ii < D / 2; ++ii) {
+            const double xi = (double)bf16_to_f32(xr[ii]);
+            const double* lr = lh + (size_t)ii * dim;
+#pragma unroll
+            for (int jj = 0; jj < kCandMaxDim; ++jj)
+                if (jj < dim) y[jj] = fma(xi, lr[jj], y[jj]);
+        }
+#pragma unroll 2
+        for (int ii = D / 2; ii < D; ++ii) {
+            const double xi = (double)bf16_to_f32(xr[ii]);
+            const double* lr = lh + (size_t)ii * dim;
+#pragma unroll
+            for (int jj = 0; jj < kCandMaxDim; ++jj)
+                if (jj < dim) y1[jj] = fma(xi, lr[jj], y1[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kCandMaxDim; ++jj) y[jj] = y[jj] + y1[jj];
+    }
+    double best = INFINITY;
+    int bg = 0x7fffffff;
+    for (int c = 0; c < nc; ++c) {
+        const int g = cand[((size_t)h * n + i) * kMaxCand + c];
+        if (g >= groups) continue;
+        const double* cg = ch + (size_t)g * cdim;
+        double dist;
+        if (full) {
+            double acc = 0.0;
+#pragma unroll
+            for (int j0 = 0; j0 < D; j0 += 16) {      // loads 16 at a time, sums in order
+                double cv[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) cv[u] = cg[j0 + u];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) acc = fma(xv(j0 + u), cv[u], acc);
+            }
+            dist = fma(-2.0, acc, c2_64[(size_t)h * groups + g]);
+        } else {
+            double acc = 0.0;
+#pragma unroll
+            for (int jj = 0; jj < kCandMaxDim; ++jj) {
+                if (jj < dim) {
+                    const double t = y[jj] - cg[jj];
+                    acc = fma(t, t, acc);
+                }
+            }
+            dist = acc;
+        }
+        if (dist < best || (dist == best && g < bg)) {
+            best = dist;
+            bg = g;
+        }
+    }
+    labels[(size_t)h * n + p] = bg < groups ? bg : 0;
+}
+
+void launch_candidates(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
+                       const float* cpn, int groups, const int32_t* flag_count, const int32_t* flag_list,
+                       int32_t* cand, int32_t* ncand, int32_t* ovf_count, int32_t* ovf_list, hipStream_t st) {
+    launch_fill_i32(ovf_count, 0, heads, st);
+    dim3 grid((n + 255) / 256, heads);
+    if (d == 128)
+        hipLaunchKernelGGL(k_candidates<128>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
+                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list);
+    else
+        hipLaunchKernelGGL(k_candidates<64>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
+                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list);
+}
+
+void launch_recheck_cand(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
+                         const double* crow, const double* c2_64, int groups, const int32_t* flag_count,
+                         const int32_t* flag_list, const int32_t* cand, const int32_t* ncand,
+                         const double* ycoord, int32_t* labels, hipStream_t st) {
+    const dim3 grid((n + 255) / 256, heads);
+    if (d == 128)
+        hipLaunchKernelGGL(k_recheck_cand<128>, grid, dim3(256), 0, st, x, n, l64, dim, crow, c2_64, groups,
+                           flag_count, flag_list, cand, ncand, ycoord, labels);
+    else
+        hipLaunchKernelGGL(k_recheck_cand<64>, grid, dim3(256), 0, st, x, n, l64, dim, crow, c2_64, groups,
+                           flag_count, flag_list, cand, ncand, ycoord, labels);
+}
+
+// Every point's coordinates y = x L [n][dim], each half of the depth summed in order, then
+// the halves added: the values k_recheck forms for a queued point, once per call instead of
+// once per queued point and round. A thread per point keeps its row in registers and reads
+// the rows of L (staged in LDS, the same row for every lane) as it goes.
+template <int D>
+__global__ __launch_bounds__(256, 1) void k_coords(const bf16_t* __restrict__ x, int n,
+                                                const double* __restrict__ l64, int dim,
+                                                double* __restrict__ y) {
+    constexpr int M = kCandMaxDim;
+    __shared__ __attribute__((aligned(16))) double s_l[D * M];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const double* lh = l64 + (size_t)h * D * dim;
+    for (int e = tid; e < D * M; e += 256) {
+        const int ii = e / M, jj = e % M;
+        s_l[e] = jj < dim ? lh[(size_t)ii * dim + jj] : 0.0;
+    }
+    __syncthreads();
+    const int p = blockIdx.x * 256 + tid;
+    if (p >= n) return;
+    const bf16_t* xr = x + ((size_t)h * n + p) * D;
+    double part[2][M];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int jj = 0; jj < M; ++jj) part[hf][jj] = 0.0;
+        // eight depth entries (one 16-byte load of the row) at a time, in order
+#pragma unroll 1
+        for (int i0 = hf * (D / 2); i0 < (hf + 1) * (D / 2); i0 += 8) {
+            const uint4 u = *reinterpret_cast<const uint4*>(xr + i0);
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double xi = (double)bf16_to_f32((bf16_t)((e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xFFFF)));
+                const double2* lr = reinterpret_cast<const double2*>(s_l + (i0 + e) * M);
+#pragma unroll
+                for (int jj = 0; jj < M; jj += 2) {
+                    const double2 l2 = lr[jj / 2];
+                    part[hf][jj] = fma(xi, l2.x, part[hf][jj]);
+                    part[hf][jj + 1] = fma(xi, l2.y, part[hf][jj + 1]);
+                }
+            }
+        }
+    }
+    double* yr = y + ((size_t)h * n + p) * dim;
+#pragma unroll
+    for (int jj = 0; jj < M; ++jj)
+        if (jj < dim) yr[jj] = part[0][jj] + part[1][jj];
+}
+
+void launch_coords(const bf16_t* x, int heads, int n, int d, const double* l64, int dim, double* y,
+                   hipStream_t st) {
+    const dim3 grid((unsigned)((n + 255) / 256), heads);
+    if (d == 128)
+        hipLaunchKernelGGL(k_coords<128>, grid, dim3(256), 0, st, x, n, l64, dim, y);
+    else
+        hipLaunchKernelGGL(k_coords<64>, grid, dim3(256), 0, st, x, n, l64, dim, y);
+}
+
+bool assign_streams(int groups, int d) {
+    const int ntiles = (groups + kAssignTG - 1) / kAssignTG;
+    return (size_t)ntiles * kAssignTG * 2 * d * 2 > (size_t)kAssignResBytes;
+}
+
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
                    int32_t* flag_list, hipStream_t st) {
@@ -701,12 +1076,12 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
 #pragma unroll
-                        for (int b = 0; b < RB; ++b) s[b] += xs[i + u][b] * lv[u];
+                        for (int b = 0; b < RB; ++b) s[b] = fma(xs[i + u][b], lv[u], s[b]);
                 }
                 for (; i < i1; ++i) {
                     const double l = lh[(size_t)i * dim + j];
 #pragma unroll
-                    for (int b = 0; b < RB; ++b) s[b] += xs[i][b] * l;
+                    for (int b = 0; b < RB; ++b) s[b] = fma(xs[i][b], l, s[b]);
                 }
 #pragma unroll
                 for (int b = 0; b < RB; ++b) part[hf][j][b] = s[b];
@@ -736,16 +1111,16 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
 #pragma unroll
-                        for (int b = 0; b < RB; ++b) acc[b] += xs[j + u][b] * cv[u];
+                        for (int b = 0; b < RB; ++b) acc[b] = fma(xs[j + u][b], cv[u], acc[b]);
                 }
                 for (; j < d; ++j) {
                     const double cj = c[(size_t)j * groups];
 #pragma unroll
-                    for (int b = 0; b < RB; ++b) acc[b] += xs[j][b] * cj;
+                    for (int b = 0; b < RB; ++b) acc[b] = fma(xs[j][b], cj, acc[b]);
                 }
                 const double c2 = c2_64[(size_t)h * groups + g];
 #pragma unroll
-                for (int b = 0; b < RB; ++b) acc[b] = c2 - 2.0 * acc[b];
+                for (int b = 0; b < RB; ++b) acc[b] = fma(-2.0, acc[b], c2);
             } else {
                 int j = 0;
                 for (; j + 16 <= dim; j += 16) {
@@ -757,7 +1132,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
                         for (int b = 0; b < RB; ++b) {
                             const double t = ys[j + u][b] - cv[u];
-                            acc[b] += t * t;
+                            acc[b] = fma(t, t, acc[b]);
                         }
                 }
                 for (; j < dim; ++j) {
@@ -765,7 +1140,7 @@ __global__ __launch_bounds__(256) void k_recheck(const bf16_t* __restrict__ x, i
 #pragma unroll
                     for (int b = 0; b < RB; ++b) {
                         const double t = ys[j][b] - cj;
-                        acc[b] += t * t;
+                        acc[b] = fma(t, t, acc[b]);
                     }
                 }
             }
@@ -1018,7 +1393,7 @@ __global__ __launch_bounds__(512) void k_group_sum(const bf16_t* __restrict__ x,
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
-                        double* c2_64, hipStream_t st) {
+                        double* c2_64, hipStream_t st, double* crow) {
     if (d == 128)
         hipLaunchKernelGGL(k_group_sum<128>, dim3(groups, heads), dim3(512), 0, st, x, n, sorted, off,
                            groups, mean_raw);
@@ -1026,7 +1401,7 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
         hipLaunchKernelGGL(k_group_sum<64>, dim3(groups, heads), dim3(512), 0, st, x, n, sorted, off,
                            groups, mean_raw);
     if (l64 != nullptr)
-        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, st);
+        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, st, crow);
 }
 
 }  // namespace spr

@@ -57,8 +57,11 @@ def _same(a, b, what):
 
 
 @pytest.mark.timeout(600)
-def test_split_partition_matches_serial_and_oracle(spr):
+@pytest.mark.parametrize("groups", [None, (96, 160)], ids=["C2", "C2-Gk96-Gq160"])
+def test_split_partition_matches_serial_and_oracle(spr, groups):
     cfg = get_config("C2")
+    if groups is not None:                      # unequal G: the groups' scratch rows differ
+        cfg = cfg.with_settings(kv_groups=groups[0], q_groups=groups[1])
     say(f"C2 split partition: generating heads {HEADS}, N={cfg.n}")
     q, k, v = make_inputs(cfg, heads=HEADS)
     dt = spr.BF16 if cfg.dtype == "bf16" else spr.F32
