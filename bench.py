@@ -41,6 +41,9 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+TRAFFIC_WORKLOAD = "C3 rho=0.26"        # the workload the committed traffic counters ran on
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
@@ -61,9 +64,12 @@ def copy_calibration(mib: int) -> int:
     return 0
 
 
-def measured_traffic(flops_per_launch: float, ms: float):
+def measured_traffic(flops_per_launch: float, ms: float, workload: str):
     """HBM bytes per launch of the attention kernel from the committed counter summary,
-    valid only while the kernel source is unchanged."""
+    valid only for the workload it was measured on and while the kernel source is
+    unchanged."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -293,7 +299,8 @@ def main() -> int:
                                  "workers": args.oracle_all_heads, "threads_per_worker": 1}
             log(f"whole oracle call {cpu['whole_call']}")
 
-    traffic = None if args.fp8_qk else measured_traffic(attn_flops, kernel_ms)
+    traffic = None if args.fp8_qk else measured_traffic(
+        attn_flops, kernel_ms, f"{args.config} rho={st.density}")
     # with fp8 logits half the flops run at the fp8 rate: the time at peak is
     # (F/2) / 5033.2 + (F/2) / 2516.6, a blended peak of 3355.5 TFLOP/s
     peak = 2.0 / (1.0 / (2.0 * BF16_PEAK_TFLOPS) + 1.0 / BF16_PEAK_TFLOPS) if args.fp8_qk else BF16_PEAK_TFLOPS
