@@ -54,3 +54,29 @@ def test_fp8_logits_match_the_oracle(spr, name, heads):
             f"rel_fro={rel_fro(g['o_sparse'][i], plain.o_sparse):.3e} "
             f"max_abs={max_abs(g['o_sparse'][i], plain.o_sparse):.3e}; O "
             f"rel_fro={rel_fro(g['o'][i], plain.o):.3e} max_abs={max_abs(g['o'][i], plain.o):.3e}")
+
+
+@pytest.mark.timeout(600)
+def test_fp8_logits_in_a_reused_call(spr):
+    """The reuse path takes the new inputs' own scales: a reused call with fp8 logits against
+    the oracle's reused call with fp8 logits (C2, steps 0 and 2)."""
+    import torch
+    from synthetic import make_step_inputs
+    from tests.gpu_common import from_dev, settings_kw, to_dev
+    cfg = get_config("C2")
+    heads = [3]
+    q0, k0, v0 = make_step_inputs(cfg, 0, heads=heads)
+    q2, k2, v2 = make_step_inputs(cfg, 2, heads=heads)
+    q2, k2 = q2 * 4.0, k2 * 0.25                     # new magnitudes (exact in bf16): new scales
+    ctx = spr.SparsePR.from_settings(1, cfg.n, cfg.d, spr.BF16, cfg.settings, flags=spr.F_FP8_QK)
+    ctx.sparsepr_attention(to_dev(q0, "bf16"), to_dev(k0, "bf16"), to_dev(v0, "bf16"))
+    o = ctx.sparsepr_attention_reuse(to_dev(q2, "bf16"), to_dev(k2, "bf16"), to_dev(v2, "bf16"))
+    torch.cuda.synchronize()
+    o_s = ctx.sparsepr_get_sparse_out().astype(np.float64)
+    o = from_dev(o)
+    ctx.close()
+    st = settings_kw(cfg.settings)
+    r0 = orc.oracle_head(q0[0], k0[0], v0[0], fp8_qk=True, **st)
+    r2 = orc.oracle_head(q2[0], k2[0], v2[0], reuse=r0, fp8_qk=True, **st)
+    check_close(o_s[0], r2.o_sparse, "C2 reused fp8 O_s", rel=3e-3, out_rel=2.0 ** -24)
+    check_close(o[0], r2.o, "C2 reused fp8 O")
