@@ -686,9 +686,10 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
 // the first for each point's best score and window, the second listing the centroids whose
 // screened score lies in the window; the exact argmin is among them, so the fp64 recheck
 // (k_recheck_cand) needs only those. A point with more than kMaxCand goes to a second queue
-// (ovf_list) for the full recheck.
+// (ovf_list) for the full recheck. The lists take 32 KB of LDS beside the two 32 KB centroid
+// tiles, so one block runs per CU.
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_candidates(const bf16_t* __restrict__ x, int n,
+__global__ __launch_bounds__(256, 1) void k_candidates(const bf16_t* __restrict__ x, int n,
                                                        const bf16_t* __restrict__ cpart,
                                                        const float* __restrict__ cn2,
                                                        const float* __restrict__ cpn, int groups,
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(256, 2) void k_candidates(const bf16_t* __restrict_
     __shared__ int s_cd[4][64][kMaxCand];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int count = flag_count[h];
-    if (blockIdx.x * 256 >= count) return;            // the whole block: no queued point
+    if ((int)blockIdx.x * 256 >= count) return;       // the whole block: no queued point
     const int ntiles = (groups + TG - 1) / TG;
     const rsrc_t rc = make_rsrc(cpart + (size_t)h * 2 * groups * D, (uint32_t)(2 * groups * D * 2));
     auto issue = [&](int t, uint4* buf) {
