@@ -121,6 +121,8 @@ struct sparsepr_ctx {
     int32_t *cand = nullptr, *ncand = nullptr, *ovf_cnt = nullptr, *ovf_list = nullptr;
     double* crow = nullptr;            // [H][G][d] row-major screening vectors / coordinates
     double* ycoord = nullptr;          // [H][N][r_K] every key's coordinates x W (candidate recheck)
+    bf16_t* zhl = nullptr;             // [H][N][2][r_K] the same split in bf16 hi, lo (key screen)
+    float* zkb = nullptr;              // [H][N] each key's screen bound coefficient
     double *mk = nullptr, *w64 = nullptr, *kc64 = nullptr, *qc64 = nullptr;
     // device eigensolve of M_K: tridiagonal form, reflectors, eigenpairs, |T|, gap
     double *eig_diag = nullptr, *eig_off = nullptr, *eig_hv = nullptr, *eig_beta = nullptr;
@@ -228,7 +230,7 @@ int32_t validate(const sparsepr_params* p) {
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
     if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE |
                      SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO | SPARSEPR_F_SERIAL_PARTITION |
-                     SPARSEPR_F_FP8_QK))
+                     SPARSEPR_F_FP8_QK | SPARSEPR_F_RAW_KEY_SCREEN))
         return SPARSEPR_ERR_INVALID_ARG;
     if ((p->flags & SPARSEPR_F_RAW_KMEANS) && (p->flags & SPARSEPR_F_SVOO)) return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
@@ -245,6 +247,14 @@ struct Arena {
         used += sizeof(T) * std::max<size_t>(count, 1);
     }
 };
+
+// The key side screens in its coordinates x W (bf16 hi + lo, depth 4 r_K instead of 2 d)
+// when the centroids stay resident in LDS and r_K has a kernel (16 or 32): the W metric
+// path only (not the identity-metric or co-clustering partitioners).
+bool key_screen_in_coords(const sparsepr_ctx& c) {
+    return !c.raw && !c.svoo && !(c.p.flags & SPARSEPR_F_RAW_KEY_SCREEN) && !assign_streams(c.Gk, c.d) &&
+           (c.rK == 16 || c.rK == 32);
+}
 
 void derive(sparsepr_ctx& c) {
     const sparsepr_params& p = c.p;
@@ -305,6 +315,10 @@ void layout(sparsepr_ctx& c, Arena& a) {
         a.take(c.ovf_list, HN);
         if (assign_streams(c.Gk, (int)d) && !c.raw && !c.svoo && c.rK <= kCandidateMaxDim)
             a.take(c.ycoord, HN * c.rK);
+    }
+    if (key_screen_in_coords(c)) {
+        a.take(c.zhl, HN * 2 * c.rK);
+        a.take(c.zkb, HN);
     }
     a.take(c.blkhist, H * c.nblk * c.gmax);
     a.take(c.blkoff, H * c.nblk * c.gmax);
@@ -454,7 +468,8 @@ int32_t recheck(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const
 
 int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const double* l64, int groups,
               int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
-              double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st) {
+              double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st,
+              const bf16_t* zhl = nullptr, const float* zkb = nullptr) {
     // heads h0 .. h0 + hh - 1: every buffer is head-major, so the slice starts h0 heads in
     const size_t h = h0, N = c->N, d = c->d, cdim = dim > 0 ? dim : c->d;
     x += h * N * d;
@@ -476,19 +491,25 @@ int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const d
     // each head group's rows start at h0 gmax d: the key side's narrower rows and the query
     // side's wider ones of two groups running at once never overlap
     double* crow = c->crow ? c->crow + h * c->gmax * c->d : nullptr;
+    // zhl, zkb (the factor side only): screen in the coordinates x W, split, instead of x
+    const int coords = zhl != nullptr;
+    if (coords) {
+        zhl += h * N * 2 * dim;
+        zkb += h * N;
+    }
     launch_seed_centroids(x, hh, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
-                          cpn, c2_64, st, crow);
+                          cpn, c2_64, st, crow, coords);
     SPR_LAUNCHED(c, "seed centroids");
     for (int t = 0; t < c->T; ++t) {
         int32_t* fc = flags + (size_t)t * c->H + h;
-        launch_assign(x, hh, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, flag_list, st);
+        launch_assign(x, hh, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, flag_list, st, zhl, zkb, dim);
         SPR_LAUNCHED(c, "assign");
         int32_t rc = recheck(c, h0, hh, x, dim, l64, c64, c2_64, cpart, cn2, cpn, groups, fc, labels, st);
         if (rc) return rc;
         launch_counting_sort(labels, hh, c->N, groups, blkhist, blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");
         launch_group_means(x, hh, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
-                           cn2, cpn, c2_64, st, crow);
+                           cn2, cpn, c2_64, st, crow, coords);
         SPR_LAUNCHED(c, "group means");
     }
     return SPARSEPR_OK;
@@ -738,8 +759,13 @@ int32_t partition_heads(sparsepr_ctx* c, int h0, int hh, const bf16_t* q16, cons
                       c->ycoord + h * c->N * c->rK, s);
         SPR_LAUNCHED(c, "key coordinates");
     }
+    if (c->zhl) {                       // the same coordinates, split, for the key screen
+        launch_zcoords(k16 + h * c->N * d, hh, c->N, c->d, c->w64 + h * d * c->rK, c->rK,
+                       c->zhl + h * c->N * 2 * c->rK, c->zkb + h * c->N, s);
+        SPR_LAUNCHED(c, "key coordinates (screen)");
+    }
     int32_t rc = lloyd(c, h0, hh, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff,
-                       c->kraw, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, s);
+                       c->kraw, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, s, c->zhl, c->zkb);
     if (rc) return rc;
     SPR_HIP(c, hipEventRecord(keys_done, s));
     launch_gram_f64(c->kraw + h * c->Gk * d, hh, c->Gk, c->d, 1.0 / c->d, c->mq + h * d * d, s);

@@ -45,10 +45,12 @@ void launch_finish_all(const double* mean_raw, int heads, int d, const double* l
                        double* crow = nullptr);
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
-                           float* cn2, float* cpn, double* c2_64, hipStream_t st, double* crow = nullptr);
+                           float* cn2, float* cpn, double* c2_64, hipStream_t st, double* crow = nullptr,
+                           int coords = 0);
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
-                   int32_t* flag_list, hipStream_t st);
+                   int32_t* flag_list, hipStream_t st, const bf16_t* zhl = nullptr, const float* kb = nullptr,
+                   int dz = 0);
 void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
                     const double* c64, const double* c2_64, int groups, const int32_t* flag_count,
                     const int32_t* flag_list, int32_t* labels, hipStream_t st);
@@ -66,17 +68,24 @@ void launch_recheck_cand(const bf16_t* x, int heads, int n, int d, const double*
                          const double* crow, const double* c2_64, int groups, const int32_t* flag_count,
                          const int32_t* flag_list, const int32_t* cand, const int32_t* ncand,
                          const double* ycoord, int32_t* labels, hipStream_t st);
-// every point's factor coordinates y = x L [heads][n][dim], as the recheck forms them
+// every point's factor coordinates y = x L [heads][n][dim] (fp64) as the recheck forms them
 void launch_coords(const bf16_t* x, int heads, int n, int d, const double* l64, int dim, double* y,
                    hipStream_t st);
+// the same coordinates on MFMA for the screen in the key coordinates (launch_assign with
+// zhl, kb; dim 16 or 32): zhl [heads][n][2][dim] bf16 (hi then lo), kb [heads][n] each
+// point's bound coefficient
+void launch_zcoords(const bf16_t* x, int heads, int n, int d, const double* l64, int dim, bf16_t* zhl,
+                    float* kb, hipStream_t st);
 void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, int32_t* blkhist,
                           int32_t* blkoff, int32_t* sorted, int32_t* off, hipStream_t st);
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
-                        double* c2_64, hipStream_t st, double* crow = nullptr);
+                        double* c2_64, hipStream_t st, double* crow = nullptr, int coords = 0);
 // crow (optional): a row-major [heads][groups][d or dout] copy of the screening vectors
-// (full metric) or of the centroid coordinates (factor) for the candidate recheck
+// (full metric) or of the centroid coordinates (factor) for the candidate recheck; coords
+// (factor only): the assignment screens in the key coordinates (launch_assign with zhl), so
+// the split centroid rows are the coordinates themselves ([heads][2][groups][dout])
 
 // ---- route ----
 void launch_permute(const bf16_t* src, const int32_t* perm, int heads, int n, int d, bf16_t* dst,

@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
                                                 const int32_t* __restrict__ off,
                                                 double* __restrict__ c64, bf16_t* __restrict__ cpart,
                                                 float* __restrict__ cn2, float* __restrict__ cpn,
-                                                double* __restrict__ c2_64, double* __restrict__ crow) {
+                                                double* __restrict__ c2_64, double* __restrict__ crow,
+                                                int coords) {
     constexpr int G = kFinG;
     const bool full = dout == 0;                 // full metric M [d][d]
     __shared__ double s_m[G][129];               // means (padded rows)
@@ -180,7 +181,8 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
         __syncthreads();
     }
     // C'[gs][i] = sum_j L[i][j] c[gs][j]: thread (range r, coordinate i) over its j range
-    if (!full) {
+    // (not needed when the assignment screens in the coordinates themselves)
+    if (!full && !coords) {
         const int nr = 256 / d;                          // d = 64 or 128
         const int i = tid % d, r = tid / d;
         const int len = (dout + nr - 1) / nr, j0 = min(r * len, dout), j1 = min(j0 + len, dout);
@@ -227,8 +229,14 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
             c64[((size_t)h * dout + j) * groups + g] = cv;          // coordinate-major
             if (crow && !full) crow[((size_t)h * groups + g) * dout + j] = cv;   // row-major copy
             a += full ? s_m[gs][j] * cv : cv * cv;
+            if (coords) {           // screened in the key coordinates: c itself, split
+                const bf16_t hi = f32_to_bf16((float)cv);
+                cpart[((size_t)(h * 2 + 0) * groups + g) * dout + j] = hi;
+                cpart[((size_t)(h * 2 + 1) * groups + g) * dout + j] = f32_to_bf16((float)(cv - (double)bf16_to_f32(hi)));
+                b += cv * cv;
+            }
         }
-        for (int i = lane; i < d; i += 64) {
+        for (int i = coords ? d : lane; i < d; i += 64) {
             const double sv = full ? s_c[gs][i] : s_s[gs][i];
             if (crow && full) crow[((size_t)h * groups + g) * d + i] = sv;       // row-major copy
             const bf16_t hi = f32_to_bf16((float)sv);
@@ -248,9 +256,9 @@ __global__ __launch_bounds__(256) void k_finish(const double* __restrict__ mean_
 
 static void launch_finish(const double* mean_raw, int heads, int d, const double* l64, int dout,
                           int groups, const int32_t* off, double* c64, bf16_t* cpart, float* cn2,
-                          float* cpn, double* c2_64, hipStream_t st, double* crow) {
+                          float* cpn, double* c2_64, hipStream_t st, double* crow, int coords = 0) {
     hipLaunchKernelGGL(k_finish, dim3((groups + kFinG - 1) / kFinG, heads), dim3(256), 0, st, mean_raw,
-                       d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, crow);
+                       d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, crow, coords);
 }
 
 // ------------------------------------------------------------------- seeds ---
@@ -276,9 +284,9 @@ void launch_finish_all(const double* mean_raw, int heads, int d, const double* l
 void launch_seed_centroids(const bf16_t* x, int heads, int n, int d, const double* l64, int dout,
                            int groups, int64_t a, double* mean_raw, double* c64, bf16_t* cpart,
                            float* cn2, float* cpn, double* c2_64, hipStream_t st,
-                           double* crow) {
+                           double* crow, int coords) {
     hipLaunchKernelGGL(k_seed, dim3(groups, heads), dim3(128), 0, st, x, n, d, groups, a, mean_raw);
-    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st, crow);
+    launch_finish(mean_raw, heads, d, l64, dout, groups, nullptr, c64, cpart, cn2, cpn, c2_64, st, crow, coords);
 }
 
 // ------------------------------------------------------------------ assign ---
@@ -320,16 +328,23 @@ __device__ __attribute__((always_inline)) inline float with_slot(float v, int r)
     return __uint_as_float((__float_as_uint(v) & ~15u) | (uint32_t)r);
 }
 
-template <int D>
+// Z: the points are the key coordinates z = x W (depth D = r_K, written by k_zcoords),
+// split into bf16 hi + lo like the centroids, and a score takes all four products (hi.hi,
+// hi.lo, lo.hi, lo.lo). The bound's per-point coefficient k_p (|computed - exact| <= k_p |c|
+// for the dot product) then comes with the coordinates instead of kappa |x|.
+template <int D, bool Z = false>
 struct AssignWave {
     static constexpr int CH = D / 8;
     static constexpr int TG = kAssignTG;
     static constexpr int SLOTS = 2 * TG * CH;   // 16-byte slots per tile (hi and lo)
     static constexpr float kU = 5.9604644775390625e-08f;
     static constexpr float kappa = 2.f * D * kU * 1.00390625f + 7.62939453125e-06f;
+    // row swizzle of the centroid tiles (chunk c of row r at c ^ sw(r), within the row)
+    __host__ __device__ static int sw(int r) { return CH >= 8 ? swz<CH>(r) : (r & (CH - 1)); }
 
-    uint4 xf[2][D / 16];
-    float xn[2];
+    uint4 xf[2][D / 16];                        // the points (Z: their hi parts)
+    uint4 xl[Z ? 2 : 1][Z ? D / 16 : 1];        // Z: their lo parts
+    float xk[2];                                // kappa |x| (Z: k_p), rounded up
     float best[2], second[2];
     int bg[2];
 
@@ -363,7 +378,40 @@ struct AssignWave {
                 }
             }
             ss += __shfl_xor(ss, 32, 64);
-            xn[pb] = sqrtf(ss) * 1.000001f;
+            xk[pb] = kappa * (sqrtf(ss) * 1.000001f);
+            best[pb] = INFINITY;
+            second[pb] = INFINITY;
+            bg[pb] = 0x7fffffff;
+        }
+    }
+
+    // Z: this wave's 64 points from their split coordinates (row of a point: D hi values
+    // then D lo values) and their bound coefficients kb [n]
+    __device__ __attribute__((always_inline)) void load_z(const bf16_t* __restrict__ zhl,
+                                                          const float* __restrict__ kb, int n,
+                                                          int h, int p_base, int lane) {
+        const int half = lane >> 5;
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            const int pt = min(p_base + 32 * pb + (lane & 31), n - 1);
+            const bf16_t* zr = zhl + ((size_t)h * n + pt) * 2 * D;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                xf[pb][kk] = *reinterpret_cast<const uint4*>(zr + 16 * kk + 8 * half);
+                xl[pb][kk] = *reinterpret_cast<const uint4*>(zr + D + 16 * kk + 8 * half);
+            }
+            xk[pb] = kb[(size_t)h * n + pt];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            if (p_base + 32 * pb + (lane & 31) >= n) {
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    xf[pb][kk] = make_uint4(0, 0, 0, 0);
+                    xl[pb][kk] = make_uint4(0, 0, 0, 0);
+                }
+            }
             best[pb] = INFINITY;
             second[pb] = INFINITY;
             bg[pb] = 0x7fffffff;
@@ -401,7 +449,7 @@ struct AssignWave {
                 }
             }
             ss += __shfl_xor(ss, 32, 64);
-            xn[pb] = sqrtf(ss) * 1.000001f;
+            xk[pb] = kappa * (sqrtf(ss) * 1.000001f);
             best[pb] = INFINITY;
             second[pb] = INFINITY;
             bg[pb] = 0x7fffffff;
@@ -416,7 +464,7 @@ struct AssignWave {
     // (both halves of the wave get the same value).
     __device__ __attribute__((always_inline)) float window(int pb, float c2max, float cpmax) const {
         const float b = fminf(best[pb], __shfl_xor(best[pb], 32, 64));
-        const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
+        const float A = fmaf(2.f * xk[pb], cpmax, kU * c2max);
         const float W = 2.4f * A + (2.4f * kU + 3.814697265625e-06f) * (2.f * fabsf(b)) + 1e-30f;
         return b + 1.25f * W;
     }
@@ -441,11 +489,37 @@ struct AssignWave {
         constexpr int KS = D / 16, PF = 2;
         const uint4* cr0 = buf + (lane & 31) * CH;
         const uint4* cr1 = buf + (32 + (lane & 31)) * CH;
-        const int sw0 = swz<CH>(lane & 31), sw1 = swz<CH>(32 + (lane & 31));
-        auto frag = [&](const uint4* cr, int sw, int i) __attribute__((always_inline)) {
-            return cr[(i / KS) * TG * CH + ((2 * (i % KS) + half) ^ sw)];
+        const int sw0 = sw(lane & 31), sw1 = sw(32 + (lane & 31));
+        auto frag = [&](const uint4* cr, int swr, int i) __attribute__((always_inline)) {
+            return cr[(i / KS) * TG * CH + ((2 * (i % KS) + half) ^ swr)];
         };
         f32x16 acc[2][2];
+        if constexpr (Z) {
+            // each depth step: both sub-tiles' hi and lo fragments against the points' hi and
+            // lo parts, the four products of each accumulator in the same order every step
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const uint4 a[2][2] = {{frag(cr0, sw0, kk), frag(cr0, sw0, KS + kk)},
+                                       {frag(cr1, sw1, kk), frag(cr1, sw1, KS + kk)}};
+#pragma unroll
+                for (int pr = 0; pr < 4; ++pr)
+#pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                        for (int pb = 0; pb < 2; ++pb) {
+                            const uint4 b = (pr & 1) ? xl[pb][kk] : xf[pb][kk];
+                            acc[sub][pb] = mfma32x32x16(a[sub][pr >> 1], b,
+                                                        (kk == 0 && pr == 0) ? f32x16{} : acc[sub][pb]);
+                        }
+            }
+#pragma unroll
+            for (int sub = 0; sub < TG / 32; ++sub) {
+                const int gb = t * TG + 32 * sub;
+                if (gb >= groups) break;
+                epi(acc[sub], gb);
+            }
+            return;
+        }
         uint4 f0[PF], f1[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
@@ -528,7 +602,7 @@ struct AssignWave {
                 b = ob;
                 gsel = og;
             }
-            const float A = fmaf(2.f * kappa * xn[pb], cpmax, kU * c2max);
+            const float A = fmaf(2.f * xk[pb], cpmax, kU * c2max);
             const float bound = 2.4f * A + (2.4f * kU + 3.814697265625e-06f) * (fabsf(s2) + fabsf(b)) + 1e-30f;
             const int pt = p_base + 32 * pb + lane;
             if (lane < 32 && pt < n) {
@@ -581,7 +655,7 @@ __device__ inline void assign_norms(const float* __restrict__ cn2, const float* 
 // ranges per block, one block per CU); where the range enters a new head the block loads
 // that head's centroids (all tiles) into LDS once, then its waves take the head's items
 // round-robin.
-template <int D>
+template <int D, bool Z>
 __global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict__ x, int n,
                                                        int heads, const bf16_t* __restrict__ cpart,
                                                        const float* __restrict__ cn2,
@@ -589,8 +663,9 @@ __global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict_
                                                        int items_per_block,
                                                        int32_t* __restrict__ labels,
                                                        int32_t* __restrict__ flag_count,
-                                                       int32_t* __restrict__ flag_list) {
-    using AW = AssignWave<D>;
+                                                       int32_t* __restrict__ flag_list,
+                                                       const float* __restrict__ kb) {
+    using AW = AssignWave<D, Z>;
     constexpr int CH = AW::CH, TG = kAssignTG, SLOTS = AW::SLOTS;
     __shared__ uint4 s_c[kAssignResBytes / 16];
     __shared__ float s_cn2[kAssignResBytes / (4 * D) + TG];
@@ -613,7 +688,7 @@ __global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict_
             const int part = rem0 / (TG * CH), rem = rem0 % (TG * CH);
             const int row = rem / CH, pc = rem % CH;
             const int g = min(t * TG + row, groups - 1);
-            lds_load16(rc, s_c + (slot - lane), ((part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8)) * 2);
+            lds_load16(rc, s_c + (slot - lane), ((part * groups + g) * D + ((pc ^ AW::sw(row)) * 8)) * 2);
         }
         float c2max, cpmax;
         assign_norms<512>(cn2, cpn, h, groups, ntiles, s_cn2, s_red, c2max, cpmax);
@@ -621,7 +696,8 @@ __global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict_
         __syncthreads();
         for (int k = it + w; k < seg_end; k += 8) {
             const int p_base = (k - h * ipw) * 64;
-            aw.load(x, n, h, p_base, lane);
+            if constexpr (Z) aw.load_z(x, kb, n, h, p_base, lane);
+            else aw.load(x, n, h, p_base, lane);
             for (int t = 0; t < ntiles; ++t) aw.tile(t, s_c + t * SLOTS, groups, s_cn2, lane);
             aw.finish(n, h, groups, p_base, lane, c2max, cpmax, labels, flag_count, flag_list);
         }
@@ -655,7 +731,7 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
             const int part = slot / (TG * CH), rem = slot % (TG * CH);
             const int row = rem / CH, pc = rem % CH;
             const int g = min(t * TG + row, groups - 1);
-            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8)) * 2);
+            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ AW::sw(row)) * 8)) * 2);
         }
     };
     issue(0, s_c0);
@@ -721,7 +797,7 @@ __global__ __launch_bounds__(256, 1) void k_candidates(const bf16_t* __restrict_
             const int part = slot / (TG * CH), rem = slot % (TG * CH);
             const int row = rem / CH, pc = rem % CH;
             const int g = min(t * TG + row, groups - 1);
-            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ swz<CH>(row)) * 8)) * 2);
+            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ AW::sw(row)) * 8)) * 2);
         }
     };
     const int q_base = blockIdx.x * 256 + w * 64;
@@ -984,6 +1060,151 @@ void launch_coords(const bf16_t* x, int heads, int n, int d, const double* l64, 
         hipLaunchKernelGGL(k_coords<64>, grid, dim3(256), 0, st, x, n, l64, dim, y);
 }
 
+// v = p0 + p1 + p2 + r in bf16 parts, each the nearest to what is left (through fp32), with
+// |r| <= 2^-25 (1 + 2^-14) |v| (every difference below is exact in fp64)
+__device__ inline void split3_bf16(double v, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+    const bf16_t a = f32_to_bf16((float)v);
+    const double r1 = v - (double)bf16_to_f32(a);
+    const bf16_t b = f32_to_bf16((float)r1);
+    p0 = a;
+    p1 = b;
+    p2 = f32_to_bf16((float)(r1 - (double)bf16_to_f32(b)));
+}
+
+// The key coordinates z = x W for the assignment's screen in those coordinates, on MFMA:
+// W's columns split into three bf16 parts (A operand, held by each wave for all its tiles),
+// the points' rows as they are (exact bf16, B operand). The top part's products are summed
+// per 16-deep step (one instruction from zero) and the steps added in fp64; the two smaller
+// parts share one fp32 chain over the whole depth. Against the exact x W this leaves, per
+// coordinate, |z - x W|_j <= 20 u a_j with a_j = sum_i |x_i| |W_ij| (16 u (1 + 2^-8) for the
+// top part, about u for the chain, u / 2 for the parts' residual), and |a| <= |x| |W|_F.
+// Each point's row holds z split into bf16 hi then lo (residual <= 2^-17 (1 + 2^-16) |z_j|,
+// by the exponent of what the hi part leaves), and kb its bound coefficient for the screen:
+// a score takes 4 dim exact products of the parts in one fp32 chain (<= 4 dim u (1 + 2^-7)^2
+// |z| |c|, as |hi| + |lo| <= (1 + 2^-7) |z_j|), the two splits' residuals add
+// 2^-16 (1 + 2^-15) |z| |c|, and the coordinates' own error 20 u |x| |W|_F |c|:
+//   kb = (4 dim u (1 + 2^-7)^2 + 2^-16 (1 + 2^-15)) |z| + 20 u |x| |W|_F   (rounded up).
+// The block stages W's split fragments in LDS once; a wave then takes tiles of 32 points,
+// and lane (point j, half) ends with the 16 coordinates 8 q + 4 half + (0..3), q = 0..3,
+// of its point.
+template <int D>
+__global__ __launch_bounds__(256, 3) void k_zcoords(const bf16_t* __restrict__ x, int n,
+                                                 const double* __restrict__ l64, int dim,
+                                                 int tiles_per_wave, bf16_t* __restrict__ zhl,
+                                                 float* __restrict__ kb) {
+    constexpr int KS = D / 16;
+    constexpr double kUd = 5.9604644775390625e-08;
+    __shared__ uint4 s_a[3 * KS * 64];          // [part][kk][lane]: the A fragment of that lane
+    __shared__ double s_red[4];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5;
+    const int col = lane & 31;
+    const double* lh = l64 + (size_t)h * D * dim;
+    // A of lane ln: row ln % 32 of W^T (column of W; zero past dim), depth 16 kk + 8 (ln / 32) + 0..7
+    double wf = 0.0;
+    for (int f = tid; f < KS * 64; f += 256) {
+        const int kk = f / 64, ln = f % 64, cj = ln & 31;
+        uint32_t pk[3][4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int i = 16 * kk + 8 * (ln >> 5) + e;
+            const double w0 = cj < dim ? lh[(size_t)i * dim + cj] : 0.0;
+            const double w1 = cj < dim ? lh[(size_t)(i + 1) * dim + cj] : 0.0;
+            wf = fma(w0, w0, fma(w1, w1, wf));
+            uint32_t x0, x1, x2, y0, y1, y2;
+            split3_bf16(w0, x0, x1, x2);
+            split3_bf16(w1, y0, y1, y2);
+            pk[0][e / 2] = x0 | (y0 << 16);
+            pk[1][e / 2] = x1 | (y1 << 16);
+            pk[2][e / 2] = x2 | (y2 << 16);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt)
+            s_a[(pt * KS + kk) * 64 + ln] = make_uint4(pk[pt][0], pk[pt][1], pk[pt][2], pk[pt][3]);
+    }
+    wf = wave_sum_f64(wf);
+    if (lane == 0) s_red[w] = wf;
+    __syncthreads();
+    const double wfro = sqrt(s_red[0] + s_red[1] + s_red[2] + s_red[3]);    // |W|_F
+    const int tiles = (n + 31) / 32;
+    const int t0 = (blockIdx.x * 4 + w) * tiles_per_wave, t1 = min(tiles, t0 + tiles_per_wave);
+    const double kz = 4.0 * dim * kUd * 1.0158 + 1.5260e-05;
+    for (int t = t0; t < t1; ++t) {
+        asm volatile("" ::: "memory");          // re-read the fragments per tile (no hoisting)
+        const int p = t * 32 + col;
+        const bf16_t* xr = x + ((size_t)h * n + min(p, n - 1)) * D + 8 * half;
+        uint4 b[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) b[kk] = *reinterpret_cast<const uint4*>(xr + 16 * kk);
+        double z[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = 0.0;
+        f32x16 ml = {};
+        float xs = 0.f;
+        // step kk's top-part products are added while step kk + 1's run (two in flight)
+        f32x16 hp = mfma32x32x16(s_a[lane], b[0], f32x16{});
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            f32x16 hn = hp;
+            if (kk + 1 < KS) hn = mfma32x32x16(s_a[(kk + 1) * 64 + lane], b[kk + 1], f32x16{});
+            ml = mfma32x32x16(s_a[(KS + kk) * 64 + lane], b[kk], ml);
+            ml = mfma32x32x16(s_a[(2 * KS + kk) * 64 + lane], b[kk], ml);
+            const uint32_t wd[4] = {b[kk].x, b[kk].y, b[kk].z, b[kk].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = bf16_to_f32((bf16_t)(wd[e] & 0xFFFF));
+                const float hi = bf16_to_f32((bf16_t)(wd[e] >> 16));
+                xs = fmaf(lo, lo, fmaf(hi, hi, xs));
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] += (double)hp[r];
+            hp = hn;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        xs += __shfl_xor(xs, 32, 64);
+        double zz = 0.0;
+        bf16_t* zr = zhl + ((size_t)h * n + p) * 2 * dim;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j0 = 8 * q + 4 * half;
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double v = z[4 * q + e] + (double)ml[4 * q + e];
+                zz = fma(v, v, zz);
+                const bf16_t hi = f32_to_bf16((float)v);
+                const bf16_t lo = f32_to_bf16((float)(v - (double)bf16_to_f32(hi)));
+                if (e & 1) {
+                    hw[e >> 1] |= (uint32_t)hi << 16;
+                    lw[e >> 1] |= (uint32_t)lo << 16;
+                } else {
+                    hw[e >> 1] = hi;
+                    lw[e >> 1] = lo;
+                }
+            }
+            if (p < n && j0 < dim) {
+                *reinterpret_cast<uint2*>(zr + j0) = make_uint2(hw[0], hw[1]);
+                *reinterpret_cast<uint2*>(zr + dim + j0) = make_uint2(lw[0], lw[1]);
+            }
+        }
+        zz += __shfl_xor(zz, 32, 64);
+        if (half == 0 && p < n) {
+            const double xn = sqrt((double)xs) * 1.0001;
+            kb[(size_t)h * n + p] = (float)((kz * sqrt(zz) + 20.0 * kUd * xn * wfro) * 1.0001);
+        }
+    }
+}
+
+void launch_zcoords(const bf16_t* x, int heads, int n, int d, const double* l64, int dim, bf16_t* zhl,
+                    float* kb, hipStream_t st) {
+    const int tiles = (n + 31) / 32;
+    const int tpw = std::max(4, (int)(((size_t)tiles * heads + 2047) / 2048));
+    const dim3 grid((unsigned)((tiles + 4 * tpw - 1) / (4 * tpw)), heads);
+    if (d == 128)
+        hipLaunchKernelGGL(k_zcoords<128>, grid, dim3(256), 0, st, x, n, l64, dim, tpw, zhl, kb);
+    else
+        hipLaunchKernelGGL(k_zcoords<64>, grid, dim3(256), 0, st, x, n, l64, dim, tpw, zhl, kb);
+}
+
 bool assign_streams(int groups, int d) {
     const int ntiles = (groups + kAssignTG - 1) / kAssignTG;
     return (size_t)ntiles * kAssignTG * 2 * d * 2 > (size_t)kAssignResBytes;
@@ -991,9 +1212,9 @@ bool assign_streams(int groups, int d) {
 
 void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                    const float* cpn, int groups, int32_t* labels, int32_t* flag_count,
-                   int32_t* flag_list, hipStream_t st) {
+                   int32_t* flag_list, hipStream_t st, const bf16_t* zhl, const float* kb, int dz) {
     const int ntiles = (groups + kAssignTG - 1) / kAssignTG;
-    if ((size_t)ntiles * kAssignTG * 2 * d * 2 <= (size_t)kAssignResBytes) {
+    if (zhl != nullptr || (size_t)ntiles * kAssignTG * 2 * d * 2 <= (size_t)kAssignResBytes) {
         static int cus = 0;
         if (cus <= 0) {
             int dev = 0;
@@ -1006,12 +1227,18 @@ void launch_assign(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart
         const int blocks = std::max(1, std::min(total, cus));
         const int ipb = (total + blocks - 1) / blocks;
         const int nb = (total + ipb - 1) / ipb;
-        if (d == 128)
-            hipLaunchKernelGGL(k_assign_res<128>, dim3(nb), dim3(512), 0, st, x, n, heads, cpart, cn2,
-                               cpn, groups, ipb, labels, flag_count, flag_list);
+        if (zhl != nullptr && dz == 32)
+            hipLaunchKernelGGL((k_assign_res<32, true>), dim3(nb), dim3(512), 0, st, zhl, n, heads, cpart, cn2,
+                               cpn, groups, ipb, labels, flag_count, flag_list, kb);
+        else if (zhl != nullptr)
+            hipLaunchKernelGGL((k_assign_res<16, true>), dim3(nb), dim3(512), 0, st, zhl, n, heads, cpart, cn2,
+                               cpn, groups, ipb, labels, flag_count, flag_list, kb);
+        else if (d == 128)
+            hipLaunchKernelGGL((k_assign_res<128, false>), dim3(nb), dim3(512), 0, st, x, n, heads, cpart, cn2,
+                               cpn, groups, ipb, labels, flag_count, flag_list, nullptr);
         else
-            hipLaunchKernelGGL(k_assign_res<64>, dim3(nb), dim3(512), 0, st, x, n, heads, cpart, cn2,
-                               cpn, groups, ipb, labels, flag_count, flag_list);
+            hipLaunchKernelGGL((k_assign_res<64, false>), dim3(nb), dim3(512), 0, st, x, n, heads, cpart, cn2,
+                               cpn, groups, ipb, labels, flag_count, flag_list, nullptr);
         return;
     }
     dim3 grid((n + 255) / 256, heads);
@@ -1394,7 +1621,7 @@ __global__ __launch_bounds__(512) void k_group_sum(const bf16_t* __restrict__ x,
 void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t* sorted,
                         const int32_t* off, int groups, double* mean_raw, const double* l64,
                         int dout, double* c64, bf16_t* cpart, float* cn2, float* cpn,
-                        double* c2_64, hipStream_t st, double* crow) {
+                        double* c2_64, hipStream_t st, double* crow, int coords) {
     if (d == 128)
         hipLaunchKernelGGL(k_group_sum<128>, dim3(groups, heads), dim3(512), 0, st, x, n, sorted, off,
                            groups, mean_raw);
@@ -1402,7 +1629,7 @@ void launch_group_means(const bf16_t* x, int heads, int n, int d, const int32_t*
         hipLaunchKernelGGL(k_group_sum<64>, dim3(groups, heads), dim3(512), 0, st, x, n, sorted, off,
                            groups, mean_raw);
     if (l64 != nullptr)
-        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, st, crow);
+        launch_finish(mean_raw, heads, d, l64, dout, groups, off, c64, cpart, cn2, cpn, c2_64, st, crow, coords);
 }
 
 }  // namespace spr

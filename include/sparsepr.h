@@ -101,6 +101,13 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        and the correction are unchanged. Quantization is the
                                        extension "SparsePR稀疏注意力..." (framerc.cn) section 8.4
                                        names. The workspace grows by one byte per K element. */
+#define SPARSEPR_F_RAW_KEY_SCREEN 128u  /* the key k-means screens each key in raw space (x against
+                                       C' = W c, depth 2 d) instead of in its coordinates x W
+                                       (split into bf16 hi + lo, depth 4 r_K, formed once per
+                                       call; the default when the key centroids fit in LDS and
+                                       r_K is 16 or 32). Both screens certify against the same
+                                       exact scores and send the rest to the same fp64 recheck,
+                                       so the labels are the same either way; for comparison. */
 #define SPARSEPR_F_CHECK_FINITE 4u  /* count non-finite values of q and k (partition), v (route)
                                        and o (correct) on the device; read the counts with
                                        sparsepr_get_stats. The stages stay asynchronous and do not

@@ -191,7 +191,9 @@ def test_validate_accepts_the_comparison_partitioner_flag():
     p.flags = 1 << 20
     assert spr.lib.sparsepr_validate(ctypes.byref(p)) == 1        # SPARSEPR_ERR_INVALID_ARG
     # the comparison partitioner needs d-wide fp64 key centroids: the workspace grows
-    # (against the method with its eigensolve on the host, which has no device eigen scratch)
+    # (against the method with its eigensolve on the host, which has no device eigen scratch,
+    # at a key rank of 8, which has no split key coordinates for the screen)
+    p.key_rank = 8
     p.flags = spr.F_HOST_SOLVE
     base = spr.lib.sparsepr_workspace_bytes(ctypes.byref(p))
     p.flags = 0
@@ -285,7 +287,23 @@ def test_serial_partition_flag_is_accepted_alone_and_combined():
     for f in (spr.F_SERIAL_PARTITION, spr.F_SERIAL_PARTITION | spr.F_STAGE_TIMING,
               spr.F_SERIAL_PARTITION | spr.F_HOST_SOLVE | spr.F_CHECK_FINITE):
         assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=f, **kw)) == 0
-    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=128, **kw)) == 1
+    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=256, **kw)) == 1
+
+
+def test_raw_key_screen_flag_drops_the_split_key_coordinates():
+    """By default the key screen runs on the split coordinates x W (bf16 hi + lo, [H][N][2][r_K])
+    and a bound coefficient per key (fp32 [H][N]); SPARSEPR_F_RAW_KEY_SCREEN screens raw keys
+    and needs neither. Key ranks without a coordinate kernel (8) and key groups that do not fit
+    in LDS (384 at d = 128) never take them."""
+    kw = dict(q_groups=16, density=0.25, probes=8, corr_rank=4)
+    ws = lambda f, rk, gk, d=64: spr.sparsepr_workspace_bytes(
+        spr.make_params(2, 1024, d, spr.BF16, flags=f, key_rank=rk, kv_groups=gk, **kw))
+    assert ws(0, 16, 16) - ws(spr.F_RAW_KEY_SCREEN, 16, 16) == 2 * 1024 * 2 * 16 * 2 + 2 * 1024 * 4
+    assert ws(0, 32, 16) - ws(spr.F_RAW_KEY_SCREEN, 32, 16) == 2 * 1024 * 2 * 32 * 2 + 2 * 1024 * 4
+    assert ws(0, 8, 16) == ws(spr.F_RAW_KEY_SCREEN, 8, 16)
+    assert ws(0, 32, 384, 128) == ws(spr.F_RAW_KEY_SCREEN, 32, 384, 128)
+    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=spr.F_RAW_KEY_SCREEN,
+                                                 kv_groups=16, **kw)) == 0
 
 
 def test_fp8_logit_flag_grows_the_workspace_by_one_byte_per_key_element():
