@@ -1494,6 +1494,34 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ blkhi
     }
 }
 
+// A wave's points pw0 + 64 r + lane (label lab[r], -1 past the end) to sorted[base + rank],
+// base from the wave's running bases wb (advanced here): in each round the lanes holding the
+// same label are found from one ballot per label bit, and rank among them follows the lane.
+template <int R>
+__device__ inline void scatter_ranked(const int (&lab)[R], int* wb, int groups, int pw0, int lane,
+                                      int32_t* __restrict__ sorted) {
+    int nbits = 0;
+    while ((1 << nbits) < groups) ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int l = lab[r];
+        const bool valid = l >= 0;
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool on = valid && ((l >> bit) & 1);
+            const uint64_t m = __ballot(on);
+            peers &= on ? m : ~m;
+        }
+        if (valid) {
+            const int prefix = __popcll(peers & below);
+            const int basev = wb[l];
+            sorted[basev + prefix] = pw0 + r * 64 + lane;
+            if (prefix == 0) wb[l] = basev + __popcll(peers);
+        }
+    }
+}
+
 // Stable scatter: the rank of a point among equal labels follows the point order. Wave w
 // takes the block's points [256 w, 256 w + 256) in 4 rounds of 64: per-wave label counts
 // give each wave its own base per label (block base + the counts of the waves before it);
@@ -1526,32 +1554,100 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ lab
         }
     }
     __syncthreads();
-    int nbits = 0;
-    while ((1 << nbits) < groups) ++nbits;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int r = 0; r < PW / 64; ++r) {
-        const int l = lab[r];
-        const bool valid = l >= 0;
-        uint64_t peers = __ballot(valid);
-        for (int bit = 0; bit < nbits; ++bit) {
-            const bool on = valid && ((l >> bit) & 1);
-            const uint64_t m = __ballot(on);
-            peers &= on ? m : ~m;
+    scatter_ranked(lab, cnt[wave], groups, pw0, lane, sorted + (size_t)h * n);
+}
+
+// k_scatter with the scan folded in, for heads of at most kFusedScanBlocks blocks: each
+// block sums its head's block histograms itself (every group's total, and its count in the
+// blocks before this one, both in block order), scans the totals over the groups, and block
+// 0 also writes the group offsets. The bases are k_scan's; one launch fewer per sort, for
+// nblk reads per group and block (a few microseconds of cached reads at these sizes).
+constexpr int kFusedScanBlocks = 256;
+__global__ __launch_bounds__(256) void k_scatter_scan(const int32_t* __restrict__ labels, int n,
+                                                      int groups, const int32_t* __restrict__ blkhist,
+                                                      int32_t* __restrict__ off,
+                                                      int32_t* __restrict__ sorted) {
+    __shared__ int cnt[4][kMaxGroups];
+    __shared__ int s_tot[kMaxGroups];          // group totals, then their exclusive prefix
+    __shared__ int s_pre[kMaxGroups];          // counts in the blocks before this one
+    __shared__ int s_wt[4];
+    const int h = blockIdx.y, b = blockIdx.x, nblk = gridDim.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int32_t* hh = blkhist + (size_t)h * nblk * groups;
+    for (int g = tid; g < groups; g += 256) {
+        int pre = 0, tot = 0;
+#pragma unroll 8
+        for (int bb = 0; bb < nblk; ++bb) {
+            const int c = hh[(size_t)bb * groups + g];
+            pre += bb < b ? c : 0;
+            tot += c;
         }
-        if (valid) {
-            const int prefix = __popcll(peers & below);
-            const int basev = cnt[wave][l];
-            sorted[(size_t)h * n + basev + prefix] = pw0 + r * 64 + lane;
-            if (prefix == 0) cnt[wave][l] = basev + __popcll(peers);
+        s_pre[g] = pre;
+        s_tot[g] = tot;
+    }
+    for (int i = tid; i < 4 * groups; i += 256) cnt[i / groups][i % groups] = 0;
+    __syncthreads();
+    // exclusive scan of the totals: thread t takes groups 4t .. 4t+3 (groups <= 1024), a
+    // wave scan of the thread sums, then the wave totals
+    const int g0 = 4 * tid;
+    int loc[4], run = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        loc[e] = (g0 + e < groups) ? s_tot[g0 + e] : 0;
+        run += loc[e];
+    }
+    int inc = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_wt[wave] = inc;
+    __syncthreads();
+    int acc = inc - run;
+    for (int k = 0; k < wave; ++k) acc += s_wt[k];
+    int32_t* oh = off + (size_t)h * (groups + 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (g0 + e < groups) {                 // only this thread reads these entries
+            s_tot[g0 + e] = acc;
+            if (b == 0) oh[g0 + e] = acc;
+            acc += loc[e];
         }
     }
+    if (b == 0 && tid == 0) oh[groups] = n;
+    // the points of this block, counted per wave
+    constexpr int PW = kSortChunk / 4;
+    const int pw0 = b * kSortChunk + wave * PW;
+    int lab[PW / 64];
+#pragma unroll
+    for (int r = 0; r < PW / 64; ++r) {
+        const int p = pw0 + r * 64 + lane;
+        lab[r] = (p < n) ? group_of(labels[(size_t)h * n + p], groups) : -1;
+        if (lab[r] >= 0) atomicAdd(&cnt[wave][lab[r]], 1);
+    }
+    __syncthreads();
+    for (int g = tid; g < groups; g += 256) {
+        int base = s_tot[g] + s_pre[g];
+        for (int w = 0; w < 4; ++w) {
+            const int c = cnt[w][g];
+            cnt[w][g] = base;
+            base += c;
+        }
+    }
+    __syncthreads();
+    scatter_ranked(lab, cnt[wave], groups, pw0, lane, sorted + (size_t)h * n);
 }
 
 void launch_counting_sort(const int32_t* labels, int heads, int n, int groups, int32_t* blkhist,
                           int32_t* blkoff, int32_t* sorted, int32_t* off, hipStream_t st) {
     const int nblk = (n + kSortChunk - 1) / kSortChunk;
     hipLaunchKernelGGL(k_hist, dim3(nblk, heads), dim3(256), 0, st, labels, n, groups, blkhist);
+    if (nblk <= kFusedScanBlocks) {
+        hipLaunchKernelGGL(k_scatter_scan, dim3(nblk, heads), dim3(256), 0, st, labels, n, groups, blkhist,
+                           off, sorted);
+        return;
+    }
     hipLaunchKernelGGL(k_scan, dim3(heads), dim3(1024), 0, st, blkhist, nblk, groups, n, blkoff, off);
     hipLaunchKernelGGL(k_scatter, dim3(nblk, heads), dim3(256), 0, st, labels, n, groups, blkoff,
                        sorted);
