@@ -339,8 +339,14 @@ struct AssignWave {
     static constexpr int SLOTS = 2 * TG * CH;   // 16-byte slots per tile (hi and lo)
     static constexpr float kU = 5.9604644775390625e-08f;
     static constexpr float kappa = 2.f * D * kU * 1.00390625f + 7.62939453125e-06f;
-    // row swizzle of the centroid tiles (chunk c of row r at c ^ sw(r), within the row)
-    __host__ __device__ static int sw(int r) { return CH >= 8 ? swz<CH>(r) : (r & (CH - 1)); }
+    // tile layout in LDS: rows of 128 or 256 bytes hold chunk c of row r at c ^ swz(r) within
+    // the row; narrower rows (CH <= 4, the key coordinates) are stored chunk-major instead
+    // (chunk c of row r at c TG + r), since 32 rows of 64 bytes read by 32 lanes would share
+    // bank groups whatever the order within a row
+    static constexpr bool CM = CH <= 4;
+    __host__ __device__ static int sw(int r) { return CM ? 0 : swz<CH>(r); }
+    // 16-byte slot (within one part's TG CH slots) of row r's chunk c
+    __host__ __device__ static int slot_of(int r, int c) { return CM ? c * TG + r : r * CH + (c ^ sw(r)); }
 
     uint4 xf[2][D / 16];                        // the points (Z: their hi parts)
     uint4 xl[Z ? 2 : 1][Z ? D / 16 : 1];        // Z: their lo parts
@@ -487,11 +493,12 @@ struct AssignWave {
                                                              int lane, EPI&& epi) {
         const int half = lane >> 5;
         constexpr int KS = D / 16, PF = 2;
-        const uint4* cr0 = buf + (lane & 31) * CH;
-        const uint4* cr1 = buf + (32 + (lane & 31)) * CH;
+        const uint4* cr0 = buf + (CM ? (lane & 31) : (lane & 31) * CH);
+        const uint4* cr1 = buf + (CM ? 32 + (lane & 31) : (32 + (lane & 31)) * CH);
         const int sw0 = sw(lane & 31), sw1 = sw(32 + (lane & 31));
         auto frag = [&](const uint4* cr, int swr, int i) __attribute__((always_inline)) {
-            return cr[(i / KS) * TG * CH + ((2 * (i % KS) + half) ^ swr)];
+            const int c = 2 * (i % KS) + half;
+            return cr[(i / KS) * TG * CH + (CM ? c * TG : (c ^ swr))];
         };
         f32x16 acc[2][2];
         if constexpr (Z) {
@@ -686,9 +693,11 @@ __global__ __launch_bounds__(512, 1) void k_assign_res(const bf16_t* __restrict_
             // lanes of a wave take consecutive slots, so each load lands at LDS base + 16 lane
             const int t = slot / SLOTS, rem0 = slot % SLOTS;
             const int part = rem0 / (TG * CH), rem = rem0 % (TG * CH);
-            const int row = rem / CH, pc = rem % CH;
+            // the row and chunk whose 16 bytes this slot holds (AW::slot_of inverted)
+            const int row = AW::CM ? rem % TG : rem / CH;
+            const int ch = AW::CM ? rem / TG : (rem % CH) ^ AW::sw(row);
             const int g = min(t * TG + row, groups - 1);
-            lds_load16(rc, s_c + (slot - lane), ((part * groups + g) * D + ((pc ^ AW::sw(row)) * 8)) * 2);
+            lds_load16(rc, s_c + (slot - lane), ((part * groups + g) * D + ch * 8) * 2);
         }
         float c2max, cpmax;
         assign_norms<512>(cn2, cpn, h, groups, ntiles, s_cn2, s_red, c2max, cpmax);
