@@ -46,8 +46,10 @@ def _inputs(kind, n, d, seed):
 
 
 CASES = [("duplicates", 64, 16, 1.0), ("duplicates", 64, 16, 2.0 ** 12), ("duplicates", 64, 16, 2.0 ** -12),
-         ("duplicates", 128, 32, 1.0), ("near", 64, 16, 1.0), ("near", 128, 32, 1.0)]
-IDS = ["dup-d64", "dup-d64-x4096", "dup-d64-x2^-12", "dup-d128", "near-d64", "near-d128"]
+         ("duplicates", 128, 32, 1.0), ("near", 64, 16, 1.0), ("near", 128, 32, 1.0),
+         ("near", 128, 16, 1.0), ("near", 64, 32, 1.0)]
+IDS = ["dup-d64", "dup-d64-x4096", "dup-d64-x2^-12", "dup-d128", "near-d64", "near-d128", "near-d128-r16",
+       "near-d64-r32"]
 
 
 def _run(spr, q, k, v, kw, flags):
@@ -91,6 +93,28 @@ def test_key_screen_in_coordinates_keeps_labels_exact(spr, kind, d, rk, scale):
     assert np.array_equal(gz["q_labels"][0], ref.q_labels), "query labels"
     assert np.array_equal(gz["blocks"][0], ref.blocks), "blocks"
     check_close(gz["o"][0], ref.o, f"O {kind} d={d}", out_rel=2.0 ** -24)
+
+
+@pytest.mark.timeout(300)
+def test_key_screen_modes_agree_on_three_heads(spr):
+    """Three heads (an uneven split into two head groups on two streams), N = 2,500 (not a
+    multiple of 64), r_K = 32: both screens bit-identical, and the oracle per head."""
+    n, d, heads = 2500, 128, 3
+    qs, ks, vs = zip(*(_inputs("near", n, d, seed=40 + i) for i in range(heads)))
+    q, k, v = (np.concatenate(a, axis=0) for a in (qs, ks, vs))
+    kw = dict(n_sample=64, key_rank=32, kv_groups=48, q_groups=24, kmeans_iters=3, density=0.4,
+              probes=16, ridge_lambda=1e-3, corr_rank=4)
+    out = []
+    for flags in (0, spr.F_RAW_KEY_SCREEN):
+        ctx = spr.SparsePR(spr.make_params(heads, n, d, spr.BF16, flags=flags, **kw))
+        out.append(run_gpu_call(ctx, q, k, v, "bf16"))
+        ctx.close()
+    for key in ("key_labels", "key_centroids", "q_labels", "blocks", "o"):
+        assert np.array_equal(out[0][key], out[1][key]), key
+    for i in range(heads):
+        ref = orc.oracle_head(q[i], k[i], v[i], **kw)
+        assert np.array_equal(out[0]["key_labels"][i], ref.key_labels), f"h{i} key labels"
+        assert np.array_equal(out[0]["q_labels"][i], ref.q_labels), f"h{i} query labels"
 
 
 @pytest.mark.timeout(600)
