@@ -170,6 +170,8 @@ def main() -> int:
                          "(SPARSEPR_F_FP8_QK); not the method's precision, never the headline")
     ap.add_argument("--serial-partition", action="store_true",
                     help="every head's partition on one stream (SPARSEPR_F_SERIAL_PARTITION)")
+    ap.add_argument("--uniform-units", action="store_true",
+                    help="sparse kernel in 128-row units only (SPARSEPR_F_UNIFORM_UNITS)")
     ap.add_argument("--raw-key-screen", action="store_true",
                     help="the key k-means screens raw keys, not their coordinates x W "
                          "(SPARSEPR_F_RAW_KEY_SCREEN; same labels)")
@@ -208,7 +210,8 @@ def main() -> int:
     base_flags = ((spr.F_HOST_SOLVE if args.host_solve else 0) |
                   (spr.F_SERIAL_PARTITION if args.serial_partition else 0) |
                   (spr.F_FP8_QK if args.fp8_qk else 0) |
-                  (spr.F_RAW_KEY_SCREEN if args.raw_key_screen else 0))
+                  (spr.F_RAW_KEY_SCREEN if args.raw_key_screen else 0) |
+                  (spr.F_UNIFORM_UNITS if args.uniform_units else 0))
     ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, st, flags=base_flags)
     stream = torch.cuda.current_stream()
 
@@ -341,6 +344,8 @@ def main() -> int:
         "partition_streams": 1 if args.serial_partition or cfg.heads < 2 else 2,
         "recheck_points": stats["recheck_points"],
         "key_screen": "raw keys" if args.raw_key_screen else "key coordinates where they apply",
+        "work_units": ("128-row" if args.uniform_units or args.fp8_qk
+                       else "256-row chunks (8-wave blocks), then 128-row remainders"),
         "dense": dense,
         "roofline": {"kernel": "k_vbsa (variable-block-sparse attention)", "bound": "mfma",
                      "achieved": round(kernel_tflops, 2), "peak": peak,

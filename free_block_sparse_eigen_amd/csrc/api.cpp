@@ -93,7 +93,8 @@ struct sparsepr_ctx {
     sparsepr_params p{};
     int device = 0;
     int H = 0, N = 0, d = 0, Gk = 0, Gq = 0, rK = 0, Dq = 0, k = 0, P = 0, T = 0;
-    int nblk = 0, maxu = 0, splits = 0, dense_units = 0, gmax = 0;
+    int nblk = 0, maxu = 0, maxu_big = 0, splits = 0, dense_units = 0, gmax = 0;
+    bool big_units = false;            // whole 256-row chunks of a query group as 8-wave units
     bool raw = false;                  // SPARSEPR_F_RAW_KMEANS: identity metrics on both sides
     bool svoo = false;                 // SPARSEPR_F_SVOO: alternating co-clustering
     bool fp8 = false;                  // SPARSEPR_F_FP8_QK: fp8 logits in the sparse kernel
@@ -137,8 +138,8 @@ struct sparsepr_ctx {
     float *kcn2 = nullptr, *qcn2 = nullptr, *kcpn = nullptr, *qcpn = nullptr;
     // route
     int32_t *blocks = nullptr, *ucount = nullptr, *probe_pos = nullptr, *probe_orig = nullptr;
-    int32_t *probe_grp = nullptr, *probe_of = nullptr, *nunits = nullptr;
-    int2* units = nullptr;
+    int32_t *probe_grp = nullptr, *probe_of = nullptr, *nunits = nullptr, *nunits_big = nullptr;
+    int2 *units = nullptr, *units_big = nullptr;
     int64_t* pairs = nullptr;
     // attention, probes, fit
     float *o_s = nullptr, *part_ml = nullptr, *part_od = nullptr, *part_os = nullptr;
@@ -166,6 +167,9 @@ struct sparsepr_ctx {
     hipEvent_t ev_qside = nullptr;    // SPARSEPR_F_FP8_QK: the side stream may read q
     bool kperm_recorded = false;      // ev_kperm has been recorded
     hipStream_t side = nullptr;       // fit means, Grams and their copy to the host
+    // the sparse kernel's 128-row units run on ustream beside the 256-row units (big_units)
+    hipStream_t ustream = nullptr;
+    hipEvent_t ev_ufork = nullptr, ev_ujoin = nullptr;
     // the partition's heads in nparts groups, group 0 on the caller's stream, group i > 0 on
     // pstream[i]
     static constexpr int kMaxParts = 4;
@@ -230,7 +234,7 @@ int32_t validate(const sparsepr_params* p) {
     if (!(p->ridge_lambda >= 0.0) || !std::isfinite(p->ridge_lambda)) return SPARSEPR_ERR_INVALID_ARG;
     if (p->flags & ~(SPARSEPR_F_STAGE_TIMING | SPARSEPR_F_RAW_KMEANS | SPARSEPR_F_CHECK_FINITE |
                      SPARSEPR_F_HOST_SOLVE | SPARSEPR_F_SVOO | SPARSEPR_F_SERIAL_PARTITION |
-                     SPARSEPR_F_FP8_QK | SPARSEPR_F_RAW_KEY_SCREEN))
+                     SPARSEPR_F_FP8_QK | SPARSEPR_F_RAW_KEY_SCREEN | SPARSEPR_F_UNIFORM_UNITS))
         return SPARSEPR_ERR_INVALID_ARG;
     if ((p->flags & SPARSEPR_F_RAW_KMEANS) && (p->flags & SPARSEPR_F_SVOO)) return SPARSEPR_ERR_INVALID_ARG;
     return SPARSEPR_OK;
@@ -273,6 +277,9 @@ void derive(sparsepr_ctx& c) {
     c.T = p.kmeans_iters;
     c.nblk = (c.N + kSortChunk - 1) / kSortChunk;
     c.maxu = (c.N + kSparseRows - 1) / kSparseRows + c.Gq;
+    // the fp8-logit experiment keeps 4-wave units only (its fp8 K tiles split over 256 lanes)
+    c.big_units = !c.fp8 && !(p.flags & SPARSEPR_F_UNIFORM_UNITS);
+    c.maxu_big = c.N / kDenseRows + 1;
     c.dense_units = (c.N + kDenseRows - 1) / kDenseRows;
     c.splits = probe_splits(c.N, c.H, c.P);
     c.gmax = std::max(c.Gk, c.Gq);
@@ -356,6 +363,8 @@ void layout(sparsepr_ctx& c, Arena& a) {
     a.take(c.probe_of, HN);
     a.take(c.nunits, H);
     a.take(c.units, H * c.maxu);
+    a.take(c.nunits_big, H);
+    a.take(c.units_big, H * c.maxu_big);
     a.take(c.pairs, H);
     a.take(c.o_s, HND);
     a.take(c.part_ml, H * c.splits * P * 4);
@@ -612,6 +621,11 @@ int32_t sparsepr_create(const sparsepr_params* p, sparsepr_ctx** out) {
             (e = hipEventCreateWithFlags(&c->ev_kperm, hipEventDisableTiming)) != hipSuccess ||
             (e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event / side stream", e);
+        if (c->big_units &&
+            ((e = hipEventCreateWithFlags(&c->ev_ufork, hipEventDisableTiming)) != hipSuccess ||
+             (e = hipEventCreateWithFlags(&c->ev_ujoin, hipEventDisableTiming)) != hipSuccess ||
+             (e = hipStreamCreateWithFlags(&c->ustream, hipStreamNonBlocking)) != hipSuccess))
+            return create_fail(c, SPARSEPR_ERR_HIP, "event / work-unit stream", e);
         if (c->fp8 && (e = hipEventCreateWithFlags(&c->ev_qside, hipEventDisableTiming)) != hipSuccess)
             return create_fail(c, SPARSEPR_ERR_HIP, "event (fp8 scales)", e);
         if (c->nparts > 1 && (e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming)) != hipSuccess)
@@ -659,6 +673,9 @@ void sparsepr_destroy(sparsepr_ctx* c) {
     if (c->ev_kperm) (void)hipEventDestroy(c->ev_kperm);
     if (c->ev_qside) (void)hipEventDestroy(c->ev_qside);
     if (c->side) (void)hipStreamDestroy(c->side);
+    if (c->ustream) (void)hipStreamDestroy(c->ustream);
+    if (c->ev_ufork) (void)hipEventDestroy(c->ev_ufork);
+    if (c->ev_ujoin) (void)hipEventDestroy(c->ev_ujoin);
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     for (int i = 1; i < sparsepr_ctx::kMaxParts; ++i) {
         if (c->ev_kd[i]) (void)hipEventDestroy(c->ev_kd[i]);
@@ -961,7 +978,8 @@ int32_t sparsepr_route(sparsepr_ctx* c, const void* q, const void* k, const void
     launch_fill_i32(c->probe_of, -1, (size_t)c->H * c->N, st);
     launch_probes(c->qoff, c->qperm, c->H, c->N, c->Gq, c->P, c->probe_pos, c->probe_orig,
                   c->probe_grp, c->probe_of, st);
-    launch_units(c->qoff, c->H, c->Gq, kSparseRows, c->maxu, c->units, c->nunits, st);
+    launch_units(c->qoff, c->H, c->Gq, kSparseRows, c->maxu, c->units, c->nunits, st,
+                 c->big_units ? kDenseRows : 0, c->maxu_big, c->units_big, c->nunits_big);
     SPR_LAUNCHED(c, "probes/units");
     mark(c, 3, st);
     c->stage = kStageRoute;
@@ -1045,9 +1063,26 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
         SPR_HIP(c, hipEventRecord(c->ev_probe, st));
     }
     mark(c, 4, st);
+    // Whole 256-row chunks of the query groups in 8-wave blocks (one key-union walk for 256
+    // rows) on this stream, and the rest of each group in 128-row units (4-wave blocks, two
+    // per CU) on a stream of their own beside them: the two write disjoint rows of O_s, and
+    // the small units fill the CUs that the large ones' last round leaves idle.
+    hipStream_t su = st;
+    if (c->big_units) {
+        SPR_HIP(c, hipEventRecord(c->ev_ufork, st));
+        SPR_HIP(c, hipStreamWaitEvent(c->ustream, c->ev_ufork, 0));
+        su = c->ustream;
+        launch_vbsa(c->q_src, c->qperm, c->kp, c->vp, c->vmax, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff,
+                    c->Gk + 1, c->blocks, c->Gq * c->k, c->k, c->units_big, c->maxu_big, c->nunits_big, 1,
+                    c->maxu_big, kDenseRows, c->o_s, 0, st);
+    }
     launch_vbsa(c->q_src, c->qperm, c->kp, c->vp, c->vmax, c->H, c->N, c->d, c->qoff, c->Gq + 1, c->koff, c->Gk + 1,
                 c->blocks, c->Gq * c->k, c->k, c->units, c->maxu, c->nunits, 1, c->maxu, kSparseRows,
-                c->o_s, 0, st, c->fp8 ? c->kp8 : nullptr, c->qmax, c->kmax);
+                c->o_s, 0, su, c->fp8 ? c->kp8 : nullptr, c->qmax, c->kmax);
+    if (c->big_units) {
+        SPR_HIP(c, hipEventRecord(c->ev_ujoin, su));
+        SPR_HIP(c, hipStreamWaitEvent(st, c->ev_ujoin, 0));
+    }
     SPR_LAUNCHED(c, "sparse attention");
     mark(c, 5, st);
     c->stage = kStageAttn;

@@ -109,17 +109,22 @@ void launch_route(const double* cq, const double* ck, double* ck_t, const int32_
 void launch_probes(const int32_t* qoff, const int32_t* qperm, int heads, int n, int gq, int probes,
                    int32_t* probe_pos, int32_t* probe_orig, int32_t* probe_grp, int32_t* probe_of,
                    hipStream_t st);
+// units / nunits: rows_per_unit-row units; with big_rows > 0 each group's whole big_rows-row
+// chunks go to units_big / nunits_big instead ([heads][max_big]) and only the rest of the
+// group to units
 void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int max_units,
-                  int2* units, int32_t* nunits, hipStream_t st);
+                  int2* units, int32_t* nunits, hipStream_t st, int big_rows = 0, int max_big = 0,
+                  int2* units_big = nullptr, int32_t* nunits_big = nullptr);
 // this thread's error detail for calls without a context (sparsepr_last_error(NULL))
 void set_call_error(const char* msg);
 
 // ---- attention ----
 // out_mode 0: fp32 rows, 1: bf16 rows (both at the unit's own row index); unit_rows is
-// kSparseRows or kDenseRows (the units' row count, which fixes the block shape)
+// kSparseRows or kDenseRows (the units' row count, which fixes the block shape: 4 or 8
+// waves)
 // qp: Q in token order; qperm [heads][n] (group-major position -> token) or nullptr
 // vp: bf16 [heads][n][d] with vmax == nullptr (dense baseline), or fp16 scaled per head by
-// 2^v_scale_exp(vmax[h]) (the sparse call, 128-row units); kp8 (with qmax, kmax: the
+// 2^v_scale_exp(vmax[h]) (the sparse call); kp8 (128-row units only) (with qmax, kmax: the
 // per-head largest |q| and |k| as bf16 magnitude bits) selects the fp8-logit experiment:
 // K group-major in FP8 E4M3 scaled by 2^f8_scale_exp(kmax[h]), Q rounded on load
 void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const void* vp,

@@ -9,10 +9,11 @@
 // skipping, not computing-then-masking, is what saves work).
 //
 // Work unit = (head, query group, up to NW x 32 query rows); NW waves x 32 rows. The sparse
-// call runs 4-wave blocks, two per CU: the blocks wait at their tile barriers independently,
-// so one block's waves keep the SIMDs busy while the other's wait (the many partial units
-// of small query groups gain most). The dense baseline, all full units, runs 8-wave
-// blocks that share each key tile over 256 rows.
+// call runs each query group's whole 256-row chunks as units of 8-wave blocks, which share
+// each key tile over 256 rows and so walk the group's routed union once per 256 rows, and
+// the rest of the group in units of 4-wave blocks, two per CU: those blocks wait at their
+// tile barriers independently, so one block's waves keep the SIMDs busy while the other's
+// wait (partial units gain most). The dense baseline, all full units, runs 8-wave blocks.
 //   S^T = K Q^T  : A = K tile from LDS (row-major), B = Q^T fragments held in VGPRs
 //   O^T += V^T P^T: A = V^T read from the row-major V tile with the transposing LDS
 //                   read, B = P^T straight from the S^T accumulators (bf16, no
@@ -415,9 +416,9 @@ void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const
                        qoff_stride, koff, koff_stride, blocks, blocks_head_stride, kblk, units,   \
                        units_head_stride, nunits, nunits_stride, heads, scale_log2, vmax, qmax,  \
                        kmax, out)
-    // the sparse call: 4-wave blocks, fp32 output, fp16 V with its per-head scale
-    // (vmax != nullptr), and with kp8 the fp8 logits; the dense baseline: 8-wave blocks,
-    // bf16 V
+    // the sparse call: fp16 V with its per-head scale (vmax != nullptr), fp32 output, 4-wave
+    // blocks for 128-row units and 8-wave blocks for 256-row units; with kp8 (128-row units
+    // only) the fp8 logits. The dense baseline: 8-wave blocks, bf16 V.
     if (unit_rows == kSparseRows && vmax && kp8) {
         if (d == 128) {
             if (out_mode == 0) SPR_VBSA(128, 0, 4, true, true, kp8); else SPR_VBSA(128, 1, 4, true, true, kp8);
@@ -429,6 +430,12 @@ void launch_vbsa(const bf16_t* qp, const int32_t* qperm, const bf16_t* kp, const
             if (out_mode == 0) SPR_VBSA(128, 0, 4, true, false, kp); else SPR_VBSA(128, 1, 4, true, false, kp);
         } else {
             if (out_mode == 0) SPR_VBSA(64, 0, 4, true, false, kp); else SPR_VBSA(64, 1, 4, true, false, kp);
+        }
+    } else if (vmax) {
+        if (d == 128) {
+            if (out_mode == 0) SPR_VBSA(128, 0, 8, true, false, kp); else SPR_VBSA(128, 1, 8, true, false, kp);
+        } else {
+            if (out_mode == 0) SPR_VBSA(64, 0, 8, true, false, kp); else SPR_VBSA(64, 1, 8, true, false, kp);
         }
     } else {
         if (d == 128) {

@@ -367,47 +367,67 @@ void launch_probes(const int32_t* qoff, const int32_t* qperm, int heads, int n, 
 }
 
 // Block per head: query tiles of `rows_per_unit` rows inside each query group.
-__global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff, int gq,
-                                                int rows_per_unit, int max_units,
-                                                int2* __restrict__ units,
-                                                int32_t* __restrict__ nunits) {
-    __shared__ int base[kMaxGroups + 1];
-    __shared__ int wtot[16];
-    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int32_t* qo = qoff + (size_t)h * (gq + 1);
-    // units per group, then their exclusive prefix over the groups (wave scans and a scan
-    // of the wave totals; gq <= 1024 = blockDim)
-    const int cnt = (tid < gq) ? (qo[tid + 1] - qo[tid] + rows_per_unit - 1) / rows_per_unit : 0;
+// exclusive prefix over the block of one count per thread (wave scans, then a scan of the
+// wave totals); `wtot` holds 16 ints, `total` gets the block's sum
+__device__ inline int block_exclusive_scan(int cnt, int* wtot, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int inc = cnt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int t = __shfl_up(inc, o, 64);
         if (lane >= o) inc += t;
     }
+    __syncthreads();                                  // earlier readers of wtot are done
     if (lane == 63) wtot[w] = inc;
     __syncthreads();
-    int wb = 0, total = 0;
+    int wb = 0;
+    total = 0;
     for (int k = 0; k < 16; ++k) {
         wb += (k < w) ? wtot[k] : 0;
         total += wtot[k];
     }
-    if (tid < gq) base[tid] = wb + inc - cnt;
+    return wb + inc - cnt;
+}
+
+// Work units of the attention kernels: (query group, first row). With big_rows > 0 every
+// whole big_rows-row chunk of a group is one unit of the big list and the rest of the group
+// is cut into rows_per_unit-row units of the other list; with big_rows = 0 the whole group
+// is cut into rows_per_unit-row units. Units of one group are consecutive in each list.
+__global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff, int gq,
+                                                int rows_per_unit, int max_units,
+                                                int2* __restrict__ units,
+                                                int32_t* __restrict__ nunits, int big_rows,
+                                                int max_big, int2* __restrict__ units_big,
+                                                int32_t* __restrict__ nunits_big) {
+    __shared__ int wtot[16];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int32_t* qo = qoff + (size_t)h * (gq + 1);
+    // gq <= 1024 = blockDim: one group per thread
+    const int rows = (tid < gq) ? qo[tid + 1] - qo[tid] : 0;
+    const int nb = big_rows > 0 ? rows / big_rows : 0;
+    const int rest = rows - nb * big_rows;
+    const int ns = (rest + rows_per_unit - 1) / rows_per_unit;
+    int tot_s = 0, tot_b = 0;
+    const int bs = block_exclusive_scan(ns, wtot, tot_s);
+    const int bb = block_exclusive_scan(nb, wtot, tot_b);
     if (tid == 0) {
-        base[gq] = total;
-        nunits[h] = total;
+        nunits[h] = tot_s;
+        if (big_rows > 0) nunits_big[h] = tot_b;
     }
-    __syncthreads();
-    for (int i = tid; i < gq; i += 1024) {
-        const int t_i = base[i + 1] - base[i];
-        for (int t = 0; t < t_i; ++t)
-            units[(size_t)h * max_units + base[i] + t] = make_int2(i, qo[i] + t * rows_per_unit);
+    if (tid < gq) {
+        for (int t = 0; t < nb; ++t)
+            units_big[(size_t)h * max_big + bb + t] = make_int2(tid, qo[tid] + t * big_rows);
+        const int r0 = qo[tid] + nb * big_rows;
+        for (int t = 0; t < ns; ++t)
+            units[(size_t)h * max_units + bs + t] = make_int2(tid, r0 + t * rows_per_unit);
     }
 }
 
 void launch_units(const int32_t* qoff, int heads, int gq, int rows_per_unit, int max_units,
-                  int2* units, int32_t* nunits, hipStream_t st) {
+                  int2* units, int32_t* nunits, hipStream_t st, int big_rows, int max_big,
+                  int2* units_big, int32_t* nunits_big) {
     hipLaunchKernelGGL(k_units, dim3(heads), dim3(1024), 0, st, qoff, gq, rows_per_unit, max_units,
-                       units, nunits);
+                       units, nunits, big_rows, max_big, units_big, nunits_big);
 }
 
 }  // namespace spr

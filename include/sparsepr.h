@@ -108,6 +108,14 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        r_K is 16 or 32). Both screens certify against the same
                                        exact scores and send the rest to the same fp64 recheck,
                                        so the labels are the same either way; for comparison. */
+#define SPARSEPR_F_UNIFORM_UNITS 256u  /* the sparse kernel takes every query group in 128-row work
+                                       units (4-wave blocks, two per CU). By default each group's
+                                       whole 256-row chunks run first as 256-row units (8-wave
+                                       blocks that walk the group's routed key union once for 256
+                                       rows) and only the rest of the group in 128-row units. The
+                                       rows' arithmetic, and so the output, is the same bit for
+                                       bit either way; for comparison. SPARSEPR_F_FP8_QK always
+                                       takes 128-row units. */
 #define SPARSEPR_F_CHECK_FINITE 4u  /* count non-finite values of q and k (partition), v (route)
                                        and o (correct) on the device; read the counts with
                                        sparsepr_get_stats. The stages stay asynchronous and do not

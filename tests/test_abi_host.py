@@ -287,7 +287,21 @@ def test_serial_partition_flag_is_accepted_alone_and_combined():
     for f in (spr.F_SERIAL_PARTITION, spr.F_SERIAL_PARTITION | spr.F_STAGE_TIMING,
               spr.F_SERIAL_PARTITION | spr.F_HOST_SOLVE | spr.F_CHECK_FINITE):
         assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=f, **kw)) == 0
-    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=256, **kw)) == 1
+    assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=512, **kw)) == 1
+
+
+def test_uniform_units_flag_is_accepted_and_keeps_the_workspace():
+    """SPARSEPR_F_UNIFORM_UNITS only changes how the sparse kernel's work is cut: it is valid
+    alone and with the other flags, and the workspace (which always holds both unit lists)
+    is the same with and without it."""
+    kw = dict(kv_groups=16, q_groups=16, density=0.25, probes=8, corr_rank=4)
+    assert spr.F_UNIFORM_UNITS == 256
+    for f in (spr.F_UNIFORM_UNITS, spr.F_UNIFORM_UNITS | spr.F_STAGE_TIMING | spr.F_SERIAL_PARTITION,
+              spr.F_UNIFORM_UNITS | spr.F_FP8_QK):
+        assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=f, **kw)) == 0
+    ws = [spr.sparsepr_workspace_bytes(spr.make_params(2, 75600, 128, spr.BF16, flags=f, **kw))
+          for f in (0, spr.F_UNIFORM_UNITS)]
+    assert ws[0] == ws[1] > 0
 
 
 def test_raw_key_screen_flag_drops_the_split_key_coordinates():
