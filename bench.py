@@ -32,9 +32,11 @@ METRIC = "ms per sparse attention call + executed-pair TFLOPS (% bf16 MFMA peak)
 BF16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "vbsa_c3_traffic.json")
-# sources that define the sparse attention kernel (the traffic counters are tied to them)
+# sources that define the sparse attention stage: its kernel, its work units and their
+# launches (the traffic counters are tied to them)
 KERNEL_SRCS = [os.path.join(ROOT, "free_block_sparse_eigen_amd", "csrc", f)
-               for f in ("kernels_attn.hip", "attn_tile.h", "common.h", "kernels.h")]
+               for f in ("kernels_attn.hip", "attn_tile.h", "common.h", "kernels.h",
+                         "kernels_route.hip", "api.cpp")]
 
 
 def log(msg: str) -> None:
@@ -65,9 +67,9 @@ def copy_calibration(mib: int) -> int:
 
 
 def measured_traffic(flops_per_launch: float, ms: float, workload: str):
-    """HBM bytes per launch of the attention kernel from the committed counter summary,
-    valid only for the workload it was measured on and while the kernel source is
-    unchanged."""
+    """HBM bytes of the sparse attention stage (its two kernel launches) from the committed
+    counter summary, valid only for the workload it was measured on and while the sources
+    of the stage are unchanged."""
     if workload != TRAFFIC_WORKLOAD:
         return None
     try:
@@ -77,7 +79,7 @@ def measured_traffic(flops_per_launch: float, ms: float, workload: str):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_stage")
 
 
 def _oracle_head(args):
@@ -242,6 +244,10 @@ def main() -> int:
     partition_only_ms = ev0.elapsed_time(ev1) / args.steps
     ctx.sparsepr_attention(qd, kd, vd, od)          # leave the context after a whole call
     torch.cuda.synchronize()
+    # One context at a time: each holds streams of its own, and the runtime maps streams onto
+    # a few hardware queues in the order they are made, so the streams of a second context
+    # alive beside the first would share queues with it (and with the caller's stream).
+    ctx.close()
 
     # stage times and the kernel's own events, in a context of their own
     log(f"stage timing: {args.steps} calls in a second context")
@@ -255,6 +261,8 @@ def main() -> int:
     torch.cuda.synchronize()
     stats = sctx.sparsepr_get_stats()
     sctx.close()
+    # the dense baseline and the parity leg in a third context
+    ctx = spr.SparsePR.from_settings(cfg.heads, cfg.n, cfg.d, dt, st, flags=base_flags)
     assert stats["routed_pairs"] == run_stats["routed_pairs"], "the two contexts routed differently"
     stage = dict(zip(["partition", "route", "sparse_attention_kernel", "probe_rows", "probe_fit",
                       "correct"], [round(x, 4) for x in stats["stage_ms"]]))
@@ -345,9 +353,13 @@ def main() -> int:
         "recheck_points": stats["recheck_points"],
         "key_screen": "raw keys" if args.raw_key_screen else "key coordinates where they apply",
         "work_units": ("128-row" if args.uniform_units or args.fp8_qk
-                       else "256-row chunks (8-wave blocks), then 128-row remainders"),
+                       else "256-row units (8-wave blocks) for whole chunks and rests over 128 rows, "
+                            "128-row units for shorter rests, two launches side by side"),
         "dense": dense,
-        "roofline": {"kernel": "k_vbsa (variable-block-sparse attention)", "bound": "mfma",
+        "roofline": {"kernel": ("k_vbsa (variable-block-sparse attention): the sparse stage, 256-row "
+                                "and 128-row units in two launches side by side" if not (args.uniform_units or args.fp8_qk)
+                                else "k_vbsa (variable-block-sparse attention), 128-row units"),
+                     "bound": "mfma",
                      "achieved": round(kernel_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": traffic,

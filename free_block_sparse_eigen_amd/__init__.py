@@ -28,7 +28,7 @@ F_SVOO = 16           # comparison partitioner: alternating Q/K co-clustering (n
 F_SERIAL_PARTITION = 32  # all heads of the partition on the caller's stream (default: two halves, two streams)
 F_FP8_QK = 64         # experiment: the sparse kernel's logits from FP8 E4M3 Q and K (per-head scales)
 F_RAW_KEY_SCREEN = 128  # the key k-means screens raw keys against W c, not their coordinates (same labels)
-F_UNIFORM_UNITS = 256  # the sparse kernel in 128-row units only (default: whole 256-row chunks as 256-row units first)
+F_UNIFORM_UNITS = 256  # the sparse kernel in 128-row units only (default: 256-row units for whole chunks and rests over 128 rows)
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "out of memory",
           4: "HIP error", 5: "stage order", 6: "numerical failure"}

@@ -279,7 +279,7 @@ void derive(sparsepr_ctx& c) {
     c.maxu = (c.N + kSparseRows - 1) / kSparseRows + c.Gq;
     // the fp8-logit experiment keeps 4-wave units only (its fp8 K tiles split over 256 lanes)
     c.big_units = !c.fp8 && !(p.flags & SPARSEPR_F_UNIFORM_UNITS);
-    c.maxu_big = c.N / kDenseRows + 1;
+    c.maxu_big = c.N / kDenseRows + c.Gq;     // whole 256-row chunks, one rest per group
     c.dense_units = (c.N + kDenseRows - 1) / kDenseRows;
     c.splits = probe_splits(c.N, c.H, c.P);
     c.gmax = std::max(c.Gk, c.Gq);
@@ -1063,10 +1063,11 @@ int32_t sparsepr_sparse_attn(sparsepr_ctx* c, void* stream) {
         SPR_HIP(c, hipEventRecord(c->ev_probe, st));
     }
     mark(c, 4, st);
-    // Whole 256-row chunks of the query groups in 8-wave blocks (one key-union walk for 256
-    // rows) on this stream, and the rest of each group in 128-row units (4-wave blocks, two
-    // per CU) on a stream of their own beside them: the two write disjoint rows of O_s, and
-    // the small units fill the CUs that the large ones' last round leaves idle.
+    // 256-row units in 8-wave blocks (one key-union walk for up to 256 rows: each group's
+    // whole 256-row chunks and a rest of more than 128 rows) on this stream, and the shorter
+    // rests in 128-row units (4-wave blocks, two per CU) on a stream of their own beside
+    // them: the two write disjoint rows of O_s, and the small units fill the CUs that the
+    // large ones' last round leaves idle.
     hipStream_t su = st;
     if (c->big_units) {
         SPR_HIP(c, hipEventRecord(c->ev_ufork, st));

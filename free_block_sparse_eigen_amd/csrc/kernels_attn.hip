@@ -9,11 +9,11 @@
 // skipping, not computing-then-masking, is what saves work).
 //
 // Work unit = (head, query group, up to NW x 32 query rows); NW waves x 32 rows. The sparse
-// call runs each query group's whole 256-row chunks as units of 8-wave blocks, which share
-// each key tile over 256 rows and so walk the group's routed union once per 256 rows, and
-// the rest of the group in units of 4-wave blocks, two per CU: those blocks wait at their
-// tile barriers independently, so one block's waves keep the SIMDs busy while the other's
-// wait (partial units gain most). The dense baseline, all full units, runs 8-wave blocks.
+// call runs each query group's whole 256-row chunks, and a rest of more than 128 rows, as
+// units of 8-wave blocks, which share each key tile over up to 256 rows and so walk the
+// group's routed union once per 256 rows; a shorter rest runs in a unit of a 4-wave block,
+// two per CU: those blocks wait at their tile barriers independently, so one block's waves
+// keep the SIMDs busy while the other's wait. The dense baseline runs 8-wave blocks.
 //   S^T = K Q^T  : A = K tile from LDS (row-major), B = Q^T fragments held in VGPRs
 //   O^T += V^T P^T: A = V^T read from the row-major V tile with the transposing LDS
 //                   read, B = P^T straight from the S^T accumulators (bf16, no
@@ -49,8 +49,10 @@ __device__ inline bool unit_of_block(const int32_t* __restrict__ nunits, int str
         if ((int)threadIdx.x < nh) s_cnt[threadIdx.x] = nunits[(size_t)(h0 + threadIdx.x) * stride];
         __syncthreads();
         for (int i = 0; i < nh && !found; ++i) {
-            const int n = s_cnt[i], c = (n + 7) >> 3;
-            const int lo = min(x * c, n), cnt = min(lo + c, n) - lo;
+            // XCD x takes units [x n / 8, (x + 1) n / 8): eighths that differ by at most one
+            // unit (ceil(n / 8) units each would leave the last XCD short on every head)
+            const int n = s_cnt[i];
+            const int lo = (x * n) >> 3, cnt = (((x + 1) * n) >> 3) - lo;
             if (k < cnt) {
                 h = h0 + i;
                 ui = lo + k;

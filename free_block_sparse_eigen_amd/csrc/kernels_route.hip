@@ -390,9 +390,11 @@ __device__ inline int block_exclusive_scan(int cnt, int* wtot, int& total) {
 }
 
 // Work units of the attention kernels: (query group, first row). With big_rows > 0 every
-// whole big_rows-row chunk of a group is one unit of the big list and the rest of the group
-// is cut into rows_per_unit-row units of the other list; with big_rows = 0 the whole group
-// is cut into rows_per_unit-row units. Units of one group are consecutive in each list.
+// whole big_rows-row chunk of a group is one unit of the big list, and so is a rest of more
+// than rows_per_unit rows (a partial unit: it fills as many wave slots as the two small units
+// it replaces, and walks the group's routed keys once instead of twice); a shorter rest is
+// one unit of the other list. With big_rows = 0 the whole group is cut into
+// rows_per_unit-row units. Units of one group are consecutive in each list.
 __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff, int gq,
                                                 int rows_per_unit, int max_units,
                                                 int2* __restrict__ units,
@@ -404,8 +406,12 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff
     const int32_t* qo = qoff + (size_t)h * (gq + 1);
     // gq <= 1024 = blockDim: one group per thread
     const int rows = (tid < gq) ? qo[tid + 1] - qo[tid] : 0;
-    const int nb = big_rows > 0 ? rows / big_rows : 0;
-    const int rest = rows - nb * big_rows;
+    int nb = big_rows > 0 ? rows / big_rows : 0;
+    int rest = rows - nb * big_rows;
+    if (big_rows > 0 && rest > rows_per_unit) {
+        ++nb;
+        rest = 0;
+    }
     const int ns = (rest + rows_per_unit - 1) / rows_per_unit;
     int tot_s = 0, tot_b = 0;
     const int bs = block_exclusive_scan(ns, wtot, tot_s);
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ qoff
     if (tid < gq) {
         for (int t = 0; t < nb; ++t)
             units_big[(size_t)h * max_big + bb + t] = make_int2(tid, qo[tid] + t * big_rows);
-        const int r0 = qo[tid] + nb * big_rows;
+        const int r0 = qo[tid] + rows - rest;
         for (int t = 0; t < ns; ++t)
             units[(size_t)h * max_units + bs + t] = make_int2(tid, r0 + t * rows_per_unit);
     }

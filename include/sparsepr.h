@@ -110,9 +110,10 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        so the labels are the same either way; for comparison. */
 #define SPARSEPR_F_UNIFORM_UNITS 256u  /* the sparse kernel takes every query group in 128-row work
                                        units (4-wave blocks, two per CU). By default each group's
-                                       whole 256-row chunks run first as 256-row units (8-wave
-                                       blocks that walk the group's routed key union once for 256
-                                       rows) and only the rest of the group in 128-row units. The
+                                       whole 256-row chunks, and a rest of more than 128 rows, run
+                                       as 256-row units (8-wave blocks that walk the group's routed
+                                       key union once for up to 256 rows), beside a second launch
+                                       that takes the shorter rests in 128-row units. The
                                        rows' arithmetic, and so the output, is the same bit for
                                        bit either way; for comparison. SPARSEPR_F_FP8_QK always
                                        takes 128-row units. */
