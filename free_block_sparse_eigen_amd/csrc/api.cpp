@@ -475,10 +475,14 @@ int32_t recheck(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const
     return SPARSEPR_OK;
 }
 
+// round: -1 enqueues the seeds only, 0 .. T-1 that Lloyd round only, kAllRounds the seeds
+// and every round (the partition interleaves the rounds of its head groups' streams so that
+// every stream is fed as the host enqueues).
+constexpr int kAllRounds = -2;
 int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const double* l64, int groups,
               int32_t* labels, int32_t* flags, int32_t* sorted, int32_t* off, double* mean_raw,
               double* c64, bf16_t* cpart, float* cn2, float* cpn, double* c2_64, hipStream_t st,
-              const bf16_t* zhl = nullptr, const float* zkb = nullptr) {
+              const bf16_t* zhl = nullptr, const float* zkb = nullptr, int round = kAllRounds) {
     // heads h0 .. h0 + hh - 1: every buffer is head-major, so the slice starts h0 heads in
     const size_t h = h0, N = c->N, d = c->d, cdim = dim > 0 ? dim : c->d;
     x += h * N * d;
@@ -506,10 +510,14 @@ int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const d
         zhl += h * N * 2 * dim;
         zkb += h * N;
     }
-    launch_seed_centroids(x, hh, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
-                          cpn, c2_64, st, crow, coords);
-    SPR_LAUNCHED(c, "seed centroids");
-    for (int t = 0; t < c->T; ++t) {
+    if (round == kAllRounds || round == -1) {
+        launch_seed_centroids(x, hh, c->N, c->d, l64, dim, groups, c->weyl_a, mean_raw, c64, cpart, cn2,
+                              cpn, c2_64, st, crow, coords);
+        SPR_LAUNCHED(c, "seed centroids");
+    }
+    const int t0 = round == kAllRounds ? 0 : std::max(round, 0);
+    const int t1 = round == kAllRounds ? c->T : (round < 0 ? 0 : round + 1);
+    for (int t = t0; t < t1; ++t) {
         int32_t* fc = flags + (size_t)t * c->H + h;
         launch_assign(x, hh, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, flag_list, st, zhl, zkb, dim);
         SPR_LAUNCHED(c, "assign");
@@ -765,38 +773,70 @@ int32_t partition_svoo(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hi
     return permute_keys_side(c, k16, st);
 }
 
-// Keys: Lloyd in the M_K eigen-coordinates W (already in c->w64); queries: the logit-profile
-// metric M = C_K^T C_K / d (fp64 Gram of the raw key centroids) used in full on the device,
-// then Lloyd. Heads h0 .. h0 + hh - 1, all on stream s.
-int32_t partition_heads(sparsepr_ctx* c, int h0, int hh, const bf16_t* q16, const bf16_t* k16,
-                        hipStream_t s, hipEvent_t keys_done) {
+// Keys of heads h0 .. h0 + hh - 1 on stream s, one Lloyd step (round -1: the key
+// coordinates and the seeds): Lloyd in the M_K eigen-coordinates W (already in c->w64);
+// keys_done is recorded after the last round.
+int32_t partition_keys(sparsepr_ctx* c, int h0, int hh, const bf16_t* k16, hipStream_t s,
+                       hipEvent_t keys_done, int round) {
     const size_t h = h0, d = c->d;
-    if (c->ycoord) {                    // every key's W coordinates, for the candidate recheck
+    if (round == -1 && c->ycoord) {                    // every key's W coordinates, for the candidate recheck
         launch_coords(k16 + h * c->N * d, hh, c->N, c->d, c->w64 + h * d * c->rK, c->rK,
                       c->ycoord + h * c->N * c->rK, s);
         SPR_LAUNCHED(c, "key coordinates");
     }
-    if (c->zhl) {                       // the same coordinates, split, for the key screen
+    if (round == -1 && c->zhl) {        // the same coordinates, split, for the key screen
         launch_zcoords(k16 + h * c->N * d, hh, c->N, c->d, c->w64 + h * d * c->rK, c->rK,
                        c->zhl + h * c->N * 2 * c->rK, c->zkb + h * c->N, s);
         SPR_LAUNCHED(c, "key coordinates (screen)");
     }
     int32_t rc = lloyd(c, h0, hh, k16, c->rK, c->w64, c->Gk, c->klab, c->flag_cnt, c->kperm, c->koff,
-                       c->kraw, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, s, c->zhl, c->zkb);
+                       c->kraw, c->kc64, c->kcp, c->kcn2, c->kcpn, c->kc2, s, c->zhl, c->zkb, round);
     if (rc) return rc;
-    SPR_HIP(c, hipEventRecord(keys_done, s));
-    launch_gram_f64(c->kraw + h * c->Gk * d, hh, c->Gk, c->d, 1.0 / c->d, c->mq + h * d * d, s);
-    SPR_LAUNCHED(c, "query metric");
+    if (round == c->T - 1) SPR_HIP(c, hipEventRecord(keys_done, s));
+    return SPARSEPR_OK;
+}
+
+// Queries of heads h0 .. h0 + hh - 1 on stream s, one Lloyd step (round -1: the
+// logit-profile metric M = C_K^T C_K / d, the fp64 Gram of the raw key centroids used in
+// full on the device, and the seeds).
+int32_t partition_queries(sparsepr_ctx* c, int h0, int hh, const bf16_t* q16, hipStream_t s, int round) {
+    const size_t h = h0, d = c->d;
+    if (round == -1) {
+        launch_gram_f64(c->kraw + h * c->Gk * d, hh, c->Gk, c->d, 1.0 / c->d, c->mq + h * d * d, s);
+        SPR_LAUNCHED(c, "query metric");
+    }
     return lloyd(c, h0, hh, q16, 0, c->mq, c->Gq, c->qlab, c->flag_cnt + (size_t)c->T * c->H, c->qperm,
-                 c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, s);
+                 c->qoff, c->qraw, c->qc64, c->qcp, c->qcn2, c->qcpn, c->qc2, s, nullptr, nullptr, round);
+}
+
+// Heads h0 .. h0 + hh - 1 of K (and of the V handed to sparsepr_attention) into group-major
+// order on the side stream, once their keys are partitioned.
+int32_t permute_group_side(sparsepr_ctx* c, int h0, int hh, const bf16_t* k16, hipEvent_t keys_done) {
+    const size_t h = h0, nd = (size_t)c->N * c->d;
+    SPR_HIP(c, hipStreamWaitEvent(c->side, keys_done, 0));
+    launch_permute(k16 + h * nd, c->kperm + h * c->N, hh, c->N, c->d, c->kp + h * nd, c->side);
+    SPR_LAUNCHED(c, "permute K");
+    if (c->fp8) {
+        launch_permute_k8(k16 + h * nd, c->kperm + h * c->N, hh, c->N, c->d, c->kmax + h, c->kp8 + h * nd,
+                          c->side);
+        SPR_LAUNCHED(c, "permute K (fp8)");
+    }
+    if (c->v_pre) {              // its magnitudes were taken during the eigensolve
+        launch_permute_f16(c->v_pre + h * nd, c->kperm + h * c->N, hh, c->N, c->d, c->vmax + h,
+                           c->vp + h * nd, c->side);
+        SPR_LAUNCHED(c, "permute V");
+    }
+    return SPARSEPR_OK;
 }
 
 // The per-head steps run as nparts groups of consecutive heads, each on its own stream
 // (group 0 on st), so that the many small, latency-bound launches of one group (recheck,
 // sort, centroid finish) overlap the other groups' work; with SPARSEPR_F_SERIAL_PARTITION
 // (or one head) all heads run on st. The other streams start after an event on st and are
-// joined back into it. K is permuted on the side stream once every group's keys are
-// partitioned, overlapping the query side.
+// joined back into it. The host enqueues the groups' steps round by round, every group's keys
+// before any group's queries, so that each stream is fed while the host works; each group's
+// K (and V) is permuted on the side stream as soon as its keys are partitioned, overlapping
+// the query side.
 int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf16_t* k16, hipStream_t st) {
     int32_t rc;
     const int np = c->nparts;
@@ -804,31 +844,36 @@ int32_t partition_keys_and_queries(sparsepr_ctx* c, const bf16_t* q16, const bf1
         SPR_HIP(c, hipEventRecord(c->ev_fork, st));
         for (int i = 1; i < np; ++i) SPR_HIP(c, hipStreamWaitEvent(c->pstream[i], c->ev_fork, 0));
     }
+    auto group = [&](int i, int& h0, int& hh, hipStream_t& s, hipEvent_t& kd) {
+        h0 = (int)((int64_t)c->H * i / np);
+        hh = (int)((int64_t)c->H * (i + 1) / np) - h0;
+        s = i == 0 ? st : c->pstream[i];
+        kd = i == 0 ? c->ev_kdone : c->ev_kd[i];
+    };
+    int h0, hh;
+    hipStream_t s;
+    hipEvent_t kd;
+    for (int r = -1; r < c->T; ++r)
+        for (int i = 0; i < np; ++i) {
+            group(i, h0, hh, s, kd);
+            if ((rc = partition_keys(c, h0, hh, k16, s, kd, r))) return rc;
+        }
     for (int i = 0; i < np; ++i) {
-        const int h0 = (int)((int64_t)c->H * i / np), h1 = (int)((int64_t)c->H * (i + 1) / np);
-        hipStream_t s = i == 0 ? st : c->pstream[i];
-        hipEvent_t kd = i == 0 ? c->ev_kdone : c->ev_kd[i];
-        if ((rc = partition_heads(c, h0, h1 - h0, q16, k16, s, kd))) return rc;
-        SPR_HIP(c, hipStreamWaitEvent(c->side, kd, 0));
+        group(i, h0, hh, s, kd);
+        if ((rc = permute_group_side(c, h0, hh, k16, kd))) return rc;
     }
+    if (c->v_pre) c->v_pre_done = true;
+    SPR_HIP(c, hipEventRecord(c->ev_kperm, c->side));           // the sparse stage waits for it
+    c->kperm_recorded = true;
+    for (int r = -1; r < c->T; ++r)
+        for (int i = 0; i < np; ++i) {
+            group(i, h0, hh, s, kd);
+            if ((rc = partition_queries(c, h0, hh, q16, s, r))) return rc;
+        }
     for (int i = 1; i < np; ++i) {
         SPR_HIP(c, hipEventRecord(c->ev_jn[i], c->pstream[i]));
         SPR_HIP(c, hipStreamWaitEvent(st, c->ev_jn[i], 0));
     }
-    // K into group-major order on the side stream; the sparse stage waits for ev_kperm
-    launch_permute(k16, c->kperm, c->H, c->N, c->d, c->kp, c->side);
-    SPR_LAUNCHED(c, "permute K");
-    if (c->fp8) {
-        launch_permute_k8(k16, c->kperm, c->H, c->N, c->d, c->kmax, c->kp8, c->side);
-        SPR_LAUNCHED(c, "permute K (fp8)");
-    }
-    if (c->v_pre) {              // its magnitudes were taken during the eigensolve
-        launch_permute_f16(c->v_pre, c->kperm, c->H, c->N, c->d, c->vmax, c->vp, c->side);
-        SPR_LAUNCHED(c, "permute V");
-        c->v_pre_done = true;
-    }
-    SPR_HIP(c, hipEventRecord(c->ev_kperm, c->side));
-    c->kperm_recorded = true;
     mark(c, 1, st);
     c->stage = kStagePartition;
     return SPARSEPR_OK;
