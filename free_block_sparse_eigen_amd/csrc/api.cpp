@@ -88,6 +88,7 @@ private:
 
 // Streams the partition's heads are spread over (one group of consecutive heads each).
 constexpr int kPartitionStreams = 2;
+constexpr int64_t kBigUnitsMinRows = int64_t(1) << 17;   // H N from which 256-row units run
 
 struct sparsepr_ctx {
     sparsepr_params p{};
@@ -277,8 +278,10 @@ void derive(sparsepr_ctx& c) {
     c.T = p.kmeans_iters;
     c.nblk = (c.N + kSortChunk - 1) / kSortChunk;
     c.maxu = (c.N + kSparseRows - 1) / kSparseRows + c.Gq;
-    // the fp8-logit experiment keeps 4-wave units only (its fp8 K tiles split over 256 lanes)
-    c.big_units = !c.fp8 && !(p.flags & SPARSEPR_F_UNIFORM_UNITS);
+    // The fp8-logit experiment keeps 4-wave units only (its fp8 K tiles split over 256 lanes).
+    // Below 2^17 query rows a call (512 units of 256 rows, two rounds of the CUs) the second
+    // launch and its stream fork and join cost more than the longer walks save.
+    c.big_units = !c.fp8 && !(p.flags & SPARSEPR_F_UNIFORM_UNITS) && (int64_t)c.H * c.N >= kBigUnitsMinRows;
     c.maxu_big = c.N / kDenseRows + c.Gq;     // whole 256-row chunks, one rest per group
     c.dense_units = (c.N + kDenseRows - 1) / kDenseRows;
     c.splits = probe_splits(c.N, c.H, c.P);

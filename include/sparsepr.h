@@ -113,7 +113,9 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
                                        whole 256-row chunks, and a rest of more than 128 rows, run
                                        as 256-row units (8-wave blocks that walk the group's routed
                                        key union once for up to 256 rows), beside a second launch
-                                       that takes the shorter rests in 128-row units. The
+                                       that takes the shorter rests in 128-row units (calls of
+                                       at least 2^17 query rows, H N; smaller ones always take
+                                       128-row units). The
                                        rows' arithmetic, and so the output, is the same bit for
                                        bit either way; for comparison. SPARSEPR_F_FP8_QK always
                                        takes 128-row units. */
