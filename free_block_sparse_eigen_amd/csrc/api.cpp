@@ -528,8 +528,11 @@ int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const d
         if (rc) return rc;
         launch_counting_sort(labels, hh, c->N, groups, blkhist, blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");
-        launch_group_means(x, hh, c->N, c->d, sorted, off, groups, mean_raw, l64, dim, c64, cpart,
-                           cn2, cpn, c2_64, st, crow, coords);
+        // the last round's raw means are the result; the screening vectors, metric-space
+        // centroids and row copies that the finish derives from them would feed only a
+        // further round, so it is skipped there
+        launch_group_means(x, hh, c->N, c->d, sorted, off, groups, mean_raw, t + 1 < c->T ? l64 : nullptr,
+                           dim, c64, cpart, cn2, cpn, c2_64, st, crow, coords);
         SPR_LAUNCHED(c, "group means");
     }
     return SPARSEPR_OK;
