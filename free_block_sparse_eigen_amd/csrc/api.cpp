@@ -254,10 +254,12 @@ struct Arena {
 };
 
 // The key side screens in its coordinates x W (bf16 hi + lo, depth 4 r_K instead of 2 d)
-// when the centroids stay resident in LDS and r_K has a kernel (16 or 32): the W metric
-// path only (not the identity-metric or co-clustering partitioners).
+// when the centroids' split coordinates stay resident in LDS (G_k r_K of them, hi and lo)
+// and r_K has a kernel (16 or 32): the W metric path only (not the identity-metric or
+// co-clustering partitioners). Where the raw screen would stream its centroids (large G_k),
+// the queued keys' candidate lists are screened in the same coordinates.
 bool key_screen_in_coords(const sparsepr_ctx& c) {
-    return !c.raw && !c.svoo && !(c.p.flags & SPARSEPR_F_RAW_KEY_SCREEN) && !assign_streams(c.Gk, c.d) &&
+    return !c.raw && !c.svoo && !(c.p.flags & SPARSEPR_F_RAW_KEY_SCREEN) && !assign_streams(c.Gk, c.rK) &&
            (c.rK == 16 || c.rK == 32);
 }
 
@@ -457,7 +459,8 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 // screened again for candidate lists first, so that only those are checked.
 int32_t recheck(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const double* l64,
                 const double* c64, const double* c2_64, const bf16_t* cpart, const float* cn2,
-                const float* cpn, int groups, const int32_t* fc, int32_t* labels, hipStream_t st) {
+                const float* cpn, int groups, const int32_t* fc, int32_t* labels, hipStream_t st,
+                const bf16_t* zhl = nullptr, const float* zkb = nullptr) {
     const size_t h = h0, N = c->N;
     const int32_t* flag_list = c->flag_list + h * N;
     if (c->cand && assign_streams(groups, c->d) && dim <= kCandidateMaxDim) {
@@ -465,8 +468,9 @@ int32_t recheck(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const
         int32_t* ncand = c->ncand + h * N;
         int32_t* ovf_cnt = c->ovf_cnt + h;
         int32_t* ovf_list = c->ovf_list + h * N;
+        // with zhl the keys were screened in their split coordinates: their candidates too
         launch_candidates(x, hh, c->N, c->d, cpart, cn2, cpn, groups, fc, flag_list, cand, ncand, ovf_cnt,
-                          ovf_list, st);
+                          ovf_list, st, zhl, zkb, dim);
         const double* yc = (dim > 0 && c->ycoord) ? c->ycoord + h * N * dim : nullptr;
         launch_recheck_cand(x, hh, c->N, c->d, l64, dim, c->crow + h * c->gmax * c->d, c2_64, groups, fc,
                             flag_list, cand, ncand, yc, labels, st);
@@ -524,7 +528,8 @@ int32_t lloyd(sparsepr_ctx* c, int h0, int hh, const bf16_t* x, int dim, const d
         int32_t* fc = flags + (size_t)t * c->H + h;
         launch_assign(x, hh, c->N, c->d, cpart, cn2, cpn, groups, labels, fc, flag_list, st, zhl, zkb, dim);
         SPR_LAUNCHED(c, "assign");
-        int32_t rc = recheck(c, h0, hh, x, dim, l64, c64, c2_64, cpart, cn2, cpn, groups, fc, labels, st);
+        int32_t rc = recheck(c, h0, hh, x, dim, l64, c64, c2_64, cpart, cn2, cpn, groups, fc, labels, st,
+                             zhl, zkb);
         if (rc) return rc;
         launch_counting_sort(labels, hh, c->N, groups, blkhist, blkoff, sorted, off, st);
         SPR_LAUNCHED(c, "counting sort");

@@ -61,9 +61,12 @@ void launch_recheck(const bf16_t* x, int heads, int n, int d, const double* l64,
 constexpr int kMaxCandidates = 32;
 constexpr int kCandidateMaxDim = 32;     // factor widths above this take the full recheck
 bool assign_streams(int groups, int d);
+// zhl, kb, dz (the key side screened in its split coordinates, dz = r_K of 16 or 32): the
+// queued keys are screened again in those coordinates against cpart's split coordinates
 void launch_candidates(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                        const float* cpn, int groups, const int32_t* flag_count, const int32_t* flag_list,
-                       int32_t* cand, int32_t* ncand, int32_t* ovf_count, int32_t* ovf_list, hipStream_t st);
+                       int32_t* cand, int32_t* ncand, int32_t* ovf_count, int32_t* ovf_list, hipStream_t st,
+                       const bf16_t* zhl = nullptr, const float* kb = nullptr, int dz = 0);
 void launch_recheck_cand(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,
                          const double* crow, const double* c2_64, int groups, const int32_t* flag_count,
                          const int32_t* flag_list, const int32_t* cand, const int32_t* ncand,

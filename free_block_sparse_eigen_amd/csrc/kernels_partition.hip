@@ -462,6 +462,40 @@ struct AssignWave {
         }
     }
 
+    // Z: as load_z, for the queued points q_base .. q_base + 63 of the head's queue fl (count
+    // entries; a lane past the end reads the last queued point and is zeroed)
+    __device__ __attribute__((always_inline)) void load_queued_z(const bf16_t* __restrict__ zhl,
+                                                                 const float* __restrict__ kb, int n, int h,
+                                                                 const int32_t* __restrict__ fl, int q_base,
+                                                                 int count, int lane) {
+        const int half = lane >> 5;
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            const int pt = fl[min(q_base + 32 * pb + (lane & 31), count - 1)];
+            const bf16_t* zr = zhl + ((size_t)h * n + pt) * 2 * D;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                xf[pb][kk] = *reinterpret_cast<const uint4*>(zr + 16 * kk + 8 * half);
+                xl[pb][kk] = *reinterpret_cast<const uint4*>(zr + D + 16 * kk + 8 * half);
+            }
+            xk[pb] = kb[(size_t)h * n + pt];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+            if (q_base + 32 * pb + (lane & 31) >= count) {
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    xf[pb][kk] = make_uint4(0, 0, 0, 0);
+                    xl[pb][kk] = make_uint4(0, 0, 0, 0);
+                }
+            }
+            best[pb] = INFINITY;
+            second[pb] = INFINITY;
+            bg[pb] = 0x7fffffff;
+        }
+    }
+
     // After the scores: the window [.., thr] of screened scores that can hold the exact
     // argmin. A centroid whose screened score s passes the certification test against the
     // best b (s - b > the test's margin at (s, b)) is certifiably worse than the best, so
@@ -773,7 +807,10 @@ __global__ __launch_bounds__(256, 2) void k_assign(const bf16_t* __restrict__ x,
 // (k_recheck_cand) needs only those. A point with more than kMaxCand goes to a second queue
 // (ovf_list) for the full recheck. The lists take 32 KB of LDS beside the two 32 KB centroid
 // tiles, so one block runs per CU.
-template <int D>
+// Z: the keys screened in their split coordinates (x = zhl, D = r_K, bound coefficients kb)
+// against the centroids' split coordinates, with the same products and bound as the
+// resident screen in the coordinates.
+template <int D, bool Z = false>
 __global__ __launch_bounds__(256, 1) void k_candidates(const bf16_t* __restrict__ x, int n,
                                                        const bf16_t* __restrict__ cpart,
                                                        const float* __restrict__ cn2,
@@ -783,10 +820,12 @@ __global__ __launch_bounds__(256, 1) void k_candidates(const bf16_t* __restrict_
                                                        int32_t* __restrict__ cand,
                                                        int32_t* __restrict__ ncand,
                                                        int32_t* __restrict__ ovf_count,
-                                                       int32_t* __restrict__ ovf_list) {
-    using AW = AssignWave<D>;
+                                                       int32_t* __restrict__ ovf_list,
+                                                       const float* __restrict__ kb) {
+    using AW = AssignWave<D, Z>;
     constexpr int CH = AW::CH, TG = kAssignTG, SLOTS = AW::SLOTS;
     constexpr int PER = SLOTS / 256;
+    static_assert(SLOTS % 256 == 0, "a tile must split evenly over the block");
     __shared__ uint4 s_c0[SLOTS];
     __shared__ uint4 s_c1[SLOTS];
     __shared__ float s_cn2[kMaxGroups + TG];
@@ -804,9 +843,11 @@ __global__ __launch_bounds__(256, 1) void k_candidates(const bf16_t* __restrict_
             const int first = (w * PER + m) * 64;
             const int slot = first + lane;
             const int part = slot / (TG * CH), rem = slot % (TG * CH);
-            const int row = rem / CH, pc = rem % CH;
+            // the row and chunk whose 16 bytes this slot holds (AW::slot_of inverted)
+            const int row = AW::CM ? rem % TG : rem / CH;
+            const int ch = AW::CM ? rem / TG : (rem % CH) ^ AW::sw(row);
             const int g = min(t * TG + row, groups - 1);
-            lds_load16(rc, buf + first, ((part * groups + g) * D + ((pc ^ AW::sw(row)) * 8)) * 2);
+            lds_load16(rc, buf + first, ((part * groups + g) * D + ch * 8) * 2);
         }
     };
     const int q_base = blockIdx.x * 256 + w * 64;
@@ -814,7 +855,8 @@ __global__ __launch_bounds__(256, 1) void k_candidates(const bf16_t* __restrict_
     s_nc[w][lane] = 0;
     issue(0, s_c0);
     AW aw;
-    aw.load_queued(x, n, h, fl, q_base, count, lane);
+    if constexpr (Z) aw.load_queued_z(x, kb, n, h, fl, q_base, count, lane);
+    else aw.load_queued(x, n, h, fl, q_base, count, lane);
     float c2max, cpmax;
     assign_norms<256>(cn2, cpn, h, groups, ntiles, s_cn2, s_red, c2max, cpmax);
     __builtin_amdgcn_s_waitcnt(0);
@@ -987,15 +1029,22 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const bf16_t* __restrict__
 
 void launch_candidates(const bf16_t* x, int heads, int n, int d, const bf16_t* cpart, const float* cn2,
                        const float* cpn, int groups, const int32_t* flag_count, const int32_t* flag_list,
-                       int32_t* cand, int32_t* ncand, int32_t* ovf_count, int32_t* ovf_list, hipStream_t st) {
+                       int32_t* cand, int32_t* ncand, int32_t* ovf_count, int32_t* ovf_list, hipStream_t st,
+                       const bf16_t* zhl, const float* kb, int dz) {
     launch_fill_i32(ovf_count, 0, heads, st);
     dim3 grid((n + 255) / 256, heads);
-    if (d == 128)
-        hipLaunchKernelGGL(k_candidates<128>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
-                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list);
+    if (zhl != nullptr && dz == 32)
+        hipLaunchKernelGGL((k_candidates<32, true>), grid, dim3(256), 0, st, zhl, n, cpart, cn2, cpn, groups,
+                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list, kb);
+    else if (zhl != nullptr)
+        hipLaunchKernelGGL((k_candidates<16, true>), grid, dim3(256), 0, st, zhl, n, cpart, cn2, cpn, groups,
+                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list, kb);
+    else if (d == 128)
+        hipLaunchKernelGGL((k_candidates<128>), grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
+                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list, nullptr);
     else
-        hipLaunchKernelGGL(k_candidates<64>, grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
-                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list);
+        hipLaunchKernelGGL((k_candidates<64>), grid, dim3(256), 0, st, x, n, cpart, cn2, cpn, groups,
+                           flag_count, flag_list, cand, ncand, ovf_count, ovf_list, nullptr);
 }
 
 void launch_recheck_cand(const bf16_t* x, int heads, int n, int d, const double* l64, int dim,

@@ -104,8 +104,9 @@ enum { SPARSEPR_BF16 = 0, SPARSEPR_F32 = 1 };
 #define SPARSEPR_F_RAW_KEY_SCREEN 128u  /* the key k-means screens each key in raw space (x against
                                        C' = W c, depth 2 d) instead of in its coordinates x W
                                        (split into bf16 hi + lo, depth 4 r_K, formed once per
-                                       call; the default when the key centroids fit in LDS and
-                                       r_K is 16 or 32). Both screens certify against the same
+                                       call; the default when the key centroids' split
+                                       coordinates fit in LDS and r_K is 16 or 32, also for the
+                                       candidate lists of a large G_k). Both screens certify against the same
                                        exact scores and send the rest to the same fp64 recheck,
                                        so the labels are the same either way; for comparison. */
 #define SPARSEPR_F_UNIFORM_UNITS 256u  /* the sparse kernel takes every query group in 128-row work

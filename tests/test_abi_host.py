@@ -307,15 +307,16 @@ def test_uniform_units_flag_is_accepted_and_keeps_the_workspace():
 def test_raw_key_screen_flag_drops_the_split_key_coordinates():
     """By default the key screen runs on the split coordinates x W (bf16 hi + lo, [H][N][2][r_K])
     and a bound coefficient per key (fp32 [H][N]); SPARSEPR_F_RAW_KEY_SCREEN screens raw keys
-    and needs neither. Key ranks without a coordinate kernel (8) and key groups that do not fit
-    in LDS (384 at d = 128) never take them."""
+    and needs neither. Key ranks without a coordinate kernel (8) never take them; key groups
+    whose raw screen streams its centroids (384 at d = 128) still do, since their split
+    coordinates fit in LDS (their candidate lists are then screened in the coordinates too)."""
     kw = dict(q_groups=16, density=0.25, probes=8, corr_rank=4)
     ws = lambda f, rk, gk, d=64: spr.sparsepr_workspace_bytes(
         spr.make_params(2, 1024, d, spr.BF16, flags=f, key_rank=rk, kv_groups=gk, **kw))
     assert ws(0, 16, 16) - ws(spr.F_RAW_KEY_SCREEN, 16, 16) == 2 * 1024 * 2 * 16 * 2 + 2 * 1024 * 4
     assert ws(0, 32, 16) - ws(spr.F_RAW_KEY_SCREEN, 32, 16) == 2 * 1024 * 2 * 32 * 2 + 2 * 1024 * 4
     assert ws(0, 8, 16) == ws(spr.F_RAW_KEY_SCREEN, 8, 16)
-    assert ws(0, 32, 384, 128) == ws(spr.F_RAW_KEY_SCREEN, 32, 384, 128)
+    assert ws(0, 32, 384, 128) - ws(spr.F_RAW_KEY_SCREEN, 32, 384, 128) == 2 * 1024 * 2 * 32 * 2 + 2 * 1024 * 4
     assert spr.sparsepr_validate(spr.make_params(2, 1024, 64, spr.BF16, flags=spr.F_RAW_KEY_SCREEN,
                                                  kv_groups=16, **kw)) == 0
 

@@ -134,3 +134,35 @@ def test_key_screen_modes_agree_on_c2(spr):
         f"{out[1]['stats']['recheck_points']} (raw keys)")
     for key in ("key_labels", "key_centroids", "q_labels", "blocks", "o"):
         assert np.array_equal(out[0][key], out[1][key]), key
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kind", ["near", "duplicates"])
+def test_key_screen_modes_agree_with_candidate_lists(spr, kind):
+    """384 key groups at d = 128: the raw screen streams its centroids and the keys it does not
+    certify get candidate lists before the fp64 check; in the coordinates the screen stays
+    resident and the lists are screened in the coordinates too. Clustered keys (and exact
+    duplicates) leave many keys near a boundary, so the lists are long and some overflow to
+    the full recheck. Both screens bit-identical, on two heads over two streams; the oracle
+    as well for the clustered keys."""
+    n, d, heads = 12000, 128, 2
+    qs, ks, vs = zip(*(_inputs(kind, n, d, seed=70 + i) for i in range(heads)))
+    q, k, v = (np.concatenate(a, axis=0) for a in (qs, ks, vs))
+    kw = dict(n_sample=64, key_rank=32, kv_groups=384, q_groups=24, kmeans_iters=3, density=0.3,
+              probes=16, ridge_lambda=1e-3, corr_rank=4)
+    out = []
+    for flags in (0, spr.F_RAW_KEY_SCREEN):
+        ctx = spr.SparsePR(spr.make_params(heads, n, d, spr.BF16, flags=flags, **kw))
+        out.append(run_gpu_call(ctx, q, k, v, "bf16"))
+        ctx.close()
+    say(f"384 groups, {kind}: recheck points {out[0]['stats']['recheck_points']} (coordinates), "
+        f"{out[1]['stats']['recheck_points']} (raw keys)")
+    assert out[0]["stats"]["recheck_points"] > 0
+    for key in ("key_labels", "key_centroids", "q_labels", "blocks", "o"):
+        assert np.array_equal(out[0][key], out[1][key]), key
+    if kind == "duplicates":
+        return
+    for i in range(heads):
+        ref = orc.oracle_head(q[i], k[i], v[i], **kw)
+        assert np.array_equal(out[0]["key_labels"][i], ref.key_labels), f"h{i} key labels"
+        assert np.array_equal(out[0]["q_labels"][i], ref.q_labels), f"h{i} query labels"
